@@ -1,0 +1,189 @@
+"""fp64 CPU oracle for the selective state-space scan -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The HIP library never does, and this package
+never imports the HIP library: the two share no code. The arithmetic lives in
+``ssm_oracle.c`` (plain sequential loops in double precision, built with gcc -O2
+-ffp-contract=off); this file only converts inputs to float64 and calls it.
+
+Inputs are torch tensors or numpy arrays in any float dtype. bfloat16 values are
+widened to float64 exactly (a bfloat16 is the top 16 bits of a float32). Outputs are
+float64 numpy arrays. Layouts are those of ``ssm_oracle.c``.
+
+Page references for what the loops compute are in ``ssm_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "libssm_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GCC_FLAGS = ["-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-std=c99"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ssm_oracle.c into libssm_oracle.so with the host C compiler."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i64, dp = ctypes.c_int64, ctypes.c_void_p
+        for name in ("oracle_scan_f64", "oracle_scan_c128"):
+            f = getattr(lib, name)
+            f.argtypes = [i64, i64, i64, i64] + [dp] * 10
+            f.restype = ctypes.c_int
+        for name in ("oracle_step_f64", "oracle_step_c128"):
+            f = getattr(lib, name)
+            f.argtypes = [i64, i64, i64, i64] + [dp] * 9
+            f.restype = ctypes.c_int
+        lib.oracle_state_bytes.argtypes = [i64, i64, i64, i64]
+        lib.oracle_state_bytes.restype = i64
+        _lib = lib
+        return lib
+
+
+def to_f64(a) -> np.ndarray:
+    """Exact widening of a tensor/array to a contiguous float64 numpy array."""
+    if a is None:
+        return None
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous()
+            if a.dtype == torch.bfloat16:
+                bits = a.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16
+                return bits.view(np.float32).astype(np.float64)
+            return a.numpy().astype(np.float64)
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(x, dt, A, B, C, D, z=None, h0=None):
+    """Real-state prefill. x, dt, z: [b, L, Dn]; B, C: [b, L, N]; A: [Dn, N]; D: [Dn];
+    h0: [b, Dn, N] or None. Returns (y [b, L, Dn], h_final [b, Dn, N]) in float64."""
+    x, dt, A, B, C, D, z, h0 = map(to_f64, (x, dt, A, B, C, D, z, h0))
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    _check(dt, (b, L, Dn), "dt"); _check(B, (b, L, N), "B"); _check(C, (b, L, N), "C")
+    _check(A, (Dn, N), "A"); _check(D, (Dn,), "D")
+    if z is not None: _check(z, (b, L, Dn), "z")
+    if h0 is not None: _check(h0, (b, Dn, N), "h0")
+    y = np.empty((b, L, Dn)); hf = np.empty((b, Dn, N))
+    rc = _load().oracle_scan_f64(b, L, Dn, N, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                                 _p(z), _p(h0), _p(y), _p(hf))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_f64 failed")
+    return y, hf
+
+
+def scan_complex(x, dt, A, B, C, D, z=None, h0=None):
+    """Complex-state prefill. A: [Dn, N, 2] (re, im); B, C: [b, L, N, 2];
+    h0: [b, Dn, N, 2]. Returns (y [b, L, Dn], h_final [b, Dn, N, 2])."""
+    x, dt, A, B, C, D, z, h0 = map(to_f64, (x, dt, A, B, C, D, z, h0))
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    _check(dt, (b, L, Dn), "dt"); _check(B, (b, L, N, 2), "B"); _check(C, (b, L, N, 2), "C")
+    _check(A, (Dn, N, 2), "A"); _check(D, (Dn,), "D")
+    if z is not None: _check(z, (b, L, Dn), "z")
+    if h0 is not None: _check(h0, (b, Dn, N, 2), "h0")
+    y = np.empty((b, L, Dn)); hf = np.empty((b, Dn, N, 2))
+    rc = _load().oracle_scan_c128(b, L, Dn, N, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                                  _p(z), _p(h0), _p(y), _p(hf))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_c128 failed")
+    return y, hf
+
+
+def step(h, x, dt, A, B, C, D, z=None):
+    """One decode token. h: [Ln, S, Dn, N]; x, dt, z: [Ln, S, Dn]; B, C: [Ln, S, N];
+    A: [Ln, Dn, N]; D: [Ln, Dn]. Returns (y [Ln, S, Dn], h_new) without touching h."""
+    h = to_f64(h).copy()
+    x, dt, A, B, C, D, z = map(to_f64, (x, dt, A, B, C, D, z))
+    Ln, S, Dn = x.shape
+    N = h.shape[-1]
+    _check(h, (Ln, S, Dn, N), "h"); _check(B, (Ln, S, N), "B"); _check(C, (Ln, S, N), "C")
+    _check(A, (Ln, Dn, N), "A"); _check(D, (Ln, Dn), "D"); _check(dt, (Ln, S, Dn), "dt")
+    if z is not None: _check(z, (Ln, S, Dn), "z")
+    y = np.empty((Ln, S, Dn))
+    rc = _load().oracle_step_f64(Ln, S, Dn, N, _p(h), _p(x), _p(dt), _p(A), _p(B), _p(C),
+                                 _p(D), _p(z), _p(y))
+    if rc != 0:
+        raise RuntimeError("oracle_step_f64 failed")
+    return y, h
+
+
+def step_complex(h, x, dt, A, B, C, D, z=None):
+    """Complex decode token. h: [Ln, S, Dn, N, 2]; A: [Ln, Dn, N, 2]; B, C: [Ln, S, N, 2]."""
+    h = to_f64(h).copy()
+    x, dt, A, B, C, D, z = map(to_f64, (x, dt, A, B, C, D, z))
+    Ln, S, Dn = x.shape
+    N = h.shape[-2]
+    _check(h, (Ln, S, Dn, N, 2), "h"); _check(B, (Ln, S, N, 2), "B")
+    _check(C, (Ln, S, N, 2), "C"); _check(A, (Ln, Dn, N, 2), "A"); _check(D, (Ln, Dn), "D")
+    y = np.empty((Ln, S, Dn))
+    rc = _load().oracle_step_c128(Ln, S, Dn, N, _p(h), _p(x), _p(dt), _p(A), _p(B), _p(C),
+                                  _p(D), _p(z), _p(y))
+    if rc != 0:
+        raise RuntimeError("oracle_step_c128 failed")
+    return y, h
+
+
+def state_bytes(n_layers: int, channels: int, d_state: int, bytes_per_value: int) -> int:
+    """Size of a fixed-size SSM state in bytes (independent of sequence length)."""
+    return int(_load().oracle_state_bytes(n_layers, channels, d_state, bytes_per_value))
+
+
+def scan_threaded(x, dt, A, B, C, D, z=None, h0=None, threads: int = 1, complex_state=False):
+    """The same oracle loop run on disjoint channel subsets from `threads` threads.
+
+    Channels are independent, so this computes exactly what ``scan`` computes; it is
+    how the benchmark times the oracle on several host cores (ctypes releases the GIL).
+    """
+    x, dt, A, B, C, D, z, h0 = map(to_f64, (x, dt, A, B, C, D, z, h0))
+    Dn = x.shape[2]
+    parts = [p for p in np.array_split(np.arange(Dn), max(1, threads)) if len(p)]
+    fn = scan_complex if complex_state else scan
+    results = [None] * len(parts)
+
+    def work(k, idx):
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, idx])
+        results[k] = fn(sub(x), sub(dt), A[idx], B, C, D[idx], sub(z),
+                        None if h0 is None else np.ascontiguousarray(h0[:, idx]))
+
+    ts = [threading.Thread(target=work, args=(k, idx)) for k, idx in enumerate(parts)]
+    for t in ts: t.start()
+    for t in ts: t.join()
+    y = np.concatenate([r[0] for r in results], axis=2)
+    hf = np.concatenate([r[1] for r in results], axis=1)
+    return y, hf
+
+
+def _check(a, shape, name):
+    if tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(a.shape)}")

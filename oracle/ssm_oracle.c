@@ -1,0 +1,222 @@
+/*
+ * ssm_oracle.c -- plain, slow, sequential fp64 reference ("oracle") for the
+ * selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+ * baseline leg load this library. The HIP product path never calls it, and the
+ * two share no code, headers or tables.
+ *
+ * What is computed
+ * ----------------
+ * The state-space recurrence of "Jamba — SSM-Transformer Híbrido"
+ * (ai-engineering.academy), section "Um SSM em uma página", also given in the
+ * zh lesson page "马巴 混合型SSM变压器" (Phase 10 · 21), section "一页的SSM":
+ *
+ *     h_t = Abar_t h_{t-1} + Bbar_t x_t ,        y_t = C_t h_t
+ *
+ * Both pages state that Mamba makes A, B, C data-dependent (the "selective"
+ * part) and that y_t needs only h_{t-1} and x_t (constant-size state).
+ *
+ * The discretisation, the skip term D and the gate follow the MambaBlock of
+ * "【大模型】- Jamba 混合 SSM-Transformer", section 4.1 "Mamba 层":
+ *     Abar = exp(dt * A)   (A diagonal: one value per channel d and state n)
+ *     Bbar = dt * B        (B and C shared by all channels of a (batch, step))
+ *     y    = (sum_n C[n] h[n] + D[d] x) * silu(z),  silu(z) = z / (1 + exp(-z)).
+ * The page's own loop sums (h * D) and never forms C or the D*x skip; the
+ * reading taken here is the recurrence's y_t = C_t h_t plus the D skip, and
+ * the whole is gated, as the MambaBlock gates the scan's output.
+ *
+ * The complex-state variant is the data-dependent rotation of the Mamba-3
+ * item "Atualização de estado com valores complexos" on the same pt page:
+ * A = (-a + i*theta) per (d, n), Abar = exp(dt * A) = exp(-dt a)(cos(dt theta)
+ * + i sin(dt theta)), h complex, y = Re(sum_n C[n] h[n]) + D x (C not
+ * conjugated), then the optional gate.
+ *
+ * Order of operations (fixed, so that special cases hold bit for bit):
+ *     dA = exp(dt * A[d][n]);  dB = dt * B[n];
+ *     h[n] = (dA * h[n]) + (dB * x);  acc = acc + C[n] * h[n]   (n ascending)
+ *     y = acc + D[d] * x;  if gated: y = y * (z / (1 + exp(-z)))
+ * Compiled with -ffp-contract=off: no fused multiply-adds.
+ *
+ * Layouts (row-major, contiguous, channel index fastest):
+ *     x, dt, z, y : [batch][L][Dn]          B, C : [batch][L][N]   (complex: [..][N][2])
+ *     A           : [Dn][N]   (complex: [Dn][N][2] = (re, im))     Dv : [Dn]
+ *     h0, h_final : [batch][Dn][N]           (complex: [batch][Dn][N][2])
+ * z and h0 may be NULL: no gate, zero initial state.
+ * Decode (one token): h [n_layers][n_seq][Dn][N] updated in place;
+ *     x, dt, z, y : [n_layers][n_seq][Dn];  B, C : [n_layers][n_seq][N];
+ *     A : [n_layers][Dn][N];  Dv : [n_layers][Dn].
+ * Return value: 0 on success, -1 on invalid sizes or allocation failure.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Prefill over a whole sequence, real diagonal state. */
+int oracle_scan_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
+                    const double *x, const double *dt, const double *A,
+                    const double *B, const double *C, const double *Dv,
+                    const double *z, const double *h0,
+                    double *y, double *h_final)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || N <= 0) return -1;
+    double *h = (double *)malloc((size_t)N * sizeof(double));
+    if (!h) return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < Dn; ++d) {
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t i = (b * L + t) * Dn + d;   /* (b, t, d) */
+                const int64_t s = (b * L + t) * N;        /* (b, t, 0) */
+                const double xv = x[i], dv = dt[i];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double dA = exp(dv * A[d * N + n]);
+                    const double dB = dv * B[s + n];
+                    h[n] = dA * h[n] + dB * xv;
+                    acc = acc + C[s + n] * h[n];
+                }
+                double yv = acc + Dv[d] * xv;
+                if (z) yv = yv * silu(z[i]);
+                y[i] = yv;
+            }
+            if (h_final)
+                for (int64_t n = 0; n < N; ++n) h_final[(b * Dn + d) * N + n] = h[n];
+        }
+    }
+    free(h);
+    return 0;
+}
+
+/* One decode token for every (layer, sequence, channel); h updated in place. */
+int oracle_step_f64(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N,
+                    double *h, const double *x, const double *dt, const double *A,
+                    const double *B, const double *C, const double *Dv,
+                    const double *z, double *y)
+{
+    if (n_layers < 0 || n_seq < 0 || Dn < 0 || N <= 0) return -1;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        for (int64_t q = 0; q < n_seq; ++q) {
+            const int64_t s = (l * n_seq + q) * N;            /* (l, q, 0) of B, C */
+            for (int64_t d = 0; d < Dn; ++d) {
+                const int64_t i = (l * n_seq + q) * Dn + d;   /* (l, q, d) */
+                double *hs = h + i * N;
+                const double *Ad = A + (l * Dn + d) * N;
+                const double xv = x[i], dv = dt[i];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double dA = exp(dv * Ad[n]);
+                    const double dB = dv * B[s + n];
+                    hs[n] = dA * hs[n] + dB * xv;
+                    acc = acc + C[s + n] * hs[n];
+                }
+                double yv = acc + Dv[l * Dn + d] * xv;
+                if (z) yv = yv * silu(z[i]);
+                y[i] = yv;
+            }
+        }
+    }
+    return 0;
+}
+
+/* Prefill with a complex diagonal state, written with explicit re/im parts. */
+int oracle_scan_c128(int64_t batch, int64_t L, int64_t Dn, int64_t N,
+                     const double *x, const double *dt, const double *A,
+                     const double *B, const double *C, const double *Dv,
+                     const double *z, const double *h0,
+                     double *y, double *h_final)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || N <= 0) return -1;
+    double *hr = (double *)malloc((size_t)N * sizeof(double));
+    double *hi = (double *)malloc((size_t)N * sizeof(double));
+    if (!hr || !hi) { free(hr); free(hi); return -1; }
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < Dn; ++d) {
+            for (int64_t n = 0; n < N; ++n) {
+                hr[n] = h0 ? h0[((b * Dn + d) * N + n) * 2 + 0] : 0.0;
+                hi[n] = h0 ? h0[((b * Dn + d) * N + n) * 2 + 1] : 0.0;
+            }
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t i = (b * L + t) * Dn + d;
+                const int64_t s = (b * L + t) * N;
+                const double xv = x[i], dv = dt[i];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double are = A[(d * N + n) * 2 + 0];
+                    const double aim = A[(d * N + n) * 2 + 1];
+                    const double mag = exp(dv * are);
+                    const double dAr = mag * cos(dv * aim);
+                    const double dAi = mag * sin(dv * aim);
+                    const double dBr = dv * B[(s + n) * 2 + 0];
+                    const double dBi = dv * B[(s + n) * 2 + 1];
+                    const double nr = (dAr * hr[n] - dAi * hi[n]) + dBr * xv;
+                    const double ni = (dAr * hi[n] + dAi * hr[n]) + dBi * xv;
+                    hr[n] = nr;
+                    hi[n] = ni;
+                    acc = acc + (C[(s + n) * 2 + 0] * hr[n] - C[(s + n) * 2 + 1] * hi[n]);
+                }
+                double yv = acc + Dv[d] * xv;
+                if (z) yv = yv * silu(z[i]);
+                y[i] = yv;
+            }
+            if (h_final)
+                for (int64_t n = 0; n < N; ++n) {
+                    h_final[((b * Dn + d) * N + n) * 2 + 0] = hr[n];
+                    h_final[((b * Dn + d) * N + n) * 2 + 1] = hi[n];
+                }
+        }
+    }
+    free(hr);
+    free(hi);
+    return 0;
+}
+
+/* One decode token with a complex state; h [n_layers][n_seq][Dn][N][2] in place. */
+int oracle_step_c128(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N,
+                     double *h, const double *x, const double *dt, const double *A,
+                     const double *B, const double *C, const double *Dv,
+                     const double *z, double *y)
+{
+    if (n_layers < 0 || n_seq < 0 || Dn < 0 || N <= 0) return -1;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        for (int64_t q = 0; q < n_seq; ++q) {
+            const int64_t s = (l * n_seq + q) * N;
+            for (int64_t d = 0; d < Dn; ++d) {
+                const int64_t i = (l * n_seq + q) * Dn + d;
+                double *hs = h + i * N * 2;
+                const double *Ad = A + (l * Dn + d) * N * 2;
+                const double xv = x[i], dv = dt[i];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double mag = exp(dv * Ad[2 * n + 0]);
+                    const double dAr = mag * cos(dv * Ad[2 * n + 1]);
+                    const double dAi = mag * sin(dv * Ad[2 * n + 1]);
+                    const double dBr = dv * B[(s + n) * 2 + 0];
+                    const double dBi = dv * B[(s + n) * 2 + 1];
+                    const double nr = (dAr * hs[2 * n] - dAi * hs[2 * n + 1]) + dBr * xv;
+                    const double ni = (dAr * hs[2 * n + 1] + dAi * hs[2 * n]) + dBi * xv;
+                    hs[2 * n] = nr;
+                    hs[2 * n + 1] = ni;
+                    acc = acc + (C[(s + n) * 2 + 0] * nr - C[(s + n) * 2 + 1] * ni);
+                }
+                double yv = acc + Dv[l * Dn + d] * xv;
+                if (z) yv = yv * silu(z[i]);
+                y[i] = yv;
+            }
+        }
+    }
+    return 0;
+}
+
+/* Bytes of a fixed-size SSM state: layers x channels x state size x bytes per
+ * value. It does not depend on the sequence length (the memory-budget section,
+ * "O orçamento de memória", of the pt page). */
+int64_t oracle_state_bytes(int64_t n_layers, int64_t channels, int64_t d_state,
+                           int64_t bytes_per_value)
+{
+    return n_layers * channels * d_state * bytes_per_value;
+}

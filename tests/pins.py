@@ -1,0 +1,328 @@
+"""Pins for the fp64 oracle: checks against definitions that do not share its code.
+
+Each ``pin_*`` function takes the oracle module (or a stand-in with the same
+functions) and raises AssertionError when the oracle disagrees with something the
+pages or plain mathematics fix:
+
+  brute force   the state written out as an explicit selective convolution,
+                y_t = sum_{s<=t} sum_n C_t[n] exp(A_n (S_t - S_s)) dt_s B_s[n] x_s
+                      + sum_n C_t[n] exp(A_n S_t) h0[n] + D x_t, then the gate,
+                with S_t the running sum of dt. It uses exp of a sum of dt where
+                the recurrence multiplies exps, so the two are independent.
+  convolution   the time-invariant case (constant dt, B, C) must equal a causal
+                convolution with kernel K_k = sum_n C_n exp(k dt A_n) dt B_n; the
+                pages tie the structured SSM of S4 to a long convolution
+                ("Jamba — SSM-Transformer Híbrido", section "Um SSM em uma página").
+  closed forms  a geometric series (one state, constant inputs); dt = 0 keeps the
+                state fixed; the complex state with no decay is a pure rotation
+                e^{i theta t} (the data-dependent rotary embedding of the Mamba-3
+                item on complex-valued state updates, same page).
+  invariants    linearity in x; splitting a sequence and resuming from h_final
+                (the state is all that carries over); L decode steps equal one
+                prefill; a NaN stays inside its channel; the complex variant with
+                theta = 0 equals the real one.
+  printed value the fixed-size state arithmetic of the memory-budget section
+                (tests/golden/state_memory.json).
+
+The pins draw their own inputs with numpy; they test only the oracle.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def tiny_real(seed, b=2, L=24, Dn=3, N=4, gated=True, with_h0=True):
+    r = np.random.default_rng(seed)
+    x = r.normal(0, 1, (b, L, Dn))
+    z = r.normal(0, 1, (b, L, Dn)) if gated else None
+    dt = np.log1p(np.exp(r.normal(-1, 0.5, (b, L, Dn))))
+    A = -np.exp(r.normal(0, 0.5, (Dn, N)))
+    B = r.normal(0, 1, (b, L, N))
+    C = r.normal(0, 1, (b, L, N))
+    D = r.normal(1, 0.1, Dn)
+    h0 = r.normal(0, 1, (b, Dn, N)) if with_h0 else None
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def tiny_complex(seed, b=2, L=20, Dn=3, N=4, gated=False, with_h0=True):
+    r = np.random.default_rng(seed)
+    x = r.normal(0, 1, (b, L, Dn))
+    z = r.normal(0, 1, (b, L, Dn)) if gated else None
+    dt = np.log1p(np.exp(r.normal(-1, 0.5, (b, L, Dn))))
+    A = np.stack([-np.exp(r.normal(0, 0.5, (Dn, N))), r.uniform(-np.pi, np.pi, (Dn, N))], -1)
+    B = r.normal(0, 1, (b, L, N, 2))
+    C = r.normal(0, 1, (b, L, N, 2))
+    D = r.normal(1, 0.1, Dn)
+    h0 = r.normal(0, 1, (b, Dn, N, 2)) if with_h0 else None
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def brute_real(x, dt, A, B, C, D, z=None, h0=None):
+    """O(L^2 N) explicit selective convolution (see the module docstring)."""
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    S = np.cumsum(dt, axis=1)
+    y = np.zeros((b, L, Dn))
+    hf = np.zeros((b, Dn, N))
+    for bi in range(b):
+        for d in range(Dn):
+            for t in range(L):
+                w = np.exp(np.outer(S[bi, t, d] - S[bi, :t + 1, d], A[d]))          # [t+1, N]
+                h_t = (w * (dt[bi, :t + 1, d] * x[bi, :t + 1, d])[:, None] * B[bi, :t + 1]).sum(0)
+                if h0 is not None:
+                    h_t = h_t + np.exp(A[d] * S[bi, t, d]) * h0[bi, d]
+                yv = float(C[bi, t] @ h_t) + D[d] * x[bi, t, d]
+                if z is not None:
+                    yv *= silu(z[bi, t, d])
+                y[bi, t, d] = yv
+                if t == L - 1:
+                    hf[bi, d] = h_t
+    return y, hf
+
+
+def brute_complex(x, dt, A, B, C, D, z=None, h0=None):
+    """Complex-state explicit convolution in complex128 arithmetic."""
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    Ac = A[..., 0] + 1j * A[..., 1]
+    Bc = B[..., 0] + 1j * B[..., 1]
+    Cc = C[..., 0] + 1j * C[..., 1]
+    H0 = None if h0 is None else h0[..., 0] + 1j * h0[..., 1]
+    S = np.cumsum(dt, axis=1)
+    y = np.zeros((b, L, Dn))
+    hf = np.zeros((b, Dn, N, 2))
+    for bi in range(b):
+        for d in range(Dn):
+            for t in range(L):
+                w = np.exp(np.outer(S[bi, t, d] - S[bi, :t + 1, d], Ac[d]))
+                h_t = (w * (dt[bi, :t + 1, d] * x[bi, :t + 1, d])[:, None] * Bc[bi, :t + 1]).sum(0)
+                if H0 is not None:
+                    h_t = h_t + np.exp(Ac[d] * S[bi, t, d]) * H0[bi, d]
+                yv = float(np.real(Cc[bi, t] @ h_t)) + D[d] * x[bi, t, d]
+                if z is not None:
+                    yv *= silu(z[bi, t, d])
+                y[bi, t, d] = yv
+                if t == L - 1:
+                    hf[bi, d, :, 0] = h_t.real
+                    hf[bi, d, :, 1] = h_t.imag
+    return y, hf
+
+
+def _rel(a, b):
+    a = np.asarray(a); b = np.asarray(b)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def _bitwise(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint64), np.asarray(b).view(np.uint64))
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_brute_force(O, tol=1e-12):
+    for seed, kw in [(1, {}), (2, dict(gated=False, with_h0=False)), (3, dict(b=1, L=64, Dn=2, N=4))]:
+        inp = tiny_real(seed, **kw)
+        y, hf = O.scan(**inp)
+        yb, hb = brute_real(**inp)
+        assert _rel(y, yb) <= tol, f"brute force y mismatch {_rel(y, yb)} (seed {seed})"
+        assert _rel(hf, hb) <= tol, f"brute force h_final mismatch {_rel(hf, hb)} (seed {seed})"
+
+
+def pin_convolution(O, tol=1e-12):
+    r = np.random.default_rng(5)
+    L, Dn, N = 48, 3, 4
+    dtc = 0.37
+    Bc, Cc = r.normal(0, 1, N), r.normal(0, 1, N)
+    A = -np.exp(r.normal(0, 0.5, (Dn, N)))
+    D = r.normal(1, 0.1, Dn)
+    x = r.normal(0, 1, (1, L, Dn))
+    y, _ = O.scan(x, np.full((1, L, Dn), dtc), A, np.tile(Bc, (1, L, 1)), np.tile(Cc, (1, L, 1)), D)
+    for d in range(Dn):
+        k = np.arange(L)[:, None]
+        K = (Cc * np.exp(k * dtc * A[d]) * dtc * Bc).sum(1)
+        ref = np.convolve(x[0, :, d], K)[:L] + D[d] * x[0, :, d]
+        assert _rel(y[0, :, d], ref) <= tol, f"time-invariant case is not the convolution (d={d})"
+
+
+def pin_geometric_series(O, tol=1e-12):
+    L, a, dtc, b_, c_, d_, xv = 40, -0.8, 0.25, 1.3, -0.7, 0.9, 0.6
+    y, hf = O.scan(np.full((1, L, 1), xv), np.full((1, L, 1), dtc), np.array([[a]]),
+                   np.full((1, L, 1), b_), np.full((1, L, 1), c_), np.array([d_]))
+    rr = np.exp(dtc * a)
+    t = np.arange(L)
+    ref = c_ * dtc * b_ * xv * (1 - rr ** (t + 1)) / (1 - rr) + d_ * xv
+    assert _rel(y[0, :, 0], ref) <= tol, "geometric-series closed form"
+    assert _rel(hf[0, 0, 0], dtc * b_ * xv * (1 - rr ** L) / (1 - rr)) <= tol, "closed-form final state"
+
+
+def pin_dt_zero(O):
+    inp = tiny_real(7, with_h0=False)
+    inp["dt"] = np.zeros_like(inp["dt"])
+    y, hf = O.scan(**inp)
+    assert np.all(hf == 0.0), "dt = 0 must keep a zero state at exactly zero"
+    ref = inp["D"] * inp["x"] * silu(inp["z"])
+    assert _rel(y, ref) <= 1e-15, "dt = 0: y must be D*x*silu(z)"
+    inp = tiny_real(8)
+    inp["dt"] = np.zeros_like(inp["dt"])
+    y, hf = O.scan(**inp)
+    assert _bitwise(hf, inp["h0"]), "dt = 0 must keep h0 unchanged"
+    ref = (np.einsum("bln,bdn->bld", inp["C"], inp["h0"]) + inp["D"] * inp["x"]) * silu(inp["z"])
+    assert _rel(y, ref) <= 1e-13, "dt = 0: y must be (C.h0 + D*x)*silu(z)"
+
+
+def pin_linearity(O, tol=1e-12):
+    i1, i2 = tiny_real(11, gated=False, with_h0=False), tiny_real(12, gated=False, with_h0=False)
+    al, be = 0.7, -1.9
+    base = {k: i1[k] for k in ("dt", "A", "B", "C", "D")}
+    y1, h1 = O.scan(i1["x"], **base)
+    y2, h2 = O.scan(i2["x"], **base)
+    y3, h3 = O.scan(al * i1["x"] + be * i2["x"], **base)
+    assert _rel(y3, al * y1 + be * y2) <= tol, "linearity in x (y)"
+    assert _rel(h3, al * h1 + be * h2) <= tol, "linearity in x (h)"
+
+
+def _slice_t(inp, t0, t1):
+    out = dict(inp)
+    for k in ("x", "dt", "z", "B", "C"):
+        if out.get(k) is not None:
+            out[k] = np.ascontiguousarray(inp[k][:, t0:t1])
+    return out
+
+
+def pin_split_resume(O, complex_state=False):
+    inp = tiny_complex(13) if complex_state else tiny_real(13, L=30)
+    fn = O.scan_complex if complex_state else O.scan
+    L = inp["x"].shape[1]
+    y, hf = fn(**inp)
+    for L1 in (1, 11, L - 1):
+        a = _slice_t(inp, 0, L1)
+        ya, ha = fn(**a)
+        bpart = _slice_t(inp, L1, L)
+        bpart["h0"] = ha
+        yb, hb = fn(**bpart)
+        assert _bitwise(np.concatenate([ya, yb], 1), y), f"split at {L1}: y differs"
+        assert _bitwise(hb, hf), f"split at {L1}: h_final differs"
+
+
+def pin_step_equals_scan(O, complex_state=False):
+    inp = tiny_complex(17) if complex_state else tiny_real(17, L=16)
+    if complex_state:
+        inp["z"] = np.random.default_rng(3).normal(0, 1, inp["x"].shape)
+    fn, st = (O.scan_complex, O.step_complex) if complex_state else (O.scan, O.step)
+    y, hf = fn(**inp)
+    h = inp["h0"][None].copy()
+    b, L, Dn = inp["x"].shape
+    for t in range(L):
+        yt, h = st(h, inp["x"][None, :, t], inp["dt"][None, :, t], inp["A"][None],
+                   inp["B"][None, :, t], inp["C"][None, :, t], inp["D"][None],
+                   None if inp["z"] is None else inp["z"][None, :, t])
+        assert _bitwise(yt[0], y[:, t]), f"decode step {t} differs from prefill"
+    assert _bitwise(h[0], hf), "state after L decode steps differs from prefill h_final"
+
+
+def pin_layers_are_independent(O, complex_state=False):
+    """A step over several layers equals one single-layer step per layer, each with
+    that layer's own A and D (single-layer steps are pinned to prefill above)."""
+    r = np.random.default_rng(37)
+    Ln, S, Dn, N = 3, 2, 4, 4
+    ext = (2,) if complex_state else ()
+    st = O.step_complex if complex_state else O.step
+    h = r.normal(0, 1, (Ln, S, Dn, N) + ext)
+    x, z = r.normal(0, 1, (Ln, S, Dn)), r.normal(0, 1, (Ln, S, Dn))
+    dt = np.log1p(np.exp(r.normal(-1, 0.5, (Ln, S, Dn))))
+    if complex_state:
+        A = np.stack([-np.exp(r.normal(0, 0.5, (Ln, Dn, N))), r.uniform(-3, 3, (Ln, Dn, N))], -1)
+    else:
+        A = -np.exp(r.normal(0, 0.5, (Ln, Dn, N)))
+    B, C = r.normal(0, 1, (Ln, S, N) + ext), r.normal(0, 1, (Ln, S, N) + ext)
+    D = r.normal(1, 0.1, (Ln, Dn))
+    y, h2 = st(h, x, dt, A, B, C, D, z)
+    for l in range(Ln):
+        sl = slice(l, l + 1)
+        yl, hl = st(h[sl], x[sl], dt[sl], A[sl], B[sl], C[sl], D[sl], z[sl])
+        assert _bitwise(yl, y[sl]) and _bitwise(hl, h2[sl]), f"layer {l} is not independent"
+
+
+def pin_isolation(O):
+    inp = tiny_real(19)
+    y, hf = O.scan(**inp)
+    bad = dict(inp)
+    bad["x"] = inp["x"].copy()
+    bad["x"][0, 5, 1] = np.nan
+    y2, h2 = O.scan(**bad)
+    other = [d for d in range(inp["x"].shape[2]) if d != 1]
+    assert _bitwise(y2[:, :, other], y[:, :, other]), "NaN leaked into other channels (y)"
+    assert _bitwise(y2[1], y[1]), "NaN leaked into the other batch row"
+    assert _bitwise(h2[:, other], hf[:, other]), "NaN leaked into other channels (h)"
+    assert np.all(np.isnan(y2[0, 5:, 1])) and np.all(np.isfinite(y2[0, :5, 1])), "NaN not confined in time"
+
+
+def pin_state_bytes(O):
+    with open(os.path.join(GOLDEN, "state_memory.json")) as f:
+        g = json.load(f)
+    nbytes = O.state_bytes(g["layers"], g["channels"], g["state_size"], g["bytes_per_value"])
+    assert nbytes == 28 * 4096 * 16 * 2 == 3670016
+    assert abs(nbytes / 1e6 - g["printed_total_MB"]) <= g["printed_rounding_MB"], "3.7 MB figure"
+    # Independent of the sequence length: the oracle's final state has the same shape.
+    shapes = set()
+    for L in (1, 8, 64):
+        _, hf = O.scan(**tiny_real(23, L=L))
+        shapes.add(hf.shape)
+    assert len(shapes) == 1, "h_final shape depends on L"
+
+
+def pin_complex_reduces_to_real(O):
+    inp = tiny_real(29, L=20)
+    y, hf = O.scan(**inp)
+    c = dict(inp)
+    c["A"] = np.stack([inp["A"], np.zeros_like(inp["A"])], -1)
+    c["B"] = np.stack([inp["B"], np.zeros_like(inp["B"])], -1)
+    c["C"] = np.stack([inp["C"], np.zeros_like(inp["C"])], -1)
+    c["h0"] = np.stack([inp["h0"], np.zeros_like(inp["h0"])], -1)
+    yc, hc = O.scan_complex(**c)
+    assert _bitwise(yc, y), "theta = 0 complex scan differs from the real scan (y)"
+    assert _bitwise(hc[..., 0], hf) and np.all(hc[..., 1] == 0.0), "theta = 0: state differs"
+
+
+def pin_rotation(O, tol=1e-12):
+    L, N = 64, 4
+    theta = np.array([0.3, -1.1, 2.5, np.pi / 7])
+    A = np.stack([np.zeros((1, N)), theta[None]], -1)
+    x = np.zeros((1, L, 1)); x[0, 0, 0] = 1.0
+    B = np.zeros((1, L, N, 2)); B[..., 0] = 1.0
+    for n in range(N):
+        C = np.zeros((1, L, N, 2)); C[:, :, n, 0] = 1.0
+        y, _ = O.scan_complex(x, np.ones((1, L, 1)), A, B, C, np.zeros(1))
+        assert _rel(y[0, :, 0], np.cos(theta[n] * np.arange(L))) <= tol, f"rotation, state {n}"
+        Cs = np.zeros((1, L, N, 2)); Cs[:, :, n, 1] = -1.0   # Re(-i h) = Im h = sin
+        ys, _ = O.scan_complex(x, np.ones((1, L, 1)), A, B, Cs, np.zeros(1))
+        assert _rel(ys[0, :, 0], np.sin(theta[n] * np.arange(L))) <= tol, f"rotation sense, state {n}"
+
+
+def pin_brute_force_complex(O, tol=1e-12):
+    for seed, kw in [(31, {}), (32, dict(gated=True, with_h0=False))]:
+        inp = tiny_complex(seed, **kw)
+        y, hf = O.scan_complex(**inp)
+        yb, hb = brute_complex(**inp)
+        assert _rel(y, yb) <= tol, f"complex brute force y mismatch {_rel(y, yb)}"
+        assert _rel(hf, hb) <= tol, f"complex brute force h_final mismatch {_rel(hf, hb)}"
+
+
+ALL_PINS = [
+    pin_brute_force, pin_convolution, pin_geometric_series, pin_dt_zero, pin_linearity,
+    pin_split_resume, pin_step_equals_scan, pin_isolation, pin_state_bytes,
+    pin_complex_reduces_to_real, pin_rotation, pin_brute_force_complex,
+    lambda O: pin_split_resume(O, complex_state=True),
+    lambda O: pin_step_equals_scan(O, complex_state=True),
+    pin_layers_are_independent,
+    lambda O: pin_layers_are_independent(O, complex_state=True),
+]

@@ -1,0 +1,78 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin (CPU only).
+
+Every case below edits one line of ``oracle/ssm_oracle.c`` in a temporary copy (a
+dropped term, a wrong sign, a wrong index, a transposed operand, a wrong order),
+compiles it with the oracle's own flags, swaps it in for the real library and runs
+the pins. A mutant that passes every pin would mean the pins cannot tell that
+mistake from the correct loop.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.c")
+
+MUTANTS = {
+    "sign_of_input_term": ("h[n] = dA * h[n] + dB * xv;", "h[n] = dA * h[n] - dB * xv;"),
+    "sign_of_A": ("const double dA = exp(dv * A[d * N + n]);", "const double dA = exp(-dv * A[d * N + n]);"),
+    "dropped_dt_in_B": ("A[d * N + n]);\n                    const double dB = dv * B[s + n];",
+                        "A[d * N + n]);\n                    const double dB = B[s + n];"),
+    "B_for_C": ("acc = acc + C[s + n] * h[n];", "acc = acc + B[s + n] * h[n];"),
+    "dropped_skip": ("double yv = acc + Dv[d] * xv;\n                if (z) yv = yv * silu(z[i]);\n                y[i] = yv;\n            }\n            if (h_final)\n                for (int64_t n = 0; n < N; ++n) h_final",
+                     "double yv = acc;\n                if (z) yv = yv * silu(z[i]);\n                y[i] = yv;\n            }\n            if (h_final)\n                for (int64_t n = 0; n < N; ++n) h_final"),
+    "gate_without_sigmoid": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
+                             "static double silu(double z) { return z; }"),
+    "transposed_A_index": ("const double dA = exp(dv * A[d * N + n]);", "const double dA = exp(dv * A[n * Dn + d]);"),
+    "output_from_old_state": ("h[n] = dA * h[n] + dB * xv;\n                    acc = acc + C[s + n] * h[n];",
+                              "acc = acc + C[s + n] * h[n];\n                    h[n] = dA * h[n] + dB * xv;"),
+    "h0_ignored": ("h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    "decode_sign": ("hs[n] = dA * hs[n] + dB * xv;", "hs[n] = dA * hs[n] - dB * xv;"),
+    "complex_decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N * 2;", "const double *Ad = A + d * N * 2;"),
+    "decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N;", "const double *Ad = A + d * N;"),
+    "complex_rotation_sense": ("const double ni = (dAr * hi[n] + dAi * hr[n]) + dBi * xv;",
+                               "const double ni = (dAr * hi[n] - dAi * hr[n]) + dBi * xv;"),
+    "complex_conjugated_C": ("acc = acc + (C[(s + n) * 2 + 0] * hr[n] - C[(s + n) * 2 + 1] * hi[n]);",
+                             "acc = acc + (C[(s + n) * 2 + 0] * hr[n] + C[(s + n) * 2 + 1] * hi[n]);"),
+    "complex_sin_cos_swapped": ("const double dAr = mag * cos(dv * aim);\n                    const double dAi = mag * sin(dv * aim);",
+                                "const double dAr = mag * sin(dv * aim);\n                    const double dAi = mag * cos(dv * aim);"),
+    "complex_decay_dropped": ("const double mag = exp(dv * are);", "const double mag = 1.0;"),
+    "complex_decode_sign": ("const double nr = (dAr * hs[2 * n] - dAi * hs[2 * n + 1]) + dBr * xv;",
+                            "const double nr = (dAr * hs[2 * n] + dAi * hs[2 * n + 1]) + dBr * xv;"),
+    "state_bytes_factor": ("return n_layers * channels * d_state * bytes_per_value;",
+                           "return n_layers * channels * d_state * 4;"),
+}
+
+
+def _run_all_pins():
+    failures = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(oracle)
+        except AssertionError as e:
+            failures.append(str(e))
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", str(so), str(path), "-lm"], check=True)
+    real = oracle._load()
+    lib = ctypes.CDLL(str(so))
+    for fname in ("oracle_scan_f64", "oracle_scan_c128", "oracle_step_f64", "oracle_step_c128",
+                  "oracle_state_bytes"):
+        f, g = getattr(lib, fname), getattr(real, fname)
+        f.argtypes, f.restype = g.argtypes, g.restype
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failures = _run_all_pins()
+    assert failures, f"mutant {name} passed every pin"
