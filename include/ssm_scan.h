@@ -1,0 +1,169 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan, a selective state-space scan for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * The linear state-space recurrence of "Jamba — SSM-Transformer Híbrido"
+ * (ai-engineering.academy), section "Um SSM em uma página":
+ *     h_t = Abar_t h_{t-1} + Bbar_t x_t,      y_t = C_t h_t,
+ * made selective (A, B, C and the step dt depend on the data), with the
+ * discretisation, skip term and gate of the MambaBlock on
+ * "【大模型】- Jamba 混合 SSM-Transformer", section 4.1 "Mamba 层":
+ *     Abar = exp(dt * A)  (A diagonal: one value per channel d and state n)
+ *     Bbar = dt * B       (B and C are shared by all channels of a (batch, step))
+ *     y    = (sum_n C[n] h[n] + D[d] x) * silu(z),    silu(z) = z / (1 + exp(-z)).
+ * The state h is fp32 and its size does not depend on the sequence length
+ * (same page, section "O orçamento de memória"). The complex variants (_c64)
+ * take A = -a + i*theta per (d, n), so Abar is a decay times a data-dependent
+ * rotation (Mamba-3 item on complex-valued state updates, same pt page), and
+ * output y = Re(sum_n C[n] h[n]) + D x, then the optional gate.
+ * dt is taken after softplus (the MambaBlock applies softplus before its scan).
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ *  - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or retains caller memory. Arrays are contiguous,
+ *    row-major, channel index fastest.
+ *  - io selects the element type of x, dt, z, B, C and y: SSM_F32 (float) or
+ *    SSM_BF16 (bfloat16, stored as 16 bits; y is rounded to nearest even).
+ *    A, D and every state (h, h0, h_final) are always float32.
+ *  - Alignment: A, h, h0 and h_final 16 bytes; B, C and the workspace 256 bytes
+ *    for the workspace and 4 bytes for B, C; x, dt, z, y element-aligned.
+ *  - d_state must be 1, 2, 4, 8 or 16.
+ *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously; the call returns once it is enqueued.
+ *  - Errors: argument errors return a status before anything is enqueued and
+ *    leave every output untouched. A failed launch returns SSM_ERR_HIP. NaN or
+ *    Inf in the data are not errors; they stay inside their channel.
+ *    ssm_last_error() gives a per-thread detail string for the last failure.
+ *  - The library keeps no state besides a per-thread error string. Calls that
+ *    share no output or workspace memory may run concurrently.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = 1,         /* a required pointer is NULL */
+    SSM_ERR_SHAPE = 2,        /* a size is negative, zero where it must not be, or too large */
+    SSM_ERR_DTYPE = 3,        /* io is not SSM_F32 or SSM_BF16 */
+    SSM_ERR_ALIGN = 4,        /* a pointer breaks the alignment rules above */
+    SSM_ERR_UNSUPPORTED = 5,  /* d_state not in {1, 2, 4, 8, 16}, or chunk_len invalid */
+    SSM_ERR_WORKSPACE = 6,    /* workspace missing or smaller than the query says */
+    SSM_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* ------------------------------------------------------------------ prefill
+ * ssm_scan_fwd: the whole recurrence over L steps for every (batch, channel).
+ *   x, dt, z, y : [batch, L, d_inner] of io      B, C : [batch, L, d_state] of io
+ *   A           : [d_inner, d_state] float32     D    : [d_inner] float32
+ *   h0          : [batch, d_inner, d_state] float32, NULL = zero initial state
+ *   h_final     : [batch, d_inner, d_state] float32, NULL = not wanted
+ *   z           : NULL = no gate (y = C.h + D x)
+ * The sequence is split into chunks that run in parallel; each chunk's end state
+ * from zero and its total decay are combined across chunks by an associative
+ * scan, and each chunk is then re-walked from its true incoming state. This is an
+ * exact re-association of the recurrence; results differ from a sequential fp32
+ * loop only by rounding. workspace must hold ssm_scan_fwd_workspace(...) bytes
+ * (0 is possible, then workspace may be NULL). It is scratch: contents on entry
+ * are ignored and on return are unspecified. L == 0 writes h_final = h0 (or
+ * zeros) and nothing else. */
+size_t ssm_scan_fwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
+
+ssm_status ssm_scan_fwd(const void *x, const void *dt, const float *A, const void *B,
+                        const void *C, const float *D, const void *z, const float *h0,
+                        void *y, float *h_final,
+                        int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                        ssm_dtype io, void *workspace, size_t workspace_bytes,
+                        void *hip_stream);
+
+/* Same, with an explicit chunk length (steps per chunk; 0 = the library's own
+ * choice, which is what ssm_scan_fwd uses). chunk_len >= L gives one chunk and
+ * needs no workspace. Results for different chunk lengths agree within rounding. */
+size_t ssm_scan_fwd_workspace_ex(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                 int64_t chunk_len);
+ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, const void *z, const float *h0,
+                           void *y, float *h_final,
+                           int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                           ssm_dtype io, int64_t chunk_len, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
+/* The chunk length ssm_scan_fwd picks for this shape (a pure host function). */
+int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
+
+/* ------------------------------------------------------------------ decode
+ * ssm_step: one token for every (layer, sequence, channel); h -> h' in place.
+ * Each layer's state needs only the previous state and the new token
+ * ("Um SSM em uma página": constant memory, O(1) per token).
+ *   h              : [n_layers, n_seq, d_inner, d_state] float32 (read and written)
+ *   x_t, dt_t, z_t : [n_layers, n_seq, d_inner] of io;  y_t: same shape, written
+ *   B_t, C_t       : [n_layers, n_seq, d_state] of io
+ *   A              : [n_layers, d_inner, d_state] float32;  D: [n_layers, d_inner]
+ *   z_t            : NULL = no gate
+ * Per channel the fp32 operations are, in this order (fma = fused multiply-add,
+ * e2 = the hardware base-2 exponential, G = d_state >= 8 ? d_state / 4 : 1 groups
+ * of K = d_state / G states):
+ *   xf, dtf, zf widened; u = dtf * xf
+ *   for each group g: p_g = 0; for k in group: a = A[n] * log2(e);
+ *       h[n] = fma(e2(dtf * a), h[n], u * Bf[n]); p_g = fma(Cf[n], h[n], p_g)
+ *   acc = pairwise sum of the p_g ((p0 + p1) + (p2 + p3) for G = 4)
+ *   y = fma(D, xf, acc); gated: y = y * (zf * rcp(1 + e2(-zf * log2(e))))
+ * ssm_step_replay performs exactly this sequence with one thread per channel and
+ * plain loops; it exists so that the decode kernel can be checked bit for bit. */
+ssm_status ssm_step(float *h, const void *x_t, const void *dt_t, const float *A,
+                    const void *B_t, const void *C_t, const float *D, const void *z_t,
+                    void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                    int32_t d_state, ssm_dtype io, void *hip_stream);
+
+ssm_status ssm_step_replay(float *h, const void *x_t, const void *dt_t, const float *A,
+                           const void *B_t, const void *C_t, const float *D, const void *z_t,
+                           void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                           int32_t d_state, ssm_dtype io, void *hip_stream);
+
+/* ------------------------------------------------------------------ complex state
+ * As above with a complex diagonal state. Complex values are (re, im) float
+ * pairs, the pair index fastest:
+ *   A        : [d_inner, d_state, 2] float32, A = (-a, theta): Abar = exp(dt * A)
+ *   B, C     : [batch, L, d_state, 2] of io (decode: [n_layers, n_seq, d_state, 2])
+ *   h0, h_final, h : [..., d_state, 2] float32
+ *   y = Re(sum_n C[n] h[n]) + D x (C not conjugated), then the optional gate.
+ * Decode groups: G = d_state >= 2 ? d_state / 2 : 1 lanes of K = d_state / G
+ * complex states, partial sums combined pairwise as in ssm_step. */
+size_t ssm_scan_fwd_c64_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                  int64_t chunk_len);
+ssm_status ssm_scan_fwd_c64(const void *x, const void *dt, const float *A, const void *B,
+                            const void *C, const float *D, const void *z, const float *h0,
+                            void *y, float *h_final,
+                            int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                            ssm_dtype io, int64_t chunk_len, void *workspace,
+                            size_t workspace_bytes, void *hip_stream);
+ssm_status ssm_step_c64(float *h, const void *x_t, const void *dt_t, const float *A,
+                        const void *B_t, const void *C_t, const float *D, const void *z_t,
+                        void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                        int32_t d_state, ssm_dtype io, void *hip_stream);
+ssm_status ssm_step_c64_replay(float *h, const void *x_t, const void *dt_t, const float *A,
+                               const void *B_t, const void *C_t, const float *D,
+                               const void *z_t, void *y_t, int64_t n_layers, int64_t n_seq,
+                               int64_t d_inner, int32_t d_state, ssm_dtype io,
+                               void *hip_stream);
+
+/* ------------------------------------------------------------------ misc */
+const char *ssm_status_str(ssm_status s);   /* static string, never NULL */
+const char *ssm_last_error(void);           /* this thread's last detail, "" if none */
+int32_t ssm_abi_version(void);              /* 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,262 @@
+// api.cpp -- the C ABI of libssmscan: argument checks, chunk planning, dispatch.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call
+// leaves all outputs untouched. Kernels are enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "ssm_internal.h"
+#include "ssm_scan.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ssm_status fail(ssm_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ssm_status ok() {
+    g_err[0] = '\0';
+    return SSM_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_state(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+size_t io_bytes(ssm_dtype io) { return io == SSM_BF16 ? 2 : 4; }
+
+// Waves wanted per launch for the chunk rescan: about four per SIMD on 256 CUs.
+constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kMinChunk = 64;       // shortest chunk the planner picks
+constexpr int64_t kMaxChunks = 65535;   // grid y limit
+constexpr size_t kWsAlign = 256;
+
+int64_t auto_chunk_len(int64_t batch, int64_t L, int64_t d_inner) {
+    if (L <= 0) return 1;
+    const int64_t waves_per_chunk = std::max<int64_t>(1, batch * ((d_inner + 63) / 64));
+    int64_t chunks = (kTargetWaves + waves_per_chunk - 1) / waves_per_chunk;
+    chunks = std::min(chunks, (L + kMinChunk - 1) / kMinChunk);
+    chunks = std::max<int64_t>(chunks, 1);
+    return (L + chunks - 1) / chunks;
+}
+
+struct Plan {
+    int64_t T;
+    int32_t n_chunks;
+    size_t ws_bytes;
+};
+
+ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, int64_t chunk_len,
+                     bool cplx, Plan *p) {
+    if (batch < 0 || L < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "batch/L must be >= 0 and d_inner >= 1");
+    if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
+    if (chunk_len < 0) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be >= 0");
+    // keep every element index inside int64 with margin
+    const double elems = (double)batch * (double)L * (double)d_inner;
+    if (elems > 4.0e18 || (double)batch * d_inner > 2.0e9)
+        return fail(SSM_ERR_SHAPE, "problem too large");
+    const int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
+                                    : auto_chunk_len(batch, L, d_inner);
+    const int64_t n_chunks = L > 0 ? (L + T - 1) / T : 1;
+    if (n_chunks > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n_chunks, (long long)kMaxChunks);
+    p->T = T;
+    p->n_chunks = (int32_t)n_chunks;
+    const size_t per = (size_t)batch * d_inner * d_state * sizeof(float) * (cplx ? 2 : 1);
+    const size_t one = ((per * (size_t)(n_chunks - 1)) + kWsAlign - 1) / kWsAlign * kWsAlign;
+    p->ws_bytes = n_chunks > 1 ? 2 * one : 0;
+    return ok();
+}
+
+ssm_status launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+ssm_status scan_common(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                       const float *D, const void *z, const float *h0, void *y, float *h_final,
+                       int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                       int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                       void *hip_stream, bool cplx) {
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
+    Plan plan;
+    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan);
+    if (st != SSM_OK) return st;
+    const bool work = batch > 0 && L > 0;
+    if (work && (!x || !dt || !A || !B || !C || !D || !y))
+        return fail(SSM_ERR_NULL, "x, dt, A, B, C, D and y are required");
+    const size_t eb = io_bytes(io);
+    if (!aligned(x, eb) || !aligned(dt, eb) || !aligned(z, eb) || !aligned(y, eb) ||
+        !aligned(B, 4) || !aligned(C, 4) || !aligned(A, 16) || !aligned(D, 4) ||
+        !aligned(h0, 16) || !aligned(h_final, 16))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (A, h0, h_final 16 B; B, C, D 4 B; x, dt, z, y element)");
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int64_t state_floats = batch * d_inner * d_state * (cplx ? 2 : 1);
+    if (!work) {
+        if (h_final) return launch_status(ssm::launch_state_fill(h_final, h0, state_floats, s), "state fill");
+        return ok();
+    }
+    if (plan.ws_bytes > 0) {
+        if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan.ws_bytes);
+        if (workspace_bytes < plan.ws_bytes)
+            return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, plan.ws_bytes);
+        if (!aligned(workspace, kWsAlign)) return fail(SSM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    }
+    ssm::ScanArgs a;
+    a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z;
+    a.A = A; a.D = D; a.h0 = h0;
+    a.y = y; a.h_final = h_final;
+    a.sumP = (float *)workspace;
+    a.sumH = plan.ws_bytes ? (float *)((char *)workspace + plan.ws_bytes / 2) : nullptr;
+    a.batch = batch; a.L = L; a.Dn = d_inner;
+    a.T = plan.T; a.n_chunks = plan.n_chunks;
+    a.threads = (int32_t)std::min<int64_t>(256, (d_inner + 63) / 64 * 64);
+    a.dblocks = (int32_t)((d_inner + a.threads - 1) / a.threads);
+    const int iot = io == SSM_BF16 ? 1 : 0;
+    hipError_t e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s)
+                        : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s);
+    return launch_status(e, "scan launch");
+}
+
+ssm_status step_common(float *h, const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const void *z, void *y, int64_t n_layers,
+                       int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                       void *hip_stream, bool cplx, bool replay) {
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
+    if (n_layers < 0 || n_seq < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "n_layers/n_seq must be >= 0 and d_inner >= 1");
+    if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
+    if ((double)n_layers * n_seq * d_inner * 16.0 > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
+    if ((double)n_layers * n_seq * d_inner * 8.0 / 256.0 > 2.0e9) return fail(SSM_ERR_SHAPE, "too many channels for one launch");
+    if (n_layers == 0 || n_seq == 0) return ok();
+    if (!h || !x || !dt || !A || !B || !C || !D || !y)
+        return fail(SSM_ERR_NULL, "h, x_t, dt_t, A, B_t, C_t, D and y_t are required");
+    const size_t eb = io_bytes(io);
+    if (!aligned(h, 16) || !aligned(A, 16) || !aligned(x, eb) || !aligned(dt, eb) ||
+        !aligned(z, eb) || !aligned(y, eb) || !aligned(B, eb) || !aligned(C, eb) || !aligned(D, 4))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; others element)");
+    ssm::StepArgs a;
+    a.h = h; a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z; a.A = A; a.D = D; a.y = y;
+    a.n_layers = n_layers; a.n_seq = n_seq; a.Dn = d_inner;
+    const int iot = io == SSM_BF16 ? 1 : 0;
+    hipStream_t s = (hipStream_t)hip_stream;
+    hipError_t e = cplx ? ssm::launch_step_complex(a, iot, d_state, z != nullptr, replay, s)
+                        : ssm::launch_step_real(a, iot, d_state, z != nullptr, replay, s);
+    return launch_status(e, "step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_scan_fwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state) {
+    return ssm_scan_fwd_workspace_ex(batch, L, d_inner, d_state, 0);
+}
+
+size_t ssm_scan_fwd_workspace_ex(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                 int64_t chunk_len) {
+    Plan p;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p) != SSM_OK) return 0;
+    return p.ws_bytes;
+}
+
+size_t ssm_scan_fwd_c64_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                  int64_t chunk_len) {
+    Plan p;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, true, &p) != SSM_OK) return 0;
+    return p.ws_bytes;
+}
+
+int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state) {
+    Plan p;
+    if (make_plan(batch, L, d_inner, d_state, 0, false, &p) != SSM_OK) return 0;
+    return p.T;
+}
+
+ssm_status ssm_scan_fwd(const void *x, const void *dt, const float *A, const void *B,
+                        const void *C, const float *D, const void *z, const float *h0, void *y,
+                        float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                        int32_t d_state, ssm_dtype io, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io, 0,
+                       workspace, workspace_bytes, hip_stream, false);
+}
+
+ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, const void *z, const float *h0, void *y,
+                           float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                           int32_t d_state, ssm_dtype io, int64_t chunk_len, void *workspace,
+                           size_t workspace_bytes, void *hip_stream) {
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false);
+}
+
+ssm_status ssm_scan_fwd_c64(const void *x, const void *dt, const float *A, const void *B,
+                            const void *C, const float *D, const void *z, const float *h0,
+                            void *y, float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                            int32_t d_state, ssm_dtype io, int64_t chunk_len, void *workspace,
+                            size_t workspace_bytes, void *hip_stream) {
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, true);
+}
+
+ssm_status ssm_step(float *h, const void *x_t, const void *dt_t, const float *A, const void *B_t,
+                    const void *C_t, const float *D, const void *z_t, void *y_t, int64_t n_layers,
+                    int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                    void *hip_stream) {
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, false);
+}
+
+ssm_status ssm_step_replay(float *h, const void *x_t, const void *dt_t, const float *A,
+                           const void *B_t, const void *C_t, const float *D, const void *z_t,
+                           void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                           int32_t d_state, ssm_dtype io, void *hip_stream) {
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, true);
+}
+
+ssm_status ssm_step_c64(float *h, const void *x_t, const void *dt_t, const float *A,
+                        const void *B_t, const void *C_t, const float *D, const void *z_t,
+                        void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                        int32_t d_state, ssm_dtype io, void *hip_stream) {
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, true, false);
+}
+
+ssm_status ssm_step_c64_replay(float *h, const void *x_t, const void *dt_t, const float *A,
+                               const void *B_t, const void *C_t, const float *D, const void *z_t,
+                               void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                               int32_t d_state, ssm_dtype io, void *hip_stream) {
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, true, true);
+}
+
+const char *ssm_status_str(ssm_status s) {
+    switch (s) {
+        case SSM_OK: return "ok";
+        case SSM_ERR_NULL: return "required pointer is NULL";
+        case SSM_ERR_SHAPE: return "invalid size";
+        case SSM_ERR_DTYPE: return "invalid io dtype";
+        case SSM_ERR_ALIGN: return "misaligned pointer";
+        case SSM_ERR_UNSUPPORTED: return "unsupported d_state or chunk length";
+        case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *ssm_last_error(void) { return g_err; }
+
+int32_t ssm_abi_version(void) { return 1; }
+
+}  // extern "C"

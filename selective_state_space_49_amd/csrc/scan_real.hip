@@ -1,0 +1,317 @@
+// scan_real.hip -- prefill of the selective scan with a real diagonal state (gfx950).
+//
+// Recurrence ("Jamba — SSM-Transformer Híbrido", section "Um SSM em uma página";
+// discretisation and gate of the MambaBlock in "【大模型】- Jamba 混合
+// SSM-Transformer", section 4.1 "Mamba 层"), per batch row b and channel d:
+//     h_t[n] = exp(dt_t A[n]) h_{t-1}[n] + dt_t B_t[n] x_t
+//     y_t    = (sum_n C_t[n] h_t[n] + D x_t) * silu(z_t)
+//
+// Work split. One lane owns one channel and keeps its N-wide fp32 state in VGPRs;
+// B_t and C_t are wave-uniform and come in through scalar loads. The sequence is cut
+// into chunks of T steps so that there are enough waves to fill 256 CUs:
+//   1. k_chunk_summary: for every chunk but the last, the end state from a zero
+//      start, H_c, and the chunk's total decay P_c = exp(A * sum of dt over the chunk).
+//   2. k_carry: per state column, an exclusive associative scan over chunks with
+//      (P1, H1) then (P2, H2) = (P2 P1, P2 H1 + H2), seeded with h0. Lanes hold
+//      chunks; the prefix uses DPP row shifts and row broadcasts; a block walks
+//      chunk tiles of 64 in order, carrying the running state between tiles.
+//   3. k_chunk_scan: re-walks every chunk from its true incoming state with the
+//      fused epilogue (C.h + D x, silu gate, rounding to the output type) and
+//      writes y once; the last chunk writes h_final.
+// With one chunk only step 3 runs. Steps 1-2 re-associate the recurrence exactly;
+// results differ from a sequential loop only by rounding.
+//
+// exp(v) is evaluated as 2^(v log2 e) with the hardware exponential: log2 e is
+// folded into A once per lane, so each state update costs one multiply, one
+// exponential, one multiply (dt x times B) and two fused multiply-adds.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+struct LaneId {
+    int64_t b, d;
+};
+
+__device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
+    LaneId r;
+    r.b = (int64_t)blockIdx.x / a.dblocks;
+    r.d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
+    return r;
+}
+
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
+    const LaneId ln = lane_id(a);
+    if (ln.d >= a.Dn) return;
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const int64_t t1 = t0 + a.T;  // every chunk that has a summary is full length
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        h[n] = 0.0f;
+    }
+    const int64_t base = (ln.b * a.L + t0) * a.Dn + ln.d;
+    const IO *xp = (const IO *)a.x + base;
+    const IO *dp = (const IO *)a.dt + base;
+    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
+    double S = 0.0;  // sum of dt over the chunk, in double so long chunks keep it exact to fp32
+    for (int64_t t = t0; t < t1; ++t) {
+        const float xv = Io<IO>::ld(xp), dv = Io<IO>::ld(dp);
+        xp += a.Dn;
+        dp += a.Dn;
+        const float u = dv * xv;
+        S += (double)dv;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float bn = Uniform<IO>::ld(Bp, t * N + n);
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+        }
+    }
+    const float Sf = (float)S;
+    const size_t o = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a.sumP[o + n] = e2(A2[n] * Sf);
+        a.sumH[o + n] = h[n];
+    }
+}
+
+// ---------------------------------------------------------------- carry scan
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                      ROW_MASK, 0xf, false));
+}
+
+// Lane i holds the segment ending at i as (p, h): state_after = p * state_before + h.
+// Combine with the earlier segment read over DPP; lanes without a source read the
+// identity (1, 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void scan_step(float &p, float &h) {
+    const float pe = dpp<CTRL, ROW_MASK>(1.0f, p);
+    const float he = dpp<CTRL, ROW_MASK>(0.0f, h);
+    h = __builtin_fmaf(p, he, h);
+    p = p * pe;
+}
+
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ void wave_scan(float &p, float &h) {
+    scan_step<0x111, 0xf>(p, h);  // row_shr:1
+    scan_step<0x112, 0xf>(p, h);  // row_shr:2
+    scan_step<0x114, 0xf>(p, h);  // row_shr:4
+    scan_step<0x118, 0xf>(p, h);  // row_shr:8
+    scan_step<0x142, 0xa>(p, h);  // row_bcast:15 into rows 1 and 3
+    scan_step<0x143, 0xc>(p, h);  // row_bcast:31 into rows 2 and 3
+}
+
+// M = batch * Dn * N state columns; block = 4 waves, 64 columns; LDS tiles are
+// [64 chunks][64 columns], loaded and stored row by row (coalesced), scanned
+// column by column with lanes = chunks.
+__global__ __launch_bounds__(256) void k_carry(ScanArgs a, int64_t M) {
+    __shared__ float sP[64][65];
+    __shared__ float sH[64][65];
+    __shared__ float sCarry[64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t col0 = (int64_t)blockIdx.x * 64;
+    const int64_t col = col0 + lane;
+    const int nsum = a.n_chunks - 1;
+    if (threadIdx.x < 64) sCarry[lane] = (col < M && a.h0) ? a.h0[col] : 0.0f;
+    for (int k0 = 0; k0 < nsum; k0 += 64) {
+        const int rows = min(64, nsum - k0);
+        __syncthreads();
+        for (int r = w; r < rows; r += 4) {
+            if (col < M) {
+                sP[r][lane] = a.sumP[(size_t)(k0 + r) * M + col];
+                sH[r][lane] = a.sumH[(size_t)(k0 + r) * M + col];
+            }
+        }
+        __syncthreads();
+        for (int jj = 0; jj < 16; ++jj) {
+            const int j = w * 16 + jj;
+            if (col0 + j >= M) break;  // uniform over the wave
+            float p = lane < rows ? sP[lane][j] : 1.0f;
+            float h = lane < rows ? sH[lane][j] : 0.0f;
+            wave_scan(p, h);
+            const float out = __builtin_fmaf(p, sCarry[j], h);
+            if (lane < rows) sH[lane][j] = out;
+            const float next = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(out), rows - 1));
+            if (lane == 0) sCarry[j] = next;
+        }
+        __syncthreads();
+        for (int r = w; r < rows; r += 4)
+            if (col < M) a.sumH[(size_t)(k0 + r) * M + col] = sH[r][lane];
+    }
+}
+
+// ---------------------------------------------------------------- rescan + epilogue
+// Steps are processed in blocks of kU. The x, dt, z values of the next block are
+// loaded into registers while the current block is computed (ping-pong buffers),
+// so the HBM latency of one block hides behind the arithmetic of the previous one.
+// Row pointers are wave-uniform (SGPR) and each lane adds its 32-bit channel
+// offset, which gives the scalar-base + vector-offset load form and no per-step
+// vector address arithmetic. A scheduling barrier between steps keeps each step's
+// scalar B/C loads next to their use instead of hoisting a whole block's worth of
+// them into SGPRs.
+constexpr int kU = 4;
+
+struct StepIn {
+    float x[kU], dt[kU], z[kU];
+};
+
+template <typename IO, bool GATED>
+__device__ __forceinline__ void load_block(StepIn &s, const IO *xr, const IO *dr, const IO *zr,
+                                           int64_t Dn, uint32_t off) {
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        s.x[k] = Io<IO>::ld(xr + k * Dn + off);
+        s.dt[k] = Io<IO>::ld(dr + k * Dn + off);
+        if (GATED) s.z[k] = Io<IO>::ld(zr + k * Dn + off);
+    }
+}
+
+// One time step of one channel: state update, y = C.h + D x, gate, store.
+template <typename IO, int N, bool GATED>
+__device__ __forceinline__ void scan_step(float xv, float dv, float zv, float (&h)[N],
+                                          const float (&A2)[N], float Dd, const IO *Bp,
+                                          const IO *Cp, int64_t t, IO *yp) {
+    const float u = dv * xv;
+    float acc = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float bn = Uniform<IO>::ld(Bp, t * N + n);
+        const float cn = Uniform<IO>::ld(Cp, t * N + n);
+        h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+        acc = __builtin_fmaf(cn, h[n], acc);
+    }
+    float yv = __builtin_fmaf(Dd, xv, acc);
+    if (GATED) yv = yv * silu(zv);
+    Io<IO>::st(yp, yv);
+}
+
+template <typename IO, int N, bool GATED>
+__device__ __forceinline__ void scan_block(const StepIn &s, float (&h)[N], const float (&A2)[N],
+                                           float Dd, const IO *Bp, const IO *Cp, int64_t t,
+                                           IO *yr, int64_t Dn, uint32_t off) {
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        scan_step<IO, N, GATED>(s.x[k], s.dt[k], GATED ? s.z[k] : 0.0f, h, A2, Dd, Bp, Cp, t + k,
+                                yr + k * Dn + off);
+    }
+}
+
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
+    const LaneId ln = lane_id(a);
+    if (ln.d >= a.Dn) return;
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const int64_t t1 = min(a.L, t0 + a.T);
+    const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
+    const float *hin = c == 0 ? (a.h0 ? a.h0 + col : nullptr)
+                              : a.sumH + (size_t)(c - 1) * a.batch * a.Dn * N + col;
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        h[n] = hin ? hin[n] : 0.0f;
+    }
+    const float Dd = a.D[ln.d];
+    const int64_t Dn = a.Dn;
+    const uint32_t off = (uint32_t)ln.d;
+    // Wave-uniform pointers to row t0 of this batch row.
+    const int64_t row0 = (ln.b * a.L + t0) * Dn;
+    const IO *xr = (const IO *)a.x + row0;
+    const IO *dr = (const IO *)a.dt + row0;
+    const IO *zr = GATED ? (const IO *)a.z + row0 : nullptr;
+    IO *yr = (IO *)a.y + row0;
+    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
+    const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
+    const int64_t full = (t1 - t0) / kU;  // whole blocks
+    const int64_t stride = kU * Dn;
+    int64_t t = t0;
+    StepIn bufA, bufB;
+    if (full > 0) load_block<IO, GATED>(bufA, xr, dr, zr, Dn, off);
+    for (int64_t k = 0; k < full; k += 2) {
+        // block k is in bufA: fetch block k+1 into bufB, then compute block k
+        if (k + 1 < full)
+            load_block<IO, GATED>(bufB, xr + stride, dr + stride, GATED ? zr + stride : nullptr,
+                                  Dn, off);
+        scan_block<IO, N, GATED>(bufA, h, A2, Dd, Bp, Cp, t, yr, Dn, off);
+        t += kU; xr += stride; dr += stride; yr += stride;
+        if (GATED) zr += stride;
+        if (k + 1 >= full) break;
+        // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
+        if (k + 2 < full)
+            load_block<IO, GATED>(bufA, xr + stride, dr + stride, GATED ? zr + stride : nullptr,
+                                  Dn, off);
+        scan_block<IO, N, GATED>(bufB, h, A2, Dd, Bp, Cp, t, yr, Dn, off);
+        t += kU; xr += stride; dr += stride; yr += stride;
+        if (GATED) zr += stride;
+    }
+    // ragged tail: fewer than kU steps, one at a time
+    for (; t < t1; ++t) {
+        const float xv = Io<IO>::ld(xr + off), dv = Io<IO>::ld(dr + off);
+        const float zv = GATED ? Io<IO>::ld(zr + off) : 0.0f;
+        scan_step<IO, N, GATED>(xv, dv, zv, h, A2, Dd, Bp, Cp, t, yr + off);
+        xr += Dn; dr += Dn; yr += Dn;
+        if (GATED) zr += Dn;
+    }
+    if (c == a.n_chunks - 1 && a.h_final) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.h_final[col + n] = h[n];
+    }
+}
+
+__global__ void k_state_fill(float *dst, const float *src, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) dst[i] = src ? src[i] : 0.0f;
+}
+
+template <typename IO, int N>
+hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s) {
+    const dim3 blk(a.threads);
+    const unsigned gx = (unsigned)(a.batch * a.dblocks);
+    if (a.n_chunks > 1) {
+        hipLaunchKernelGGL((k_chunk_summary<IO, N>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+        const int64_t M = a.batch * a.Dn * N;
+        hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+    }
+    if (gated)
+        hipLaunchKernelGGL((k_chunk_scan<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_chunk_scan<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s) {
+    switch (d_state) {
+        case 1: return launch_t<IO, 1>(a, gated, s);
+        case 2: return launch_t<IO, 2>(a, gated, s);
+        case 4: return launch_t<IO, 4>(a, gated, s);
+        case 8: return launch_t<IO, 8>(a, gated, s);
+        case 16: return launch_t<IO, 16>(a, gated, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s) {
+    return io == 0 ? launch_io<float>(a, d_state, gated, s)
+                   : launch_io<bf16_bits>(a, d_state, gated, s);
+}
+
+hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_state_fill, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, dst,
+                       src, count);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

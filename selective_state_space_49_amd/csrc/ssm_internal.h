@@ -1,0 +1,44 @@
+// ssm_internal.h -- host-side launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// One prefill call, already validated. Pointers are device pointers.
+struct ScanArgs {
+    const void *x, *dt, *B, *C, *z;
+    const float *A, *D, *h0;
+    void *y;
+    float *h_final;
+    float *sumP;   // workspace: per-chunk decay over the chunk   [n_chunks-1][batch][Dn][N](x2 if complex)
+    float *sumH;   // workspace: per-chunk end state from zero; the carry scan overwrites
+                   // entry c with the state entering chunk c+1
+    int64_t batch, L, Dn;
+    int64_t T;         // steps per chunk
+    int32_t n_chunks;  // ceil(L / T), >= 1
+    int32_t dblocks;   // channel blocks per batch row (grid x = batch * dblocks)
+    int32_t threads;   // threads per block (multiple of 64, <= 256)
+};
+
+struct StepArgs {
+    float *h;
+    const void *x, *dt, *B, *C, *z;
+    const float *A, *D;
+    void *y;
+    int64_t n_layers, n_seq, Dn;
+};
+
+// Real diagonal state. io: 0 = f32, 1 = bf16. Returns hipSuccess or the launch error.
+hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s);
+hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s);
+hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStream_t s);
+
+hipError_t launch_step_real(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                            hipStream_t s);
+hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                               hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,293 @@
+// step.hip -- single-token decode for many (layer, sequence) states (gfx950).
+//
+// A state-space layer needs only its previous state and the new token to emit the
+// next output, so decoding keeps one fixed-size state per layer instead of a
+// growing cache ("Jamba — SSM-Transformer Híbrido", section "Um SSM em uma
+// página"; the same section of the zh lesson page). One call advances every
+// (layer, sequence, channel) by one token, in place.
+//
+// The work is bound by HBM: per channel the 16-state fp32 state is read and
+// written (128 of the 136 bytes moved). G lanes share one channel, each owning
+// K = N / G consecutive states, so a wave reads and writes the state with fully
+// coalesced 16-byte accesses; the G partial outputs are combined with lane
+// shuffles in a fixed pairwise tree.
+//
+// The replay kernels run one thread per channel with plain loops and perform the
+// same fp32 operations in the same order (the tree included), so that the decode
+// kernels can be checked bit for bit against them. The library is built with
+// floating-point contraction off; every fused multiply-add below is explicit.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+// Channel index ch = (l * n_seq + q) * Dn + d.
+struct Chan {
+    int64_t ch, l, d, lq;
+};
+
+__device__ __forceinline__ Chan chan_of(const StepArgs &a, int64_t ch) {
+    Chan c;
+    c.ch = ch;
+    c.d = ch % a.Dn;
+    c.lq = ch / a.Dn;
+    c.l = c.lq / a.n_seq;
+    return c;
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float p) {
+    // Pairwise tree over the G lanes of a group: after the xor-1 step lanes hold
+    // p0+p1, p2+p3, ...; after xor-2, (p0+p1)+(p2+p3), ... Addition is commutative,
+    // so both lanes of a pair compute the same bits.
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) p = p + __shfl_xor(p, m, 64);
+    return p;
+}
+
+template <int G>
+__device__ __forceinline__ float tree_sum(float (&p)[G]) {
+#pragma unroll
+    for (int s = 1; s < G; s <<= 1)
+#pragma unroll
+        for (int i = 0; i < G; i += 2 * s) p[i] = p[i] + p[i + s];
+    return p[0];
+}
+
+// ---------------------------------------------------------------- real state
+template <int N> struct RealGroups {
+    static constexpr int G = N >= 8 ? N / 4 : 1;
+    static constexpr int K = N / G;
+};
+
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_step(StepArgs a) {
+    constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n_ch = a.n_layers * a.n_seq * a.Dn;
+    const int64_t ch = gid / G;
+    const int g = (int)(gid % G);
+    if (ch >= n_ch) return;  // G divides 64: a group is wholly in or out of range
+    const Chan c = chan_of(a, ch);
+    float *hp = a.h + ch * N + g * K;
+    const float *Ap = a.A + (c.l * a.Dn + c.d) * N + g * K;
+    const IO *Bp = (const IO *)a.B + c.lq * N + g * K;
+    const IO *Cp = (const IO *)a.C + c.lq * N + g * K;
+    float hv[K], av[K];
+    if constexpr (K == 4) {
+        const float4 h4 = *(const float4 *)hp, a4 = *(const float4 *)Ap;
+        hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
+        av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) { hv[k] = hp[k]; av[k] = Ap[k]; }
+    }
+    const float xv = Io<IO>::ld((const IO *)a.x + ch);
+    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    const float u = dv * xv;
+    float p = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float a2 = av[k] * kLog2e;
+        hv[k] = __builtin_fmaf(e2(dv * a2), hv[k], u * Io<IO>::ld(Bp + k));
+        p = __builtin_fmaf(Io<IO>::ld(Cp + k), hv[k], p);
+    }
+    const float acc = group_sum<G>(p);
+    if constexpr (K == 4) {
+        *(float4 *)hp = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) hp[k] = hv[k];
+    }
+    if (g == 0) {
+        float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, acc);
+        if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + ch));
+        Io<IO>::st((IO *)a.y + ch, yv);
+    }
+}
+
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
+    constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
+    const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (ch >= a.n_layers * a.n_seq * a.Dn) return;
+    const Chan c = chan_of(a, ch);
+    float *hp = a.h + ch * N;
+    const float *Ap = a.A + (c.l * a.Dn + c.d) * N;
+    const IO *Bp = (const IO *)a.B + c.lq * N;
+    const IO *Cp = (const IO *)a.C + c.lq * N;
+    const float xv = Io<IO>::ld((const IO *)a.x + ch);
+    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    const float u = dv * xv;
+    float p[G];
+    for (int g = 0; g < G; ++g) {
+        p[g] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int n = g * K + k;
+            const float a2 = Ap[n] * kLog2e;
+            hp[n] = __builtin_fmaf(e2(dv * a2), hp[n], u * Io<IO>::ld(Bp + n));
+            p[g] = __builtin_fmaf(Io<IO>::ld(Cp + n), hp[n], p[g]);
+        }
+    }
+    float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, tree_sum<G>(p));
+    if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + ch));
+    Io<IO>::st((IO *)a.y + ch, yv);
+}
+
+// ---------------------------------------------------------------- complex state
+template <int N> struct CplxGroups {
+    static constexpr int G = N >= 2 ? N / 2 : 1;
+    static constexpr int K = N / G;
+};
+
+// One complex state update: h <- exp(dt A) h + dt x B.
+__device__ __forceinline__ void cstep(float dv, float u, float are, float aim, float br, float bi,
+                                      float &hr, float &hi) {
+    const float mag = e2(dv * (are * kLog2e));
+    const float r = fract(dv * (aim * kInv2Pi));
+    const float pr = mag * cos_rev(r), pi = mag * sin_rev(r);
+    const float nr = __builtin_fmaf(pr, hr, __builtin_fmaf(-pi, hi, u * br));
+    const float ni = __builtin_fmaf(pr, hi, __builtin_fmaf(pi, hr, u * bi));
+    hr = nr;
+    hi = ni;
+}
+
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_step_c(StepArgs a) {
+    constexpr int G = CplxGroups<N>::G, K = CplxGroups<N>::K;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n_ch = a.n_layers * a.n_seq * a.Dn;
+    const int64_t ch = gid / G;
+    const int g = (int)(gid % G);
+    if (ch >= n_ch) return;
+    const Chan c = chan_of(a, ch);
+    float *hp = a.h + (ch * N + g * K) * 2;
+    const float *Ap = a.A + ((c.l * a.Dn + c.d) * N + g * K) * 2;
+    const IO *Bp = (const IO *)a.B + (c.lq * N + g * K) * 2;
+    const IO *Cp = (const IO *)a.C + (c.lq * N + g * K) * 2;
+    float hv[2 * K], av[2 * K];
+    if constexpr (K == 2) {
+        const float4 h4 = *(const float4 *)hp, a4 = *(const float4 *)Ap;
+        hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
+        av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 2 * K; ++k) { hv[k] = hp[k]; av[k] = Ap[k]; }
+    }
+    const float xv = Io<IO>::ld((const IO *)a.x + ch);
+    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    const float u = dv * xv;
+    float p = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        cstep(dv, u, av[2 * k], av[2 * k + 1], Io<IO>::ld(Bp + 2 * k), Io<IO>::ld(Bp + 2 * k + 1),
+              hv[2 * k], hv[2 * k + 1]);
+        p = __builtin_fmaf(Io<IO>::ld(Cp + 2 * k), hv[2 * k], p);
+        p = __builtin_fmaf(-Io<IO>::ld(Cp + 2 * k + 1), hv[2 * k + 1], p);
+    }
+    const float acc = group_sum<G>(p);
+    if constexpr (K == 2) {
+        *(float4 *)hp = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 2 * K; ++k) hp[k] = hv[k];
+    }
+    if (g == 0) {
+        float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, acc);
+        if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + ch));
+        Io<IO>::st((IO *)a.y + ch, yv);
+    }
+}
+
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_step_c_replay(StepArgs a) {
+    constexpr int G = CplxGroups<N>::G, K = CplxGroups<N>::K;
+    const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (ch >= a.n_layers * a.n_seq * a.Dn) return;
+    const Chan c = chan_of(a, ch);
+    float *hp = a.h + ch * N * 2;
+    const float *Ap = a.A + (c.l * a.Dn + c.d) * N * 2;
+    const IO *Bp = (const IO *)a.B + c.lq * N * 2;
+    const IO *Cp = (const IO *)a.C + c.lq * N * 2;
+    const float xv = Io<IO>::ld((const IO *)a.x + ch);
+    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    const float u = dv * xv;
+    float p[G];
+    for (int g = 0; g < G; ++g) {
+        p[g] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int n = g * K + k;
+            float hr = hp[2 * n], hi = hp[2 * n + 1];
+            cstep(dv, u, Ap[2 * n], Ap[2 * n + 1], Io<IO>::ld(Bp + 2 * n),
+                  Io<IO>::ld(Bp + 2 * n + 1), hr, hi);
+            hp[2 * n] = hr;
+            hp[2 * n + 1] = hi;
+            p[g] = __builtin_fmaf(Io<IO>::ld(Cp + 2 * n), hr, p[g]);
+            p[g] = __builtin_fmaf(-Io<IO>::ld(Cp + 2 * n + 1), hi, p[g]);
+        }
+    }
+    float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, tree_sum<G>(p));
+    if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + ch));
+    Io<IO>::st((IO *)a.y + ch, yv);
+}
+
+// ---------------------------------------------------------------- launch
+inline unsigned grid_for(const StepArgs &a, int lanes_per_ch) {
+    const int64_t threads = a.n_layers * a.n_seq * a.Dn * lanes_per_ch;
+    return (unsigned)((threads + 255) / 256);
+}
+
+template <typename IO, int N>
+hipError_t launch_real_n(const StepArgs &a, bool gated, bool replay, hipStream_t s) {
+    const dim3 blk(256), grid(grid_for(a, replay ? 1 : RealGroups<N>::G));
+    if (replay) {
+        if (gated) hipLaunchKernelGGL((k_step_replay<IO, N, true>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_step_replay<IO, N, false>), grid, blk, 0, s, a);
+    } else {
+        if (gated) hipLaunchKernelGGL((k_step<IO, N, true>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_step<IO, N, false>), grid, blk, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename IO, int N>
+hipError_t launch_cplx_n(const StepArgs &a, bool gated, bool replay, hipStream_t s) {
+    const dim3 blk(256), grid(grid_for(a, replay ? 1 : CplxGroups<N>::G));
+    if (replay) {
+        if (gated) hipLaunchKernelGGL((k_step_c_replay<IO, N, true>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_step_c_replay<IO, N, false>), grid, blk, 0, s, a);
+    } else {
+        if (gated) hipLaunchKernelGGL((k_step_c<IO, N, true>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_step_c<IO, N, false>), grid, blk, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename IO, bool CPLX>
+hipError_t launch_io(const StepArgs &a, int d_state, bool gated, bool replay, hipStream_t s) {
+    switch (d_state) {
+        case 1: return CPLX ? launch_cplx_n<IO, 1>(a, gated, replay, s) : launch_real_n<IO, 1>(a, gated, replay, s);
+        case 2: return CPLX ? launch_cplx_n<IO, 2>(a, gated, replay, s) : launch_real_n<IO, 2>(a, gated, replay, s);
+        case 4: return CPLX ? launch_cplx_n<IO, 4>(a, gated, replay, s) : launch_real_n<IO, 4>(a, gated, replay, s);
+        case 8: return CPLX ? launch_cplx_n<IO, 8>(a, gated, replay, s) : launch_real_n<IO, 8>(a, gated, replay, s);
+        case 16: return CPLX ? launch_cplx_n<IO, 16>(a, gated, replay, s) : launch_real_n<IO, 16>(a, gated, replay, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_step_real(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                            hipStream_t s) {
+    return io == 0 ? launch_io<float, false>(a, d_state, gated, replay, s)
+                   : launch_io<bf16_bits, false>(a, d_state, gated, replay, s);
+}
+
+hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                               hipStream_t s) {
+    return io == 0 ? launch_io<float, true>(a, d_state, gated, replay, s)
+                   : launch_io<bf16_bits, true>(a, d_state, gated, replay, s);
+}
+
+}  // namespace ssm

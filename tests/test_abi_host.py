@@ -1,0 +1,112 @@
+"""The C ABI on the host: the library loads, exports what the header declares, and
+rejects bad arguments before anything is enqueued (no GPU is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_49_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssm.library_path()):
+        from selective_state_space_49_amd import build
+        build.build()
+    return ssm.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = header_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in ssm_scan.h but not exported"
+    assert sorted(declared) == sorted(ssm.EXPORTED_SYMBOLS)
+
+
+def test_version_and_status_strings(lib):
+    assert ssm.ssm_abi_version() == 1
+    for s in range(8):
+        assert ssm.ssm_status_str(s)
+    assert ssm.ssm_status_str(99) == "unknown status"
+
+
+def test_plan_and_workspace(lib):
+    # One chunk needs no workspace.
+    assert ssm.ssm_scan_fwd_workspace_ex(1, 64, 16, 4, 64) == 0
+    assert ssm.ssm_scan_fwd_workspace_ex(1, 64, 16, 4, 1000) == 0
+    # Two chunks: one summary pair of batch*d_inner*d_state floats, 256-byte rounded.
+    ws = ssm.ssm_scan_fwd_workspace_ex(2, 100, 10, 4, 50)
+    assert ws == 2 * ((2 * 10 * 4 * 4 + 255) // 256 * 256)
+    assert ssm.ssm_scan_fwd_c64_workspace(2, 100, 10, 4, 50) == 2 * ((2 * 10 * 4 * 8 + 255) // 256 * 256)
+    # Auto plan for the two long workloads gives whole chunks and enough waves.
+    for (b, L, Dn) in [(2, 4096, 8192), (1, 262144, 8192), (4, 8192, 4096)]:
+        T = ssm.ssm_scan_fwd_chunk_len(b, L, Dn, 16)
+        chunks = -(-L // T)
+        assert 64 <= T <= L and chunks * b * (Dn // 64) >= 2048
+        assert ssm.ssm_scan_fwd_workspace(b, L, Dn, 16) == ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, 16, 0)
+    # Invalid sizes give 0 from the query.
+    assert ssm.ssm_scan_fwd_workspace(1, 10, 8, 3) == 0
+
+
+def _scan_raw(lib, x=0x1000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None, h0=None,
+              y=0x1000, hf=None, batch=1, L=8, Dn=4, N=4, io=0, chunk=0, ws=None, wsb=0):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lib.ssm_scan_fwd_ex(p(x), p(dt), p(A), p(B), p(C), p(D), p(z), p(h0), p(y), p(hf),
+                               batch, L, Dn, N, io, chunk, p(ws), wsb, None)
+
+
+def test_scan_argument_errors(lib):
+    # These all fail validation on the host; the fake addresses are never used.
+    assert _scan_raw(lib, N=3) == UNSUP
+    assert _scan_raw(lib, N=32) == UNSUP
+    assert _scan_raw(lib, io=2) == DTYPE
+    assert _scan_raw(lib, x=None) == NULL
+    assert _scan_raw(lib, y=None) == NULL
+    assert _scan_raw(lib, batch=-1) == SHAPE
+    assert _scan_raw(lib, Dn=0) == SHAPE
+    assert _scan_raw(lib, L=-5) == SHAPE
+    assert _scan_raw(lib, chunk=-1) == UNSUP
+    assert _scan_raw(lib, A=0x1004) == ALIGN
+    assert _scan_raw(lib, h0=0x1008) == ALIGN
+    assert _scan_raw(lib, B=0x1002) == ALIGN
+    assert _scan_raw(lib, io=0, x=0x1002) == ALIGN
+    # several chunks without / with too little workspace
+    assert _scan_raw(lib, L=200, chunk=64) == WS
+    need = ssm.ssm_scan_fwd_workspace_ex(1, 200, 4, 4, 64)
+    assert _scan_raw(lib, L=200, chunk=64, ws=0x10000, wsb=need - 1) == WS
+    assert _scan_raw(lib, L=200, chunk=64, ws=0x10080, wsb=need) == ALIGN
+    assert _scan_raw(lib, L=10 ** 6, chunk=1) == UNSUP  # more chunks than one grid allows
+    assert "d_state" in ssm.ssm_last_error() or "chunk" in ssm.ssm_last_error()
+
+
+def test_step_argument_errors(lib):
+    p = ctypes.c_void_p
+    a = dict(h=0x1000, x=0x1000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None, y=0x1000)
+
+    def call(fn="ssm_step", Ln=2, S=3, Dn=4, N=16, io=1, **kw):
+        v = dict(a, **kw)
+        args = [None if v[k] is None else p(v[k]) for k in ("h", "x", "dt", "A", "B", "C", "D", "z", "y")]
+        return getattr(lib, fn)(*args, Ln, S, Dn, N, io, None)
+
+    for fn in ("ssm_step", "ssm_step_replay", "ssm_step_c64", "ssm_step_c64_replay"):
+        assert call(fn, N=5) == UNSUP
+        assert call(fn, io=9) == DTYPE
+        assert call(fn, h=None) == NULL
+        assert call(fn, h=0x1004) == ALIGN
+        assert call(fn, A=0x1008) == ALIGN
+        assert call(fn, Dn=0) == SHAPE
+        assert call(fn, Ln=-1) == SHAPE
+        assert call(fn, Ln=0) == OK  # nothing to do, nothing enqueued
