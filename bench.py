@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one full pass of the path over one batch of synthetic input: for the
+prefill workloads one ssm_scan_fwd call (chunk summaries, carry scan, rescan with
+the fused epilogue); for the decode workload one token for every layer and
+sequence (one ssm_step call per layer, as a model would issue them). Inputs are
+drawn with the seeded recipe of ``workloads`` and are resident in HBM before the
+timed region starts. W untimed warm-up steps are followed by exactly K timed
+steps bracketed by device synchronisation. Prints one JSON line.
+
+The default workload is the long-context prefill (batch 1, L = 262144, 8192
+channels, N = 16, bf16 inputs, fp32 state) at which the throughput target is set.
+
+Roofline: the dominant kernel's average duration is measured with HIP events
+recorded by the library itself on the launch stream (ssm_scan_fwd_profiled), and
+its algorithmic work is compared with two ceilings: HBM bytes against 8 TB/s, and
+vector-ALU issue slots against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. The
+reported bound is the one the kernel is closer to. HBM traffic measured with
+rocprofv3 counters is read from profiles/traffic.json when it was taken on the
+current kernel source (by hash), else null.
+
+The CPU baseline is the fp64 oracle as it stands, run on a bounded sample of the
+same workload (a subset of channels over the full sequence; channels are
+independent) from several host threads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one fp32 lane-op per lane per clock.
+VALU_PEAK_TLANE = 256 * 4 * 16 * 2.4e9 / 1e12
+METRIC = "scan elements (batch·L·D_inner)/s at N=16; achieved HBM GB/s vs peak"
+KERNEL_SOURCES = {
+    "real": "selective_state_space_49_amd/csrc/scan_real.hip",
+    "complex": "selective_state_space_49_amd/csrc/scan_complex.hip",
+    "step": "selective_state_space_49_amd/csrc/step.hip",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kind], "selective_state_space_49_amd/csrc/ssm_device.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------- algorithmic work
+def prefill_bytes(s, io_bytes: int) -> float:
+    """Each input read once, each output written once (never dA or dB)."""
+    b, L, Dn, N = s.batch, s.L, s.d_inner, s.d_state
+    c = 2 if s.complex_state else 1
+    streams = 3 + (1 if s.gated else 0)                     # x, dt, (z), y
+    return (b * L * Dn * streams * io_bytes + 2 * b * L * N * c * io_bytes
+            + Dn * N * c * 4 + Dn * 4 + b * Dn * N * c * 4)
+
+
+def prefill_lane_ops(s) -> float:
+    """Vector-ALU issue slots per scan element on the fp32 path (transcendentals
+    count 2: the hardware issues them at half rate). Real state, per state:
+    dt*A, exp, (dt x)*B, fma (state), fma (output). Complex state, per state:
+    dt*a, exp, dt*theta, fract, sin, cos, 2 mul (decay*rotation), 2 mul (dt x B),
+    4 fma (complex update), 2 fma (real part of C h). Per element: widening of
+    x, dt (and z), dt*x, D*x + acc, the gate (mul, exp, add, rcp, 2 mul) and the
+    output conversion."""
+    per_state = 18 if s.complex_state else 6
+    per_elem = 2 + 1 + 1 + 1 + (1 + 8 if s.gated else 0)
+    return s.d_state * per_state + per_elem
+
+
+def decode_bytes(s, io_bytes: int) -> float:
+    """Per token for all layers: state read + write, token inputs/outputs, A, D."""
+    Ln, S, Dn, N = s.n_layers, s.n_seq, s.d_inner, s.d_state
+    return (Ln * S * Dn * N * 4 * 2 + Ln * S * Dn * (4 if s.gated else 3) * io_bytes
+            + 2 * Ln * S * N * io_bytes + Ln * Dn * (N + 1) * 4)
+
+
+# ----------------------------------------------------------------- runs
+def run_prefill(shape, steps, warmup, torch, ssm, workloads):
+    dev = "cuda"
+    log("drawing inputs for", shape.name)
+    d = workloads.make_scan_inputs(shape, dev)
+    b, L, Dn, N = shape.batch, shape.L, shape.d_inner, shape.d_state
+    cplx = shape.complex_state
+    y = torch.empty_like(d["x"])
+    hf = torch.empty((b, Dn, N) + ((2,) if cplx else ()), dtype=torch.float32, device=dev)
+    T = ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N)
+    ws_n = (ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, 0) if cplx
+            else ssm.ssm_scan_fwd_workspace(b, L, Dn, N))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    fn = ssm.ssm_scan_fwd_c64_profiled if cplx else ssm.ssm_scan_fwd_profiled
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for row in ev:                      # create the underlying HIP events
+        for e in row:
+            e.record()
+    warm_ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in warm_ev:
+        e.record()
+    torch.cuda.synchronize()
+
+    def call(events):
+        fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None, y=y, h_final=hf,
+           workspace=ws, events=[e.cuda_event for e in events])
+
+    log("warmup", warmup)
+    for _ in range(warmup):
+        call(warm_ev)
+    torch.cuda.synchronize()
+    log("timing", steps, "steps")
+    t0 = time.perf_counter()
+    for k in range(steps):
+        call(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = {"summary": 0.0, "carry": 0.0, "rescan": 0.0}
+    for row in ev:
+        phases["summary"] += row[0].elapsed_time(row[1])
+        phases["carry"] += row[1].elapsed_time(row[2])
+        phases["rescan"] += row[2].elapsed_time(row[3])
+    phases = {k: v / steps for k, v in phases.items()}
+    gpu_ms = sum(phases.values())
+    io_bytes = 2 if shape.io == "bf16" else 4
+    elems = shape.elements
+    info = {
+        "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": phases,
+        "elements_per_step": elems, "bytes_per_step": prefill_bytes(shape, io_bytes),
+        "lane_ops_per_elem": prefill_lane_ops(shape), "chunk_len": T,
+        "n_chunks": -(-L // T), "dominant_ms": phases["rescan"], "gpu_ms": gpu_ms,
+        "kernel": "k_chunk_scan_c" if cplx else "k_chunk_scan",
+        "source": "complex" if cplx else "real",
+    }
+    return info, d
+
+
+def run_decode(shape, steps, warmup, torch, ssm, workloads):
+    dev = "cuda"
+    Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
+    par = workloads.make_decode_params(shape, dev)
+    h = torch.zeros((Ln, S, Dn, N), device=dev)
+    log("drawing", warmup + steps, "token steps of inputs")
+    toks = [workloads.make_decode_step(shape, k, dev) for k in range(warmup + steps)]
+    y = torch.empty((Ln, S, Dn), dtype=toks[0]["x"].dtype, device=dev)
+    A_l = [par["A"][l:l + 1] for l in range(Ln)]
+    D_l = [par["D"][l:l + 1] for l in range(Ln)]
+    h_l = [h[l:l + 1] for l in range(Ln)]
+    per_layer = [{k: (None if v is None else v[l:l + 1]) for k, v in t.items()} for t in toks
+                 for l in range(Ln)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps * Ln)]
+
+    def token(k, timed):
+        for l in range(Ln):
+            t = per_layer[k * Ln + l]
+            if timed:
+                ev[2 * ((k - warmup) * Ln + l)].record()
+            ssm.ssm_step(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
+                         y_t=y[l:l + 1])
+            if timed:
+                ev[2 * ((k - warmup) * Ln + l) + 1].record()
+
+    for k in range(warmup):
+        token(k, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(warmup, warmup + steps):
+        token(k, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps * Ln)) / (steps * Ln)
+    io_bytes = 2 if shape.io == "bf16" else 4
+    info = {
+        "wall_s": wall, "ms_per_step": wall / steps * 1e3,
+        "elements_per_step": Ln * S * Dn, "bytes_per_step": decode_bytes(shape, io_bytes),
+        "lane_ops_per_elem": 6 * N + 14, "dominant_ms": kern * Ln, "per_call_ms": kern,
+        "kernel": "k_step", "source": "step", "phases_ms": {"ssm_step_per_layer": kern},
+    }
+    return info, None
+
+
+def traffic_for(info, workload):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(workload)
+    if not ent or ent.get("source_sha") != source_hash(info["source"]):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, d, torch, workloads, threads):
+    import oracle
+    oracle.build(force=False)
+    if shape.complex_state:
+        k = 32
+    else:
+        k = 512 if shape.L >= 100000 else 128
+    k = min(k, shape.d_inner)
+    idx = workloads.sample_channels(shape.d_inner, k, seed=5).to("cuda")
+    g = lambda t: None if t is None else t.index_select(2, idx).cpu()
+    args = (g(d["x"]), g(d["dt"]), d["A"].index_select(0, idx).cpu(), d["B"].cpu(), d["C"].cpu(),
+            d["D"].index_select(0, idx).cpu(), g(d["z"]))
+    log("cpu baseline: oracle on", k, "channels x", shape.L, "steps x batch", shape.batch,
+        "with", threads, "threads")
+    t0 = time.perf_counter()
+    oracle.scan_threaded(*args, threads=threads, complex_state=shape.complex_state)
+    dt = time.perf_counter() - t0
+    elems = shape.batch * shape.L * k
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{k} of {shape.d_inner} channels over all {shape.L} steps x batch "
+                      f"{shape.batch} ({elems} elements, {dt:.1f} s wall), fp64 sequential loop "
+                      f"per channel, channels split over {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_context_256k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path is built and measured on a single "
+              f"MI355X (asked for --gpus {args.gpus}); sharding is described in DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_49_amd as ssm
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ssm.load_library()
+    shape = workloads.WORKLOADS[args.workload]
+    is_decode = isinstance(shape, workloads.DecodeShape)
+    steps = max(1, args.steps if not is_decode else min(args.steps, 64))
+    if is_decode:
+        info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads)
+    else:
+        info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads)
+
+    elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
+    dom_s = info["dominant_ms"] / 1e3
+    hbm_ach = info["bytes_per_step"] / dom_s / 1e9
+    alu_ach = info["elements_per_step"] * info["lane_ops_per_elem"] / dom_s / 1e12
+    hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
+    traffic = traffic_for(info, args.workload)
+    if hbm_frac >= alu_frac:
+        roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_frac, 4)}
+    else:
+        roof = {"bound": "alu", "achieved": round(alu_ach, 2), "peak": round(VALU_PEAK_TLANE, 2),
+                "unit": "T VALU lane-op/s", "frac": round(alu_frac, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = info["kernel"]
+    roof["kernel_ms"] = round(info["dominant_ms"] if not is_decode else info["per_call_ms"], 4)
+    roof["hbm_view"] = {"achieved_GBps": round(hbm_ach, 1), "peak_GBps": HBM_PEAK_GBS,
+                        "frac": round(hbm_frac, 4)}
+    roof["alu_view"] = {"achieved_Tlane_op_s": round(alu_ach, 2),
+                        "peak_Tlane_op_s": round(VALU_PEAK_TLANE, 2), "frac": round(alu_frac, 4),
+                        "lane_ops_per_elem": info["lane_ops_per_elem"]}
+    if is_decode:
+        cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
+               "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
+               "calls_per_step": shape.n_layers}
+    else:
+        cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L,
+               "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
+               "complex_state": shape.complex_state, "gated": shape.gated,
+               "chunk_len": info["chunk_len"], "n_chunks": info["n_chunks"]}
+    out = {
+        "metric": METRIC, "value": round(elems_s, 1), "unit": "elements/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(info["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded, resident in HBM before timing)", "config": cfg,
+        "achieved_hbm_GBps_whole_step": round(info["bytes_per_step"] / (info["ms_per_step"] / 1e3) / 1e9, 1),
+        "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline and not is_decode:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,10 @@
  * take A = -a + i*theta per (d, n), so Abar is a decay times a data-dependent
  * rotation (Mamba-3 item on complex-valued state updates, same pt page), and
  * output y = Re(sum_n C[n] h[n]) + D x, then the optional gate.
- * dt is taken after softplus (the MambaBlock applies softplus before its scan).
+ * dt is taken after softplus (the MambaBlock applies softplus before its scan), so
+ * dt >= 0 is part of the input contract; with dt >= 0 and Re A < 0 the decay of
+ * the state only grows with distance in time, which the chunked prefill uses (see
+ * ssm_scan_fwd). Negative dt is outside the contract.
  *
  * Conventions (all entry points)
  * ------------------------------
@@ -28,8 +31,10 @@
  *  - io selects the element type of x, dt, z, B, C and y: SSM_F32 (float) or
  *    SSM_BF16 (bfloat16, stored as 16 bits; y is rounded to nearest even).
  *    A, D and every state (h, h0, h_final) are always float32.
- *  - Alignment: A, h, h0 and h_final 16 bytes; B, C and the workspace 256 bytes
- *    for the workspace and 4 bytes for B, C; x, dt, z, y element-aligned.
+ *  - Alignment: A, h, h0 and h_final 16 bytes; the workspace 256 bytes; B and C
+ *    4 bytes for prefill (their rows are read as 32-bit words: with bf16 and an
+ *    odd number of elements the last word is read whole) and element-aligned for
+ *    decode; D 4 bytes; x, dt, z, y element-aligned.
  *  - d_state must be 1, 2, 4, 8 or 16.
  *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream) and
  *    runs asynchronously; the call returns once it is enqueued.
@@ -74,7 +79,10 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * from zero and its total decay are combined across chunks by an associative
  * scan, and each chunk is then re-walked from its true incoming state. This is an
  * exact re-association of the recurrence; results differ from a sequential fp32
- * loop only by rounding. workspace must hold ssm_scan_fwd_workspace(...) bytes
+ * loop only by rounding. A chunk's end state is accumulated only over its last
+ * steps back to the point where the decay exp(A * sum of dt) of every state of 64
+ * neighbouring channels is below 2^-160: anything older reaches the end state
+ * scaled below the smallest fp32 subnormal, i.e. by exactly zero in fp32. workspace must hold ssm_scan_fwd_workspace(...) bytes
  * (0 is possible, then workspace may be NULL). It is scratch: contents on entry
  * are ignored and on return are unspecified. L == 0 writes h_final = h0 (or
  * zeros) and nothing else. */
@@ -157,6 +165,29 @@ ssm_status ssm_step_c64_replay(float *h, const void *x_t, const void *dt_t, cons
                                const void *z_t, void *y_t, int64_t n_layers, int64_t n_seq,
                                int64_t d_inner, int32_t d_state, ssm_dtype io,
                                void *hip_stream);
+
+/* ------------------------------------------------------------------ profiling
+ * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64, which additionally
+ * records four caller-created HIP events (hipEvent_t, passed as void*) on
+ * hip_stream: events[0] before the chunk-summary kernel, events[1] after it,
+ * events[2] after the carry-scan kernel, events[3] after the rescan kernel. With a
+ * single chunk the first two phases launch nothing and their events are recorded
+ * back to back. No work is skipped. n_events must be 4 (else SSM_ERR_NULL). For
+ * benchmarks that time the kernels from inside the library's stream order. */
+ssm_status ssm_scan_fwd_profiled(const void *x, const void *dt, const float *A, const void *B,
+                                 const void *C, const float *D, const void *z, const float *h0,
+                                 void *y, float *h_final,
+                                 int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                 ssm_dtype io, int64_t chunk_len, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream,
+                                 void *const *events, int32_t n_events);
+ssm_status ssm_scan_fwd_c64_profiled(const void *x, const void *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const void *z, const float *h0, void *y, float *h_final,
+                                     int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                     ssm_dtype io, int64_t chunk_len, void *workspace,
+                                     size_t workspace_bytes, void *hip_stream,
+                                     void *const *events, int32_t n_events);
 
 /* ------------------------------------------------------------------ misc */
 const char *ssm_status_str(ssm_status s);   /* static string, never NULL */

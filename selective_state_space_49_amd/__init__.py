@@ -21,6 +21,7 @@ __all__ = [
     "ssm_scan_fwd_workspace_ex", "ssm_scan_fwd_c64_workspace", "ssm_scan_fwd_chunk_len",
     "ssm_step", "ssm_step_replay", "ssm_step_c64", "ssm_step_c64_replay",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version", "EXPORTED_SYMBOLS",
+    "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,7 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_workspace_ex", "ssm_scan_fwd_c64_workspace", "ssm_scan_fwd_chunk_len",
     "ssm_step", "ssm_step_replay", "ssm_step_c64", "ssm_step_c64_replay",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
+    "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
 ]
 
 
@@ -68,6 +70,8 @@ def load_library():
         "ssm_scan_fwd": (scan + [vp, sz, vp], ci),
         "ssm_scan_fwd_ex": (scan + [i64, vp, sz, vp], ci),
         "ssm_scan_fwd_c64": (scan + [i64, vp, sz, vp], ci),
+        "ssm_scan_fwd_profiled": (scan + [i64, vp, sz, vp, vp, i32], ci),
+        "ssm_scan_fwd_c64_profiled": (scan + [i64, vp, sz, vp, vp, i32], ci),
         "ssm_status_str": ([ci], ctypes.c_char_p),
         "ssm_last_error": ([], ctypes.c_char_p),
         "ssm_abi_version": ([], i32),
@@ -151,7 +155,8 @@ def ssm_scan_fwd_chunk_len(batch, L, d_inner, d_state) -> int:
 
 
 # ------------------------------------------------------------------ prefill
-def _scan(fn_name, cplx, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final, workspace, want_h_final):
+def _scan(fn_name, cplx, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final, workspace, want_h_final,
+          events=None):
     lib = load_library()
     b, L, Dn = x.shape
     N = A.shape[1]
@@ -179,6 +184,10 @@ def _scan(fn_name, cplx, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final, worksp
             _ptr(h_final), b, L, Dn, N, io]
     if fn_name == "ssm_scan_fwd":
         st = lib.ssm_scan_fwd(*args, _ptr(workspace), ws_bytes, _stream(x))
+    elif events is not None:
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) for e in events])
+        st = getattr(lib, fn_name)(*args, chunk_len, _ptr(workspace), ws_bytes, _stream(x),
+                                   handles, len(events))
     else:
         st = getattr(lib, fn_name)(*args, chunk_len, _ptr(workspace), ws_bytes, _stream(x))
     _check(st)
@@ -204,6 +213,21 @@ def ssm_scan_fwd_c64(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None,
     """Complex-state prefill: A [d_inner, d_state, 2]; B, C [b, L, d_state, 2]."""
     return _scan("ssm_scan_fwd_c64", True, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final,
                  workspace, want_h_final)
+
+
+def ssm_scan_fwd_profiled(x, dt, A, B, C, D, z=None, h0=None, *, events, chunk_len=0, y=None,
+                          h_final=None, workspace=None, want_h_final=True, complex_state=False):
+    """Prefill that records 4 HIP events (raw hipEvent_t handles as ints) at the
+    kernel boundaries on the current stream; see ssm_scan.h."""
+    if len(events) != 4:
+        raise ValueError("need exactly 4 event handles")
+    name = "ssm_scan_fwd_c64_profiled" if complex_state else "ssm_scan_fwd_profiled"
+    return _scan(name, complex_state, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final, workspace,
+                 want_h_final, events=list(events))
+
+
+def ssm_scan_fwd_c64_profiled(*a, **k):
+    return ssm_scan_fwd_profiled(*a, complex_state=True, **k)
 
 
 # ------------------------------------------------------------------ decode

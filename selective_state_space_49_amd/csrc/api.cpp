@@ -87,7 +87,8 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
                        const float *D, const void *z, const float *h0, void *y, float *h_final,
                        int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
                        int64_t chunk_len, void *workspace, size_t workspace_bytes,
-                       void *hip_stream, bool cplx) {
+                       void *hip_stream, bool cplx, void *const *events = nullptr,
+                       int32_t n_events = 0) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     Plan plan;
     ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan);
@@ -100,6 +101,10 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         !aligned(B, 4) || !aligned(C, 4) || !aligned(A, 16) || !aligned(D, 4) ||
         !aligned(h0, 16) || !aligned(h_final, 16))
         return fail(SSM_ERR_ALIGN, "pointer alignment (A, h0, h_final 16 B; B, C, D 4 B; x, dt, z, y element)");
+    if (events && n_events != 4) return fail(SSM_ERR_NULL, "profiling needs exactly 4 events");
+    if (events)
+        for (int i = 0; i < 4; ++i)
+            if (!events[i]) return fail(SSM_ERR_NULL, "profiling event %d is NULL", i);
     hipStream_t s = (hipStream_t)hip_stream;
     const int64_t state_floats = batch * d_inner * d_state * (cplx ? 2 : 1);
     if (!work) {
@@ -123,8 +128,9 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     a.threads = (int32_t)std::min<int64_t>(256, (d_inner + 63) / 64 * 64);
     a.dblocks = (int32_t)((d_inner + a.threads - 1) / a.threads);
     const int iot = io == SSM_BF16 ? 1 : 0;
-    hipError_t e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s)
-                        : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s);
+    hipEvent_t const *ev = (hipEvent_t const *)events;
+    hipError_t e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s, ev)
+                        : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s, ev);
     return launch_status(e, "scan launch");
 }
 
@@ -207,6 +213,29 @@ ssm_status ssm_scan_fwd_c64(const void *x, const void *dt, const float *A, const
                             size_t workspace_bytes, void *hip_stream) {
     return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
                        chunk_len, workspace, workspace_bytes, hip_stream, true);
+}
+
+ssm_status ssm_scan_fwd_profiled(const void *x, const void *dt, const float *A, const void *B,
+                                 const void *C, const float *D, const void *z, const float *h0,
+                                 void *y, float *h_final, int64_t batch, int64_t L,
+                                 int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                 int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream, void *const *events, int32_t n_events) {
+    if (!events) return fail(SSM_ERR_NULL, "events are required");
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, events, n_events);
+}
+
+ssm_status ssm_scan_fwd_c64_profiled(const void *x, const void *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const void *z, const float *h0, void *y, float *h_final,
+                                     int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                     ssm_dtype io, int64_t chunk_len, void *workspace,
+                                     size_t workspace_bytes, void *hip_stream,
+                                     void *const *events, int32_t n_events) {
+    if (!events) return fail(SSM_ERR_NULL, "events are required");
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, true, events, n_events);
 }
 
 ssm_status ssm_step(float *h, const void *x_t, const void *dt_t, const float *A, const void *B_t,

@@ -38,6 +38,14 @@ __device__ __forceinline__ void decay_rotation(float dv, float are2, float arev,
     pi = mag * sin_rev(r);
 }
 
+// Decay horizon as in the real-state summary: the rotation has modulus one, so only
+// the real part of A decays. Once log2e * Re A[n] * (sum of dt over the window) <=
+// -kHorizon for every state of every lane, earlier steps reach the chunk's end state
+// scaled by less than 2^-160 (zero in fp32), and the chunk's total transfer factor
+// has modulus below 2^-160 (zero in fp32).
+constexpr float kHorizon = 160.0f;
+constexpr int kB = 16;
+
 template <typename IO, int N>
 __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
     const LaneId ln = lane_id(a);
@@ -45,23 +53,46 @@ __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
     const int c = blockIdx.y;
     const int64_t t0 = (int64_t)c * a.T;
     const int64_t t1 = t0 + a.T;
+    const int64_t Dn = a.Dn;
+    const uint32_t off = (uint32_t)ln.d;
     float Ar2[N], Arev[N], hr[N], hi[N];
+    float amax = -INFINITY;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         Ar2[n] = a.A[(ln.d * N + n) * 2 + 0] * kLog2e;
         Arev[n] = a.A[(ln.d * N + n) * 2 + 1] * kInv2Pi;
+        amax = fmaxf(amax, Ar2[n]);
         hr[n] = 0.0f;
         hi[n] = 0.0f;
     }
-    const int64_t base = (ln.b * a.L + t0) * a.Dn + ln.d;
-    const IO *xp = (const IO *)a.x + base;
-    const IO *dp = (const IO *)a.dt + base;
+    const int64_t row0 = (ln.b * a.L + t0) * Dn;
+    const IO *dr = (const IO *)a.dt + row0;
+    int64_t ts = t0;
+    {
+        float S = 0.0f;
+        for (int64_t tb = t1; tb > t0; tb -= kB) {
+            const int cnt = (int)min<int64_t>(kB, tb - t0);
+            float v[kB];
+#pragma unroll
+            for (int k = 0; k < kB; ++k)
+                if (k < cnt) v[k] = Io<IO>::ld(dr + (tb - t0 - 1 - k) * Dn + off);
+#pragma unroll
+            for (int k = 0; k < kB; ++k)
+                if (k < cnt) S += v[k];
+            if (__all(amax * S <= -kHorizon)) {
+                ts = tb - cnt;
+                break;
+            }
+        }
+    }
+    const IO *xp = (const IO *)a.x + row0 + (ts - t0) * Dn + off;
+    const IO *dp = dr + (ts - t0) * Dn + off;
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N * 2;
     double S = 0.0;
-    for (int64_t t = t0; t < t1; ++t) {
+    for (int64_t t = ts; t < t1; ++t) {
         const float xv = Io<IO>::ld(xp), dv = Io<IO>::ld(dp);
-        xp += a.Dn;
-        dp += a.Dn;
+        xp += Dn;
+        dp += Dn;
         const float u = dv * xv;
         S += (double)dv;
 #pragma unroll
@@ -79,13 +110,18 @@ __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
     const size_t o = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N * 2;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        // total decay and rotation of the chunk: exp(S * A); the angle in double
-        const double aim = (double)a.A[(ln.d * N + n) * 2 + 1];
-        const double rev = aim * kInv2PiD * S;
-        const float r = (float)(rev - floor(rev));
-        const float mag = e2(Ar2[n] * (float)S);
-        a.sumP[o + 2 * n + 0] = mag * cos_rev(r);
-        a.sumP[o + 2 * n + 1] = mag * sin_rev(r);
+        float pr = 0.0f, pi = 0.0f;
+        if (ts == t0) {
+            // total decay and rotation of the chunk: exp(S * A); the angle in double
+            const double aim = (double)a.A[(ln.d * N + n) * 2 + 1];
+            const double rev = aim * kInv2PiD * S;
+            const float r = (float)(rev - floor(rev));
+            const float mag = e2(Ar2[n] * (float)S);
+            pr = mag * cos_rev(r);
+            pi = mag * sin_rev(r);
+        }
+        a.sumP[o + 2 * n + 0] = pr;
+        a.sumP[o + 2 * n + 1] = pi;
         a.sumH[o + 2 * n + 0] = hr[n];
         a.sumH[o + 2 * n + 1] = hi[n];
     }
@@ -231,39 +267,50 @@ __global__ __launch_bounds__(256) void k_chunk_scan_c(ScanArgs a) {
     }
 }
 
+inline void mark(hipEvent_t const *ev, int i, hipStream_t s) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+}
+
 template <typename IO, int N>
-hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s) {
+hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s, hipEvent_t const *ev) {
     const dim3 blk(a.threads);
     const unsigned gx = (unsigned)(a.batch * a.dblocks);
-    if (a.n_chunks > 1) {
+    mark(ev, 0, s);
+    if (a.n_chunks > 1)
         hipLaunchKernelGGL((k_chunk_summary_c<IO, N>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+    mark(ev, 1, s);
+    if (a.n_chunks > 1) {
         const int64_t M = a.batch * a.Dn * N;
         hipLaunchKernelGGL(k_carry_c, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
     }
+    mark(ev, 2, s);
     if (gated)
         hipLaunchKernelGGL((k_chunk_scan_c<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
     else
         hipLaunchKernelGGL((k_chunk_scan_c<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    mark(ev, 3, s);
     return hipGetLastError();
 }
 
 template <typename IO>
-hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s) {
+hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
+                     hipEvent_t const *ev) {
     switch (d_state) {
-        case 1: return launch_t<IO, 1>(a, gated, s);
-        case 2: return launch_t<IO, 2>(a, gated, s);
-        case 4: return launch_t<IO, 4>(a, gated, s);
-        case 8: return launch_t<IO, 8>(a, gated, s);
-        case 16: return launch_t<IO, 16>(a, gated, s);
+        case 1: return launch_t<IO, 1>(a, gated, s, ev);
+        case 2: return launch_t<IO, 2>(a, gated, s, ev);
+        case 4: return launch_t<IO, 4>(a, gated, s, ev);
+        case 8: return launch_t<IO, 8>(a, gated, s, ev);
+        case 16: return launch_t<IO, 16>(a, gated, s, ev);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s) {
-    return io == 0 ? launch_io<float>(a, d_state, gated, s)
-                   : launch_io<bf16_bits>(a, d_state, gated, s);
+hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev) {
+    return io == 0 ? launch_io<float>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits>(a, d_state, gated, s, ev);
 }
 
 }  // namespace ssm

@@ -10,7 +10,8 @@
 // B_t and C_t are wave-uniform and come in through scalar loads. The sequence is cut
 // into chunks of T steps so that there are enough waves to fill 256 CUs:
 //   1. k_chunk_summary: for every chunk but the last, the end state from a zero
-//      start, H_c, and the chunk's total decay P_c = exp(A * sum of dt over the chunk).
+//      start, H_c, and the chunk's total decay P_c = exp(A * sum of dt over the chunk),
+//      walking only the steps that can still reach the chunk's end (decay horizon).
 //   2. k_carry: per state column, an exclusive associative scan over chunks with
 //      (P1, H1) then (P2, H2) = (P2 P1, P2 H1 + H2), seeded with h0. Lanes hold
 //      chunks; the prefix uses DPP row shifts and row broadcasts; a block walks
@@ -39,45 +40,6 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
     r.b = (int64_t)blockIdx.x / a.dblocks;
     r.d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
     return r;
-}
-
-template <typename IO, int N>
-__global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
-    const LaneId ln = lane_id(a);
-    if (ln.d >= a.Dn) return;
-    const int c = blockIdx.y;
-    const int64_t t0 = (int64_t)c * a.T;
-    const int64_t t1 = t0 + a.T;  // every chunk that has a summary is full length
-    float A2[N], h[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[ln.d * N + n] * kLog2e;
-        h[n] = 0.0f;
-    }
-    const int64_t base = (ln.b * a.L + t0) * a.Dn + ln.d;
-    const IO *xp = (const IO *)a.x + base;
-    const IO *dp = (const IO *)a.dt + base;
-    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
-    double S = 0.0;  // sum of dt over the chunk, in double so long chunks keep it exact to fp32
-    for (int64_t t = t0; t < t1; ++t) {
-        const float xv = Io<IO>::ld(xp), dv = Io<IO>::ld(dp);
-        xp += a.Dn;
-        dp += a.Dn;
-        const float u = dv * xv;
-        S += (double)dv;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float bn = Uniform<IO>::ld(Bp, t * N + n);
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
-        }
-    }
-    const float Sf = (float)S;
-    const size_t o = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N;
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-        a.sumP[o + n] = e2(A2[n] * Sf);
-        a.sumH[o + n] = h[n];
-    }
 }
 
 // ---------------------------------------------------------------- carry scan
@@ -147,8 +109,8 @@ __global__ __launch_bounds__(256) void k_carry(ScanArgs a, int64_t M) {
     }
 }
 
-// ---------------------------------------------------------------- rescan + epilogue
-// Steps are processed in blocks of kU. The x, dt, z values of the next block are
+// ---------------------------------------------------------------- streaming steps
+// Steps are visited in blocks of kU. The x, dt (and z) values of the next block are
 // loaded into registers while the current block is computed (ping-pong buffers),
 // so the HBM latency of one block hides behind the arithmetic of the previous one.
 // Row pointers are wave-uniform (SGPR) and each lane adds its 32-bit channel
@@ -173,37 +135,122 @@ __device__ __forceinline__ void load_block(StepIn &s, const IO *xr, const IO *dr
     }
 }
 
-// One time step of one channel: state update, y = C.h + D x, gate, store.
-template <typename IO, int N, bool GATED>
-__device__ __forceinline__ void scan_step(float xv, float dv, float zv, float (&h)[N],
-                                          const float (&A2)[N], float Dd, const IO *Bp,
-                                          const IO *Cp, int64_t t, IO *yp) {
-    const float u = dv * xv;
-    float acc = 0.0f;
+// Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1, rows xr + i*Dn (and dr, zr).
+template <typename IO, bool GATED, typename Body>
+__device__ __forceinline__ void stream_steps(const IO *xr, const IO *dr, const IO *zr, int64_t Dn,
+                                             uint32_t off, int64_t steps, Body &&body) {
+    const int64_t full = steps / kU;
+    const int64_t stride = kU * Dn;
+    int64_t i = 0;
+    StepIn bufA, bufB;
+    if (full > 0) load_block<IO, GATED>(bufA, xr, dr, zr, Dn, off);
+    for (int64_t k = 0; k < full; k += 2) {
+        // block k is in bufA: fetch block k+1 into bufB, then compute block k
+        if (k + 1 < full)
+            load_block<IO, GATED>(bufB, xr + stride, dr + stride, GATED ? zr + stride : nullptr, Dn, off);
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(i + j, bufA.x[j], bufA.dt[j], GATED ? bufA.z[j] : 0.0f);
+        }
+        i += kU; xr += stride; dr += stride;
+        if (GATED) zr += stride;
+        if (k + 1 >= full) break;
+        // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
+        if (k + 2 < full)
+            load_block<IO, GATED>(bufA, xr + stride, dr + stride, GATED ? zr + stride : nullptr, Dn, off);
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(i + j, bufB.x[j], bufB.dt[j], GATED ? bufB.z[j] : 0.0f);
+        }
+        i += kU; xr += stride; dr += stride;
+        if (GATED) zr += stride;
+    }
+    for (; i < steps; ++i) {  // ragged tail, one step at a time
+        const float xv = Io<IO>::ld(xr + off), dv = Io<IO>::ld(dr + off);
+        const float zv = GATED ? Io<IO>::ld(zr + off) : 0.0f;
+        body(i, xv, dv, zv);
+        xr += Dn; dr += Dn;
+        if (GATED) zr += Dn;
+    }
+}
+
+// ---------------------------------------------------------------- chunk summary
+// Decay horizon. With dt >= 0 and A < 0 the weight of step s in the end state of a
+// chunk is 2^(A log2e * sum of dt after s), which only shrinks going back in time.
+// Once log2e * A[n] * (sum of dt over the last steps) <= -kHorizon for every state of
+// every lane of the wave, everything before that window reaches the chunk's end
+// state multiplied by less than 2^-160: below the smallest fp32 subnormal (2^-149),
+// i.e. exactly zero in fp32. The summary then walks only that window, and the
+// chunk's total decay exp(A * sum dt) is also below 2^-160, so 0. A wave with a
+// state that never decays (A >= 0), dt = 0 or NaN never reaches the horizon and
+// walks the whole chunk. The window search reads dt backwards in blocks of kB.
+constexpr float kHorizon = 160.0f;
+constexpr int kB = 16;
+
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
+    const LaneId ln = lane_id(a);
+    if (ln.d >= a.Dn) return;
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const int64_t t1 = t0 + a.T;  // every chunk that has a summary is full length
+    const int64_t Dn = a.Dn;
+    const uint32_t off = (uint32_t)ln.d;
+    float A2[N], h[N];
+    float amax = -INFINITY;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        const float bn = Uniform<IO>::ld(Bp, t * N + n);
-        const float cn = Uniform<IO>::ld(Cp, t * N + n);
-        h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
-        acc = __builtin_fmaf(cn, h[n], acc);
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        amax = fmaxf(amax, A2[n]);
+        h[n] = 0.0f;
     }
-    float yv = __builtin_fmaf(Dd, xv, acc);
-    if (GATED) yv = yv * silu(zv);
-    Io<IO>::st(yp, yv);
-}
-
-template <typename IO, int N, bool GATED>
-__device__ __forceinline__ void scan_block(const StepIn &s, float (&h)[N], const float (&A2)[N],
-                                           float Dd, const IO *Bp, const IO *Cp, int64_t t,
-                                           IO *yr, int64_t Dn, uint32_t off) {
+    const int64_t row0 = (ln.b * a.L + t0) * Dn;
+    const IO *dr = (const IO *)a.dt + row0;
+    // 1. window start ts: walk dt backwards from the chunk end
+    int64_t ts = t0;
+    {
+        float S = 0.0f;
+        for (int64_t tb = t1; tb > t0; tb -= kB) {
+            const int cnt = (int)min<int64_t>(kB, tb - t0);
+            float v[kB];
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        __builtin_amdgcn_sched_barrier(0);
-        scan_step<IO, N, GATED>(s.x[k], s.dt[k], GATED ? s.z[k] : 0.0f, h, A2, Dd, Bp, Cp, t + k,
-                                yr + k * Dn + off);
+            for (int k = 0; k < kB; ++k)
+                if (k < cnt) v[k] = Io<IO>::ld(dr + (tb - t0 - 1 - k) * Dn + off);
+#pragma unroll
+            for (int k = 0; k < kB; ++k)
+                if (k < cnt) S += v[k];
+            if (__all(amax * S <= -kHorizon)) {
+                ts = tb - cnt;
+                break;
+            }
+        }
+    }
+    // 2. end state from zero over [ts, t1)
+    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
+    double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
+    stream_steps<IO, false>((const IO *)a.x + row0 + (ts - t0) * Dn, dr + (ts - t0) * Dn, nullptr,
+                            Dn, off, t1 - ts, [&](int64_t i, float xv, float dv, float) {
+        const int64_t t = ts + i;
+        const float u = dv * xv;
+        S += (double)dv;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float bn = Uniform<IO>::ld(Bp, t * N + n);
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+        }
+    });
+    const float Sf = (float)S;
+    const size_t o = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a.sumP[o + n] = ts == t0 ? e2(A2[n] * Sf) : 0.0f;
+        a.sumH[o + n] = h[n];
     }
 }
 
+// ---------------------------------------------------------------- rescan + epilogue
 template <typename IO, int N, bool GATED>
 __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     const LaneId ln = lane_id(a);
@@ -223,44 +270,27 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     const float Dd = a.D[ln.d];
     const int64_t Dn = a.Dn;
     const uint32_t off = (uint32_t)ln.d;
-    // Wave-uniform pointers to row t0 of this batch row.
     const int64_t row0 = (ln.b * a.L + t0) * Dn;
-    const IO *xr = (const IO *)a.x + row0;
-    const IO *dr = (const IO *)a.dt + row0;
-    const IO *zr = GATED ? (const IO *)a.z + row0 : nullptr;
     IO *yr = (IO *)a.y + row0;
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
-    const int64_t full = (t1 - t0) / kU;  // whole blocks
-    const int64_t stride = kU * Dn;
-    int64_t t = t0;
-    StepIn bufA, bufB;
-    if (full > 0) load_block<IO, GATED>(bufA, xr, dr, zr, Dn, off);
-    for (int64_t k = 0; k < full; k += 2) {
-        // block k is in bufA: fetch block k+1 into bufB, then compute block k
-        if (k + 1 < full)
-            load_block<IO, GATED>(bufB, xr + stride, dr + stride, GATED ? zr + stride : nullptr,
-                                  Dn, off);
-        scan_block<IO, N, GATED>(bufA, h, A2, Dd, Bp, Cp, t, yr, Dn, off);
-        t += kU; xr += stride; dr += stride; yr += stride;
-        if (GATED) zr += stride;
-        if (k + 1 >= full) break;
-        // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
-        if (k + 2 < full)
-            load_block<IO, GATED>(bufA, xr + stride, dr + stride, GATED ? zr + stride : nullptr,
-                                  Dn, off);
-        scan_block<IO, N, GATED>(bufB, h, A2, Dd, Bp, Cp, t, yr, Dn, off);
-        t += kU; xr += stride; dr += stride; yr += stride;
-        if (GATED) zr += stride;
-    }
-    // ragged tail: fewer than kU steps, one at a time
-    for (; t < t1; ++t) {
-        const float xv = Io<IO>::ld(xr + off), dv = Io<IO>::ld(dr + off);
-        const float zv = GATED ? Io<IO>::ld(zr + off) : 0.0f;
-        scan_step<IO, N, GATED>(xv, dv, zv, h, A2, Dd, Bp, Cp, t, yr + off);
-        xr += Dn; dr += Dn; yr += Dn;
-        if (GATED) zr += Dn;
-    }
+    stream_steps<IO, GATED>((const IO *)a.x + row0, (const IO *)a.dt + row0,
+                            GATED ? (const IO *)a.z + row0 : nullptr, Dn, off, t1 - t0,
+                            [&](int64_t i, float xv, float dv, float zv) {
+        const int64_t t = t0 + i;
+        const float u = dv * xv;
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float bn = Uniform<IO>::ld(Bp, t * N + n);
+            const float cn = Uniform<IO>::ld(Cp, t * N + n);
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+            acc = __builtin_fmaf(cn, h[n], acc);
+        }
+        float yv = __builtin_fmaf(Dd, xv, acc);
+        if (GATED) yv = yv * silu(zv);
+        Io<IO>::st(yr + i * Dn + off, yv);
+    });
     if (c == a.n_chunks - 1 && a.h_final) {
 #pragma unroll
         for (int n = 0; n < N; ++n) a.h_final[col + n] = h[n];
@@ -272,39 +302,50 @@ __global__ void k_state_fill(float *dst, const float *src, int64_t count) {
     if (i < count) dst[i] = src ? src[i] : 0.0f;
 }
 
+inline void mark(hipEvent_t const *ev, int i, hipStream_t s) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+}
+
 template <typename IO, int N>
-hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s) {
+hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s, hipEvent_t const *ev) {
     const dim3 blk(a.threads);
     const unsigned gx = (unsigned)(a.batch * a.dblocks);
-    if (a.n_chunks > 1) {
+    mark(ev, 0, s);
+    if (a.n_chunks > 1)
         hipLaunchKernelGGL((k_chunk_summary<IO, N>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+    mark(ev, 1, s);
+    if (a.n_chunks > 1) {
         const int64_t M = a.batch * a.Dn * N;
         hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
     }
+    mark(ev, 2, s);
     if (gated)
         hipLaunchKernelGGL((k_chunk_scan<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
     else
         hipLaunchKernelGGL((k_chunk_scan<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    mark(ev, 3, s);
     return hipGetLastError();
 }
 
 template <typename IO>
-hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s) {
+hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
+                     hipEvent_t const *ev) {
     switch (d_state) {
-        case 1: return launch_t<IO, 1>(a, gated, s);
-        case 2: return launch_t<IO, 2>(a, gated, s);
-        case 4: return launch_t<IO, 4>(a, gated, s);
-        case 8: return launch_t<IO, 8>(a, gated, s);
-        case 16: return launch_t<IO, 16>(a, gated, s);
+        case 1: return launch_t<IO, 1>(a, gated, s, ev);
+        case 2: return launch_t<IO, 2>(a, gated, s, ev);
+        case 4: return launch_t<IO, 4>(a, gated, s, ev);
+        case 8: return launch_t<IO, 8>(a, gated, s, ev);
+        case 16: return launch_t<IO, 16>(a, gated, s, ev);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s) {
-    return io == 0 ? launch_io<float>(a, d_state, gated, s)
-                   : launch_io<bf16_bits>(a, d_state, gated, s);
+hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev) {
+    return io == 0 ? launch_io<float>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits>(a, d_state, gated, s, ev);
 }
 
 hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStream_t s) {

@@ -32,8 +32,13 @@ struct StepArgs {
 };
 
 // Real diagonal state. io: 0 = f32, 1 = bf16. Returns hipSuccess or the launch error.
-hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s);
-hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s);
+// ev: NULL, or 4 events recorded on s before the summary kernel, after it, after the
+// carry kernel and after the rescan kernel (phases that do not run leave two
+// consecutive records).
+hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev);
+hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                               hipEvent_t const *ev);
 hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStream_t s);
 
 hipError_t launch_step_real(const StepArgs &a, int io, int d_state, bool gated, bool replay,

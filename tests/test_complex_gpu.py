@@ -75,3 +75,26 @@ def test_pure_rotation_impulse_response():
                                     C.cuda(), torch.zeros(1, device="cuda"), chunk_len=64)
         ref = torch.cos(theta[n].double() * torch.arange(L, dtype=torch.float64))
         assert rel_err(y, ref.view(1, L, 1).numpy()) <= 1e-4
+
+
+@pytest.mark.parametrize("variant", ["slow_decay", "frozen_states", "fast_decay"])
+def test_complex_decay_horizon_edge_cases(variant):
+    shape = ScanShape("hc", 1, 2000, 70, 16, "f32", complex_state=True, gated=False, seed=63)
+    inp = make_scan_inputs(shape, "cpu")
+    if variant == "slow_decay":
+        inp["A"][..., 0] = inp["A"][..., 0] * 1e-3
+    elif variant == "frozen_states":
+        inp["A"][5, :, 0] = 0.0                          # a pure rotation channel
+        inp["A"][66, 2, 0] = 0.0
+    elif variant == "fast_decay":
+        inp["dt"] = inp["dt"] * 20.0
+    h0 = make_h0(1, 70, 16, complex_state=True, seed=64)
+    d = to_dev(inp)
+    say("complex horizon", variant)
+    y, hf = ssm.ssm_scan_fwd_c64(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], h0.cuda(),
+                                 chunk_len=300)
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_complex(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                 inp["z"], h0)
+    assert rel_err(y, yr) <= TOL["f32"], f"y error {rel_err(y, yr)}"
+    assert rel_err(hf, hr) <= TOL["f32"], f"h_final error {rel_err(hf, hr)}"

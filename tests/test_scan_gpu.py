@@ -201,3 +201,29 @@ def test_state_size_does_not_depend_on_length():
         _, hf = ssm.ssm_scan_fwd(x, x, -torch.ones((64, 16), device="cuda"), B, B,
                                  torch.ones(64, device="cuda"))
         assert hf.shape == (1, 64, 16)
+
+
+@pytest.mark.parametrize("variant", ["slow_decay", "frozen_states", "fast_decay", "dt_zero_block"])
+def test_decay_horizon_edge_cases(variant):
+    # The chunk summaries walk back only to the point where every state of a wave has
+    # decayed below 2^-160; these inputs make that point come early, late or never.
+    shape = ScanShape("h", 1, 3000, 130, 16, "f32", seed=61)
+    inp = make_scan_inputs(shape, "cpu")
+    if variant == "slow_decay":
+        inp["A"] = inp["A"] * 1e-3                      # never within one chunk
+    elif variant == "frozen_states":
+        inp["A"][5] = 0.0                                # one channel never decays
+        inp["A"][70, 3] = 0.0                            # one state of another wave
+    elif variant == "fast_decay":
+        inp["dt"] = inp["dt"] * 20.0                     # horizon within a few steps
+    elif variant == "dt_zero_block":
+        inp["dt"][:, 400:1400] = 0.0                     # no decay across a whole chunk
+    h0 = make_h0(1, 130, 16, seed=62)
+    d = to_dev(inp)
+    say("horizon", variant)
+    y, hf = ssm.ssm_scan_fwd_ex(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], h0.cuda(),
+                                chunk_len=500)
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0)
+    assert rel_err(y, yr) <= TOL["f32"], f"y error {rel_err(y, yr)}"
+    assert rel_err(hf, hr) <= TOL["f32"], f"h_final error {rel_err(hf, hr)}"
