@@ -92,7 +92,7 @@ def decode_bytes(s, io_bytes: int) -> float:
 
 
 # ----------------------------------------------------------------- runs
-def run_prefill(shape, steps, warmup, torch, ssm, workloads):
+def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     dev = "cuda"
     log("drawing inputs for", shape.name)
     d = workloads.make_scan_inputs(shape, dev)
@@ -100,9 +100,9 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads):
     cplx = shape.complex_state
     y = torch.empty_like(d["x"])
     hf = torch.empty((b, Dn, N) + ((2,) if cplx else ()), dtype=torch.float32, device=dev)
-    T = ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N)
-    ws_n = (ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, 0) if cplx
-            else ssm.ssm_scan_fwd_workspace(b, L, Dn, N))
+    T = chunk_len or ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N)
+    ws_n = (ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, T) if cplx
+            else ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, N, T))
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     fn = ssm.ssm_scan_fwd_c64_profiled if cplx else ssm.ssm_scan_fwd_profiled
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -116,7 +116,7 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads):
 
     def call(events):
         fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None, y=y, h_final=hf,
-           workspace=ws, events=[e.cuda_event for e in events])
+           workspace=ws, chunk_len=T, events=[e.cuda_event for e in events])
 
     log("warmup", warmup)
     for _ in range(warmup):
@@ -236,6 +236,8 @@ def main():
     ap.add_argument("--workload", default="long_context_256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--chunk-len", type=int, default=0,
+                    help="prefill chunk length (0 = the library's own plan)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path is built and measured on a single "
@@ -255,7 +257,7 @@ def main():
     if is_decode:
         info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads)
     else:
-        info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads)
+        info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
 
     elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
     dom_s = info["dominant_ms"] / 1e3

@@ -79,10 +79,13 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * from zero and its total decay are combined across chunks by an associative
  * scan, and each chunk is then re-walked from its true incoming state. This is an
  * exact re-association of the recurrence; results differ from a sequential fp32
- * loop only by rounding. A chunk's end state is accumulated only over its last
- * steps back to the point where the decay exp(A * sum of dt) of every state of 64
- * neighbouring channels is below 2^-160: anything older reaches the end state
- * scaled below the smallest fp32 subnormal, i.e. by exactly zero in fp32. workspace must hold ssm_scan_fwd_workspace(...) bytes
+ * loop only by rounding and by one bounded truncation: a chunk's end state is
+ * accumulated only over its last steps back to the point where the decay
+ * exp(Re A * sum of dt) of every state of 64 neighbouring channels is below 2^-64.
+ * What is dropped changes a carried state by at most 2^-64 * (chunk_len *
+ * max|dt x B| + |incoming state|), about 2^-44 of the input scale, far below fp32
+ * resolution. NaN or Inf older than that window do not propagate past the chunk
+ * boundary. workspace must hold ssm_scan_fwd_workspace(...) bytes
  * (0 is possible, then workspace may be NULL). It is scratch: contents on entry
  * are ignored and on return are unspecified. L == 0 writes h_final = h0 (or
  * zeros) and nothing else. */
@@ -97,7 +100,9 @@ ssm_status ssm_scan_fwd(const void *x, const void *dt, const float *A, const voi
 
 /* Same, with an explicit chunk length (steps per chunk; 0 = the library's own
  * choice, which is what ssm_scan_fwd uses). chunk_len >= L gives one chunk and
- * needs no workspace. Results for different chunk lengths agree within rounding. */
+ * needs no workspace. The chunk length is capped so that one chunk spans less than
+ * 2 GiB of a [L, d_inner] stream at 4 bytes per element. Results for different
+ * chunk lengths agree within rounding. */
 size_t ssm_scan_fwd_workspace_ex(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
                                  int64_t chunk_len);
 ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const void *B,

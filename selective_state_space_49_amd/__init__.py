@@ -25,7 +25,8 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+# SSMSCAN_LIBRARY may point at another build of the same library (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("SSMSCAN_LIBRARY") or os.path.join(_HERE, "libssmscan.so")
 _lib = None
 
 SSM_F32, SSM_BF16 = 0, 1

@@ -35,9 +35,9 @@ def _hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON]
+def _compile(src: str, verbose: bool, objdir: str, defines) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON, *[f"-D{d}" for d in defines]]
     if src.endswith(".hip"):
         cmd += DEVICE
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -49,20 +49,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libssmscan.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link libssmscan.so; returns the library path.
+
+    out and defines (NAME=VALUE strings, e.g. build-time tuning knobs) allow
+    building variants elsewhere; the default is the package's own library.
+    """
+    objdir = OBJDIR if out == LIB else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), HIP_SOURCES + CPP_SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, objdir, defines), HIP_SOURCES + CPP_SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libssmscan.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

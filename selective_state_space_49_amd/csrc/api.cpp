@@ -66,8 +66,12 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
     const double elems = (double)batch * (double)L * (double)d_inner;
     if (elems > 4.0e18 || (double)batch * d_inner > 2.0e9)
         return fail(SSM_ERR_SHAPE, "problem too large");
-    const int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
-                                    : auto_chunk_len(batch, L, d_inner);
+    // A chunk spans less than 2 GiB of every [rows][d_inner] stream (4-byte elements
+    // at most), so the kernels address a chunk with 32-bit byte offsets.
+    const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 31) / (d_inner * 4) - 1);
+    int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
+                              : auto_chunk_len(batch, L, d_inner);
+    T = std::min(T, cap);
     const int64_t n_chunks = L > 0 ? (L + T - 1) / T : 1;
     if (n_chunks > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n_chunks, (long long)kMaxChunks);
     p->T = T;

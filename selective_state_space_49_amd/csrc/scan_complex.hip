@@ -14,6 +14,7 @@
 // argument from fract().
 #include "ssm_device.h"
 #include "ssm_internal.h"
+#include "ssm_stream.h"
 
 namespace ssm {
 namespace {
@@ -38,14 +39,8 @@ __device__ __forceinline__ void decay_rotation(float dv, float are2, float arev,
     pi = mag * sin_rev(r);
 }
 
-// Decay horizon as in the real-state summary: the rotation has modulus one, so only
-// the real part of A decays. Once log2e * Re A[n] * (sum of dt over the window) <=
-// -kHorizon for every state of every lane, earlier steps reach the chunk's end state
-// scaled by less than 2^-160 (zero in fp32), and the chunk's total transfer factor
-// has modulus below 2^-160 (zero in fp32).
-constexpr float kHorizon = 160.0f;
-constexpr int kB = 16;
-
+// Chunk summary as in the real-state scan. The rotation has modulus one, so only the
+// real part of A decays and the decay horizon is computed from Re A.
 template <typename IO, int N>
 __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
     const LaneId ln = lane_id(a);
@@ -54,7 +49,6 @@ __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
     const int64_t t0 = (int64_t)c * a.T;
     const int64_t t1 = t0 + a.T;
     const int64_t Dn = a.Dn;
-    const uint32_t off = (uint32_t)ln.d;
     float Ar2[N], Arev[N], hr[N], hi[N];
     float amax = -INFINITY;
 #pragma unroll
@@ -66,33 +60,17 @@ __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
         hi[n] = 0.0f;
     }
     const int64_t row0 = (ln.b * a.L + t0) * Dn;
-    const IO *dr = (const IO *)a.dt + row0;
-    int64_t ts = t0;
-    {
-        float S = 0.0f;
-        for (int64_t tb = t1; tb > t0; tb -= kB) {
-            const int cnt = (int)min<int64_t>(kB, tb - t0);
-            float v[kB];
-#pragma unroll
-            for (int k = 0; k < kB; ++k)
-                if (k < cnt) v[k] = Io<IO>::ld(dr + (tb - t0 - 1 - k) * Dn + off);
-#pragma unroll
-            for (int k = 0; k < kB; ++k)
-                if (k < cnt) S += v[k];
-            if (__all(amax * S <= -kHorizon)) {
-                ts = tb - cnt;
-                break;
-            }
-        }
-    }
-    const IO *xp = (const IO *)a.x + row0 + (ts - t0) * Dn + off;
-    const IO *dp = dr + (ts - t0) * Dn + off;
+    const uint32_t T = (uint32_t)a.T;
+    const uint32_t rb = (uint32_t)(Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
+    const RowStream<IO> dts((const IO *)a.dt + row0);
+    const uint32_t ts = horizon_start<IO>(dts, voff, rb, T, amax);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N * 2;
+    const int64_t rw = row0 + (int64_t)ts * Dn;
+    const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;
-    for (int64_t t = ts; t < t1; ++t) {
-        const float xv = Io<IO>::ld(xp), dv = Io<IO>::ld(dp);
-        xp += Dn;
-        dp += Dn;
+    stream_steps<IO, false>(xs, dws, dws, voff, rb, T - ts, [&](uint32_t i, float xv, float dv, float) {
+        const int64_t t = t0 + ts + i;
         const float u = dv * xv;
         S += (double)dv;
 #pragma unroll
@@ -106,12 +84,12 @@ __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
             hr[n] = nr;
             hi[n] = ni;
         }
-    }
+    });
     const size_t o = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N * 2;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         float pr = 0.0f, pi = 0.0f;
-        if (ts == t0) {
+        if (ts == 0) {
             // total decay and rotation of the chunk: exp(S * A); the angle in double
             const double aim = (double)a.A[(ln.d * N + n) * 2 + 1];
             const double rev = aim * kInv2PiD * S;
@@ -221,18 +199,16 @@ __global__ __launch_bounds__(256) void k_chunk_scan_c(ScanArgs a) {
         hi[n] = hin ? hin[2 * n + 1] : 0.0f;
     }
     const float Dd = a.D[ln.d];
-    const int64_t Dn = a.Dn;
-    const uint32_t off = (uint32_t)ln.d;
-    const int64_t row0 = (ln.b * a.L + t0) * Dn;
-    const IO *xr = (const IO *)a.x + row0;
-    const IO *dr = (const IO *)a.dt + row0;
-    const IO *zr = GATED ? (const IO *)a.z + row0 : nullptr;
-    IO *yr = (IO *)a.y + row0;
+    const uint32_t rb = (uint32_t)(a.Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
+    const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
+    const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
+        zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N * 2;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N * 2;
-    for (int64_t t = t0; t < t1; ++t) {
-        const float xv = Io<IO>::ld(xr + off), dv = Io<IO>::ld(dr + off);
-        const float zv = GATED ? Io<IO>::ld(zr + off) : 0.0f;
+    stream_steps<IO, GATED>(xs, dts, zs, voff, rb, (uint32_t)(t1 - t0),
+                            [&](uint32_t i, float xv, float dv, float zv) {
+        const int64_t t = t0 + i;
         const float u = dv * xv;
         float acc = 0.0f;
 #pragma unroll
@@ -252,12 +228,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan_c(ScanArgs a) {
         }
         float yv = __builtin_fmaf(Dd, xv, acc);
         if (GATED) yv = yv * silu(zv);
-        Io<IO>::st(yr + off, yv);
-        xr += Dn;
-        dr += Dn;
-        yr += Dn;
-        if (GATED) zr += Dn;
-    }
+        ys.st(voff, i * rb, yv);
+    });
     if (c == a.n_chunks - 1 && a.h_final) {
 #pragma unroll
         for (int n = 0; n < N; ++n) {

@@ -27,6 +27,7 @@
 // exponential, one multiply (dt x times B) and two fused multiply-adds.
 #include "ssm_device.h"
 #include "ssm_internal.h"
+#include "ssm_stream.h"
 
 namespace ssm {
 namespace {
@@ -109,95 +110,18 @@ __global__ __launch_bounds__(256) void k_carry(ScanArgs a, int64_t M) {
     }
 }
 
-// ---------------------------------------------------------------- streaming steps
-// Steps are visited in blocks of kU. The x, dt (and z) values of the next block are
-// loaded into registers while the current block is computed (ping-pong buffers),
-// so the HBM latency of one block hides behind the arithmetic of the previous one.
-// Row pointers are wave-uniform (SGPR) and each lane adds its 32-bit channel
-// offset, which gives the scalar-base + vector-offset load form and no per-step
-// vector address arithmetic. A scheduling barrier between steps keeps each step's
-// scalar B/C loads next to their use instead of hoisting a whole block's worth of
-// them into SGPRs.
-constexpr int kU = 4;
-
-struct StepIn {
-    float x[kU], dt[kU], z[kU];
-};
-
-template <typename IO, bool GATED>
-__device__ __forceinline__ void load_block(StepIn &s, const IO *xr, const IO *dr, const IO *zr,
-                                           int64_t Dn, uint32_t off) {
-#pragma unroll
-    for (int k = 0; k < kU; ++k) {
-        s.x[k] = Io<IO>::ld(xr + k * Dn + off);
-        s.dt[k] = Io<IO>::ld(dr + k * Dn + off);
-        if (GATED) s.z[k] = Io<IO>::ld(zr + k * Dn + off);
-    }
-}
-
-// Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1, rows xr + i*Dn (and dr, zr).
-template <typename IO, bool GATED, typename Body>
-__device__ __forceinline__ void stream_steps(const IO *xr, const IO *dr, const IO *zr, int64_t Dn,
-                                             uint32_t off, int64_t steps, Body &&body) {
-    const int64_t full = steps / kU;
-    const int64_t stride = kU * Dn;
-    int64_t i = 0;
-    StepIn bufA, bufB;
-    if (full > 0) load_block<IO, GATED>(bufA, xr, dr, zr, Dn, off);
-    for (int64_t k = 0; k < full; k += 2) {
-        // block k is in bufA: fetch block k+1 into bufB, then compute block k
-        if (k + 1 < full)
-            load_block<IO, GATED>(bufB, xr + stride, dr + stride, GATED ? zr + stride : nullptr, Dn, off);
-#pragma unroll
-        for (int j = 0; j < kU; ++j) {
-            __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufA.x[j], bufA.dt[j], GATED ? bufA.z[j] : 0.0f);
-        }
-        i += kU; xr += stride; dr += stride;
-        if (GATED) zr += stride;
-        if (k + 1 >= full) break;
-        // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
-        if (k + 2 < full)
-            load_block<IO, GATED>(bufA, xr + stride, dr + stride, GATED ? zr + stride : nullptr, Dn, off);
-#pragma unroll
-        for (int j = 0; j < kU; ++j) {
-            __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufB.x[j], bufB.dt[j], GATED ? bufB.z[j] : 0.0f);
-        }
-        i += kU; xr += stride; dr += stride;
-        if (GATED) zr += stride;
-    }
-    for (; i < steps; ++i) {  // ragged tail, one step at a time
-        const float xv = Io<IO>::ld(xr + off), dv = Io<IO>::ld(dr + off);
-        const float zv = GATED ? Io<IO>::ld(zr + off) : 0.0f;
-        body(i, xv, dv, zv);
-        xr += Dn; dr += Dn;
-        if (GATED) zr += Dn;
-    }
-}
-
 // ---------------------------------------------------------------- chunk summary
-// Decay horizon. With dt >= 0 and A < 0 the weight of step s in the end state of a
-// chunk is 2^(A log2e * sum of dt after s), which only shrinks going back in time.
-// Once log2e * A[n] * (sum of dt over the last steps) <= -kHorizon for every state of
-// every lane of the wave, everything before that window reaches the chunk's end
-// state multiplied by less than 2^-160: below the smallest fp32 subnormal (2^-149),
-// i.e. exactly zero in fp32. The summary then walks only that window, and the
-// chunk's total decay exp(A * sum dt) is also below 2^-160, so 0. A wave with a
-// state that never decays (A >= 0), dt = 0 or NaN never reaches the horizon and
-// walks the whole chunk. The window search reads dt backwards in blocks of kB.
-constexpr float kHorizon = 160.0f;
-constexpr int kB = 16;
-
+// Chunk summary: end state from a zero start and total decay, walking only the
+// window back to the decay horizon (see horizon_start).
 template <typename IO, int N>
 __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const LaneId ln = lane_id(a);
     if (ln.d >= a.Dn) return;
     const int c = blockIdx.y;
     const int64_t t0 = (int64_t)c * a.T;
-    const int64_t t1 = t0 + a.T;  // every chunk that has a summary is full length
-    const int64_t Dn = a.Dn;
-    const uint32_t off = (uint32_t)ln.d;
+    const uint32_t T = (uint32_t)a.T;  // every chunk that has a summary is full length
+    const uint32_t rb = (uint32_t)(a.Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
     float A2[N], h[N];
     float amax = -INFINITY;
 #pragma unroll
@@ -206,33 +130,17 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
         amax = fmaxf(amax, A2[n]);
         h[n] = 0.0f;
     }
-    const int64_t row0 = (ln.b * a.L + t0) * Dn;
-    const IO *dr = (const IO *)a.dt + row0;
-    // 1. window start ts: walk dt backwards from the chunk end
-    int64_t ts = t0;
-    {
-        float S = 0.0f;
-        for (int64_t tb = t1; tb > t0; tb -= kB) {
-            const int cnt = (int)min<int64_t>(kB, tb - t0);
-            float v[kB];
-#pragma unroll
-            for (int k = 0; k < kB; ++k)
-                if (k < cnt) v[k] = Io<IO>::ld(dr + (tb - t0 - 1 - k) * Dn + off);
-#pragma unroll
-            for (int k = 0; k < kB; ++k)
-                if (k < cnt) S += v[k];
-            if (__all(amax * S <= -kHorizon)) {
-                ts = tb - cnt;
-                break;
-            }
-        }
-    }
-    // 2. end state from zero over [ts, t1)
+    const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
+    const RowStream<IO> dts((const IO *)a.dt + row0);
+    // 1. window start ts (chunk-relative): walk dt backwards from the chunk end
+    const uint32_t ts = horizon_start<IO>(dts, voff, rb, T, amax);
+    // 2. end state from zero over rows [ts, T) of the chunk
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
+    const int64_t rw = row0 + (int64_t)ts * a.Dn;
+    const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
-    stream_steps<IO, false>((const IO *)a.x + row0 + (ts - t0) * Dn, dr + (ts - t0) * Dn, nullptr,
-                            Dn, off, t1 - ts, [&](int64_t i, float xv, float dv, float) {
-        const int64_t t = ts + i;
+    stream_steps<IO, false>(xs, dws, dws, voff, rb, T - ts, [&](uint32_t i, float xv, float dv, float) {
+        const int64_t t = t0 + ts + i;
         const float u = dv * xv;
         S += (double)dv;
 #pragma unroll
@@ -245,19 +153,30 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const size_t o = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        a.sumP[o + n] = ts == t0 ? e2(A2[n] * Sf) : 0.0f;
+        a.sumP[o + n] = ts == 0 ? e2(A2[n] * Sf) : 0.0f;
         a.sumH[o + n] = h[n];
     }
 }
 
 // ---------------------------------------------------------------- rescan + epilogue
+// Occupancy request for the rescan kernel (waves per SIMD; 0 = the compiler's own
+// register allocation). A build-time tuning knob.
+#ifndef SSM_RESCAN_WAVES_PER_EU
+#define SSM_RESCAN_WAVES_PER_EU 0
+#endif
+#if SSM_RESCAN_WAVES_PER_EU > 0
+#define SSM_RESCAN_OCC __attribute__((amdgpu_waves_per_eu(SSM_RESCAN_WAVES_PER_EU)))
+#else
+#define SSM_RESCAN_OCC
+#endif
+
 template <typename IO, int N, bool GATED>
-__global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
+__global__ __launch_bounds__(256) SSM_RESCAN_OCC void k_chunk_scan(ScanArgs a) {
     const LaneId ln = lane_id(a);
     if (ln.d >= a.Dn) return;
     const int c = blockIdx.y;
     const int64_t t0 = (int64_t)c * a.T;
-    const int64_t t1 = min(a.L, t0 + a.T);
+    const uint32_t steps = (uint32_t)(min(a.L, t0 + a.T) - t0);
     const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
     const float *hin = c == 0 ? (a.h0 ? a.h0 + col : nullptr)
                               : a.sumH + (size_t)(c - 1) * a.batch * a.Dn * N + col;
@@ -268,15 +187,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         h[n] = hin ? hin[n] : 0.0f;
     }
     const float Dd = a.D[ln.d];
-    const int64_t Dn = a.Dn;
-    const uint32_t off = (uint32_t)ln.d;
-    const int64_t row0 = (ln.b * a.L + t0) * Dn;
-    IO *yr = (IO *)a.y + row0;
+    const uint32_t rb = (uint32_t)(a.Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
+    const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
+    const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
+        zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
-    stream_steps<IO, GATED>((const IO *)a.x + row0, (const IO *)a.dt + row0,
-                            GATED ? (const IO *)a.z + row0 : nullptr, Dn, off, t1 - t0,
-                            [&](int64_t i, float xv, float dv, float zv) {
+    stream_steps<IO, GATED>(xs, dts, zs, voff, rb, steps, [&](uint32_t i, float xv, float dv, float zv) {
         const int64_t t = t0 + i;
         const float u = dv * xv;
         float acc = 0.0f;
@@ -289,7 +207,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         }
         float yv = __builtin_fmaf(Dd, xv, acc);
         if (GATED) yv = yv * silu(zv);
-        Io<IO>::st(yr + i * Dn + off, yv);
+        ys.st(voff, i * rb, yv);
     });
     if (c == a.n_chunks - 1 && a.h_final) {
 #pragma unroll

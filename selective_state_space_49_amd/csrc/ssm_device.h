@@ -39,6 +39,19 @@ template <> struct Io<bf16_bits> {
     static __device__ __forceinline__ void st(bf16_bits *p, float v) { *p = f32_to_bf16(v); }
 };
 
+// Element at a wave-uniform row pointer plus a per-lane 32-bit byte offset. Keeping
+// the lane part a zero-extended 32-bit value lets the compiler use the global
+// load/store form with a scalar 64-bit base and a vector 32-bit offset, so walking
+// rows costs scalar adds only.
+template <typename IO>
+__device__ __forceinline__ float ld_row(const IO *row, uint32_t byte_off) {
+    return Io<IO>::ld((const IO *)((const char *)row + byte_off));
+}
+template <typename IO>
+__device__ __forceinline__ void st_row(IO *row, uint32_t byte_off, float v) {
+    Io<IO>::st((IO *)((char *)row + byte_off), v);
+}
+
 // Element e (wave-uniform) of a float / bf16 array through the scalar path.
 template <typename IO> struct Uniform;
 template <> struct Uniform<float> {

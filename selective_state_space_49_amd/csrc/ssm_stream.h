@@ -1,0 +1,164 @@
+// ssm_stream.h -- walking [rows][Dn] arrays row by row in the prefill kernels.
+//
+// Each stream (x, dt, z, y) is addressed through a buffer resource based at the
+// first row of the chunk: the lane's byte offset sits in a VGPR for the whole
+// kernel and the row's byte offset is a wave-uniform SGPR, so a load or store is
+// one buffer instruction with no vector address arithmetic. A chunk spans less
+// than 2 GiB of any stream (the planner guarantees it), so 32-bit offsets suffice.
+// The resource's record count is the maximum; the kernels keep every access in
+// bounds by construction.
+#pragma once
+
+#include "ssm_device.h"
+
+namespace ssm {
+
+// Word 3 of a gfx9-family buffer resource (raw byte addressing, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <typename IO> struct RowStream;
+
+template <> struct RowStream<bf16_bits> {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit RowStream(const void *base)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, kRsrcWord3)) {}
+    __device__ __forceinline__ float ld(uint32_t voff, uint32_t soff) const {
+        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+    }
+    // The element's raw bits, to be widened later with widen().
+    __device__ __forceinline__ uint32_t ldraw(uint32_t voff, uint32_t soff) const {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float widen(uint32_t raw) { return bf16_to_f32(raw); }
+    __device__ __forceinline__ void st(uint32_t voff, uint32_t soff, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, soff, 0);
+    }
+};
+
+template <> struct RowStream<float> {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit RowStream(const void *base)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, kRsrcWord3)) {}
+    __device__ __forceinline__ float ld(uint32_t voff, uint32_t soff) const {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    __device__ __forceinline__ uint32_t ldraw(uint32_t voff, uint32_t soff) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw); }
+    __device__ __forceinline__ void st(uint32_t voff, uint32_t soff, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+};
+
+// Steps are visited in blocks of kU. The x, dt (and z) values of the next block are
+// loaded into registers while the current block is computed (ping-pong buffers), so
+// the HBM latency of one block hides behind the arithmetic of the previous one. A
+// scheduling barrier between steps keeps each step's scalar B/C loads next to their
+// use instead of hoisting a whole block's worth of them into SGPRs.
+// Steps per prefetch block (a build-time tuning knob).
+#ifndef SSM_STEP_BLOCK
+#define SSM_STEP_BLOCK 4
+#endif
+constexpr int kU = SSM_STEP_BLOCK;
+
+struct StepIn {
+    float x[kU], dt[kU], z[kU];
+};
+
+template <typename IO, bool GATED>
+__device__ __forceinline__ void load_block(StepIn &s, const RowStream<IO> &x,
+                                           const RowStream<IO> &dt, const RowStream<IO> &z,
+                                           uint32_t voff, uint32_t row, uint32_t rb) {
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        s.x[k] = x.ld(voff, (row + k) * rb);
+        s.dt[k] = dt.ld(voff, (row + k) * rb);
+        if (GATED) s.z[k] = z.ld(voff, (row + k) * rb);
+    }
+}
+
+// Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1 (rows of the streams); voff is
+// the lane's byte offset in a row and rb the bytes per row.
+template <typename IO, bool GATED, typename Body>
+__device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowStream<IO> &dt,
+                                             const RowStream<IO> &z, uint32_t voff, uint32_t rb,
+                                             uint32_t steps, Body &&body) {
+    const uint32_t full = steps / kU;
+    uint32_t i = 0;
+    StepIn bufA, bufB;
+    if (full > 0) load_block<IO, GATED>(bufA, x, dt, z, voff, 0, rb);
+    for (uint32_t k = 0; k < full; k += 2) {
+        // block k is in bufA: fetch block k+1 into bufB, then compute block k
+        if (k + 1 < full) load_block<IO, GATED>(bufB, x, dt, z, voff, i + kU, rb);
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(i + j, bufA.x[j], bufA.dt[j], GATED ? bufA.z[j] : 0.0f);
+        }
+        i += kU;
+        if (k + 1 >= full) break;
+        // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
+        if (k + 2 < full) load_block<IO, GATED>(bufA, x, dt, z, voff, i + kU, rb);
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(i + j, bufB.x[j], bufB.dt[j], GATED ? bufB.z[j] : 0.0f);
+        }
+        i += kU;
+    }
+    for (; i < steps; ++i) {  // ragged tail, one step at a time
+        const float xv = x.ld(voff, i * rb), dv = dt.ld(voff, i * rb);
+        const float zv = GATED ? z.ld(voff, i * rb) : 0.0f;
+        body(i, xv, dv, zv);
+    }
+}
+
+// ---------------------------------------------------------------- decay horizon
+// The end state of a chunk from a zero start is sum_s W_s[n] dt_s x_s B_s[n] with
+// W_s[n] = exp(A[n] * sum of dt after s). With dt >= 0 and Re A < 0 the weights only
+// shrink going back in time. Once log2(e) * Re A[n] * (sum of dt over the last rows)
+// <= -kHorizon for every state of every lane of a wave, everything older enters the
+// end state with weight below 2^-kHorizon. Dropping it changes a carried state by at
+// most 2^-64 * T * max|dt x B| (about 2^-44 of the input scale for T < 2^20): far
+// below fp32 resolution. The chunk's total transfer factor exp(A * sum dt) is then
+// below 2^-64 in modulus and is dropped the same way.
+constexpr float kHorizon = 64.0f;
+constexpr int kB = 32;  // rows per block of the backward walk
+
+// First row (chunk-relative) of the window that covers the horizon, walking dt back
+// from row T-1 in whole blocks of kB rows; the next block is loaded while the
+// current one is summed, and every load of a block is issued before any is waited
+// on. amax = max over the lane's states of log2(e) * Re A. Returns 0 (the whole
+// chunk) when some lane does not reach the horizon within the whole blocks (A >= 0,
+// dt = 0, NaN, or simply a short chunk).
+template <typename IO>
+__device__ __forceinline__ uint32_t horizon_start(const RowStream<IO> &dt, uint32_t voff,
+                                                  uint32_t rb, uint32_t T, float amax) {
+    if (!__any(amax < 0.0f) || T < (uint32_t)kB) return 0;
+    float S = 0.0f;
+    float cur[kB];
+    uint32_t nxt[kB];
+    uint32_t tb = T;
+#pragma unroll
+    for (int k = 0; k < kB; ++k) cur[k] = dt.ld(voff, (tb - 1 - k) * rb);
+    while (true) {
+        const uint32_t tn = tb - kB;  // rows [tn, tb) are in cur
+        const bool more = tn >= (uint32_t)kB;
+        if (more) {
+#pragma unroll
+            for (int k = 0; k < kB; ++k) nxt[k] = dt.ldraw(voff, (tn - 1 - k) * rb);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // sum the current block while nxt is in flight
+#pragma unroll
+        for (int k = 0; k < kB; ++k) S += cur[k];
+        if (__all(amax * S <= -kHorizon)) return tn;
+        if (!more) return 0;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kB; ++k) cur[k] = RowStream<IO>::widen(nxt[k]);
+        tb = tn;
+    }
+}
+
+}  // namespace ssm
