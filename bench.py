@@ -55,7 +55,8 @@ def log(*a):
 
 def source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[kind], "selective_state_space_49_amd/csrc/ssm_device.h"):
+    for rel in (KERNEL_SOURCES[kind], "selective_state_space_49_amd/csrc/ssm_device.h",
+                "selective_state_space_49_amd/csrc/ssm_stream.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -238,6 +239,9 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--chunk-len", type=int, default=0,
                     help="prefill chunk length (0 = the library's own plan)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB three times (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path is built and measured on a single "
@@ -250,6 +254,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
+        return
     ssm.load_library()
     shape = workloads.WORKLOADS[args.workload]
     is_decode = isinstance(shape, workloads.DecodeShape)

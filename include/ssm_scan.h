@@ -33,8 +33,9 @@
  *    A, D and every state (h, h0, h_final) are always float32.
  *  - Alignment: A, h, h0 and h_final 16 bytes; the workspace 256 bytes; B and C
  *    4 bytes for prefill (their rows are read as 32-bit words: with bf16 and an
- *    odd number of elements the last word is read whole) and element-aligned for
- *    decode; D 4 bytes; x, dt, z, y element-aligned.
+ *    odd number of elements the last word is read whole), and for real-state
+ *    decode min(d_state, 4) elements (read as vectors), element-aligned for
+ *    complex decode; D 4 bytes; x, dt, z, y element-aligned.
  *  - d_state must be 1, 2, 4, 8 or 16.
  *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the null stream) and
  *    runs asynchronously; the call returns once it is enqueued.
@@ -124,6 +125,7 @@ int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_
  *   B_t, C_t       : [n_layers, n_seq, d_state] of io
  *   A              : [n_layers, d_inner, d_state] float32;  D: [n_layers, d_inner]
  *   z_t            : NULL = no gate
+ * n_layers and n_seq are at most 65535 each, d_inner at most 2^28.
  * Per channel the fp32 operations are, in this order (fma = fused multiply-add,
  * e2 = the hardware base-2 exponential, G = d_state >= 8 ? d_state / 4 : 1 groups
  * of K = d_state / G states):

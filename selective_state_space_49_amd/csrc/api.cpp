@@ -146,14 +146,18 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     if (n_layers < 0 || n_seq < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "n_layers/n_seq must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
     if ((double)n_layers * n_seq * d_inner * 16.0 > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
-    if ((double)n_layers * n_seq * d_inner * 8.0 / 256.0 > 2.0e9) return fail(SSM_ERR_SHAPE, "too many channels for one launch");
+    if (n_layers > 65535 || n_seq > 65535 || d_inner > ((int64_t)1 << 28))
+        return fail(SSM_ERR_SHAPE, "n_layers and n_seq must be <= 65535, d_inner <= 2^28");
     if (n_layers == 0 || n_seq == 0) return ok();
     if (!h || !x || !dt || !A || !B || !C || !D || !y)
         return fail(SSM_ERR_NULL, "h, x_t, dt_t, A, B_t, C_t, D and y_t are required");
     const size_t eb = io_bytes(io);
+    // B_t and C_t rows are read K values at a time: K = 4 states per lane for
+    // d_state >= 4 (real), else d_state; complex rows are read one value at a time.
+    const size_t bc = cplx ? eb : eb * (size_t)std::min<int32_t>(d_state, 4);
     if (!aligned(h, 16) || !aligned(A, 16) || !aligned(x, eb) || !aligned(dt, eb) ||
-        !aligned(z, eb) || !aligned(y, eb) || !aligned(B, eb) || !aligned(C, eb) || !aligned(D, 4))
-        return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; others element)");
+        !aligned(z, eb) || !aligned(y, eb) || !aligned(B, bc) || !aligned(C, bc) || !aligned(D, 4))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; B_t, C_t min(d_state,4) elements; others element)");
     ssm::StepArgs a;
     a.h = h; a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z; a.A = A; a.D = D; a.y = y;
     a.n_layers = n_layers; a.n_seq = n_seq; a.Dn = d_inner;

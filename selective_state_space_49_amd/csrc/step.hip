@@ -22,19 +22,55 @@
 namespace ssm {
 namespace {
 
-// Channel index ch = (l * n_seq + q) * Dn + d.
+// Grid: x = blocks of 256 threads over (channel, group lane), y = sequence q,
+// z = layer l. Channel index ch = (l * n_seq + q) * Dn + d; lq = l * n_seq + q.
 struct Chan {
-    int64_t ch, l, d, lq;
+    int64_t ch, lq;
+    int64_t l, d;
 };
 
-__device__ __forceinline__ Chan chan_of(const StepArgs &a, int64_t ch) {
-    Chan c;
-    c.ch = ch;
-    c.d = ch % a.Dn;
-    c.lq = ch / a.Dn;
-    c.l = c.lq / a.n_seq;
-    return c;
+template <int G>
+__device__ __forceinline__ bool chan_of(const StepArgs &a, Chan &c, int &g) {
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    c.d = t / G;  // G is a power of two
+    g = (int)(t % G);
+    if (c.d >= a.Dn) return false;
+    c.l = blockIdx.z;
+    c.lq = (int64_t)blockIdx.z * a.n_seq + blockIdx.y;
+    c.ch = c.lq * a.Dn + c.d;
+    return true;
 }
+
+// Vector load of K consecutive elements (K = 1, 2 or 4; 4-byte aligned for K >= 2
+// with bf16 and 8/16-byte aligned for f32, which the layouts guarantee).
+template <typename IO, int K> struct VecLd;
+template <int K> struct VecLd<float, K> {
+    static __device__ __forceinline__ void ld(const float *p, float (&v)[K]) {
+        if constexpr (K == 4) {
+            const float4 q = *(const float4 *)p;
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        } else if constexpr (K == 2) {
+            const float2 q = *(const float2 *)p;
+            v[0] = q.x; v[1] = q.y;
+        } else {
+            v[0] = *p;
+        }
+    }
+};
+template <int K> struct VecLd<bf16_bits, K> {
+    static __device__ __forceinline__ void ld(const bf16_bits *p, float (&v)[K]) {
+        if constexpr (K == 4) {
+            const uint2 q = *(const uint2 *)p;
+            v[0] = bf16_to_f32(q.x & 0xffffu); v[1] = __uint_as_float(q.x & 0xffff0000u);
+            v[2] = bf16_to_f32(q.y & 0xffffu); v[3] = __uint_as_float(q.y & 0xffff0000u);
+        } else if constexpr (K == 2) {
+            const uint32_t q = *(const uint32_t *)p;
+            v[0] = bf16_to_f32(q & 0xffffu); v[1] = __uint_as_float(q & 0xffff0000u);
+        } else {
+            v[0] = bf16_to_f32(*p);
+        }
+    }
+};
 
 template <int G>
 __device__ __forceinline__ float group_sum(float p) {
@@ -64,55 +100,47 @@ template <int N> struct RealGroups {
 template <typename IO, int N, bool GATED>
 __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n_ch = a.n_layers * a.n_seq * a.Dn;
-    const int64_t ch = gid / G;
-    const int g = (int)(gid % G);
-    if (ch >= n_ch) return;  // G divides 64: a group is wholly in or out of range
-    const Chan c = chan_of(a, ch);
-    float *hp = a.h + ch * N + g * K;
-    const float *Ap = a.A + (c.l * a.Dn + c.d) * N + g * K;
-    const IO *Bp = (const IO *)a.B + c.lq * N + g * K;
-    const IO *Cp = (const IO *)a.C + c.lq * N + g * K;
-    float hv[K], av[K];
-    if constexpr (K == 4) {
-        const float4 h4 = *(const float4 *)hp, a4 = *(const float4 *)Ap;
-        hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
-        av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
-    } else {
-#pragma unroll
-        for (int k = 0; k < K; ++k) { hv[k] = hp[k]; av[k] = Ap[k]; }
-    }
-    const float xv = Io<IO>::ld((const IO *)a.x + ch);
-    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    Chan c;
+    int g;
+    if (!chan_of<G>(a, c, g)) return;  // G divides 64: a group is wholly in or out
+    float *hp = a.h + c.ch * N + g * K;
+    float hv[K], av[K], bv[K], cv[K];
+    VecLd<float, K>::ld(hp, hv);
+    VecLd<float, K>::ld(a.A + (c.l * a.Dn + c.d) * N + g * K, av);
+    VecLd<IO, K>::ld((const IO *)a.B + c.lq * N + g * K, bv);
+    VecLd<IO, K>::ld((const IO *)a.C + c.lq * N + g * K, cv);
+    const float xv = Io<IO>::ld((const IO *)a.x + c.ch);
+    const float dv = Io<IO>::ld((const IO *)a.dt + c.ch);
     const float u = dv * xv;
     float p = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const float a2 = av[k] * kLog2e;
-        hv[k] = __builtin_fmaf(e2(dv * a2), hv[k], u * Io<IO>::ld(Bp + k));
-        p = __builtin_fmaf(Io<IO>::ld(Cp + k), hv[k], p);
+        hv[k] = __builtin_fmaf(e2(dv * a2), hv[k], u * bv[k]);
+        p = __builtin_fmaf(cv[k], hv[k], p);
     }
     const float acc = group_sum<G>(p);
     if constexpr (K == 4) {
         *(float4 *)hp = make_float4(hv[0], hv[1], hv[2], hv[3]);
+    } else if constexpr (K == 2) {
+        *(float2 *)hp = make_float2(hv[0], hv[1]);
     } else {
-#pragma unroll
-        for (int k = 0; k < K; ++k) hp[k] = hv[k];
+        hp[0] = hv[0];
     }
     if (g == 0) {
         float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, acc);
-        if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + ch));
-        Io<IO>::st((IO *)a.y + ch, yv);
+        if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + c.ch));
+        Io<IO>::st((IO *)a.y + c.ch, yv);
     }
 }
 
 template <typename IO, int N, bool GATED>
 __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
-    const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (ch >= a.n_layers * a.n_seq * a.Dn) return;
-    const Chan c = chan_of(a, ch);
+    Chan c;
+    int g0;
+    if (!chan_of<1>(a, c, g0)) return;
+    const int64_t ch = c.ch;
     float *hp = a.h + ch * N;
     const float *Ap = a.A + (c.l * a.Dn + c.d) * N;
     const IO *Bp = (const IO *)a.B + c.lq * N;
@@ -156,12 +184,10 @@ __device__ __forceinline__ void cstep(float dv, float u, float are, float aim, f
 template <typename IO, int N, bool GATED>
 __global__ __launch_bounds__(256) void k_step_c(StepArgs a) {
     constexpr int G = CplxGroups<N>::G, K = CplxGroups<N>::K;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n_ch = a.n_layers * a.n_seq * a.Dn;
-    const int64_t ch = gid / G;
-    const int g = (int)(gid % G);
-    if (ch >= n_ch) return;
-    const Chan c = chan_of(a, ch);
+    Chan c;
+    int g;
+    if (!chan_of<G>(a, c, g)) return;
+    const int64_t ch = c.ch;
     float *hp = a.h + (ch * N + g * K) * 2;
     const float *Ap = a.A + ((c.l * a.Dn + c.d) * N + g * K) * 2;
     const IO *Bp = (const IO *)a.B + (c.lq * N + g * K) * 2;
@@ -203,9 +229,10 @@ __global__ __launch_bounds__(256) void k_step_c(StepArgs a) {
 template <typename IO, int N, bool GATED>
 __global__ __launch_bounds__(256) void k_step_c_replay(StepArgs a) {
     constexpr int G = CplxGroups<N>::G, K = CplxGroups<N>::K;
-    const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (ch >= a.n_layers * a.n_seq * a.Dn) return;
-    const Chan c = chan_of(a, ch);
+    Chan c;
+    int g0;
+    if (!chan_of<1>(a, c, g0)) return;
+    const int64_t ch = c.ch;
     float *hp = a.h + ch * N * 2;
     const float *Ap = a.A + (c.l * a.Dn + c.d) * N * 2;
     const IO *Bp = (const IO *)a.B + c.lq * N * 2;
@@ -233,9 +260,9 @@ __global__ __launch_bounds__(256) void k_step_c_replay(StepArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
-inline unsigned grid_for(const StepArgs &a, int lanes_per_ch) {
-    const int64_t threads = a.n_layers * a.n_seq * a.Dn * lanes_per_ch;
-    return (unsigned)((threads + 255) / 256);
+inline dim3 grid_for(const StepArgs &a, int lanes_per_ch) {
+    return dim3((unsigned)((a.Dn * lanes_per_ch + 255) / 256), (unsigned)a.n_seq,
+                (unsigned)a.n_layers);
 }
 
 template <typename IO, int N>
