@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const int64_t rw = row0 + (int64_t)ts * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
-    stream_steps<IO, false>(xs, dws, dws, voff, rb, T - ts, [&](uint32_t i, float xv, float dv, float) {
+    stream_steps<IO, false>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xv, float dv, float) {
         const int64_t t = t0 + ts + i;
         const float u = dv * xv;
         S += (double)dv;
@@ -159,19 +159,8 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------- rescan + epilogue
-// Occupancy request for the rescan kernel (waves per SIMD; 0 = the compiler's own
-// register allocation). A build-time tuning knob.
-#ifndef SSM_RESCAN_WAVES_PER_EU
-#define SSM_RESCAN_WAVES_PER_EU 0
-#endif
-#if SSM_RESCAN_WAVES_PER_EU > 0
-#define SSM_RESCAN_OCC __attribute__((amdgpu_waves_per_eu(SSM_RESCAN_WAVES_PER_EU)))
-#else
-#define SSM_RESCAN_OCC
-#endif
-
 template <typename IO, int N, bool GATED>
-__global__ __launch_bounds__(256) SSM_RESCAN_OCC void k_chunk_scan(ScanArgs a) {
+__global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     const LaneId ln = lane_id(a);
     if (ln.d >= a.Dn) return;
     const int c = blockIdx.y;
@@ -194,7 +183,7 @@ __global__ __launch_bounds__(256) SSM_RESCAN_OCC void k_chunk_scan(ScanArgs a) {
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
-    stream_steps<IO, GATED>(xs, dts, zs, voff, rb, steps, [&](uint32_t i, float xv, float dv, float zv) {
+    stream_steps<IO, GATED>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xv, float dv, float zv) {
         const int64_t t = t0 + i;
         const float u = dv * xv;
         float acc = 0.0f;
