@@ -149,7 +149,7 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     return info, d
 
 
-def run_decode(shape, steps, warmup, torch, ssm, workloads):
+def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True):
     dev = "cuda"
     Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
     par = workloads.make_decode_params(shape, dev)
@@ -177,18 +177,46 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads):
     for k in range(warmup):
         token(k, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(warmup, warmup + steps):
-        token(k, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps * Ln)) / (steps * Ln)
+    if graph:
+        # One captured graph per token: the Ln per-layer calls, bound to that token's
+        # inputs (drawn beforehand), replayed back to back. Capture happens outside the
+        # timed region; the graph holds no memset nodes.
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(warmup, warmup + steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    token(k, False)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        h.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gev[0].record()
+        for g in graphs:
+            g.replay()
+        gev[1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = gev[0].elapsed_time(gev[1]) / (steps * Ln)
+    else:
+        t0 = time.perf_counter()
+        for k in range(warmup, warmup + steps):
+            token(k, True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps * Ln)) / (steps * Ln)
     io_bytes = 2 if shape.io == "bf16" else 4
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3,
         "elements_per_step": Ln * S * Dn, "bytes_per_step": decode_bytes(shape, io_bytes),
         "lane_ops_per_elem": 6 * N + 14, "dominant_ms": kern * Ln, "per_call_ms": kern,
         "kernel": "k_step", "source": "step", "phases_ms": {"ssm_step_per_layer": kern},
+        "graph": graph,
     }
     return info, None
 
@@ -239,6 +267,9 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--chunk-len", type=int, default=0,
                     help="prefill chunk length (0 = the library's own plan)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="decode: launch the per-layer calls eagerly instead of replaying one "
+                         "captured HIP graph per token")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -269,7 +300,7 @@ def main():
     is_decode = isinstance(shape, workloads.DecodeShape)
     steps = max(1, args.steps if not is_decode else min(args.steps, 64))
     if is_decode:
-        info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads)
+        info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph)
     else:
         info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
 
@@ -296,7 +327,7 @@ def main():
     if is_decode:
         cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
-               "calls_per_step": shape.n_layers}
+               "calls_per_step": shape.n_layers, "hip_graph_per_token": info["graph"]}
     else:
         cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary_c(ScanArgs a) {
     const int64_t rw = row0 + (int64_t)ts * Dn;
     const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;
-    stream_steps<IO, false>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xv, float dv, float) {
+    stream_steps<IO, false, 2>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xv, float dv, float) {
         const int64_t t = t0 + ts + i;
         const float u = dv * xv;
         S += (double)dv;
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_c(ScanArgs a) {
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N * 2;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N * 2;
-    stream_steps<IO, GATED>(xs, dts, zs, voff, rb, (uint32_t)(t1 - t0),
+    stream_steps<IO, GATED, 2>(xs, dts, zs, voff, rb, (uint32_t)(t1 - t0),
                             (uint32_t)(t1 - t0), [&](uint32_t i, float xv, float dv, float zv) {
         const int64_t t = t0 + i;
         const float u = dv * xv;

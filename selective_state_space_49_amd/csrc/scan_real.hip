@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const int64_t rw = row0 + (int64_t)ts * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
-    stream_steps<IO, false>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xv, float dv, float) {
+    stream_steps<IO, false, 4>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xv, float dv, float) {
         const int64_t t = t0 + ts + i;
         const float u = dv * xv;
         S += (double)dv;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
-    stream_steps<IO, GATED>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xv, float dv, float zv) {
+    stream_steps<IO, GATED, 4>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xv, float dv, float zv) {
         const int64_t t = t0 + i;
         const float u = dv * xv;
         float acc = 0.0f;

@@ -51,19 +51,16 @@ template <> struct RowStream<float> {
     }
 };
 
-// Steps are visited in blocks of kU. The x, dt (and z) values of the next block are
+// Steps are visited in blocks of KU. The x, dt (and z) values of the next block are
 // loaded into registers while the current block is computed (ping-pong buffers), so
 // the HBM latency of one block hides behind the arithmetic of the previous one. A
 // scheduling barrier between steps keeps each step's scalar B/C loads next to their
-// use instead of hoisting a whole block's worth of them into SGPRs.
-// Steps per prefetch block (a build-time tuning knob).
-#ifndef SSM_STEP_BLOCK
-#define SSM_STEP_BLOCK 4
-#endif
-constexpr int kU = SSM_STEP_BLOCK;
-
+// use instead of hoisting a whole block's worth of them into SGPRs. KU is 4 for the
+// real state and 2 for the complex state, whose larger state would otherwise push
+// the kernel past 128 VGPRs (below four waves per SIMD).
+template <int KU>
 struct StepIn {
-    float x[kU], dt[kU], z[kU];
+    float x[KU], dt[KU], z[KU];
 };
 
 // Issue priority by remaining work. The SIMD arbiter favours the oldest of the waves
@@ -82,12 +79,12 @@ __device__ __forceinline__ void set_priority(uint32_t remaining, uint32_t scale)
     else __builtin_amdgcn_s_setprio(0);
 }
 
-template <typename IO, bool GATED>
-__device__ __forceinline__ void load_block(StepIn &s, const RowStream<IO> &x,
+template <typename IO, bool GATED, int KU>
+__device__ __forceinline__ void load_block(StepIn<KU> &s, const RowStream<IO> &x,
                                            const RowStream<IO> &dt, const RowStream<IO> &z,
                                            uint32_t voff, uint32_t row, uint32_t rb) {
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
+    for (int k = 0; k < KU; ++k) {
         s.x[k] = x.ld(voff, (row + k) * rb);
         s.dt[k] = dt.ld(voff, (row + k) * rb);
         if (GATED) s.z[k] = z.ld(voff, (row + k) * rb);
@@ -97,33 +94,33 @@ __device__ __forceinline__ void load_block(StepIn &s, const RowStream<IO> &x,
 // Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1 (rows of the streams); voff is
 // the lane's byte offset in a row and rb the bytes per row. prio_scale: see
 // set_priority (0 = leave the priority alone).
-template <typename IO, bool GATED, typename Body>
+template <typename IO, bool GATED, int KU, typename Body>
 __device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowStream<IO> &dt,
                                              const RowStream<IO> &z, uint32_t voff, uint32_t rb,
                                              uint32_t steps, uint32_t prio_scale, Body &&body) {
-    const uint32_t full = steps / kU;
+    const uint32_t full = steps / KU;
     uint32_t i = 0;
-    StepIn bufA, bufB;
-    if (full > 0) load_block<IO, GATED>(bufA, x, dt, z, voff, 0, rb);
+    StepIn<KU> bufA, bufB;
+    if (full > 0) load_block<IO, GATED, KU>(bufA, x, dt, z, voff, 0, rb);
     for (uint32_t k = 0; k < full; k += 2) {
         if (prio_scale) set_priority(steps - i, prio_scale);
         // block k is in bufA: fetch block k+1 into bufB, then compute block k
-        if (k + 1 < full) load_block<IO, GATED>(bufB, x, dt, z, voff, i + kU, rb);
+        if (k + 1 < full) load_block<IO, GATED, KU>(bufB, x, dt, z, voff, i + KU, rb);
 #pragma unroll
-        for (int j = 0; j < kU; ++j) {
+        for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
             body(i + j, bufA.x[j], bufA.dt[j], GATED ? bufA.z[j] : 0.0f);
         }
-        i += kU;
+        i += KU;
         if (k + 1 >= full) break;
         // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
-        if (k + 2 < full) load_block<IO, GATED>(bufA, x, dt, z, voff, i + kU, rb);
+        if (k + 2 < full) load_block<IO, GATED, KU>(bufA, x, dt, z, voff, i + KU, rb);
 #pragma unroll
-        for (int j = 0; j < kU; ++j) {
+        for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
             body(i + j, bufB.x[j], bufB.dt[j], GATED ? bufB.z[j] : 0.0f);
         }
-        i += kU;
+        i += KU;
     }
     if (prio_scale) __builtin_amdgcn_s_setprio(0);
     for (; i < steps; ++i) {  // ragged tail, one step at a time

@@ -41,6 +41,19 @@ __device__ __forceinline__ bool chan_of(const StepArgs &a, Chan &c, int &g) {
     return true;
 }
 
+// The state is read once and written once per call: non-temporal (streaming) 16-byte
+// accesses keep it from displacing the reused A, B, C rows in the caches.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void ld_state4(const float *p, float *v) {
+    const f4v q = __builtin_nontemporal_load((const f4v *)p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void st_state4(float *p, const float *v) {
+    f4v q;
+    q.x = v[0]; q.y = v[1]; q.z = v[2]; q.w = v[3];
+    __builtin_nontemporal_store(q, (f4v *)p);
+}
+
 // Vector load of K consecutive elements (K = 1, 2 or 4; 4-byte aligned for K >= 2
 // with bf16 and 8/16-byte aligned for f32, which the layouts guarantee).
 template <typename IO, int K> struct VecLd;
@@ -105,7 +118,8 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     if (!chan_of<G>(a, c, g)) return;  // G divides 64: a group is wholly in or out
     float *hp = a.h + c.ch * N + g * K;
     float hv[K], av[K], bv[K], cv[K];
-    VecLd<float, K>::ld(hp, hv);
+    if constexpr (K == 4) ld_state4(hp, hv);
+    else VecLd<float, K>::ld(hp, hv);
     VecLd<float, K>::ld(a.A + (c.l * a.Dn + c.d) * N + g * K, av);
     VecLd<IO, K>::ld((const IO *)a.B + c.lq * N + g * K, bv);
     VecLd<IO, K>::ld((const IO *)a.C + c.lq * N + g * K, cv);
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     }
     const float acc = group_sum<G>(p);
     if constexpr (K == 4) {
-        *(float4 *)hp = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        st_state4(hp, hv);
     } else if constexpr (K == 2) {
         *(float2 *)hp = make_float2(hv[0], hv[1]);
     } else {
@@ -194,8 +208,8 @@ __global__ __launch_bounds__(256) void k_step_c(StepArgs a) {
     const IO *Cp = (const IO *)a.C + (c.lq * N + g * K) * 2;
     float hv[2 * K], av[2 * K];
     if constexpr (K == 2) {
-        const float4 h4 = *(const float4 *)hp, a4 = *(const float4 *)Ap;
-        hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
+        ld_state4(hp, hv);
+        const float4 a4 = *(const float4 *)Ap;
         av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
     } else {
 #pragma unroll
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256) void k_step_c(StepArgs a) {
     }
     const float acc = group_sum<G>(p);
     if constexpr (K == 2) {
-        *(float4 *)hp = make_float4(hv[0], hv[1], hv[2], hv[3]);
+        st_state4(hp, hv);
     } else {
 #pragma unroll
         for (int k = 0; k < 2 * K; ++k) hp[k] = hv[k];

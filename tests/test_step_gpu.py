@@ -97,3 +97,39 @@ def test_state_survives_a_host_round_trip():
         yb.append(ssm.ssm_step(h_b, s["x"], s["dt"], par["A"], s["B"], s["C"], par["D"], s["z"]))
     torch.cuda.synchronize()
     assert all(bitwise_equal(a, b) for a, b in zip(ya, yb)) and bitwise_equal(h_a, h_b)
+
+
+def test_decode_in_captured_graph_matches_eager():
+    # A captured graph of per-layer ssm_step calls, replayed several times with eager
+    # work and synchronisation between replays: every replay must equal the eager run
+    # bit for bit (the calls enqueue kernels only; no memset nodes).
+    shape = DecodeShape("graph", 3, 4, 192, 16, 1, "bf16", seed=31)
+    par = make_decode_params(shape, "cuda")
+    tok = make_decode_step(shape, 0, "cuda")
+    h0 = torch.randn((3, 4, 192, 16), device="cuda")
+    layers = lambda h, y: [ssm.ssm_step(h[l:l + 1], tok["x"][l:l + 1], tok["dt"][l:l + 1],
+                                        par["A"][l:l + 1], tok["B"][l:l + 1], tok["C"][l:l + 1],
+                                        par["D"][l:l + 1], tok["z"][l:l + 1], y_t=y[l:l + 1])
+                           for l in range(3)]
+    h_e, y_e = h0.clone(), torch.empty_like(tok["x"])
+    layers(h_e, y_e)
+    torch.cuda.synchronize()
+    h_g, y_g = h0.clone(), torch.empty_like(tok["x"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            layers(h_g, y_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say("graph replay", rep)
+        h_g.copy_(h0)
+        y_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bitwise_equal(y_g, y_e) and bitwise_equal(h_g, h_e), f"replay {rep} differs"
+        layers(h0.clone(), torch.empty_like(y_e))   # eager work between replays
+        torch.cuda.synchronize()
