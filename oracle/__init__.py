@@ -59,6 +59,10 @@ def _load():
             f.restype = ctypes.c_int
         lib.oracle_state_bytes.argtypes = [i64, i64, i64, i64]
         lib.oracle_state_bytes.restype = i64
+        lib.oracle_conv_silu_f64.argtypes = [i64, i64, i64, i64] + [dp] * 6
+        lib.oracle_conv_silu_f64.restype = ctypes.c_int
+        lib.oracle_softplus_f64.argtypes = [i64, i64, dp, dp, dp]
+        lib.oracle_softplus_f64.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -157,6 +161,64 @@ def step_complex(h, x, dt, A, B, C, D, z=None):
 def state_bytes(n_layers: int, channels: int, d_state: int, bytes_per_value: int) -> int:
     """Size of a fixed-size SSM state in bytes (independent of sequence length)."""
     return int(_load().oracle_state_bytes(n_layers, channels, d_state, bytes_per_value))
+
+
+def conv_silu(x, w, cb=None, state0=None):
+    """Causal depthwise convolution over time, then silu (the MambaBlock's input stage).
+    x: [b, L, Dn]; w: [Dn, K]; cb: [Dn] or None; state0: [b, K-1, Dn] or None (zeros).
+    Returns (u [b, L, Dn], state_out [b, K-1, Dn] = the last K-1 inputs)."""
+    x, w, cb, state0 = map(to_f64, (x, w, cb, state0))
+    b, L, Dn = x.shape
+    K = w.shape[1]
+    _check(w, (Dn, K), "conv_w")
+    if cb is not None: _check(cb, (Dn,), "conv_b")
+    if state0 is not None: _check(state0, (b, K - 1, Dn), "conv_state0")
+    u = np.empty((b, L, Dn)); so = np.empty((b, K - 1, Dn))
+    if _load().oracle_conv_silu_f64(b, L, Dn, K, _p(x), _p(w), _p(cb), _p(state0), _p(u), _p(so)) != 0:
+        raise RuntimeError("oracle_conv_silu_f64 failed")
+    return u, so
+
+
+def softplus(raw, bias=None):
+    """softplus(raw + bias) with bias [Dn] broadcast over the leading dimensions."""
+    raw, bias = to_f64(raw), to_f64(bias)
+    Dn = raw.shape[-1]
+    if bias is not None: _check(bias, (Dn,), "dt_bias")
+    out = np.empty(raw.shape)
+    rows = raw.size // Dn if Dn else 0
+    if _load().oracle_softplus_f64(rows, Dn, _p(raw), _p(bias), _p(out)) != 0:
+        raise RuntimeError("oracle_softplus_f64 failed")
+    return out
+
+
+def scan_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, conv_w=None, conv_b=None,
+               conv_state0=None, dt_bias=None):
+    """The MambaBlock's input stage followed by the real-state scan:
+    u = silu(causal conv(x_in)), dt = softplus(dt_raw + dt_bias), then scan(u, dt, ...).
+    Returns (y, h_final, conv_state_out)."""
+    u, so = conv_silu(x_in, conv_w, conv_b, conv_state0)
+    y, hf = scan(u, softplus(dt_raw, dt_bias), A, B, C, D, z, h0)
+    return y, hf, so
+
+
+def step_fused(h, conv_state, x_in, dt_raw, A, B, C, D, z=None, conv_w=None, conv_b=None,
+               dt_bias=None):
+    """One decode token through the input stage and the scan, per layer:
+    conv_state [Ln, S, K-1, Dn]; conv_w [Ln, Dn, K]; conv_b, dt_bias [Ln, Dn] or None.
+    Returns (y, h_new, conv_state_new) without touching the inputs."""
+    x_in, dt_raw, conv_state, conv_w, conv_b, dt_bias = map(
+        to_f64, (x_in, dt_raw, conv_state, conv_w, conv_b, dt_bias))
+    Ln, S, Dn = x_in.shape
+    K = conv_w.shape[2]
+    _check(conv_w, (Ln, Dn, K), "conv_w"); _check(conv_state, (Ln, S, K - 1, Dn), "conv_state")
+    u = np.empty((Ln, S, Dn)); dt = np.empty((Ln, S, Dn)); cs = np.empty((Ln, S, K - 1, Dn))
+    for l in range(Ln):
+        ul, cs[l] = conv_silu(x_in[l][:, None, :], conv_w[l], None if conv_b is None else conv_b[l],
+                              conv_state[l])
+        u[l] = ul[:, 0, :]
+        dt[l] = softplus(dt_raw[l], None if dt_bias is None else dt_bias[l])
+    y, hn = step(h, u, dt, A, B, C, D, z)
+    return y, hn, cs
 
 
 def scan_threaded(x, dt, A, B, C, D, z=None, h0=None, threads: int = 1, complex_state=False):

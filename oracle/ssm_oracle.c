@@ -220,3 +220,69 @@ int64_t oracle_state_bytes(int64_t n_layers, int64_t channels, int64_t d_state,
 {
     return n_layers * channels * d_state * bytes_per_value;
 }
+
+/* ------------------------------------------------------------------ input stage
+ * What the MambaBlock ("【大模型】- Jamba 混合 SSM-Transformer", section 4.1
+ * "Mamba 层") does to its inputs before the scan:
+ *  - x: a depthwise 1-D convolution over time (one filter of K taps and one bias
+ *    per channel), with K-1 zeros of padding in front and the output cut back to
+ *    the first L steps, so output t sees inputs t-K+1 .. t only; then silu.
+ *  - dt: softplus of the dt projection's output, softplus(v) = log(1 + e^v).
+ * A convolution in the deep-learning sense takes no flip: tap k multiplies the
+ * input k steps after the window's first one, i.e. x_{t-(K-1)+k}.
+ *
+ * Inputs before step 0 come from a carried "conv state" (the last K-1 inputs of
+ * the previous call, oldest first) or are zero, which is the padding above. The
+ * state after the call is the last K-1 inputs, so that calls can be chained.
+ *
+ * Layouts: x, u [batch][L][Dn]; w [Dn][K]; cb [Dn] (NULL = no bias);
+ * state0, state_out [batch][K-1][Dn] (state0 NULL = zeros; state_out NULL = not
+ * wanted); K >= 1. */
+static double conv_input(const double *x, const double *state0, int64_t b, int64_t s,
+                         int64_t d, int64_t L, int64_t Dn, int64_t K)
+{
+    if (s >= 0) return x[(b * L + s) * Dn + d];
+    if (!state0) return 0.0;
+    return state0[(b * (K - 1) + (K - 1 + s)) * Dn + d];
+}
+
+int oracle_conv_silu_f64(int64_t batch, int64_t L, int64_t Dn, int64_t K,
+                         const double *x, const double *w, const double *cb,
+                         const double *state0, double *u, double *state_out)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || K < 1) return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t t = 0; t < L; ++t) {
+            for (int64_t d = 0; d < Dn; ++d) {
+                double acc = cb ? cb[d] : 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc = acc + w[d * K + k] * conv_input(x, state0, b, t - (K - 1) + k, d, L, Dn, K);
+                u[(b * L + t) * Dn + d] = silu(acc);
+            }
+        }
+        if (state_out)
+            for (int64_t j = 0; j < K - 1; ++j)
+                for (int64_t d = 0; d < Dn; ++d)
+                    state_out[(b * (K - 1) + j) * Dn + d] =
+                        conv_input(x, state0, b, L - (K - 1) + j, d, L, Dn, K);
+    }
+    return 0;
+}
+
+/* softplus(v) = log(1 + e^v), written as max(v, 0) + log(1 + e^-|v|) so that it
+ * neither overflows for large v nor loses the small result for very negative v;
+ * the two forms are equal (for v > 0, 1 + e^v = e^v (1 + e^-v)). */
+static double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
+
+/* dt[i][d] = softplus(raw[i][d] + bias[d]) for rows i < rows (bias NULL = 0). The
+ * bias is that of the dt projection, applied here so the projection itself can run
+ * without one. */
+int oracle_softplus_f64(int64_t rows, int64_t Dn, const double *raw, const double *bias,
+                        double *dt)
+{
+    if (rows < 0 || Dn < 0) return -1;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t d = 0; d < Dn; ++d)
+            dt[i * Dn + d] = softplus(raw[i * Dn + d] + (bias ? bias[d] : 0.0));
+    return 0;
+}

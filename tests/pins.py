@@ -23,6 +23,14 @@ pages or plain mathematics fix:
                 theta = 0 equals the real one.
   printed value the fixed-size state arithmetic of the memory-budget section
                 (tests/golden/state_memory.json).
+  input stage   the MambaBlock's causal depthwise convolution against numpy's
+                np.convolve (a true convolution, so the taps go in reversed) and an
+                impulse response; the carried conv state against the plain
+                concatenation of two calls' inputs; softplus against numpy's
+                logaddexp(0, v) and its identities softplus(v) - softplus(-v) = v,
+                softplus(0) = log 2; the fused scan with an identity filter and an
+                inverse-softplus step against the plain scan of silu(x); L fused
+                decode steps against one fused prefill.
 
 The pins draw their own inputs with numpy; they test only the oracle.
 """
@@ -317,6 +325,112 @@ def pin_brute_force_complex(O, tol=1e-12):
         assert _rel(hf, hb) <= tol, f"complex brute force h_final mismatch {_rel(hf, hb)}"
 
 
+# ---------------------------------------------------------------- input stage
+def pin_conv_matches_numpy(O, tol=1e-12):
+    # With a large bias the silu is the identity to far below fp64 resolution
+    # (silu(v) = v (1 - e^-v + ...), e^-55 ~ 1e-24), so the convolution itself shows.
+    r = np.random.default_rng(41)
+    for K in (1, 2, 3, 4):
+        b, L, Dn = 2, 13, 3
+        x = r.normal(0, 1, (b, L, Dn))
+        w = r.normal(0, 1, (Dn, K))
+        cb = 60.0 + r.normal(0, 1, Dn)
+        u, _ = O.conv_silu(x, w, cb)
+        for bb in range(b):
+            for d in range(Dn):
+                ref = np.convolve(x[bb, :, d], w[d, ::-1])[:L] + cb[d]
+                assert _rel(u[bb, :, d], ref) <= tol, f"conv vs np.convolve, K={K}, b={bb}, d={d}"
+
+
+def pin_conv_impulse(O):
+    # A unit impulse at step t0 of one channel: output t0 + j is silu(w[K-1-j]) for
+    # j < K and silu(0) = 0 everywhere else (no bias); other channels stay 0.
+    K, L, Dn, t0 = 4, 11, 3, 5
+    w = np.array([[0.5, -1.5, 2.0, 3.0], [1.0, 1.0, 1.0, 1.0], [0.25, 0.75, -0.5, 1.25]])
+    x = np.zeros((1, L, Dn)); x[0, t0, 2] = 1.0
+    u, _ = O.conv_silu(x, w)
+    ref = np.zeros((1, L, Dn))
+    for j in range(K):
+        ref[0, t0 + j, 2] = silu(w[2, K - 1 - j])
+    assert np.array_equal(u, ref), "conv impulse response"
+
+
+def pin_conv_state_carry(O):
+    # Running a sequence in two calls with the conv state carried must equal one call
+    # over the concatenation, also when the second part is shorter than K-1.
+    r = np.random.default_rng(43)
+    for K, L1, L2 in [(4, 7, 9), (4, 5, 2), (3, 6, 1), (2, 4, 5), (4, 1, 0)]:
+        b, Dn = 2, 3
+        x = r.normal(0, 1, (b, L1 + L2, Dn))
+        w = r.normal(0, 1, (Dn, K)); cb = r.normal(0, 1, Dn)
+        s0 = r.normal(0, 1, (b, K - 1, Dn))
+        u, so = O.conv_silu(x, w, cb, s0)
+        u1, so1 = O.conv_silu(x[:, :L1], w, cb, s0)
+        u2, so2 = O.conv_silu(x[:, L1:], w, cb, so1)
+        assert np.array_equal(np.concatenate([u1, u2], axis=1), u), f"conv split, K={K}"
+        full = np.concatenate([s0, x], axis=1)
+        assert np.array_equal(so2, full[:, full.shape[1] - (K - 1):]), f"conv state, K={K}"
+        assert np.array_equal(so, so2), f"conv state of one call vs two, K={K}"
+
+
+def pin_softplus(O):
+    v = np.linspace(-30.0, 30.0, 241)
+    assert _rel(O.softplus(v[None]), np.logaddexp(0.0, v)[None]) <= 1e-15, "softplus vs logaddexp"
+    assert _rel(O.softplus(v[None]) - O.softplus(-v[None]), v[None]) <= 1e-14, "softplus(v) - softplus(-v) = v"
+    assert abs(O.softplus(np.zeros((1, 1)))[0, 0] - np.log(2.0)) <= 1e-16, "softplus(0) = log 2"
+    big = O.softplus(np.array([[800.0, -800.0, -40.0]]))
+    assert big[0, 0] == 800.0 and 0.0 <= big[0, 1] < 1e-300, "softplus far from 0"
+    assert abs(big[0, 2] - np.exp(-40.0)) <= 1e-15 * np.exp(-40.0), "softplus keeps tiny values"
+    bias = np.array([-2.0, 0.5, 3.0, 7.0])
+    out = O.softplus(np.zeros((3, 2, 4)), bias)
+    assert _rel(out, np.broadcast_to(np.logaddexp(0.0, bias), (3, 2, 4))) <= 1e-15, "dt bias per channel"
+
+
+def _inv_softplus(dt):
+    return np.log(np.expm1(dt))
+
+
+def pin_fused_identity_filter(O, tol=1e-12):
+    # Filter (0, .., 0, 1) with no bias passes x through the convolution; the step
+    # softplus^-1(dt) comes back as dt. The fused scan then equals the plain scan of
+    # silu(x) with that dt, whatever the carried conv state holds.
+    for seed, K in [(51, 4), (52, 2)]:
+        inp = tiny_real(seed)
+        b, L, Dn = inp["x"].shape
+        w = np.zeros((Dn, K)); w[:, K - 1] = 1.0
+        s0 = np.random.default_rng(seed).normal(0, 1, (b, K - 1, Dn))
+        y, hf, _ = O.scan_fused(inp["x"], _inv_softplus(inp["dt"]), inp["A"], inp["B"], inp["C"],
+                                inp["D"], inp["z"], inp["h0"], conv_w=w, conv_state0=s0)
+        yr, hr = O.scan(silu(inp["x"]), inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                        inp["z"], inp["h0"])
+        assert _rel(y, yr) <= tol and _rel(hf, hr) <= tol, f"fused identity filter, K={K}"
+
+
+def pin_fused_step_equals_scan(O, tol=1e-12):
+    # L fused decode steps (conv state and SSM state carried, two layers with their
+    # own weights) against one fused prefill per layer.
+    r = np.random.default_rng(61)
+    Ln, S, Dn, N, K, L = 2, 2, 3, 4, 4, 9
+    xin = r.normal(0, 1, (Ln, S, L, Dn)); dtr = r.normal(-1, 0.5, (Ln, S, L, Dn))
+    z = r.normal(0, 1, (Ln, S, L, Dn))
+    B = r.normal(0, 1, (Ln, S, L, N)); C = r.normal(0, 1, (Ln, S, L, N))
+    A = -np.exp(r.normal(0, 0.5, (Ln, Dn, N))); D = r.normal(1, 0.1, (Ln, Dn))
+    w = r.normal(0, 1, (Ln, Dn, K)); cb = r.normal(0, 0.5, (Ln, Dn)); db = r.normal(0, 0.5, (Ln, Dn))
+    cs = r.normal(0, 1, (Ln, S, K - 1, Dn)); h = r.normal(0, 1, (Ln, S, Dn, N))
+    ys = []
+    hs, css = h, cs
+    for t in range(L):
+        yt, hs, css = O.step_fused(hs, css, xin[:, :, t], dtr[:, :, t], A, B[:, :, t], C[:, :, t], D,
+                                   z[:, :, t], conv_w=w, conv_b=cb, dt_bias=db)
+        ys.append(yt)
+    ys = np.stack(ys, axis=2)
+    for l in range(Ln):
+        y, hf, so = O.scan_fused(xin[l], dtr[l], A[l], B[l], C[l], D[l], z[l], h[l], conv_w=w[l],
+                                 conv_b=cb[l], conv_state0=cs[l], dt_bias=db[l])
+        assert _rel(ys[l], y) <= tol and _rel(hs[l], hf) <= tol, f"fused decode vs prefill, layer {l}"
+        assert np.array_equal(css[l], so), f"fused decode conv state, layer {l}"
+
+
 ALL_PINS = [
     pin_brute_force, pin_convolution, pin_geometric_series, pin_dt_zero, pin_linearity,
     pin_split_resume, pin_step_equals_scan, pin_isolation, pin_state_bytes,
@@ -325,4 +439,6 @@ ALL_PINS = [
     lambda O: pin_step_equals_scan(O, complex_state=True),
     pin_layers_are_independent,
     lambda O: pin_layers_are_independent(O, complex_state=True),
+    pin_conv_matches_numpy, pin_conv_impulse, pin_conv_state_carry, pin_softplus,
+    pin_fused_identity_filter, pin_fused_step_equals_scan,
 ]

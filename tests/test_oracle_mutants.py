@@ -45,6 +45,20 @@ MUTANTS = {
                             "const double nr = (dAr * hs[2 * n] + dAi * hs[2 * n + 1]) + dBr * xv;"),
     "state_bytes_factor": ("return n_layers * channels * d_state * bytes_per_value;",
                            "return n_layers * channels * d_state * 4;"),
+    "conv_taps_flipped": ("acc = acc + w[d * K + k] * conv_input", "acc = acc + w[d * K + (K - 1 - k)] * conv_input"),
+    "conv_off_by_one": ("conv_input(x, state0, b, t - (K - 1) + k, d, L, Dn, K)",
+                        "conv_input(x, state0, b, t - K + k, d, L, Dn, K)"),
+    "conv_bias_dropped": ("double acc = cb ? cb[d] : 0.0;", "double acc = 0.0;"),
+    "conv_without_silu": ("u[(b * L + t) * Dn + d] = silu(acc);", "u[(b * L + t) * Dn + d] = acc;"),
+    "conv_state_reversed": ("return state0[(b * (K - 1) + (K - 1 + s)) * Dn + d];",
+                            "return state0[(b * (K - 1) + (-1 - s)) * Dn + d];"),
+    "conv_state_out_shifted": ("conv_input(x, state0, b, L - (K - 1) + j, d, L, Dn, K);",
+                               "conv_input(x, state0, b, L - K + j, d, L, Dn, K);"),
+    "softplus_sign": ("return fmax(v, 0.0) + log1p(exp(-fabs(v)));", "return fmax(v, 0.0) + log1p(exp(fabs(v)));"),
+    "softplus_no_max": ("return fmax(v, 0.0) + log1p(exp(-fabs(v)));", "return log1p(exp(-fabs(v)));"),
+    "dt_bias_dropped": ("softplus(raw[i * Dn + d] + (bias ? bias[d] : 0.0));", "softplus(raw[i * Dn + d]);"),
+    "dt_bias_row_index": ("softplus(raw[i * Dn + d] + (bias ? bias[d] : 0.0));",
+                          "softplus(raw[i * Dn + d] + (bias ? bias[i % Dn] : 0.0));"),
 }
 
 
@@ -70,7 +84,7 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     real = oracle._load()
     lib = ctypes.CDLL(str(so))
     for fname in ("oracle_scan_f64", "oracle_scan_c128", "oracle_step_f64", "oracle_step_c128",
-                  "oracle_state_bytes"):
+                  "oracle_state_bytes", "oracle_conv_silu_f64", "oracle_softplus_f64"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
