@@ -17,14 +17,20 @@ channels, N = 16, bf16 inputs, fp32 state) at which the throughput target is set
 Roofline: the dominant kernel's average duration is measured with HIP events
 recorded by the library itself on the launch stream (ssm_scan_fwd_profiled), and
 its algorithmic work is compared with two ceilings: HBM bytes against 8 TB/s, and
-vector-ALU issue slots against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. The
-reported bound is the one the kernel is closer to. HBM traffic measured with
+vector-ALU instructions (one lane-op each, transcendentals included) against
+256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. The reported bound is the one the kernel
+is closer to. HBM traffic measured with
 rocprofv3 counters is read from profiles/traffic.json when it was taken on the
 current kernel source (by hash), else null.
 
 The CPU baseline is the fp64 oracle as it stands, run on a bounded sample of the
 same workload (a subset of channels over the full sequence; channels are
 independent) from several host threads.
+
+--fused times the same prefill workload through ssm_scan_fwd_fused instead: x is the
+input of the MambaBlock's causal depthwise convolution (--conv-k taps, default 4) and
+dt the raw dt projection output, and the convolution + silu and softplus run inside
+the scan's load stage.
 """
 from __future__ import annotations
 
@@ -39,13 +45,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one fp32 lane-op per lane per clock.
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one fp32 VALU instruction per lane per clock
+# (non-packed; the published 157.3 TFLOP/s counts packed fp32 FMAs as 4 flops).
 VALU_PEAK_TLANE = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "scan elements (batch·L·D_inner)/s at N=16; achieved HBM GB/s vs peak"
+CSRC = "selective_state_space_49_amd/csrc/"
+COMMON_HEADERS = [CSRC + "ssm_device.h", CSRC + "ssm_stream.h"]
 KERNEL_SOURCES = {
-    "real": "selective_state_space_49_amd/csrc/scan_real.hip",
-    "complex": "selective_state_space_49_amd/csrc/scan_complex.hip",
-    "step": "selective_state_space_49_amd/csrc/step.hip",
+    "real": [CSRC + "scan_real.hip", CSRC + "ssm_input_stage.h"],
+    "complex": [CSRC + "scan_complex.hip"],
+    "step": [CSRC + "step.hip", CSRC + "ssm_input_stage.h"],
 }
 
 
@@ -55,8 +64,7 @@ def log(*a):
 
 def source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[kind], "selective_state_space_49_amd/csrc/ssm_device.h",
-                "selective_state_space_49_amd/csrc/ssm_stream.h"):
+    for rel in KERNEL_SOURCES[kind] + COMMON_HEADERS:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -73,16 +81,32 @@ def prefill_bytes(s, io_bytes: int) -> float:
 
 
 def prefill_lane_ops(s) -> float:
-    """Vector-ALU issue slots per scan element on the fp32 path (transcendentals
-    count 2: the hardware issues them at half rate). Real state, per state:
-    dt*A, exp, (dt x)*B, fma (state), fma (output). Complex state, per state:
-    dt*a, exp, dt*theta, fract, sin, cos, 2 mul (decay*rotation), 2 mul (dt x B),
-    4 fma (complex update), 2 fma (real part of C h). Per element: widening of
-    x, dt (and z), dt*x, D*x + acc, the gate (mul, exp, add, rcp, 2 mul) and the
-    output conversion."""
-    per_state = 18 if s.complex_state else 6
-    per_elem = 2 + 1 + 1 + 1 + (1 + 8 if s.gated else 0)
+    """Vector-ALU instructions per scan element (one lane-op each; a transcendental
+    counts as one instruction like any other). Real state, per state: dt*A, exp,
+    (dt x)*B, fma (state), fma (output) = 5. Complex state, per state: dt*a, exp,
+    dt*theta, fract, sin, cos, 2 mul (decay x rotation), 2 mul (dt x B), 4 fma (complex
+    update), 2 fma (real part of C h) = 16. Per element: dt*x, D*x + acc; with bf16 I/O
+    the widening of x and dt and the output conversion; gated: the gate (mul, exp, add,
+    rcp, mul, mul) and, with bf16 I/O, the widening of z."""
+    bf16 = s.io == "bf16"
+    per_state = 16 if s.complex_state else 5
+    per_elem = 2 + (3 if bf16 else 0)
+    if s.gated:
+        per_elem += 6 + (1 if bf16 else 0)
     return s.d_state * per_state + per_elem
+
+
+def input_stage_bytes(s, io_bytes: int, K: int) -> float:
+    """Extra bytes of the fused input stage: filter, biases, carried conv state in/out
+    (the raw x and dt replace x and dt one for one)."""
+    return s.d_inner * (K + (1 if K else 0) + 1) * 4 + 2 * s.batch * max(K - 1, 0) * s.d_inner * io_bytes
+
+
+def input_stage_lane_ops(K: int) -> float:
+    """Vector-ALU instructions per element of the fused input stage. softplus(dt + bias):
+    add, mul, exp, add, sub, log, mul, rcp, mul, mul, compare, select, max, add = 14.
+    Convolution: K fma, then silu (mul, exp, add, rcp, mul) = K + 5."""
+    return 14 + (K + 5 if K else 0)
 
 
 def decode_bytes(s, io_bytes: int) -> float:
@@ -93,10 +117,15 @@ def decode_bytes(s, io_bytes: int) -> float:
 
 
 # ----------------------------------------------------------------- runs
-def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
+def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None):
+    """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter."""
     dev = "cuda"
     log("drawing inputs for", shape.name)
     d = workloads.make_scan_inputs(shape, dev)
+    fused = conv_k is not None
+    if fused:
+        d.update(workloads.make_input_stage(shape, conv_k, dev))
+        d["dt"] = None                      # the fused path reads dt_raw instead
     b, L, Dn, N = shape.batch, shape.L, shape.d_inner, shape.d_state
     cplx = shape.complex_state
     y = torch.empty_like(d["x"])
@@ -106,6 +135,7 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
             else ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, N, T))
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     fn = ssm.ssm_scan_fwd_c64_profiled if cplx else ssm.ssm_scan_fwd_profiled
+    so = (torch.empty_like(d["conv_state0"]) if fused and d["conv_state0"] is not None else None)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for row in ev:                      # create the underlying HIP events
         for e in row:
@@ -116,8 +146,15 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     torch.cuda.synchronize()
 
     def call(events):
-        fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None, y=y, h_final=hf,
-           workspace=ws, chunk_len=T, events=[e.cuda_event for e in events])
+        if fused:
+            ssm.ssm_scan_fwd_fused(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
+                                   conv_w=d["conv_w"], conv_b=d["conv_b"],
+                                   conv_state0=d["conv_state0"], dt_bias=d["dt_bias"], y=y,
+                                   h_final=hf, conv_state_out=so, workspace=ws, chunk_len=T,
+                                   events=[e.cuda_event for e in events])
+        else:
+            fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None, y=y, h_final=hf,
+               workspace=ws, chunk_len=T, events=[e.cuda_event for e in events])
 
     log("warmup", warmup)
     for _ in range(warmup):
@@ -138,10 +175,15 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     gpu_ms = sum(phases.values())
     io_bytes = 2 if shape.io == "bf16" else 4
     elems = shape.elements
+    nbytes = prefill_bytes(shape, io_bytes)
+    lane_ops = prefill_lane_ops(shape)
+    if fused:
+        nbytes += input_stage_bytes(shape, io_bytes, conv_k)
+        lane_ops += input_stage_lane_ops(conv_k)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": phases,
-        "elements_per_step": elems, "bytes_per_step": prefill_bytes(shape, io_bytes),
-        "lane_ops_per_elem": prefill_lane_ops(shape), "chunk_len": T,
+        "elements_per_step": elems, "bytes_per_step": nbytes,
+        "lane_ops_per_elem": lane_ops, "chunk_len": T,
         "n_chunks": -(-L // T), "dominant_ms": phases["rescan"], "gpu_ms": gpu_ms,
         "kernel": "k_chunk_scan_c" if cplx else "k_chunk_scan",
         "source": "complex" if cplx else "real",
@@ -233,7 +275,7 @@ def traffic_for(info, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(shape, d, torch, workloads, threads):
+def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None):
     import oracle
     oracle.build(force=False)
     if shape.complex_state:
@@ -248,6 +290,13 @@ def cpu_baseline(shape, d, torch, workloads, threads):
     log("cpu baseline: oracle on", k, "channels x", shape.L, "steps x batch", shape.batch,
         "with", threads, "threads")
     t0 = time.perf_counter()
+    if conv_k is not None:
+        # the oracle's input stage on the sample (one thread), then its scan as above
+        sel = lambda t: None if t is None else t.index_select(0, idx).cpu()
+        u = (oracle.conv_silu(args[0], sel(d["conv_w"]), sel(d["conv_b"]),
+                              g(d["conv_state0"]))[0] if conv_k else args[0])
+        dts = oracle.softplus(g(d["dt_raw"]), sel(d["dt_bias"]))
+        args = (u, dts) + args[2:]
     oracle.scan_threaded(*args, threads=threads, complex_state=shape.complex_state)
     dt = time.perf_counter() - t0
     elems = shape.batch * shape.L * k
@@ -270,6 +319,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="decode: launch the per-layer calls eagerly instead of replaying one "
                          "captured HIP graph per token")
+    ap.add_argument("--fused", action="store_true",
+                    help="prefill through ssm_scan_fwd_fused (conv + silu and softplus fused "
+                         "into the load stage)")
+    ap.add_argument("--conv-k", type=int, default=4, help="filter taps with --fused (0..4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -302,20 +355,26 @@ def main():
     if is_decode:
         info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph)
     else:
-        info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
+        if args.fused and shape.complex_state:
+            print("--fused applies to the real-state prefill workloads", file=sys.stderr)
+            sys.exit(2)
+        conv_k = args.conv_k if args.fused else None
+        info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
+                              conv_k)
 
     elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
     dom_s = info["dominant_ms"] / 1e3
     hbm_ach = info["bytes_per_step"] / dom_s / 1e9
     alu_ach = info["elements_per_step"] * info["lane_ops_per_elem"] / dom_s / 1e12
     hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
-    traffic = traffic_for(info, args.workload)
+    traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "")
+    traffic = traffic_for(info, traffic_key)
     if hbm_frac >= alu_frac:
         roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(hbm_frac, 4)}
     else:
         roof = {"bound": "alu", "achieved": round(alu_ach, 2), "peak": round(VALU_PEAK_TLANE, 2),
-                "unit": "T VALU lane-op/s", "frac": round(alu_frac, 4)}
+                "unit": "T VALU lane-instr/s", "frac": round(alu_frac, 4)}
     roof["traffic"] = traffic
     roof["kernel"] = info["kernel"]
     roof["kernel_ms"] = round(info["dominant_ms"] if not is_decode else info["per_call_ms"], 4)
@@ -333,6 +392,9 @@ def main():
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
                "complex_state": shape.complex_state, "gated": shape.gated,
                "chunk_len": info["chunk_len"], "n_chunks": info["n_chunks"]}
+        if args.fused:
+            cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
+                                  "softplus_dt": True, "entry_point": "ssm_scan_fwd_fused"}
     out = {
         "metric": METRIC, "value": round(elems_s, 1), "unit": "elements/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(info["ms_per_step"], 4),
@@ -344,7 +406,8 @@ def main():
     }
     if not args.no_cpu_baseline and not is_decode:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads)
+        out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
+                                           args.conv_k if args.fused else None)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

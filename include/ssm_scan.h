@@ -62,7 +62,8 @@ typedef enum {
     SSM_ERR_SHAPE = 2,        /* a size is negative, zero where it must not be, or too large */
     SSM_ERR_DTYPE = 3,        /* io is not SSM_F32 or SSM_BF16 */
     SSM_ERR_ALIGN = 4,        /* a pointer breaks the alignment rules above */
-    SSM_ERR_UNSUPPORTED = 5,  /* d_state not in {1, 2, 4, 8, 16}, or chunk_len invalid */
+    SSM_ERR_UNSUPPORTED = 5,  /* d_state not in {1, 2, 4, 8, 16}, chunk_len or conv_k invalid,
+                                 or a forbidden overlap (fused prefill) */
     SSM_ERR_WORKSPACE = 6,    /* workspace missing or smaller than the query says */
     SSM_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
 } ssm_status;
@@ -173,10 +174,72 @@ ssm_status ssm_step_c64_replay(float *h, const void *x_t, const void *dt_t, cons
                                int64_t d_inner, int32_t d_state, ssm_dtype io,
                                void *hip_stream);
 
+/* ------------------------------------------------------------------ fused input stage
+ * Between its input projection and its scan, the MambaBlock ("【大模型】- Jamba 混合
+ * SSM-Transformer", section 4.1 "Mamba 层") computes
+ *     u  = silu(conv(x_in)),   conv = a causal depthwise convolution over time:
+ *          conv(x)_t[d] = conv_b[d] + sum_{k<K} conv_w[d][k] * x_{t-(K-1)+k}[d]
+ *          (K = conv_k taps; K-1 zeros of padding in front, output cut back to L steps;
+ *          inputs before step 0 come from the carried conv state)
+ *     dt = softplus(dt_raw + dt_bias),   softplus(v) = log(1 + e^v)
+ *          (dt_raw is the dt projection's output without its bias)
+ * and scans with u in place of x (the skip term uses u as well). These entry points
+ * apply both while loading x_in and dt_raw, so neither u nor dt is ever written to
+ * memory. Real state only; the recurrence, gate and outputs are those of
+ * ssm_scan_fwd / ssm_step, and dt >= 0 holds by construction.
+ *   conv_k        0 = no convolution (x_in is used as is and the conv pointers are
+ *                 ignored), else 1..4 (the page's d_conv is 4). Other values:
+ *                 SSM_ERR_UNSUPPORTED.
+ *   conv_w        [d_inner, conv_k] float32 (decode: [n_layers, d_inner, conv_k]);
+ *                 required when conv_k > 0.
+ *   conv_b        [d_inner] float32 (decode: [n_layers, d_inner]); NULL = no bias.
+ *   dt_bias       [d_inner] float32 (decode: [n_layers, d_inner]); NULL = 0.
+ *   conv state    the last conv_k-1 inputs x_in, oldest first, in the io type:
+ *                 prefill [batch, conv_k-1, d_inner], decode [n_layers, n_seq,
+ *                 conv_k-1, d_inner]. Alignment: one element; conv_w, conv_b, dt_bias
+ *                 4 bytes.
+ * Inside the kernels: dt as e = e2(-|v| log2 e), w = 1 + e, l = (w == 1) ? e :
+ * (log2(w) ln 2) (e rcp(w - 1)) (Goldberg's log1p correction), dt = max(v, 0) + l
+ * for v = dt_raw + dt_bias; u as acc = conv_b, acc = fma(conv_w[k], input, acc) for
+ * k ascending, u = acc rcp(1 + e2(-acc log2 e)).
+ *
+ * ssm_scan_fwd_fused: prefill. conv_state0 NULL = zeros before step 0 (the page's
+ * padding). conv_state_out NULL = not wanted; else it receives the last conv_k-1
+ * inputs (from conv_state0 where L < conv_k-1). workspace: ssm_scan_fwd_workspace_ex
+ * bytes for the same shape and chunk_len. With conv_k > 1, y must not overlap x_in
+ * (a chunk reads the previous chunk's last inputs), and conv_state_out must not
+ * overlap x_in or conv_state0: SSM_ERR_UNSUPPORTED otherwise. L == 0 writes
+ * h_final = h0 and conv_state_out = conv_state0 (or zeros). */
+ssm_status ssm_scan_fwd_fused(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *h0,
+                              const float *conv_w, const float *conv_b, int32_t conv_k,
+                              const void *conv_state0, void *conv_state_out,
+                              const float *dt_bias, void *y, float *h_final,
+                              int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                              ssm_dtype io, int64_t chunk_len, void *workspace,
+                              size_t workspace_bytes, void *hip_stream);
+
+/* ssm_step_fused: one decode token; h and conv_state (required when conv_k > 1) are
+ * updated in place. x_t is the convolution's new input and dt_t the raw dt.
+ * ssm_step_fused_replay: the same in the written-down order, one thread per channel
+ * (bit-for-bit reference for ssm_step_fused). */
+ssm_status ssm_step_fused(float *h, void *conv_state, const void *x_t, const void *dt_t,
+                          const float *A, const void *B_t, const void *C_t, const float *D,
+                          const void *z_t, const float *conv_w, const float *conv_b,
+                          int32_t conv_k, const float *dt_bias, void *y_t, int64_t n_layers,
+                          int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                          void *hip_stream);
+ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, const void *dt_t,
+                                 const float *A, const void *B_t, const void *C_t, const float *D,
+                                 const void *z_t, const float *conv_w, const float *conv_b,
+                                 int32_t conv_k, const float *dt_bias, void *y_t,
+                                 int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                                 int32_t d_state, ssm_dtype io, void *hip_stream);
+
 /* ------------------------------------------------------------------ profiling
- * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64, which additionally
- * records four caller-created HIP events (hipEvent_t, passed as void*) on
- * hip_stream: events[0] before the chunk-summary kernel, events[1] after it,
+ * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64 / ssm_scan_fwd_fused,
+ * which additionally records four caller-created HIP events (hipEvent_t, passed
+ * as void*) on hip_stream: events[0] before the chunk-summary kernel, events[1] after it,
  * events[2] after the carry-scan kernel, events[3] after the rescan kernel. With a
  * single chunk the first two phases launch nothing and their events are recorded
  * back to back. No work is skipped. n_events must be 4 (else SSM_ERR_NULL). For
@@ -195,6 +258,16 @@ ssm_status ssm_scan_fwd_c64_profiled(const void *x, const void *dt, const float 
                                      ssm_dtype io, int64_t chunk_len, void *workspace,
                                      size_t workspace_bytes, void *hip_stream,
                                      void *const *events, int32_t n_events);
+ssm_status ssm_scan_fwd_fused_profiled(const void *x_in, const void *dt_raw, const float *A,
+                                       const void *B, const void *C, const float *D,
+                                       const void *z, const float *h0, const float *conv_w,
+                                       const float *conv_b, int32_t conv_k,
+                                       const void *conv_state0, void *conv_state_out,
+                                       const float *dt_bias, void *y, float *h_final,
+                                       int64_t batch, int64_t L, int64_t d_inner,
+                                       int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                                       void *workspace, size_t workspace_bytes, void *hip_stream,
+                                       void *const *events, int32_t n_events);
 
 /* ------------------------------------------------------------------ misc */
 const char *ssm_status_str(ssm_status s);   /* static string, never NULL */

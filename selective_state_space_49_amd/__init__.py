@@ -22,6 +22,7 @@ __all__ = [
     "ssm_step", "ssm_step_replay", "ssm_step_c64", "ssm_step_c64_replay",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version", "EXPORTED_SYMBOLS",
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
+    "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = [
     "ssm_step", "ssm_step_replay", "ssm_step_c64", "ssm_step_c64_replay",
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
+    "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
 ]
 
 
@@ -80,6 +82,12 @@ def load_library():
     step = [vp] * 9 + [i64, i64, i64, i32, ci, vp]
     for name in ("ssm_step", "ssm_step_replay", "ssm_step_c64", "ssm_step_c64_replay"):
         sig[name] = (step, ci)
+    fused = [vp] * 10 + [i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, ci, i64, vp, sz, vp]
+    sig["ssm_scan_fwd_fused"] = (fused, ci)
+    sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
+    step_fused = [vp] * 11 + [i32, vp, vp, i64, i64, i64, i32, ci, vp]
+    for name in ("ssm_step_fused", "ssm_step_fused_replay"):
+        sig[name] = (step_fused, ci)
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
         f.argtypes, f.restype = args, res
@@ -268,3 +276,109 @@ def ssm_step_c64(h, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
 
 def ssm_step_c64_replay(h, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
     return _step("ssm_step_c64_replay", True, h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t)
+
+
+# ------------------------------------------------------------------ fused input stage
+def _input_stage(conv_w, conv_b, dt_bias, lead, Dn, conv_k):
+    f32 = torch.float32
+    _dev(conv_w, "conv_w", lead + (Dn, conv_k), f32)
+    _dev(conv_b, "conv_b", lead + (Dn,), f32)
+    _dev(dt_bias, "dt_bias", lead + (Dn,), f32)
+
+
+def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
+                       conv_state0=None, dt_bias=None, chunk_len=0, y=None, h_final=None,
+                       conv_state_out=None, workspace=None, want_h_final=True,
+                       want_conv_state=True, events=None):
+    """Prefill with the MambaBlock input stage fused into the load: the scan runs on
+    u = silu(causal depthwise conv(x_in)) and dt = softplus(dt_raw + dt_bias).
+    conv_w [d_inner, K] (None: no convolution); conv_b, dt_bias [d_inner] or None;
+    conv_state0 [b, K-1, d_inner] or None (zeros). Returns (y, h_final, conv_state_out)."""
+    lib = load_library()
+    b, L, Dn = x_in.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    K = 0 if conv_w is None else conv_w.shape[-1]
+    _dev(x_in, "x_in"); _dev(dt_raw, "dt_raw", (b, L, Dn)); _dev(z, "z", (b, L, Dn))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N)); _dev(h0, "h0", (b, Dn, N), f32)
+    _input_stage(conv_w, conv_b, dt_bias, (), Dn, K)
+    io = _io(x_in, dt_raw, z, B, C)
+    if K > 1:
+        _dev(conv_state0, "conv_state0", (b, K - 1, Dn), x_in.dtype)
+        if conv_state_out is None and want_conv_state:
+            conv_state_out = torch.empty((b, K - 1, Dn), dtype=x_in.dtype, device=x_in.device)
+        _dev(conv_state_out, "conv_state_out", (b, K - 1, Dn), x_in.dtype)
+    else:
+        conv_state0 = conv_state_out = None
+    if y is None:
+        y = torch.empty_like(x_in)
+    _dev(y, "y", (b, L, Dn), x_in.dtype)
+    if h_final is None and want_h_final:
+        h_final = torch.empty((b, Dn, N), dtype=f32, device=x_in.device)
+    _dev(h_final, "h_final", (b, Dn, N), f32)
+    need = ssm_scan_fwd_workspace_ex(b, L, Dn, N, chunk_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_in.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+            _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_state0), _ptr(conv_state_out),
+            _ptr(dt_bias), _ptr(y), _ptr(h_final), b, L, Dn, N, io, chunk_len, _ptr(workspace),
+            ws_bytes, _stream(x_in)]
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("need exactly 4 event handles")
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) for e in events])
+        st = lib.ssm_scan_fwd_fused_profiled(*args, handles, 4)
+    else:
+        st = lib.ssm_scan_fwd_fused(*args)
+    _check(st)
+    return y, h_final, conv_state_out
+
+
+def ssm_scan_fwd_fused_profiled(*a, events, **k):
+    """ssm_scan_fwd_fused recording 4 HIP events at the kernel boundaries."""
+    return ssm_scan_fwd_fused(*a, events=events, **k)
+
+
+def _step_fused(fn_name, h, conv_state, x, dt, A, B, C, D, z, conv_w, conv_b, dt_bias, y):
+    lib = load_library()
+    Ln, S, Dn = x.shape
+    N = A.shape[2]
+    f32 = torch.float32
+    K = 0 if conv_w is None else conv_w.shape[-1]
+    _dev(h, "h", (Ln, S, Dn, N), f32)
+    _dev(x, "x_t"); _dev(dt, "dt_t", (Ln, S, Dn)); _dev(z, "z_t", (Ln, S, Dn))
+    _dev(A, "A", (Ln, Dn, N), f32); _dev(D, "D", (Ln, Dn), f32)
+    _dev(B, "B_t", (Ln, S, N)); _dev(C, "C_t", (Ln, S, N))
+    _input_stage(conv_w, conv_b, dt_bias, (Ln,), Dn, K)
+    if K > 1:
+        if conv_state is None:
+            raise ValueError("conv_state [n_layers, n_seq, K-1, d_inner] is required")
+        _dev(conv_state, "conv_state", (Ln, S, K - 1, Dn), x.dtype)
+    else:
+        conv_state = None
+    io = _io(x, dt, z, B, C)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y_t", (Ln, S, Dn), x.dtype)
+    st = getattr(lib, fn_name)(_ptr(h), _ptr(conv_state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(conv_w), _ptr(conv_b), K,
+                               _ptr(dt_bias), _ptr(y), Ln, S, Dn, N, io, _stream(x))
+    _check(st)
+    return y
+
+
+def ssm_step_fused(h, conv_state, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, conv_w=None,
+                   conv_b=None, dt_bias=None, y_t=None):
+    """One decode token through the input stage and the recurrence; h and conv_state
+    [n_layers, n_seq, K-1, d_inner] are updated in place. Returns y_t."""
+    return _step_fused("ssm_step_fused", h, conv_state, x_t, dt_t, A, B_t, C_t, D, z_t, conv_w,
+                       conv_b, dt_bias, y_t)
+
+
+def ssm_step_fused_replay(h, conv_state, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, conv_w=None,
+                          conv_b=None, dt_bias=None, y_t=None):
+    """ssm_step_fused in its written-down order, one thread per channel."""
+    return _step_fused("ssm_step_fused_replay", h, conv_state, x_t, dt_t, A, B_t, C_t, D, z_t,
+                       conv_w, conv_b, dt_bias, y_t)

@@ -87,12 +87,35 @@ ssm_status launch_status(hipError_t e, const char *what) {
     return ok();
 }
 
+// The MambaBlock input stage of the fused entry points.
+struct InputStage {
+    const float *conv_w, *conv_b, *dt_bias;
+    int32_t conv_k;
+    const void *conv_state0;  // prefill only
+    void *conv_state;         // prefill: conv_state_out; decode: the state, in place
+};
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+ssm_status check_input_stage(const InputStage &in, size_t eb) {
+    if (in.conv_k < 0 || in.conv_k > 4) return fail(SSM_ERR_UNSUPPORTED, "conv_k %d not in 0..4", in.conv_k);
+    if (in.conv_k > 0 && !in.conv_w) return fail(SSM_ERR_NULL, "conv_w is required when conv_k > 0");
+    if (!aligned(in.conv_w, 4) || !aligned(in.conv_b, 4) || !aligned(in.dt_bias, 4) ||
+        !aligned(in.conv_state0, eb) || !aligned(in.conv_state, eb))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (conv_w, conv_b, dt_bias 4 B; conv state element)");
+    return ok();
+}
+
 ssm_status scan_common(const void *x, const void *dt, const float *A, const void *B, const void *C,
                        const float *D, const void *z, const float *h0, void *y, float *h_final,
                        int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
                        int64_t chunk_len, void *workspace, size_t workspace_bytes,
                        void *hip_stream, bool cplx, void *const *events = nullptr,
-                       int32_t n_events = 0) {
+                       int32_t n_events = 0, const InputStage *in = nullptr) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     Plan plan;
     ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan);
@@ -109,10 +132,32 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     if (events)
         for (int i = 0; i < 4; ++i)
             if (!events[i]) return fail(SSM_ERR_NULL, "profiling event %d is NULL", i);
+    // conv state rows carried between calls: conv_k - 1 per batch row
+    const int64_t conv_rows = in && in->conv_k > 1 ? in->conv_k - 1 : 0;
+    if (in) {
+        st = check_input_stage(*in, eb);
+        if (st != SSM_OK) return st;
+        const size_t stream_bytes = (size_t)(batch * L * d_inner) * eb;
+        const size_t state_bytes = (size_t)(batch * conv_rows * d_inner) * eb;
+        // The rescan of chunk c reads the last conv_k-1 inputs of chunk c-1 while that
+        // chunk's y and the final conv state are written.
+        if (in->conv_k > 1 && overlaps(y, stream_bytes, x, stream_bytes))
+            return fail(SSM_ERR_UNSUPPORTED, "y must not overlap x_in when the convolution is fused");
+        if (overlaps(in->conv_state, state_bytes, x, stream_bytes) ||
+            overlaps(in->conv_state, state_bytes, in->conv_state0, state_bytes))
+            return fail(SSM_ERR_UNSUPPORTED, "conv_state_out must not overlap x_in or conv_state0");
+    }
     hipStream_t s = (hipStream_t)hip_stream;
     const int64_t state_floats = batch * d_inner * d_state * (cplx ? 2 : 1);
     if (!work) {
-        if (h_final) return launch_status(ssm::launch_state_fill(h_final, h0, state_floats, s), "state fill");
+        if (h_final) {
+            st = launch_status(ssm::launch_state_fill(h_final, h0, state_floats, s), "state fill");
+            if (st != SSM_OK) return st;
+        }
+        if (conv_rows && in->conv_state)
+            return launch_status(ssm::launch_elem_fill(in->conv_state, in->conv_state0,
+                                                       batch * conv_rows * d_inner, (int)eb, s),
+                                 "conv state fill");
         return ok();
     }
     if (plan.ws_bytes > 0) {
@@ -121,7 +166,7 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
             return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, plan.ws_bytes);
         if (!aligned(workspace, kWsAlign)) return fail(SSM_ERR_ALIGN, "workspace must be 256-byte aligned");
     }
-    ssm::ScanArgs a;
+    ssm::ScanArgs a{};
     a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z;
     a.A = A; a.D = D; a.h0 = h0;
     a.y = y; a.h_final = h_final;
@@ -133,15 +178,27 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     a.dblocks = (int32_t)((d_inner + a.threads - 1) / a.threads);
     const int iot = io == SSM_BF16 ? 1 : 0;
     hipEvent_t const *ev = (hipEvent_t const *)events;
-    hipError_t e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s, ev)
-                        : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s, ev);
+    hipError_t e;
+    if (in) {
+        a.conv_k = in->conv_k;
+        a.conv_w = in->conv_k > 0 ? in->conv_w : nullptr;
+        a.conv_b = in->conv_k > 0 ? in->conv_b : nullptr;
+        a.conv_state0 = conv_rows ? in->conv_state0 : nullptr;
+        a.conv_state_out = conv_rows ? in->conv_state : nullptr;
+        a.dt_bias = in->dt_bias;
+        e = ssm::launch_scan_fused(a, iot, d_state, z != nullptr, s, ev);
+    } else {
+        e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s, ev)
+                 : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s, ev);
+    }
     return launch_status(e, "scan launch");
 }
 
 ssm_status step_common(float *h, const void *x, const void *dt, const float *A, const void *B,
                        const void *C, const float *D, const void *z, void *y, int64_t n_layers,
                        int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
-                       void *hip_stream, bool cplx, bool replay) {
+                       void *hip_stream, bool cplx, bool replay,
+                       const InputStage *in = nullptr) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     if (n_layers < 0 || n_seq < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "n_layers/n_seq must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
@@ -158,13 +215,27 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     if (!aligned(h, 16) || !aligned(A, 16) || !aligned(x, eb) || !aligned(dt, eb) ||
         !aligned(z, eb) || !aligned(y, eb) || !aligned(B, bc) || !aligned(C, bc) || !aligned(D, 4))
         return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; B_t, C_t min(d_state,4) elements; others element)");
-    ssm::StepArgs a;
+    ssm::StepArgs a{};
     a.h = h; a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z; a.A = A; a.D = D; a.y = y;
     a.n_layers = n_layers; a.n_seq = n_seq; a.Dn = d_inner;
     const int iot = io == SSM_BF16 ? 1 : 0;
     hipStream_t s = (hipStream_t)hip_stream;
-    hipError_t e = cplx ? ssm::launch_step_complex(a, iot, d_state, z != nullptr, replay, s)
-                        : ssm::launch_step_real(a, iot, d_state, z != nullptr, replay, s);
+    hipError_t e;
+    if (in) {
+        ssm_status st = check_input_stage(*in, eb);
+        if (st != SSM_OK) return st;
+        if (in->conv_k > 1 && !in->conv_state)
+            return fail(SSM_ERR_NULL, "conv_state is required when conv_k > 1");
+        a.conv_k = in->conv_k;
+        a.conv_w = in->conv_k > 0 ? in->conv_w : nullptr;
+        a.conv_b = in->conv_k > 0 ? in->conv_b : nullptr;
+        a.conv_state = in->conv_k > 1 ? in->conv_state : nullptr;
+        a.dt_bias = in->dt_bias;
+        e = ssm::launch_step_fused(a, iot, d_state, z != nullptr, replay, s);
+    } else {
+        e = cplx ? ssm::launch_step_complex(a, iot, d_state, z != nullptr, replay, s)
+                 : ssm::launch_step_real(a, iot, d_state, z != nullptr, replay, s);
+    }
     return launch_status(e, "step launch");
 }
 
@@ -278,6 +349,58 @@ ssm_status ssm_step_c64_replay(float *h, const void *x_t, const void *dt_t, cons
                        io, hip_stream, true, true);
 }
 
+ssm_status ssm_scan_fwd_fused(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *h0,
+                              const float *conv_w, const float *conv_b, int32_t conv_k,
+                              const void *conv_state0, void *conv_state_out,
+                              const float *dt_bias, void *y, float *h_final, int64_t batch,
+                              int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                              int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+    const InputStage in{conv_w, conv_b, dt_bias, conv_k, conv_state0, conv_state_out};
+    return scan_common(x_in, dt_raw, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0, &in);
+}
+
+ssm_status ssm_scan_fwd_fused_profiled(const void *x_in, const void *dt_raw, const float *A,
+                                       const void *B, const void *C, const float *D,
+                                       const void *z, const float *h0, const float *conv_w,
+                                       const float *conv_b, int32_t conv_k,
+                                       const void *conv_state0, void *conv_state_out,
+                                       const float *dt_bias, void *y, float *h_final,
+                                       int64_t batch, int64_t L, int64_t d_inner,
+                                       int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                                       void *workspace, size_t workspace_bytes, void *hip_stream,
+                                       void *const *events, int32_t n_events) {
+    if (!events) return fail(SSM_ERR_NULL, "events are required");
+    const InputStage in{conv_w, conv_b, dt_bias, conv_k, conv_state0, conv_state_out};
+    return scan_common(x_in, dt_raw, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, events, n_events,
+                       &in);
+}
+
+ssm_status ssm_step_fused(float *h, void *conv_state, const void *x_t, const void *dt_t,
+                          const float *A, const void *B_t, const void *C_t, const float *D,
+                          const void *z_t, const float *conv_w, const float *conv_b,
+                          int32_t conv_k, const float *dt_bias, void *y_t, int64_t n_layers,
+                          int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                          void *hip_stream) {
+    const InputStage in{conv_w, conv_b, dt_bias, conv_k, nullptr, conv_state};
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, false, &in);
+}
+
+ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, const void *dt_t,
+                                 const float *A, const void *B_t, const void *C_t, const float *D,
+                                 const void *z_t, const float *conv_w, const float *conv_b,
+                                 int32_t conv_k, const float *dt_bias, void *y_t,
+                                 int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                                 int32_t d_state, ssm_dtype io, void *hip_stream) {
+    const InputStage in{conv_w, conv_b, dt_bias, conv_k, nullptr, conv_state};
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, true, &in);
+}
+
 const char *ssm_status_str(ssm_status s) {
     switch (s) {
         case SSM_OK: return "ok";
@@ -285,7 +408,7 @@ const char *ssm_status_str(ssm_status s) {
         case SSM_ERR_SHAPE: return "invalid size";
         case SSM_ERR_DTYPE: return "invalid io dtype";
         case SSM_ERR_ALIGN: return "misaligned pointer";
-        case SSM_ERR_UNSUPPORTED: return "unsupported d_state or chunk length";
+        case SSM_ERR_UNSUPPORTED: return "unsupported d_state, chunk length, conv_k or overlap";
         case SSM_ERR_WORKSPACE: return "workspace missing or too small";
         case SSM_ERR_HIP: return "HIP runtime error";
     }

@@ -25,7 +25,15 @@
 // exp(v) is evaluated as 2^(v log2 e) with the hardware exponential: log2 e is
 // folded into A once per lane, so each state update costs one multiply, one
 // exponential, one multiply (dt x times B) and two fused multiply-adds.
+//
+// The same kernels, instantiated with the MambaBlock input stage (MambaInput below),
+// take the convolution's input in place of x and the raw dt projection output in
+// place of dt, and apply the causal convolution + silu and softplus to each value as
+// it is loaded (ssm_input_stage.h). Every lane then walks its chunk with the last
+// KC-1 convolution inputs in registers, starting from the rows just before the
+// chunk (or the carried convolution state before step 0).
 #include "ssm_device.h"
+#include "ssm_input_stage.h"
 #include "ssm_internal.h"
 #include "ssm_stream.h"
 
@@ -42,6 +50,64 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
     r.d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
     return r;
 }
+
+// ---------------------------------------------------------------- input stage
+// The kernels read x and dt as given.
+struct NoInput {
+    __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
+    __device__ __forceinline__ void history(const ScanArgs &, int64_t, int64_t, int64_t) {}
+    __device__ __forceinline__ float x(float v) { return v; }
+    __device__ __forceinline__ float dt(float v) const { return v; }
+    __device__ __forceinline__ void store_state(const ScanArgs &, int64_t, int64_t) const {}
+};
+
+// The MambaBlock input stage: u = silu(causal conv of KC taps over x) (KC = 0: x as
+// is) and dt = softplus(dt + dt_bias).
+template <typename IO, int KC>
+struct MambaInput {
+    ConvSilu<(KC > 0 ? KC : 1)> conv;
+    float dbias;
+
+    __device__ __forceinline__ void params(const ScanArgs &a, int64_t d) {
+        dbias = a.dt_bias ? a.dt_bias[d] : 0.0f;
+        if constexpr (KC > 0) {
+#pragma unroll
+            for (int k = 0; k < KC; ++k) conv.w[k] = a.conv_w[d * KC + k];
+            conv.bias = a.conv_b ? a.conv_b[d] : 0.0f;
+        }
+    }
+    // The KC-1 inputs before step t: rows of x, or of the carried state before step 0.
+    __device__ __forceinline__ void history(const ScanArgs &a, int64_t b, int64_t d, int64_t t) {
+        if constexpr (KC > 1) {
+#pragma unroll
+            for (int j = 0; j < KC - 1; ++j) {
+                const int64_t r = t - (KC - 1) + j;
+                if (r >= 0)
+                    conv.hist[j] = Io<IO>::ld((const IO *)a.x + (b * a.L + r) * a.Dn + d);
+                else if (a.conv_state0)
+                    conv.hist[j] = Io<IO>::ld((const IO *)a.conv_state0 +
+                                              (b * (KC - 1) + (KC - 1 + r)) * a.Dn + d);
+                else
+                    conv.hist[j] = 0.0f;
+            }
+        }
+    }
+    __device__ __forceinline__ float x(float v) {
+        if constexpr (KC > 0) return conv(v);
+        else return v;
+    }
+    __device__ __forceinline__ float dt(float v) const { return softplus(v + dbias); }
+    // After the last step: the last KC-1 inputs, for the next call.
+    __device__ __forceinline__ void store_state(const ScanArgs &a, int64_t b, int64_t d) const {
+        if constexpr (KC > 1) {
+            if (a.conv_state_out) {
+#pragma unroll
+                for (int j = 0; j < KC - 1; ++j)
+                    Io<IO>::st((IO *)a.conv_state_out + (b * (KC - 1) + j) * a.Dn + d, conv.hist[j]);
+            }
+        }
+    }
+};
 
 // ---------------------------------------------------------------- carry scan
 template <int CTRL, int ROW_MASK>
@@ -113,7 +179,7 @@ __global__ __launch_bounds__(256) void k_carry(ScanArgs a, int64_t M) {
 // ---------------------------------------------------------------- chunk summary
 // Chunk summary: end state from a zero start and total decay, walking only the
 // window back to the decay horizon (see horizon_start).
-template <typename IO, int N>
+template <typename IO, int N, typename In>
 __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const LaneId ln = lane_id(a);
     if (ln.d >= a.Dn) return;
@@ -132,14 +198,18 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     }
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> dts((const IO *)a.dt + row0);
+    In in;
+    in.params(a, ln.d);
     // 1. window start ts (chunk-relative): walk dt backwards from the chunk end
-    const uint32_t ts = horizon_start<IO>(dts, voff, rb, T, amax);
+    const uint32_t ts = horizon_start<IO>(dts, voff, rb, T, amax, [&](float v) { return in.dt(v); });
+    in.history(a, ln.b, ln.d, t0 + ts);
     // 2. end state from zero over rows [ts, T) of the chunk
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
     const int64_t rw = row0 + (int64_t)ts * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
-    stream_steps<IO, false, 4>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xv, float dv, float) {
+    stream_steps<IO, false, 4>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float) {
+        const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + ts + i;
         const float u = dv * xv;
         S += (double)dv;
@@ -159,7 +229,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------- rescan + epilogue
-template <typename IO, int N, bool GATED>
+template <typename IO, int N, bool GATED, typename In>
 __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     const LaneId ln = lane_id(a);
     if (ln.d >= a.Dn) return;
@@ -183,7 +253,11 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
     const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
-    stream_steps<IO, GATED, 4>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xv, float dv, float zv) {
+    In in;
+    in.params(a, ln.d);
+    in.history(a, ln.b, ln.d, t0);
+    stream_steps<IO, GATED, 4>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv) {
+        const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
         const float u = dv * xv;
         float acc = 0.0f;
@@ -198,9 +272,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         if (GATED) yv = yv * silu(zv);
         ys.st(voff, i * rb, yv);
     });
-    if (c == a.n_chunks - 1 && a.h_final) {
+    if (c == a.n_chunks - 1) {
+        if (a.h_final) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) a.h_final[col + n] = h[n];
+            for (int n = 0; n < N; ++n) a.h_final[col + n] = h[n];
+        }
+        in.store_state(a, ln.b, ln.d);
     }
 }
 
@@ -209,17 +286,22 @@ __global__ void k_state_fill(float *dst, const float *src, int64_t count) {
     if (i < count) dst[i] = src ? src[i] : 0.0f;
 }
 
+__global__ void k_fill16(uint16_t *dst, const uint16_t *src, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) dst[i] = src ? src[i] : (uint16_t)0;
+}
+
 inline void mark(hipEvent_t const *ev, int i, hipStream_t s) {
     if (ev) (void)hipEventRecord(ev[i], s);
 }
 
-template <typename IO, int N>
+template <typename IO, int N, typename In>
 hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s, hipEvent_t const *ev) {
     const dim3 blk(a.threads);
     const unsigned gx = (unsigned)(a.batch * a.dblocks);
     mark(ev, 0, s);
     if (a.n_chunks > 1)
-        hipLaunchKernelGGL((k_chunk_summary<IO, N>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+        hipLaunchKernelGGL((k_chunk_summary<IO, N, In>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
     mark(ev, 1, s);
     if (a.n_chunks > 1) {
         const int64_t M = a.batch * a.Dn * N;
@@ -227,22 +309,35 @@ hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s, hipEvent_t con
     }
     mark(ev, 2, s);
     if (gated)
-        hipLaunchKernelGGL((k_chunk_scan<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
+        hipLaunchKernelGGL((k_chunk_scan<IO, N, true, In>), dim3(gx, a.n_chunks), blk, 0, s, a);
     else
-        hipLaunchKernelGGL((k_chunk_scan<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
+        hipLaunchKernelGGL((k_chunk_scan<IO, N, false, In>), dim3(gx, a.n_chunks), blk, 0, s, a);
     mark(ev, 3, s);
     return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, typename In>
 hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
                      hipEvent_t const *ev) {
     switch (d_state) {
-        case 1: return launch_t<IO, 1>(a, gated, s, ev);
-        case 2: return launch_t<IO, 2>(a, gated, s, ev);
-        case 4: return launch_t<IO, 4>(a, gated, s, ev);
-        case 8: return launch_t<IO, 8>(a, gated, s, ev);
-        case 16: return launch_t<IO, 16>(a, gated, s, ev);
+        case 1: return launch_t<IO, 1, In>(a, gated, s, ev);
+        case 2: return launch_t<IO, 2, In>(a, gated, s, ev);
+        case 4: return launch_t<IO, 4, In>(a, gated, s, ev);
+        case 8: return launch_t<IO, 8, In>(a, gated, s, ev);
+        case 16: return launch_t<IO, 16, In>(a, gated, s, ev);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t launch_fused_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
+                           hipEvent_t const *ev) {
+    switch (a.conv_k) {
+        case 0: return launch_io<IO, MambaInput<IO, 0>>(a, d_state, gated, s, ev);
+        case 1: return launch_io<IO, MambaInput<IO, 1>>(a, d_state, gated, s, ev);
+        case 2: return launch_io<IO, MambaInput<IO, 2>>(a, d_state, gated, s, ev);
+        case 3: return launch_io<IO, MambaInput<IO, 3>>(a, d_state, gated, s, ev);
+        case 4: return launch_io<IO, MambaInput<IO, 4>>(a, d_state, gated, s, ev);
     }
     return hipErrorInvalidValue;
 }
@@ -251,8 +346,25 @@ hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
 
 hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev) {
-    return io == 0 ? launch_io<float>(a, d_state, gated, s, ev)
-                   : launch_io<bf16_bits>(a, d_state, gated, s, ev);
+    return io == 0 ? launch_io<float, NoInput>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits, NoInput>(a, d_state, gated, s, ev);
+}
+
+hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                             hipEvent_t const *ev) {
+    return io == 0 ? launch_fused_io<float>(a, d_state, gated, s, ev)
+                   : launch_fused_io<bf16_bits>(a, d_state, gated, s, ev);
+}
+
+hipError_t launch_elem_fill(void *dst, const void *src, int64_t count, int elem_bytes,
+                            hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((count + 255) / 256));
+    if (elem_bytes == 4)
+        hipLaunchKernelGGL(k_state_fill, grid, dim3(256), 0, s, (float *)dst, (const float *)src, count);
+    else
+        hipLaunchKernelGGL(k_fill16, grid, dim3(256), 0, s, (uint16_t *)dst, (const uint16_t *)src, count);
+    return hipGetLastError();
 }
 
 hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStream_t s) {

@@ -21,6 +21,14 @@ struct ScanArgs {
     int32_t n_chunks;  // ceil(L / T), >= 1
     int32_t dblocks;   // channel blocks per batch row (grid x = batch * dblocks)
     int32_t threads;   // threads per block (multiple of 64, <= 256)
+    // Input stage (fused entry point only; conv_k = 0 and null pointers otherwise):
+    // x is the convolution's input and dt the raw step before softplus.
+    const float *conv_w;      // [Dn][conv_k], or null: x is used as is
+    const float *conv_b;      // [Dn], or null: no bias
+    const void *conv_state0;  // [batch][conv_k-1][Dn] of io, or null: zeros before step 0
+    void *conv_state_out;     // [batch][conv_k-1][Dn] of io, or null
+    const float *dt_bias;     // [Dn], or null
+    int32_t conv_k;           // 0 (no convolution) or 1..4
 };
 
 struct StepArgs {
@@ -29,6 +37,12 @@ struct StepArgs {
     const float *A, *D;
     void *y;
     int64_t n_layers, n_seq, Dn;
+    // Input stage (fused entry point only), as in ScanArgs with a leading layer index:
+    const float *conv_w;  // [n_layers][Dn][conv_k], or null
+    const float *conv_b;  // [n_layers][Dn], or null
+    void *conv_state;     // [n_layers][n_seq][conv_k-1][Dn] of io, read and written
+    const float *dt_bias; // [n_layers][Dn], or null
+    int32_t conv_k;       // 0 or 1..4
 };
 
 // Real diagonal state. io: 0 = f32, 1 = bf16. Returns hipSuccess or the launch error.
@@ -40,10 +54,18 @@ hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, 
 hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                                hipEvent_t const *ev);
 hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStream_t s);
+// Real state with the input stage: conv (a.conv_k in 0..4) and softplus on dt.
+hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                             hipEvent_t const *ev);
+// dst[i] = src ? src[i] : 0 for count elements of elem_bytes (2 or 4) bytes each.
+hipError_t launch_elem_fill(void *dst, const void *src, int64_t count, int elem_bytes,
+                            hipStream_t s);
 
 hipError_t launch_step_real(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                             hipStream_t s);
 hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                                hipStream_t s);
+hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                             hipStream_t s);
 
 }  // namespace ssm

@@ -147,12 +147,18 @@ constexpr int kB = 32;  // rows per block of the backward walk
 // First row (chunk-relative) of the window that covers the horizon, walking dt back
 // from row T-1 in whole blocks of kB rows; the next block is loaded while the
 // current one is summed, and every load of a block is issued before any is waited
-// on. amax = max over the lane's states of log2(e) * Re A. Returns 0 (the whole
-// chunk) when some lane does not reach the horizon within the whole blocks (A >= 0,
-// dt = 0, NaN, or simply a short chunk).
-template <typename IO>
+// on. amax = max over the lane's states of log2(e) * Re A; dtf maps a loaded value to
+// the step (the identity, or softplus when the kernel applies the input stage).
+// Returns 0 (the whole chunk) when some lane does not reach the horizon within the
+// whole blocks (A >= 0, dt = 0, NaN, or simply a short chunk).
+struct Identity {
+    __device__ __forceinline__ float operator()(float v) const { return v; }
+};
+
+template <typename IO, typename DtF = Identity>
 __device__ __forceinline__ uint32_t horizon_start(const RowStream<IO> &dt, uint32_t voff,
-                                                  uint32_t rb, uint32_t T, float amax) {
+                                                  uint32_t rb, uint32_t T, float amax,
+                                                  DtF dtf = DtF()) {
     if (!__any(amax < 0.0f) || T < (uint32_t)kB) return 0;
     float S = 0.0f;
     float cur[kB];
@@ -169,7 +175,7 @@ __device__ __forceinline__ uint32_t horizon_start(const RowStream<IO> &dt, uint3
         }
         __builtin_amdgcn_sched_barrier(0);  // sum the current block while nxt is in flight
 #pragma unroll
-        for (int k = 0; k < kB; ++k) S += cur[k];
+        for (int k = 0; k < kB; ++k) S += dtf(cur[k]);
         if (__all(amax * S <= -kHorizon)) return tn;
         if (!more) return 0;
         __builtin_amdgcn_sched_barrier(0);

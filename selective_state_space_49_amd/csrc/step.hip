@@ -16,7 +16,14 @@
 // same fp32 operations in the same order (the tree included), so that the decode
 // kernels can be checked bit for bit against them. The library is built with
 // floating-point contraction off; every fused multiply-add below is explicit.
+//
+// The fused entry point adds the MambaBlock input stage (ssm_input_stage.h): x_t is
+// the convolution's new input and dt_t the raw dt projection output. Every lane of a
+// channel computes u = silu(conv) from the carried convolution state and
+// dt = softplus(dt + bias) with the same operations (so the G lanes and the replay
+// agree bit for bit), and the channel's first lane writes the shifted state back.
 #include "ssm_device.h"
+#include "ssm_input_stage.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -40,6 +47,45 @@ __device__ __forceinline__ bool chan_of(const StepArgs &a, Chan &c, int &g) {
     c.ch = c.lq * a.Dn + c.d;
     return true;
 }
+
+// Input stage of one decode token: maps the loaded (x, dt) of a channel to the values
+// the recurrence uses.
+struct NoStepInput {
+    template <typename Chan>
+    static __device__ __forceinline__ void apply(const StepArgs &, const Chan &, bool, float &,
+                                                 float &) {}
+};
+
+// Ordered as in ssm_input_stage.h: dt = softplus(dt + bias); u = silu(conv over the
+// KC-1 carried inputs and x) (KC = 0: u = x). writer: this lane stores the new state
+// (the KC-1 newest inputs, x included) in place of the old one.
+template <typename IO, int KC>
+struct StepMamba {
+    template <typename Chan>
+    static __device__ __forceinline__ void apply(const StepArgs &a, const Chan &c, bool writer,
+                                                 float &xv, float &dv) {
+        const int64_t pd = c.l * a.Dn + c.d;  // (layer, channel) parameter index
+        dv = softplus(dv + (a.dt_bias ? a.dt_bias[pd] : 0.0f));
+        if constexpr (KC > 0) {
+            ConvSilu<KC> conv;
+#pragma unroll
+            for (int k = 0; k < KC; ++k) conv.w[k] = a.conv_w[pd * KC + k];
+            conv.bias = a.conv_b ? a.conv_b[pd] : 0.0f;
+            IO *st = (IO *)a.conv_state + c.lq * (KC - 1) * a.Dn + c.d;  // row j at st + j * Dn
+            if constexpr (KC > 1) {
+#pragma unroll
+                for (int j = 0; j < KC - 1; ++j) conv.hist[j] = Io<IO>::ld(st + j * a.Dn);
+            }
+            xv = conv(xv);
+            if constexpr (KC > 1) {
+                if (writer) {
+#pragma unroll
+                    for (int j = 0; j < KC - 1; ++j) Io<IO>::st(st + j * a.Dn, conv.hist[j]);
+                }
+            }
+        }
+    }
+};
 
 // The state is read once and written once per call: non-temporal (streaming) 16-byte
 // accesses keep it from displacing the reused A, B, C rows in the caches.
@@ -110,7 +156,7 @@ template <int N> struct RealGroups {
     static constexpr int K = N / G;
 };
 
-template <typename IO, int N, bool GATED>
+template <typename IO, int N, bool GATED, typename In>
 __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
     Chan c;
@@ -123,8 +169,9 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     VecLd<float, K>::ld(a.A + (c.l * a.Dn + c.d) * N + g * K, av);
     VecLd<IO, K>::ld((const IO *)a.B + c.lq * N + g * K, bv);
     VecLd<IO, K>::ld((const IO *)a.C + c.lq * N + g * K, cv);
-    const float xv = Io<IO>::ld((const IO *)a.x + c.ch);
-    const float dv = Io<IO>::ld((const IO *)a.dt + c.ch);
+    float xv = Io<IO>::ld((const IO *)a.x + c.ch);
+    float dv = Io<IO>::ld((const IO *)a.dt + c.ch);
+    In::apply(a, c, g == 0, xv, dv);
     const float u = dv * xv;
     float p = 0.0f;
 #pragma unroll
@@ -148,7 +195,7 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     }
 }
 
-template <typename IO, int N, bool GATED>
+template <typename IO, int N, bool GATED, typename In>
 __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
     Chan c;
@@ -159,8 +206,9 @@ __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     const float *Ap = a.A + (c.l * a.Dn + c.d) * N;
     const IO *Bp = (const IO *)a.B + c.lq * N;
     const IO *Cp = (const IO *)a.C + c.lq * N;
-    const float xv = Io<IO>::ld((const IO *)a.x + ch);
-    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    float xv = Io<IO>::ld((const IO *)a.x + ch);
+    float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    In::apply(a, c, true, xv, dv);
     const float u = dv * xv;
     float p[G];
     for (int g = 0; g < G; ++g) {
@@ -279,17 +327,41 @@ inline dim3 grid_for(const StepArgs &a, int lanes_per_ch) {
                 (unsigned)a.n_layers);
 }
 
-template <typename IO, int N>
+template <typename IO, int N, typename In = NoStepInput>
 hipError_t launch_real_n(const StepArgs &a, bool gated, bool replay, hipStream_t s) {
     const dim3 blk(256), grid(grid_for(a, replay ? 1 : RealGroups<N>::G));
     if (replay) {
-        if (gated) hipLaunchKernelGGL((k_step_replay<IO, N, true>), grid, blk, 0, s, a);
-        else hipLaunchKernelGGL((k_step_replay<IO, N, false>), grid, blk, 0, s, a);
+        if (gated) hipLaunchKernelGGL((k_step_replay<IO, N, true, In>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_step_replay<IO, N, false, In>), grid, blk, 0, s, a);
     } else {
-        if (gated) hipLaunchKernelGGL((k_step<IO, N, true>), grid, blk, 0, s, a);
-        else hipLaunchKernelGGL((k_step<IO, N, false>), grid, blk, 0, s, a);
+        if (gated) hipLaunchKernelGGL((k_step<IO, N, true, In>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_step<IO, N, false, In>), grid, blk, 0, s, a);
     }
     return hipGetLastError();
+}
+
+template <typename IO, typename In>
+hipError_t launch_fused_n(const StepArgs &a, int d_state, bool gated, bool replay, hipStream_t s) {
+    switch (d_state) {
+        case 1: return launch_real_n<IO, 1, In>(a, gated, replay, s);
+        case 2: return launch_real_n<IO, 2, In>(a, gated, replay, s);
+        case 4: return launch_real_n<IO, 4, In>(a, gated, replay, s);
+        case 8: return launch_real_n<IO, 8, In>(a, gated, replay, s);
+        case 16: return launch_real_n<IO, 16, In>(a, gated, replay, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t launch_fused_io(const StepArgs &a, int d_state, bool gated, bool replay, hipStream_t s) {
+    switch (a.conv_k) {
+        case 0: return launch_fused_n<IO, StepMamba<IO, 0>>(a, d_state, gated, replay, s);
+        case 1: return launch_fused_n<IO, StepMamba<IO, 1>>(a, d_state, gated, replay, s);
+        case 2: return launch_fused_n<IO, StepMamba<IO, 2>>(a, d_state, gated, replay, s);
+        case 3: return launch_fused_n<IO, StepMamba<IO, 3>>(a, d_state, gated, replay, s);
+        case 4: return launch_fused_n<IO, StepMamba<IO, 4>>(a, d_state, gated, replay, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename IO, int N>
@@ -329,6 +401,12 @@ hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gate
                                hipStream_t s) {
     return io == 0 ? launch_io<float, true>(a, d_state, gated, replay, s)
                    : launch_io<bf16_bits, true>(a, d_state, gated, replay, s);
+}
+
+hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                             hipStream_t s) {
+    return io == 0 ? launch_fused_io<float>(a, d_state, gated, replay, s)
+                   : launch_fused_io<bf16_bits>(a, d_state, gated, replay, s);
 }
 
 }  // namespace ssm

@@ -110,3 +110,46 @@ def test_step_argument_errors(lib):
         assert call(fn, Dn=0) == SHAPE
         assert call(fn, Ln=-1) == SHAPE
         assert call(fn, Ln=0) == OK  # nothing to do, nothing enqueued
+
+
+def _fused_raw(lib, x=0x100000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None,
+               h0=None, w=0x1000, cb=None, K=4, s0=None, so=None, db=None, y=0x200000, hf=None,
+               batch=1, L=8, Dn=4, N=4, io=0, chunk=0, ws=None, wsb=0):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lib.ssm_scan_fwd_fused(p(x), p(dt), p(A), p(B), p(C), p(D), p(z), p(h0), p(w), p(cb), K,
+                                  p(s0), p(so), p(db), p(y), p(hf), batch, L, Dn, N, io, chunk,
+                                  p(ws), wsb, None)
+
+
+def test_fused_scan_argument_errors(lib):
+    assert _fused_raw(lib, K=5) == UNSUP
+    assert _fused_raw(lib, K=-1) == UNSUP
+    assert _fused_raw(lib, w=None) == NULL            # conv_k > 0 needs the filter
+    assert _fused_raw(lib, w=0x1002) == ALIGN
+    assert _fused_raw(lib, db=0x1001) == ALIGN
+    assert _fused_raw(lib, io=1, s0=0x3001) == ALIGN  # bf16 state must be element-aligned
+    assert _fused_raw(lib, N=3) == UNSUP
+    # x_in is 1*8*4*4 = 128 bytes at 0x100000: y inside it, or the state out inside it
+    assert _fused_raw(lib, y=0x100040) == UNSUP
+    assert _fused_raw(lib, so=0x100010) == UNSUP
+    assert "overlap" in ssm.ssm_last_error()
+    # the state out over the state in (3 rows of 4 floats = 48 bytes)
+    assert _fused_raw(lib, s0=0x5000, so=0x5020) == UNSUP
+    assert _fused_raw(lib, L=200, chunk=64) == WS
+
+
+def test_fused_step_argument_errors(lib):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def call(fn, cs=0x2000, w=0x1000, K=4, db=None, N=16, io=1, Ln=2, h=0x1000):
+        return getattr(lib, fn)(p(h), p(cs), p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                p(0x1000), None, p(w), None, K, p(db), p(0x1000), Ln, 3, 4, N, io, None)
+
+    for fn in ("ssm_step_fused", "ssm_step_fused_replay"):
+        assert call(fn, K=7) == UNSUP
+        assert call(fn, cs=None) == NULL               # conv_k > 1 needs the carried state
+        assert call(fn, w=None) == NULL
+        assert call(fn, w=0x1001) == ALIGN
+        assert call(fn, N=5) == UNSUP
+        assert call(fn, h=None) == NULL
+        assert call(fn, Ln=0) == OK

@@ -18,6 +18,14 @@ Distributions (``N(mu, s)`` means mean mu, standard deviation s):
 Complex-state workload: a = exp(N(0, 0.5)), theta ~ U(-pi, pi), A = (-a, theta) as
 (re, im); Re/Im of B and C each ~ N(0, 1).
 
+Input stage of the MambaBlock (fused entry points; a generator of its own, seeded
+seed + 17, so the draws above do not change): the convolution filter and bias
+~ U(-1/sqrt(K), 1/sqrt(K)) per channel (PyTorch's default Conv1d initialisation for a
+depthwise filter, fan-in K); dt_bias ~ N(0, 0.1) per channel; the carried conv state
+~ N(0, 1); the raw step dt_raw ~ N(-1, 0.5) (so softplus(dt_raw + dt_bias) follows the
+dt recipe above). x doubles as the convolution's input. Draw order: conv_w, conv_b,
+dt_bias, conv_state0, dt_raw.
+
 Every draw is made in float32 and then rounded to the I/O dtype (round-to-nearest-
 even for bfloat16), so both sides read exactly the same bits. The draw order within a
 call is fixed: A, D, x, z, dt, B, C. Large tensors are drawn in fixed-size slabs so
@@ -34,7 +42,8 @@ import torch
 __all__ = [
     "ScanShape", "DecodeShape", "WORKLOADS", "SCAN_WORKLOADS", "io_torch_dtype",
     "make_scan_inputs", "make_decode_params", "make_decode_step", "make_h0",
-    "sample_channels", "SLAB_ELEMS",
+    "sample_channels", "SLAB_ELEMS", "make_input_stage", "make_decode_input_stage",
+    "make_decode_dt_raw",
 ]
 
 # Elements drawn per randn call for big tensors (fixed: part of the seeded recipe).
@@ -222,3 +231,54 @@ def sample_channels(n_total: int, k: int, seed: int = 11) -> torch.Tensor:
     if k > 1:
         idx[1] = n_total - 1
     return torch.unique(idx)
+
+
+def make_input_stage(shape: ScanShape, K: int, device="cpu", seed: Optional[int] = None,
+                     with_state=True) -> dict:
+    """Input-stage tensors of a prefill workload for a K-tap filter (K = 0: none):
+    conv_w [d_inner, K], conv_b [d_inner], dt_bias [d_inner] (float32),
+    conv_state0 [batch, K-1, d_inner] and dt_raw [batch, L, d_inner] (I/O dtype)."""
+    seed = (shape.seed if seed is None else seed) + 17
+    g = _gen(seed, device)
+    io = io_torch_dtype(shape.io)
+    b, L, Dn = shape.batch, shape.L, shape.d_inner
+    out = {"conv_w": None, "conv_b": None, "conv_state0": None}
+    if K > 0:
+        bound = 1.0 / math.sqrt(K)
+        out["conv_w"] = _uniform((Dn, K), -bound, bound, g, device)
+        out["conv_b"] = _uniform((Dn,), -bound, bound, g, device)
+    out["dt_bias"] = _normal((Dn,), 0.0, 0.1, g, device, torch.float32)
+    if K > 1 and with_state:
+        out["conv_state0"] = _normal((b, K - 1, Dn), 0.0, 1.0, g, device, io)
+    out["dt_raw"] = _normal((b, L, Dn), -1.0, 0.5, g, device, io)
+    return out
+
+
+def make_decode_input_stage(shape: DecodeShape, K: int, device="cpu",
+                            seed: Optional[int] = None) -> dict:
+    """Per-layer input-stage parameters of a decode workload: conv_w [n_layers,
+    d_inner, K], conv_b and dt_bias [n_layers, d_inner] (float32) and the initial conv
+    state [n_layers, n_seq, K-1, d_inner] (I/O dtype)."""
+    seed = (shape.seed if seed is None else seed) + 17
+    g = _gen(seed, device)
+    io = io_torch_dtype(shape.io)
+    Ln, S, Dn = shape.n_layers, shape.n_seq, shape.d_inner
+    out = {"conv_w": None, "conv_b": None, "conv_state": None}
+    if K > 0:
+        bound = 1.0 / math.sqrt(K)
+        out["conv_w"] = _uniform((Ln, Dn, K), -bound, bound, g, device)
+        out["conv_b"] = _uniform((Ln, Dn), -bound, bound, g, device)
+    out["dt_bias"] = _normal((Ln, Dn), 0.0, 0.1, g, device, torch.float32)
+    if K > 1:
+        out["conv_state"] = _normal((Ln, S, K - 1, Dn), 0.0, 1.0, g, device, io)
+    return out
+
+
+def make_decode_dt_raw(shape: DecodeShape, step: int, device="cpu",
+                       seed: Optional[int] = None) -> torch.Tensor:
+    """The raw step dt_raw ~ N(-1, 0.5) [n_layers, n_seq, d_inner] of one decode step
+    (its own generator per step, seeded from (seed + 17, step))."""
+    seed = (shape.seed if seed is None else seed) + 17
+    g = _gen(seed * 100003 + 1 + int(step), device)
+    Ln, S, Dn = shape.n_layers, shape.n_seq, shape.d_inner
+    return _normal((Ln, S, Dn), -1.0, 0.5, g, device, io_torch_dtype(shape.io))
