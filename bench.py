@@ -27,10 +27,10 @@ The CPU baseline is the fp64 oracle as it stands, run on a bounded sample of the
 same workload (a subset of channels over the full sequence; channels are
 independent) from several host threads.
 
---fused times the same prefill workload through ssm_scan_fwd_fused instead: x is the
-input of the MambaBlock's causal depthwise convolution (--conv-k taps, default 4) and
-dt the raw dt projection output, and the convolution + silu and softplus run inside
-the scan's load stage.
+--fused times the same workload through ssm_scan_fwd_fused / ssm_step_fused instead:
+x is the input of the MambaBlock's causal depthwise convolution (--conv-k taps,
+default 4) and dt the raw dt projection output, and the convolution + silu and
+softplus run inside the scan's load stage (decode: with the carried conv state).
 """
 from __future__ import annotations
 
@@ -116,6 +116,17 @@ def decode_bytes(s, io_bytes: int) -> float:
             + 2 * Ln * S * N * io_bytes + Ln * Dn * (N + 1) * 4)
 
 
+def decode_lane_ops(s) -> float:
+    """Vector-ALU instructions per channel of a decode step: 5 per state as in prefill,
+    dt*x, D*x + acc, the pairwise tree over the G = 4 lanes of a channel (2 adds), and
+    with bf16 I/O the widening and conversion; gated: the gate and the widening of z."""
+    bf16 = s.io == "bf16"
+    per_elem = 2 + 2 + (3 if bf16 else 0)
+    if s.gated:
+        per_elem += 6 + (1 if bf16 else 0)
+    return 5 * s.d_state + per_elem
+
+
 # ----------------------------------------------------------------- runs
 def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None):
     """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter."""
@@ -191,13 +202,21 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     return info, d
 
 
-def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True):
+def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None):
+    """conv_k None: ssm_step; else ssm_step_fused with a conv_k-tap filter."""
     dev = "cuda"
     Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
     par = workloads.make_decode_params(shape, dev)
     h = torch.zeros((Ln, S, Dn, N), device=dev)
     log("drawing", warmup + steps, "token steps of inputs")
     toks = [workloads.make_decode_step(shape, k, dev) for k in range(warmup + steps)]
+    fused = conv_k is not None
+    if fused:
+        ist = workloads.make_decode_input_stage(shape, conv_k, dev)
+        for k, t in enumerate(toks):
+            t["dt"] = workloads.make_decode_dt_raw(shape, k, dev)
+        sl = lambda v, l: None if v is None else v[l:l + 1]
+        ist_l = [{k: sl(v, l) for k, v in ist.items()} for l in range(Ln)]
     y = torch.empty((Ln, S, Dn), dtype=toks[0]["x"].dtype, device=dev)
     A_l = [par["A"][l:l + 1] for l in range(Ln)]
     D_l = [par["D"][l:l + 1] for l in range(Ln)]
@@ -211,8 +230,14 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True):
             t = per_layer[k * Ln + l]
             if timed:
                 ev[2 * ((k - warmup) * Ln + l)].record()
-            ssm.ssm_step(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
-                         y_t=y[l:l + 1])
+            if fused:
+                p = ist_l[l]
+                ssm.ssm_step_fused(h_l[l], p["conv_state"], t["x"], t["dt"], A_l[l], t["B"], t["C"],
+                                   D_l[l], t["z"], conv_w=p["conv_w"], conv_b=p["conv_b"],
+                                   dt_bias=p["dt_bias"], y_t=y[l:l + 1])
+            else:
+                ssm.ssm_step(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
+                             y_t=y[l:l + 1])
             if timed:
                 ev[2 * ((k - warmup) * Ln + l) + 1].record()
 
@@ -253,10 +278,16 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True):
         wall = time.perf_counter() - t0
         kern = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps * Ln)) / (steps * Ln)
     io_bytes = 2 if shape.io == "bf16" else 4
+    nbytes = decode_bytes(shape, io_bytes)
+    lane_ops = decode_lane_ops(shape)
+    if fused:
+        K = conv_k
+        nbytes += Ln * S * Dn * 2 * max(K - 1, 0) * io_bytes + Ln * Dn * (K + (1 if K else 0) + 1) * 4
+        lane_ops += input_stage_lane_ops(K)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3,
-        "elements_per_step": Ln * S * Dn, "bytes_per_step": decode_bytes(shape, io_bytes),
-        "lane_ops_per_elem": 6 * N + 14, "dominant_ms": kern * Ln, "per_call_ms": kern,
+        "elements_per_step": Ln * S * Dn, "bytes_per_step": nbytes,
+        "lane_ops_per_elem": lane_ops, "dominant_ms": kern * Ln, "per_call_ms": kern,
         "kernel": "k_step", "source": "step", "phases_ms": {"ssm_step_per_layer": kern},
         "graph": graph,
     }
@@ -320,8 +351,8 @@ def main():
                     help="decode: launch the per-layer calls eagerly instead of replaying one "
                          "captured HIP graph per token")
     ap.add_argument("--fused", action="store_true",
-                    help="prefill through ssm_scan_fwd_fused (conv + silu and softplus fused "
-                         "into the load stage)")
+                    help="through ssm_scan_fwd_fused / ssm_step_fused (conv + silu and softplus "
+                         "fused into the load stage)")
     ap.add_argument("--conv-k", type=int, default=4, help="filter taps with --fused (0..4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for "
@@ -353,7 +384,8 @@ def main():
     is_decode = isinstance(shape, workloads.DecodeShape)
     steps = max(1, args.steps if not is_decode else min(args.steps, 64))
     if is_decode:
-        info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph)
+        info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph,
+                             conv_k=args.conv_k if args.fused else None)
     else:
         if args.fused and shape.complex_state:
             print("--fused applies to the real-state prefill workloads", file=sys.stderr)
@@ -387,6 +419,9 @@ def main():
         cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
                "calls_per_step": shape.n_layers, "hip_graph_per_token": info["graph"]}
+        if args.fused:
+            cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
+                                  "softplus_dt": True, "entry_point": "ssm_step_fused"}
     else:
         cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,

@@ -48,41 +48,43 @@ __device__ __forceinline__ bool chan_of(const StepArgs &a, Chan &c, int &g) {
     return true;
 }
 
-// Input stage of one decode token: maps the loaded (x, dt) of a channel to the values
-// the recurrence uses.
+// Input stage of one decode token: apply() maps the loaded (x, dt) of a channel to the
+// values the recurrence uses; store() writes what the next token needs. store() is
+// called after the channel's output, so its stores wait on nothing.
 struct NoStepInput {
     template <typename Chan>
-    static __device__ __forceinline__ void apply(const StepArgs &, const Chan &, bool, float &,
-                                                 float &) {}
+    __device__ __forceinline__ void apply(const StepArgs &, const Chan &, float &, float &) {}
+    __device__ __forceinline__ void store(const StepArgs &) const {}
 };
 
 // Ordered as in ssm_input_stage.h: dt = softplus(dt + bias); u = silu(conv over the
-// KC-1 carried inputs and x) (KC = 0: u = x). writer: this lane stores the new state
-// (the KC-1 newest inputs, x included) in place of the old one.
+// KC-1 carried inputs and x) (KC = 0: u = x). store() puts the KC-1 newest inputs,
+// x included, in place of the old state.
 template <typename IO, int KC>
 struct StepMamba {
+    ConvSilu<(KC > 0 ? KC : 1)> conv;
+    IO *st;  // the channel's conv state: row j at st + j * Dn
+
     template <typename Chan>
-    static __device__ __forceinline__ void apply(const StepArgs &a, const Chan &c, bool writer,
-                                                 float &xv, float &dv) {
+    __device__ __forceinline__ void apply(const StepArgs &a, const Chan &c, float &xv, float &dv) {
         const int64_t pd = c.l * a.Dn + c.d;  // (layer, channel) parameter index
         dv = softplus(dv + (a.dt_bias ? a.dt_bias[pd] : 0.0f));
         if constexpr (KC > 0) {
-            ConvSilu<KC> conv;
 #pragma unroll
             for (int k = 0; k < KC; ++k) conv.w[k] = a.conv_w[pd * KC + k];
             conv.bias = a.conv_b ? a.conv_b[pd] : 0.0f;
-            IO *st = (IO *)a.conv_state + c.lq * (KC - 1) * a.Dn + c.d;  // row j at st + j * Dn
+            st = (IO *)a.conv_state + c.lq * (KC - 1) * a.Dn + c.d;
             if constexpr (KC > 1) {
 #pragma unroll
                 for (int j = 0; j < KC - 1; ++j) conv.hist[j] = Io<IO>::ld(st + j * a.Dn);
             }
             xv = conv(xv);
-            if constexpr (KC > 1) {
-                if (writer) {
+        }
+    }
+    __device__ __forceinline__ void store(const StepArgs &a) const {
+        if constexpr (KC > 1) {
 #pragma unroll
-                    for (int j = 0; j < KC - 1; ++j) Io<IO>::st(st + j * a.Dn, conv.hist[j]);
-                }
-            }
+            for (int j = 0; j < KC - 1; ++j) Io<IO>::st(st + j * a.Dn, conv.hist[j]);
         }
     }
 };
@@ -171,7 +173,13 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     VecLd<IO, K>::ld((const IO *)a.C + c.lq * N + g * K, cv);
     float xv = Io<IO>::ld((const IO *)a.x + c.ch);
     float dv = Io<IO>::ld((const IO *)a.dt + c.ch);
-    In::apply(a, c, g == 0, xv, dv);
+    // z and D are needed by the group's first lane only; every lane loads them here,
+    // with the rest (the lanes of a group read the same address), so that no load is
+    // issued after the arithmetic.
+    const float zv = GATED ? Io<IO>::ld((const IO *)a.z + c.ch) : 0.0f;
+    const float Dd = a.D[c.l * a.Dn + c.d];
+    In in;
+    in.apply(a, c, xv, dv);
     const float u = dv * xv;
     float p = 0.0f;
 #pragma unroll
@@ -189,9 +197,10 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
         hp[0] = hv[0];
     }
     if (g == 0) {
-        float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, acc);
-        if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + c.ch));
+        float yv = __builtin_fmaf(Dd, xv, acc);
+        if (GATED) yv = yv * silu(zv);
         Io<IO>::st((IO *)a.y + c.ch, yv);
+        in.store(a);
     }
 }
 
@@ -208,7 +217,8 @@ __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     const IO *Cp = (const IO *)a.C + c.lq * N;
     float xv = Io<IO>::ld((const IO *)a.x + ch);
     float dv = Io<IO>::ld((const IO *)a.dt + ch);
-    In::apply(a, c, true, xv, dv);
+    In in;
+    in.apply(a, c, xv, dv);
     const float u = dv * xv;
     float p[G];
     for (int g = 0; g < G; ++g) {
@@ -223,6 +233,7 @@ __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, tree_sum<G>(p));
     if (GATED) yv = yv * silu(Io<IO>::ld((const IO *)a.z + ch));
     Io<IO>::st((IO *)a.y + ch, yv);
+    in.store(a);
 }
 
 // ---------------------------------------------------------------- complex state
