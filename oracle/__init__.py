@@ -63,6 +63,8 @@ def _load():
         lib.oracle_conv_silu_f64.restype = ctypes.c_int
         lib.oracle_softplus_f64.argtypes = [i64, i64, dp, dp, dp]
         lib.oracle_softplus_f64.restype = ctypes.c_int
+        lib.oracle_scan_bwd_f64.argtypes = [i64, i64, i64, i64] + [dp] * 18
+        lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -161,6 +163,31 @@ def step_complex(h, x, dt, A, B, C, D, z=None):
 def state_bytes(n_layers: int, channels: int, d_state: int, bytes_per_value: int) -> int:
     """Size of a fixed-size SSM state in bytes (independent of sequence length)."""
     return int(_load().oracle_state_bytes(n_layers, channels, d_state, bytes_per_value))
+
+
+def scan_bwd(x, dt, A, B, C, D, z=None, h0=None, dy=None, dh_final=None):
+    """Gradients of sum(dy * y) + sum(dh_final * h_final) of the real-state prefill.
+    Returns a dict with dx, ddt, dz (None when ungated) [b, L, Dn]; dA [Dn, N];
+    dB, dC [b, L, N]; dD [Dn]; dh0 [b, Dn, N]."""
+    x, dt, A, B, C, D, z, h0, dy, dh_final = map(to_f64, (x, dt, A, B, C, D, z, h0, dy, dh_final))
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    _check(dt, (b, L, Dn), "dt"); _check(B, (b, L, N), "B"); _check(C, (b, L, N), "C")
+    _check(A, (Dn, N), "A"); _check(D, (Dn,), "D"); _check(dy, (b, L, Dn), "dy")
+    if z is not None: _check(z, (b, L, Dn), "z")
+    if h0 is not None: _check(h0, (b, Dn, N), "h0")
+    if dh_final is not None: _check(dh_final, (b, Dn, N), "dh_final")
+    g = {k: np.empty(shp) for k, shp in [("dx", (b, L, Dn)), ("ddt", (b, L, Dn)), ("dA", (Dn, N)),
+                                         ("dB", (b, L, N)), ("dC", (b, L, N)), ("dD", (Dn,)),
+                                         ("dh0", (b, Dn, N))]}
+    g["dz"] = np.empty((b, L, Dn)) if z is not None else None
+    rc = _load().oracle_scan_bwd_f64(b, L, Dn, N, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(z),
+                                     _p(h0), _p(dy), _p(dh_final), _p(g["dx"]), _p(g["ddt"]),
+                                     _p(g["dA"]), _p(g["dB"]), _p(g["dC"]), _p(g["dD"]), _p(g["dz"]),
+                                     _p(g["dh0"]))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_bwd_f64 failed")
+    return g
 
 
 def conv_silu(x, w, cb=None, state0=None):

@@ -286,3 +286,92 @@ int oracle_softplus_f64(int64_t rows, int64_t Dn, const double *raw, const doubl
             dt[i * Dn + d] = softplus(raw[i * Dn + d] + (bias ? bias[d] : 0.0));
     return 0;
 }
+
+/* ------------------------------------------------------------------ backward
+ * Gradients of the real-state prefill, for training: given dy = dLoss/dy and
+ * optionally dh_final = dLoss/dh_final, the gradients of
+ *     Loss = sum dy * y + sum dh_final * h_final
+ * with respect to x, dt, z [batch][L][Dn], A [Dn][N], B, C [batch][L][N],
+ * Dv [Dn] and h0 [batch][Dn][N]. The pages name the training-time evaluation of
+ * the SSM ("Jamba — SSM-Transformer Híbrido", section "Um SSM em uma página", the
+ * convolution form used in training) but print no backward; this is the chain
+ * rule through the forward loop above, written out step by step:
+ *     h_t = a_t h_{t-1} + dt_t B_t x_t,  a_t = exp(dt_t A),  o_t = C_t.h_t + D x_t,
+ *     y_t = o_t g(z_t),  g = silu,  g'(z) = s (1 + z (1 - s)),  s = 1 / (1 + e^-z).
+ * The adjoint lam_t = dLoss/dh_t obeys lam_t = do_t C_t + a_{t+1} lam_{t+1}, run
+ * backwards from lam = dh_final, with do_t = dy_t g(z_t). Then, per step,
+ *     dx_t  = do_t D + sum_n lam_t[n] dt_t B_t[n]
+ *     ddt_t = sum_n lam_t[n] (x_t B_t[n] + A[n] a_t[n] h_{t-1}[n])
+ *     dz_t  = dy_t o_t g'(z_t)
+ *     dA[n] += lam_t[n] dt_t a_t[n] h_{t-1}[n]      dD += do_t x_t
+ *     dB_t[n] += lam_t[n] dt_t x_t                  dC_t[n] += do_t h_t[n]
+ * (dA, dD summed over batch and steps; dB, dC over channels), and
+ * dh0 = a_0 lam_0. The states h_t are kept from a forward pass over the channel.
+ * dh_final, z, h0 may be NULL (zero, ungated, zero); dz, dh0 may be NULL (not
+ * wanted). Every output is overwritten. */
+int oracle_scan_bwd_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
+                        const double *x, const double *dt, const double *A,
+                        const double *B, const double *C, const double *Dv,
+                        const double *z, const double *h0, const double *dy,
+                        const double *dh_final, double *dx, double *ddt, double *dA,
+                        double *dB, double *dC, double *dD, double *dz, double *dh0)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || N <= 0) return -1;
+    double *hs = (double *)malloc((size_t)(L + 1) * (size_t)N * sizeof(double));
+    double *lam = (double *)malloc((size_t)N * sizeof(double));
+    if (!hs || !lam) { free(hs); free(lam); return -1; }
+    memset(dA, 0, (size_t)(Dn * N) * sizeof(double));
+    memset(dD, 0, (size_t)Dn * sizeof(double));
+    memset(dB, 0, (size_t)(batch * L * N) * sizeof(double));
+    memset(dC, 0, (size_t)(batch * L * N) * sizeof(double));
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < Dn; ++d) {
+            /* forward, keeping every state: hs[t + 1] = h_t, hs[0] = h0 */
+            for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t i = (b * L + t) * Dn + d;
+                const int64_t s = (b * L + t) * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double a = exp(dt[i] * A[d * N + n]);
+                    hs[(t + 1) * N + n] = a * hs[t * N + n] + (dt[i] * B[s + n]) * x[i];
+                }
+            }
+            /* backward */
+            for (int64_t n = 0; n < N; ++n) lam[n] = dh_final ? dh_final[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t i = (b * L + t) * Dn + d;
+                const int64_t s = (b * L + t) * N;
+                const double xv = x[i], dv = dt[i];
+                double o = Dv[d] * xv;
+                for (int64_t n = 0; n < N; ++n) o = o + C[s + n] * hs[(t + 1) * N + n];
+                double dout = dy[i];
+                if (z) {
+                    const double sg = 1.0 / (1.0 + exp(-z[i]));
+                    dout = dy[i] * (z[i] * sg);
+                    if (dz) dz[i] = dy[i] * o * (sg * (1.0 + z[i] * (1.0 - sg)));
+                }
+                dD[d] += dout * xv;
+                double gx = dout * Dv[d], gdt = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double lt = lam[n] + dout * C[s + n];       /* lam_t[n] */
+                    const double a = exp(dv * A[d * N + n]);
+                    const double hp = hs[t * N + n];                   /* h_{t-1}[n] */
+                    dC[s + n] += dout * hs[(t + 1) * N + n];
+                    dB[s + n] += lt * dv * xv;
+                    gx += lt * dv * B[s + n];
+                    gdt += lt * (xv * B[s + n] + A[d * N + n] * a * hp);
+                    dA[d * N + n] += lt * dv * a * hp;
+                    lam[n] = a * lt;                                  /* a_t lam_t */
+                }
+                dx[i] = gx;
+                ddt[i] = gdt;
+            }
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n) dh0[(b * Dn + d) * N + n] = lam[n];
+        }
+    }
+    if (z == NULL && dz != NULL) memset(dz, 0, (size_t)(batch * L * Dn) * sizeof(double));
+    free(hs);
+    free(lam);
+    return 0;
+}

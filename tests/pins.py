@@ -23,6 +23,9 @@ pages or plain mathematics fix:
                 theta = 0 equals the real one.
   printed value the fixed-size state arithmetic of the memory-budget section
                 (tests/golden/state_memory.json).
+  backward      central finite differences of sum(dy y) + sum(dh_final h_final)
+                through the forward oracle, for every element of every input, against
+                the backward oracle's gradients.
   input stage   the MambaBlock's causal depthwise convolution against numpy's
                 np.convolve (a true convolution, so the taps go in reversed) and an
                 impulse response; the carried conv state against the plain
@@ -431,6 +434,40 @@ def pin_fused_step_equals_scan(O, tol=1e-12):
         assert np.array_equal(css[l], so), f"fused decode conv state, layer {l}"
 
 
+# ---------------------------------------------------------------- backward
+def _loss(O, inp, dy, dhf):
+    y, hf = O.scan(**inp)
+    return float(np.sum(dy * y) + (np.sum(dhf * hf) if dhf is not None else 0.0))
+
+
+def pin_backward_finite_differences(O, tol=1e-7):
+    # Every element of every input is perturbed by +-eps (relative to its size) and
+    # the loss difference quotient compared with the gradient: truncation is
+    # O(eps^2) ~ 1e-12 and rounding ~1e-16 / eps ~ 1e-10, far inside tol.
+    for seed, kw, with_dhf in [(71, {}, True), (72, dict(gated=False, with_h0=False), False)]:
+        inp = tiny_real(seed, b=2, L=5, Dn=2, N=3, **kw)
+        r = np.random.default_rng(seed + 1)
+        dy = r.normal(0, 1, inp["x"].shape)
+        dhf = r.normal(0, 1, (2, 2, 3)) if with_dhf else None
+        g = O.scan_bwd(**inp, dy=dy, dh_final=dhf)
+        names = {"x": "dx", "dt": "ddt", "z": "dz", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+        for name, gname in names.items():
+            if inp[name] is None:
+                continue
+            base = inp[name]
+            fd = np.empty(base.shape)
+            for idx in np.ndindex(base.shape):
+                eps = 1e-6 * max(1.0, abs(base[idx]))
+                hi = dict(inp); hi[name] = base.copy(); hi[name][idx] += eps
+                lo = dict(inp); lo[name] = base.copy(); lo[name][idx] -= eps
+                fd[idx] = (_loss(O, hi, dy, dhf) - _loss(O, lo, dy, dhf)) / (2 * eps)
+            scale = max(1.0, float(np.max(np.abs(fd))))
+            err = float(np.max(np.abs(fd - g[gname]))) / scale
+            assert err <= tol, f"backward {gname} vs finite differences: {err:.2e} (seed {seed})"
+        if inp["z"] is None:
+            assert g["dz"] is None
+
+
 ALL_PINS = [
     pin_brute_force, pin_convolution, pin_geometric_series, pin_dt_zero, pin_linearity,
     pin_split_resume, pin_step_equals_scan, pin_isolation, pin_state_bytes,
@@ -440,5 +477,5 @@ ALL_PINS = [
     pin_layers_are_independent,
     lambda O: pin_layers_are_independent(O, complex_state=True),
     pin_conv_matches_numpy, pin_conv_impulse, pin_conv_state_carry, pin_softplus,
-    pin_fused_identity_filter, pin_fused_step_equals_scan,
+    pin_fused_identity_filter, pin_fused_step_equals_scan, pin_backward_finite_differences,
 ]

@@ -59,6 +59,15 @@ MUTANTS = {
     "dt_bias_dropped": ("softplus(raw[i * Dn + d] + (bias ? bias[d] : 0.0));", "softplus(raw[i * Dn + d]);"),
     "dt_bias_row_index": ("softplus(raw[i * Dn + d] + (bias ? bias[d] : 0.0));",
                           "softplus(raw[i * Dn + d] + (bias ? bias[i % Dn] : 0.0));"),
+    "bwd_ddt_without_decay_term": ("gdt += lt * (xv * B[s + n] + A[d * N + n] * a * hp);", "gdt += lt * (xv * B[s + n]);"),
+    "bwd_dA_from_new_state": ("dA[d * N + n] += lt * dv * a * hp;", "dA[d * N + n] += lt * dv * a * hs[(t + 1) * N + n];"),
+    "bwd_adjoint_not_decayed": ("lam[n] = a * lt;", "lam[n] = lt;"),
+    "bwd_gate_derivative": ("(sg * (1.0 + z[i] * (1.0 - sg)))", "(sg)"),
+    "bwd_dC_from_old_state": ("dC[s + n] += dout * hs[(t + 1) * N + n];", "dC[s + n] += dout * hs[t * N + n];"),
+    "bwd_dx_skip_dropped": ("double gx = dout * Dv[d], gdt = 0.0;", "double gx = 0.0, gdt = 0.0;"),
+    "bwd_dD_ungated": ("dD[d] += dout * xv;", "dD[d] += dy[i] * xv;"),
+    "bwd_dh_final_ignored": ("lam[n] = dh_final ? dh_final[(b * Dn + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
+    "bwd_dB_without_dt": ("dB[s + n] += lt * dv * xv;", "dB[s + n] += lt * xv;"),
 }
 
 
@@ -84,7 +93,8 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     real = oracle._load()
     lib = ctypes.CDLL(str(so))
     for fname in ("oracle_scan_f64", "oracle_scan_c128", "oracle_step_f64", "oracle_step_c128",
-                  "oracle_state_bytes", "oracle_conv_silu_f64", "oracle_softplus_f64"):
+                  "oracle_state_bytes", "oracle_conv_silu_f64", "oracle_softplus_f64",
+                  "oracle_scan_bwd_f64"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
