@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "real": [CSRC + "scan_real.hip", CSRC + "ssm_input_stage.h"],
     "complex": [CSRC + "scan_complex.hip"],
     "step": [CSRC + "step.hip", CSRC + "ssm_input_stage.h"],
+    "bwd": [CSRC + "scan_bwd.hip", CSRC + "scan_real.hip", CSRC + "ssm_input_stage.h"],
 }
 
 
@@ -116,6 +117,28 @@ def decode_bytes(s, io_bytes: int) -> float:
             + 2 * Ln * S * N * io_bytes + Ln * Dn * (N + 1) * 4)
 
 
+def backward_bytes(s, io_bytes: int) -> float:
+    """Backward, each input read once and each gradient written once: x, dt, z, dy read,
+    dx, ddt, dz written; B, C read and dB, dC (fp32) written; A, D, dA, dD. The states
+    stored every 4 steps and read back are traffic of the method, not of the algorithm."""
+    b, L, Dn, N = s.batch, s.L, s.d_inner, s.d_state
+    streams = 3 + 2 * (1 if s.gated else 0) + 1 + 1          # x, dt, (z), dy / dx, ddt, (dz)
+    return (b * L * Dn * streams * io_bytes + 2 * b * L * N * (io_bytes + 4)
+            + 2 * Dn * (N + 1) * 4)
+
+
+def backward_lane_ops(s) -> float:
+    """VALU instructions per element of the gradient kernel: a forward walk storing the
+    states (4 per state + dt*x and widening), the recomputation of each 4-step piece (the
+    same), and the backward step (12 per state: exp argument, exp, lam, a h, lam a h,
+    dB and dC terms, B.lam, A.lam a h, dA, lam a, C.h; plus about 20 per element for the
+    gate's derivative, dx, ddt, dz and conversions), plus the sums of dB and dC over the
+    wave (2N values over 64 lanes: 2 selects and an add per exchange, about 3 per value)."""
+    N = s.d_state
+    walk = 4 * N + 3
+    return 2 * walk + 12 * N + 20 + 3 * 2 * N
+
+
 def decode_lane_ops(s) -> float:
     """Vector-ALU instructions per channel of a decode step: 5 per state as in prefill,
     dt*x, D*x + acc, the pairwise tree over the G = 4 lanes of a channel (2 adds), and
@@ -128,6 +151,49 @@ def decode_lane_ops(s) -> float:
 
 
 # ----------------------------------------------------------------- runs
+def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
+    """One step = one ssm_scan_bwd call over the workload (dy ~ N(0, 1) in the I/O dtype)."""
+    dev = "cuda"
+    log("drawing inputs for", shape.name, "(backward)")
+    d = workloads.make_scan_inputs(shape, dev)
+    g = torch.Generator(device=dev).manual_seed(shape.seed + 29)
+    dy = torch.randn(d["x"].shape, generator=g, device=dev).to(d["x"].dtype)
+    b, L, Dn, N = shape.batch, shape.L, shape.d_inner, shape.d_state
+    ws = torch.empty(max(ssm.ssm_scan_bwd_workspace(b, L, Dn, N, chunk_len), 1), dtype=torch.uint8,
+                     device=dev)
+    log("backward workspace", ws.numel() / 1e9, "GB")
+    out = {}
+
+    def call():
+        r = ssm.ssm_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy,
+                             chunk_len=chunk_len, workspace=ws, out=out, want_dh0=False)
+        out.update(r)
+
+    log("warmup", warmup)
+    for _ in range(max(warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log("timing", steps, "steps")
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / steps
+    io_bytes = 2 if shape.io == "bf16" else 4
+    info = {
+        "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": {"backward_call": gpu_ms},
+        "elements_per_step": shape.elements, "bytes_per_step": backward_bytes(shape, io_bytes),
+        "lane_ops_per_elem": backward_lane_ops(shape), "chunk_len": chunk_len,
+        "n_chunks": None, "dominant_ms": gpu_ms, "gpu_ms": gpu_ms,
+        "kernel": "ssm_scan_bwd (all launches)", "source": "bwd",
+    }
+    return info, d
+
+
 def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None):
     """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter."""
     dev = "cuda"
@@ -337,6 +403,41 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None):
                       f"per channel, channels split over {threads} threads"}
 
 
+def cpu_baseline_backward(shape, d, torch, workloads, threads):
+    """The oracle's backward on a channel sample over the full sequence, channel groups on
+    several threads (dB and dC then cover the sampled channels only; the per-element work
+    is the same)."""
+    import threading
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    k = min(256 if shape.L >= 100000 else 128, shape.d_inner)
+    idx = workloads.sample_channels(shape.d_inner, k, seed=5)
+    g = lambda t: None if t is None else oracle.to_f64(t.index_select(2, idx.to(t.device)))
+    x, dt, z = g(d["x"]), g(d["dt"]), g(d["z"])
+    A, B, C, D = (oracle.to_f64(d["A"].index_select(0, idx.to(d["A"].device))), oracle.to_f64(d["B"]),
+                  oracle.to_f64(d["C"]), oracle.to_f64(d["D"].index_select(0, idx.to(d["D"].device))))
+    dy = np.random.default_rng(3).normal(0, 1, x.shape)
+    parts = [p for p in np.array_split(np.arange(k), threads) if len(p)]
+    log("cpu baseline (backward): oracle on", k, "channels x", shape.L, "steps with", len(parts), "threads")
+
+    def work(p):
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, p])
+        oracle.scan_bwd(sub(x), sub(dt), A[p], B, C, D[p], sub(z), dy=sub(dy))
+
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=work, args=(p,)) for p in parts]
+    for t in ts: t.start()
+    for t in ts: t.join()
+    dtm = time.perf_counter() - t0
+    elems = shape.batch * shape.L * k
+    return {"value": elems / dtm, "unit": "elements/s", "cores": len(parts), "kind": "oracle",
+            "sample": f"backward: {k} of {shape.d_inner} channels over all {shape.L} steps x batch "
+                      f"{shape.batch} ({elems} elements, {dtm:.1f} s wall), fp64 loops per channel "
+                      f"(forward keeping every state, then backward), channels split over "
+                      f"{len(parts)} threads"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +455,8 @@ def main():
                     help="through ssm_scan_fwd_fused / ssm_step_fused (conv + silu and softplus "
                          "fused into the load stage)")
     ap.add_argument("--conv-k", type=int, default=4, help="filter taps with --fused (0..4)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time ssm_scan_bwd (gradients of the prefill) on the prefill workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -387,19 +490,26 @@ def main():
         info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph,
                              conv_k=args.conv_k if args.fused else None)
     else:
+        if args.backward and (shape.complex_state or args.fused):
+            print("--backward applies to the real-state prefill workloads", file=sys.stderr)
+            sys.exit(2)
         if args.fused and shape.complex_state:
             print("--fused applies to the real-state prefill workloads", file=sys.stderr)
             sys.exit(2)
         conv_k = args.conv_k if args.fused else None
-        info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
-                              conv_k)
+        if args.backward:
+            info, d = run_backward(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
+        else:
+            info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
+                                  conv_k)
 
     elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
     dom_s = info["dominant_ms"] / 1e3
     hbm_ach = info["bytes_per_step"] / dom_s / 1e9
     alu_ach = info["elements_per_step"] * info["lane_ops_per_elem"] / dom_s / 1e12
     hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
-    traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "")
+    traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "") + \
+        ("+backward" if args.backward else "")
     traffic = traffic_for(info, traffic_key)
     if hbm_frac >= alu_frac:
         roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
@@ -430,6 +540,8 @@ def main():
         if args.fused:
             cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
                                   "softplus_dt": True, "entry_point": "ssm_scan_fwd_fused"}
+        if args.backward:
+            cfg["pass"] = "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)"
     out = {
         "metric": METRIC, "value": round(elems_s, 1), "unit": "elements/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(info["ms_per_step"], 4),
@@ -441,8 +553,11 @@ def main():
     }
     if not args.no_cpu_baseline and not is_decode:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
-                                           args.conv_k if args.fused else None)
+        if args.backward:
+            out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads)
+        else:
+            out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
+                                               args.conv_k if args.fused else None)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

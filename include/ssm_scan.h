@@ -236,6 +236,43 @@ ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, co
                                  int64_t n_layers, int64_t n_seq, int64_t d_inner,
                                  int32_t d_state, ssm_dtype io, void *hip_stream);
 
+/* ------------------------------------------------------------------ backward
+ * ssm_scan_bwd: gradients of the real-state prefill, for training. Given the
+ * forward's inputs and the upstream gradients dy = dLoss/dy [batch, L, d_inner] (io)
+ * and dh_final = dLoss/dh_final [batch, d_inner, d_state] float32 (NULL = 0), it
+ * writes the gradients of Loss = sum(dy * y) + sum(dh_final * h_final):
+ *   dx, ddt, dz : [batch, L, d_inner] of io (dz only when z is given; NULL = not wanted)
+ *   dA          : [d_inner, d_state] float32 (summed over batch and steps)
+ *   dB, dC      : [batch, L, d_state] float32 (summed over channels)
+ *   dD          : [d_inner] float32;   dh0: [batch, d_inner, d_state] float32 (NULL = not wanted)
+ * It is the chain rule through the recurrence of ssm_scan_fwd ("Jamba — SSM-Transformer
+ * Híbrido", section "Um SSM em uma página"; gate and skip of the MambaBlock,
+ * "【大模型】- Jamba 混合 SSM-Transformer", section 4.1): the adjoint
+ * lam_t = dLoss/dh_t = do_t C_t + exp(dt_{t+1} A) lam_{t+1} with do_t = dy_t silu(z_t)
+ * runs backwards, and dx_t = do_t D + dt_t lam_t.B_t, ddt_t = lam_t.(x_t B_t + A a_t h_{t-1}),
+ * dz_t = dy_t o_t silu'(z_t), dA += dt_t lam_t a_t h_{t-1}, dB_t += lam_t dt_t x_t,
+ * dC_t += do_t h_t, dD += do_t x_t, dh0 = a_0 lam_0 (o_t = C_t.h_t + D x_t before the
+ * gate, a_t = exp(dt_t A)).
+ * The states are recomputed: chunked as in the forward (the same decay-horizon
+ * truncation, applied to the state and, mirrored, to the adjoint), with the state
+ * stored every 4 steps in the workspace and each 4-step piece recomputed in
+ * registers. The workspace (ssm_scan_bwd_workspace bytes, 256-byte aligned) holds
+ * those states (16 bytes per element and state at fp32) and per-chunk and per-wave
+ * partial sums; dA, dB, dC and dD are reduced from them in a fixed order, so results
+ * are deterministic. chunk_len: as in ssm_scan_fwd_ex (rounded down to a multiple of
+ * 4 when there are several chunks). L == 0: dA = dD = 0, dh0 = dh_final (or 0).
+ * Alignment: A, h0, dh_final, dh0 16 bytes; B, C, D, dA, dB, dC, dD 4 bytes; streams
+ * one element; workspace 256 bytes. */
+size_t ssm_scan_bwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                              int64_t chunk_len);
+ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const void *B,
+                        const void *C, const float *D, const void *z, const float *h0,
+                        const void *dy, const float *dh_final, void *dx, void *ddt, void *dz,
+                        float *dA, float *dB, float *dC, float *dD, float *dh0,
+                        int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                        ssm_dtype io, int64_t chunk_len, void *workspace,
+                        size_t workspace_bytes, void *hip_stream);
+
 /* ------------------------------------------------------------------ profiling
  * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64 / ssm_scan_fwd_fused,
  * which additionally records four caller-created HIP events (hipEvent_t, passed

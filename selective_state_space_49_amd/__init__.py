@@ -23,6 +23,7 @@ __all__ = [
     "ssm_status_str", "ssm_last_error", "ssm_abi_version", "EXPORTED_SYMBOLS",
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
+    "ssm_scan_bwd", "ssm_scan_bwd_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +39,7 @@ EXPORTED_SYMBOLS = [
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
+    "ssm_scan_bwd", "ssm_scan_bwd_workspace",
 ]
 
 
@@ -85,6 +87,8 @@ def load_library():
     fused = [vp] * 10 + [i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_fused"] = (fused, ci)
     sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
+    sig["ssm_scan_bwd_workspace"] = ([i64, i64, i64, i32, i64], sz)
+    sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     step_fused = [vp] * 11 + [i32, vp, vp, i64, i64, i64, i32, ci, vp]
     for name in ("ssm_step_fused", "ssm_step_fused_replay"):
         sig[name] = (step_fused, ci)
@@ -382,3 +386,51 @@ def ssm_step_fused_replay(h, conv_state, x_t, dt_t, A, B_t, C_t, D, z_t=None, *,
     """ssm_step_fused in its written-down order, one thread per channel."""
     return _step_fused("ssm_step_fused_replay", h, conv_state, x_t, dt_t, A, B_t, C_t, D, z_t,
                        conv_w, conv_b, dt_bias, y_t)
+
+
+# ------------------------------------------------------------------ backward
+def ssm_scan_bwd_workspace(batch, L, d_inner, d_state, chunk_len=0) -> int:
+    return int(load_library().ssm_scan_bwd_workspace(batch, L, d_inner, d_state, chunk_len))
+
+
+def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk_len=0,
+                 want_dz=True, want_dh0=True, workspace=None, out=None):
+    """Gradients of sum(dy * y) + sum(dh_final * h_final) of the real-state prefill.
+    Returns a dict: dx, ddt, dz (io dtype, dz None when ungated or not wanted), dA, dB, dC,
+    dD, dh0 (float32; dh0 None when not wanted). out: an optional dict of preallocated
+    outputs with those names."""
+    lib = load_library()
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    _dev(x, "x"); _dev(dt, "dt", (b, L, Dn)); _dev(z, "z", (b, L, Dn)); _dev(dy, "dy", (b, L, Dn))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N))
+    _dev(h0, "h0", (b, Dn, N), f32); _dev(dh_final, "dh_final", (b, Dn, N), f32)
+    io = _io(x, dt, z, B, C, dy)
+    out = dict(out or {})
+    dev = x.device
+    shapes = {"dx": ((b, L, Dn), x.dtype), "ddt": ((b, L, Dn), x.dtype),
+              "dA": ((Dn, N), f32), "dB": ((b, L, N), f32), "dC": ((b, L, N), f32),
+              "dD": ((Dn,), f32)}
+    if z is not None and want_dz:
+        shapes["dz"] = ((b, L, Dn), x.dtype)
+    if want_dh0:
+        shapes["dh0"] = ((b, Dn, N), f32)
+    for k, (shp, dtp) in shapes.items():
+        if out.get(k) is None:
+            out[k] = torch.empty(shp, dtype=dtp, device=dev)
+        _dev(out[k], k, shp, dtp)
+    out.setdefault("dz", None)
+    out.setdefault("dh0", None)
+    need = ssm_scan_bwd_workspace(b, L, Dn, N, chunk_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                          _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
+                          _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                          _ptr(out["dD"]), _ptr(out["dh0"]), b, L, Dn, N, io, chunk_len,
+                          _ptr(workspace), ws_bytes, _stream(x))
+    _check(st)
+    return out

@@ -239,6 +239,107 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     return launch_status(e, "step launch");
 }
 
+// Backward plan: the forward's chunks, with the length a multiple of kSub when there is
+// more than one chunk, so that every chunk starts on a sub-chunk boundary.
+struct BwdPlan {
+    Plan fwd;
+    size_t off[8];  // byte offsets of sumP, sumH, revQ, revG, ckpt, partA, partD, partBC
+    size_t bytes;
+    int32_t waves, threads, dblocks;
+};
+
+size_t ws_round(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+ssm_status make_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                         int64_t chunk_len, BwdPlan *p) {
+    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, false, &p->fwd);
+    if (st != SSM_OK) return st;
+    if (p->fwd.n_chunks > 1) {
+        int64_t T = p->fwd.T / ssm::kSub * ssm::kSub;
+        if (T < ssm::kSub) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be at least %d for the backward", ssm::kSub);
+        const int64_t n = (L + T - 1) / T;
+        if (n > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n, (long long)kMaxChunks);
+        p->fwd.T = T;
+        p->fwd.n_chunks = (int32_t)n;
+    }
+    p->threads = (int32_t)std::min<int64_t>(256, (d_inner + 63) / 64 * 64);
+    p->dblocks = (int32_t)((d_inner + p->threads - 1) / p->threads);
+    p->waves = p->dblocks * (p->threads / 64);
+    const size_t M = (size_t)batch * d_inner * d_state * sizeof(float);
+    const size_t C = (size_t)p->fwd.n_chunks;
+    const size_t sizes[8] = {(C - 1) * M, (C - 1) * M, (C - 1) * M, (C - 1) * M,
+                             (size_t)((L + ssm::kSub - 1) / ssm::kSub) * M, C * M,
+                             C * (size_t)batch * d_inner * sizeof(float),
+                             (size_t)batch * L * p->waves * 2 * d_state * sizeof(float)};
+    size_t at = 0;
+    for (int i = 0; i < 8; ++i) {
+        p->off[i] = at;
+        at += ws_round(sizes[i]);
+    }
+    p->bytes = (batch > 0 && L > 0) ? at : 0;
+    return ok();
+}
+
+ssm_status bwd_common(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                      const float *D, const void *z, const float *h0, const void *dy,
+                      const float *dh_final, void *dx, void *ddt, void *dz, float *dA, float *dB,
+                      float *dC, float *dD, float *dh0, int64_t batch, int64_t L, int64_t d_inner,
+                      int32_t d_state, ssm_dtype io, int64_t chunk_len, void *workspace,
+                      size_t workspace_bytes, void *hip_stream) {
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
+    BwdPlan plan;
+    ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &plan);
+    if (st != SSM_OK) return st;
+    if (!A || !D || !dA || !dD) return fail(SSM_ERR_NULL, "A, D, dA and dD are required");
+    const bool work = batch > 0 && L > 0;
+    if (work && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
+        return fail(SSM_ERR_NULL, "x, dt, B, C, dy, dx, ddt, dB and dC are required");
+    const size_t eb = io_bytes(io);
+    if (!aligned(x, eb) || !aligned(dt, eb) || !aligned(z, eb) || !aligned(dy, eb) ||
+        !aligned(dx, eb) || !aligned(ddt, eb) || !aligned(dz, eb) || !aligned(B, 4) ||
+        !aligned(C, 4) || !aligned(A, 16) || !aligned(D, 4) || !aligned(h0, 16) ||
+        !aligned(dh_final, 16) || !aligned(dh0, 16) || !aligned(dA, 4) || !aligned(dB, 4) ||
+        !aligned(dC, 4) || !aligned(dD, 4))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (A, h0, dh_final, dh0 16 B; B, C, D, dA, dB, dC, dD 4 B; streams element)");
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int64_t DN = d_inner * d_state;
+    if (!work) {  // no steps: dA = dD = 0 and dh0 = dh_final
+        st = launch_status(ssm::launch_state_fill(dA, nullptr, DN, s), "fill");
+        if (st == SSM_OK) st = launch_status(ssm::launch_state_fill(dD, nullptr, d_inner, s), "fill");
+        if (st == SSM_OK && dh0) st = launch_status(ssm::launch_state_fill(dh0, dh_final, batch * DN, s), "fill");
+        return st;
+    }
+    if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan.bytes);
+    if (workspace_bytes < plan.bytes)
+        return fail(SSM_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, plan.bytes);
+    if (!aligned(workspace, kWsAlign)) return fail(SSM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    char *ws = (char *)workspace;
+    ssm::ScanArgs f{};
+    f.x = x; f.dt = dt; f.B = B; f.C = C; f.z = z; f.A = A; f.D = D; f.h0 = h0;
+    f.sumP = (float *)(ws + plan.off[0]);
+    f.sumH = (float *)(ws + plan.off[1]);
+    f.batch = batch; f.L = L; f.Dn = d_inner;
+    f.T = plan.fwd.T; f.n_chunks = plan.fwd.n_chunks;
+    f.threads = plan.threads; f.dblocks = plan.dblocks;
+    ssm::BwdArgs a{};
+    a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z; a.dy = dy;
+    a.A = A; a.D = D; a.h0 = h0; a.dh_final = dh_final;
+    a.dx = dx; a.ddt = ddt; a.dz = z ? dz : nullptr;
+    a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dh0 = dh0;
+    a.sumH = f.sumH;
+    a.revQ = (float *)(ws + plan.off[2]);
+    a.revG = (float *)(ws + plan.off[3]);
+    a.ckpt = (float *)(ws + plan.off[4]);
+    a.partA = (float *)(ws + plan.off[5]);
+    a.partD = (float *)(ws + plan.off[6]);
+    a.partBC = (float *)(ws + plan.off[7]);
+    a.batch = batch; a.L = L; a.Dn = d_inner; a.T = plan.fwd.T;
+    a.n_chunks = plan.fwd.n_chunks; a.dblocks = plan.dblocks; a.threads = plan.threads;
+    a.waves = plan.waves;
+    const int iot = io == SSM_BF16 ? 1 : 0;
+    return launch_status(ssm::launch_scan_bwd(a, f, iot, d_state, z != nullptr, s), "backward launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -399,6 +500,24 @@ ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, co
     const InputStage in{conv_w, conv_b, dt_bias, conv_k, nullptr, conv_state};
     return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
                        io, hip_stream, false, true, &in);
+}
+
+size_t ssm_scan_bwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                              int64_t chunk_len) {
+    BwdPlan p;
+    if (make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &p) != SSM_OK) return 0;
+    return p.bytes;
+}
+
+ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                        const float *D, const void *z, const float *h0, const void *dy,
+                        const float *dh_final, void *dx, void *ddt, void *dz, float *dA, float *dB,
+                        float *dC, float *dD, float *dh0, int64_t batch, int64_t L,
+                        int64_t d_inner, int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                        void *workspace, size_t workspace_bytes, void *hip_stream) {
+    return bwd_common(x, dt, A, B, C, D, z, h0, dy, dh_final, dx, ddt, dz, dA, dB, dC, dD, dh0,
+                      batch, L, d_inner, d_state, io, chunk_len, workspace, workspace_bytes,
+                      hip_stream);
 }
 
 const char *ssm_status_str(ssm_status s) {

@@ -1,0 +1,445 @@
+// scan_bwd.hip -- gradients of the real-state prefill (gfx950).
+//
+// Training differentiates the scan ("Jamba — SSM-Transformer Híbrido", section "Um
+// SSM em uma página", on evaluating the SSM at training time; the recurrence and the
+// MambaBlock's gate from "【大模型】- Jamba 混合 SSM-Transformer", section 4.1). With
+//     h_t = a_t h_{t-1} + dt_t x_t B_t,  a_t = exp(dt_t A),  o_t = C_t.h_t + D x_t,
+//     y_t = o_t silu(z_t),
+// and the upstream dy (and dh_final), the adjoint lam_t = dLoss/dh_t runs backwards:
+//     lam_t = do_t C_t + a_{t+1} lam_{t+1},   do_t = dy_t silu(z_t),
+// and per step
+//     dx_t = do_t D + dt_t sum_n lam_t[n] B_t[n]
+//     ddt_t = x_t sum_n lam_t[n] B_t[n] + sum_n A[n] lam_t[n] w_t[n]
+//     dA[n] += dt_t lam_t[n] w_t[n],  dB_t[n] += lam_t[n] dt_t x_t,  dC_t[n] += do_t h_t[n]
+// where w_t = a_t h_{t-1} = h_t - dt_t x_t B_t, so only h_t is needed at step t.
+//
+// The state runs forwards and the adjoint backwards, and neither recurrence can be
+// inverted stably (a_t may be tiny), so states are recomputed. Phases, one lane per
+// channel as in the forward kernels:
+//   1. the forward's chunk summaries and carry: the state entering every chunk;
+//   2. k_bwd_summary: per chunk c >= 1 the adjoint it passes to chunk c-1 from a zero
+//      carry-in, G_c, and its total decay Q_c, over a window that ends where the
+//      decay reaches 2^-64 (the mirror of the forward's horizon);
+//   3. the forward's carry kernel over the chunks in reverse order, seeded with
+//      dh_final: the adjoint entering every chunk from the right;
+//   4. k_bwd_chunk: per chunk, a forward walk from the incoming state that stores the
+//      state every kSub steps, then a backward walk by sub-chunks: each sub-chunk's
+//      kSub states are recomputed into registers from its stored start and the
+//      gradients of its steps emitted. dB_t and dC_t, summed over channels, are reduced
+//      across the 64 lanes of the wave (a transposing butterfly: 2N values over 64
+//      lanes in 2N - 1 exchanges plus the final levels) and stored per wave;
+//   5. k_bwd_reduce_*: dA and dD summed over chunks and batch rows, dB and dC over waves.
+// Every sum is over a fixed order: results are deterministic.
+#include "ssm_device.h"
+#include "ssm_input_stage.h"
+#include "ssm_internal.h"
+#include "ssm_stream.h"
+
+namespace ssm {
+namespace {
+
+struct Lane {
+    int64_t b, d;    // batch row, channel (d clamped to a valid channel)
+    bool valid;      // false for the padding lanes of the last channel block
+    int32_t w;       // channel wave within the batch row
+};
+
+__device__ __forceinline__ Lane lane_of(const BwdArgs &a) {
+    Lane r;
+    r.b = (int64_t)blockIdx.x / a.dblocks;
+    const int64_t d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
+    r.valid = d < a.Dn;
+    r.d = r.valid ? d : a.Dn - 1;
+    r.w = (int32_t)(((int64_t)blockIdx.x % a.dblocks) * (a.threads / 64) + threadIdx.x / 64);
+    return r;
+}
+
+// Sum over the 64 lanes of a wave of each of V values. At each level of a butterfly
+// over lane bits 32, 16, .., 1, a lane keeps the half of its values selected by its
+// lane bit and adds the partner's copy of that half; once one value is left the
+// remaining levels add it to the partner's. On return lane l holds the total of value
+// l >> (6 - log2 V) (the lanes sharing that index hold the same total).
+template <int K, int S, int V>
+struct Butterfly {
+    static __device__ __forceinline__ void run(float (&v)[V], int lane) {
+        if constexpr (S > 0) {
+            if constexpr (K > 1) {
+                constexpr int half = K / 2;
+                const bool hi = (lane & S) != 0;
+#pragma unroll
+                for (int i = 0; i < half; ++i) {
+                    const float send = hi ? v[i] : v[i + half];
+                    const float keep = hi ? v[i + half] : v[i];
+                    v[i] = keep + __shfl_xor(send, S, 64);
+                }
+                Butterfly<half, S / 2, V>::run(v, lane);
+            } else {
+                v[0] = v[0] + __shfl_xor(v[0], S, 64);
+                Butterfly<1, S / 2, V>::run(v, lane);
+            }
+        }
+    }
+};
+
+template <int V>
+__device__ __forceinline__ float wave_reduce_transpose(float (&v)[V]) {
+    Butterfly<V, 32, V>::run(v, threadIdx.x & 63);
+    return v[0];
+}
+
+template <int V> struct Log2;
+template <> struct Log2<2> { static constexpr int v = 1; };
+template <> struct Log2<4> { static constexpr int v = 2; };
+template <> struct Log2<8> { static constexpr int v = 3; };
+template <> struct Log2<16> { static constexpr int v = 4; };
+template <> struct Log2<32> { static constexpr int v = 5; };
+
+// Walks rows steps-1 .. 0 of up to three streams (s2 only if THREE), fetching the
+// block of KU rows below the current one while the current one is computed; calls
+// body(i, v0, v1, v2).
+template <typename IO, bool THREE, int KU, typename Body>
+__device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStream<IO> &s1,
+                                           const RowStream<IO> &s2, uint32_t voff, uint32_t rb,
+                                           uint32_t steps, Body &&body) {
+    const uint32_t full = steps / KU;
+    for (uint32_t i = steps; i > full * KU;) {  // ragged top rows first, one at a time
+        --i;
+        body(i, s0.ld(voff, i * rb), s1.ld(voff, i * rb), THREE ? s2.ld(voff, i * rb) : 0.0f);
+    }
+    if (full == 0) return;
+    float a0[KU], a1[KU], a2[KU], b0[KU], b1[KU], b2[KU];
+    auto load = [&](float(&v0)[KU], float(&v1)[KU], float(&v2)[KU], uint32_t blk) {
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const uint32_t r = blk * KU + k;
+            v0[k] = s0.ld(voff, r * rb);
+            v1[k] = s1.ld(voff, r * rb);
+            if (THREE) v2[k] = s2.ld(voff, r * rb);
+        }
+    };
+    load(a0, a1, a2, full - 1);
+    for (uint32_t blk = full; blk > 0;) {
+        --blk;  // block blk is in a*: fetch blk-1 into b*, compute blk
+        if (blk > 0) load(b0, b1, b2, blk - 1);
+#pragma unroll
+        for (int k = KU - 1; k >= 0; --k) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(blk * KU + k, a0[k], a1[k], THREE ? a2[k] : 0.0f);
+        }
+        if (blk == 0) break;
+        --blk;  // block blk is in b*: fetch blk-1 into a*, compute blk
+        if (blk > 0) load(a0, a1, a2, blk - 1);
+#pragma unroll
+        for (int k = KU - 1; k >= 0; --k) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(blk * KU + k, b0[k], b1[k], THREE ? b2[k] : 0.0f);
+        }
+        if (blk == 0) break;
+    }
+}
+
+// First row (chunk-relative) from which the decay back to row 0 is below 2^-kHorizon
+// for every state of every lane of the wave, walking dt forward in whole blocks of
+// kB rows: rows at or beyond it reach row 0 with weight below 2^-64. Returns T when
+// the horizon is not reached within the whole blocks (A >= 0, dt = 0, NaN, short T).
+template <typename IO>
+__device__ __forceinline__ uint32_t horizon_end(const RowStream<IO> &dt, uint32_t voff,
+                                                uint32_t rb, uint32_t T, float amax) {
+    if (!__any(amax < 0.0f) || T < (uint32_t)kB) return T;
+    float S = 0.0f;
+    float cur[kB];
+    uint32_t nxt[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) cur[k] = dt.ld(voff, k * rb);
+    uint32_t tb = 0;
+    while (true) {
+        const uint32_t tn = tb + kB;  // rows [tb, tn) are in cur
+        const bool more = tn + kB <= T;
+        if (more) {
+#pragma unroll
+            for (int k = 0; k < kB; ++k) nxt[k] = dt.ldraw(voff, (tn + k) * rb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kB; ++k) S += cur[k];
+        if (__all(amax * S <= -kHorizon)) return tn;
+        if (!more) return T;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < kB; ++k) cur[k] = RowStream<IO>::widen(nxt[k]);
+        tb = tn;
+    }
+}
+
+// d(output) of one step: dy times the gate, and the gate's derivative factor.
+template <bool GATED>
+__device__ __forceinline__ float gate_grad(float dy, float z, float &gp) {
+    if (!GATED) {
+        gp = 0.0f;
+        return dy;
+    }
+    const float s = rcp(1.0f + e2(-z * kLog2e));  // sigmoid(z)
+    gp = s * __builtin_fmaf(z, 1.0f - s, 1.0f);   // silu'(z) = s (1 + z (1 - s))
+    return dy * (z * s);
+}
+
+// ---------------------------------------------------------------- reverse summary
+// Chunks c = 1 .. n_chunks-1: G_c = sum over the chunk's steps t of
+// (prod_{r = t0}^{t} a_r) do_t C_t and Q_c = prod of a_t over the chunk, stored at
+// entry n_chunks-1-c of revG / revQ.
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_bwd_summary(BwdArgs a) {
+    const Lane ln = lane_of(a);
+    if (!ln.valid) return;  // no cross-lane work here
+    const int c = blockIdx.y + 1;
+    const int64_t t0 = (int64_t)c * a.T;
+    const uint32_t T = (uint32_t)(min(a.L, t0 + a.T) - t0);
+    const uint32_t rb = (uint32_t)(a.Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
+    float A2[N], lam[N];
+    float amax = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        amax = fmaxf(amax, A2[n]);
+        lam[n] = 0.0f;
+    }
+    const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
+    const RowStream<IO> dts((const IO *)a.dt + row0), dys((const IO *)a.dy + row0),
+        zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.dt + row0);
+    const uint32_t te = horizon_end<IO>(dts, voff, rb, T, amax);
+    const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
+    double S = 0.0;
+    stream_rev<IO, GATED, 4>(dts, dys, zs, voff, rb, te, [&](uint32_t i, float dv, float dy, float zv) {
+        const int64_t t = t0 + i;
+        float gp;
+        const float dout = gate_grad<GATED>(dy, zv, gp);
+        S += (double)dv;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float lt = __builtin_fmaf(dout, Uniform<IO>::ld(Cp, t * N + n), lam[n]);
+            lam[n] = e2(dv * A2[n]) * lt;
+        }
+    });
+    const float Sf = (float)S;
+    const size_t M = (size_t)a.batch * a.Dn * N;
+    const size_t o = (size_t)(a.n_chunks - 1 - c) * M + (size_t)(ln.b * a.Dn + ln.d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a.revQ[o + n] = te == T ? e2(A2[n] * Sf) : 0.0f;
+        a.revG[o + n] = lam[n];
+    }
+}
+
+// ---------------------------------------------------------------- gradients
+template <typename IO, int N, bool GATED>
+__global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
+    constexpr int V = 2 * N;
+    const Lane ln = lane_of(a);
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const uint32_t steps = (uint32_t)(min(a.L, t0 + a.T) - t0);
+    const uint32_t rb = (uint32_t)(a.Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
+    const size_t M = (size_t)a.batch * a.Dn * N;
+    const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
+    const float *hin = c == 0 ? (a.h0 ? a.h0 + col : nullptr) : a.sumH + (size_t)(c - 1) * M + col;
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        h[n] = hin ? hin[n] : 0.0f;
+    }
+    const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
+    const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
+        dys((const IO *)a.dy + row0), zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0);
+    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
+    const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
+    const size_t sub0 = (size_t)(t0 / kSub);  // global index of the chunk's first sub-chunk
+    // 1. forward walk, storing the state entering every sub-chunk but the first
+    stream_steps<IO, false, 4>(xs, dts, dts, voff, rb, steps, 0, [&](uint32_t i, float xv, float dv, float) {
+        if (i > 0 && i % kSub == 0 && ln.valid) {
+            float *ck = a.ckpt + (sub0 + i / kSub) * M + col;
+#pragma unroll
+            for (int n = 0; n < N; ++n) ck[n] = h[n];
+        }
+        const int64_t t = t0 + i;
+        const float u = dv * xv;
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * Uniform<IO>::ld(Bp, t * N + n));
+    });
+    // 2. backward walk by sub-chunks
+    const int64_t mu_entry = (int64_t)a.n_chunks - 2 - c;  // adjoint entering from the right
+    const float *mu = mu_entry < 0 ? (a.dh_final ? a.dh_final + col : nullptr)
+                                   : a.revG + (size_t)mu_entry * M + col;
+    float lam[N], dA[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        lam[n] = mu ? mu[n] : 0.0f;
+        dA[n] = 0.0f;
+    }
+    float dD = 0.0f;
+    const float Dd = a.D[ln.d];
+    const RowStream<IO> dxs((IO *)a.dx + row0), ddts((IO *)a.ddt + row0),
+        dzs((GATED && a.dz) ? (IO *)a.dz + row0 : (IO *)a.dx + row0);
+    const bool want_dz = GATED && a.dz != nullptr;
+    float *pbc = a.partBC + (size_t)ln.w * V;
+    const size_t pbc_step = (size_t)a.waves * V;  // floats per (b, t) row of partials
+    const uint32_t nsub = (steps + kSub - 1) / kSub;
+    for (uint32_t k = nsub; k > 0;) {
+        --k;
+        const uint32_t j0 = k * kSub;
+        const uint32_t ns = min((uint32_t)kSub, steps - j0);
+        float xv[kSub], dv[kSub], yv[kSub], zv[kSub];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            const uint32_t r = (j0 + (j < (int)ns ? j : 0)) * rb;  // rows past the chunk read row j0
+            xv[j] = xs.ld(voff, r);
+            dv[j] = dts.ld(voff, r);
+            yv[j] = dys.ld(voff, r);
+            zv[j] = GATED ? zs.ld(voff, r) : 0.0f;
+        }
+        // padding lanes (which store no checkpoints) restart from the incoming state
+        const float *start = (k == 0 || !ln.valid) ? hin : a.ckpt + (sub0 + k) * M + col;
+        float hs[kSub][N];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            const int64_t t = t0 + j0 + (j < (int)ns ? j : 0);
+            const float u = dv[j] * xv[j];
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float prev = j == 0 ? (start ? start[n] : 0.0f) : hs[j - 1][n];
+                hs[j][n] = __builtin_fmaf(e2(dv[j] * A2[n]), prev, u * Uniform<IO>::ld(Bp, t * N + n));
+            }
+        }
+#pragma unroll
+        for (int j = kSub - 1; j >= 0; --j) {
+            if (j >= (int)ns) continue;  // uniform: every lane of the block has the same ns
+            const int64_t t = t0 + j0 + j;
+            float acc = 0.0f;
+#pragma unroll
+            for (int n = 0; n < N; ++n) acc = __builtin_fmaf(Uniform<IO>::ld(Cp, t * N + n), hs[j][n], acc);
+            const float o = __builtin_fmaf(Dd, xv[j], acc);
+            float gp;
+            const float dout = gate_grad<GATED>(yv[j], zv[j], gp);
+            dD = __builtin_fmaf(dout, xv[j], dD);
+            const float u = dv[j] * xv[j];
+            float gx = 0.0f, gA = 0.0f;
+            float vals[V];
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float bn = Uniform<IO>::ld(Bp, t * N + n);
+                const float lt = __builtin_fmaf(dout, Uniform<IO>::ld(Cp, t * N + n), lam[n]);
+                const float w = __builtin_fmaf(-u, bn, hs[j][n]);  // a_t h_{t-1}
+                const float q = lt * w;
+                vals[n] = ln.valid ? lt * u : 0.0f;                 // dB_t[n] term
+                vals[N + n] = ln.valid ? dout * hs[j][n] : 0.0f;    // dC_t[n] term
+                gx = __builtin_fmaf(lt, bn, gx);
+                gA = __builtin_fmaf(A2[n], q, gA);
+                dA[n] = __builtin_fmaf(dv[j], q, dA[n]);
+                lam[n] = e2(dv[j] * A2[n]) * lt;
+            }
+            if (ln.valid) {
+                const uint32_t r = (j0 + j) * rb;
+                dxs.st(voff, r, __builtin_fmaf(dout, Dd, dv[j] * gx));
+                ddts.st(voff, r, __builtin_fmaf(xv[j], gx, gA * kLn2));
+                if (want_dz) dzs.st(voff, r, yv[j] * o * gp);
+            }
+            const float tot = wave_reduce_transpose<V>(vals);
+            const int lane = threadIdx.x & 63;
+            constexpr int sh = 6 - Log2<V>::v;
+            if ((lane & ((1 << sh) - 1)) == 0)
+                pbc[(size_t)(ln.b * a.L + t) * pbc_step + (lane >> sh)] = tot;
+        }
+    }
+    if (ln.valid) {
+        const size_t pa = ((size_t)c * a.batch + ln.b) * a.Dn + ln.d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.partA[pa * N + n] = dA[n];
+        a.partD[pa] = dD;
+        if (c == 0 && a.dh0) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) a.dh0[col + n] = lam[n];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- reductions
+// dA[d][n] and dD[d]: sums over chunks and batch rows, in that fixed order.
+__global__ void k_bwd_reduce_AD(BwdArgs a, int N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over Dn * (N + 1)
+    const int64_t DN = a.Dn * N;
+    if (i >= DN + a.Dn) return;
+    const int64_t rows = (int64_t)a.n_chunks * a.batch;
+    float s = 0.0f;
+    if (i < DN) {
+        for (int64_t r = 0; r < rows; ++r) s += a.partA[r * DN + i];
+        a.dA[i] = s;
+    } else {
+        const int64_t d = i - DN;
+        for (int64_t r = 0; r < rows; ++r) s += a.partD[r * a.Dn + d];
+        a.dD[d] = s;
+    }
+}
+
+// dB[b][t][n] and dC[b][t][n]: sums over the channel waves.
+__global__ void k_bwd_reduce_BC(BwdArgs a, int N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over batch * L * 2N
+    const int64_t V = 2 * N;
+    if (i >= a.batch * a.L * V) return;
+    const int64_t bt = i / V, j = i % V;
+    const float *p = a.partBC + bt * a.waves * V + j;
+    float s = 0.0f;
+    for (int w = 0; w < a.waves; ++w) s += p[(int64_t)w * V];
+    if (j < N) a.dB[bt * N + j] = s;
+    else a.dC[bt * N + (j - N)] = s;
+}
+
+template <typename IO, int N>
+hipError_t launch_n(const BwdArgs &a, const ScanArgs &fwd, int io, bool gated, hipStream_t s) {
+    hipError_t e = launch_summary_carry(fwd, io, N, s);
+    if (e != hipSuccess) return e;
+    const unsigned gx = (unsigned)(a.batch * a.dblocks);
+    const dim3 blk(a.threads);
+    if (a.n_chunks > 1) {
+        if (gated) hipLaunchKernelGGL((k_bwd_summary<IO, N, true>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+        else hipLaunchKernelGGL((k_bwd_summary<IO, N, false>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+        ScanArgs r = fwd;
+        r.sumP = a.revQ;
+        r.sumH = a.revG;
+        r.h0 = a.dh_final;
+        e = launch_carry(r, N, s);
+        if (e != hipSuccess) return e;
+    }
+    if (gated) hipLaunchKernelGGL((k_bwd_chunk<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    else hipLaunchKernelGGL((k_bwd_chunk<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    const int64_t nad = a.Dn * (N + 1);
+    hipLaunchKernelGGL(k_bwd_reduce_AD, dim3((unsigned)((nad + 255) / 256)), dim3(256), 0, s, a, N);
+    const int64_t nbc = a.batch * a.L * 2 * N;
+    hipLaunchKernelGGL(k_bwd_reduce_BC, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a, N);
+    return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_io(const BwdArgs &a, const ScanArgs &fwd, int io, int d_state, bool gated,
+                     hipStream_t s) {
+    switch (d_state) {
+        case 1: return launch_n<IO, 1>(a, fwd, io, gated, s);
+        case 2: return launch_n<IO, 2>(a, fwd, io, gated, s);
+        case 4: return launch_n<IO, 4>(a, fwd, io, gated, s);
+        case 8: return launch_n<IO, 8>(a, fwd, io, gated, s);
+        case 16: return launch_n<IO, 16>(a, fwd, io, gated, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdArgs &a, const ScanArgs &fwd, int io, int d_state, bool gated,
+                           hipStream_t s) {
+    return io == 0 ? launch_io<float>(a, fwd, io, d_state, gated, s)
+                   : launch_io<bf16_bits>(a, fwd, io, d_state, gated, s);
+}
+
+}  // namespace ssm

@@ -356,6 +356,38 @@ hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated,
                    : launch_fused_io<bf16_bits>(a, d_state, gated, s, ev);
 }
 
+namespace {
+template <typename IO>
+hipError_t launch_summary_carry_io(const ScanArgs &a, int d_state, hipStream_t s) {
+    if (a.n_chunks <= 1) return hipSuccess;
+    const unsigned gx = (unsigned)(a.batch * a.dblocks);
+    const dim3 grid(gx, a.n_chunks - 1), blk(a.threads);
+    switch (d_state) {
+        case 1: hipLaunchKernelGGL((k_chunk_summary<IO, 1, NoInput>), grid, blk, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_chunk_summary<IO, 2, NoInput>), grid, blk, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_chunk_summary<IO, 4, NoInput>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((k_chunk_summary<IO, 8, NoInput>), grid, blk, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((k_chunk_summary<IO, 16, NoInput>), grid, blk, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    const int64_t M = a.batch * a.Dn * d_state;
+    hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_summary_carry(const ScanArgs &a, int io, int d_state, hipStream_t s) {
+    return io == 0 ? launch_summary_carry_io<float>(a, d_state, s)
+                   : launch_summary_carry_io<bf16_bits>(a, d_state, s);
+}
+
+hipError_t launch_carry(const ScanArgs &a, int d_state, hipStream_t s) {
+    if (a.n_chunks <= 1) return hipSuccess;
+    const int64_t M = a.batch * a.Dn * d_state;
+    hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+    return hipGetLastError();
+}
+
 hipError_t launch_elem_fill(void *dst, const void *src, int64_t count, int elem_bytes,
                             hipStream_t s) {
     if (count <= 0) return hipSuccess;

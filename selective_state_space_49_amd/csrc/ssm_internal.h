@@ -57,6 +57,11 @@ hipError_t launch_state_fill(float *dst, const float *src, int64_t count, hipStr
 // Real state with the input stage: conv (a.conv_k in 0..4) and softplus on dt.
 hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                              hipEvent_t const *ev);
+// The first two phases of the real prefill only (chunk summaries, carry scan): on
+// return a.sumH[c] holds the state entering chunk c+1. Nothing when n_chunks == 1.
+hipError_t launch_summary_carry(const ScanArgs &a, int io, int d_state, hipStream_t s);
+// The carry scan alone over a.sumP / a.sumH seeded with a.h0 (a.n_chunks - 1 entries).
+hipError_t launch_carry(const ScanArgs &a, int d_state, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for count elements of elem_bytes (2 or 4) bytes each.
 hipError_t launch_elem_fill(void *dst, const void *src, int64_t count, int elem_bytes,
                             hipStream_t s);
@@ -67,5 +72,30 @@ hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gate
                                hipStream_t s);
 hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                              hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+// One backward call, already validated and planned. The forward phases use a ScanArgs
+// built from the same pointers.
+struct BwdArgs {
+    const void *x, *dt, *B, *C, *z, *dy;
+    const float *A, *D, *h0, *dh_final;
+    void *dx, *ddt, *dz;          // [batch][L][Dn] of io (dz only when z is given)
+    float *dA, *dB, *dC, *dD, *dh0;
+    // workspace
+    float *sumH;    // forward carry: entry c = state entering chunk c+1   [n_chunks-1][batch][Dn][N]
+    float *revQ;    // reverse summaries, reversed chunk order: entry j is chunk n_chunks-1-j
+    float *revG;    //   (decay over the chunk, adjoint passed left from a zero carry-in); after
+                    //   the reverse carry revG[j] = adjoint entering chunk n_chunks-2-j from the right
+    float *ckpt;    // states every kSub steps   [ceil(L / kSub)][batch][Dn][N]
+    float *partA;   // per-chunk dA              [n_chunks][batch][Dn][N]
+    float *partD;   // per-chunk dD              [n_chunks][batch][Dn]
+    float *partBC;  // per-wave dB, dC           [batch][L][waves][2N]
+    int64_t batch, L, Dn;
+    int64_t T;
+    int32_t n_chunks, dblocks, threads, waves;  // waves = channel waves per batch row
+};
+constexpr int kSub = 4;  // steps per recomputed sub-chunk of the backward
+hipError_t launch_scan_bwd(const BwdArgs &a, const ScanArgs &fwd, int io, int d_state, bool gated,
+                           hipStream_t s);
 
 }  // namespace ssm
