@@ -26,8 +26,9 @@
 //      state every kSub steps, then a backward walk by sub-chunks: each sub-chunk's
 //      kSub states are recomputed into registers from its stored start and the
 //      gradients of its steps emitted. dB_t and dC_t, summed over channels, are reduced
-//      across the 64 lanes of the wave (a transposing butterfly: 2N values over 64
-//      lanes in 2N - 1 exchanges plus the final levels) and stored per wave;
+//      across the 64 lanes of the wave (a transposing butterfly of lane permutations:
+//      2N values over 64 lanes in 2N - 1 exchanges plus the final levels) and stored
+//      per wave;
 //   5. k_bwd_reduce_*: dA and dD summed over chunks and batch rows, dB and dC over waves.
 // Every sum is over a fixed order: results are deterministic.
 #include "ssm_device.h"
@@ -59,24 +60,54 @@ __device__ __forceinline__ Lane lane_of(const BwdArgs &a) {
 // lane bit and adds the partner's copy of that half; once one value is left the
 // remaining levels add it to the partner's. On return lane l holds the total of value
 // l >> (6 - log2 V) (the lanes sharing that index hold the same total).
+// Partners: lane bits 5 and 4 through v_permlane32_swap / v_permlane16_swap, whose two
+// results already pair (own kept value, partner's) for both lanes, so a pair costs the
+// swap and an add; bits 3 .. 0 through DPP row mirror (lane i with 15 - i), half-row
+// mirror (i with 7 - i) and quad permutations (xor 2, xor 1), with a select of the half
+// to send and to keep. The mirrors also flip lower bits, which only reorders partners
+// within a group: the masks 15, 7, 2, 1 are independent, so every lane enters every
+// total once.
+__device__ __forceinline__ float swap32_sum(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_sum(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int S> struct Partner;
+template <> struct Partner<8> { static constexpr int ctrl = 0x140; };  // row_mirror
+template <> struct Partner<4> { static constexpr int ctrl = 0x141; };  // row_half_mirror
+template <> struct Partner<2> { static constexpr int ctrl = 0x4E; };   // quad_perm [2,3,0,1]
+template <> struct Partner<1> { static constexpr int ctrl = 0xB1; };   // quad_perm [1,0,3,2]
+
 template <int K, int S, int V>
 struct Butterfly {
     static __device__ __forceinline__ void run(float (&v)[V], int lane) {
         if constexpr (S > 0) {
-            if constexpr (K > 1) {
-                constexpr int half = K / 2;
-                const bool hi = (lane & S) != 0;
+            constexpr int half = K > 1 ? K / 2 : 1;
+            if constexpr (S >= 16) {
 #pragma unroll
                 for (int i = 0; i < half; ++i) {
-                    const float send = hi ? v[i] : v[i + half];
-                    const float keep = hi ? v[i + half] : v[i];
-                    v[i] = keep + __shfl_xor(send, S, 64);
+                    const float lo = v[i], hi = K > 1 ? v[i + half] : v[i];
+                    v[i] = S == 32 ? swap32_sum(lo, hi) : swap16_sum(lo, hi);
                 }
-                Butterfly<half, S / 2, V>::run(v, lane);
+            } else if constexpr (K > 1) {
+                const bool up = (lane & S) != 0;
+#pragma unroll
+                for (int i = 0; i < half; ++i) {
+                    const float send = up ? v[i] : v[i + half];
+                    const float keep = up ? v[i + half] : v[i];
+                    v[i] = keep + dpp<Partner<S>::ctrl>(send);
+                }
             } else {
-                v[0] = v[0] + __shfl_xor(v[0], S, 64);
-                Butterfly<1, S / 2, V>::run(v, lane);
+                v[0] = v[0] + dpp<Partner<S>::ctrl>(v[0]);
             }
+            Butterfly<half, S / 2, V>::run(v, lane);
         }
     }
 };
@@ -257,6 +288,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
     const size_t sub0 = (size_t)(t0 / kSub);  // global index of the chunk's first sub-chunk
     // 1. forward walk, storing the state entering every sub-chunk but the first
+    // Issue priority by remaining work (see set_priority): the walk comes first, then
+    // the sub-chunks count down, so the waves sharing a SIMD finish close together.
+    __builtin_amdgcn_s_setprio(3);
     stream_steps<IO, false, 4>(xs, dts, dts, voff, rb, steps, 0, [&](uint32_t i, float xv, float dv, float) {
         if (i > 0 && i % kSub == 0 && ln.valid) {
             float *ck = a.ckpt + (sub0 + i / kSub) * M + col;
@@ -289,6 +323,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const uint32_t nsub = (steps + kSub - 1) / kSub;
     for (uint32_t k = nsub; k > 0;) {
         --k;
+        set_priority(k + 1, nsub);
         const uint32_t j0 = k * kSub;
         const uint32_t ns = min((uint32_t)kSub, steps - j0);
         float xv[kSub], dv[kSub], yv[kSub], zv[kSub];
