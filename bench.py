@@ -133,10 +133,12 @@ def backward_lane_ops(s) -> float:
     same), and the backward step (12 per state: exp argument, exp, lam, a h, lam a h,
     dB and dC terms, B.lam, A.lam a h, dA, lam a, C.h; plus about 20 per element for the
     gate's derivative, dx, ddt, dz and conversions), plus the sums of dB and dC over the
-    wave (2N values over 64 lanes: 2 selects and an add per exchange, about 3 per value)."""
+    wave (2N values over 64 lanes: 2N - 1 exchanges of two or three instructions plus the
+    last levels, 70 for N = 16)."""
     N = s.d_state
     walk = 4 * N + 3
-    return 2 * walk + 12 * N + 20 + 3 * 2 * N
+    bfly = {1: 6, 2: 8, 4: 15, 8: 33, 16: 70}[N]
+    return 2 * walk + 12 * N + 20 + bfly
 
 
 def decode_lane_ops(s) -> float:
