@@ -18,10 +18,11 @@
 // floating-point contraction off; every fused multiply-add below is explicit.
 //
 // The fused entry point adds the MambaBlock input stage (ssm_input_stage.h): x_t is
-// the convolution's new input and dt_t the raw dt projection output. Every lane of a
+// the convolution's new input and dt_t the raw dt projection output. One lane per
 // channel computes u = silu(conv) from the carried convolution state and
-// dt = softplus(dt + bias) with the same operations (so the G lanes and the replay
-// agree bit for bit), and the channel's first lane writes the shifted state back.
+// dt = softplus(dt + bias), hands both to the G lanes of the channel's state update
+// (k_step), and writes the shifted conv state back; the replay performs the same
+// operations, so the two agree bit for bit.
 #include "ssm_device.h"
 #include "ssm_input_stage.h"
 #include "ssm_internal.h"
@@ -29,8 +30,9 @@
 namespace ssm {
 namespace {
 
-// Grid: x = blocks of 256 threads over (channel, group lane), y = sequence q,
-// z = layer l. Channel index ch = (l * n_seq + q) * Dn + d; lq = l * n_seq + q.
+// Grid: x = blocks of 256 threads over channels (the real-state kernels) or over
+// (channel, group lane) pairs (the complex-state kernel), y = sequence q, z = layer l.
+// Channel index ch = (l * n_seq + q) * Dn + d; lq = l * n_seq + q.
 struct Chan {
     int64_t ch, lq;
     int64_t l, d;
@@ -158,48 +160,93 @@ template <int N> struct RealGroups {
     static constexpr int K = N / G;
 };
 
+// A wave owns 64 consecutive channels. Each lane first loads (and, with an input
+// stage, transforms) x and dt of its "home" channel (wave base + lane), so per-channel
+// work is done once, not once per lane of the channel. The state update then takes
+// G rounds, in which lane t works on channel r * 64/G + t/G, states (t % G) * K ..;
+// it fetches that channel's (x, dt) from the home lane with a lane permute, and the
+// round's output sum goes back to the home lane the same way. The home lane finishes
+// y (and writes the conv state). Each wave has 4G state loads in flight before its
+// first arithmetic. Every operation and its order are those of the replay, so the
+// results agree bit for bit. Lanes past the last channel are clamped to it for
+// their loads and store nothing; no lane leaves early, since its home and round
+// channels differ.
 template <typename IO, int N, bool GATED, typename In>
 __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     constexpr int G = RealGroups<N>::G, K = RealGroups<N>::K;
-    Chan c;
-    int g;
-    if (!chan_of<G>(a, c, g)) return;  // G divides 64: a group is wholly in or out
-    float *hp = a.h + c.ch * N + g * K;
-    float hv[K], av[K], bv[K], cv[K];
-    if constexpr (K == 4) ld_state4(hp, hv);
-    else VecLd<float, K>::ld(hp, hv);
-    VecLd<float, K>::ld(a.A + (c.l * a.Dn + c.d) * N + g * K, av);
-    VecLd<IO, K>::ld((const IO *)a.B + c.lq * N + g * K, bv);
-    VecLd<IO, K>::ld((const IO *)a.C + c.lq * N + g * K, cv);
-    float xv = Io<IO>::ld((const IO *)a.x + c.ch);
-    float dv = Io<IO>::ld((const IO *)a.dt + c.ch);
-    // z and D are needed by the group's first lane only; every lane loads them here,
-    // with the rest (the lanes of a group read the same address), so that no load is
-    // issued after the arithmetic.
-    const float zv = GATED ? Io<IO>::ld((const IO *)a.z + c.ch) : 0.0f;
-    const float Dd = a.D[c.l * a.Dn + c.d];
-    In in;
-    in.apply(a, c, xv, dv);
-    const float u = dv * xv;
-    float p = 0.0f;
+    constexpr int CPR = 64 / G;  // channels per round
+    const int lane = (int)(threadIdx.x & 63u);
+    const int64_t d0 = (int64_t)blockIdx.x * 256 + (threadIdx.x & ~63u);
+    const int g = lane % G;
+    Chan hc;
+    hc.l = blockIdx.z;
+    hc.lq = (int64_t)blockIdx.z * a.n_seq + blockIdx.y;
+    const bool home_ok = d0 + lane < a.Dn;
+    hc.d = home_ok ? d0 + lane : a.Dn - 1;
+    hc.ch = hc.lq * a.Dn + hc.d;
+
+    // Every load first: the state and A of each round's channel, the token's B and C
+    // (one row per (layer, sequence), the same in every round), the home channel's
+    // x, dt, z, D and (in apply) the input-stage parameters and conv state.
+    float hv[G][K], av[G][K], bv[K], cv[K];
+    bool rok[G];
+    int64_t rch[G];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const float a2 = av[k] * kLog2e;
-        hv[k] = __builtin_fmaf(e2(dv * a2), hv[k], u * bv[k]);
-        p = __builtin_fmaf(cv[k], hv[k], p);
+    for (int r = 0; r < G; ++r) {
+        const int64_t d = d0 + r * CPR + lane / G;
+        rok[r] = d < a.Dn;
+        const int64_t dc = rok[r] ? d : a.Dn - 1;
+        rch[r] = hc.lq * a.Dn + dc;
+        const float *hp = a.h + rch[r] * N + g * K;
+        if constexpr (K == 4) ld_state4(hp, hv[r]);
+        else VecLd<float, K>::ld(hp, hv[r]);
+        VecLd<float, K>::ld(a.A + (hc.l * a.Dn + dc) * N + g * K, av[r]);
     }
-    const float acc = group_sum<G>(p);
-    if constexpr (K == 4) {
-        st_state4(hp, hv);
-    } else if constexpr (K == 2) {
-        *(float2 *)hp = make_float2(hv[0], hv[1]);
-    } else {
-        hp[0] = hv[0];
+    VecLd<IO, K>::ld((const IO *)a.B + hc.lq * N + g * K, bv);
+    VecLd<IO, K>::ld((const IO *)a.C + hc.lq * N + g * K, cv);
+    float xv = Io<IO>::ld((const IO *)a.x + hc.ch);
+    float dv = Io<IO>::ld((const IO *)a.dt + hc.ch);
+    const float zv = GATED ? Io<IO>::ld((const IO *)a.z + hc.ch) : 0.0f;
+    const float Dd = a.D[hc.l * a.Dn + hc.d];
+    In in;
+    in.apply(a, hc, xv, dv);
+
+    float acc = 0.0f;
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+        const int src = r * CPR + lane / G;
+        const float xr = G == 1 ? xv : __shfl(xv, src, 64);
+        const float dr = G == 1 ? dv : __shfl(dv, src, 64);
+        const float u = dr * xr;
+        float p = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float a2 = av[r][k] * kLog2e;
+            hv[r][k] = __builtin_fmaf(e2(dr * a2), hv[r][k], u * bv[k]);
+            p = __builtin_fmaf(cv[k], hv[r][k], p);
+        }
+        const float s = group_sum<G>(p);
+        if (rok[r]) {
+            float *hp = a.h + rch[r] * N + g * K;
+            if constexpr (K == 4) {
+                st_state4(hp, hv[r]);
+            } else if constexpr (K == 2) {
+                *(float2 *)hp = make_float2(hv[r][0], hv[r][1]);
+            } else {
+                hp[0] = hv[r][0];
+            }
+        }
+        if constexpr (G == 1) {
+            acc = s;
+        } else {
+            const float sh = __shfl(s, (lane % CPR) * G, 64);
+            if (lane / CPR == r) acc = sh;
+        }
     }
-    if (g == 0) {
+    if (home_ok) {
         float yv = __builtin_fmaf(Dd, xv, acc);
         if (GATED) yv = yv * silu(zv);
-        Io<IO>::st((IO *)a.y + c.ch, yv);
+        Io<IO>::st((IO *)a.y + hc.ch, yv);
         in.store(a);
     }
 }
@@ -340,7 +387,7 @@ inline dim3 grid_for(const StepArgs &a, int lanes_per_ch) {
 
 template <typename IO, int N, typename In = NoStepInput>
 hipError_t launch_real_n(const StepArgs &a, bool gated, bool replay, hipStream_t s) {
-    const dim3 blk(256), grid(grid_for(a, replay ? 1 : RealGroups<N>::G));
+    const dim3 blk(256), grid(grid_for(a, 1));  // both kernels: 256 channels per block
     if (replay) {
         if (gated) hipLaunchKernelGGL((k_step_replay<IO, N, true, In>), grid, blk, 0, s, a);
         else hipLaunchKernelGGL((k_step_replay<IO, N, false, In>), grid, blk, 0, s, a);

@@ -183,6 +183,7 @@ DECODE_CASES = [
     (1, 7, 33, 4, "bf16", True, 2),
     (2, 2, 40, 2, "f32", True, 1),
     (2, 2, 40, 16, "bf16", True, 0),
+    (1, 2, 600, 16, "bf16", True, 4),   # three blocks of 256 channels, the last ragged
 ]
 STEPS = 6
 
