@@ -262,6 +262,8 @@ ssm_status make_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_st
         p->fwd.T = T;
         p->fwd.n_chunks = (int32_t)n;
     }
+    if ((double)batch * d_inner * d_state * 4.0 >= 2147483648.0)
+        return fail(SSM_ERR_UNSUPPORTED, "the backward needs batch * d_inner * d_state * 4 below 2 GiB");
     p->threads = (int32_t)std::min<int64_t>(256, (d_inner + 63) / 64 * 64);
     p->dblocks = (int32_t)((d_inner + p->threads - 1) / p->threads);
     p->waves = p->dblocks * (p->threads / 64);

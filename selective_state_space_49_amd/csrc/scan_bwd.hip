@@ -262,6 +262,72 @@ __global__ __launch_bounds__(256) void k_bwd_summary(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- sub-chunk staging
+// At the start of each sub-chunk the backward walk needs its kSub rows of x, dt, dy
+// (and z) and the state stored at its start. Loading them there would expose the HBM
+// latency once per sub-chunk, with only two waves per SIMD to cover it. Instead they
+// are copied into LDS by direct-to-LDS loads (no registers held while in flight) one
+// sub-chunk ahead, while the current one is computed. Per wave, in dwords:
+//   rows[s][j][lane]  stream s (x, dt, dy, z), row j of the sub-chunk; a 2-byte
+//                     element lands zero-extended in its lane's dword;
+//   st[q][lane][4]    the stored state in 16-byte pieces (N % 4 == 0), or st[n][lane].
+// The compiler does not order these loads against LDS reads, so the kernel waits
+// explicitly: vmcnt(0) before the LDS is read, lgkmcnt(0) before it is refilled.
+#define SSM_LDS __attribute__((address_space(3)))
+constexpr int kStageRows = 4 * kSub * 64;
+template <int N> struct Stage { static constexpr int dwords = kStageRows + N * 64; };
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+constexpr int kWaitVm0 = 0x0F70;    // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0)
+
+template <typename IO>
+__device__ __forceinline__ void row_to_lds(const RowStream<IO> &s, SSM_LDS uint32_t *dst,
+                                           uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(IO) == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.r, (SSM_LDS void *)dst, 2, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s.r, (SSM_LDS void *)dst, 4, voff, soff, 0, 0);
+}
+
+// Stage sub-chunk rows j0 .. j0 + kSub - 1 (rows past the chunk's ns read row j0) and
+// the lane's state entering the sub-chunk, at byte st_voff of the [batch][Dn][N] state
+// array st (null: a zero state). Both use buffer loads: the compiler then leaves their
+// waits to the kernel (a global-address load to LDS makes it wait for every store in
+// flight before the next LDS read).
+template <typename IO, int N, bool GATED>
+__device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream<IO> &xs,
+                                          const RowStream<IO> &dts, const RowStream<IO> &dys,
+                                          const RowStream<IO> &zs, uint32_t voff, uint32_t rb,
+                                          uint32_t j0, uint32_t ns, const float *st,
+                                          uint32_t st_voff, int lane) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+        const uint32_t r = (j0 + (j < (int)ns ? j : 0)) * rb;
+        row_to_lds<IO>(xs, stg + (0 * kSub + j) * 64, voff, r);
+        row_to_lds<IO>(dts, stg + (1 * kSub + j) * 64, voff, r);
+        row_to_lds<IO>(dys, stg + (2 * kSub + j) * 64, voff, r);
+        if (GATED) row_to_lds<IO>(zs, stg + (3 * kSub + j) * 64, voff, r);
+    }
+    if (!st) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) stg[kStageRows + n * 64 + lane] = 0u;  // either layout
+    } else {
+        const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(st), 0, -1, kRsrcWord3);
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSM_LDS void *)(stg + kStageRows + q * 256), 16,
+                                                         st_voff + 16 * q, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSM_LDS void *)(stg + kStageRows + n * 64), 4,
+                                                         st_voff + 4 * n, 0, 0, 0);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- gradients
 template <typename IO, int N, bool GATED>
 __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
@@ -274,7 +340,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
     const size_t M = (size_t)a.batch * a.Dn * N;
     const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
-    const float *hin = c == 0 ? (a.h0 ? a.h0 + col : nullptr) : a.sumH + (size_t)(c - 1) * M + col;
+    const float *hin_row = c == 0 ? a.h0 : a.sumH + (size_t)(c - 1) * M;  // state entering the chunk
+    const float *hin = hin_row ? hin_row + col : nullptr;
+    const uint32_t st_voff = (uint32_t)(col * sizeof(float));  // < 2 GiB (checked on the host)
     float A2[N], h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -303,7 +371,18 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         for (int n = 0; n < N; ++n)
             h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * Uniform<IO>::ld(Bp, t * N + n));
     });
-    // 2. backward walk by sub-chunks
+    // 2. backward walk by sub-chunks, each staged in LDS during the previous one
+    __shared__ uint32_t stage_mem[4 * Stage<N>::dwords];  // blocks have at most 4 waves
+    SSM_LDS uint32_t *stg = (SSM_LDS uint32_t *)stage_mem + (threadIdx.x / 64) * Stage<N>::dwords;
+    const int lane = threadIdx.x & 63;
+    const uint32_t nsub = (steps + kSub - 1) / kSub;
+    __builtin_amdgcn_s_waitcnt(0);  // the walk's stored states are written before they are read back
+    if (nsub > 0) {
+        const uint32_t k = nsub - 1;
+        stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, k * kSub, steps - k * kSub,
+                                k > 0 ? a.ckpt + (sub0 + k) * M : hin_row, st_voff, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     const int64_t mu_entry = (int64_t)a.n_chunks - 2 - c;  // adjoint entering from the right
     const float *mu = mu_entry < 0 ? (a.dh_final ? a.dh_final + col : nullptr)
                                    : a.revG + (size_t)mu_entry * M + col;
@@ -320,23 +399,38 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const bool want_dz = GATED && a.dz != nullptr;
     float *pbc = a.partBC + (size_t)ln.w * V;
     const size_t pbc_step = (size_t)a.waves * V;  // floats per (b, t) row of partials
-    const uint32_t nsub = (steps + kSub - 1) / kSub;
     for (uint32_t k = nsub; k > 0;) {
         --k;
         set_priority(k + 1, nsub);
         const uint32_t j0 = k * kSub;
         const uint32_t ns = min((uint32_t)kSub, steps - j0);
-        float xv[kSub], dv[kSub], yv[kSub], zv[kSub];
+        // The staged rows and state (complete: the last wait on vmcnt came after their
+        // loads were issued; the state is the stored one, or the chunk's incoming state
+        // for the first sub-chunk). Padding lanes read their clamped channel's values;
+        // their results are discarded.
+        float xv[kSub], dv[kSub], yv[kSub], zv[kSub], start[N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
-            const uint32_t r = (j0 + (j < (int)ns ? j : 0)) * rb;  // rows past the chunk read row j0
-            xv[j] = xs.ld(voff, r);
-            dv[j] = dts.ld(voff, r);
-            yv[j] = dys.ld(voff, r);
-            zv[j] = GATED ? zs.ld(voff, r) : 0.0f;
+            xv[j] = RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]);
+            dv[j] = RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]);
+            yv[j] = RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]);
+            zv[j] = GATED ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
         }
-        // padding lanes (which store no checkpoints) restart from the incoming state
-        const float *start = (k == 0 || !ln.valid) ? hin : a.ckpt + (sub0 + k) * M + col;
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < N / 4; ++q) {
+                const f4v v = *(const SSM_LDS f4v *)(stg + kStageRows + q * 256 + lane * 4);
+                start[4 * q] = v.x; start[4 * q + 1] = v.y; start[4 * q + 2] = v.z; start[4 * q + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < N; ++n) start[n] = __uint_as_float(stg[kStageRows + n * 64 + lane]);
+        }
+        if (k > 0) {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the LDS reads above are done
+            stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, (k - 1) * kSub, kSub,
+                                    k > 1 ? a.ckpt + (sub0 + k - 1) * M : hin_row, st_voff, lane);
+        }
         float hs[kSub][N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
@@ -344,13 +438,16 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
             const float u = dv[j] * xv[j];
 #pragma unroll
             for (int n = 0; n < N; ++n) {
-                const float prev = j == 0 ? (start ? start[n] : 0.0f) : hs[j - 1][n];
+                const float prev = j == 0 ? start[n] : hs[j - 1][n];
                 hs[j][n] = __builtin_fmaf(e2(dv[j] * A2[n]), prev, u * Uniform<IO>::ld(Bp, t * N + n));
             }
         }
 #pragma unroll
         for (int j = kSub - 1; j >= 0; --j) {
             if (j >= (int)ns) continue;  // uniform: every lane of the block has the same ns
+            // The next sub-chunk's staging loads were issued before any store still in
+            // flight here but this step's: wait for them before its stores.
+            if (j == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
             const int64_t t = t0 + j0 + j;
             float acc = 0.0f;
 #pragma unroll
@@ -382,7 +479,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
                 if (want_dz) dzs.st(voff, r, yv[j] * o * gp);
             }
             const float tot = wave_reduce_transpose<V>(vals);
-            const int lane = threadIdx.x & 63;
             constexpr int sh = 6 - Log2<V>::v;
             if ((lane & ((1 << sh) - 1)) == 0)
                 pbc[(size_t)(ln.b * a.L + t) * pbc_step + (lane >> sh)] = tot;
