@@ -261,8 +261,9 @@ ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, co
  * partial sums; dA, dB, dC and dD are reduced from them in a fixed order, so results
  * are deterministic. chunk_len: as in ssm_scan_fwd_ex (rounded down to a multiple of
  * 4 when there are several chunks). L == 0: dA = dD = 0, dh0 = dh_final (or 0).
- * Alignment: A, h0, dh_final, dh0 16 bytes; B, C, D, dA, dB, dC, dD 4 bytes; streams
- * one element; workspace 256 bytes. */
+ * SSM_ERR_UNSUPPORTED when batch * d_inner * d_state * 4 bytes (one state array) is
+ * 2 GiB or more. Alignment: A, h0, dh_final, dh0 16 bytes; B, C, D, dA, dB, dC, dD
+ * 4 bytes; streams one element; workspace 256 bytes. */
 size_t ssm_scan_bwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
                               int64_t chunk_len);
 ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const void *B,

@@ -153,3 +153,36 @@ def test_fused_step_argument_errors(lib):
         assert call(fn, N=5) == UNSUP
         assert call(fn, h=None) == NULL
         assert call(fn, Ln=0) == OK
+
+
+def _bwd_raw(lib, x=0x1000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None, h0=None,
+             dy=0x1000, dhf=None, dx=0x1000, ddt=0x1000, dz=None, dA=0x1000, dB=0x1000, dC=0x1000,
+             dD=0x1000, dh0=None, batch=1, L=8, Dn=4, N=4, io=0, chunk=0, ws=None, wsb=0):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lib.ssm_scan_bwd(p(x), p(dt), p(A), p(B), p(C), p(D), p(z), p(h0), p(dy), p(dhf), p(dx),
+                            p(ddt), p(dz), p(dA), p(dB), p(dC), p(dD), p(dh0), batch, L, Dn, N, io,
+                            chunk, p(ws), wsb, None)
+
+
+def test_backward_argument_errors(lib):
+    assert _bwd_raw(lib, N=3) == UNSUP
+    assert _bwd_raw(lib, io=4) == DTYPE
+    for k in ("x", "dt", "B", "C", "dy", "dx", "ddt", "dB", "dC", "A", "D", "dA", "dD"):
+        assert _bwd_raw(lib, **{k: None}) == NULL, k
+    assert _bwd_raw(lib, A=0x1004) == ALIGN
+    assert _bwd_raw(lib, dh0=0x1008) == ALIGN
+    assert _bwd_raw(lib, dhf=0x1004) == ALIGN
+    assert _bwd_raw(lib, dB=0x1002) == ALIGN
+    assert _bwd_raw(lib, io=1, dx=0x1001) == ALIGN
+    assert _bwd_raw(lib, Dn=0) == SHAPE
+    # several chunks need the workspace: states every 4 steps and the partial sums
+    need = ssm.ssm_scan_bwd_workspace(1, 200, 4, 4, 64)
+    assert need > ssm.ssm_scan_fwd_workspace_ex(1, 200, 4, 4, 64)
+    assert _bwd_raw(lib, L=200, chunk=64) == WS
+    assert _bwd_raw(lib, L=200, chunk=64, ws=0x10000, wsb=need - 1) == WS
+    assert _bwd_raw(lib, L=200, chunk=64, ws=0x10080, wsb=need) == ALIGN
+    assert _bwd_raw(lib, L=200, chunk=2) == UNSUP  # sub-chunks of 4 steps need chunks of 4
+    # one [batch][d_inner][d_state] fp32 state array must stay below 2 GiB
+    assert _bwd_raw(lib, batch=4, Dn=1 << 23, N=16, L=8) == UNSUP
+    assert "2 GiB" in ssm.ssm_last_error()
+    assert ssm.ssm_scan_bwd_workspace(4, 8, 1 << 23, 16, 0) == 0
