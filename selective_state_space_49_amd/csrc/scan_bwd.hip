@@ -514,17 +514,51 @@ __global__ void k_bwd_reduce_AD(BwdArgs a, int N) {
     }
 }
 
-// dB[b][t][n] and dC[b][t][n]: sums over the channel waves.
+// dB[b][t][n] and dC[b][t][n]: sums over the channel waves. A thread sums 4 adjacent
+// values (16-byte loads; 2N is a multiple of 4 for N >= 2) with four running sums over
+// the waves w = 0, 1, 2, 3 mod 4, added as (s0 + s1) + (s2 + s3): a fixed order.
 __global__ void k_bwd_reduce_BC(BwdArgs a, int N) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over batch * L * 2N
-    const int64_t V = 2 * N;
-    if (i >= a.batch * a.L * V) return;
-    const int64_t bt = i / V, j = i % V;
-    const float *p = a.partBC + bt * a.waves * V + j;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over batch * L * 2N / 4
+    const int64_t V = 2 * N, Q = V / 4;
+    if (i >= a.batch * a.L * Q) return;
+    const int64_t bt = i / Q, j = (i % Q) * 4;
+    const float4 *p = (const float4 *)(a.partBC + bt * a.waves * V + j);
+    const int64_t step = V / 4;  // float4s per wave
+    float4 s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    int w = 0;
+    for (; w + 4 <= a.waves; w += 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 v = p[(int64_t)(w + r) * step];
+            s[r].x += v.x; s[r].y += v.y; s[r].z += v.z; s[r].w += v.w;
+        }
+    }
+    for (int r = 0; w < a.waves; ++w, ++r) {
+        const float4 v = p[(int64_t)w * step];
+        s[r].x += v.x; s[r].y += v.y; s[r].z += v.z; s[r].w += v.w;
+    }
+    const float o[4] = {(s[0].x + s[1].x) + (s[2].x + s[3].x), (s[0].y + s[1].y) + (s[2].y + s[3].y),
+                        (s[0].z + s[1].z) + (s[2].z + s[3].z), (s[0].w + s[1].w) + (s[2].w + s[3].w)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t jj = j + k;
+        if (jj < N) a.dB[bt * N + jj] = o[k];
+        else a.dC[bt * N + (jj - N)] = o[k];
+    }
+}
+
+// The same for N = 1 (2 values per row), one value per thread.
+__global__ void k_bwd_reduce_BC1(BwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over batch * L * 2
+    if (i >= a.batch * a.L * 2) return;
+    const int64_t bt = i / 2, j = i % 2;
+    const float *p = a.partBC + bt * a.waves * 2 + j;
     float s = 0.0f;
-    for (int w = 0; w < a.waves; ++w) s += p[(int64_t)w * V];
-    if (j < N) a.dB[bt * N + j] = s;
-    else a.dC[bt * N + (j - N)] = s;
+    for (int w = 0; w < a.waves; ++w) s += p[(int64_t)w * 2];
+    if (j == 0) a.dB[bt] = s;
+    else a.dC[bt] = s;
 }
 
 template <typename IO, int N>
@@ -547,8 +581,13 @@ hipError_t launch_n(const BwdArgs &a, const ScanArgs &fwd, int io, bool gated, h
     else hipLaunchKernelGGL((k_bwd_chunk<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
     const int64_t nad = a.Dn * (N + 1);
     hipLaunchKernelGGL(k_bwd_reduce_AD, dim3((unsigned)((nad + 255) / 256)), dim3(256), 0, s, a, N);
-    const int64_t nbc = a.batch * a.L * 2 * N;
-    hipLaunchKernelGGL(k_bwd_reduce_BC, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a, N);
+    if constexpr (N >= 2) {
+        const int64_t nbc = a.batch * a.L * 2 * N / 4;
+        hipLaunchKernelGGL(k_bwd_reduce_BC, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a, N);
+    } else {
+        const int64_t nbc = a.batch * a.L * 2;
+        hipLaunchKernelGGL(k_bwd_reduce_BC1, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
