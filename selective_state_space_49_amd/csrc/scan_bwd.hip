@@ -406,14 +406,16 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         const uint32_t ns = min((uint32_t)kSub, steps - j0);
         // The staged rows and state (complete: the last wait on vmcnt came after their
         // loads were issued; the state is the stored one, or the chunk's incoming state
-        // for the first sub-chunk). Padding lanes read their clamped channel's values;
-        // their results are discarded.
+        // for the first sub-chunk). Padding lanes read their clamped channel's values
+        // with x and dy set to 0: then dt x = 0 and do = 0, so their dB and dC terms
+        // (lam dt x, do h) are exactly 0 for finite data and need no mask in the
+        // channel sums; their own outputs are not stored.
         float xv[kSub], dv[kSub], yv[kSub], zv[kSub], start[N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
-            xv[j] = RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]);
+            xv[j] = ln.valid ? RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]) : 0.0f;
             dv[j] = RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]);
-            yv[j] = RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]);
+            yv[j] = ln.valid ? RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]) : 0.0f;
             zv[j] = GATED ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
         }
         if constexpr (N % 4 == 0) {
@@ -465,8 +467,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
                 const float lt = __builtin_fmaf(dout, Uniform<IO>::ld(Cp, t * N + n), lam[n]);
                 const float w = __builtin_fmaf(-u, bn, hs[j][n]);  // a_t h_{t-1}
                 const float q = lt * w;
-                vals[n] = ln.valid ? lt * u : 0.0f;                 // dB_t[n] term
-                vals[N + n] = ln.valid ? dout * hs[j][n] : 0.0f;    // dC_t[n] term
+                vals[n] = lt * u;                // dB_t[n] term
+                vals[N + n] = dout * hs[j][n];   // dC_t[n] term
                 gx = __builtin_fmaf(lt, bn, gx);
                 gA = __builtin_fmaf(A2[n], q, gA);
                 dA[n] = __builtin_fmaf(dv[j], q, dA[n]);
