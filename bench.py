@@ -374,14 +374,21 @@ def traffic_for(info, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
+# Elements in the oracle's CPU sample: about 1-2 s of wall time on 16 host threads
+# (10-30 s of CPU work) for the real-state forward and backward; the complex oracle
+# costs about 4 times more per element.
+CPU_SAMPLE_ELEMS = 1 << 27
+
+
+def sample_width(shape, elems):
+    # channels to sample so that the whole sequence of every batch row gives ~elems
+    return max(1, min(shape.d_inner, -(-elems // (shape.batch * max(shape.L, 1)))))
+
+
 def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None):
     import oracle
     oracle.build(force=False)
-    if shape.complex_state:
-        k = 32
-    else:
-        k = 512 if shape.L >= 100000 else 128
-    k = min(k, shape.d_inner)
+    k = sample_width(shape, CPU_SAMPLE_ELEMS // (4 if shape.complex_state else 1))
     idx = workloads.sample_channels(shape.d_inner, k, seed=5).to("cuda")
     g = lambda t: None if t is None else t.index_select(2, idx).cpu()
     args = (g(d["x"]), g(d["dt"]), d["A"].index_select(0, idx).cpu(), d["B"].cpu(), d["C"].cpu(),
@@ -413,7 +420,7 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
     import numpy as np
     import oracle
     oracle.build(force=False)
-    k = min(256 if shape.L >= 100000 else 128, shape.d_inner)
+    k = sample_width(shape, CPU_SAMPLE_ELEMS // 2)
     idx = workloads.sample_channels(shape.d_inner, k, seed=5)
     g = lambda t: None if t is None else oracle.to_f64(t.index_select(2, idx.to(t.device)))
     x, dt, z = g(d["x"]), g(d["dt"]), g(d["z"])
@@ -438,6 +445,62 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
                       f"{shape.batch} ({elems} elements, {dtm:.1f} s wall), fp64 loops per channel "
                       f"(forward keeping every state, then backward), channels split over "
                       f"{len(parts)} threads"}
+
+
+def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=64):
+    """The oracle's decode step (or, with conv_k, its fused step) for every layer on the
+    first `seqs` sequences, `tokens` tokens in a row with the state carried, the layers
+    split over host threads. Inputs are drawn once; the timed region is the oracle."""
+    import threading
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    Ln, Dn, N = shape.n_layers, shape.d_inner, shape.d_state
+    S = min(seqs, shape.n_seq)
+    par = workloads.make_decode_params(shape, "cpu")
+    tok = workloads.make_decode_step(shape, 0, "cpu")
+    sl = lambda t: None if t is None else np.ascontiguousarray(oracle.to_f64(t[:, :S]))
+    x, z, B, C = sl(tok["x"]), sl(tok["z"]), sl(tok["B"]), sl(tok["C"])
+    A, D = oracle.to_f64(par["A"]), oracle.to_f64(par["D"])
+    fused = conv_k is not None
+    if fused:
+        ist = workloads.make_decode_input_stage(shape, conv_k, "cpu")
+        dt = sl(workloads.make_decode_dt_raw(shape, 0, "cpu"))
+        f64 = lambda t: None if t is None else oracle.to_f64(t)
+        cw, cb, db = f64(ist["conv_w"]), f64(ist["conv_b"]), f64(ist["dt_bias"])
+        cs = sl(ist["conv_state"]) if ist["conv_state"] is not None else np.zeros((Ln, S, max(conv_k - 1, 0), Dn))
+        if conv_k == 0:  # no convolution: the input stage is softplus(dt + bias) alone
+            dt = np.stack([oracle.softplus(dt[l], db[l]) for l in range(Ln)])
+    else:
+        dt = sl(tok["dt"])
+    h = np.zeros((Ln, S, Dn, N))
+    groups = [(int(g[0]), int(g[-1]) + 1) for g in np.array_split(np.arange(Ln), min(threads, Ln)) if len(g)]
+    log("cpu baseline (decode): oracle on", Ln, "layers x", S, "sequences x", tokens, "tokens with",
+        len(groups), "threads")
+
+    def work(l0, l1):
+        r = slice(l0, l1)
+        hh, cc = h[r], (cs[r] if fused else None)
+        for _ in range(tokens):
+            if fused and conv_k > 0:
+                _, hh, cc = oracle.step_fused(hh, cc, x[r], dt[r], A[r], B[r], C[r], D[r], z if z is None else z[r],
+                                              conv_w=cw[r], conv_b=None if cb is None else cb[r],
+                                              dt_bias=None if db is None else db[r])
+            else:
+                _, hh = oracle.step(hh, x[r], dt[r], A[r], B[r], C[r], D[r], None if z is None else z[r])
+
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=work, args=g) for g in groups]
+    for t in ts: t.start()
+    for t in ts: t.join()
+    dtm = time.perf_counter() - t0
+    elems = Ln * S * Dn * tokens
+    what = "fused decode step (conv + silu, softplus, scan)" if fused else "decode step"
+    return {"value": elems / dtm, "unit": "elements/s", "cores": len(groups), "kind": "oracle",
+            "sample": f"{what}: all {Ln} layers x {S} of {shape.n_seq} sequences x {Dn} channels, "
+                      f"{tokens} tokens (token 0's inputs each time) with the state carried ({elems} "
+                      f"elements, {dtm:.1f} s wall), "
+                      f"fp64, layers split over {len(groups)} threads"}
 
 
 def main():
@@ -553,7 +616,11 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not is_decode:
+    if not args.no_cpu_baseline and is_decode and not shape.complex_state:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline_decode(shape, workloads, threads,
+                                                  args.conv_k if args.fused else None)
+    elif not args.no_cpu_baseline and not is_decode:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         if args.backward:
             out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads)
