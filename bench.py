@@ -447,7 +447,7 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
                       f"{len(parts)} threads"}
 
 
-def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=64):
+def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=192):
     """The oracle's decode step (or, with conv_k, its fused step) for every layer on the
     first `seqs` sequences, `tokens` tokens in a row with the state carried, the layers
     split over host threads. Inputs are drawn once; the timed region is the oracle."""
