@@ -83,10 +83,10 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * exact re-association of the recurrence; results differ from a sequential fp32
  * loop only by rounding and by one bounded truncation: a chunk's end state is
  * accumulated only over its last steps back to the point where the decay
- * exp(Re A * sum of dt) of every state of 64 neighbouring channels is below 2^-64.
- * What is dropped changes a carried state by at most 2^-64 * (chunk_len *
- * max|dt x B| + |incoming state|), about 2^-44 of the input scale, far below fp32
- * resolution. NaN or Inf older than that window do not propagate past the chunk
+ * exp(Re A * sum of dt) of every state of 64 neighbouring channels is below 2^-48.
+ * What is dropped changes a carried state by at most 2^-48 * (chunk_len *
+ * max|dt x B| + |incoming state|), at most 2^-28 of the input scale for chunks
+ * below 2^20 steps, below fp32 resolution. NaN or Inf older than that window do not propagate past the chunk
  * boundary. workspace must hold ssm_scan_fwd_workspace(...) bytes
  * (0 is possible, then workspace may be NULL). It is scratch: contents on entry
  * are ignored and on return are unspecified. L == 0 writes h_final = h0 (or

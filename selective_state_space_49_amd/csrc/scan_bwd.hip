@@ -19,7 +19,7 @@
 //   1. the forward's chunk summaries and carry: the state entering every chunk;
 //   2. k_bwd_summary: per chunk c >= 1 the adjoint it passes to chunk c-1 from a zero
 //      carry-in, G_c, and its total decay Q_c, over a window that ends where the
-//      decay reaches 2^-64 (the mirror of the forward's horizon);
+//      decay reaches 2^-kHorizon (the mirror of the forward's horizon);
 //   3. the forward's carry kernel over the chunks in reverse order, seeded with
 //      dh_final: the adjoint entering every chunk from the right;
 //   4. k_bwd_chunk: per chunk, a forward walk from the incoming state that stores the
@@ -171,7 +171,7 @@ __device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStr
 
 // First row (chunk-relative) from which the decay back to row 0 is below 2^-kHorizon
 // for every state of every lane of the wave, walking dt forward in whole blocks of
-// kB rows: rows at or beyond it reach row 0 with weight below 2^-64. Returns T when
+// kB rows: rows at or beyond it reach row 0 with weight below 2^-kHorizon. Returns T when
 // the horizon is not reached within the whole blocks (A >= 0, dt = 0, NaN, short T).
 template <typename IO>
 __device__ __forceinline__ uint32_t horizon_end(const RowStream<IO> &dt, uint32_t voff,

@@ -136,10 +136,10 @@ __device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowSt
 // shrink going back in time. Once log2(e) * Re A[n] * (sum of dt over the last rows)
 // <= -kHorizon for every state of every lane of a wave, everything older enters the
 // end state with weight below 2^-kHorizon. Dropping it changes a carried state by at
-// most 2^-64 * T * max|dt x B| (about 2^-44 of the input scale for T < 2^20): far
-// below fp32 resolution. The chunk's total transfer factor exp(A * sum dt) is then
-// below 2^-64 in modulus and is dropped the same way.
-constexpr float kHorizon = 64.0f;
+// most 2^-48 * T * max|dt x B| (at most 2^-28 of the input scale for T < 2^20): below
+// fp32 resolution (2^-24). The chunk's total transfer factor exp(A * sum dt) is then
+// below 2^-48 in modulus and is dropped the same way.
+constexpr float kHorizon = 48.0f;
 // Priority scale of the summary windows (steps): longer windows go first.
 constexpr uint32_t kSummaryPrioScale = 2048;
 constexpr int kB = 32;  // rows per block of the backward walk
