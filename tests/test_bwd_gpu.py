@@ -17,6 +17,7 @@ import oracle
 import selective_state_space_49_amd as ssm
 from tests.gpu_util import TOL, bitwise_equal, rel_err, say, to_dev
 from workloads import WORKLOADS, ScanShape, make_h0, make_scan_inputs, sample_channels
+from tests.gpu_util import gather_channels
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +159,40 @@ def test_backward_full_size_jamba_layer():
     _compare(got, ref, TOL["bf16"])
     for k in ("dx", "ddt", "dz", "dA", "dB", "dC", "dD"):
         assert torch.isfinite(got[k].float()).all(), k
+
+
+def test_backward_full_size_long_context_sampled():
+    # The 256k prefill's backward (batch 1, L 262144, 8192 channels, N 16, bf16) in the
+    # library's own chunk plan, as the benchmark times it. dy is nonzero on a channel
+    # sample only: the other channels then carry a zero adjoint, so dB and dC (sums over
+    # channels) hold exactly the sample's contributions and the oracle on the sample
+    # checks every gradient; the other channels' dx, ddt and dz must be exactly 0.
+    shape = WORKLOADS["long_context_256k"]
+    say("backward 256k: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    idx = sample_channels(shape.d_inner, 24, seed=13)
+    g = torch.Generator(device="cuda").manual_seed(79)
+    dy = torch.zeros(d["x"].shape, dtype=d["x"].dtype, device="cuda")
+    dy[:, :, idx.cuda()] = torch.randn((shape.batch, shape.L, len(idx)), generator=g,
+                                       device="cuda").to(dy.dtype)
+    say("backward 256k: running")
+    got = ssm.ssm_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy)
+    torch.cuda.synchronize()
+    rest = torch.ones(shape.d_inner, dtype=torch.bool)
+    rest[idx] = False
+    for k in ("dx", "ddt", "dz"):
+        assert not got[k][:, :, rest.cuda()].any(), f"{k} nonzero outside the sample"
+    gc = lambda t: gather_channels(t, idx)
+    sub = {"x": gc(d["x"]), "dt": gc(d["dt"]), "z": gc(d["z"]), "dy": gc(dy), "A": d["A"].cpu()[idx],
+           "B": d["B"].cpu(), "C": d["C"].cpu(), "D": d["D"].cpu()[idx], "h0": None, "dh_final": None}
+    say("backward 256k: oracle on", len(idx), "channels")
+    ref = _oracle_threaded(sub)
+    tol = TOL["bf16"]
+    for k in ("dx", "ddt", "dz"):
+        e = rel_err(gc(got[k]), ref[k])
+        assert e <= tol, f"{k}: error {e:.3e}"
+    for k, v in (("dA", got["dA"].cpu()[idx]), ("dD", got["dD"].cpu()[idx]), ("dB", got["dB"]),
+                 ("dC", got["dC"])):
+        e = rel_err(v, ref[k])
+        assert e <= tol, f"{k}: error {e:.3e}"
+    assert rel_err(got["dh0"].index_select(1, idx.cuda()).cpu(), ref["dh0"]) <= tol

@@ -262,11 +262,13 @@ def test_fused_prefill_equals_decode():
     assert bitwise_equal(cs[0], so)
 
 
-def test_fused_full_size_jamba_layer_sampled():
-    # The Jamba-shaped layer (batch 2, L 4096, 8192 channels, N 16, bf16) through the
-    # fused entry point in the library's own chunk plan; sampled channels vs the oracle.
-    shape = WORKLOADS["jamba_layer_prefill"]
-    say("fused full size: generating inputs")
+@pytest.mark.parametrize("name,k", [("jamba_layer_prefill", 128), ("long_context_256k", 24)])
+def test_fused_full_size_sampled(name, k):
+    # The Jamba-shaped layer (batch 2, L 4096) and the 256k prefill (batch 1, L 262144),
+    # 8192 channels, N 16, bf16, through the fused entry point in the library's own chunk
+    # plan (the configuration the benchmark times); sampled channels vs the oracle.
+    shape = WORKLOADS[name]
+    say("fused full size:", name, "generating inputs")
     d = make_scan_inputs(shape, "cuda")
     s = make_input_stage(shape, 4, "cuda")
     say("fused full size: running")
@@ -274,7 +276,7 @@ def test_fused_full_size_jamba_layer_sampled():
                                        conv_w=s["conv_w"], conv_b=s["conv_b"],
                                        conv_state0=s["conv_state0"], dt_bias=s["dt_bias"])
     torch.cuda.synchronize()
-    idx = sample_channels(shape.d_inner, 128, seed=9)
+    idx = sample_channels(shape.d_inner, k, seed=9)
     g = lambda t: gather_channels(t, idx)
     say("fused full size: oracle on", len(idx), "channels")
     yr, hr, sr = oracle.scan_fused(g(d["x"]), g(s["dt_raw"]), d["A"].cpu()[idx], d["B"].cpu(),
