@@ -65,6 +65,10 @@ def _load():
         lib.oracle_softplus_f64.restype = ctypes.c_int
         lib.oracle_scan_bwd_f64.argtypes = [i64, i64, i64, i64] + [dp] * 18
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
+        lib.oracle_scan_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 12
+        lib.oracle_scan_trap_f64.restype = ctypes.c_int
+        lib.oracle_step_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 11
+        lib.oracle_step_trap_f64.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -276,3 +280,46 @@ def scan_threaded(x, dt, A, B, C, D, z=None, h0=None, threads: int = 1, complex_
 def _check(a, shape, name):
     if tuple(a.shape) != tuple(shape):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(a.shape)}")
+
+
+def scan_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
+    """Real-state prefill with the exponential-trapezoidal discretisation. As scan(),
+    plus the input before step 0: x_prev [b, Dn] and B_prev [b, N] (None: zero).
+    Returns (y [b, L, Dn], h_final [b, Dn, N])."""
+    x, dt, A, B, C, D, z, h0, x_prev, B_prev = map(to_f64, (x, dt, A, B, C, D, z, h0, x_prev, B_prev))
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    _check(dt, (b, L, Dn), "dt"); _check(B, (b, L, N), "B"); _check(C, (b, L, N), "C")
+    _check(A, (Dn, N), "A"); _check(D, (Dn,), "D")
+    if z is not None: _check(z, (b, L, Dn), "z")
+    if h0 is not None: _check(h0, (b, Dn, N), "h0")
+    if x_prev is not None: _check(x_prev, (b, Dn), "x_prev")
+    if B_prev is not None: _check(B_prev, (b, N), "B_prev")
+    y = np.empty((b, L, Dn)); hf = np.empty((b, Dn, N))
+    rc = _load().oracle_scan_trap_f64(b, L, Dn, N, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                                      _p(z), _p(h0), _p(x_prev), _p(B_prev), _p(y), _p(hf))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_trap_f64 failed")
+    return y, hf
+
+
+def step_trap(h, x_prev, B_prev, x, dt, A, B, C, D, z=None):
+    """One exponential-trapezoidal decode token. h: [Ln, S, Dn, N]; x_prev, x, dt, z:
+    [Ln, S, Dn]; B_prev, B, C: [Ln, S, N]; A: [Ln, Dn, N]; D: [Ln, Dn]. x_prev and
+    B_prev are the previous token's x and B (None: no previous input). Returns
+    (y [Ln, S, Dn], h_new) without touching h."""
+    h = to_f64(h).copy()
+    x_prev, B_prev, x, dt, A, B, C, D, z = map(to_f64, (x_prev, B_prev, x, dt, A, B, C, D, z))
+    Ln, S, Dn = x.shape
+    N = h.shape[-1]
+    _check(h, (Ln, S, Dn, N), "h"); _check(B, (Ln, S, N), "B"); _check(C, (Ln, S, N), "C")
+    _check(A, (Ln, Dn, N), "A"); _check(D, (Ln, Dn), "D"); _check(dt, (Ln, S, Dn), "dt")
+    if z is not None: _check(z, (Ln, S, Dn), "z")
+    if x_prev is not None: _check(x_prev, (Ln, S, Dn), "x_prev")
+    if B_prev is not None: _check(B_prev, (Ln, S, N), "B_prev")
+    y = np.empty((Ln, S, Dn))
+    rc = _load().oracle_step_trap_f64(Ln, S, Dn, N, _p(h), _p(x_prev), _p(B_prev), _p(x), _p(dt),
+                                      _p(A), _p(B), _p(C), _p(D), _p(z), _p(y))
+    if rc != 0:
+        raise RuntimeError("oracle_step_trap_f64 failed")
+    return y, h

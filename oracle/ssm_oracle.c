@@ -375,3 +375,105 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
     free(lam);
     return 0;
 }
+
+/*
+ * Exponential-trapezoidal discretisation (real diagonal state).
+ *
+ * "Jamba — SSM-Transformer Híbrido", section "Mamba-3: a linha de base de SSM puro
+ * em 2026", item 1: Mamba-3 replaces the Euler discretisation (Bbar = dt B, above)
+ * by a recurrence in which a convolution-like operation acts on the state input
+ * inside the recurrence. The page gives no formula; the reading taken here is the
+ * plain rule the name describes. Over a step of length dt the exact update of
+ * h' = A h + B(s) x(s) adds the integral of exp(A (dt - s)) B(s) x(s) over [0, dt];
+ * Euler takes dt B_t x_t, the trapezoid rule averages the integrand at both ends:
+ *
+ *     h_t = dA h_{t-1} + (dt/2) (dA B_{t-1} x_{t-1} + B_t x_t),   dA = exp(dt A),
+ *
+ * a two-tap filter over the state inputs B x, with the older tap decayed. The first
+ * step's previous input is B_prev x_prev (NULL: zero, a sequence with no input
+ * before it); a caller resuming a sequence passes the last step of the previous
+ * part. y_t is as in the Euler scan. Order of operations:
+ *     dA = exp(dt * A[d][n]);  w = 0.5 * dt;
+ *     h[n] = (dA * h[n]) + w * ((dA * (Bp[n] * xp)) + (B[n] * x));
+ *     acc = acc + C[n] * h[n]  (n ascending);  y = acc + D[d] * x;  then the gate.
+ * Layouts as above; x_prev [batch][Dn], B_prev [batch][N].
+ */
+int oracle_scan_trap_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
+                         const double *x, const double *dt, const double *A,
+                         const double *B, const double *C, const double *Dv,
+                         const double *z, const double *h0,
+                         const double *x_prev, const double *B_prev,
+                         double *y, double *h_final)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || N <= 0) return -1;
+    double *h = (double *)malloc((size_t)N * sizeof(double));
+    if (!h) return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < Dn; ++d) {
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+            /* the input before step 0 */
+            const int has_prev = x_prev && B_prev;
+            double xp = has_prev ? x_prev[b * Dn + d] : 0.0;
+            const double *Bp = has_prev ? B_prev + b * N : NULL;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t i = (b * L + t) * Dn + d;
+                const int64_t s = (b * L + t) * N;
+                const double xv = x[i], dv = dt[i];
+                const double w = 0.5 * dv;
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double dA = exp(dv * A[d * N + n]);
+                    const double prev = Bp ? Bp[n] * xp : 0.0;
+                    h[n] = dA * h[n] + w * (dA * prev + B[s + n] * xv);
+                    acc = acc + C[s + n] * h[n];
+                }
+                double yv = acc + Dv[d] * xv;
+                if (z) yv = yv * silu(z[i]);
+                y[i] = yv;
+                xp = xv;
+                Bp = B + s;
+            }
+            if (h_final)
+                for (int64_t n = 0; n < N; ++n) h_final[(b * Dn + d) * N + n] = h[n];
+        }
+    }
+    free(h);
+    return 0;
+}
+
+/* One decode token of the exponential-trapezoidal recurrence; h updated in place.
+ * x_prev [n_layers][n_seq][Dn] and B_prev [n_layers][n_seq][N] are the previous
+ * token's x and B (NULL: no previous input). */
+int oracle_step_trap_f64(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N,
+                         double *h, const double *x_prev, const double *B_prev,
+                         const double *x, const double *dt, const double *A,
+                         const double *B, const double *C, const double *Dv,
+                         const double *z, double *y)
+{
+    if (n_layers < 0 || n_seq < 0 || Dn < 0 || N <= 0) return -1;
+    const int has_prev = x_prev && B_prev;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        for (int64_t q = 0; q < n_seq; ++q) {
+            const int64_t s = (l * n_seq + q) * N;
+            for (int64_t d = 0; d < Dn; ++d) {
+                const int64_t i = (l * n_seq + q) * Dn + d;
+                double *hs = h + i * N;
+                const double *Ad = A + (l * Dn + d) * N;
+                const double xv = x[i], dv = dt[i];
+                const double w = 0.5 * dv;
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double dA = exp(dv * Ad[n]);
+                    const double prev = has_prev ? B_prev[s + n] * x_prev[i] : 0.0;
+                    hs[n] = dA * hs[n] + w * (dA * prev + B[s + n] * xv);
+                    acc = acc + C[s + n] * hs[n];
+                }
+                double yv = acc + Dv[l * Dn + d] * xv;
+                if (z) yv = yv * silu(z[i]);
+                y[i] = yv;
+            }
+        }
+    }
+    return 0;
+}

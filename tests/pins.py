@@ -26,6 +26,13 @@ pages or plain mathematics fix:
   backward      central finite differences of sum(dy y) + sum(dh_final h_final)
                 through the forward oracle, for every element of every input, against
                 the backward oracle's gradients.
+  trapezoid     the exponential-trapezoidal discretisation (the plain reading of the
+                Mamba-3 item on the same page): each step's two input taps written
+                out as a sum with exp of summed dt; with A = 0 the state is exactly
+                numpy's trapezoid rule over the samples B x on the time grid; against
+                the closed-form solution of the continuous ODE the error falls about
+                4x per halved step (second order), where Euler's halves; split/resume
+                with the previous input passed on, and L decode steps, bit for bit.
   input stage   the MambaBlock's causal depthwise convolution against numpy's
                 np.convolve (a true convolution, so the taps go in reversed) and an
                 impulse response; the carried conv state against the plain
@@ -468,6 +475,135 @@ def pin_backward_finite_differences(O, tol=1e-7):
             assert g["dz"] is None
 
 
+# ----------------------------------------------------------------------------- trapezoid
+
+def brute_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
+    """The exponential-trapezoidal state written out: with S_t the running sum of dt
+    (S_-1 = 0), p_s = B_s x_s and p_-1 the input before step 0,
+        h_t = exp(A S_t) h0 + sum_{s<=t} (dt_s / 2) (exp(A (S_t - S_s)) p_s
+                                                  + exp(A (S_t - S_{s-1})) p_{s-1})."""
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    S = np.concatenate([np.zeros((b, 1, Dn)), np.cumsum(dt, axis=1)], axis=1)   # S[:, t+1] = S_t
+    y = np.zeros((b, L, Dn)); hf = np.zeros((b, Dn, N))
+    for bi in range(b):
+        for d in range(Dn):
+            p = np.zeros((L + 1, N))                                        # p[s+1] = p_s
+            if x_prev is not None:
+                p[0] = B_prev[bi] * x_prev[bi, d]
+            p[1:] = B[bi] * x[bi, :, d][:, None]
+            for t in range(L):
+                h = np.zeros(N) if h0 is None else np.exp(A[d] * S[bi, t + 1, d]) * h0[bi, d]
+                for s_ in range(t + 1):
+                    wgt = dt[bi, s_, d] / 2.0
+                    h = h + wgt * (np.exp(A[d] * (S[bi, t + 1, d] - S[bi, s_ + 1, d])) * p[s_ + 1]
+                                   + np.exp(A[d] * (S[bi, t + 1, d] - S[bi, s_, d])) * p[s_])
+                yv = float(C[bi, t] @ h) + D[d] * x[bi, t, d]
+                if z is not None:
+                    yv *= silu(z[bi, t, d])
+                y[bi, t, d] = yv
+                if t == L - 1:
+                    hf[bi, d] = h
+    return y, hf
+
+
+def pin_trap_brute_force(O, tol=1e-12):
+    for seed, with_prev in [(71, True), (72, False)]:
+        inp = tiny_real(seed, L=16)
+        r = np.random.default_rng(seed + 100)
+        b, L, Dn = inp["x"].shape
+        xp = r.normal(0, 1, (b, Dn)) if with_prev else None
+        Bp = r.normal(0, 1, (b, inp["A"].shape[1])) if with_prev else None
+        y, hf = O.scan_trap(**inp, x_prev=xp, B_prev=Bp)
+        yb, hb = brute_trap(**inp, x_prev=xp, B_prev=Bp)
+        assert _rel(y, yb) <= tol and _rel(hf, hb) <= tol, f"trapezoid vs brute force (prev={with_prev})"
+
+
+def pin_trap_a_zero_is_trapezoid_rule(O, tol=1e-12):
+    # With A = 0 nothing decays: the state is h0 plus the trapezoid-rule integral of
+    # the samples p_s = B_s x_s over the time grid (0, dt_0, dt_0 + dt_1, ..), p_-1 at 0.
+    r = np.random.default_rng(73)
+    b, L, Dn, N = 2, 11, 3, 4
+    x = r.normal(0, 1, (b, L, Dn)); dt = r.uniform(0.05, 0.9, (b, L, Dn))
+    B = r.normal(0, 1, (b, L, N)); C = r.normal(0, 1, (b, L, N))
+    xp = r.normal(0, 1, (b, Dn)); Bp = r.normal(0, 1, (b, N)); h0 = r.normal(0, 1, (b, Dn, N))
+    y, hf = O.scan_trap(x, dt, np.zeros((Dn, N)), B, C, np.zeros(Dn), None, h0, x_prev=xp, B_prev=Bp)
+    for bi in range(b):
+        for d in range(Dn):
+            grid = np.concatenate([[0.0], np.cumsum(dt[bi, :, d])])
+            samples = np.concatenate([(Bp[bi] * xp[bi, d])[None], B[bi] * x[bi, :, d][:, None]])  # [L+1, N]
+            for t in range(L):
+                h = h0[bi, d] + np.trapezoid(samples[:t + 2], grid[:t + 2], axis=0)
+                assert abs(y[bi, t, d] - float(C[bi, t] @ h)) <= tol * max(1.0, np.abs(h).max()), "A = 0: y"
+            assert _rel(hf[bi, d], h) <= tol, "A = 0: trapezoid rule"
+
+
+def pin_trap_second_order(O):
+    # h' = -a h + b cos(w s) from h(0) = h0, sampled at s = k T / M: the discrete state
+    # after M steps against the closed form
+    #   h(T) = e^{-aT} h0 + b (a cos wT + w sin wT - a e^{-aT}) / (a^2 + w^2).
+    # The trapezoid rule is second order: the error falls ~4x per halved step; the
+    # Euler scan's (first order) ~2x.
+    a, bb, w, T, h0 = 1.3, 0.7, 2.1, 3.0, 0.4
+    exact = np.exp(-a * T) * h0 + bb * (a * np.cos(w * T) + w * np.sin(w * T) - a * np.exp(-a * T)) / (a * a + w * w)
+    errs, errs_euler = [], []
+    for M in (40, 80, 160):
+        dt = np.full((1, M, 1), T / M)
+        s = np.arange(1, M + 1) * (T / M)
+        x = np.cos(w * s).reshape(1, M, 1)
+        B = np.full((1, M, 1), bb); C = np.ones((1, M, 1))
+        A = np.full((1, 1), -a); D = np.zeros(1); H0 = np.full((1, 1, 1), h0)
+        _, hf = O.scan_trap(x, dt, A, B, C, D, None, H0, x_prev=np.ones((1, 1)), B_prev=np.full((1, 1), bb))
+        _, he = O.scan(x, dt, A, B, C, D, None, H0)
+        errs.append(abs(hf[0, 0, 0] - exact)); errs_euler.append(abs(he[0, 0, 0] - exact))
+    for e1, e2 in zip(errs, errs[1:]):
+        assert 3.6 <= e1 / e2 <= 4.4, f"trapezoid convergence ratio {e1 / e2:.3f}"
+    for e1, e2 in zip(errs_euler, errs_euler[1:]):
+        assert 1.7 <= e1 / e2 <= 2.3, f"Euler convergence ratio {e1 / e2:.3f}"
+
+
+def pin_trap_split_resume(O):
+    inp = tiny_real(74, L=30)
+    r = np.random.default_rng(174)
+    b, L, Dn = inp["x"].shape
+    N = inp["A"].shape[1]
+    xp, Bp = r.normal(0, 1, (b, Dn)), r.normal(0, 1, (b, N))
+    y, hf = O.scan_trap(**inp, x_prev=xp, B_prev=Bp)
+    k = 13
+    part = lambda v, sl: None if v is None else v[:, sl]
+    y1, h1 = O.scan_trap(part(inp["x"], slice(0, k)), part(inp["dt"], slice(0, k)), inp["A"],
+                         part(inp["B"], slice(0, k)), part(inp["C"], slice(0, k)), inp["D"],
+                         part(inp["z"], slice(0, k)), inp["h0"], x_prev=xp, B_prev=Bp)
+    y2, h2 = O.scan_trap(part(inp["x"], slice(k, L)), part(inp["dt"], slice(k, L)), inp["A"],
+                         part(inp["B"], slice(k, L)), part(inp["C"], slice(k, L)), inp["D"],
+                         part(inp["z"], slice(k, L)), h1, x_prev=inp["x"][:, k - 1],
+                         B_prev=inp["B"][:, k - 1])
+    assert _bitwise(np.concatenate([y1, y2], axis=1), y) and _bitwise(h2, hf), "trapezoid split/resume"
+
+
+def pin_trap_step_equals_scan(O):
+    # L decode steps, each given the previous token's x and B, against one prefill per
+    # (layer, sequence); two layers with their own A and D.
+    r = np.random.default_rng(75)
+    Ln, S, Dn, N, L = 2, 3, 3, 4, 8
+    x = r.normal(0, 1, (Ln, S, L, Dn)); dt = np.log1p(np.exp(r.normal(-1, 0.5, (Ln, S, L, Dn))))
+    z = r.normal(0, 1, (Ln, S, L, Dn))
+    B = r.normal(0, 1, (Ln, S, L, N)); C = r.normal(0, 1, (Ln, S, L, N))
+    A = -np.exp(r.normal(0, 0.5, (Ln, Dn, N))); D = r.normal(1, 0.1, (Ln, Dn))
+    h = r.normal(0, 1, (Ln, S, Dn, N))
+    xp0, Bp0 = r.normal(0, 1, (Ln, S, Dn)), r.normal(0, 1, (Ln, S, N))
+    hs, ys = h, []
+    for t in range(L):
+        xp = xp0 if t == 0 else x[:, :, t - 1]
+        Bp = Bp0 if t == 0 else B[:, :, t - 1]
+        yt, hs = O.step_trap(hs, xp, Bp, x[:, :, t], dt[:, :, t], A, B[:, :, t], C[:, :, t], D, z[:, :, t])
+        ys.append(yt)
+    ys = np.stack(ys, axis=2)
+    for l in range(Ln):
+        yl, hl = O.scan_trap(x[l], dt[l], A[l], B[l], C[l], D[l], z[l], h[l], x_prev=xp0[l], B_prev=Bp0[l])
+        assert _bitwise(ys[l], yl) and _bitwise(hs[l], hl), f"trapezoid decode vs prefill, layer {l}"
+
+
 ALL_PINS = [
     pin_brute_force, pin_convolution, pin_geometric_series, pin_dt_zero, pin_linearity,
     pin_split_resume, pin_step_equals_scan, pin_isolation, pin_state_bytes,
@@ -478,4 +614,6 @@ ALL_PINS = [
     lambda O: pin_layers_are_independent(O, complex_state=True),
     pin_conv_matches_numpy, pin_conv_impulse, pin_conv_state_carry, pin_softplus,
     pin_fused_identity_filter, pin_fused_step_equals_scan, pin_backward_finite_differences,
+    pin_trap_brute_force, pin_trap_a_zero_is_trapezoid_rule, pin_trap_second_order,
+    pin_trap_split_resume, pin_trap_step_equals_scan,
 ]

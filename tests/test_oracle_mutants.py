@@ -68,6 +68,17 @@ MUTANTS = {
     "bwd_dD_ungated": ("dD[d] += dout * xv;", "dD[d] += dy[i] * xv;"),
     "bwd_dh_final_ignored": ("lam[n] = dh_final ? dh_final[(b * Dn + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
     "bwd_dB_without_dt": ("dB[s + n] += lt * dv * xv;", "dB[s + n] += lt * xv;"),
+    "trap_prev_not_decayed": ("                    const double prev = Bp ? Bp[n] * xp : 0.0;\n                    h[n] = dA * h[n] + w * (dA * prev + B[s + n] * xv);",
+                              "                    const double prev = Bp ? Bp[n] * xp : 0.0;\n                    h[n] = dA * h[n] + w * (prev + B[s + n] * xv);"),
+    "trap_full_step_weight": ("const double w = 0.5 * dv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);\n                    const double prev = Bp",
+                              "const double w = dv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);\n                    const double prev = Bp"),
+    "trap_prev_input_not_advanced": ("                xp = xv;\n", ""),
+    "trap_prev_B_row_ahead": ("                Bp = B + s;", "                Bp = B + s + N;"),
+    "trap_first_prev_ignored": ("double xp = has_prev ? x_prev[b * Dn + d] : 0.0;", "double xp = 0.0;"),
+    "trap_decode_prev_is_current_B": ("const double prev = has_prev ? B_prev[s + n] * x_prev[i] : 0.0;",
+                                      "const double prev = has_prev ? B[s + n] * x_prev[i] : 0.0;"),
+    "trap_decode_prev_not_decayed": ("hs[n] = dA * hs[n] + w * (dA * prev + B[s + n] * xv);",
+                                     "hs[n] = dA * hs[n] + w * (prev + B[s + n] * xv);"),
 }
 
 
@@ -94,7 +105,7 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     lib = ctypes.CDLL(str(so))
     for fname in ("oracle_scan_f64", "oracle_scan_c128", "oracle_step_f64", "oracle_step_c128",
                   "oracle_state_bytes", "oracle_conv_silu_f64", "oracle_softplus_f64",
-                  "oracle_scan_bwd_f64"):
+                  "oracle_scan_bwd_f64", "oracle_scan_trap_f64", "oracle_step_trap_f64"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
