@@ -19,21 +19,21 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.c")
 
 MUTANTS = {
     "sign_of_input_term": ("h[n] = dA * h[n] + dB * xv;", "h[n] = dA * h[n] - dB * xv;"),
-    "sign_of_A": ("const double dA = exp(dv * A[d * N + n]);", "const double dA = exp(-dv * A[d * N + n]);"),
+    "sign_of_A": ("const double dA = exp(dv * A[d * N + n]);\n                    const double dB", "const double dA = exp(-dv * A[d * N + n]);\n                    const double dB"),
     "dropped_dt_in_B": ("A[d * N + n]);\n                    const double dB = dv * B[s + n];",
                         "A[d * N + n]);\n                    const double dB = B[s + n];"),
-    "B_for_C": ("acc = acc + C[s + n] * h[n];", "acc = acc + B[s + n] * h[n];"),
+    "B_for_C": ("h[n] = dA * h[n] + dB * xv;\n                    acc = acc + C[s + n] * h[n];", "h[n] = dA * h[n] + dB * xv;\n                    acc = acc + B[s + n] * h[n];"),
     "dropped_skip": ("double yv = acc + Dv[d] * xv;\n                if (z) yv = yv * silu(z[i]);\n                y[i] = yv;\n            }\n            if (h_final)\n                for (int64_t n = 0; n < N; ++n) h_final",
                      "double yv = acc;\n                if (z) yv = yv * silu(z[i]);\n                y[i] = yv;\n            }\n            if (h_final)\n                for (int64_t n = 0; n < N; ++n) h_final"),
     "gate_without_sigmoid": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
                              "static double silu(double z) { return z; }"),
-    "transposed_A_index": ("const double dA = exp(dv * A[d * N + n]);", "const double dA = exp(dv * A[n * Dn + d]);"),
+    "transposed_A_index": ("const double dA = exp(dv * A[d * N + n]);\n                    const double dB", "const double dA = exp(dv * A[n * Dn + d]);\n                    const double dB"),
     "output_from_old_state": ("h[n] = dA * h[n] + dB * xv;\n                    acc = acc + C[s + n] * h[n];",
                               "acc = acc + C[s + n] * h[n];\n                    h[n] = dA * h[n] + dB * xv;"),
-    "h0_ignored": ("h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    "h0_ignored": ("h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;\n            for (int64_t t = 0; t < L; ++t) {", "h[n] = 0.0;\n            for (int64_t t = 0; t < L; ++t) {"),
     "decode_sign": ("hs[n] = dA * hs[n] + dB * xv;", "hs[n] = dA * hs[n] - dB * xv;"),
     "complex_decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N * 2;", "const double *Ad = A + d * N * 2;"),
-    "decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N;", "const double *Ad = A + d * N;"),
+    "decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N;\n                const double xv = x[i], dv = dt[i];\n                double acc", "const double *Ad = A + d * N;\n                const double xv = x[i], dv = dt[i];\n                double acc"),
     "complex_rotation_sense": ("const double ni = (dAr * hi[n] + dAi * hr[n]) + dBi * xv;",
                                "const double ni = (dAr * hi[n] - dAi * hr[n]) + dBi * xv;"),
     "complex_conjugated_C": ("acc = acc + (C[(s + n) * 2 + 0] * hr[n] - C[(s + n) * 2 + 1] * hi[n]);",
