@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void k_bwd_summary(BwdArgs a) {
     const RowStream<IO> dts((const IO *)a.dt + row0), dys((const IO *)a.dy + row0),
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.dt + row0);
     const uint32_t te = horizon_end<IO>(dts, voff, rb, T, amax);
-    const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
+    const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     double S = 0.0;
     stream_rev<IO, GATED, 4>(dts, dys, zs, voff, rb, te, [&](uint32_t i, float dv, float dy, float zv) {
         const int64_t t = t0 + i;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void k_bwd_summary(BwdArgs a) {
         S += (double)dv;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float lt = __builtin_fmaf(dout, Uniform<IO>::ld(Cp, t * N + n), lam[n]);
+            const float lt = __builtin_fmaf(dout, Cp.ld(t * N + n), lam[n]);
             lam[n] = e2(dv * A2[n]) * lt;
         }
     });
@@ -352,8 +352,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
         dys((const IO *)a.dy + row0), zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0);
-    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
-    const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
+    const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
+    const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     const size_t sub0 = (size_t)(t0 / kSub);  // global index of the chunk's first sub-chunk
     // 1. forward walk, storing the state entering every sub-chunk but the first
     // Issue priority by remaining work (see set_priority): the walk comes first, then
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         const float u = dv * xv;
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * Uniform<IO>::ld(Bp, t * N + n));
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * Bp.ld(t * N + n));
     });
     // 2. backward walk by sub-chunks, each staged in LDS during the previous one
     __shared__ uint32_t stage_mem[4 * Stage<N>::dwords];  // blocks have at most 4 waves
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float prev = j == 0 ? start[n] : hs[j - 1][n];
-                hs[j][n] = __builtin_fmaf(e2(dv[j] * A2[n]), prev, u * Uniform<IO>::ld(Bp, t * N + n));
+                hs[j][n] = __builtin_fmaf(e2(dv[j] * A2[n]), prev, u * Bp.ld(t * N + n));
             }
         }
 #pragma unroll
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
             const int64_t t = t0 + j0 + j;
             float acc = 0.0f;
 #pragma unroll
-            for (int n = 0; n < N; ++n) acc = __builtin_fmaf(Uniform<IO>::ld(Cp, t * N + n), hs[j][n], acc);
+            for (int n = 0; n < N; ++n) acc = __builtin_fmaf(Cp.ld(t * N + n), hs[j][n], acc);
             const float o = __builtin_fmaf(Dd, xv[j], acc);
             float gp;
             const float dout = gate_grad<GATED>(yv[j], zv[j], gp);
@@ -463,8 +463,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
             float vals[V];
 #pragma unroll
             for (int n = 0; n < N; ++n) {
-                const float bn = Uniform<IO>::ld(Bp, t * N + n);
-                const float lt = __builtin_fmaf(dout, Uniform<IO>::ld(Cp, t * N + n), lam[n]);
+                const float bn = Bp.ld(t * N + n);
+                const float lt = __builtin_fmaf(dout, Cp.ld(t * N + n), lam[n]);
                 const float w = __builtin_fmaf(-u, bn, hs[j][n]);  // a_t h_{t-1}
                 const float q = lt * w;
                 vals[n] = lt * u;                // dB_t[n] term

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const uint32_t ts = horizon_start<IO>(dts, voff, rb, T, amax, [&](float v) { return in.dt(v); });
     in.history(a, ln.b, ln.d, t0 + ts);
     // 2. end state from zero over rows [ts, T) of the chunk
-    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
+    const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
     const int64_t rw = row0 + (int64_t)ts * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
         S += (double)dv;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float bn = Uniform<IO>::ld(Bp, t * N + n);
+            const float bn = Bp.ld(t * N + n);
             h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
         }
     });
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
-    const IO *Bp = (const IO *)a.B + ln.b * a.L * N;
-    const IO *Cp = (const IO *)a.C + ln.b * a.L * N;
+    const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
+    const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     In in;
     in.params(a, ln.d);
     in.history(a, ln.b, ln.d, t0);
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         float acc = 0.0f;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float bn = Uniform<IO>::ld(Bp, t * N + n);
-            const float cn = Uniform<IO>::ld(Cp, t * N + n);
+            const float bn = Bp.ld(t * N + n);
+            const float cn = Cp.ld(t * N + n);
             h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
             acc = __builtin_fmaf(cn, h[n], acc);
         }

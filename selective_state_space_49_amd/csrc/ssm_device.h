@@ -52,7 +52,8 @@ __device__ __forceinline__ void st_row(IO *row, uint32_t byte_off, float v) {
     Io<IO>::st((IO *)((char *)row + byte_off), v);
 }
 
-// Element e (wave-uniform) of a float / bf16 array through the scalar path.
+// Element e (wave-uniform) of a float / bf16 array through the scalar path. A bf16
+// value is taken out of a dword load, so a bf16 base must be 4-byte aligned.
 template <typename IO> struct Uniform;
 template <> struct Uniform<float> {
     static __device__ __forceinline__ float ld(const float *base, int64_t e) {
@@ -64,6 +65,25 @@ template <> struct Uniform<bf16_bits> {
         const uint32_t w = ((cu32 *)base)[e >> 1];
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     }
+};
+
+// Row b of a [batch][L][N] array (B or C) read through the scalar path, from the
+// array's (4-byte aligned) start p and the row's first element e0 = b L N. With bf16
+// and N odd (N = 1) a row starts at an odd element whenever b L is odd; the base is
+// then rounded down to an even element and the index carries the parity. With N even
+// or fp32 the row start is aligned and no parity is kept.
+template <typename IO, int N, bool ODD = (sizeof(IO) == 2 && (N & 1) != 0)> struct UniRow;
+template <typename IO, int N> struct UniRow<IO, N, false> {
+    const IO *base;
+    __device__ __forceinline__ UniRow(const void *p, int64_t e0) : base((const IO *)p + e0) {}
+    __device__ __forceinline__ float ld(int64_t e) const { return Uniform<IO>::ld(base, e); }
+};
+template <typename IO, int N> struct UniRow<IO, N, true> {
+    const IO *base;
+    int64_t par;
+    __device__ __forceinline__ UniRow(const void *p, int64_t e0)
+        : base((const IO *)p + (e0 & ~(int64_t)1)), par(e0 & 1) {}
+    __device__ __forceinline__ float ld(int64_t e) const { return Uniform<IO>::ld(base, e + par); }
 };
 
 // Hardware base-2 exponential (v_exp_f32) and reciprocal (v_rcp_f32).

@@ -34,6 +34,7 @@ CASES = [
     (3, 600, 70, 16, "f32", True, 102, True, True),   # chunk length rounded down to 100
     (1, 3, 16, 16, "f32", True, 0, True, True),       # shorter than one sub-chunk
     (1, 1000, 300, 16, "bf16", True, 128, True, True),  # whole padding waves in a block
+    (3, 101, 40, 1, "bf16", True, 16, True, True),      # bf16, N = 1, odd L: rows of B, C start at odd elements
 ]
 
 

@@ -31,6 +31,7 @@ CASES = [
     (2, 64, 48, 16, "bf16", True, 0, 16, True, False),     # softplus only, x as is
     (1, 2, 16, 16, "f32", True, 4, 1, True, True),         # L < K-1: the state out mixes old rows
     (3, 1000, 70, 16, "f32", True, 4, 128, True, True),
+    (3, 131, 40, 1, "bf16", True, 4, 32, True, True),     # bf16, N = 1, odd L
 ]
 
 

@@ -29,6 +29,7 @@ CASES = [
     (1, 1, 1, 1, "f32", True, True, 0),           # one step, one channel
     (1, 4501, 33, 16, "f32", True, True, 64),     # 71 chunks: two tiles of the carry scan
     (2, 777, 96, 16, "bf16", False, True, 5),     # chunks shorter than a register block
+    (3, 129, 64, 1, "bf16", True, True, 16),      # bf16, N = 1, odd L: rows of B, C start at odd elements
 ]
 
 
