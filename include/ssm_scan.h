@@ -274,8 +274,52 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
                         ssm_dtype io, int64_t chunk_len, void *workspace,
                         size_t workspace_bytes, void *hip_stream);
 
+/* ------------------------------------------------------------------ exponential-trapezoidal
+ * ssm_scan_fwd_trap: the prefill of ssm_scan_fwd_ex with the exponential-trapezoidal
+ * discretisation that Mamba-3 puts in place of Euler's ("Jamba — SSM-Transformer
+ * Híbrido", section "Mamba-3: a linha de base de SSM puro em 2026", item 1: a
+ * convolution-like operation on the state input inside the recurrence). The page gives
+ * no formula; the reading implemented is the trapezoid rule on the step's input
+ * integral:
+ *     h_t = exp(dt_t A) h_{t-1} + (dt_t / 2) (exp(dt_t A) B_{t-1} x_{t-1} + B_t x_t),
+ * y_t as in ssm_scan_fwd. x_prev [batch, d_inner] and B_prev [batch, d_state] (io
+ * dtype) are the input before step 0: NULL and NULL for a sequence with no earlier
+ * input; to resume a sequence pass the last step's x and B of the previous part (with
+ * its h_final as h0). Given together or not at all (else SSM_ERR_NULL). Other arguments,
+ * layouts, the chunking (with the same decay-horizon bound) and the workspace
+ * (ssm_scan_fwd_workspace_ex) are those of ssm_scan_fwd_ex. y must not overlap x or
+ * x_prev (SSM_ERR_UNSUPPORTED): a chunk's rescan reads the row before it. Alignment:
+ * as ssm_scan_fwd_ex; x_prev one element, B_prev 4 bytes.
+ *
+ * ssm_step_trap: one decode token of the same recurrence. x_prev [n_layers, n_seq,
+ * d_inner] and B_prev [n_layers, n_seq, d_state] are the previous token's x_t and B_t
+ * (NULL and NULL before the first token); the caller keeps them, the library keeps
+ * only h. Otherwise as ssm_step; B_prev is aligned like B_t. ssm_step_trap_replay is
+ * its one-thread-per-channel reference with the same fp32 operations in the same
+ * order: per state n, with w = 0.5 dt_t and a = exp(dt_t A[n]),
+ *     h[n] = fma(a, fma(w x_prev, B_prev[n], h[n]), (w x_t) B_t[n]),
+ * then the output as in ssm_step; the two agree bit for bit. */
+ssm_status ssm_scan_fwd_trap(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, const float *h0,
+                             const void *x_prev, const void *B_prev, void *y, float *h_final,
+                             int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                             ssm_dtype io, int64_t chunk_len, void *workspace,
+                             size_t workspace_bytes, void *hip_stream);
+ssm_status ssm_step_trap(float *h, const void *x_prev, const void *B_prev, const void *x_t,
+                         const void *dt_t, const float *A, const void *B_t, const void *C_t,
+                         const float *D, const void *z_t, void *y_t, int64_t n_layers,
+                         int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                         void *hip_stream);
+ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev,
+                                const void *x_t, const void *dt_t, const float *A,
+                                const void *B_t, const void *C_t, const float *D,
+                                const void *z_t, void *y_t, int64_t n_layers, int64_t n_seq,
+                                int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                void *hip_stream);
+
 /* ------------------------------------------------------------------ profiling
- * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64 / ssm_scan_fwd_fused,
+ * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64 / ssm_scan_fwd_fused /
+ * ssm_scan_fwd_trap,
  * which additionally records four caller-created HIP events (hipEvent_t, passed
  * as void*) on hip_stream: events[0] before the chunk-summary kernel, events[1] after it,
  * events[2] after the carry-scan kernel, events[3] after the rescan kernel. With a
@@ -308,6 +352,13 @@ ssm_status ssm_scan_fwd_fused_profiled(const void *x_in, const void *dt_raw, con
                                        void *const *events, int32_t n_events);
 
 /* ------------------------------------------------------------------ misc */
+ssm_status ssm_scan_fwd_trap_profiled(const void *x, const void *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const void *z, const float *h0, const void *x_prev,
+                                      const void *B_prev, void *y, float *h_final, int64_t batch,
+                                      int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                      int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                      void *hip_stream, void *const *events, int32_t n_events);
 const char *ssm_status_str(ssm_status s);   /* static string, never NULL */
 const char *ssm_last_error(void);           /* this thread's last detail, "" if none */
 int32_t ssm_abi_version(void);              /* 1 */

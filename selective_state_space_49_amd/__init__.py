@@ -24,6 +24,7 @@ __all__ = [
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
     "ssm_scan_bwd", "ssm_scan_bwd_workspace",
+    "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
     "ssm_scan_bwd", "ssm_scan_bwd_workspace",
+    "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
 ]
 
 
@@ -89,6 +91,11 @@ def load_library():
     sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
     sig["ssm_scan_bwd_workspace"] = ([i64, i64, i64, i32, i64], sz)
     sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    trap = [vp] * 12 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
+    sig["ssm_scan_fwd_trap"] = (trap, ci)
+    sig["ssm_scan_fwd_trap_profiled"] = (trap + [vp, i32], ci)
+    for name in ("ssm_step_trap", "ssm_step_trap_replay"):
+        sig[name] = ([vp] * 11 + [i64, i64, i64, i32, ci, vp], ci)
     step_fused = [vp] * 11 + [i32, vp, vp, i64, i64, i64, i32, ci, vp]
     for name in ("ssm_step_fused", "ssm_step_fused_replay"):
         sig[name] = (step_fused, ci)
@@ -280,6 +287,81 @@ def ssm_step_c64(h, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
 
 def ssm_step_c64_replay(h, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
     return _step("ssm_step_c64_replay", True, h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t)
+
+
+# ------------------------------------------------------------------ exponential-trapezoidal
+def ssm_scan_fwd_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None, *,
+                      chunk_len=0, y=None, h_final=None, workspace=None, want_h_final=True,
+                      events=None):
+    """Prefill with the exponential-trapezoidal discretisation (see ssm_scan.h):
+    h_t = a_t h_{t-1} + (dt_t/2)(a_t B_{t-1} x_{t-1} + B_t x_t). x_prev [b, d_inner] and
+    B_prev [b, d_state] (io dtype, both or neither) are the input before step 0.
+    events: None, or 4 raw hipEvent_t handles for the profiled entry point.
+    Returns (y, h_final)."""
+    lib = load_library()
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    _dev(x, "x"); _dev(dt, "dt", (b, L, Dn)); _dev(z, "z", (b, L, Dn))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N)); _dev(h0, "h0", (b, Dn, N), f32)
+    _dev(x_prev, "x_prev", (b, Dn)); _dev(B_prev, "B_prev", (b, N))
+    io = _io(x, dt, z, B, C, x_prev, B_prev)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", (b, L, Dn), x.dtype)
+    if h_final is None and want_h_final:
+        h_final = torch.empty((b, Dn, N), dtype=f32, device=x.device)
+    _dev(h_final, "h_final", (b, Dn, N), f32)
+    need = ssm_scan_fwd_workspace_ex(b, L, Dn, N, chunk_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev),
+            _ptr(B_prev), _ptr(y), _ptr(h_final), b, L, Dn, N, io, chunk_len, _ptr(workspace),
+            ws_bytes, _stream(x)]
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("need exactly 4 event handles")
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) for e in events])
+        st = lib.ssm_scan_fwd_trap_profiled(*args, handles, 4)
+    else:
+        st = lib.ssm_scan_fwd_trap(*args)
+    _check(st)
+    return y, h_final
+
+
+def _step_trap(fn_name, h, x_prev, B_prev, x, dt, A, B, C, D, z, y):
+    lib = load_library()
+    Ln, S, Dn = x.shape
+    N = A.shape[2]
+    f32 = torch.float32
+    _dev(h, "h", (Ln, S, Dn, N), f32)
+    _dev(x, "x_t"); _dev(dt, "dt_t", (Ln, S, Dn)); _dev(z, "z_t", (Ln, S, Dn))
+    _dev(A, "A", (Ln, Dn, N), f32); _dev(D, "D", (Ln, Dn), f32)
+    _dev(B, "B_t", (Ln, S, N)); _dev(C, "C_t", (Ln, S, N))
+    _dev(x_prev, "x_prev", (Ln, S, Dn)); _dev(B_prev, "B_prev", (Ln, S, N))
+    io = _io(x, dt, z, B, C, x_prev, B_prev)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y_t", (Ln, S, Dn), x.dtype)
+    st = getattr(lib, fn_name)(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x), _ptr(dt), _ptr(A),
+                               _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), Ln, S, Dn, N, io,
+                               _stream(x))
+    _check(st)
+    return y
+
+
+def ssm_step_trap(h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
+    """One exponential-trapezoidal decode token: h updated in place, returns y_t.
+    x_prev and B_prev are the previous token's x_t and B_t (None and None at the start)."""
+    return _step_trap("ssm_step_trap", h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t, y_t)
+
+
+def ssm_step_trap_replay(h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
+    """Reference-order replay of ssm_step_trap, one thread per channel."""
+    return _step_trap("ssm_step_trap_replay", h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t,
+                      y_t)
 
 
 # ------------------------------------------------------------------ fused input stage

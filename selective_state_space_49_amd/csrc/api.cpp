@@ -95,6 +95,12 @@ struct InputStage {
     void *conv_state;         // prefill: conv_state_out; decode: the state, in place
 };
 
+// The exponential-trapezoidal entry points: the input before the first step (prefill:
+// [batch][Dn] and [batch][N]; decode: the previous token's x and B). Both or neither.
+struct Trap {
+    const void *x_prev, *B_prev;
+};
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
     const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
@@ -115,7 +121,8 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
                        int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
                        int64_t chunk_len, void *workspace, size_t workspace_bytes,
                        void *hip_stream, bool cplx, void *const *events = nullptr,
-                       int32_t n_events = 0, const InputStage *in = nullptr) {
+                       int32_t n_events = 0, const InputStage *in = nullptr,
+                       const Trap *trap = nullptr) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     Plan plan;
     ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan);
@@ -146,6 +153,17 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         if (overlaps(in->conv_state, state_bytes, x, stream_bytes) ||
             overlaps(in->conv_state, state_bytes, in->conv_state0, state_bytes))
             return fail(SSM_ERR_UNSUPPORTED, "conv_state_out must not overlap x_in or conv_state0");
+    }
+    if (trap) {
+        if ((trap->x_prev == nullptr) != (trap->B_prev == nullptr))
+            return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
+        if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, 4))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev element, B_prev 4 B)");
+        // The rescan of chunk c reads the last row of chunk c-1 while y is written.
+        const size_t stream_bytes = (size_t)(batch * L * d_inner) * eb;
+        if (overlaps(y, stream_bytes, x, stream_bytes) ||
+            overlaps(y, stream_bytes, trap->x_prev, (size_t)(batch * d_inner) * eb))
+            return fail(SSM_ERR_UNSUPPORTED, "y must not overlap x or x_prev in the trapezoidal scan");
     }
     hipStream_t s = (hipStream_t)hip_stream;
     const int64_t state_floats = batch * d_inner * d_state * (cplx ? 2 : 1);
@@ -187,6 +205,10 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         a.conv_state_out = conv_rows ? in->conv_state : nullptr;
         a.dt_bias = in->dt_bias;
         e = ssm::launch_scan_fused(a, iot, d_state, z != nullptr, s, ev);
+    } else if (trap) {
+        a.x_prev = trap->x_prev;
+        a.B_prev = trap->B_prev;
+        e = ssm::launch_scan_trap(a, iot, d_state, z != nullptr, s, ev);
     } else {
         e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s, ev)
                  : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s, ev);
@@ -198,7 +220,7 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
                        const void *C, const float *D, const void *z, void *y, int64_t n_layers,
                        int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
                        void *hip_stream, bool cplx, bool replay,
-                       const InputStage *in = nullptr) {
+                       const InputStage *in = nullptr, const Trap *trap = nullptr) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     if (n_layers < 0 || n_seq < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "n_layers/n_seq must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
@@ -215,6 +237,12 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     if (!aligned(h, 16) || !aligned(A, 16) || !aligned(x, eb) || !aligned(dt, eb) ||
         !aligned(z, eb) || !aligned(y, eb) || !aligned(B, bc) || !aligned(C, bc) || !aligned(D, 4))
         return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; B_t, C_t min(d_state,4) elements; others element)");
+    if (trap) {
+        if ((trap->x_prev == nullptr) != (trap->B_prev == nullptr))
+            return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
+        if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, bc))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev element; B_prev as B_t)");
+    }
     ssm::StepArgs a{};
     a.h = h; a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z; a.A = A; a.D = D; a.y = y;
     a.n_layers = n_layers; a.n_seq = n_seq; a.Dn = d_inner;
@@ -232,6 +260,10 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
         a.conv_state = in->conv_k > 1 ? in->conv_state : nullptr;
         a.dt_bias = in->dt_bias;
         e = ssm::launch_step_fused(a, iot, d_state, z != nullptr, replay, s);
+    } else if (trap) {
+        a.x_prev = trap->x_prev;
+        a.B_prev = trap->B_prev;
+        e = ssm::launch_step_trap(a, iot, d_state, z != nullptr, replay, s);
     } else {
         e = cplx ? ssm::launch_step_complex(a, iot, d_state, z != nullptr, replay, s)
                  : ssm::launch_step_real(a, iot, d_state, z != nullptr, replay, s);
@@ -502,6 +534,53 @@ ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, co
     const InputStage in{conv_w, conv_b, dt_bias, conv_k, nullptr, conv_state};
     return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
                        io, hip_stream, false, true, &in);
+}
+
+ssm_status ssm_scan_fwd_trap(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, const float *h0,
+                             const void *x_prev, const void *B_prev, void *y, float *h_final,
+                             int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                             ssm_dtype io, int64_t chunk_len, void *workspace,
+                             size_t workspace_bytes, void *hip_stream) {
+    const Trap tr{x_prev, B_prev};
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0,
+                       nullptr, &tr);
+}
+
+ssm_status ssm_scan_fwd_trap_profiled(const void *x, const void *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const void *z, const float *h0, const void *x_prev,
+                                      const void *B_prev, void *y, float *h_final, int64_t batch,
+                                      int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                      int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                      void *hip_stream, void *const *events, int32_t n_events) {
+    if (!events) return fail(SSM_ERR_NULL, "events are required");
+    const Trap tr{x_prev, B_prev};
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, events, n_events,
+                       nullptr, &tr);
+}
+
+ssm_status ssm_step_trap(float *h, const void *x_prev, const void *B_prev, const void *x_t,
+                         const void *dt_t, const float *A, const void *B_t, const void *C_t,
+                         const float *D, const void *z_t, void *y_t, int64_t n_layers,
+                         int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                         void *hip_stream) {
+    const Trap tr{x_prev, B_prev};
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, false, nullptr, &tr);
+}
+
+ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev,
+                                const void *x_t, const void *dt_t, const float *A,
+                                const void *B_t, const void *C_t, const float *D,
+                                const void *z_t, void *y_t, int64_t n_layers, int64_t n_seq,
+                                int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                void *hip_stream) {
+    const Trap tr{x_prev, B_prev};
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, true, nullptr, &tr);
 }
 
 size_t ssm_scan_bwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,

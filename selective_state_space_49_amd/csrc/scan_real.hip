@@ -54,6 +54,7 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
 // ---------------------------------------------------------------- input stage
 // The kernels read x and dt as given.
 struct NoInput {
+    static constexpr bool kTrap = false;
     __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
     __device__ __forceinline__ void history(const ScanArgs &, int64_t, int64_t, int64_t) {}
     __device__ __forceinline__ float x(float v) { return v; }
@@ -65,6 +66,7 @@ struct NoInput {
 // is) and dt = softplus(dt + dt_bias).
 template <typename IO, int KC>
 struct MambaInput {
+    static constexpr bool kTrap = false;
     ConvSilu<(KC > 0 ? KC : 1)> conv;
     float dbias;
 
@@ -105,6 +107,46 @@ struct MambaInput {
                 for (int j = 0; j < KC - 1; ++j)
                     Io<IO>::st((IO *)a.conv_state_out + (b * (KC - 1) + j) * a.Dn + d, conv.hist[j]);
             }
+        }
+    }
+};
+
+// The exponential-trapezoidal discretisation (the Mamba-3 item of "Jamba —
+// SSM-Transformer Híbrido", section "Mamba-3: a linha de base de SSM puro em 2026",
+// which names the rule but gives no formula): the step's input integral is taken by
+// the trapezoid rule over its two ends,
+//     h_t = a_t h_{t-1} + (dt_t / 2) (a_t B_{t-1} x_{t-1} + B_t x_t),
+// evaluated as a_t (h_{t-1} + (dt_t/2) x_{t-1} B_{t-1}) + (dt_t/2) x_t B_t. The
+// recurrence stays linear in h with a known input term, so chunk summaries, the carry
+// and the rescan are unchanged apart from that term; each walk starts with the input
+// before its first row (the row before, or x_prev / B_prev before step 0). x and dt are
+// read as given.
+template <typename IO>
+struct TrapInput {
+    static constexpr bool kTrap = true;
+    float xprev;  // x of the step before the current one
+    __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
+    __device__ __forceinline__ void history(const ScanArgs &a, int64_t b, int64_t d, int64_t t) {
+        if (t > 0) xprev = Io<IO>::ld((const IO *)a.x + (b * a.L + t - 1) * a.Dn + d);
+        else xprev = a.x_prev ? Io<IO>::ld((const IO *)a.x_prev + b * a.Dn + d) : 0.0f;
+    }
+    __device__ __forceinline__ float x(float v) { return v; }
+    __device__ __forceinline__ float dt(float v) const { return v; }
+    __device__ __forceinline__ void store_state(const ScanArgs &, int64_t, int64_t) const {}
+    // B of the step before step t (wave-uniform t).
+    template <int N, typename Row>
+    __device__ __forceinline__ void prev_row(const ScanArgs &a, const Row &Bp, int64_t b, int64_t t,
+                                             float (&bp)[N]) const {
+        if (t > 0) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) bp[n] = Bp.ld((t - 1) * N + n);
+        } else if (a.B_prev) {
+            const UniRow<IO, N> P(a.B_prev, b * N);
+#pragma unroll
+            for (int n = 0; n < N; ++n) bp[n] = P.ld(n);
+        } else {
+#pragma unroll
+            for (int n = 0; n < N; ++n) bp[n] = 0.0f;
         }
     }
 };
@@ -211,12 +253,25 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     stream_steps<IO, false, 4>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + ts + i;
-        const float u = dv * xv;
         S += (double)dv;
+        if constexpr (In::kTrap) {
+            const float w = 0.5f * dv;
+            const float up = w * in.xprev, uc = w * xv;
+            float bp[N];
+            in.template prev_row<N>(a, Bp, ln.b, t, bp);
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float bn = Bp.ld(t * N + n);
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+            for (int n = 0; n < N; ++n) {
+                const float bn = Bp.ld(t * N + n);
+                h[n] = __builtin_fmaf(e2(dv * A2[n]), __builtin_fmaf(up, bp[n], h[n]), uc * bn);
+            }
+            in.xprev = xv;
+        } else {
+            const float u = dv * xv;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float bn = Bp.ld(t * N + n);
+                h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+            }
         }
     });
     const float Sf = (float)S;
@@ -259,14 +314,29 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     stream_steps<IO, GATED, 4>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
-        const float u = dv * xv;
         float acc = 0.0f;
+        if constexpr (In::kTrap) {
+            const float w = 0.5f * dv;
+            const float up = w * in.xprev, uc = w * xv;
+            float bp[N];
+            in.template prev_row<N>(a, Bp, ln.b, t, bp);
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float bn = Bp.ld(t * N + n);
-            const float cn = Cp.ld(t * N + n);
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
-            acc = __builtin_fmaf(cn, h[n], acc);
+            for (int n = 0; n < N; ++n) {
+                const float bn = Bp.ld(t * N + n);
+                const float cn = Cp.ld(t * N + n);
+                h[n] = __builtin_fmaf(e2(dv * A2[n]), __builtin_fmaf(up, bp[n], h[n]), uc * bn);
+                acc = __builtin_fmaf(cn, h[n], acc);
+            }
+            in.xprev = xv;
+        } else {
+            const float u = dv * xv;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float bn = Bp.ld(t * N + n);
+                const float cn = Cp.ld(t * N + n);
+                h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * bn);
+                acc = __builtin_fmaf(cn, h[n], acc);
+            }
         }
         float yv = __builtin_fmaf(Dd, xv, acc);
         if (GATED) yv = yv * silu(zv);
@@ -348,6 +418,12 @@ hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, 
                             hipEvent_t const *ev) {
     return io == 0 ? launch_io<float, NoInput>(a, d_state, gated, s, ev)
                    : launch_io<bf16_bits, NoInput>(a, d_state, gated, s, ev);
+}
+
+hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev) {
+    return io == 0 ? launch_io<float, TrapInput<float>>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits, TrapInput<bf16_bits>>(a, d_state, gated, s, ev);
 }
 
 hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,

@@ -29,6 +29,9 @@ struct ScanArgs {
     void *conv_state_out;     // [batch][conv_k-1][Dn] of io, or null
     const float *dt_bias;     // [Dn], or null
     int32_t conv_k;           // 0 (no convolution) or 1..4
+    // Exponential-trapezoidal entry point only: the input before step 0.
+    const void *x_prev;       // [batch][Dn] of io, or null (then B_prev is null too)
+    const void *B_prev;       // [batch][N] of io, or null
 };
 
 struct StepArgs {
@@ -43,6 +46,9 @@ struct StepArgs {
     void *conv_state;     // [n_layers][n_seq][conv_k-1][Dn] of io, read and written
     const float *dt_bias; // [n_layers][Dn], or null
     int32_t conv_k;       // 0 or 1..4
+    // Exponential-trapezoidal entry point only: the previous token's x and B.
+    const void *x_prev;   // [n_layers][n_seq][Dn] of io, or null (then B_prev is null too)
+    const void *B_prev;   // [n_layers][n_seq][N] of io, or null
 };
 
 // Real diagonal state. io: 0 = f32, 1 = bf16. Returns hipSuccess or the launch error.
@@ -50,6 +56,9 @@ struct StepArgs {
 // carry kernel and after the rescan kernel (phases that do not run leave two
 // consecutive records).
 hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev);
+// The same with the exponential-trapezoidal discretisation (x_prev, B_prev of a).
+hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev);
 hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                                hipEvent_t const *ev);
@@ -72,6 +81,9 @@ hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gate
                                hipStream_t s);
 hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                              hipStream_t s);
+// Exponential-trapezoidal decode (x_prev, B_prev of a).
+hipError_t launch_step_trap(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                            hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // One backward call, already validated and planned. The forward phases use a ScanArgs

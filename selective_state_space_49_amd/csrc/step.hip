@@ -54,6 +54,7 @@ __device__ __forceinline__ bool chan_of(const StepArgs &a, Chan &c, int &g) {
 // values the recurrence uses; store() writes what the next token needs. store() is
 // called after the channel's output, so its stores wait on nothing.
 struct NoStepInput {
+    static constexpr bool kTrap = false;
     template <typename Chan>
     __device__ __forceinline__ void apply(const StepArgs &, const Chan &, float &, float &) {}
     __device__ __forceinline__ void store(const StepArgs &) const {}
@@ -64,6 +65,7 @@ struct NoStepInput {
 // x included, in place of the old state.
 template <typename IO, int KC>
 struct StepMamba {
+    static constexpr bool kTrap = false;
     ConvSilu<(KC > 0 ? KC : 1)> conv;
     IO *st;  // the channel's conv state: row j at st + j * Dn
 
@@ -89,6 +91,22 @@ struct StepMamba {
             for (int j = 0; j < KC - 1; ++j) Io<IO>::st(st + j * a.Dn, conv.hist[j]);
         }
     }
+};
+
+// The exponential-trapezoidal step (see scan_real.hip): x and dt as given, plus the
+// previous token's x (x_prev, per channel) and B (B_prev, per sequence); null x_prev
+// and B_prev (the entry point accepts both or neither) mean no previous input. The
+// update of state n is
+//     h = a (h + w x_prev B_prev[n]) + w x B[n],   w = dt / 2, a = exp(dt A[n]).
+template <typename IO>
+struct StepTrap {
+    static constexpr bool kTrap = true;
+    float xprev;
+    template <typename Chan>
+    __device__ __forceinline__ void apply(const StepArgs &a, const Chan &c, float &, float &) {
+        xprev = a.x_prev ? Io<IO>::ld((const IO *)a.x_prev + c.ch) : 0.0f;
+    }
+    __device__ __forceinline__ void store(const StepArgs &) const {}
 };
 
 // The state is read once and written once per call: non-temporal (streaming) 16-byte
@@ -204,6 +222,15 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     }
     VecLd<IO, K>::ld((const IO *)a.B + hc.lq * N + g * K, bv);
     VecLd<IO, K>::ld((const IO *)a.C + hc.lq * N + g * K, cv);
+    float pv[K];  // exponential-trapezoidal step: the previous token's B
+    if constexpr (In::kTrap) {
+        if (a.B_prev) {
+            VecLd<IO, K>::ld((const IO *)a.B_prev + hc.lq * N + g * K, pv);
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) pv[k] = 0.0f;
+        }
+    }
     float xv = Io<IO>::ld((const IO *)a.x + hc.ch);
     float dv = Io<IO>::ld((const IO *)a.dt + hc.ch);
     const float zv = GATED ? Io<IO>::ld((const IO *)a.z + hc.ch) : 0.0f;
@@ -217,13 +244,25 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
         const int src = r * CPR + lane / G;
         const float xr = G == 1 ? xv : __shfl(xv, src, 64);
         const float dr = G == 1 ? dv : __shfl(dv, src, 64);
-        const float u = dr * xr;
         float p = 0.0f;
+        if constexpr (In::kTrap) {
+            const float xpr = G == 1 ? in.xprev : __shfl(in.xprev, src, 64);
+            const float w = 0.5f * dr;
+            const float up = w * xpr, uc = w * xr;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float a2 = av[r][k] * kLog2e;
-            hv[r][k] = __builtin_fmaf(e2(dr * a2), hv[r][k], u * bv[k]);
-            p = __builtin_fmaf(cv[k], hv[r][k], p);
+            for (int k = 0; k < K; ++k) {
+                const float a2 = av[r][k] * kLog2e;
+                hv[r][k] = __builtin_fmaf(e2(dr * a2), __builtin_fmaf(up, pv[k], hv[r][k]), uc * bv[k]);
+                p = __builtin_fmaf(cv[k], hv[r][k], p);
+            }
+        } else {
+            const float u = dr * xr;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float a2 = av[r][k] * kLog2e;
+                hv[r][k] = __builtin_fmaf(e2(dr * a2), hv[r][k], u * bv[k]);
+                p = __builtin_fmaf(cv[k], hv[r][k], p);
+            }
         }
         const float s = group_sum<G>(p);
         if (rok[r]) {
@@ -266,15 +305,31 @@ __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     float dv = Io<IO>::ld((const IO *)a.dt + ch);
     In in;
     in.apply(a, c, xv, dv);
-    const float u = dv * xv;
     float p[G];
-    for (int g = 0; g < G; ++g) {
-        p[g] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int n = g * K + k;
-            const float a2 = Ap[n] * kLog2e;
-            hp[n] = __builtin_fmaf(e2(dv * a2), hp[n], u * Io<IO>::ld(Bp + n));
-            p[g] = __builtin_fmaf(Io<IO>::ld(Cp + n), hp[n], p[g]);
+    if constexpr (In::kTrap) {
+        const IO *Pp = a.B_prev ? (const IO *)a.B_prev + c.lq * N : nullptr;
+        const float w = 0.5f * dv;
+        const float up = w * in.xprev, uc = w * xv;
+        for (int g = 0; g < G; ++g) {
+            p[g] = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                const int n = g * K + k;
+                const float a2 = Ap[n] * kLog2e;
+                const float pb = Pp ? Io<IO>::ld(Pp + n) : 0.0f;
+                hp[n] = __builtin_fmaf(e2(dv * a2), __builtin_fmaf(up, pb, hp[n]), uc * Io<IO>::ld(Bp + n));
+                p[g] = __builtin_fmaf(Io<IO>::ld(Cp + n), hp[n], p[g]);
+            }
+        }
+    } else {
+        const float u = dv * xv;
+        for (int g = 0; g < G; ++g) {
+            p[g] = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                const int n = g * K + k;
+                const float a2 = Ap[n] * kLog2e;
+                hp[n] = __builtin_fmaf(e2(dv * a2), hp[n], u * Io<IO>::ld(Bp + n));
+                p[g] = __builtin_fmaf(Io<IO>::ld(Cp + n), hp[n], p[g]);
+            }
         }
     }
     float yv = __builtin_fmaf(a.D[c.l * a.Dn + c.d], xv, tree_sum<G>(p));
@@ -459,6 +514,12 @@ hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gate
                                hipStream_t s) {
     return io == 0 ? launch_io<float, true>(a, d_state, gated, replay, s)
                    : launch_io<bf16_bits, true>(a, d_state, gated, replay, s);
+}
+
+hipError_t launch_step_trap(const StepArgs &a, int io, int d_state, bool gated, bool replay,
+                            hipStream_t s) {
+    return io == 0 ? launch_fused_n<float, StepTrap<float>>(a, d_state, gated, replay, s)
+                   : launch_fused_n<bf16_bits, StepTrap<bf16_bits>>(a, d_state, gated, replay, s);
 }
 
 hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated, bool replay,

@@ -186,3 +186,28 @@ def test_backward_argument_errors(lib):
     assert _bwd_raw(lib, batch=4, Dn=1 << 23, N=16, L=8) == UNSUP
     assert "2 GiB" in ssm.ssm_last_error()
     assert ssm.ssm_scan_bwd_workspace(4, 8, 1 << 23, 16, 0) == 0
+
+
+def test_trapezoid_argument_errors(lib):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def scan(xp=0x3000, Bp=0x3100, x=0x100000, y=0x200000, N=4, io=0, L=8, **kw):
+        return lib.ssm_scan_fwd_trap(p(x), p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                     None, None, p(xp), p(Bp), p(y), None, 1, L, 4, N, io, 0, None, 0,
+                                     None)
+    assert scan(xp=None) == NULL              # x_prev and B_prev come together
+    assert scan(Bp=None) == NULL
+    assert scan(Bp=0x3102) == ALIGN
+    assert scan(io=1, xp=0x3001) == ALIGN
+    assert scan(N=3) == UNSUP
+    assert scan(y=0x100010) == UNSUP          # y over x: the rescan reads the row before a chunk
+    assert "overlap" in ssm.ssm_last_error()
+    assert scan(y=0x3000 - 8) == UNSUP        # y over x_prev
+
+    def step(fn, xp=0x3000, Bp=0x3100, N=16, io=1):
+        return getattr(lib, fn)(p(0x1000), p(xp), p(Bp), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                p(0x1000), p(0x1000), None, p(0x1000), 2, 3, 4, N, io, None)
+    for fn in ("ssm_step_trap", "ssm_step_trap_replay"):
+        assert step(fn, xp=None) == NULL
+        assert step(fn, Bp=0x3104) == ALIGN   # aligned like B_t: 4 bf16 states per lane
+        assert step(fn, N=5) == UNSUP

@@ -207,7 +207,7 @@ def test_state_size_does_not_depend_on_length():
 @pytest.mark.parametrize("variant", ["slow_decay", "frozen_states", "fast_decay", "dt_zero_block"])
 def test_decay_horizon_edge_cases(variant):
     # The chunk summaries walk back only to the point where every state of a wave has
-    # decayed below 2^-160; these inputs make that point come early, late or never.
+    # decayed below 2^-48; these inputs make that point come early, late or never.
     shape = ScanShape("h", 1, 3000, 130, 16, "f32", seed=61)
     inp = make_scan_inputs(shape, "cpu")
     if variant == "slow_decay":

@@ -179,6 +179,16 @@ def make_scan_inputs(shape: ScanShape, device="cpu", seed: Optional[int] = None)
     return {"x": x, "dt": dt, "z": z, "A": A, "B": B, "C": C, "D": D}
 
 
+def make_prev_input(batch: int, d_inner: int, d_state: int, io: str = "f32", device="cpu",
+                    seed: int = 29) -> dict:
+    """The input before step 0 of an exponential-trapezoidal prefill: x_prev [batch,
+    d_inner] and B_prev [batch, d_state], ~ N(0, 1) like x and B, in the I/O dtype."""
+    g = _gen(seed, device)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    return {"x_prev": _normal((batch, d_inner), 0.0, 1.0, g, device, dt),
+            "B_prev": _normal((batch, d_state), 0.0, 1.0, g, device, dt)}
+
+
 def make_h0(batch: int, d_inner: int, d_state: int, complex_state=False, device="cpu",
             seed: int = 7) -> torch.Tensor:
     """A non-zero initial state ~ N(0, 1), float32 [batch, d_inner, d_state(, 2)]."""
