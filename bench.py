@@ -97,6 +97,13 @@ def prefill_lane_ops(s) -> float:
     return s.d_state * per_state + per_elem
 
 
+def trap_lane_ops(N: int) -> float:
+    """Extra VALU instructions per element of the exponential-trapezoidal update: per
+    state one more fused multiply-add (the previous input term), per element w = dt/2,
+    w x_prev and w x in place of dt x (two more)."""
+    return N + 2
+
+
 def input_stage_bytes(s, io_bytes: int, K: int) -> float:
     """Extra bytes of the fused input stage: filter, biases, carried conv state in/out
     (the raw x and dt replace x and dt one for one)."""
@@ -196,11 +203,14 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     return info, d
 
 
-def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None):
-    """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter."""
+def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None, trap=False):
+    """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter.
+    trap: ssm_scan_fwd_trap (exponential-trapezoidal), with an input before step 0."""
     dev = "cuda"
     log("drawing inputs for", shape.name)
     d = workloads.make_scan_inputs(shape, dev)
+    if trap:
+        d.update(workloads.make_prev_input(shape.batch, shape.d_inner, shape.d_state, shape.io, dev))
     fused = conv_k is not None
     if fused:
         d.update(workloads.make_input_stage(shape, conv_k, dev))
@@ -231,6 +241,10 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
                                    conv_state0=d["conv_state0"], dt_bias=d["dt_bias"], y=y,
                                    h_final=hf, conv_state_out=so, workspace=ws, chunk_len=T,
                                    events=[e.cuda_event for e in events])
+        elif trap:
+            ssm.ssm_scan_fwd_trap(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
+                                  d["x_prev"], d["B_prev"], y=y, h_final=hf, workspace=ws,
+                                  chunk_len=T, events=[e.cuda_event for e in events])
         else:
             fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None, y=y, h_final=hf,
                workspace=ws, chunk_len=T, events=[e.cuda_event for e in events])
@@ -259,6 +273,9 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     if fused:
         nbytes += input_stage_bytes(shape, io_bytes, conv_k)
         lane_ops += input_stage_lane_ops(conv_k)
+    if trap:
+        nbytes += shape.batch * (shape.d_inner + shape.d_state) * io_bytes   # x_prev, B_prev
+        lane_ops += trap_lane_ops(shape.d_state)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": phases,
         "elements_per_step": elems, "bytes_per_step": nbytes,
@@ -270,8 +287,9 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     return info, d
 
 
-def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None):
-    """conv_k None: ssm_step; else ssm_step_fused with a conv_k-tap filter."""
+def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None, trap=False):
+    """conv_k None: ssm_step; else ssm_step_fused with a conv_k-tap filter. trap:
+    ssm_step_trap, given the previous token's x and B."""
     dev = "cuda"
     Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
     par = workloads.make_decode_params(shape, dev)
@@ -303,6 +321,10 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
                 ssm.ssm_step_fused(h_l[l], p["conv_state"], t["x"], t["dt"], A_l[l], t["B"], t["C"],
                                    D_l[l], t["z"], conv_w=p["conv_w"], conv_b=p["conv_b"],
                                    dt_bias=p["dt_bias"], y_t=y[l:l + 1])
+            elif trap:
+                pv = per_layer[(k - 1) * Ln + l] if k > 0 else {"x": None, "B": None}
+                ssm.ssm_step_trap(h_l[l], pv["x"], pv["B"], t["x"], t["dt"], A_l[l], t["B"], t["C"],
+                                  D_l[l], t["z"], y_t=y[l:l + 1])
             else:
                 ssm.ssm_step(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
                              y_t=y[l:l + 1])
@@ -352,6 +374,9 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
         K = conv_k
         nbytes += Ln * S * Dn * 2 * max(K - 1, 0) * io_bytes + Ln * Dn * (K + (1 if K else 0) + 1) * 4
         lane_ops += input_stage_lane_ops(K)
+    if trap:
+        nbytes += Ln * S * (Dn + N) * io_bytes   # the previous token's x and B
+        lane_ops += trap_lane_ops(N)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3,
         "elements_per_step": Ln * S * Dn, "bytes_per_step": nbytes,
@@ -385,7 +410,7 @@ def sample_width(shape, elems):
     return max(1, min(shape.d_inner, -(-elems // (shape.batch * max(shape.L, 1)))))
 
 
-def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None):
+def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False):
     import oracle
     oracle.build(force=False)
     k = sample_width(shape, CPU_SAMPLE_ELEMS // (4 if shape.complex_state else 1))
@@ -403,13 +428,31 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None):
                               g(d["conv_state0"]))[0] if conv_k else args[0])
         dts = oracle.softplus(g(d["dt_raw"]), sel(d["dt_bias"]))
         args = (u, dts) + args[2:]
-    oracle.scan_threaded(*args, threads=threads, complex_state=shape.complex_state)
+    if trap:
+        import threading
+        import numpy as np
+        xp = oracle.to_f64(d["x_prev"].index_select(1, idx).cpu())
+        Bq = oracle.to_f64(d["B_prev"].cpu())
+        f = [oracle.to_f64(a) for a in args]
+        parts = [p for p in np.array_split(np.arange(k), threads) if len(p)]
+
+        def work(p):
+            sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, p])
+            oracle.scan_trap(sub(f[0]), sub(f[1]), f[2][p], f[3], f[4], f[5][p], sub(f[6]),
+                             x_prev=np.ascontiguousarray(xp[:, p]), B_prev=Bq)
+        t0 = time.perf_counter()
+        ts = [threading.Thread(target=work, args=(p,)) for p in parts]
+        for t in ts: t.start()
+        for t in ts: t.join()
+    else:
+        oracle.scan_threaded(*args, threads=threads, complex_state=shape.complex_state)
     dt = time.perf_counter() - t0
     elems = shape.batch * shape.L * k
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{k} of {shape.d_inner} channels over all {shape.L} steps x batch "
                       f"{shape.batch} ({elems} elements, {dt:.1f} s wall), fp64 sequential loop "
-                      f"per channel, channels split over {threads} threads"}
+                      f"per channel{' (exponential-trapezoidal)' if trap else ''}, channels split "
+                      f"over {threads} threads"}
 
 
 def cpu_baseline_backward(shape, d, torch, workloads, threads):
@@ -447,7 +490,7 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
                       f"{len(parts)} threads"}
 
 
-def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=192):
+def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=192, trap=False):
     """The oracle's decode step (or, with conv_k, its fused step) for every layer on the
     first `seqs` sequences, `tokens` tokens in a row with the state carried, the layers
     split over host threads. Inputs are drawn once; the timed region is the oracle."""
@@ -486,6 +529,9 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
                 _, hh, cc = oracle.step_fused(hh, cc, x[r], dt[r], A[r], B[r], C[r], D[r], z if z is None else z[r],
                                               conv_w=cw[r], conv_b=None if cb is None else cb[r],
                                               dt_bias=None if db is None else db[r])
+            elif trap:  # the same token's x and B stand in for the previous token's
+                _, hh = oracle.step_trap(hh, x[r], B[r], x[r], dt[r], A[r], B[r], C[r], D[r],
+                                         None if z is None else z[r])
             else:
                 _, hh = oracle.step(hh, x[r], dt[r], A[r], B[r], C[r], D[r], None if z is None else z[r])
 
@@ -495,7 +541,8 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
     for t in ts: t.join()
     dtm = time.perf_counter() - t0
     elems = Ln * S * Dn * tokens
-    what = "fused decode step (conv + silu, softplus, scan)" if fused else "decode step"
+    what = ("fused decode step (conv + silu, softplus, scan)" if fused else
+            "exponential-trapezoidal decode step" if trap else "decode step")
     return {"value": elems / dtm, "unit": "elements/s", "cores": len(groups), "kind": "oracle",
             "sample": f"{what}: all {Ln} layers x {S} of {shape.n_seq} sequences x {Dn} channels, "
                       f"{tokens} tokens (token 0's inputs each time) with the state carried ({elems} "
@@ -520,6 +567,8 @@ def main():
                     help="through ssm_scan_fwd_fused / ssm_step_fused (conv + silu and softplus "
                          "fused into the load stage)")
     ap.add_argument("--conv-k", type=int, default=4, help="filter taps with --fused (0..4)")
+    ap.add_argument("--trap", action="store_true",
+                    help="the exponential-trapezoidal entry points (ssm_scan_fwd_trap, ssm_step_trap)")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (gradients of the prefill) on the prefill workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -551,9 +600,13 @@ def main():
     shape = workloads.WORKLOADS[args.workload]
     is_decode = isinstance(shape, workloads.DecodeShape)
     steps = max(1, args.steps if not is_decode else min(args.steps, 64))
+    if args.trap and (args.fused or args.backward or shape.complex_state):
+        print("--trap applies to the real-state prefill and decode workloads, without --fused "
+              "or --backward", file=sys.stderr)
+        sys.exit(2)
     if is_decode:
         info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph,
-                             conv_k=args.conv_k if args.fused else None)
+                             conv_k=args.conv_k if args.fused else None, trap=args.trap)
     else:
         if args.backward and (shape.complex_state or args.fused):
             print("--backward applies to the real-state prefill workloads", file=sys.stderr)
@@ -566,7 +619,7 @@ def main():
             info, d = run_backward(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
         else:
             info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
-                                  conv_k)
+                                  conv_k, trap=args.trap)
 
     elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
     dom_s = info["dominant_ms"] / 1e3
@@ -574,7 +627,7 @@ def main():
     alu_ach = info["elements_per_step"] * info["lane_ops_per_elem"] / dom_s / 1e12
     hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
     traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "") + \
-        ("+backward" if args.backward else "")
+        ("+backward" if args.backward else "") + ("+trap" if args.trap else "")
     traffic = traffic_for(info, traffic_key)
     if hbm_frac >= alu_frac:
         roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
@@ -597,6 +650,8 @@ def main():
         if args.fused:
             cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
                                   "softplus_dt": True, "entry_point": "ssm_step_fused"}
+        if args.trap:
+            cfg["discretisation"] = "exponential-trapezoidal (ssm_step_trap)"
     else:
         cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
@@ -607,6 +662,8 @@ def main():
                                   "softplus_dt": True, "entry_point": "ssm_scan_fwd_fused"}
         if args.backward:
             cfg["pass"] = "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)"
+        if args.trap:
+            cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
     out = {
         "metric": METRIC, "value": round(elems_s, 1), "unit": "elements/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(info["ms_per_step"], 4),
@@ -619,14 +676,14 @@ def main():
     if not args.no_cpu_baseline and is_decode and not shape.complex_state:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline_decode(shape, workloads, threads,
-                                                  args.conv_k if args.fused else None)
+                                                  args.conv_k if args.fused else None, trap=args.trap)
     elif not args.no_cpu_baseline and not is_decode:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         if args.backward:
             out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads)
         else:
             out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
-                                               args.conv_k if args.fused else None)
+                                               args.conv_k if args.fused else None, trap=args.trap)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

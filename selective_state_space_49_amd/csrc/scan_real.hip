@@ -133,7 +133,7 @@ struct TrapInput {
     __device__ __forceinline__ float x(float v) { return v; }
     __device__ __forceinline__ float dt(float v) const { return v; }
     __device__ __forceinline__ void store_state(const ScanArgs &, int64_t, int64_t) const {}
-    // B of the step before step t (wave-uniform t).
+    // B of the step before step t (wave-uniform t): the start of a walk.
     template <int N, typename Row>
     __device__ __forceinline__ void prev_row(const ScanArgs &a, const Row &Bp, int64_t b, int64_t t,
                                              float (&bp)[N]) const {
@@ -250,6 +250,8 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     const int64_t rw = row0 + (int64_t)ts * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
+    float bp[N];     // trapezoidal rule: B of the step before, carried from step to step
+    if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0 + ts, bp);
     stream_steps<IO, false, 4>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + ts + i;
@@ -257,12 +259,11 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
         if constexpr (In::kTrap) {
             const float w = 0.5f * dv;
             const float up = w * in.xprev, uc = w * xv;
-            float bp[N];
-            in.template prev_row<N>(a, Bp, ln.b, t, bp);
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float bn = Bp.ld(t * N + n);
                 h[n] = __builtin_fmaf(e2(dv * A2[n]), __builtin_fmaf(up, bp[n], h[n]), uc * bn);
+                bp[n] = bn;
             }
             in.xprev = xv;
         } else {
@@ -311,6 +312,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
     In in;
     in.params(a, ln.d);
     in.history(a, ln.b, ln.d, t0);
+    float bp[N];  // trapezoidal rule: B of the step before, carried from step to step
+    if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0, bp);
     stream_steps<IO, GATED, 4>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
@@ -318,14 +321,13 @@ __global__ __launch_bounds__(256) void k_chunk_scan(ScanArgs a) {
         if constexpr (In::kTrap) {
             const float w = 0.5f * dv;
             const float up = w * in.xprev, uc = w * xv;
-            float bp[N];
-            in.template prev_row<N>(a, Bp, ln.b, t, bp);
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float bn = Bp.ld(t * N + n);
                 const float cn = Cp.ld(t * N + n);
                 h[n] = __builtin_fmaf(e2(dv * A2[n]), __builtin_fmaf(up, bp[n], h[n]), uc * bn);
                 acc = __builtin_fmaf(cn, h[n], acc);
+                bp[n] = bn;
             }
             in.xprev = xv;
         } else {
