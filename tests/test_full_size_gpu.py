@@ -5,6 +5,7 @@ Channels are independent, so the oracle run on a subset of channels over the ful
 sequence is exact for those channels. Inputs are drawn on the GPU with a seeded
 generator; the sampled channels are copied to the host for the oracle.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -78,3 +79,76 @@ def test_full_size_batched_decode_512_steps():
         assert rel_err(y[lic, sic, dic].cpu(), yr.reshape(-1)) <= TOL["bf16"], f"step {k}"
     torch.cuda.synchronize()
     assert rel_err(h[lic, sic, dic].cpu(), h_ref.reshape(4096, N)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", ["fused", "trap"])
+def test_full_size_decode_fused_and_trapezoidal(variant):
+    # The batched-decode workload (28 layers x 256 sequences x 8192 channels, bf16) through
+    # ssm_step_fused (conv K = 4 + silu, softplus) or ssm_step_trap (the previous token's
+    # x and B), one call per layer as the benchmark makes them, for 8 tokens: bit for bit
+    # against the replay kernel at every token, and 1024 sampled (layer, sequence,
+    # channel) triples against the oracle.
+    from workloads import make_decode_dt_raw, make_decode_input_stage
+    shape = WORKLOADS["batched_decode"]
+    Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
+    par = make_decode_params(shape, "cuda")
+    h = torch.zeros((Ln, S, Dn, N), device="cuda")
+    h_rep = torch.zeros_like(h)
+    K = 4
+    if variant == "fused":
+        ist = make_decode_input_stage(shape, K, "cuda")
+        cs, cs_rep = ist["conv_state"].clone(), ist["conv_state"].clone()
+    g = torch.Generator().manual_seed(23)
+    flat = torch.randperm(Ln * S * Dn, generator=g)[:1024]
+    li, si, di = flat // (S * Dn), (flat // Dn) % S, flat % Dn
+    lic, sic, dic = li.cuda(), si.cuda(), di.cuda()
+    M = len(flat)
+    A_s = par["A"][lic, dic].cpu().view(M, 1, N)
+    D_s = par["D"][lic, dic].cpu().view(M, 1)
+    h_ref = np.zeros((M, 1, 1, N))
+    if variant == "fused":
+        w_s = ist["conv_w"][lic, dic].cpu().view(M, 1, K)
+        b_s = ist["conv_b"][lic, dic].cpu().view(M, 1)
+        db_s = ist["dt_bias"][lic, dic].cpu().view(M, 1)
+        cs_ref = oracle.to_f64(ist["conv_state"][lic, sic, :, dic].cpu()).reshape(M, 1, K - 1, 1)
+    prev = None
+    sm = lambda v: v[lic, sic, dic].cpu().view(M, 1, 1)
+    for k in range(8):
+        inp = make_decode_step(shape, k, "cuda")
+        say("decode full size", variant, "token", k)
+        y = torch.empty_like(inp["x"]); y_rep = torch.empty_like(inp["x"])
+        if variant == "fused":
+            dtr = make_decode_dt_raw(shape, k, "cuda")
+        for l in range(Ln):
+            r = slice(l, l + 1)
+            if variant == "fused":
+                kw = dict(conv_w=ist["conv_w"][r], conv_b=ist["conv_b"][r], dt_bias=ist["dt_bias"][r])
+                ssm.ssm_step_fused(h[r], cs[r], inp["x"][r], dtr[r], par["A"][r], inp["B"][r], inp["C"][r],
+                                   par["D"][r], inp["z"][r], y_t=y[r], **kw)
+                ssm.ssm_step_fused_replay(h_rep[r], cs_rep[r], inp["x"][r], dtr[r], par["A"][r], inp["B"][r],
+                                          inp["C"][r], par["D"][r], inp["z"][r], y_t=y_rep[r], **kw)
+            else:
+                xp = None if prev is None else prev["x"][r]
+                Bp = None if prev is None else prev["B"][r]
+                ssm.ssm_step_trap(h[r], xp, Bp, inp["x"][r], inp["dt"][r], par["A"][r], inp["B"][r],
+                                  inp["C"][r], par["D"][r], inp["z"][r], y_t=y[r])
+                ssm.ssm_step_trap_replay(h_rep[r], xp, Bp, inp["x"][r], inp["dt"][r], par["A"][r],
+                                         inp["B"][r], inp["C"][r], par["D"][r], inp["z"][r], y_t=y_rep[r])
+        torch.cuda.synchronize()
+        assert bitwise_equal(y, y_rep), f"y differs from replay at token {k}"
+        assert bitwise_equal(h, h_rep), f"state differs from replay at token {k}"
+        Bs = inp["B"][lic, sic].cpu().view(M, 1, N)
+        Cs = inp["C"][lic, sic].cpu().view(M, 1, N)
+        if variant == "fused":
+            yr, h_ref, cs_ref = oracle.step_fused(h_ref, cs_ref, sm(inp["x"]), sm(dtr), A_s, Bs, Cs, D_s,
+                                                  sm(inp["z"]), conv_w=w_s, conv_b=b_s, dt_bias=db_s)
+        else:
+            xps = None if prev is None else sm(prev["x"])
+            Bps = None if prev is None else prev["B"][lic, sic].cpu().view(M, 1, N)
+            yr, h_ref = oracle.step_trap(h_ref, xps, Bps, sm(inp["x"]), sm(inp["dt"]), A_s, Bs, Cs, D_s,
+                                         sm(inp["z"]))
+        assert rel_err(y[lic, sic, dic].cpu(), yr.reshape(-1)) <= TOL["bf16"], f"token {k}"
+        prev = inp
+    assert rel_err(h[lic, sic, dic].cpu(), h_ref.reshape(M, N)) <= TOL["bf16"]
+    if variant == "fused":
+        assert bitwise_equal(cs, cs_rep)
