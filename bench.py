@@ -577,7 +577,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path is built and measured on a single "
-              f"MI355X (asked for --gpus {args.gpus}); sharding is described in DESIGN.md.",
+              f"MI355X (asked for --gpus {args.gpus}). Across GPUs the channels would shard with no "
+              f"exchange, or the sequence with one exchange of chunk summaries; neither is implemented.",
               file=sys.stderr)
         sys.exit(2)
     import torch
