@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests need a visible device; they are selected with -m gpu on a GPU machine.
+    # GPU tests need a visible device; they are selected with -m gpu on a machine with one.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
