@@ -69,6 +69,10 @@ def _load():
         lib.oracle_scan_trap_f64.restype = ctypes.c_int
         lib.oracle_step_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 11
         lib.oracle_step_trap_f64.restype = ctypes.c_int
+        lib.oracle_scan_mimo_f64.argtypes = [i64] * 5 + [dp] * 10
+        lib.oracle_scan_mimo_f64.restype = ctypes.c_int
+        lib.oracle_step_mimo_f64.argtypes = [i64] * 5 + [dp] * 9
+        lib.oracle_step_mimo_f64.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -322,4 +326,42 @@ def step_trap(h, x_prev, B_prev, x, dt, A, B, C, D, z=None):
                                       _p(A), _p(B), _p(C), _p(D), _p(z), _p(y))
     if rc != 0:
         raise RuntimeError("oracle_step_trap_f64 failed")
+    return y, h
+
+
+def scan_mimo(x, dt, A, B, C, D, z=None, h0=None):
+    """Real-state prefill with MIMO projections of rank R. x, z: [b, L, Dn, R];
+    dt: [b, L, Dn]; B, C: [b, L, N, R]; A: [Dn, N]; D: [Dn]; h0: [b, Dn, N] or None.
+    Returns (y [b, L, Dn, R], h_final [b, Dn, N])."""
+    x, dt, A, B, C, D, z, h0 = map(to_f64, (x, dt, A, B, C, D, z, h0))
+    b, L, Dn, R = x.shape
+    N = A.shape[1]
+    _check(dt, (b, L, Dn), "dt"); _check(B, (b, L, N, R), "B"); _check(C, (b, L, N, R), "C")
+    _check(A, (Dn, N), "A"); _check(D, (Dn,), "D")
+    if z is not None: _check(z, (b, L, Dn, R), "z")
+    if h0 is not None: _check(h0, (b, Dn, N), "h0")
+    y = np.empty((b, L, Dn, R)); hf = np.empty((b, Dn, N))
+    rc = _load().oracle_scan_mimo_f64(b, L, Dn, N, R, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                                      _p(z), _p(h0), _p(y), _p(hf))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_mimo_f64 failed")
+    return y, hf
+
+
+def step_mimo(h, x, dt, A, B, C, D, z=None):
+    """One MIMO decode token. h: [Ln, S, Dn, N]; x, z: [Ln, S, Dn, R]; dt: [Ln, S, Dn];
+    B, C: [Ln, S, N, R]; A: [Ln, Dn, N]; D: [Ln, Dn]. Returns (y [Ln, S, Dn, R], h_new)
+    without touching h."""
+    h = to_f64(h).copy()
+    x, dt, A, B, C, D, z = map(to_f64, (x, dt, A, B, C, D, z))
+    Ln, S, Dn, R = x.shape
+    N = h.shape[-1]
+    _check(h, (Ln, S, Dn, N), "h"); _check(B, (Ln, S, N, R), "B"); _check(C, (Ln, S, N, R), "C")
+    _check(A, (Ln, Dn, N), "A"); _check(D, (Ln, Dn), "D"); _check(dt, (Ln, S, Dn), "dt")
+    if z is not None: _check(z, (Ln, S, Dn, R), "z")
+    y = np.empty((Ln, S, Dn, R))
+    rc = _load().oracle_step_mimo_f64(Ln, S, Dn, N, R, _p(h), _p(x), _p(dt), _p(A), _p(B), _p(C),
+                                      _p(D), _p(z), _p(y))
+    if rc != 0:
+        raise RuntimeError("oracle_step_mimo_f64 failed")
     return y, h

@@ -477,3 +477,109 @@ int oracle_step_trap_f64(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N,
     }
     return 0;
 }
+
+/*
+ * Multi-input multi-output (MIMO) projections, real diagonal state.
+ *
+ * "Jamba — SSM-Transformer Híbrido", section "Mamba-3: a linha de base de SSM puro
+ * em 2026", item 3 (and the glossary entry "MIMO" of the zh and hi lesson pages):
+ * Mamba-3 replaces the scalar per-feature projections with matrix-valued ones, for
+ * more modelling power and better use of the hardware at inference without a longer
+ * decode. The pages give no formula. The reading taken here: a channel's input and
+ * output become R-vectors instead of scalars, and B_t, C_t become N x R matrices
+ * (the projections into and out of the N-wide state), so
+ *
+ *     h_t[n] = exp(dt_t A[n]) h_{t-1}[n] + dt_t sum_r B_t[n][r] x_t[r]
+ *     y_t[r] = (sum_n C_t[n][r] h_t[n] + D x_t[r]) * silu(z_t[r])
+ *
+ * The state per channel keeps its size N, so the decode step moves the same state
+ * bytes while doing R times the multiply-adds. R = 1 is the scan above, term for
+ * term: the order of operations below reduces to it.
+ *     dA = exp(dt * A[d][n]);  u = sum over r ascending of ((dt * B[n][r]) * x[r]);
+ *     h[n] = (dA * h[n]) + u;  acc[r] = acc[r] + C[n][r] * h[n]   (n ascending)
+ *     y[r] = acc[r] + D[d] * x[r];  if gated: y[r] = y[r] * silu(z[r])
+ * Layouts: x, z, y [batch][L][Dn][R]; dt [batch][L][Dn]; B, C [batch][L][N][R];
+ * A [Dn][N]; Dv [Dn]; h0, h_final [batch][Dn][N].
+ */
+int oracle_scan_mimo_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N, int64_t R,
+                         const double *x, const double *dt, const double *A,
+                         const double *B, const double *C, const double *Dv,
+                         const double *z, const double *h0,
+                         double *y, double *h_final)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || N <= 0 || R <= 0) return -1;
+    double *h = (double *)malloc((size_t)(N + R) * sizeof(double));
+    if (!h) return -1;
+    double *acc = h + N;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < Dn; ++d) {
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t i = (b * L + t) * Dn + d;        /* (b, t, d) of dt */
+                const double *xv = x + i * R;                 /* (b, t, d, 0) */
+                const double *Bt = B + (b * L + t) * N * R;   /* (b, t, 0, 0) */
+                const double *Ct = C + (b * L + t) * N * R;
+                const double dv = dt[i];
+                for (int64_t r = 0; r < R; ++r) acc[r] = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double dA = exp(dv * A[d * N + n]);
+                    double u = 0.0;
+                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[n * R + r]) * xv[r];
+                    h[n] = dA * h[n] + u;
+                    for (int64_t r = 0; r < R; ++r) acc[r] = acc[r] + Ct[n * R + r] * h[n];
+                }
+                for (int64_t r = 0; r < R; ++r) {
+                    double yv = acc[r] + Dv[d] * xv[r];
+                    if (z) yv = yv * silu(z[i * R + r]);
+                    y[i * R + r] = yv;
+                }
+            }
+            if (h_final)
+                for (int64_t n = 0; n < N; ++n) h_final[(b * Dn + d) * N + n] = h[n];
+        }
+    }
+    free(h);
+    return 0;
+}
+
+/* One MIMO decode token for every (layer, sequence, channel); h updated in place.
+ * h [n_layers][n_seq][Dn][N]; x, z, y [n_layers][n_seq][Dn][R]; dt [n_layers][n_seq][Dn];
+ * B, C [n_layers][n_seq][N][R]; A [n_layers][Dn][N]; Dv [n_layers][Dn]. */
+int oracle_step_mimo_f64(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N, int64_t R,
+                         double *h, const double *x, const double *dt, const double *A,
+                         const double *B, const double *C, const double *Dv,
+                         const double *z, double *y)
+{
+    if (n_layers < 0 || n_seq < 0 || Dn < 0 || N <= 0 || R <= 0) return -1;
+    double *acc = (double *)malloc((size_t)R * sizeof(double));
+    if (!acc) return -1;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        for (int64_t q = 0; q < n_seq; ++q) {
+            const double *Bt = B + (l * n_seq + q) * N * R;
+            const double *Ct = C + (l * n_seq + q) * N * R;
+            for (int64_t d = 0; d < Dn; ++d) {
+                const int64_t i = (l * n_seq + q) * Dn + d;
+                double *hs = h + i * N;
+                const double *Ad = A + (l * Dn + d) * N;
+                const double *xv = x + i * R;
+                const double dv = dt[i];
+                for (int64_t r = 0; r < R; ++r) acc[r] = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double dA = exp(dv * Ad[n]);
+                    double u = 0.0;
+                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[n * R + r]) * xv[r];
+                    hs[n] = dA * hs[n] + u;
+                    for (int64_t r = 0; r < R; ++r) acc[r] = acc[r] + Ct[n * R + r] * hs[n];
+                }
+                for (int64_t r = 0; r < R; ++r) {
+                    double yv = acc[r] + Dv[l * Dn + d] * xv[r];
+                    if (z) yv = yv * silu(z[i * R + r]);
+                    y[i * R + r] = yv;
+                }
+            }
+        }
+    }
+    free(acc);
+    return 0;
+}

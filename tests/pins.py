@@ -33,6 +33,12 @@ pages or plain mathematics fix:
                 the closed-form solution of the continuous ODE the error falls about
                 4x per halved step (second order), where Euler's halves; split/resume
                 with the previous input passed on, and L decode steps, bit for bit.
+  MIMO          the reading of Mamba-3's matrix-valued projections (B_t, C_t of size
+                N x R, R inputs and outputs per channel): rank 1 is the scan above
+                bit for bit; with no skip, gate or initial state each output is the
+                sum over inputs of rank-1 scans (superposition, since the state is
+                linear in the input); the explicit convolution with exp of summed dt;
+                split/resume and L decode steps bit for bit.
   input stage   the MambaBlock's causal depthwise convolution against numpy's
                 np.convolve (a true convolution, so the taps go in reversed) and an
                 impulse response; the carried conv state against the plain
@@ -604,6 +610,105 @@ def pin_trap_step_equals_scan(O):
         assert _bitwise(ys[l], yl) and _bitwise(hs[l], hl), f"trapezoid decode vs prefill, layer {l}"
 
 
+# ----------------------------------------------------------------------------- MIMO
+
+def tiny_mimo(seed, b=2, L=20, Dn=3, N=4, R=3, gated=True, with_h0=True):
+    r = np.random.default_rng(seed)
+    inp = tiny_real(seed, b=b, L=L, Dn=Dn, N=N, gated=False, with_h0=with_h0)
+    inp["x"] = r.normal(0, 1, (b, L, Dn, R))
+    inp["B"] = r.normal(0, 1, (b, L, N, R))
+    inp["C"] = r.normal(0, 1, (b, L, N, R))
+    inp["z"] = r.normal(0, 1, (b, L, Dn, R)) if gated else None
+    return inp
+
+
+def brute_mimo(x, dt, A, B, C, D, z=None, h0=None):
+    """The MIMO state written out with S_t the running sum of dt:
+        h_t = exp(A S_t) h0 + sum_{s<=t} exp(A (S_t - S_s)) dt_s B_s x_s   (B_s: N x R),
+        y_t = C_t^T h_t + D x_t, then the gate per output."""
+    b, L, Dn, R = x.shape
+    N = A.shape[1]
+    S = np.cumsum(dt, axis=1)
+    y = np.zeros((b, L, Dn, R)); hf = np.zeros((b, Dn, N))
+    for bi in range(b):
+        for d in range(Dn):
+            for t in range(L):
+                h = np.zeros(N) if h0 is None else np.exp(A[d] * S[bi, t, d]) * h0[bi, d]
+                for s_ in range(t + 1):
+                    h = h + np.exp(A[d] * (S[bi, t, d] - S[bi, s_, d])) * dt[bi, s_, d] * (B[bi, s_] @ x[bi, s_, d])
+                yv = C[bi, t].T @ h + D[d] * x[bi, t, d]
+                if z is not None:
+                    yv = yv * silu(z[bi, t, d])
+                y[bi, t, d] = yv
+                if t == L - 1:
+                    hf[bi, d] = h
+    return y, hf
+
+
+def pin_mimo_rank_one_is_siso(O):
+    inp = tiny_mimo(81, R=1)
+    y, hf = O.scan_mimo(**inp)
+    ys, hs = O.scan(inp["x"][..., 0], inp["dt"], inp["A"], inp["B"][..., 0], inp["C"][..., 0],
+                    inp["D"], inp["z"][..., 0], inp["h0"])
+    assert _bitwise(y[..., 0], ys) and _bitwise(hf, hs), "MIMO rank 1 vs the scan"
+
+
+def pin_mimo_superposition(O, tol=1e-12):
+    # No skip, gate or initial state: the state is linear in the input, so output r is
+    # the sum over inputs r' of the scan that reads only input r' (through column r' of
+    # B) and reads out through column r of C.
+    inp = tiny_mimo(82, R=3, gated=False, with_h0=False)
+    x, dt, A, B, C = inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"]
+    b, L, Dn, R = x.shape
+    zero = np.zeros(Dn)
+    y, hf = O.scan_mimo(x, dt, A, B, C, zero)
+    for r in range(R):
+        acc = np.zeros((b, L, Dn)); hacc = np.zeros(hf.shape)
+        for rp in range(R):
+            ys, hs = O.scan(x[..., rp], dt, A, B[..., rp], C[..., r], zero)
+            acc += ys; hacc += hs
+        assert _rel(y[..., r], acc) <= tol, f"MIMO superposition, output {r}"
+        assert _rel(hf, hacc) <= tol, "MIMO superposition, final state"
+
+
+def pin_mimo_brute_force(O, tol=1e-12):
+    for seed, R, gated in [(83, 4, True), (84, 2, False)]:
+        inp = tiny_mimo(seed, L=14, R=R, gated=gated)
+        y, hf = O.scan_mimo(**inp)
+        yb, hb = brute_mimo(**inp)
+        assert _rel(y, yb) <= tol and _rel(hf, hb) <= tol, f"MIMO vs brute force (R={R})"
+
+
+def pin_mimo_split_resume(O):
+    inp = tiny_mimo(85, L=27, R=4)
+    y, hf = O.scan_mimo(**inp)
+    k = 11
+    part = lambda v, sl: None if v is None else v[:, sl]
+    args = lambda sl: (part(inp["x"], sl), part(inp["dt"], sl), inp["A"], part(inp["B"], sl),
+                       part(inp["C"], sl), inp["D"], part(inp["z"], sl))
+    y1, h1 = O.scan_mimo(*args(slice(0, k)), inp["h0"])
+    y2, h2 = O.scan_mimo(*args(slice(k, None)), h1)
+    assert _bitwise(np.concatenate([y1, y2], axis=1), y) and _bitwise(h2, hf), "MIMO split/resume"
+
+
+def pin_mimo_step_equals_scan(O):
+    r = np.random.default_rng(86)
+    Ln, S, Dn, N, R, L = 2, 3, 3, 4, 4, 7
+    x = r.normal(0, 1, (Ln, S, L, Dn, R)); z = r.normal(0, 1, (Ln, S, L, Dn, R))
+    dt = np.log1p(np.exp(r.normal(-1, 0.5, (Ln, S, L, Dn))))
+    B = r.normal(0, 1, (Ln, S, L, N, R)); C = r.normal(0, 1, (Ln, S, L, N, R))
+    A = -np.exp(r.normal(0, 0.5, (Ln, Dn, N))); D = r.normal(1, 0.1, (Ln, Dn))
+    h = r.normal(0, 1, (Ln, S, Dn, N))
+    hs, ys = h, []
+    for t in range(L):
+        yt, hs = O.step_mimo(hs, x[:, :, t], dt[:, :, t], A, B[:, :, t], C[:, :, t], D, z[:, :, t])
+        ys.append(yt)
+    ys = np.stack(ys, axis=2)
+    for l in range(Ln):
+        yl, hl = O.scan_mimo(x[l], dt[l], A[l], B[l], C[l], D[l], z[l], h[l])
+        assert _bitwise(ys[l], yl) and _bitwise(hs[l], hl), f"MIMO decode vs prefill, layer {l}"
+
+
 ALL_PINS = [
     pin_brute_force, pin_convolution, pin_geometric_series, pin_dt_zero, pin_linearity,
     pin_split_resume, pin_step_equals_scan, pin_isolation, pin_state_bytes,
@@ -616,4 +721,6 @@ ALL_PINS = [
     pin_fused_identity_filter, pin_fused_step_equals_scan, pin_backward_finite_differences,
     pin_trap_brute_force, pin_trap_a_zero_is_trapezoid_rule, pin_trap_second_order,
     pin_trap_split_resume, pin_trap_step_equals_scan,
+    pin_mimo_rank_one_is_siso, pin_mimo_superposition, pin_mimo_brute_force,
+    pin_mimo_split_resume, pin_mimo_step_equals_scan,
 ]

@@ -30,7 +30,8 @@ MUTANTS = {
     "transposed_A_index": ("const double dA = exp(dv * A[d * N + n]);\n                    const double dB", "const double dA = exp(dv * A[n * Dn + d]);\n                    const double dB"),
     "output_from_old_state": ("h[n] = dA * h[n] + dB * xv;\n                    acc = acc + C[s + n] * h[n];",
                               "acc = acc + C[s + n] * h[n];\n                    h[n] = dA * h[n] + dB * xv;"),
-    "h0_ignored": ("h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;\n            for (int64_t t = 0; t < L; ++t) {", "h[n] = 0.0;\n            for (int64_t t = 0; t < L; ++t) {"),
+    "h0_ignored": ("h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;\n            for (int64_t t = 0; t < L; ++t) {\n                const int64_t i = (b * L + t) * Dn + d;   /* (b, t, d) */",
+                   "h[n] = 0.0;\n            for (int64_t t = 0; t < L; ++t) {\n                const int64_t i = (b * L + t) * Dn + d;   /* (b, t, d) */"),
     "decode_sign": ("hs[n] = dA * hs[n] + dB * xv;", "hs[n] = dA * hs[n] - dB * xv;"),
     "complex_decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N * 2;", "const double *Ad = A + d * N * 2;"),
     "decode_A_layer_index": ("const double *Ad = A + (l * Dn + d) * N;\n                const double xv = x[i], dv = dt[i];\n                double acc", "const double *Ad = A + d * N;\n                const double xv = x[i], dv = dt[i];\n                double acc"),
@@ -79,6 +80,25 @@ MUTANTS = {
                                       "const double prev = has_prev ? B[s + n] * x_prev[i] : 0.0;"),
     "trap_decode_prev_not_decayed": ("hs[n] = dA * hs[n] + w * (dA * prev + B[s + n] * xv);",
                                      "hs[n] = dA * hs[n] + w * (prev + B[s + n] * xv);"),
+    "mimo_B_transposed": ("const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[n * R + r]) * xv[r];",
+                          "const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[r * N + n]) * xv[r];"),
+    "mimo_dt_dropped_from_input": ("const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[n * R + r]) * xv[r];",
+                                   "const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + Bt[n * R + r] * xv[r];"),
+    "mimo_C_transposed": ("acc[r] = acc[r] + Ct[n * R + r] * h[n];", "acc[r] = acc[r] + Ct[r * N + n] * h[n];"),
+    "mimo_skip_reads_first_input": ("double yv = acc[r] + Dv[d] * xv[r];", "double yv = acc[r] + Dv[d] * xv[0];"),
+    "mimo_gate_reads_first_input": ("double yv = acc[r] + Dv[d] * xv[r];\n                    if (z) yv = yv * silu(z[i * R + r]);",
+                                    "double yv = acc[r] + Dv[d] * xv[r];\n                    if (z) yv = yv * silu(z[i * R]);"),
+    "mimo_x_row_stride": ("const double *xv = x + i * R;                 /* (b, t, d, 0) */",
+                          "const double *xv = x + i;                 /* (b, t, d, 0) */"),
+    "mimo_B_row_stride": ("const double *Bt = B + (b * L + t) * N * R;   /* (b, t, 0, 0) */",
+                          "const double *Bt = B + (b * L + t) * N;   /* (b, t, 0, 0) */"),
+    "mimo_h0_ignored": ("h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;\n            for (int64_t t = 0; t < L; ++t) {\n                const int64_t i = (b * L + t) * Dn + d;        /* (b, t, d) of dt */",
+                        "h[n] = 0.0;\n            for (int64_t t = 0; t < L; ++t) {\n                const int64_t i = (b * L + t) * Dn + d;        /* (b, t, d) of dt */"),
+    "mimo_outputs_accumulate_across_steps": ("for (int64_t r = 0; r < R; ++r) acc[r] = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+                                             "for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "mimo_decode_B_layer_dropped": ("const double *Bt = B + (l * n_seq + q) * N * R;", "const double *Bt = B + q * N * R;"),
+    "mimo_decode_output_from_old_state": ("hs[n] = dA * hs[n] + u;\n                    for (int64_t r = 0; r < R; ++r) acc[r] = acc[r] + Ct[n * R + r] * hs[n];",
+                                          "for (int64_t r = 0; r < R; ++r) acc[r] = acc[r] + Ct[n * R + r] * hs[n];\n                    hs[n] = dA * hs[n] + u;"),
 }
 
 
@@ -105,7 +125,8 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     lib = ctypes.CDLL(str(so))
     for fname in ("oracle_scan_f64", "oracle_scan_c128", "oracle_step_f64", "oracle_step_c128",
                   "oracle_state_bytes", "oracle_conv_silu_f64", "oracle_softplus_f64",
-                  "oracle_scan_bwd_f64", "oracle_scan_trap_f64", "oracle_step_trap_f64"):
+                  "oracle_scan_bwd_f64", "oracle_scan_trap_f64", "oracle_step_trap_f64",
+                  "oracle_scan_mimo_f64", "oracle_step_mimo_f64"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
