@@ -317,10 +317,51 @@ ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev
                                 int64_t d_inner, int32_t d_state, ssm_dtype io,
                                 void *hip_stream);
 
+/* ------------------------------------------------------------------ MIMO projections
+ * ssm_scan_fwd_mimo: the prefill with multi-input multi-output projections, the third
+ * Mamba-3 item of "Jamba — SSM-Transformer Híbrido", section "Mamba-3: a linha de base
+ * de SSM puro em 2026" (matrix-valued projections in place of scalar per-feature ones,
+ * for more modelling power and better hardware use at inference without a longer
+ * decode). The page gives no formula; the reading implemented: each channel takes
+ * `rank` inputs and gives `rank` outputs, and B_t, C_t are d_state x rank matrices,
+ *     h_t[n] = exp(dt_t A[n]) h_{t-1}[n] + dt_t sum_r B_t[n][r] x_t[r]
+ *     y_t[r] = (sum_n C_t[n][r] h_t[n] + D x_t[r]) * silu(z_t[r])
+ * The state is d_state per channel as in ssm_scan_fwd; rank = 1 is ssm_scan_fwd_ex.
+ *   x, z, y : [batch, L, d_inner, rank] of io (rank fastest); dt: [batch, L, d_inner]
+ *   B, C    : [batch, L, d_state, rank] of io;  A, D, h0, h_final as ssm_scan_fwd
+ * rank is 1, 2, 4 or 8 (else SSM_ERR_UNSUPPORTED). x, z and y are aligned to
+ * min(16, rank * element size) bytes; other alignments, the chunking (with the same
+ * decay-horizon bound, which does not depend on rank) and the errors are those of
+ * ssm_scan_fwd_ex. The workspace comes from ssm_scan_fwd_mimo_workspace (0 for an
+ * invalid shape or rank). y may be x itself but must not overlap it otherwise.
+ *
+ * ssm_step_mimo: one decode token of the same recurrence for every (layer, sequence,
+ * channel), h updated in place.
+ *   h          : [n_layers, n_seq, d_inner, d_state] float32
+ *   x_t, z_t, y_t : [n_layers, n_seq, d_inner, rank] of io;  dt_t: [n_layers, n_seq, d_inner]
+ *   B_t, C_t   : [n_layers, n_seq, d_state, rank] of io (4-byte aligned)
+ *   A, D       : as ssm_step
+ * Per channel the fp32 operations are, in this order (the same as the prefill's, so
+ * L steps equal a one-chunk prefill, chunk_len = L, bit for bit):
+ *   xd[r] = dt x[r];  for n ascending: u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u)
+ *   for r = 1 .. rank-1; h[n] = fma(e2(dt (A[n] log2 e)), h[n], u);
+ *   acc[r] = fma(C[n][r], h[n], acc[r]) (acc from 0);  y[r] = fma(D, x[r], acc[r]),
+ *   gated y[r] * (z[r] * rcp(1 + e2(-z[r] log2 e))). */
+size_t ssm_scan_fwd_mimo_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                   int32_t rank, int64_t chunk_len);
+ssm_status ssm_scan_fwd_mimo(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, const float *h0,
+                             void *y, float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                             int32_t d_state, int32_t rank, ssm_dtype io, int64_t chunk_len,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+ssm_status ssm_step_mimo(float *h, const void *x_t, const void *dt_t, const float *A,
+                         const void *B_t, const void *C_t, const float *D, const void *z_t,
+                         void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                         int32_t d_state, int32_t rank, ssm_dtype io, void *hip_stream);
+
 /* ------------------------------------------------------------------ profiling
  * The same computation as ssm_scan_fwd_ex / ssm_scan_fwd_c64 / ssm_scan_fwd_fused /
- * ssm_scan_fwd_trap,
- * which additionally records four caller-created HIP events (hipEvent_t, passed
+ * ssm_scan_fwd_trap / ssm_scan_fwd_mimo, which additionally records four caller-created HIP events (hipEvent_t, passed
  * as void*) on hip_stream: events[0] before the chunk-summary kernel, events[1] after it,
  * events[2] after the carry-scan kernel, events[3] after the rescan kernel. With a
  * single chunk the first two phases launch nothing and their events are recorded
@@ -351,7 +392,6 @@ ssm_status ssm_scan_fwd_fused_profiled(const void *x_in, const void *dt_raw, con
                                        void *workspace, size_t workspace_bytes, void *hip_stream,
                                        void *const *events, int32_t n_events);
 
-/* ------------------------------------------------------------------ misc */
 ssm_status ssm_scan_fwd_trap_profiled(const void *x, const void *dt, const float *A,
                                       const void *B, const void *C, const float *D,
                                       const void *z, const float *h0, const void *x_prev,
@@ -359,6 +399,15 @@ ssm_status ssm_scan_fwd_trap_profiled(const void *x, const void *dt, const float
                                       int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
                                       int64_t chunk_len, void *workspace, size_t workspace_bytes,
                                       void *hip_stream, void *const *events, int32_t n_events);
+ssm_status ssm_scan_fwd_mimo_profiled(const void *x, const void *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const void *z, const float *h0, void *y, float *h_final,
+                                      int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                      int32_t rank, ssm_dtype io, int64_t chunk_len,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream,
+                                      void *const *events, int32_t n_events);
+
+/* ------------------------------------------------------------------ misc */
 const char *ssm_status_str(ssm_status s);   /* static string, never NULL */
 const char *ssm_last_error(void);           /* this thread's last detail, "" if none */
 int32_t ssm_abi_version(void);              /* 1 */

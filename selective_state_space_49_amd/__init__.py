@@ -25,6 +25,8 @@ __all__ = [
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
     "ssm_scan_bwd", "ssm_scan_bwd_workspace",
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
+    "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
+    "ssm_step_mimo",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +44,8 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
     "ssm_scan_bwd", "ssm_scan_bwd_workspace",
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
+    "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
+    "ssm_step_mimo",
 ]
 
 
@@ -96,6 +100,11 @@ def load_library():
     sig["ssm_scan_fwd_trap_profiled"] = (trap + [vp, i32], ci)
     for name in ("ssm_step_trap", "ssm_step_trap_replay"):
         sig[name] = ([vp] * 11 + [i64, i64, i64, i32, ci, vp], ci)
+    sig["ssm_scan_fwd_mimo_workspace"] = ([i64, i64, i64, i32, i32, i64], sz)
+    mimo = [vp] * 10 + [i64, i64, i64, i32, i32, ci, i64, vp, sz, vp]
+    sig["ssm_scan_fwd_mimo"] = (mimo, ci)
+    sig["ssm_scan_fwd_mimo_profiled"] = (mimo + [vp, i32], ci)
+    sig["ssm_step_mimo"] = ([vp] * 9 + [i64, i64, i64, i32, i32, ci, vp], ci)
     step_fused = [vp] * 11 + [i32, vp, vp, i64, i64, i64, i32, ci, vp]
     for name in ("ssm_step_fused", "ssm_step_fused_replay"):
         sig[name] = (step_fused, ci)
@@ -516,3 +525,65 @@ def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk
                           _ptr(workspace), ws_bytes, _stream(x))
     _check(st)
     return out
+
+
+# ------------------------------------------------------------------ MIMO projections
+def ssm_scan_fwd_mimo_workspace(batch, L, d_inner, d_state, rank, chunk_len=0) -> int:
+    return int(load_library().ssm_scan_fwd_mimo_workspace(batch, L, d_inner, d_state, rank,
+                                                          chunk_len))
+
+
+def ssm_scan_fwd_mimo(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, h_final=None,
+                      workspace=None, want_h_final=True, events=None):
+    """Prefill with MIMO projections (see ssm_scan.h): x, z [b, L, d_inner, R]; dt
+    [b, L, d_inner]; B, C [b, L, d_state, R]. Returns (y [b, L, d_inner, R], h_final)."""
+    lib = load_library()
+    b, L, Dn, R = x.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    _dev(x, "x"); _dev(dt, "dt", (b, L, Dn)); _dev(z, "z", (b, L, Dn, R))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N, R)); _dev(C, "C", (b, L, N, R)); _dev(h0, "h0", (b, Dn, N), f32)
+    io = _io(x, dt, z, B, C)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", (b, L, Dn, R), x.dtype)
+    if h_final is None and want_h_final:
+        h_final = torch.empty((b, Dn, N), dtype=f32, device=x.device)
+    _dev(h_final, "h_final", (b, Dn, N), f32)
+    need = ssm_scan_fwd_mimo_workspace(b, L, Dn, N, R, chunk_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+            _ptr(h_final), b, L, Dn, N, R, io, chunk_len, _ptr(workspace), ws_bytes, _stream(x)]
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("need exactly 4 event handles")
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) for e in events])
+        st = lib.ssm_scan_fwd_mimo_profiled(*args, handles, 4)
+    else:
+        st = lib.ssm_scan_fwd_mimo(*args)
+    _check(st)
+    return y, h_final
+
+
+def ssm_step_mimo(h, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
+    """One MIMO decode token: h [Ln, S, d_inner, N] updated in place; x_t, z_t
+    [Ln, S, d_inner, R]; dt_t [Ln, S, d_inner]; B_t, C_t [Ln, S, N, R]. Returns y_t."""
+    lib = load_library()
+    Ln, S, Dn, R = x_t.shape
+    N = A.shape[2]
+    f32 = torch.float32
+    _dev(h, "h", (Ln, S, Dn, N), f32)
+    _dev(x_t, "x_t"); _dev(dt_t, "dt_t", (Ln, S, Dn)); _dev(z_t, "z_t", (Ln, S, Dn, R))
+    _dev(A, "A", (Ln, Dn, N), f32); _dev(D, "D", (Ln, Dn), f32)
+    _dev(B_t, "B_t", (Ln, S, N, R)); _dev(C_t, "C_t", (Ln, S, N, R))
+    io = _io(x_t, dt_t, z_t, B_t, C_t)
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    _dev(y_t, "y_t", (Ln, S, Dn, R), x_t.dtype)
+    st = lib.ssm_step_mimo(_ptr(h), _ptr(x_t), _ptr(dt_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D),
+                           _ptr(z_t), _ptr(y_t), Ln, S, Dn, N, R, io, _stream(x_t))
+    _check(st)
+    return y_t

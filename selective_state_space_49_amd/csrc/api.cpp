@@ -34,6 +34,8 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool valid_state(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
 
+bool valid_rank(int32_t r) { return r == 1 || r == 2 || r == 4 || r == 8; }
+
 size_t io_bytes(ssm_dtype io) { return io == SSM_BF16 ? 2 : 4; }
 
 // Waves wanted per launch for the chunk rescan: about four per SIMD on 256 CUs.
@@ -58,7 +60,7 @@ struct Plan {
 };
 
 ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, int64_t chunk_len,
-                     bool cplx, Plan *p) {
+                     bool cplx, Plan *p, int32_t rank = 1) {
     if (batch < 0 || L < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "batch/L must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
     if (chunk_len < 0) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be >= 0");
@@ -68,7 +70,8 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
         return fail(SSM_ERR_SHAPE, "problem too large");
     // A chunk spans less than 2 GiB of every [rows][d_inner] stream (4-byte elements
     // at most), so the kernels address a chunk with 32-bit byte offsets.
-    const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 31) / (d_inner * 4) - 1);
+    // (MIMO rows of x, z and y hold rank elements per channel.)
+    const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 31) / (d_inner * rank * 4) - 1);
     int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
                               : auto_chunk_len(batch, L, d_inner);
     T = std::min(T, cap);
@@ -122,10 +125,12 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
                        int64_t chunk_len, void *workspace, size_t workspace_bytes,
                        void *hip_stream, bool cplx, void *const *events = nullptr,
                        int32_t n_events = 0, const InputStage *in = nullptr,
-                       const Trap *trap = nullptr) {
+                       const Trap *trap = nullptr, int32_t rank = 0) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
+    const bool mimo = rank != 0;
+    if (mimo && !valid_rank(rank)) return fail(SSM_ERR_UNSUPPORTED, "rank %d not in {1,2,4,8}", rank);
     Plan plan;
-    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan);
+    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan, mimo ? rank : 1);
     if (st != SSM_OK) return st;
     const bool work = batch > 0 && L > 0;
     if (work && (!x || !dt || !A || !B || !C || !D || !y))
@@ -135,6 +140,14 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         !aligned(B, 4) || !aligned(C, 4) || !aligned(A, 16) || !aligned(D, 4) ||
         !aligned(h0, 16) || !aligned(h_final, 16))
         return fail(SSM_ERR_ALIGN, "pointer alignment (A, h0, h_final 16 B; B, C, D 4 B; x, dt, z, y element)");
+    if (mimo) {
+        // x, z and y are read and written R elements (up to 16 bytes) at a time.
+        const size_t va = std::min<size_t>(16, (size_t)rank * eb);
+        if (!aligned(x, va) || !aligned(z, va) || !aligned(y, va))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x, z, y: min(16, rank * element) bytes)");
+        if ((double)batch * L * d_inner * rank > 4.0e18)
+            return fail(SSM_ERR_SHAPE, "problem too large");
+    }
     if (events && n_events != 4) return fail(SSM_ERR_NULL, "profiling needs exactly 4 events");
     if (events)
         for (int i = 0; i < 4; ++i)
@@ -192,6 +205,7 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     a.sumH = plan.ws_bytes ? (float *)((char *)workspace + plan.ws_bytes / 2) : nullptr;
     a.batch = batch; a.L = L; a.Dn = d_inner;
     a.T = plan.T; a.n_chunks = plan.n_chunks;
+    a.rank = mimo ? rank : 1;
     a.threads = (int32_t)std::min<int64_t>(256, (d_inner + 63) / 64 * 64);
     a.dblocks = (int32_t)((d_inner + a.threads - 1) / a.threads);
     const int iot = io == SSM_BF16 ? 1 : 0;
@@ -209,6 +223,8 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         a.x_prev = trap->x_prev;
         a.B_prev = trap->B_prev;
         e = ssm::launch_scan_trap(a, iot, d_state, z != nullptr, s, ev);
+    } else if (mimo) {
+        e = ssm::launch_scan_mimo(a, iot, d_state, z != nullptr, s, ev);
     } else {
         e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s, ev)
                  : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s, ev);
@@ -220,10 +236,13 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
                        const void *C, const float *D, const void *z, void *y, int64_t n_layers,
                        int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
                        void *hip_stream, bool cplx, bool replay,
-                       const InputStage *in = nullptr, const Trap *trap = nullptr) {
+                       const InputStage *in = nullptr, const Trap *trap = nullptr,
+                       int32_t rank = 0) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     if (n_layers < 0 || n_seq < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "n_layers/n_seq must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
+    const bool mimo = rank != 0;
+    if (mimo && !valid_rank(rank)) return fail(SSM_ERR_UNSUPPORTED, "rank %d not in {1,2,4,8}", rank);
     if ((double)n_layers * n_seq * d_inner * 16.0 > 4.0e18) return fail(SSM_ERR_SHAPE, "problem too large");
     if (n_layers > 65535 || n_seq > 65535 || d_inner > ((int64_t)1 << 28))
         return fail(SSM_ERR_SHAPE, "n_layers and n_seq must be <= 65535, d_inner <= 2^28");
@@ -233,7 +252,8 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     const size_t eb = io_bytes(io);
     // B_t and C_t rows are read K values at a time: K = 4 states per lane for
     // d_state >= 4 (real), else d_state; complex rows are read one value at a time.
-    const size_t bc = cplx ? eb : eb * (size_t)std::min<int32_t>(d_state, 4);
+    // MIMO rows of B_t and C_t go through the scalar unit (4-byte aligned).
+    const size_t bc = mimo ? 4 : cplx ? eb : eb * (size_t)std::min<int32_t>(d_state, 4);
     if (!aligned(h, 16) || !aligned(A, 16) || !aligned(x, eb) || !aligned(dt, eb) ||
         !aligned(z, eb) || !aligned(y, eb) || !aligned(B, bc) || !aligned(C, bc) || !aligned(D, 4))
         return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; B_t, C_t min(d_state,4) elements; others element)");
@@ -242,6 +262,11 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
             return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
         if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, bc))
             return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev element; B_prev as B_t)");
+    }
+    if (mimo) {
+        const size_t va = std::min<size_t>(16, (size_t)rank * eb);
+        if (!aligned(x, va) || !aligned(z, va) || !aligned(y, va))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x_t, z_t, y_t: min(16, rank * element) bytes)");
     }
     ssm::StepArgs a{};
     a.h = h; a.x = x; a.dt = dt; a.B = B; a.C = C; a.z = z; a.A = A; a.D = D; a.y = y;
@@ -264,6 +289,9 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
         a.x_prev = trap->x_prev;
         a.B_prev = trap->B_prev;
         e = ssm::launch_step_trap(a, iot, d_state, z != nullptr, replay, s);
+    } else if (mimo) {
+        a.rank = rank;
+        e = ssm::launch_step_mimo(a, iot, d_state, z != nullptr, s);
     } else {
         e = cplx ? ssm::launch_step_complex(a, iot, d_state, z != nullptr, replay, s)
                  : ssm::launch_step_real(a, iot, d_state, z != nullptr, replay, s);
@@ -581,6 +609,48 @@ ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev
     const Trap tr{x_prev, B_prev};
     return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
                        io, hip_stream, false, true, nullptr, &tr);
+}
+
+size_t ssm_scan_fwd_mimo_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                   int32_t rank, int64_t chunk_len) {
+    Plan p;
+    if (!valid_rank(rank)) return 0;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p, rank) != SSM_OK) return 0;
+    return p.ws_bytes;
+}
+
+ssm_status ssm_scan_fwd_mimo(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, const float *h0,
+                             void *y, float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                             int32_t d_state, int32_t rank, ssm_dtype io, int64_t chunk_len,
+                             void *workspace, size_t workspace_bytes, void *hip_stream) {
+    if (rank == 0) return fail(SSM_ERR_UNSUPPORTED, "rank 0 not in {1,2,4,8}");
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0,
+                       nullptr, nullptr, rank);
+}
+
+ssm_status ssm_scan_fwd_mimo_profiled(const void *x, const void *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const void *z, const float *h0, void *y, float *h_final,
+                                      int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                      int32_t rank, ssm_dtype io, int64_t chunk_len,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream,
+                                      void *const *events, int32_t n_events) {
+    if (!events) return fail(SSM_ERR_NULL, "events are required");
+    if (rank == 0) return fail(SSM_ERR_UNSUPPORTED, "rank 0 not in {1,2,4,8}");
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, events, n_events,
+                       nullptr, nullptr, rank);
+}
+
+ssm_status ssm_step_mimo(float *h, const void *x_t, const void *dt_t, const float *A,
+                         const void *B_t, const void *C_t, const float *D, const void *z_t,
+                         void *y_t, int64_t n_layers, int64_t n_seq, int64_t d_inner,
+                         int32_t d_state, int32_t rank, ssm_dtype io, void *hip_stream) {
+    if (rank == 0) return fail(SSM_ERR_UNSUPPORTED, "rank 0 not in {1,2,4,8}");
+    return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
+                       io, hip_stream, false, false, nullptr, nullptr, rank);
 }
 
 size_t ssm_scan_bwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,

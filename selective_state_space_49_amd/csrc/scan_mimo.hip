@@ -1,0 +1,525 @@
+// scan_mimo.hip -- prefill with multi-input multi-output (MIMO) projections (gfx950).
+//
+// The Mamba-3 item on MIMO ("Jamba — SSM-Transformer Híbrido", section "Mamba-3: a
+// linha de base de SSM puro em 2026", item 3) makes the per-feature projections
+// matrix-valued. Read here as: each channel takes R inputs and gives R outputs, and
+// B_t, C_t are N x R matrices shared by the channels of a (batch, step):
+//     h_t[n] = exp(dt_t A[n]) h_{t-1}[n] + dt_t sum_r B_t[n][r] x_t[r]
+//     y_t[r] = (sum_n C_t[n][r] h_t[n] + D x_t[r]) * silu(z_t[r])
+// The state stays N wide per channel; R = 1 is the plain scan.
+//
+// Work split and phases are those of the plain prefill: one lane per channel with its
+// N states in VGPRs, the sequence cut into chunks (summary from a zero start over the
+// decay window, carry scan over chunks, rescan with the epilogue). The decay of a step
+// does not depend on R, so the decay horizon and the carry kernel are shared as they
+// are. What changes is the per-step work: the R inputs of a channel are one vector
+// load (R consecutive elements of a [rows][Dn][R] stream), B_t and C_t come in through
+// the scalar unit as N*R wave-uniform values, and each state update costs R
+// multiply-adds for B_t x_t and each output R more for C_t h_t, against one
+// exponential per state: the exponential is shared by R outputs.
+//
+// The decode step (k_mimo_step) advances one token per (layer, sequence, channel)
+// with the same per-step arithmetic as the rescan, from the same shared function.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+#include "ssm_stream.h"
+
+namespace ssm {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((vector_size(8)));
+typedef uint32_t u32x4 __attribute__((vector_size(16)));
+
+// The R elements of one channel in one row, as loaded (raw bits).
+template <typename IO, int R>
+struct VecRaw {
+    static constexpr int kBytes = R * (int)sizeof(IO);
+    static constexpr int kWords = kBytes >= 4 ? kBytes / 4 : 1;
+    uint32_t w[kWords];
+    // Element r, widened to fp32 (exact).
+    __device__ __forceinline__ float at(int r) const {
+        if constexpr (sizeof(IO) == 2) {
+            const uint32_t v = w[r >> 1];
+            return __uint_as_float((r & 1) ? (v & 0xffff0000u) : (v << 16));
+        } else {
+            return __uint_as_float(w[r]);
+        }
+    }
+};
+
+// A [rows][Dn][R] stream walked row by row through a buffer resource, like RowStream:
+// voff = the lane's channel times R elements, soff = the row's byte offset.
+template <typename IO, int R>
+struct VecStream {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit VecStream(const void *base)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, kRsrcWord3)) {}
+
+    __device__ __forceinline__ VecRaw<IO, R> ld(uint32_t voff, uint32_t soff) const {
+        VecRaw<IO, R> v;
+        constexpr int B = VecRaw<IO, R>::kBytes;
+        if constexpr (B == 2) {
+            v.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        } else if constexpr (B == 4) {
+            v.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        } else if constexpr (B == 8) {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+            v.w[0] = t[0]; v.w[1] = t[1];
+        } else if constexpr (B == 16) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v.w[k] = t[k];
+        } else {
+            static_assert(B == 32, "R * element size must be 2..32 bytes");
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16u * h, soff, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v.w[4 * h + k] = t[k];
+            }
+        }
+        return v;
+    }
+
+    // Stores y[0..R) (rounded to the element type) with one vector store.
+    __device__ __forceinline__ void st(uint32_t voff, uint32_t soff, const float (&y)[R]) const {
+        VecRaw<IO, R> v;
+        if constexpr (sizeof(IO) == 2) {
+            if constexpr (R == 1) {
+                v.w[0] = f32_to_bf16(y[0]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < R / 2; ++k)
+                    v.w[k] = (uint32_t)f32_to_bf16(y[2 * k]) | ((uint32_t)f32_to_bf16(y[2 * k + 1]) << 16);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < R; ++k) v.w[k] = __float_as_uint(y[k]);
+        }
+        constexpr int B = VecRaw<IO, R>::kBytes;
+        if constexpr (B == 2) {
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v.w[0], r, voff, soff, 0);
+        } else if constexpr (B == 4) {
+            __builtin_amdgcn_raw_buffer_store_b32(v.w[0], r, voff, soff, 0);
+        } else if constexpr (B == 8) {
+            u32x2 t = {v.w[0], v.w[1]};
+            __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, 0);
+        } else if constexpr (B == 16) {
+            u32x4 t = {v.w[0], v.w[1], v.w[2], v.w[3]};
+            __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, 0);
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4 t = {v.w[4 * h], v.w[4 * h + 1], v.w[4 * h + 2], v.w[4 * h + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(t, r, voff + 16u * h, soff, 0);
+            }
+        }
+    }
+};
+
+// R consecutive elements at a global pointer (aligned to min(16, R * element) bytes).
+template <typename IO, int R>
+__device__ __forceinline__ VecRaw<IO, R> ld_vec(const IO *p) {
+    VecRaw<IO, R> v;
+    constexpr int B = VecRaw<IO, R>::kBytes;
+    if constexpr (B == 2) {
+        v.w[0] = *(const uint16_t *)p;
+    } else if constexpr (B == 4) {
+        v.w[0] = *(const uint32_t *)p;
+    } else if constexpr (B == 8) {
+        const u32x2 t = *(const u32x2 *)p;
+        v.w[0] = t[0]; v.w[1] = t[1];
+    } else {
+#pragma unroll
+        for (int h = 0; h < B / 16; ++h) {
+            const u32x4 t = *((const u32x4 *)p + h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v.w[4 * h + k] = t[k];
+        }
+    }
+    return v;
+}
+
+template <typename IO, int R>
+__device__ __forceinline__ void st_vec(IO *p, const float (&y)[R]) {
+    if constexpr (sizeof(IO) == 2) {
+        if constexpr (R == 1) {
+            *(uint16_t *)p = f32_to_bf16(y[0]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < R / 2; ++k)
+                ((uint32_t *)p)[k] = (uint32_t)f32_to_bf16(y[2 * k]) | ((uint32_t)f32_to_bf16(y[2 * k + 1]) << 16);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < R; ++k) ((float *)p)[k] = y[k];
+    }
+}
+
+// One step of one channel, in the fixed order that the prefill rescan and the decode
+// step share (so that L decode steps equal a one-chunk prefill bit for bit):
+//     xd[r] = dt x[r];  for n ascending:
+//         u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u) for r = 1 .. R-1;
+//         h[n] = fma(e2(dt A[n] log2 e), h[n], u);  acc[r] = fma(C[n][r], h[n], acc[r])
+// Row reads element e0 + n R + r of the step's B (and C) through the scalar unit.
+template <int N, int R, typename Row>
+__device__ __forceinline__ void mimo_update(float (&h)[N], const float (&A2)[N], float dv,
+                                            const float (&xv)[R], const Row &Bp, const Row &Cp,
+                                            int64_t e0, float (&acc)[R]) {
+    float xd[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        xd[r] = dv * xv[r];
+        acc[r] = 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const int64_t e = e0 + n * R;
+        float u = Bp.ld(e) * xd[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) u = __builtin_fmaf(Bp.ld(e + r), xd[r], u);
+        h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
+    }
+}
+
+// y[r] = fma(D, x[r], acc[r]), gated: y[r] * silu(z[r]).
+template <typename IO, int R, bool GATED>
+__device__ __forceinline__ void mimo_out(float Dd, const float (&xv)[R], const float (&acc)[R],
+                                         const VecRaw<IO, R> &zr, float (&yv)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        yv[r] = __builtin_fmaf(Dd, xv[r], acc[r]);
+        if (GATED) yv[r] = yv[r] * silu(zr.at(r));
+    }
+}
+
+// One block of KU steps of loaded inputs (raw bits, widened at use).
+template <typename IO, int R, int KU>
+struct MimoBlock {
+    VecRaw<IO, R> x[KU], z[KU];
+    uint32_t dt[KU];
+};
+
+struct MimoStreams {
+    uint32_t vx;   // lane's byte offset in an x / z / y row
+    uint32_t vd;   // lane's byte offset in a dt row
+    uint32_t rbx;  // bytes per x / z / y row
+    uint32_t rbd;  // bytes per dt row
+};
+
+template <typename IO, int R, bool GATED, int KU>
+__device__ __forceinline__ void load_mimo_block(MimoBlock<IO, R, KU> &s, const VecStream<IO, R> &x,
+                                                const RowStream<IO> &dt, const VecStream<IO, R> &z,
+                                                const MimoStreams &o, uint32_t row) {
+#pragma unroll
+    for (int k = 0; k < KU; ++k) {
+        s.x[k] = x.ld(o.vx, (row + k) * o.rbx);
+        s.dt[k] = dt.ldraw(o.vd, (row + k) * o.rbd);
+        if (GATED) s.z[k] = z.ld(o.vx, (row + k) * o.rbx);
+    }
+}
+
+// Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1, with the next block of KU rows in
+// flight while the current one is computed (as stream_steps does for scalar rows).
+template <typename IO, int R, bool GATED, int KU, typename Body>
+__device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowStream<IO> &dt,
+                                           const VecStream<IO, R> &z, const MimoStreams &o,
+                                           uint32_t steps, uint32_t prio_scale, Body &&body) {
+    const uint32_t full = steps / KU;
+    uint32_t i = 0;
+    MimoBlock<IO, R, KU> bufA, bufB;
+    if (full > 0) load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, 0);
+    for (uint32_t k = 0; k < full; k += 2) {
+        if (prio_scale) set_priority(steps - i, prio_scale);
+        if (k + 1 < full) load_mimo_block<IO, R, GATED, KU>(bufB, x, dt, z, o, i + KU);
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(i + j, bufA.x[j], RowStream<IO>::widen(bufA.dt[j]), bufA.z[j]);
+        }
+        i += KU;
+        if (k + 1 >= full) break;
+        if (k + 2 < full) load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, i + KU);
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            body(i + j, bufB.x[j], RowStream<IO>::widen(bufB.dt[j]), bufB.z[j]);
+        }
+        i += KU;
+    }
+    if (prio_scale) __builtin_amdgcn_s_setprio(0);
+    for (; i < steps; ++i) {  // ragged tail, one step at a time
+        const VecRaw<IO, R> xv = x.ld(o.vx, i * o.rbx);
+        const float dv = dt.ld(o.vd, i * o.rbd);
+        VecRaw<IO, R> zv{};
+        if (GATED) zv = z.ld(o.vx, i * o.rbx);
+        body(i, xv, dv, zv);
+    }
+}
+
+struct LaneId {
+    int64_t b, d;
+};
+
+__device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
+    LaneId r;
+    r.b = (int64_t)blockIdx.x / a.dblocks;
+    r.d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
+    return r;
+}
+
+__device__ __forceinline__ MimoStreams mimo_offsets(const ScanArgs &a, int64_t d, int R, int eb) {
+    MimoStreams o;
+    o.vx = (uint32_t)d * (uint32_t)(R * eb);
+    o.vd = (uint32_t)d * (uint32_t)eb;
+    o.rbx = (uint32_t)(a.Dn * R * eb);
+    o.rbd = (uint32_t)(a.Dn * eb);
+    return o;
+}
+
+// Steps of x / z / y rows are R elements per channel: blocks of 4 steps for R <= 2,
+// 2 for wider ranks (keeps the ping-pong buffers within the register budget).
+template <int R> constexpr int kMimoKU = R <= 2 ? 4 : 2;
+
+// ---------------------------------------------------------------- chunk summary
+template <typename IO, int N, int R>
+__global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
+    const LaneId ln = lane_id(a);
+    if (ln.d >= a.Dn) return;
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const uint32_t T = (uint32_t)a.T;  // every chunk that has a summary is full length
+    constexpr int eb = (int)sizeof(IO);
+    const MimoStreams o = mimo_offsets(a, ln.d, R, eb);
+    float A2[N], h[N];
+    float amax = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        amax = fmaxf(amax, A2[n]);
+        h[n] = 0.0f;
+    }
+    const int64_t t_row0 = ln.b * a.L + t0;  // row of (b, t0)
+    const RowStream<IO> dts((const IO *)a.dt + t_row0 * a.Dn);
+    const uint32_t ts = horizon_start<IO>(dts, o.vd, o.rbd, T, amax);
+    const int64_t rw = t_row0 + ts;
+    const VecStream<IO, R> xs((const IO *)a.x + rw * a.Dn * R);
+    const RowStream<IO> dws((const IO *)a.dt + rw * a.Dn);
+    const UniRow<IO, N * R> Bp(a.B, ln.b * a.L * N * R);
+    double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
+    mimo_steps<IO, R, false, kMimoKU<R>>(xs, dws, xs, o, T - ts, kSummaryPrioScale,
+                                         [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &) {
+        const int64_t t = t0 + ts + i;
+        S += (double)dv;
+        float xd[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) xd[r] = dv * xr.at(r);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            float u = Bp.ld((t * N + n) * R) * xd[0];
+#pragma unroll
+            for (int r = 1; r < R; ++r) u = __builtin_fmaf(Bp.ld((t * N + n) * R + r), xd[r], u);
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u);
+        }
+    });
+    const float Sf = (float)S;
+    const size_t so = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a.sumP[so + n] = ts == 0 ? e2(A2[n] * Sf) : 0.0f;
+        a.sumH[so + n] = h[n];
+    }
+}
+
+// ---------------------------------------------------------------- rescan + epilogue
+template <typename IO, int N, int R, bool GATED>
+__global__ __launch_bounds__(256) void k_mimo_scan(ScanArgs a) {
+    const LaneId ln = lane_id(a);
+    if (ln.d >= a.Dn) return;
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const uint32_t steps = (uint32_t)(min(a.L, t0 + a.T) - t0);
+    const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
+    const float *hin = c == 0 ? (a.h0 ? a.h0 + col : nullptr)
+                              : a.sumH + (size_t)(c - 1) * a.batch * a.Dn * N + col;
+    constexpr int eb = (int)sizeof(IO);
+    const MimoStreams o = mimo_offsets(a, ln.d, R, eb);
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        h[n] = hin ? hin[n] : 0.0f;
+    }
+    const float Dd = a.D[ln.d];
+    const int64_t t_row0 = ln.b * a.L + t0;
+    const VecStream<IO, R> xs((const IO *)a.x + t_row0 * a.Dn * R),
+        zs(GATED ? (const IO *)a.z + t_row0 * a.Dn * R : (const IO *)a.x + t_row0 * a.Dn * R),
+        ys((IO *)a.y + t_row0 * a.Dn * R);
+    const RowStream<IO> dts((const IO *)a.dt + t_row0 * a.Dn);
+    const UniRow<IO, N * R> Bp(a.B, ln.b * a.L * N * R);
+    const UniRow<IO, N * R> Cp(a.C, ln.b * a.L * N * R);
+    mimo_steps<IO, R, GATED, kMimoKU<R>>(xs, dts, zs, o, steps, steps,
+                                         [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &zr) {
+        const int64_t t = t0 + i;
+        float xv[R], acc[R], yv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
+        mimo_update<N, R>(h, A2, dv, xv, Bp, Cp, t * N * R, acc);
+        mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
+        ys.st(o.vx, i * o.rbx, yv);
+    });
+    if (c == a.n_chunks - 1 && a.h_final) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.h_final[col + n] = h[n];
+    }
+}
+
+// ---------------------------------------------------------------- decode step
+// One token for every (layer, sequence, channel). One lane per channel holds the
+// channel's N states; B_t and C_t are one row per (layer, sequence), the same for the
+// whole block (grid y = sequence, z = layer), so they come in through the scalar unit.
+// The state is read and written once, with streaming 16-byte accesses.
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <typename IO, int N, int R, bool GATED>
+__global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
+    const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (d >= a.Dn) return;
+    const int64_t l = blockIdx.z;
+    const int64_t lq = l * a.n_seq + blockIdx.y;
+    const int64_t ch = lq * a.Dn + d;
+    float *hp = a.h + ch * N;
+    const float *Ap = a.A + (l * a.Dn + d) * N;
+    float h[N], A2[N];
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int n = 0; n < N; n += 4) {
+            const f4v q = __builtin_nontemporal_load((const f4v *)(hp + n));
+            const f4v w = *(const f4v *)(Ap + n);
+            h[n] = q.x; h[n + 1] = q.y; h[n + 2] = q.z; h[n + 3] = q.w;
+            A2[n] = w.x; A2[n + 1] = w.y; A2[n + 2] = w.z; A2[n + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) { h[n] = hp[n]; A2[n] = Ap[n]; }
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] *= kLog2e;
+    const VecRaw<IO, R> xr = ld_vec<IO, R>((const IO *)a.x + ch * R);
+    VecRaw<IO, R> zr{};
+    if (GATED) zr = ld_vec<IO, R>((const IO *)a.z + ch * R);
+    const float dv = Io<IO>::ld((const IO *)a.dt + ch);
+    const float Dd = a.D[l * a.Dn + d];
+    const UniRow<IO, N * R> Bp(a.B, lq * N * R), Cp(a.C, lq * N * R);
+    float xv[R], acc[R], yv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
+    mimo_update<N, R>(h, A2, dv, xv, Bp, Cp, 0, acc);
+    mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int n = 0; n < N; n += 4) {
+            f4v q;
+            q.x = h[n]; q.y = h[n + 1]; q.z = h[n + 2]; q.w = h[n + 3];
+            __builtin_nontemporal_store(q, (f4v *)(hp + n));
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) hp[n] = h[n];
+    }
+    st_vec<IO, R>((IO *)a.y + ch * R, yv);
+}
+
+template <typename IO, int N, int R>
+hipError_t launch_step_t(const StepArgs &a, bool gated, hipStream_t s) {
+    const dim3 grid((unsigned)((a.Dn + 255) / 256), (unsigned)a.n_seq, (unsigned)a.n_layers);
+    if (gated) hipLaunchKernelGGL((k_mimo_step<IO, N, R, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_mimo_step<IO, N, R, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename IO, int R>
+hipError_t launch_step_n(const StepArgs &a, int d_state, bool gated, hipStream_t s) {
+    switch (d_state) {
+        case 1: return launch_step_t<IO, 1, R>(a, gated, s);
+        case 2: return launch_step_t<IO, 2, R>(a, gated, s);
+        case 4: return launch_step_t<IO, 4, R>(a, gated, s);
+        case 8: return launch_step_t<IO, 8, R>(a, gated, s);
+        case 16: return launch_step_t<IO, 16, R>(a, gated, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t launch_step_io(const StepArgs &a, int d_state, bool gated, hipStream_t s) {
+    switch (a.rank) {
+        case 1: return launch_step_n<IO, 1>(a, d_state, gated, s);
+        case 2: return launch_step_n<IO, 2>(a, d_state, gated, s);
+        case 4: return launch_step_n<IO, 4>(a, d_state, gated, s);
+        case 8: return launch_step_n<IO, 8>(a, d_state, gated, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+inline void mark(hipEvent_t const *ev, int i, hipStream_t s) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+}
+
+template <typename IO, int N, int R>
+hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s, hipEvent_t const *ev) {
+    const dim3 blk(a.threads);
+    const unsigned gx = (unsigned)(a.batch * a.dblocks);
+    mark(ev, 0, s);
+    if (a.n_chunks > 1)
+        hipLaunchKernelGGL((k_mimo_summary<IO, N, R>), dim3(gx, a.n_chunks - 1), blk, 0, s, a);
+    mark(ev, 1, s);
+    hipError_t e = launch_carry(a, N, s);
+    if (e != hipSuccess) return e;
+    mark(ev, 2, s);
+    if (gated)
+        hipLaunchKernelGGL((k_mimo_scan<IO, N, R, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_mimo_scan<IO, N, R, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    mark(ev, 3, s);
+    return hipGetLastError();
+}
+
+template <typename IO, int R>
+hipError_t launch_n(const ScanArgs &a, int d_state, bool gated, hipStream_t s, hipEvent_t const *ev) {
+    switch (d_state) {
+        case 1: return launch_t<IO, 1, R>(a, gated, s, ev);
+        case 2: return launch_t<IO, 2, R>(a, gated, s, ev);
+        case 4: return launch_t<IO, 4, R>(a, gated, s, ev);
+        case 8: return launch_t<IO, 8, R>(a, gated, s, ev);
+        case 16: return launch_t<IO, 16, R>(a, gated, s, ev);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s, hipEvent_t const *ev) {
+    switch (a.rank) {
+        case 1: return launch_n<IO, 1>(a, d_state, gated, s, ev);
+        case 2: return launch_n<IO, 2>(a, d_state, gated, s, ev);
+        case 4: return launch_n<IO, 4>(a, d_state, gated, s, ev);
+        case 8: return launch_n<IO, 8>(a, d_state, gated, s, ev);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_scan_mimo(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev) {
+    return io == 0 ? launch_io<float>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits>(a, d_state, gated, s, ev);
+}
+
+hipError_t launch_step_mimo(const StepArgs &a, int io, int d_state, bool gated, hipStream_t s) {
+    return io == 0 ? launch_step_io<float>(a, d_state, gated, s)
+                   : launch_step_io<bf16_bits>(a, d_state, gated, s);
+}
+
+}  // namespace ssm

@@ -32,6 +32,9 @@ struct ScanArgs {
     // Exponential-trapezoidal entry point only: the input before step 0.
     const void *x_prev;       // [batch][Dn] of io, or null (then B_prev is null too)
     const void *B_prev;       // [batch][N] of io, or null
+    // MIMO entry point only: inputs and outputs per channel (x, z, y are [batch][L][Dn][rank],
+    // B and C [batch][L][N][rank]); 1 elsewhere.
+    int32_t rank;
 };
 
 struct StepArgs {
@@ -49,6 +52,9 @@ struct StepArgs {
     // Exponential-trapezoidal entry point only: the previous token's x and B.
     const void *x_prev;   // [n_layers][n_seq][Dn] of io, or null (then B_prev is null too)
     const void *B_prev;   // [n_layers][n_seq][N] of io, or null
+    // MIMO entry point only: rank (x, z, y are [n_layers][n_seq][Dn][rank], B and C
+    // [n_layers][n_seq][N][rank]); 1 elsewhere.
+    int32_t rank;
 };
 
 // Real diagonal state. io: 0 = f32, 1 = bf16. Returns hipSuccess or the launch error.
@@ -59,6 +65,9 @@ hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, 
                             hipEvent_t const *ev);
 // The same with the exponential-trapezoidal discretisation (x_prev, B_prev of a).
 hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev);
+// The same with MIMO projections of rank a.rank (1, 2, 4 or 8).
+hipError_t launch_scan_mimo(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev);
 hipError_t launch_scan_complex(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                                hipEvent_t const *ev);
@@ -81,6 +90,8 @@ hipError_t launch_step_complex(const StepArgs &a, int io, int d_state, bool gate
                                hipStream_t s);
 hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                              hipStream_t s);
+// MIMO decode of rank a.rank (1, 2, 4 or 8).
+hipError_t launch_step_mimo(const StepArgs &a, int io, int d_state, bool gated, hipStream_t s);
 // Exponential-trapezoidal decode (x_prev, B_prev of a).
 hipError_t launch_step_trap(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                             hipStream_t s);

@@ -211,3 +211,39 @@ def test_trapezoid_argument_errors(lib):
         assert step(fn, xp=None) == NULL
         assert step(fn, Bp=0x3104) == ALIGN   # aligned like B_t: 4 bf16 states per lane
         assert step(fn, N=5) == UNSUP
+
+
+def test_mimo_argument_errors(lib):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def scan(x=0x100000, z=None, y=0x200000, B=0x1000, N=4, R=4, io=1, L=8, ws=None, wsb=0, Dn=4):
+        return lib.ssm_scan_fwd_mimo(p(x), p(0x1000), p(0x1000), p(B), p(0x1000), p(0x1000), p(z),
+                                     None, p(y), None, 1, L, Dn, N, R, io, 0, p(ws), wsb, None)
+    for bad in (0, 3, 16, -1):
+        assert scan(R=bad) == UNSUP
+        assert lib.ssm_scan_fwd_mimo_workspace(1, 64, 4, 4, bad, 0) == 0
+    assert scan(N=3) == UNSUP
+    assert scan(x=0x100004) == ALIGN          # bf16, rank 4: 8-byte vectors
+    assert scan(y=0x200002, R=2) == ALIGN     # bf16, rank 2: 4-byte vectors
+    assert scan(z=0x300008, R=8, io=0) == ALIGN   # fp32, rank 8: 16-byte vectors
+    assert scan(B=0x1002) == ALIGN            # B, C through the scalar unit: 4 bytes
+    assert scan(x=None) == NULL
+    # workspace: the chunk cap keeps a chunk's x / y rows (d_inner * rank elements)
+    # below 2 GiB, so wide ranks can need more chunks than the plain scan
+    big = lib.ssm_scan_fwd_mimo_workspace(1, 262144, 8192, 16, 4, 0)
+    assert big == lib.ssm_scan_fwd_workspace(1, 262144, 8192, 16) > 0
+    assert scan(L=262144, Dn=8192, N=16) == WS
+    T8 = (1 << 31) // (8192 * 8 * 4) - 1
+    assert lib.ssm_scan_fwd_mimo_workspace(1, 262144, 8192, 16, 8, 262144) == \
+        2 * (((-(-262144 // T8) - 1) * 8192 * 16 * 4 + 255) // 256 * 256)
+    assert scan(L=0) == OK                    # nothing to do, nothing enqueued
+
+    def step(R=4, N=16, io=1, x=0x1000, y=0x2000, B=0x1000):
+        return lib.ssm_step_mimo(p(0x1000), p(x), p(0x1000), p(0x1000), p(B), p(0x1000), p(0x1000),
+                                 None, p(y), 2, 3, 4, N, R, io, None)
+    assert step(R=3) == UNSUP
+    assert step(R=0) == UNSUP
+    assert step(N=5) == UNSUP
+    assert step(x=0x1004) == ALIGN
+    assert step(y=0x2008, R=8, io=0) == ALIGN
+    assert step(B=0x1002) == ALIGN

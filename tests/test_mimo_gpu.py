@@ -1,0 +1,246 @@
+"""The MIMO scan (ssm_scan_fwd_mimo) and decode step (ssm_step_mimo) on the GPU against
+the fp64 oracle's scan_mimo / step_mimo, plus invariants.
+
+Prefill cases span several chunks and 64-lane waves with ragged tails, every state
+size and rank, fp32 and bf16, with and without gate and h0. Rank 1 equals the plain
+scan bit for bit; the result does not depend on the chunk length; resuming from
+h_final equals one call; L decode steps equal a one-chunk prefill bit for bit; the
+256k prefill and the 28-layer decode at full size on sampled channels.
+"""
+import pytest
+import torch
+
+import oracle
+import selective_state_space_49_amd as ssm
+from tests.gpu_util import TOL, bitwise_equal, gather_channels, rel_err, say, to_dev
+from workloads import (WORKLOADS, DecodeShape, ScanShape, make_decode_params, make_h0,
+                       make_mimo_decode_step, make_mimo_inputs, sample_channels)
+
+pytestmark = pytest.mark.gpu
+
+# (batch, L, d_inner, d_state, rank, io, gated, with_h0, chunk_len)
+CASES = [
+    (2, 300, 200, 16, 4, "bf16", True, True, 64),     # 5 chunks, ragged last chunk
+    (2, 300, 200, 16, 4, "f32", False, True, 37),     # 9 chunks of odd length
+    (1, 1000, 130, 8, 2, "bf16", True, False, 0),     # library's own plan
+    (2, 257, 70, 4, 8, "f32", True, True, 50),        # fp32 rank 8: two 16-byte vectors
+    (1, 203, 65, 16, 8, "bf16", True, True, 50),      # bf16 rank 8: one 16-byte vector
+    (3, 129, 64, 1, 1, "f32", False, False, 16),
+    (3, 131, 40, 1, 1, "bf16", True, True, 16),       # bf16, N * R = 1: odd rows of B, C
+    (2, 131, 40, 1, 2, "bf16", True, True, 16),
+    (1, 1, 1, 4, 4, "f32", True, True, 0),            # one step, one channel
+    (1, 4501, 33, 16, 4, "f32", True, True, 64),      # 71 chunks
+    (2, 777, 96, 16, 2, "bf16", False, True, 5),      # chunks shorter than a register block
+]
+
+
+def _ids(c):
+    b, L, Dn, N, R, io, g, h0, T = c
+    return (f"b{b}_L{L}_D{Dn}_N{N}_R{R}_{io}_{'gated' if g else 'nogate'}_"
+            f"{'h0' if h0 else 'zero'}_T{T}")
+
+
+def _draw(case, seed=0):
+    b, L, Dn, N, R, io, gated, with_h0, T = case
+    shape = ScanShape("mimo", b, L, Dn, N, io, gated=gated, seed=500 + seed)
+    inp = make_mimo_inputs(shape, R, "cpu")
+    inp["h0"] = make_h0(b, Dn, N, seed=19 + seed) if with_h0 else None
+    return shape, inp
+
+
+def _gpu(d, chunk_len):
+    g = to_dev(d)
+    return ssm.ssm_scan_fwd_mimo(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], g["h0"],
+                                 chunk_len=chunk_len)
+
+
+def _oracle(d):
+    return oracle.scan_mimo(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], d["h0"])
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_mimo_prefill_matches_oracle(case):
+    shape, d = _draw(case)
+    say("MIMO prefill", _ids(case))
+    y, hf = _gpu(d, case[-1])
+    torch.cuda.synchronize()
+    yr, hr = _oracle(d)
+    tol = TOL[shape.io]
+    assert rel_err(y, yr) <= tol, f"y error {rel_err(y, yr)}"
+    assert rel_err(hf, hr) <= tol, f"h_final error {rel_err(hf, hr)}"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mimo_rank_one_is_the_plain_scan(io):
+    # Rank 1 performs the plain scan's operations in the plain scan's order.
+    case = (2, 500, 130, 16, 1, io, True, True, 64)
+    shape, d = _draw(case, seed=1)
+    g = to_dev(d)
+    say("MIMO rank 1 vs plain scan", io)
+    y, hf = _gpu(d, 64)
+    y1, h1 = ssm.ssm_scan_fwd_ex(g["x"][..., 0].contiguous(), g["dt"], g["A"], g["B"][..., 0].contiguous(),
+                                 g["C"][..., 0].contiguous(), g["D"], g["z"][..., 0].contiguous(), g["h0"],
+                                 chunk_len=64)
+    torch.cuda.synchronize()
+    assert bitwise_equal(y[..., 0].contiguous(), y1) and bitwise_equal(hf, h1)
+
+
+def test_mimo_chunking_determinism_and_empty():
+    case = (2, 600, 96, 16, 4, "f32", True, True, 0)
+    shape, d = _draw(case, seed=2)
+    say("MIMO chunk independence")
+    y0, h0 = _gpu(d, 0)
+    y1, h1 = _gpu(d, 0)
+    torch.cuda.synchronize()
+    assert bitwise_equal(y0, y1) and bitwise_equal(h0, h1), "not deterministic"
+    for T in (600, 64, 41, 8):
+        y, hf = _gpu(d, T)
+        torch.cuda.synchronize()
+        assert rel_err(y, oracle.to_f64(y0)) <= TOL["f32"], f"chunk {T}"
+        assert rel_err(hf, oracle.to_f64(h0)) <= TOL["f32"], f"chunk {T}"
+    # L = 0: h_final = h0 and nothing else is read
+    g = to_dev(d)
+    e = lambda t: t[:, :0].contiguous()
+    y, hf = ssm.ssm_scan_fwd_mimo(e(g["x"]), e(g["dt"]), g["A"], e(g["B"]), e(g["C"]), g["D"],
+                                  e(g["z"]), g["h0"])
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and bitwise_equal(hf, g["h0"])
+
+
+def test_mimo_in_place_and_split_resume():
+    case = (2, 700, 96, 16, 4, "bf16", True, True, 64)
+    shape, d = _draw(case, seed=3)
+    g = to_dev(d)
+    say("MIMO split/resume and in place")
+    y, hf = _gpu(d, 64)
+    k = 333
+    p = lambda t, sl: t[:, sl].contiguous()
+    y1, h1 = ssm.ssm_scan_fwd_mimo(p(g["x"], slice(0, k)), p(g["dt"], slice(0, k)), g["A"],
+                                   p(g["B"], slice(0, k)), p(g["C"], slice(0, k)), g["D"],
+                                   p(g["z"], slice(0, k)), g["h0"], chunk_len=64)
+    y2, h2 = ssm.ssm_scan_fwd_mimo(p(g["x"], slice(k, None)), p(g["dt"], slice(k, None)), g["A"],
+                                   p(g["B"], slice(k, None)), p(g["C"], slice(k, None)), g["D"],
+                                   p(g["z"], slice(k, None)), h1, chunk_len=64)
+    # y written over x itself
+    xi = g["x"].clone()
+    yi, hi = ssm.ssm_scan_fwd_mimo(xi, g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], g["h0"],
+                                   chunk_len=64, y=xi)
+    torch.cuda.synchronize()
+    yy = torch.cat([y1, y2], dim=1)
+    assert rel_err(yy, oracle.to_f64(y)) <= TOL["bf16"] and rel_err(h2, oracle.to_f64(hf)) <= TOL["f32"]
+    assert bitwise_equal(yi, y) and bitwise_equal(hi, hf)
+
+
+def test_mimo_slow_decay_and_frozen_state():
+    # Decay horizons that are never reached within a chunk (whole-chunk windows).
+    shape, d = _draw((1, 3000, 130, 16, 4, "f32", True, True, 500), seed=4)
+    d["A"] = d["A"] * 1e-3
+    d["A"][5] = 0.0
+    say("MIMO slow decay")
+    y, hf = _gpu(d, 500)
+    torch.cuda.synchronize()
+    yr, hr = _oracle(d)
+    assert rel_err(y, yr) <= TOL["f32"] and rel_err(hf, hr) <= TOL["f32"]
+
+
+# ---------------------------------------------------------------- decode
+# (n_layers, n_seq, d_inner, d_state, rank, io, gated)
+DECODE_CASES = [
+    (3, 5, 130, 16, 4, "bf16", True),
+    (2, 4, 64, 16, 4, "f32", False),
+    (2, 3, 77, 8, 2, "f32", True),
+    (1, 7, 33, 4, 8, "bf16", True),
+    (2, 2, 40, 2, 8, "f32", True),
+    (2, 3, 20, 1, 1, "bf16", True),
+    (1, 2, 600, 16, 4, "bf16", True),   # three blocks of 256 channels, the last ragged
+]
+STEPS = 5
+
+
+def _dids(c):
+    Ln, S, Dn, N, R, io, g = c
+    return f"L{Ln}_S{S}_D{Dn}_N{N}_R{R}_{io}_{'gated' if g else 'nogate'}"
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=_dids)
+def test_mimo_step_matches_oracle(case):
+    Ln, S, Dn, N, R, io, gated = case
+    shape = DecodeShape("mimo", Ln, S, Dn, N, STEPS, io, gated=gated, seed=570)
+    par = make_decode_params(shape, "cpu")
+    h0 = torch.randn((Ln, S, Dn, N), generator=torch.Generator().manual_seed(9))
+    h, h_ref = h0.cuda(), h0.double().numpy()
+    A, D = par["A"].cuda(), par["D"].cuda()
+    for k in range(STEPS):
+        inp = make_mimo_decode_step(shape, R, k, "cpu")
+        g = to_dev(inp)
+        say("MIMO decode", _dids(case), "step", k)
+        y = ssm.ssm_step_mimo(h, g["x"], g["dt"], A, g["B"], g["C"], D, g["z"])
+        torch.cuda.synchronize()
+        yr, h_ref = oracle.step_mimo(h_ref, inp["x"], inp["dt"], par["A"], inp["B"], inp["C"],
+                                     par["D"], inp["z"])
+        assert rel_err(y, yr) <= TOL[io], f"y vs oracle {rel_err(y, yr)} at step {k}"
+        assert rel_err(h, h_ref) <= TOL[io], f"h vs oracle at step {k}"
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mimo_decode_equals_one_chunk_prefill(io):
+    # L decode steps (one layer, n_seq = batch) against a one-chunk prefill of the same
+    # tokens: the two kernels share the per-step arithmetic, so bit for bit.
+    b, L, Dn, N, R = 3, 40, 96, 16, 4
+    shape, d = _draw((b, L, Dn, N, R, io, True, True, L), seed=5)
+    say("MIMO prefill vs decode", io)
+    y, hf = _gpu(d, L)
+    g = to_dev(d)
+    h = g["h0"].view(1, b, Dn, N).clone()
+    row = lambda v, t: v[:, t].unsqueeze(0).contiguous()
+    ys = []
+    for t in range(L):
+        ys.append(ssm.ssm_step_mimo(h, row(g["x"], t), row(g["dt"], t), g["A"].unsqueeze(0),
+                                    row(g["B"], t), row(g["C"], t), g["D"].unsqueeze(0),
+                                    row(g["z"], t))[0])
+    torch.cuda.synchronize()
+    assert bitwise_equal(torch.stack(ys, dim=1), y)
+    assert bitwise_equal(h[0], hf)
+
+
+def test_mimo_full_size_long_context_sampled():
+    # The 256k prefill (batch 1, L 262144, 8192 channels, N 16, bf16) with rank 4 in the
+    # library's own chunk plan, as the benchmark times it; sampled channels vs the oracle.
+    shape = WORKLOADS["long_context_256k"]
+    R = 4
+    say("MIMO full size: inputs")
+    d = make_mimo_inputs(shape, R, "cuda")
+    say("MIMO full size: running")
+    y, hf = ssm.ssm_scan_fwd_mimo(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None)
+    torch.cuda.synchronize()
+    idx = sample_channels(shape.d_inner, 12, seed=16)
+    gc = lambda t: gather_channels(t, idx)
+    say("MIMO full size: oracle on", len(idx), "channels")
+    yr, hr = oracle.scan_mimo(gc(d["x"]), gc(d["dt"]), d["A"].cpu()[idx], d["B"].cpu(), d["C"].cpu(),
+                              d["D"].cpu()[idx], gc(d["z"]), None)
+    assert rel_err(gc(y), yr) <= TOL["bf16"], f"y error {rel_err(gc(y), yr)}"
+    assert rel_err(hf.index_select(1, idx.cuda()).cpu(), hr) <= TOL["bf16"]
+    assert torch.isfinite(y.float()).all()
+
+
+def test_mimo_full_size_decode_sampled():
+    # Two tokens of the 28-layer x 256-sequence x 8192-channel decode with rank 4; all
+    # layers and sequences on sampled channels vs the oracle.
+    base = WORKLOADS["batched_decode"]
+    R = 4
+    shape = base.scaled(steps=2)
+    par = make_decode_params(shape, "cuda")
+    h = torch.zeros((shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state), device="cuda")
+    idx = sample_channels(shape.d_inner, 16, seed=18)
+    h_ref = h.index_select(2, idx.cuda()).cpu().double().numpy()
+    for k in range(2):
+        inp = make_mimo_decode_step(shape, R, k, "cuda")
+        say("MIMO full-size decode step", k)
+        y = ssm.ssm_step_mimo(h, inp["x"], inp["dt"], par["A"], inp["B"], inp["C"], par["D"], inp["z"])
+        torch.cuda.synchronize()
+        gc = lambda t: gather_channels(t, idx)
+        yr, h_ref = oracle.step_mimo(h_ref, gc(inp["x"]), gc(inp["dt"]), gather_channels(par["A"], idx, 1),
+                                     inp["B"].cpu(), inp["C"].cpu(), gather_channels(par["D"], idx, 1),
+                                     gc(inp["z"]))
+        assert rel_err(gc(y), yr) <= TOL["bf16"], f"y error at step {k}"
+        assert rel_err(h.index_select(2, idx.cuda()).cpu(), h_ref) <= TOL["bf16"], f"h error at step {k}"

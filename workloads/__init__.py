@@ -43,7 +43,7 @@ __all__ = [
     "ScanShape", "DecodeShape", "WORKLOADS", "SCAN_WORKLOADS", "io_torch_dtype",
     "make_scan_inputs", "make_decode_params", "make_decode_step", "make_h0",
     "sample_channels", "SLAB_ELEMS", "make_input_stage", "make_decode_input_stage",
-    "make_decode_dt_raw",
+    "make_decode_dt_raw", "make_mimo_inputs", "make_mimo_decode_step",
 ]
 
 # Elements drawn per randn call for big tensors (fixed: part of the seeded recipe).
@@ -292,3 +292,40 @@ def make_decode_dt_raw(shape: DecodeShape, step: int, device="cpu",
     g = _gen(seed * 100003 + 1 + int(step), device)
     Ln, S, Dn = shape.n_layers, shape.n_seq, shape.d_inner
     return _normal((Ln, S, Dn), -1.0, 0.5, g, device, io_torch_dtype(shape.io))
+
+
+def make_mimo_inputs(shape: ScanShape, rank: int, device="cpu", seed: Optional[int] = None) -> dict:
+    """A prefill workload with MIMO projections of rank R: the plain scan's recipe with
+    x, z ~ N(0, 1) of shape [batch, L, d_inner, R] and B, C ~ N(0, 1) of shape
+    [batch, L, d_state, R]; dt ~ softplus(N(-1, 0.5)) [batch, L, d_inner]; A, D as
+    make_scan_inputs. Drawn from its own generator (seed + 23)."""
+    seed = (shape.seed if seed is None else seed) + 23
+    g = _gen(seed, device)
+    io = io_torch_dtype(shape.io)
+    b, L, Dn, N, R = shape.batch, shape.L, shape.d_inner, shape.d_state, int(rank)
+    f32 = torch.float32
+    A = -torch.exp(_normal((Dn, N), 0.0, 0.5, g, device, f32))
+    D = _normal((Dn,), 1.0, 0.1, g, device, f32)
+    x = _normal((b, L, Dn, R), 0.0, 1.0, g, device, io)
+    z = _normal((b, L, Dn, R), 0.0, 1.0, g, device, io) if shape.gated else None
+    dt = _softplus_normal((b, L, Dn), -1.0, 0.5, g, device, io)
+    B = _normal((b, L, N, R), 0.0, 1.0, g, device, io)
+    C = _normal((b, L, N, R), 0.0, 1.0, g, device, io)
+    return {"x": x, "dt": dt, "z": z, "A": A, "B": B, "C": C, "D": D}
+
+
+def make_mimo_decode_step(shape: DecodeShape, rank: int, step: int, device="cpu",
+                          seed: Optional[int] = None) -> dict:
+    """One MIMO decode token for every (layer, sequence): x_t, z_t [n_layers, n_seq,
+    d_inner, R]; dt_t [n_layers, n_seq, d_inner]; B_t, C_t [n_layers, n_seq, d_state, R];
+    distributions as make_decode_step, its own generator per (seed + 23, step)."""
+    seed = (shape.seed if seed is None else seed) + 23
+    g = _gen(seed * 100003 + 1 + int(step), device)
+    io = io_torch_dtype(shape.io)
+    Ln, S, Dn, N, R = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state, int(rank)
+    x = _normal((Ln, S, Dn, R), 0.0, 1.0, g, device, io)
+    z = _normal((Ln, S, Dn, R), 0.0, 1.0, g, device, io) if shape.gated else None
+    dt = _softplus_normal((Ln, S, Dn), -1.0, 0.5, g, device, io)
+    B = _normal((Ln, S, N, R), 0.0, 1.0, g, device, io)
+    C = _normal((Ln, S, N, R), 0.0, 1.0, g, device, io)
+    return {"x": x, "dt": dt, "z": z, "B": B, "C": C}
