@@ -31,6 +31,8 @@ independent) from several host threads.
 x is the input of the MambaBlock's causal depthwise convolution (--conv-k taps,
 default 4) and dt the raw dt projection output, and the convolution + silu and
 softplus run inside the scan's load stage (decode: with the carried conv state).
+--trap times the exponential-trapezoidal entry points, --mimo R the MIMO ones (rank-R
+inputs and outputs per channel; elements stay channel-steps, each with R outputs).
 """
 from __future__ import annotations
 
@@ -56,6 +58,8 @@ KERNEL_SOURCES = {
     "complex": [CSRC + "scan_complex.hip"],
     "step": [CSRC + "step.hip", CSRC + "ssm_input_stage.h"],
     "bwd": [CSRC + "scan_bwd.hip", CSRC + "scan_real.hip", CSRC + "ssm_input_stage.h"],
+    "mimo": [CSRC + "scan_mimo.hip", CSRC + "scan_real.hip"],
+    "mimo_step": [CSRC + "scan_mimo.hip"],
 }
 
 
@@ -102,6 +106,37 @@ def trap_lane_ops(N: int) -> float:
     state one more fused multiply-add (the previous input term), per element w = dt/2,
     w x_prev and w x in place of dt x (two more)."""
     return N + 2
+
+
+def mimo_prefill_bytes(s, io_bytes: int, R: int) -> float:
+    """MIMO prefill: x, (z), y of R elements per channel-step, dt of one, B and C of N x R
+    per step, A, D, h_final; each read or written once."""
+    b, L, Dn, N = s.batch, s.L, s.d_inner, s.d_state
+    streams = R * (2 + (1 if s.gated else 0)) + 1
+    return (b * L * Dn * streams * io_bytes + 2 * b * L * N * R * io_bytes
+            + Dn * N * 4 + Dn * 4 + b * Dn * N * 4)
+
+
+def mimo_lane_ops(s, R: int) -> float:
+    """VALU instructions per channel-step of the MIMO update (one lane per channel). Per
+    state: dt*A, exp, the R-term sum B x (one multiply, R-1 fused multiply-adds), the
+    state's fused multiply-add, and R output fused multiply-adds = 3 + 2R. Per
+    channel-step: dt*x[r] and D x[r] + acc[r] (2R); with bf16 I/O the widening of x and
+    dt and the output conversion (2R + 1); gated: the gate per output (6R) and, with
+    bf16, the widening of z (R). R = 1 gives prefill_lane_ops."""
+    bf16 = s.io == "bf16"
+    per_elem = 2 * R + ((2 * R + 1) if bf16 else 0)
+    if s.gated:
+        per_elem += 6 * R + (R if bf16 else 0)
+    return s.d_state * (3 + 2 * R) + per_elem
+
+
+def mimo_decode_bytes(s, io_bytes: int, R: int) -> float:
+    """MIMO decode token for all layers: state read + write, x, (z), y of R elements and
+    dt per channel, B and C of N x R per (layer, sequence), A, D."""
+    Ln, S, Dn, N = s.n_layers, s.n_seq, s.d_inner, s.d_state
+    return (Ln * S * Dn * N * 4 * 2 + Ln * S * Dn * (R * (2 + (1 if s.gated else 0)) + 1) * io_bytes
+            + 2 * Ln * S * N * R * io_bytes + Ln * Dn * (N + 1) * 4)
 
 
 def input_stage_bytes(s, io_bytes: int, K: int) -> float:
@@ -203,12 +238,14 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     return info, d
 
 
-def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None, trap=False):
+def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None, trap=False,
+                mimo=0):
     """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter.
-    trap: ssm_scan_fwd_trap (exponential-trapezoidal), with an input before step 0."""
+    trap: ssm_scan_fwd_trap (exponential-trapezoidal), with an input before step 0.
+    mimo R > 0: ssm_scan_fwd_mimo with rank-R projections."""
     dev = "cuda"
     log("drawing inputs for", shape.name)
-    d = workloads.make_scan_inputs(shape, dev)
+    d = workloads.make_mimo_inputs(shape, mimo, dev) if mimo else workloads.make_scan_inputs(shape, dev)
     if trap:
         d.update(workloads.make_prev_input(shape.batch, shape.d_inner, shape.d_state, shape.io, dev))
     fused = conv_k is not None
@@ -219,8 +256,12 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     cplx = shape.complex_state
     y = torch.empty_like(d["x"])
     hf = torch.empty((b, Dn, N) + ((2,) if cplx else ()), dtype=torch.float32, device=dev)
-    T = chunk_len or ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N)
+    T = chunk_len or (ssm.ssm_scan_fwd_c64_chunk_len(b, L, Dn, N) if cplx
+                      else ssm.ssm_scan_fwd_mimo_chunk_len(b, L, Dn, N, mimo) if mimo
+                      else ssm.ssm_scan_fwd_fused_chunk_len(b, L, Dn, N) if fused
+                      else ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N))
     ws_n = (ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, T) if cplx
+            else ssm.ssm_scan_fwd_mimo_workspace(b, L, Dn, N, mimo, T) if mimo
             else ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, N, T))
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     fn = ssm.ssm_scan_fwd_c64_profiled if cplx else ssm.ssm_scan_fwd_profiled
@@ -245,6 +286,10 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
             ssm.ssm_scan_fwd_trap(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
                                   d["x_prev"], d["B_prev"], y=y, h_final=hf, workspace=ws,
                                   chunk_len=T, events=[e.cuda_event for e in events])
+        elif mimo:
+            ssm.ssm_scan_fwd_mimo(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
+                                  y=y, h_final=hf, workspace=ws, chunk_len=T,
+                                  events=[e.cuda_event for e in events])
         else:
             fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None, y=y, h_final=hf,
                workspace=ws, chunk_len=T, events=[e.cuda_event for e in events])
@@ -276,26 +321,31 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     if trap:
         nbytes += shape.batch * (shape.d_inner + shape.d_state) * io_bytes   # x_prev, B_prev
         lane_ops += trap_lane_ops(shape.d_state)
+    if mimo:
+        nbytes = mimo_prefill_bytes(shape, io_bytes, mimo)
+        lane_ops = mimo_lane_ops(shape, mimo)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": phases,
         "elements_per_step": elems, "bytes_per_step": nbytes,
         "lane_ops_per_elem": lane_ops, "chunk_len": T,
         "n_chunks": -(-L // T), "dominant_ms": phases["rescan"], "gpu_ms": gpu_ms,
-        "kernel": "k_chunk_scan_c" if cplx else "k_chunk_scan",
-        "source": "complex" if cplx else "real",
+        "kernel": "k_chunk_scan_c" if cplx else "k_mimo_scan" if mimo else "k_chunk_scan",
+        "source": "complex" if cplx else "mimo" if mimo else "real",
     }
     return info, d
 
 
-def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None, trap=False):
+def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None, trap=False,
+               mimo=0):
     """conv_k None: ssm_step; else ssm_step_fused with a conv_k-tap filter. trap:
-    ssm_step_trap, given the previous token's x and B."""
+    ssm_step_trap, given the previous token's x and B. mimo R > 0: ssm_step_mimo."""
     dev = "cuda"
     Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
     par = workloads.make_decode_params(shape, dev)
     h = torch.zeros((Ln, S, Dn, N), device=dev)
     log("drawing", warmup + steps, "token steps of inputs")
-    toks = [workloads.make_decode_step(shape, k, dev) for k in range(warmup + steps)]
+    toks = [workloads.make_mimo_decode_step(shape, mimo, k, dev) if mimo
+            else workloads.make_decode_step(shape, k, dev) for k in range(warmup + steps)]
     fused = conv_k is not None
     if fused:
         ist = workloads.make_decode_input_stage(shape, conv_k, dev)
@@ -303,7 +353,7 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
             t["dt"] = workloads.make_decode_dt_raw(shape, k, dev)
         sl = lambda v, l: None if v is None else v[l:l + 1]
         ist_l = [{k: sl(v, l) for k, v in ist.items()} for l in range(Ln)]
-    y = torch.empty((Ln, S, Dn), dtype=toks[0]["x"].dtype, device=dev)
+    y = torch.empty(tuple(toks[0]["x"].shape), dtype=toks[0]["x"].dtype, device=dev)
     A_l = [par["A"][l:l + 1] for l in range(Ln)]
     D_l = [par["D"][l:l + 1] for l in range(Ln)]
     h_l = [h[l:l + 1] for l in range(Ln)]
@@ -325,6 +375,9 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
                 pv = per_layer[(k - 1) * Ln + l] if k > 0 else {"x": None, "B": None}
                 ssm.ssm_step_trap(h_l[l], pv["x"], pv["B"], t["x"], t["dt"], A_l[l], t["B"], t["C"],
                                   D_l[l], t["z"], y_t=y[l:l + 1])
+            elif mimo:
+                ssm.ssm_step_mimo(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
+                                  y_t=y[l:l + 1])
             else:
                 ssm.ssm_step(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
                              y_t=y[l:l + 1])
@@ -377,11 +430,15 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
     if trap:
         nbytes += Ln * S * (Dn + N) * io_bytes   # the previous token's x and B
         lane_ops += trap_lane_ops(N)
+    if mimo:
+        nbytes = mimo_decode_bytes(shape, io_bytes, mimo)
+        lane_ops = mimo_lane_ops(shape, mimo)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3,
         "elements_per_step": Ln * S * Dn, "bytes_per_step": nbytes,
         "lane_ops_per_elem": lane_ops, "dominant_ms": kern * Ln, "per_call_ms": kern,
-        "kernel": "k_step", "source": "step", "phases_ms": {"ssm_step_per_layer": kern},
+        "kernel": "k_mimo_step" if mimo else "k_step", "source": "mimo_step" if mimo else "step",
+        "phases_ms": {"ssm_step_per_layer": kern},
         "graph": graph,
     }
     return info, None
@@ -410,10 +467,10 @@ def sample_width(shape, elems):
     return max(1, min(shape.d_inner, -(-elems // (shape.batch * max(shape.L, 1)))))
 
 
-def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False):
+def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False, mimo=0):
     import oracle
     oracle.build(force=False)
-    k = sample_width(shape, CPU_SAMPLE_ELEMS // (4 if shape.complex_state else 1))
+    k = sample_width(shape, CPU_SAMPLE_ELEMS // (4 if shape.complex_state else max(1, mimo)))
     idx = workloads.sample_channels(shape.d_inner, k, seed=5).to("cuda")
     g = lambda t: None if t is None else t.index_select(2, idx).cpu()
     args = (g(d["x"]), g(d["dt"]), d["A"].index_select(0, idx).cpu(), d["B"].cpu(), d["C"].cpu(),
@@ -428,18 +485,21 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False):
                               g(d["conv_state0"]))[0] if conv_k else args[0])
         dts = oracle.softplus(g(d["dt_raw"]), sel(d["dt_bias"]))
         args = (u, dts) + args[2:]
-    if trap:
+    if trap or mimo:
         import threading
         import numpy as np
-        xp = oracle.to_f64(d["x_prev"].index_select(1, idx).cpu())
-        Bq = oracle.to_f64(d["B_prev"].cpu())
+        xp = oracle.to_f64(d["x_prev"].index_select(1, idx).cpu()) if trap else None
+        Bq = oracle.to_f64(d["B_prev"].cpu()) if trap else None
         f = [oracle.to_f64(a) for a in args]
         parts = [p for p in np.array_split(np.arange(k), threads) if len(p)]
 
         def work(p):
             sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, p])
-            oracle.scan_trap(sub(f[0]), sub(f[1]), f[2][p], f[3], f[4], f[5][p], sub(f[6]),
-                             x_prev=np.ascontiguousarray(xp[:, p]), B_prev=Bq)
+            if mimo:
+                oracle.scan_mimo(sub(f[0]), sub(f[1]), f[2][p], f[3], f[4], f[5][p], sub(f[6]))
+            else:
+                oracle.scan_trap(sub(f[0]), sub(f[1]), f[2][p], f[3], f[4], f[5][p], sub(f[6]),
+                                 x_prev=np.ascontiguousarray(xp[:, p]), B_prev=Bq)
         t0 = time.perf_counter()
         ts = [threading.Thread(target=work, args=(p,)) for p in parts]
         for t in ts: t.start()
@@ -451,7 +511,8 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False):
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{k} of {shape.d_inner} channels over all {shape.L} steps x batch "
                       f"{shape.batch} ({elems} elements, {dt:.1f} s wall), fp64 sequential loop "
-                      f"per channel{' (exponential-trapezoidal)' if trap else ''}, channels split "
+                      f"per channel{' (exponential-trapezoidal)' if trap else ''}"
+                      f"{f' (MIMO, rank {mimo})' if mimo else ''}, channels split "
                       f"over {threads} threads"}
 
 
@@ -490,7 +551,8 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
                       f"{len(parts)} threads"}
 
 
-def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=192, trap=False):
+def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=192, trap=False,
+                        mimo=0):
     """The oracle's decode step (or, with conv_k, its fused step) for every layer on the
     first `seqs` sequences, `tokens` tokens in a row with the state carried, the layers
     split over host threads. Inputs are drawn once; the timed region is the oracle."""
@@ -501,7 +563,10 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
     Ln, Dn, N = shape.n_layers, shape.d_inner, shape.d_state
     S = min(seqs, shape.n_seq)
     par = workloads.make_decode_params(shape, "cpu")
-    tok = workloads.make_decode_step(shape, 0, "cpu")
+    tok = (workloads.make_mimo_decode_step(shape, mimo, 0, "cpu") if mimo
+           else workloads.make_decode_step(shape, 0, "cpu"))
+    if mimo:
+        tokens = max(24, tokens // mimo)
     sl = lambda t: None if t is None else np.ascontiguousarray(oracle.to_f64(t[:, :S]))
     x, z, B, C = sl(tok["x"]), sl(tok["z"]), sl(tok["B"]), sl(tok["C"])
     A, D = oracle.to_f64(par["A"]), oracle.to_f64(par["D"])
@@ -529,6 +594,8 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
                 _, hh, cc = oracle.step_fused(hh, cc, x[r], dt[r], A[r], B[r], C[r], D[r], z if z is None else z[r],
                                               conv_w=cw[r], conv_b=None if cb is None else cb[r],
                                               dt_bias=None if db is None else db[r])
+            elif mimo:
+                _, hh = oracle.step_mimo(hh, x[r], dt[r], A[r], B[r], C[r], D[r], None if z is None else z[r])
             elif trap:  # the same token's x and B stand in for the previous token's
                 _, hh = oracle.step_trap(hh, x[r], B[r], x[r], dt[r], A[r], B[r], C[r], D[r],
                                          None if z is None else z[r])
@@ -542,7 +609,8 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
     dtm = time.perf_counter() - t0
     elems = Ln * S * Dn * tokens
     what = ("fused decode step (conv + silu, softplus, scan)" if fused else
-            "exponential-trapezoidal decode step" if trap else "decode step")
+            "exponential-trapezoidal decode step" if trap else
+            f"MIMO decode step (rank {mimo})" if mimo else "decode step")
     return {"value": elems / dtm, "unit": "elements/s", "cores": len(groups), "kind": "oracle",
             "sample": f"{what}: all {Ln} layers x {S} of {shape.n_seq} sequences x {Dn} channels, "
                       f"{tokens} tokens (token 0's inputs each time) with the state carried ({elems} "
@@ -569,6 +637,9 @@ def main():
     ap.add_argument("--conv-k", type=int, default=4, help="filter taps with --fused (0..4)")
     ap.add_argument("--trap", action="store_true",
                     help="the exponential-trapezoidal entry points (ssm_scan_fwd_trap, ssm_step_trap)")
+    ap.add_argument("--mimo", type=int, default=0, metavar="R",
+                    help="the MIMO entry points (ssm_scan_fwd_mimo, ssm_step_mimo) with rank R "
+                         "(1, 2, 4 or 8)")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (gradients of the prefill) on the prefill workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -605,9 +676,15 @@ def main():
         print("--trap applies to the real-state prefill and decode workloads, without --fused "
               "or --backward", file=sys.stderr)
         sys.exit(2)
+    if args.mimo and (args.mimo not in (1, 2, 4, 8) or args.fused or args.backward or args.trap
+                      or shape.complex_state):
+        print("--mimo R (R in 1, 2, 4, 8) applies to the real-state prefill and decode workloads, "
+              "without --fused, --backward or --trap", file=sys.stderr)
+        sys.exit(2)
     if is_decode:
         info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph,
-                             conv_k=args.conv_k if args.fused else None, trap=args.trap)
+                             conv_k=args.conv_k if args.fused else None, trap=args.trap,
+                             mimo=args.mimo)
     else:
         if args.backward and (shape.complex_state or args.fused):
             print("--backward applies to the real-state prefill workloads", file=sys.stderr)
@@ -620,7 +697,7 @@ def main():
             info, d = run_backward(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
         else:
             info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
-                                  conv_k, trap=args.trap)
+                                  conv_k, trap=args.trap, mimo=args.mimo)
 
     elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
     dom_s = info["dominant_ms"] / 1e3
@@ -628,7 +705,8 @@ def main():
     alu_ach = info["elements_per_step"] * info["lane_ops_per_elem"] / dom_s / 1e12
     hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
     traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "") + \
-        ("+backward" if args.backward else "") + ("+trap" if args.trap else "")
+        ("+backward" if args.backward else "") + ("+trap" if args.trap else "") + \
+        (f"+mimo{args.mimo}" if args.mimo else "")
     traffic = traffic_for(info, traffic_key)
     if hbm_frac >= alu_frac:
         roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
@@ -653,6 +731,9 @@ def main():
                                   "softplus_dt": True, "entry_point": "ssm_step_fused"}
         if args.trap:
             cfg["discretisation"] = "exponential-trapezoidal (ssm_step_trap)"
+        if args.mimo:
+            cfg["mimo_rank"] = args.mimo
+            cfg["entry_point"] = "ssm_step_mimo"
     else:
         cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
@@ -665,6 +746,9 @@ def main():
             cfg["pass"] = "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)"
         if args.trap:
             cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
+        if args.mimo:
+            cfg["mimo_rank"] = args.mimo
+            cfg["entry_point"] = "ssm_scan_fwd_mimo"
     out = {
         "metric": METRIC, "value": round(elems_s, 1), "unit": "elements/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(info["ms_per_step"], 4),
@@ -674,17 +758,22 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
         "roofline": roof,
     }
+    if args.mimo:
+        # each element (channel-step) has R inputs and R outputs
+        out["mimo_outputs_per_s"] = round(elems_s * args.mimo, 1)
     if not args.no_cpu_baseline and is_decode and not shape.complex_state:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline_decode(shape, workloads, threads,
-                                                  args.conv_k if args.fused else None, trap=args.trap)
+                                                  args.conv_k if args.fused else None, trap=args.trap,
+                                                  mimo=args.mimo)
     elif not args.no_cpu_baseline and not is_decode:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         if args.backward:
             out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads)
         else:
             out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
-                                               args.conv_k if args.fused else None, trap=args.trap)
+                                               args.conv_k if args.fused else None, trap=args.trap,
+                                               mimo=args.mimo)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -114,8 +114,18 @@ ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const 
                            ssm_dtype io, int64_t chunk_len, void *workspace,
                            size_t workspace_bytes, void *hip_stream);
 
-/* The chunk length ssm_scan_fwd picks for this shape (a pure host function). */
+/* The chunk length each prefill entry point picks for this shape with chunk_len = 0
+ * (pure host functions; 0 for an invalid shape). The library cuts the sequence into
+ * enough chunks to keep as many waves per SIMD resident as the entry point's rescan
+ * kernel is compiled for: 5 for ssm_scan_fwd / _ex / _trap and ssm_scan_fwd_mimo up to
+ * rank 4, 4 for ssm_scan_fwd_fused, ssm_scan_fwd_c64 and rank 8 (and the backward).
+ * A plan with fewer chunks needs no more workspace, so ssm_scan_fwd_workspace_ex(...,
+ * 0) also suffices for ssm_scan_fwd_fused. */
 int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
+int64_t ssm_scan_fwd_fused_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
+int64_t ssm_scan_fwd_c64_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
+int64_t ssm_scan_fwd_mimo_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                    int32_t rank);
 
 /* ------------------------------------------------------------------ decode
  * ssm_step: one token for every (layer, sequence, channel); h -> h' in place.
@@ -206,7 +216,8 @@ ssm_status ssm_step_c64_replay(float *h, const void *x_t, const void *dt_t, cons
  * ssm_scan_fwd_fused: prefill. conv_state0 NULL = zeros before step 0 (the page's
  * padding). conv_state_out NULL = not wanted; else it receives the last conv_k-1
  * inputs (from conv_state0 where L < conv_k-1). workspace: ssm_scan_fwd_workspace_ex
- * bytes for the same shape and chunk_len. With conv_k > 1, y must not overlap x_in
+ * bytes for the same shape and chunk_len (enough for its own plan when chunk_len is 0:
+ * see ssm_scan_fwd_fused_chunk_len). With conv_k > 1, y must not overlap x_in
  * (a chunk reads the previous chunk's last inputs), and conv_state_out must not
  * overlap x_in or conv_state0: SSM_ERR_UNSUPPORTED otherwise. L == 0 writes
  * h_final = h0 and conv_state_out = conv_state0 (or zeros). */

@@ -26,7 +26,8 @@ __all__ = [
     "ssm_scan_bwd", "ssm_scan_bwd_workspace",
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
-    "ssm_step_mimo",
+    "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
+    "ssm_scan_fwd_mimo_chunk_len",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +46,8 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_bwd", "ssm_scan_bwd_workspace",
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
-    "ssm_step_mimo",
+    "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
+    "ssm_scan_fwd_mimo_chunk_len",
 ]
 
 
@@ -78,6 +80,9 @@ def load_library():
         "ssm_scan_fwd_workspace_ex": ([i64, i64, i64, i32, i64], sz),
         "ssm_scan_fwd_c64_workspace": ([i64, i64, i64, i32, i64], sz),
         "ssm_scan_fwd_chunk_len": ([i64, i64, i64, i32], i64),
+        "ssm_scan_fwd_fused_chunk_len": ([i64, i64, i64, i32], i64),
+        "ssm_scan_fwd_c64_chunk_len": ([i64, i64, i64, i32], i64),
+        "ssm_scan_fwd_mimo_chunk_len": ([i64, i64, i64, i32, i32], i64),
         "ssm_scan_fwd": (scan + [vp, sz, vp], ci),
         "ssm_scan_fwd_ex": (scan + [i64, vp, sz, vp], ci),
         "ssm_scan_fwd_c64": (scan + [i64, vp, sz, vp], ci),
@@ -181,6 +186,18 @@ def ssm_scan_fwd_c64_workspace(batch, L, d_inner, d_state, chunk_len=0) -> int:
 
 def ssm_scan_fwd_chunk_len(batch, L, d_inner, d_state) -> int:
     return int(load_library().ssm_scan_fwd_chunk_len(batch, L, d_inner, d_state))
+
+
+def ssm_scan_fwd_fused_chunk_len(batch, L, d_inner, d_state) -> int:
+    return int(load_library().ssm_scan_fwd_fused_chunk_len(batch, L, d_inner, d_state))
+
+
+def ssm_scan_fwd_c64_chunk_len(batch, L, d_inner, d_state) -> int:
+    return int(load_library().ssm_scan_fwd_c64_chunk_len(batch, L, d_inner, d_state))
+
+
+def ssm_scan_fwd_mimo_chunk_len(batch, L, d_inner, d_state, rank) -> int:
+    return int(load_library().ssm_scan_fwd_mimo_chunk_len(batch, L, d_inner, d_state, rank))
 
 
 # ------------------------------------------------------------------ prefill

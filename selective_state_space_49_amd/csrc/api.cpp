@@ -38,16 +38,30 @@ bool valid_rank(int32_t r) { return r == 1 || r == 2 || r == 4 || r == 8; }
 
 size_t io_bytes(ssm_dtype io) { return io == SSM_BF16 ? 2 : 4; }
 
-// Waves wanted per launch for the chunk rescan: about four per SIMD on 256 CUs.
-constexpr int64_t kTargetWaves = 4096;
+// Waves wanted per launch for the chunk rescan: as many as the rescan kernel is
+// compiled to keep resident per SIMD, on 1024 SIMDs (256 CUs). One wave more than a
+// round holds would start a second, mostly idle round, so the count must not exceed it.
+constexpr int64_t kSimds = 1024;
+constexpr int64_t kTargetWaves = 4 * kSimds;
+
+// Waves per SIMD each rescan is compiled for (its __launch_bounds__ minimum, or what
+// its registers allow).
+enum class Family { Plain, Fused, Complex, Mimo, Backward };
+int32_t waves_per_simd(Family f, int32_t rank = 1) {
+    switch (f) {
+        case Family::Plain: return 5;     // plain and exponential-trapezoidal rescans
+        case Family::Mimo: return rank <= 4 ? 5 : 4;
+        default: return 4;                // input stage, complex state, backward
+    }
+}
 constexpr int64_t kMinChunk = 64;       // shortest chunk the planner picks
 constexpr int64_t kMaxChunks = 65535;   // grid y limit
 constexpr size_t kWsAlign = 256;
 
-int64_t auto_chunk_len(int64_t batch, int64_t L, int64_t d_inner) {
+int64_t auto_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int64_t target_waves = kTargetWaves) {
     if (L <= 0) return 1;
     const int64_t waves_per_chunk = std::max<int64_t>(1, batch * ((d_inner + 63) / 64));
-    int64_t chunks = (kTargetWaves + waves_per_chunk - 1) / waves_per_chunk;
+    int64_t chunks = (target_waves + waves_per_chunk - 1) / waves_per_chunk;
     chunks = std::min(chunks, (L + kMinChunk - 1) / kMinChunk);
     chunks = std::max<int64_t>(chunks, 1);
     return (L + chunks - 1) / chunks;
@@ -59,8 +73,11 @@ struct Plan {
     size_t ws_bytes;
 };
 
+// waves_per_simd: what the rescan of the entry point is compiled for (5 for the plain,
+// trapezoidal and MIMO rescans up to rank 4; 4 for the input stage, the complex state,
+// MIMO rank 8 and the backward's own plan).
 ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, int64_t chunk_len,
-                     bool cplx, Plan *p, int32_t rank = 1) {
+                     bool cplx, Plan *p, int32_t rank = 1, int32_t waves_per_simd = 4) {
     if (batch < 0 || L < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "batch/L must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
     if (chunk_len < 0) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be >= 0");
@@ -73,7 +90,7 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
     // (MIMO rows of x, z and y hold rank elements per channel.)
     const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 31) / (d_inner * rank * 4) - 1);
     int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
-                              : auto_chunk_len(batch, L, d_inner);
+                              : auto_chunk_len(batch, L, d_inner, waves_per_simd * kSimds);
     T = std::min(T, cap);
     const int64_t n_chunks = L > 0 ? (L + T - 1) / T : 1;
     if (n_chunks > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n_chunks, (long long)kMaxChunks);
@@ -130,7 +147,9 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     const bool mimo = rank != 0;
     if (mimo && !valid_rank(rank)) return fail(SSM_ERR_UNSUPPORTED, "rank %d not in {1,2,4,8}", rank);
     Plan plan;
-    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan, mimo ? rank : 1);
+    const Family fam = cplx ? Family::Complex : in ? Family::Fused : mimo ? Family::Mimo : Family::Plain;
+    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan, mimo ? rank : 1,
+                              waves_per_simd(fam, rank));
     if (st != SSM_OK) return st;
     const bool work = batch > 0 && L > 0;
     if (work && (!x || !dt || !A || !B || !C || !D || !y))
@@ -312,7 +331,8 @@ size_t ws_round(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 ssm_status make_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
                          int64_t chunk_len, BwdPlan *p) {
-    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, false, &p->fwd);
+    ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, false, &p->fwd, 1,
+                              waves_per_simd(Family::Backward));
     if (st != SSM_OK) return st;
     if (p->fwd.n_chunks > 1) {
         int64_t T = p->fwd.T / ssm::kSub * ssm::kSub;
@@ -413,20 +433,49 @@ size_t ssm_scan_fwd_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t
 size_t ssm_scan_fwd_workspace_ex(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
                                  int64_t chunk_len) {
     Plan p;
-    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p) != SSM_OK) return 0;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p, 1,
+                  waves_per_simd(Family::Plain)) != SSM_OK)
+        return 0;
     return p.ws_bytes;
 }
 
 size_t ssm_scan_fwd_c64_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
                                   int64_t chunk_len) {
     Plan p;
-    if (make_plan(batch, L, d_inner, d_state, chunk_len, true, &p) != SSM_OK) return 0;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, true, &p, 1,
+                  waves_per_simd(Family::Complex)) != SSM_OK)
+        return 0;
     return p.ws_bytes;
 }
 
 int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state) {
     Plan p;
-    if (make_plan(batch, L, d_inner, d_state, 0, false, &p) != SSM_OK) return 0;
+    if (make_plan(batch, L, d_inner, d_state, 0, false, &p, 1, waves_per_simd(Family::Plain)) != SSM_OK)
+        return 0;
+    return p.T;
+}
+
+int64_t ssm_scan_fwd_fused_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state) {
+    Plan p;
+    if (make_plan(batch, L, d_inner, d_state, 0, false, &p, 1, waves_per_simd(Family::Fused)) != SSM_OK)
+        return 0;
+    return p.T;
+}
+
+int64_t ssm_scan_fwd_c64_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state) {
+    Plan p;
+    if (make_plan(batch, L, d_inner, d_state, 0, true, &p, 1, waves_per_simd(Family::Complex)) != SSM_OK)
+        return 0;
+    return p.T;
+}
+
+int64_t ssm_scan_fwd_mimo_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                    int32_t rank) {
+    Plan p;
+    if (!valid_rank(rank)) return 0;
+    if (make_plan(batch, L, d_inner, d_state, 0, false, &p, rank,
+                  waves_per_simd(Family::Mimo, rank)) != SSM_OK)
+        return 0;
     return p.T;
 }
 
@@ -615,7 +664,9 @@ size_t ssm_scan_fwd_mimo_workspace(int64_t batch, int64_t L, int64_t d_inner, in
                                    int32_t rank, int64_t chunk_len) {
     Plan p;
     if (!valid_rank(rank)) return 0;
-    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p, rank) != SSM_OK) return 0;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p, rank,
+                  waves_per_simd(Family::Mimo, rank)) != SSM_OK)
+        return 0;
     return p.ws_bytes;
 }
 

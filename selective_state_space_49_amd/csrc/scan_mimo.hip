@@ -140,27 +140,53 @@ __device__ __forceinline__ VecRaw<IO, R> ld_vec(const IO *p) {
     return v;
 }
 
+// Stores y[0..R), rounded to the element type, with one vector store (two for 32 bytes).
 template <typename IO, int R>
 __device__ __forceinline__ void st_vec(IO *p, const float (&y)[R]) {
+    VecRaw<IO, R> v;
     if constexpr (sizeof(IO) == 2) {
         if constexpr (R == 1) {
             *(uint16_t *)p = f32_to_bf16(y[0]);
+            return;
         } else {
 #pragma unroll
             for (int k = 0; k < R / 2; ++k)
-                ((uint32_t *)p)[k] = (uint32_t)f32_to_bf16(y[2 * k]) | ((uint32_t)f32_to_bf16(y[2 * k + 1]) << 16);
+                v.w[k] = (uint32_t)f32_to_bf16(y[2 * k]) | ((uint32_t)f32_to_bf16(y[2 * k + 1]) << 16);
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < R; ++k) ((float *)p)[k] = y[k];
+        for (int k = 0; k < R; ++k) v.w[k] = __float_as_uint(y[k]);
     }
+    constexpr int B = VecRaw<IO, R>::kBytes;
+    if constexpr (B == 4) {
+        *(uint32_t *)p = v.w[0];
+    } else if constexpr (B == 8) {
+        const u32x2 t = {v.w[0], v.w[1]};
+        *(u32x2 *)p = t;
+    } else {
+#pragma unroll
+        for (int h = 0; h < B / 16; ++h) {
+            const u32x4 t = {v.w[4 * h], v.w[4 * h + 1], v.w[4 * h + 2], v.w[4 * h + 3]};
+            *((u32x4 *)p + h) = t;
+        }
+    }
+}
+
+// The input term of state n at row element e = e0 + n R: u = sum_r B[n][r] xd[r] with
+// xd = dt x, as u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u) for r = 1 .. R-1.
+template <int R, typename Row>
+__device__ __forceinline__ float mimo_input(const Row &Bp, int64_t e, const float (&xd)[R]) {
+    float u = Bp.ld(e) * xd[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) u = __builtin_fmaf(Bp.ld(e + r), xd[r], u);
+    return u;
 }
 
 // One step of one channel, in the fixed order that the prefill rescan and the decode
 // step share (so that L decode steps equal a one-chunk prefill bit for bit):
-//     xd[r] = dt x[r];  for n ascending:
-//         u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u) for r = 1 .. R-1;
-//         h[n] = fma(e2(dt A[n] log2 e), h[n], u);  acc[r] = fma(C[n][r], h[n], acc[r])
+//     xd[r] = dt x[r];  for n ascending: u = mimo_input(n);
+//     h[n] = fma(e2(dt A[n] log2 e), h[n], u);  acc[r] = fma(C[n][r], h[n], acc[r])
+//     (r ascending, acc from 0)
 // Row reads element e0 + n R + r of the step's B (and C) through the scalar unit.
 template <int N, int R, typename Row>
 __device__ __forceinline__ void mimo_update(float (&h)[N], const float (&A2)[N], float dv,
@@ -175,9 +201,7 @@ __device__ __forceinline__ void mimo_update(float (&h)[N], const float (&A2)[N],
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         const int64_t e = e0 + n * R;
-        float u = Bp.ld(e) * xd[0];
-#pragma unroll
-        for (int r = 1; r < R; ++r) u = __builtin_fmaf(Bp.ld(e + r), xd[r], u);
+        const float u = mimo_input<R>(Bp, e, xd);
         h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u);
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
@@ -318,9 +342,7 @@ __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
         for (int r = 0; r < R; ++r) xd[r] = dv * xr.at(r);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            float u = Bp.ld((t * N + n) * R) * xd[0];
-#pragma unroll
-            for (int r = 1; r < R; ++r) u = __builtin_fmaf(Bp.ld((t * N + n) * R + r), xd[r], u);
+            const float u = mimo_input<R>(Bp, (t * N + n) * R, xd);
             h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u);
         }
     });
@@ -334,8 +356,14 @@ __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------- rescan + epilogue
+// Waves per SIMD the rescan is compiled for: 5 up to rank 4 (the planner then cuts
+// the sequence into enough chunks for 5 waves on every SIMD). Rank 8 is left to the
+// compiler (4 waves with bf16 inputs, 3 with fp32 and a gate, whose registers would
+// otherwise spill).
+template <int R> constexpr int kMimoWavesPerSimd = R <= 4 ? 5 : 1;
+
 template <typename IO, int N, int R, bool GATED>
-__global__ __launch_bounds__(256) void k_mimo_scan(ScanArgs a) {
+__global__ __launch_bounds__(256, kMimoWavesPerSimd<R>) void k_mimo_scan(ScanArgs a) {
     const LaneId ln = lane_id(a);
     if (ln.d >= a.Dn) return;
     const int c = blockIdx.y;
@@ -380,56 +408,101 @@ __global__ __launch_bounds__(256) void k_mimo_scan(ScanArgs a) {
 // One token for every (layer, sequence, channel). One lane per channel holds the
 // channel's N states; B_t and C_t are one row per (layer, sequence), the same for the
 // whole block (grid y = sequence, z = layer), so they come in through the scalar unit.
-// The state is read and written once, with streaming 16-byte accesses.
+// A block's 256 channels own one contiguous run of state: it is moved between HBM and
+// LDS with coalesced, streaming 16-byte accesses (it is read and written once per
+// token), and each lane reads and writes its channel's row of LDS. Rows are padded to
+// P floats so that the 16 lanes of one LDS access start on distinct banks. A is read
+// per lane from its own rows: it is the same for every sequence of a layer, so those
+// reads are served by the caches (staging it through LDS as well halved the blocks
+// per CU and made the call slower: 71.7 against 57.7 us on the 28 x 256 x 8192 decode).
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-template <typename IO, int N, int R, bool GATED>
-__global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
-    const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (d >= a.Dn) return;
-    const int64_t l = blockIdx.z;
-    const int64_t lq = l * a.n_seq + blockIdx.y;
-    const int64_t ch = lq * a.Dn + d;
-    float *hp = a.h + ch * N;
-    const float *Ap = a.A + (l * a.Dn + d) * N;
-    float h[N], A2[N];
+template <int N> constexpr int kLdsRow = N == 16 ? 20 : N == 8 ? 12 : N;
+
+// dst[c * P + n] = src[c * N + n] for the block's nch channels (thread tid of 256),
+// streaming loads.
+template <int N>
+__device__ __forceinline__ void rows_to_lds(float *dst, const float *src, int nch, int tid) {
+    constexpr int P = kLdsRow<N>;
     if constexpr (N % 4 == 0) {
 #pragma unroll
-        for (int n = 0; n < N; n += 4) {
-            const f4v q = __builtin_nontemporal_load((const f4v *)(hp + n));
-            const f4v w = *(const f4v *)(Ap + n);
-            h[n] = q.x; h[n + 1] = q.y; h[n + 2] = q.z; h[n + 3] = q.w;
-            A2[n] = w.x; A2[n + 1] = w.y; A2[n + 2] = w.z; A2[n + 3] = w.w;
+        for (int j = 0; j < N / 4; ++j) {
+            const int v = tid + 256 * j;  // float4 index in the block's run
+            if (v < nch * (N / 4)) {
+                const f4v q = __builtin_nontemporal_load((const f4v *)src + v);
+                const int c = (4 * v) / N, n = (4 * v) % N;
+                *(f4v *)(dst + c * P + n) = q;
+            }
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) { h[n] = hp[n]; A2[n] = Ap[n]; }
+        for (int j = 0; j < N; ++j) {
+            const int e = tid + 256 * j;
+            if (e < nch * N) dst[(e / N) * P + e % N] = src[e];
+        }
     }
+}
+
+// dst[c * N + n] = src[c * P + n], streaming stores.
+template <int N>
+__device__ __forceinline__ void lds_to_rows(float *dst, const float *src, int nch, int tid) {
+    constexpr int P = kLdsRow<N>;
+    if constexpr (N % 4 == 0) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] *= kLog2e;
+        for (int j = 0; j < N / 4; ++j) {
+            const int v = tid + 256 * j;
+            if (v < nch * (N / 4)) {
+                const int c = (4 * v) / N, n = (4 * v) % N;
+                __builtin_nontemporal_store(*(const f4v *)(src + c * P + n), (f4v *)dst + v);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int e = tid + 256 * j;
+            if (e < nch * N) dst[e] = src[(e / N) * P + e % N];
+        }
+    }
+}
+
+template <typename IO, int N, int R, bool GATED>
+__global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
+    constexpr int P = kLdsRow<N>;
+    __shared__ __attribute__((aligned(16))) float sh[256 * P];  // the block's states
+    const int tid = (int)threadIdx.x;
+    const int64_t d0 = (int64_t)blockIdx.x * 256;
+    const int nch = (int)min((int64_t)256, a.Dn - d0);  // channels of this block
+    const int64_t l = blockIdx.z;
+    const int64_t lq = l * a.n_seq + blockIdx.y;
+    const bool live = tid < nch;
+    const int64_t d = d0 + (live ? tid : nch - 1);
+    const int64_t ch = lq * a.Dn + d;
+    // the lane's own token inputs first, then the block's state and A through LDS
     const VecRaw<IO, R> xr = ld_vec<IO, R>((const IO *)a.x + ch * R);
     VecRaw<IO, R> zr{};
     if (GATED) zr = ld_vec<IO, R>((const IO *)a.z + ch * R);
     const float dv = Io<IO>::ld((const IO *)a.dt + ch);
     const float Dd = a.D[l * a.Dn + d];
+    float *hblk = a.h + (lq * a.Dn + d0) * N;
+    rows_to_lds<N>(sh, hblk, nch, tid);
+    float h[N], A2[N];
+    const float *Ap = a.A + (l * a.Dn + d) * N;  // shared by every sequence: cached
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = Ap[n] * kLog2e;
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = sh[tid * P + n];
     const UniRow<IO, N * R> Bp(a.B, lq * N * R), Cp(a.C, lq * N * R);
     float xv[R], acc[R], yv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
     mimo_update<N, R>(h, A2, dv, xv, Bp, Cp, 0, acc);
     mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
-    if constexpr (N % 4 == 0) {
 #pragma unroll
-        for (int n = 0; n < N; n += 4) {
-            f4v q;
-            q.x = h[n]; q.y = h[n + 1]; q.z = h[n + 2]; q.w = h[n + 3];
-            __builtin_nontemporal_store(q, (f4v *)(hp + n));
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) hp[n] = h[n];
-    }
-    st_vec<IO, R>((IO *)a.y + ch * R, yv);
+    for (int n = 0; n < N; ++n) sh[tid * P + n] = h[n];
+    if (live) st_vec<IO, R>((IO *)a.y + ch * R, yv);
+    __syncthreads();
+    lds_to_rows<N>(hblk, sh, nch, tid);
 }
 
 template <typename IO, int N, int R>

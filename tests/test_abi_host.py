@@ -57,8 +57,21 @@ def test_plan_and_workspace(lib):
         chunks = -(-L // T)
         assert 64 <= T <= L and chunks * b * (Dn // 64) >= 2048
         assert ssm.ssm_scan_fwd_workspace(b, L, Dn, 16) == ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, 16, 0)
+    # Each entry point's plan gives every one of the 1024 SIMDs as many waves as its
+    # rescan is compiled to keep: 5 (plain, trapezoidal) -> 40 chunks of the 256k
+    # sequence over its 128 channel waves; 4 (input stage) -> 32; complex: 4 x 64 waves
+    # per chunk, 4 per SIMD -> 16 chunks.
+    n_chunks = lambda L, T: -(-L // T)
+    assert n_chunks(262144, ssm.ssm_scan_fwd_chunk_len(1, 262144, 8192, 16)) == 40
+    assert n_chunks(262144, ssm.ssm_scan_fwd_fused_chunk_len(1, 262144, 8192, 16)) == 32
+    assert n_chunks(8192, ssm.ssm_scan_fwd_c64_chunk_len(4, 8192, 4096, 16)) == 16
+    assert n_chunks(4096, ssm.ssm_scan_fwd_chunk_len(2, 4096, 8192, 16)) == 20
+    Tf = ssm.ssm_scan_fwd_fused_chunk_len(1, 262144, 8192, 16)
+    assert ssm.ssm_scan_fwd_workspace_ex(1, 262144, 8192, 16, 0) >= \
+        ssm.ssm_scan_fwd_workspace_ex(1, 262144, 8192, 16, Tf) > 0
     # Invalid sizes give 0 from the query.
     assert ssm.ssm_scan_fwd_workspace(1, 10, 8, 3) == 0
+    assert ssm.ssm_scan_fwd_fused_chunk_len(1, 10, 8, 3) == 0
 
 
 def _scan_raw(lib, x=0x1000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None, h0=None,
@@ -228,14 +241,21 @@ def test_mimo_argument_errors(lib):
     assert scan(z=0x300008, R=8, io=0) == ALIGN   # fp32, rank 8: 16-byte vectors
     assert scan(B=0x1002) == ALIGN            # B, C through the scalar unit: 4 bytes
     assert scan(x=None) == NULL
-    # workspace: the chunk cap keeps a chunk's x / y rows (d_inner * rank elements)
-    # below 2 GiB, so wide ranks can need more chunks than the plain scan
+    # workspace: two [n_chunks - 1][batch][d_inner][d_state] fp32 arrays. Ranks 2 and 4
+    # are planned for 5 waves per SIMD (40 chunks of the 256k sequence over 128
+    # channel waves), rank 8 for 4 (32 chunks, but the 2 GiB cap on a chunk's rows of
+    # 8192 * 8 elements allows 8191 steps: 33 chunks)
+    ws = lambda chunks: 2 * (((chunks - 1) * 8192 * 16 * 4 + 255) // 256 * 256)
     big = lib.ssm_scan_fwd_mimo_workspace(1, 262144, 8192, 16, 4, 0)
-    assert big == lib.ssm_scan_fwd_workspace(1, 262144, 8192, 16) > 0
+    assert big == ws(40)
+    assert lib.ssm_scan_fwd_mimo_workspace(1, 262144, 8192, 16, 8, 0) == ws(33)
+    for R, chunks in ((1, 40), (2, 40), (4, 40), (8, 33)):
+        assert -(-262144 // lib.ssm_scan_fwd_mimo_chunk_len(1, 262144, 8192, 16, R)) == chunks
     assert scan(L=262144, Dn=8192, N=16) == WS
+    # the chunk cap keeps a chunk's x / y rows (d_inner * rank elements) below 2 GiB,
+    # so a wide rank can need more chunks than asked for
     T8 = (1 << 31) // (8192 * 8 * 4) - 1
-    assert lib.ssm_scan_fwd_mimo_workspace(1, 262144, 8192, 16, 8, 262144) == \
-        2 * (((-(-262144 // T8) - 1) * 8192 * 16 * 4 + 255) // 256 * 256)
+    assert lib.ssm_scan_fwd_mimo_workspace(1, 262144, 8192, 16, 8, 262144) == ws(-(-262144 // T8))
     assert scan(L=0) == OK                    # nothing to do, nothing enqueued
 
     def step(R=4, N=16, io=1, x=0x1000, y=0x2000, B=0x1000):
