@@ -470,7 +470,7 @@ def sample_width(shape, elems):
 def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False, mimo=0):
     import oracle
     oracle.build(force=False)
-    k = sample_width(shape, CPU_SAMPLE_ELEMS // (4 if shape.complex_state else max(1, mimo)))
+    k = sample_width(shape, CPU_SAMPLE_ELEMS // (4 if shape.complex_state else 1))
     idx = workloads.sample_channels(shape.d_inner, k, seed=5).to("cuda")
     g = lambda t: None if t is None else t.index_select(2, idx).cpu()
     args = (g(d["x"]), g(d["dt"]), d["A"].index_select(0, idx).cpu(), d["B"].cpu(), d["C"].cpu(),
@@ -565,8 +565,6 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
     par = workloads.make_decode_params(shape, "cpu")
     tok = (workloads.make_mimo_decode_step(shape, mimo, 0, "cpu") if mimo
            else workloads.make_decode_step(shape, 0, "cpu"))
-    if mimo:
-        tokens = max(24, tokens // mimo)
     sl = lambda t: None if t is None else np.ascontiguousarray(oracle.to_f64(t[:, :S]))
     x, z, B, C = sl(tok["x"]), sl(tok["z"]), sl(tok["B"]), sl(tok["C"])
     A, D = oracle.to_f64(par["A"]), oracle.to_f64(par["D"])
