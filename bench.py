@@ -117,18 +117,22 @@ def mimo_prefill_bytes(s, io_bytes: int, R: int) -> float:
             + Dn * N * 4 + Dn * 4 + b * Dn * N * 4)
 
 
-def mimo_lane_ops(s, R: int) -> float:
-    """VALU instructions per channel-step of the MIMO update (one lane per channel). Per
-    state: dt*A, exp, the R-term sum B x (one multiply, R-1 fused multiply-adds), the
-    state's fused multiply-add, and R output fused multiply-adds = 3 + 2R. Per
-    channel-step: dt*x[r] and D x[r] + acc[r] (2R); with bf16 I/O the widening of x and
-    dt and the output conversion (2R + 1); gated: the gate per output (6R) and, with
-    bf16, the widening of z (R). R = 1 gives prefill_lane_ops."""
+def mimo_lane_ops(s, R: int, matrix: bool = False) -> float:
+    """VALU instructions per channel-step of the MIMO update (one lane per channel).
+    VALU path, per state: dt*A, exp, the R-term sum B x (one multiply, R-1 fused
+    multiply-adds), the state's fused multiply-add, and R output fused multiply-adds =
+    3 + 2R; per channel-step: dt*x[r] and D x[r] + acc[r] (2R). Matrix path (the prefill
+    from rank 4: B x on the matrix cores), per state: dt*A, exp, dt*v, the state's fused
+    multiply-add and R output fused multiply-adds = 4 + R; per channel-step D x[r] + acc[r]
+    (R). Both: with bf16 I/O the widening of x and dt and the output conversion (2R + 1);
+    gated: the gate per output (6R) and, with bf16, the widening of z (R). The matrix
+    operations (2 N R flops per channel-step) are not VALU work. R = 1 gives
+    prefill_lane_ops."""
     bf16 = s.io == "bf16"
-    per_elem = 2 * R + ((2 * R + 1) if bf16 else 0)
+    per_elem = (R if matrix else 2 * R) + ((2 * R + 1) if bf16 else 0)
     if s.gated:
         per_elem += 6 * R + (R if bf16 else 0)
-    return s.d_state * (3 + 2 * R) + per_elem
+    return s.d_state * ((4 + R) if matrix else (3 + 2 * R)) + per_elem
 
 
 def mimo_decode_bytes(s, io_bytes: int, R: int) -> float:
@@ -323,7 +327,7 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
         lane_ops += trap_lane_ops(shape.d_state)
     if mimo:
         nbytes = mimo_prefill_bytes(shape, io_bytes, mimo)
-        lane_ops = mimo_lane_ops(shape, mimo)
+        lane_ops = mimo_lane_ops(shape, mimo, matrix=mimo >= 4)
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": phases,
         "elements_per_step": elems, "bytes_per_step": nbytes,

@@ -92,6 +92,9 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
     int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
                               : auto_chunk_len(batch, L, d_inner, waves_per_simd * kSimds);
     T = std::min(T, cap);
+    // MIMO: a chunk's rows of B (d_state * rank elements each) also span less than 2 GiB,
+    // since the matrix path stages them through buffer loads with 32-bit offsets.
+    if (rank > 1) T = std::min(T, std::max<int64_t>(1, ((int64_t)1 << 31) / ((int64_t)d_state * rank * 4) - 1));
     const int64_t n_chunks = L > 0 ? (L + T - 1) / T : 1;
     if (n_chunks > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n_chunks, (long long)kMaxChunks);
     p->T = T;
@@ -162,8 +165,8 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     if (mimo) {
         // x, z and y are read and written R elements (up to 16 bytes) at a time.
         const size_t va = std::min<size_t>(16, (size_t)rank * eb);
-        if (!aligned(x, va) || !aligned(z, va) || !aligned(y, va))
-            return fail(SSM_ERR_ALIGN, "pointer alignment (x, z, y: min(16, rank * element) bytes)");
+        if (!aligned(x, va) || !aligned(z, va) || !aligned(y, va) || (rank >= 4 && !aligned(B, va)))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x, z, y, and B for rank >= 4: min(16, rank * element) bytes)");
         if ((double)batch * L * d_inner * rank > 4.0e18)
             return fail(SSM_ERR_SHAPE, "problem too large");
     }
@@ -271,8 +274,11 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     const size_t eb = io_bytes(io);
     // B_t and C_t rows are read K values at a time: K = 4 states per lane for
     // d_state >= 4 (real), else d_state; complex rows are read one value at a time.
-    // MIMO rows of B_t and C_t go through the scalar unit (4-byte aligned).
+    // MIMO rows of B_t and C_t go through the scalar unit (4-byte aligned); from rank 4 B_t
+    // is also read as matrix operands, min(16, rank * element) bytes at a time.
     const size_t bc = mimo ? 4 : cplx ? eb : eb * (size_t)std::min<int32_t>(d_state, 4);
+    if (mimo && rank >= 4 && !aligned(B, std::min<size_t>(16, (size_t)rank * eb)))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (B_t for rank >= 4: min(16, rank * element) bytes)");
     if (!aligned(h, 16) || !aligned(A, 16) || !aligned(x, eb) || !aligned(dt, eb) ||
         !aligned(z, eb) || !aligned(y, eb) || !aligned(B, bc) || !aligned(C, bc) || !aligned(D, 4))
         return fail(SSM_ERR_ALIGN, "pointer alignment (h, A 16 B; B_t, C_t min(d_state,4) elements; others element)");

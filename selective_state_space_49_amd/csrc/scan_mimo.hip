@@ -18,8 +18,10 @@
 // multiply-adds for B_t x_t and each output R more for C_t h_t, against one
 // exponential per state: the exponential is shared by R outputs.
 //
-// The decode step (k_mimo_step) advances one token per (layer, sequence, channel)
-// with the same per-step arithmetic as the rescan, from the same shared function.
+// From rank 4 the rescan and the summaries compute B_t x_t on the matrix cores, with
+// B_t's rows staged through LDS (mimo_bx, mimo_steps). The decode step (k_mimo_step)
+// advances one token per (layer, sequence, channel) with the VALU form of the same step
+// function.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 #include "ssm_stream.h"
@@ -172,8 +174,12 @@ __device__ __forceinline__ void st_vec(IO *p, const float (&y)[R]) {
     }
 }
 
-// The input term of state n at row element e = e0 + n R: u = sum_r B[n][r] xd[r] with
-// xd = dt x, as u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u) for r = 1 .. R-1.
+// Ranks 4 and 8 compute B_t x_t on the matrix cores; ranks 1 and 2 on the VALU, rank 1
+// with exactly the plain scan's operations (rank 2 measured faster on the VALU).
+template <int R> constexpr bool kMatInput = R >= 4;
+
+// The input term of state n at row element e = e0 + n R (VALU path): u = sum_r B[n][r]
+// xd[r] with xd = dt x, as u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u).
 template <int R, typename Row>
 __device__ __forceinline__ float mimo_input(const Row &Bp, int64_t e, const float (&xd)[R]) {
     float u = Bp.ld(e) * xd[0];
@@ -182,29 +188,103 @@ __device__ __forceinline__ float mimo_input(const Row &Bp, int64_t e, const floa
     return u;
 }
 
-// One step of one channel, in the fixed order that the prefill rescan and the decode
-// step share (so that L decode steps equal a one-chunk prefill bit for bit):
-//     xd[r] = dt x[r];  for n ascending: u = mimo_input(n);
-//     h[n] = fma(e2(dt A[n] log2 e), h[n], u);  acc[r] = fma(C[n][r], h[n], acc[r])
-//     (r ascending, acc from 0)
-// Row reads element e0 + n R + r of the step's B (and C) through the scalar unit.
-template <int N, int R, typename Row>
-__device__ __forceinline__ void mimo_update(float (&h)[N], const float (&A2)[N], float dv,
-                                            const float (&xv)[R], const Row &Bp, const Row &Cp,
-                                            int64_t e0, float (&acc)[R]) {
-    float xd[R];
+// B_t x_t on the matrix cores (ranks 4 and 8): v[n] = sum_r B_t[n][r] x[r] for all N
+// states of every lane's channel. For each group of four states n0 .. n0+3, bf16 takes
+// one v_mfma_f32_4x4x4_16b_bf16 per 4 ranks and fp32 one v_mfma_f32_4x4x1_16b_f32 per
+// rank: lane l supplies row n0 + l%4 of B_t as the A operand and its own x as the B
+// operand, and the 16-block 4x4 forms give D[l][i] = sum_k A[4 (l/4) + i][k] B[l][k]
+// (a layout a probe confirmed), so result register i of lane l is v[n0 + i] of lane
+// l's channel: the layout the state is kept in. Products of bf16 values are exact in
+// fp32. Every lane of the wave takes part (a block reads the A operand of all four of
+// its lanes), so the kernels keep lanes past the last channel running on clamped
+// indices. brow: the step's B row ([N][R], 16-byte aligned), in LDS or global memory.
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef float f4m __attribute__((ext_vector_type(4)));
+#define SSM_LDS __attribute__((address_space(3)))
+
+// A T at byte pointer p, in global memory or in LDS.
+template <typename T> __device__ __forceinline__ T ld_at(const char *p) { return *(const T *)p; }
+template <typename T> __device__ __forceinline__ T ld_at(const SSM_LDS char *p) {
+    return *(const SSM_LDS T *)p;
+}
+
+__device__ __forceinline__ f4m mma_bf16(u32x2 a, u32x2 b, f4m c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s4v, a), __builtin_bit_cast(s4v, b),
+                                                  c, 0, 0, 0);
+}
+
+template <typename IO, int N, int R, typename P>
+__device__ __forceinline__ void mimo_bx(P brow, const VecRaw<IO, R> &xr, float (&v)[N]) {
+    static_assert(R == 4 || R == 8, "matrix path: ranks 4 and 8");
+    const uint32_t q = threadIdx.x & 3u;
+    constexpr int G = (N + 3) / 4;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        xd[r] = dv * xv[r];
-        acc[r] = 0.0f;
+    for (int g = 0; g < G; ++g) {
+        // N < 4: rows past the last state only fill result registers that are not used
+        const uint32_t n = min(4u * g + q, (uint32_t)N - 1u);
+        const P p = brow + n * (uint32_t)(R * sizeof(IO));
+        f4m d = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+            for (int k = 0; k < R / 4; ++k) {
+                const u32x2 av = ld_at<u32x2>(p + 8 * k);
+                const u32x2 bv = {xr.w[2 * k], xr.w[2 * k + 1]};
+                d = mma_bf16(av, bv, d);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < R / 4; ++k) {
+                const u32x4 t = ld_at<u32x4>(p + 16 * k);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    d = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(t[j]), xr.at(4 * k + j), d, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * g + i < N) v[4 * g + i] = d[i];
     }
+}
+
+// One step of one channel. The prefill rescan takes the matrix path from rank 4 (MAT),
+// the decode step always the VALU path: it is bound by HBM, and the matrix operands'
+// registers would cost it waves (65.3 against 58-60 us per call at rank 4). Up to rank 2
+// the two therefore perform the same operations and L decode steps equal a one-chunk
+// prefill bit for bit; from rank 4 they differ in the rounding of the input sum.
+// VALU path:  xd[r] = dt x[r];  for n ascending: h[n] = fma(e2(dt A[n] log2 e), h[n],
+//             mimo_input(n));  acc[r] = fma(C[n][r], h[n], acc[r])
+// Matrix path: v = B_t x_t (mimo_bx);  for n ascending: h[n] = fma(e2(dt A[n] log2 e),
+//             h[n], dt v[n]);  acc[r] = fma(C[n][r], h[n], acc[r])
+// (r ascending, acc from 0). Bp / Cp read element e0 + n R + r of the step's B / C
+// through the scalar unit; brow is the step's B row for the matrix operands.
+template <typename IO, int N, int R, bool MAT, typename Row, typename P>
+__device__ __forceinline__ void mimo_update(float (&h)[N], const float (&A2)[N], float dv,
+                                            const VecRaw<IO, R> &xr, const float (&xv)[R],
+                                            const Row &Bp, const Row &Cp, P brow, int64_t e0,
+                                            float (&acc)[R]) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        const int64_t e = e0 + n * R;
-        const float u = mimo_input<R>(Bp, e, xd);
-        h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u);
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    if constexpr (MAT) {
+        float v[N];
+        mimo_bx<IO, N, R>(brow, xr, v);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
+        for (int n = 0; n < N; ++n) {
+            const int64_t e = e0 + n * R;
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], dv * v[n]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
+        }
+    } else {
+        float xd[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) xd[r] = dv * xv[r];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const int64_t e = e0 + n * R;
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], mimo_input<R>(Bp, e, xd));
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
+        }
     }
 }
 
@@ -245,54 +325,153 @@ __device__ __forceinline__ void load_mimo_block(MimoBlock<IO, R, KU> &s, const V
     }
 }
 
-// Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1, with the next block of KU rows in
-// flight while the current one is computed (as stream_steps does for scalar rows).
-template <typename IO, int R, bool GATED, int KU, typename Body>
+// s_waitcnt for the vector-memory counter only (lgkmcnt and expcnt left at their
+// maxima), and for the LDS / scalar counter only.
+__device__ __forceinline__ constexpr int wait_vm(int n) {
+    return (n & 0xF) | ((n >> 4) & 0x3) << 14 | 0x70 | 0xF00;
+}
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Staging of B_t rows for the matrix path. Each wave owns a ring of two slots of KU
+// rows in LDS; the rows of the next block are copied in by direct-to-LDS buffer loads
+// (4 bytes per lane, so 256 bytes per instruction, no registers held while in flight)
+// together with that block's x, dt and z, while the current block is computed. The
+// compiler does not order these loads against LDS reads, so the loop waits itself:
+//   - before a slot is refilled, lgkmcnt(0): the reads of the block that used it are done;
+//   - before a block's rows are read, vmcnt(n) with n = the vector-memory instructions
+//     issued for the next block just before: memory operations retire in order, so
+//     everything older, this block's staging loads among it, is then complete.
+template <typename IO, int N, int R, int KU>
+struct BStage {
+    static constexpr int kRowBytes = N * R * (int)sizeof(IO);
+    static constexpr int kSlotBytes = KU * kRowBytes;
+    static constexpr int kLoads = (kSlotBytes + 255) / 256;            // per slot
+    static constexpr int kLastLanes = (kSlotBytes - 256 * (kLoads - 1)) / 4;
+    __amdgpu_buffer_rsrc_t r;  // this walk's B rows, from its first row on
+    SSM_LDS char *ring;        // 2 slots of kSlotBytes
+    __device__ __forceinline__ void stage(int slot, uint32_t row) const {
+        const uint32_t lane = threadIdx.x & 63u;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+        for (int d = 0; d < kLoads; ++d) {
+            if (d < kLoads - 1 || lane < (uint32_t)kLastLanes)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSM_LDS void *)(ring + slot * kSlotBytes + 256 * d), 4,
+                                                         lane * 4u + 256u * d, row * (uint32_t)kRowBytes, 0, 0);
+        }
+    }
+    __device__ __forceinline__ const SSM_LDS char *row_at(int slot, int j) const {
+        return ring + slot * kSlotBytes + j * kRowBytes;
+    }
+};
+
+// Vector-memory instructions one block of KU steps issues: x, dt (and z) per step, and
+// the B staging loads on the matrix path.
+template <typename IO, int N, int R, bool GATED, int KU>
+constexpr int block_vm_ops() {
+    constexpr int vx = VecRaw<IO, R>::kBytes == 32 ? 2 : 1;
+    return KU * (vx + 1 + (GATED ? vx : 0)) + (kMatInput<R> ? BStage<IO, N, R, KU>::kLoads : 0);
+}
+
+// Calls body(i, x_i, dt_i, z_i, brow_i) for i = 0 .. steps-1, with the next block of KU
+// rows in flight while the current one is computed (as stream_steps does for scalar
+// rows). brow_i is step i's row of B (an LDS pointer from the staging ring, or, in the
+// ragged tail, a global pointer) on the matrix path, and unused (null) otherwise.
+// B0: the walk's first B row (global; matrix path only); ring: the wave's 2 slots.
+template <typename IO, int N, int R, bool GATED, int KU, typename Body>
 __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowStream<IO> &dt,
                                            const VecStream<IO, R> &z, const MimoStreams &o,
-                                           uint32_t steps, uint32_t prio_scale, Body &&body) {
+                                           const IO *B0, SSM_LDS char *ring, uint32_t steps,
+                                           uint32_t prio_scale, Body &&body) {
+    constexpr bool kMat = kMatInput<R>;
+    constexpr int kOps = block_vm_ops<IO, N, R, GATED, KU>();
+    typedef BStage<IO, N, R, KU> Stg;
+    Stg st;
+    if constexpr (kMat) {
+        st.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<IO *>(B0), 0, -1, kRsrcWord3);
+        st.ring = ring;
+    }
+    // this block's staged rows are complete once only the next block's loads are pending
+    auto ready = [&](bool more) {
+        if constexpr (kMat) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) __builtin_amdgcn_s_waitcnt(wait_vm(kOps));
+            else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto brow = [&](int slot, int j) {
+        if constexpr (kMat) return st.row_at(slot, j);
+        else return (const SSM_LDS char *)nullptr;
+    };
     const uint32_t full = steps / KU;
     uint32_t i = 0;
     MimoBlock<IO, R, KU> bufA, bufB;
-    if (full > 0) load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, 0);
+    if (full > 0) {
+        if constexpr (kMat) st.stage(0, 0);
+        load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, 0);
+    }
     for (uint32_t k = 0; k < full; k += 2) {
         if (prio_scale) set_priority(steps - i, prio_scale);
-        if (k + 1 < full) load_mimo_block<IO, R, GATED, KU>(bufB, x, dt, z, o, i + KU);
+        const bool more1 = k + 1 < full;
+        if (more1) {
+            if constexpr (kMat) st.stage(1, i + KU);
+            load_mimo_block<IO, R, GATED, KU>(bufB, x, dt, z, o, i + KU);
+        }
+        ready(more1);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufA.x[j], RowStream<IO>::widen(bufA.dt[j]), bufA.z[j]);
+            body(i + j, bufA.x[j], RowStream<IO>::widen(bufA.dt[j]), bufA.z[j], brow(0, j));
         }
         i += KU;
-        if (k + 1 >= full) break;
-        if (k + 2 < full) load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, i + KU);
+        if (!more1) break;
+        const bool more2 = k + 2 < full;
+        if (more2) {
+            if constexpr (kMat) st.stage(0, i + KU);
+            load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, i + KU);
+        }
+        ready(more2);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufB.x[j], RowStream<IO>::widen(bufB.dt[j]), bufB.z[j]);
+            body(i + j, bufB.x[j], RowStream<IO>::widen(bufB.dt[j]), bufB.z[j], brow(1, j));
         }
         i += KU;
     }
     if (prio_scale) __builtin_amdgcn_s_setprio(0);
-    for (; i < steps; ++i) {  // ragged tail, one step at a time
+    for (; i < steps; ++i) {  // ragged tail, one step at a time, B rows read directly
         const VecRaw<IO, R> xv = x.ld(o.vx, i * o.rbx);
         const float dv = dt.ld(o.vd, i * o.rbd);
         VecRaw<IO, R> zv{};
         if (GATED) zv = z.ld(o.vx, i * o.rbx);
-        body(i, xv, dv, zv);
+        const char *g = kMat ? (const char *)B0 + (size_t)i * BStage<IO, N, R, KU>::kRowBytes : nullptr;
+        body(i, xv, dv, zv, g);
     }
 }
 
+// A lane's batch row and channel. Lanes past the last channel keep running on the
+// last channel (the matrix operations read operands from every lane of the wave) and
+// store nothing.
 struct LaneId {
     int64_t b, d;
+    bool live;
 };
 
 __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
     LaneId r;
     r.b = (int64_t)blockIdx.x / a.dblocks;
-    r.d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
+    const int64_t d = ((int64_t)blockIdx.x % a.dblocks) * a.threads + threadIdx.x;
+    r.live = d < a.Dn;
+    r.d = r.live ? d : a.Dn - 1;
     return r;
 }
+
+// The wave's staging ring for B rows (matrix path), in a block's LDS of 4 waves.
+template <typename IO, int N, int R, int KU>
+struct Ring {
+    static constexpr int kBytes = kMatInput<R> ? 2 * BStage<IO, N, R, KU>::kSlotBytes : 16;
+};
 
 __device__ __forceinline__ MimoStreams mimo_offsets(const ScanArgs &a, int64_t d, int R, int eb) {
     MimoStreams o;
@@ -310,8 +489,9 @@ template <int R> constexpr int kMimoKU = R <= 2 ? 4 : 2;
 // ---------------------------------------------------------------- chunk summary
 template <typename IO, int N, int R>
 __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
+    constexpr int KU = kMimoKU<R>;
+    __shared__ __attribute__((aligned(16))) char ring_mem[4 * Ring<IO, N, R, KU>::kBytes];
     const LaneId ln = lane_id(a);
-    if (ln.d >= a.Dn) return;
     const int c = blockIdx.y;
     const int64_t t0 = (int64_t)c * a.T;
     const uint32_t T = (uint32_t)a.T;  // every chunk that has a summary is full length
@@ -332,20 +512,28 @@ __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
     const VecStream<IO, R> xs((const IO *)a.x + rw * a.Dn * R);
     const RowStream<IO> dws((const IO *)a.dt + rw * a.Dn);
     const UniRow<IO, N * R> Bp(a.B, ln.b * a.L * N * R);
+    SSM_LDS char *ring = (SSM_LDS char *)ring_mem + (threadIdx.x / 64) * Ring<IO, N, R, KU>::kBytes;
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
-    mimo_steps<IO, R, false, kMimoKU<R>>(xs, dws, xs, o, T - ts, kSummaryPrioScale,
-                                         [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &) {
+    mimo_steps<IO, N, R, false, KU>(xs, dws, xs, o, (const IO *)a.B + rw * N * R, ring, T - ts,
+                                    kSummaryPrioScale,
+                                    [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &, auto brow) {
         const int64_t t = t0 + ts + i;
         S += (double)dv;
-        float xd[R];
+        if constexpr (kMatInput<R>) {
+            float v[N];
+            mimo_bx<IO, N, R>(brow, xr, v);
 #pragma unroll
-        for (int r = 0; r < R; ++r) xd[r] = dv * xr.at(r);
+            for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], dv * v[n]);
+        } else {
+            float xd[R];
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float u = mimo_input<R>(Bp, (t * N + n) * R, xd);
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u);
+            for (int r = 0; r < R; ++r) xd[r] = dv * xr.at(r);
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], mimo_input<R>(Bp, (t * N + n) * R, xd));
         }
     });
+    if (!ln.live) return;
     const float Sf = (float)S;
     const size_t so = (((size_t)c * a.batch + ln.b) * a.Dn + ln.d) * N;
 #pragma unroll
@@ -364,8 +552,9 @@ template <int R> constexpr int kMimoWavesPerSimd = R <= 4 ? 5 : 1;
 
 template <typename IO, int N, int R, bool GATED>
 __global__ __launch_bounds__(256, kMimoWavesPerSimd<R>) void k_mimo_scan(ScanArgs a) {
+    constexpr int KU = kMimoKU<R>;
+    __shared__ __attribute__((aligned(16))) char ring_mem[4 * Ring<IO, N, R, KU>::kBytes];
     const LaneId ln = lane_id(a);
-    if (ln.d >= a.Dn) return;
     const int c = blockIdx.y;
     const int64_t t0 = (int64_t)c * a.T;
     const uint32_t steps = (uint32_t)(min(a.L, t0 + a.T) - t0);
@@ -388,16 +577,18 @@ __global__ __launch_bounds__(256, kMimoWavesPerSimd<R>) void k_mimo_scan(ScanArg
     const RowStream<IO> dts((const IO *)a.dt + t_row0 * a.Dn);
     const UniRow<IO, N * R> Bp(a.B, ln.b * a.L * N * R);
     const UniRow<IO, N * R> Cp(a.C, ln.b * a.L * N * R);
-    mimo_steps<IO, R, GATED, kMimoKU<R>>(xs, dts, zs, o, steps, steps,
-                                         [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &zr) {
+    SSM_LDS char *ring = (SSM_LDS char *)ring_mem + (threadIdx.x / 64) * Ring<IO, N, R, KU>::kBytes;
+    mimo_steps<IO, N, R, GATED, KU>(xs, dts, zs, o, (const IO *)a.B + t_row0 * N * R, ring, steps, steps,
+                                    [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &zr, auto brow) {
         const int64_t t = t0 + i;
         float xv[R], acc[R], yv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
-        mimo_update<N, R>(h, A2, dv, xv, Bp, Cp, t * N * R, acc);
+        mimo_update<IO, N, R, kMatInput<R>>(h, A2, dv, xr, xv, Bp, Cp, brow, t * N * R, acc);
         mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
-        ys.st(o.vx, i * o.rbx, yv);
+        if (ln.live) ys.st(o.vx, i * o.rbx, yv);
     });
+    if (!ln.live) return;
     if (c == a.n_chunks - 1 && a.h_final) {
 #pragma unroll
         for (int n = 0; n < N; ++n) a.h_final[col + n] = h[n];
@@ -469,6 +660,7 @@ template <typename IO, int N, int R, bool GATED>
 __global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
     constexpr int P = kLdsRow<N>;
     __shared__ __attribute__((aligned(16))) float sh[256 * P];  // the block's states
+
     const int tid = (int)threadIdx.x;
     const int64_t d0 = (int64_t)blockIdx.x * 256;
     const int nch = (int)min((int64_t)256, a.Dn - d0);  // channels of this block
@@ -485,6 +677,7 @@ __global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
     const float Dd = a.D[l * a.Dn + d];
     float *hblk = a.h + (lq * a.Dn + d0) * N;
     rows_to_lds<N>(sh, hblk, nch, tid);
+
     float h[N], A2[N];
     const float *Ap = a.A + (l * a.Dn + d) * N;  // shared by every sequence: cached
 #pragma unroll
@@ -496,7 +689,7 @@ __global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
     float xv[R], acc[R], yv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
-    mimo_update<N, R>(h, A2, dv, xv, Bp, Cp, 0, acc);
+    mimo_update<IO, N, R, false>(h, A2, dv, xr, xv, Bp, Cp, (const char *)nullptr, 0, acc);
     mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
 #pragma unroll
     for (int n = 0; n < N; ++n) sh[tid * P + n] = h[n];

@@ -4,8 +4,9 @@ the fp64 oracle's scan_mimo / step_mimo, plus invariants.
 Prefill cases span several chunks and 64-lane waves with ragged tails, every state
 size and rank, fp32 and bf16, with and without gate and h0. Rank 1 equals the plain
 scan bit for bit; the result does not depend on the chunk length; resuming from
-h_final equals one call; L decode steps equal a one-chunk prefill bit for bit; the
-256k prefill and the 28-layer decode at full size on sampled channels.
+h_final equals one call; L decode steps equal a one-chunk prefill (bit for bit up to rank
+2, where both run on the VALU); the 256k prefill and the 28-layer decode at full size on
+sampled channels.
 """
 import pytest
 import torch
@@ -183,10 +184,13 @@ def test_mimo_step_matches_oracle(case):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_mimo_decode_equals_one_chunk_prefill(io):
+@pytest.mark.parametrize("R", [2, 4])
+def test_mimo_decode_equals_one_chunk_prefill(io, R):
     # L decode steps (one layer, n_seq = batch) against a one-chunk prefill of the same
-    # tokens: the two kernels share the per-step arithmetic, so bit for bit.
-    b, L, Dn, N, R = 3, 40, 96, 16, 4
+    # tokens. Up to rank 2 both run the same VALU operations: bit for bit. From rank 4
+    # the prefill sums B_t x_t on the matrix cores and the decode on the VALU: the same
+    # fp32 results up to the rounding of that sum.
+    b, L, Dn, N = 3, 40, 96, 16
     shape, d = _draw((b, L, Dn, N, R, io, True, True, L), seed=5)
     say("MIMO prefill vs decode", io)
     y, hf = _gpu(d, L)
@@ -199,8 +203,13 @@ def test_mimo_decode_equals_one_chunk_prefill(io):
                                     row(g["B"], t), row(g["C"], t), g["D"].unsqueeze(0),
                                     row(g["z"], t))[0])
     torch.cuda.synchronize()
-    assert bitwise_equal(torch.stack(ys, dim=1), y)
-    assert bitwise_equal(h[0], hf)
+    yd = torch.stack(ys, dim=1)
+    if R <= 2:
+        assert bitwise_equal(yd, y) and bitwise_equal(h[0], hf)
+    else:
+        # y: one rounding step of the output type; h: fp32 rounding over L = 40 steps
+        assert rel_err(yd, oracle.to_f64(y)) <= (1e-5 if io == "f32" else 2 ** -7)
+        assert rel_err(h[0], oracle.to_f64(hf)) <= 1e-5
 
 
 def test_mimo_full_size_long_context_sampled():
