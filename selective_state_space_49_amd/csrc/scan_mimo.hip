@@ -391,12 +391,16 @@ __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowS
         st.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<IO *>(B0), 0, -1, kRsrcWord3);
         st.ring = ring;
     }
-    // this block's staged rows are complete once only the next block's loads are pending
-    auto ready = [&](bool more) {
+    // This block's staged rows are complete once only the next block's loads are pending.
+    // On the matrix path a next block is always issued (the last block loads its own rows
+    // again, into the idle buffer and slot), so that this wait is one straight-line
+    // vmcnt(kOps): behind a branch the compiler's own wait tracking does not see it and
+    // falls back to vmcnt(0) before each step's first use of x, which also waits for the
+    // next block's loads.
+    auto ready = [&]() {
         if constexpr (kMat) {
             __builtin_amdgcn_sched_barrier(0);
-            if (more) __builtin_amdgcn_s_waitcnt(wait_vm(kOps));
-            else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            __builtin_amdgcn_s_waitcnt(wait_vm(kOps));
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -414,11 +418,12 @@ __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowS
     for (uint32_t k = 0; k < full; k += 2) {
         if (prio_scale) set_priority(steps - i, prio_scale);
         const bool more1 = k + 1 < full;
-        if (more1) {
-            if constexpr (kMat) st.stage(1, i + KU);
-            load_mimo_block<IO, R, GATED, KU>(bufB, x, dt, z, o, i + KU);
+        if (kMat || more1) {
+            const uint32_t nxt = more1 ? i + KU : i;
+            if constexpr (kMat) st.stage(1, nxt);
+            load_mimo_block<IO, R, GATED, KU>(bufB, x, dt, z, o, nxt);
         }
-        ready(more1);
+        ready();
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
@@ -427,11 +432,12 @@ __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowS
         i += KU;
         if (!more1) break;
         const bool more2 = k + 2 < full;
-        if (more2) {
-            if constexpr (kMat) st.stage(0, i + KU);
-            load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, i + KU);
+        if (kMat || more2) {
+            const uint32_t nxt = more2 ? i + KU : i;
+            if constexpr (kMat) st.stage(0, nxt);
+            load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, nxt);
         }
-        ready(more2);
+        ready();
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);

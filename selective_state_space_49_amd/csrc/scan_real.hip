@@ -56,6 +56,7 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
 struct NoInput {
     static constexpr bool kTrap = false;
     static constexpr int kWavesPerSimd = 5;
+    static constexpr bool kRawPrefetch = true;  // see StepIn (ssm_stream.h)
     __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
     __device__ __forceinline__ void history(const ScanArgs &, int64_t, int64_t, int64_t) {}
     __device__ __forceinline__ float x(float v) { return v; }
@@ -69,6 +70,7 @@ template <typename IO, int KC>
 struct MambaInput {
     static constexpr bool kTrap = false;
     static constexpr int kWavesPerSimd = 4;
+    static constexpr bool kRawPrefetch = false;
     ConvSilu<(KC > 0 ? KC : 1)> conv;
     float dbias;
 
@@ -127,6 +129,7 @@ template <typename IO>
 struct TrapInput {
     static constexpr bool kTrap = true;
     static constexpr int kWavesPerSimd = 5;
+    static constexpr bool kRawPrefetch = false;
     float xprev;  // x of the step before the current one
     __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
     __device__ __forceinline__ void history(const ScanArgs &a, int64_t b, int64_t d, int64_t t) {
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
     float bp[N];     // trapezoidal rule: B of the step before, carried from step to step
     if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0 + ts, bp);
-    stream_steps<IO, false, 4>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float) {
+    stream_steps<IO, false, 4, In::kRawPrefetch>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + ts + i;
         S += (double)dv;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     in.history(a, ln.b, ln.d, t0);
     float bp[N];  // trapezoidal rule: B of the step before, carried from step to step
     if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0, bp);
-    stream_steps<IO, GATED, 4>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv) {
+    stream_steps<IO, GATED, 4, In::kRawPrefetch>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
         float acc = 0.0f;

@@ -9,6 +9,8 @@
 // bounds by construction.
 #pragma once
 
+#include <type_traits>
+
 #include "ssm_device.h"
 
 namespace ssm {
@@ -58,9 +60,19 @@ template <> struct RowStream<float> {
 // use instead of hoisting a whole block's worth of them into SGPRs. KU is 4 for the
 // real state and 2 for the complex state, whose larger state would otherwise push
 // the kernel past 128 VGPRs (below four waves per SIMD).
-template <int KU>
+//
+// RAW: the buffers hold the bits as loaded (a bf16 value zero-extended in its dword) and
+// the values are widened in the step that uses them. Widening at load time makes the
+// compiler wait for the loads right after issuing them, which leaves the prefetch
+// nothing to overlap (256k rescan 5.90-6.03 -> 5.84 ms, complex 1.08 -> 1.01 ms). It
+// keeps each raw value live until its step, though, and the kernels with the most
+// registers in use (the exponential-trapezoidal and input-stage rescans) then spill
+// (6.9 -> 19.7 ms): they widen at load time (RAW = false).
+template <int KU, bool RAW>
 struct StepIn {
-    float x[KU], dt[KU], z[KU];
+    // raw bits (RAW), else the widened values
+    typedef typename std::conditional<RAW, uint32_t, float>::type T;
+    T x[KU], dt[KU], z[KU];
 };
 
 // Issue priority by remaining work. The SIMD arbiter favours the oldest of the waves
@@ -79,46 +91,60 @@ __device__ __forceinline__ void set_priority(uint32_t remaining, uint32_t scale)
     else __builtin_amdgcn_s_setprio(0);
 }
 
-template <typename IO, bool GATED, int KU>
-__device__ __forceinline__ void load_block(StepIn<KU> &s, const RowStream<IO> &x,
+template <typename IO, bool GATED, int KU, bool RAW>
+__device__ __forceinline__ void load_block(StepIn<KU, RAW> &s, const RowStream<IO> &x,
                                            const RowStream<IO> &dt, const RowStream<IO> &z,
                                            uint32_t voff, uint32_t row, uint32_t rb) {
 #pragma unroll
     for (int k = 0; k < KU; ++k) {
-        s.x[k] = x.ld(voff, (row + k) * rb);
-        s.dt[k] = dt.ld(voff, (row + k) * rb);
-        if (GATED) s.z[k] = z.ld(voff, (row + k) * rb);
+        if constexpr (RAW) {
+            s.x[k] = x.ldraw(voff, (row + k) * rb);
+            s.dt[k] = dt.ldraw(voff, (row + k) * rb);
+            if (GATED) s.z[k] = z.ldraw(voff, (row + k) * rb);
+        } else {
+            s.x[k] = x.ld(voff, (row + k) * rb);
+            s.dt[k] = dt.ld(voff, (row + k) * rb);
+            if (GATED) s.z[k] = z.ld(voff, (row + k) * rb);
+        }
     }
+}
+
+template <typename IO, bool RAW, typename T>
+__device__ __forceinline__ float use_value(T v) {
+    if constexpr (RAW) return RowStream<IO>::widen(v);
+    else return v;
 }
 
 // Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1 (rows of the streams); voff is
 // the lane's byte offset in a row and rb the bytes per row. prio_scale: see
 // set_priority (0 = leave the priority alone).
-template <typename IO, bool GATED, int KU, typename Body>
+template <typename IO, bool GATED, int KU, bool RAW = true, typename Body>
 __device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowStream<IO> &dt,
                                              const RowStream<IO> &z, uint32_t voff, uint32_t rb,
                                              uint32_t steps, uint32_t prio_scale, Body &&body) {
     const uint32_t full = steps / KU;
     uint32_t i = 0;
-    StepIn<KU> bufA, bufB;
-    if (full > 0) load_block<IO, GATED, KU>(bufA, x, dt, z, voff, 0, rb);
+    StepIn<KU, RAW> bufA, bufB;
+    if (full > 0) load_block<IO, GATED, KU, RAW>(bufA, x, dt, z, voff, 0, rb);
     for (uint32_t k = 0; k < full; k += 2) {
         if (prio_scale) set_priority(steps - i, prio_scale);
         // block k is in bufA: fetch block k+1 into bufB, then compute block k
-        if (k + 1 < full) load_block<IO, GATED, KU>(bufB, x, dt, z, voff, i + KU, rb);
+        if (k + 1 < full) load_block<IO, GATED, KU, RAW>(bufB, x, dt, z, voff, i + KU, rb);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufA.x[j], bufA.dt[j], GATED ? bufA.z[j] : 0.0f);
+            body(i + j, use_value<IO, RAW>(bufA.x[j]), use_value<IO, RAW>(bufA.dt[j]),
+                 GATED ? use_value<IO, RAW>(bufA.z[j]) : 0.0f);
         }
         i += KU;
         if (k + 1 >= full) break;
         // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
-        if (k + 2 < full) load_block<IO, GATED, KU>(bufA, x, dt, z, voff, i + KU, rb);
+        if (k + 2 < full) load_block<IO, GATED, KU, RAW>(bufA, x, dt, z, voff, i + KU, rb);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufB.x[j], bufB.dt[j], GATED ? bufB.z[j] : 0.0f);
+            body(i + j, use_value<IO, RAW>(bufB.x[j]), use_value<IO, RAW>(bufB.dt[j]),
+                 GATED ? use_value<IO, RAW>(bufB.z[j]) : 0.0f);
         }
         i += KU;
     }
