@@ -123,16 +123,22 @@ def mimo_lane_ops(s, R: int, matrix: bool = False) -> float:
     multiply-adds), the state's fused multiply-add, and R output fused multiply-adds =
     3 + 2R; per channel-step: dt*x[r] and D x[r] + acc[r] (2R). Matrix path (the prefill
     from rank 4: B x on the matrix cores), per state: dt*A, exp, dt*v, the state's fused
-    multiply-add and R output fused multiply-adds = 4 + R; per channel-step D x[r] + acc[r]
-    (R). Both: with bf16 I/O the widening of x and dt and the output conversion (2R + 1);
-    gated: the gate per output (6R) and, with bf16, the widening of z (R). The matrix
-    operations (2 N R flops per channel-step) are not VALU work. R = 1 gives
+    multiply-add and R output fused multiply-adds = 4 + R; with bf16 I/O and at least 4
+    states the output sums run on the matrix cores too, leaving per state dt*A, exp, dt*v,
+    the state's fused multiply-add and half a conversion (the state packed to bf16 two
+    at a time for the matrix operand) = 4.5. Per channel-step on the matrix path D x[r] +
+    acc[r] (R). All: with bf16 I/O the widening of x and dt and the output conversion
+    (R + 1 + ceil(R/2): outputs are packed two to an instruction); gated: the gate per
+    output (6R) and, with bf16, the widening of z (R). The matrix operations (2 N R flops
+    per channel-step for B x, 2 N R more for the outputs) are not VALU work. R = 1 gives
     prefill_lane_ops."""
     bf16 = s.io == "bf16"
-    per_elem = (R if matrix else 2 * R) + ((2 * R + 1) if bf16 else 0)
+    out_matrix = matrix and bf16 and s.d_state >= 4
+    per_elem = (R if matrix else 2 * R) + ((R + 1 + (R + 1) // 2) if bf16 else 0)
     if s.gated:
         per_elem += 6 * R + (R if bf16 else 0)
-    return s.d_state * ((4 + R) if matrix else (3 + 2 * R)) + per_elem
+    per_state = 4.5 if out_matrix else (4 + R) if matrix else (3 + 2 * R)
+    return s.d_state * per_state + per_elem
 
 
 def mimo_decode_bytes(s, io_bytes: int, R: int) -> float:

@@ -340,8 +340,9 @@ ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev
  * The state is d_state per channel as in ssm_scan_fwd; rank = 1 is ssm_scan_fwd_ex.
  *   x, z, y : [batch, L, d_inner, rank] of io (rank fastest); dt: [batch, L, d_inner]
  *   B, C    : [batch, L, d_state, rank] of io;  A, D, h0, h_final as ssm_scan_fwd
- * rank is 1, 2, 4 or 8 (else SSM_ERR_UNSUPPORTED). x, z and y are aligned to
- * min(16, rank * element size) bytes; other alignments, the chunking (with the same
+ * rank is 1, 2, 4 or 8 (else SSM_ERR_UNSUPPORTED). x, z and y, and from rank 4 also
+ * B and C, are aligned to min(16, rank * element size) bytes (else SSM_ERR_ALIGN);
+ * other alignments, the chunking (with the same
  * decay-horizon bound, which does not depend on rank) and the errors are those of
  * ssm_scan_fwd_ex. The workspace comes from ssm_scan_fwd_mimo_workspace (0 for an
  * invalid shape or rank). y may be x itself but must not overlap it otherwise.

@@ -165,8 +165,9 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     if (mimo) {
         // x, z and y are read and written R elements (up to 16 bytes) at a time.
         const size_t va = std::min<size_t>(16, (size_t)rank * eb);
-        if (!aligned(x, va) || !aligned(z, va) || !aligned(y, va) || (rank >= 4 && !aligned(B, va)))
-            return fail(SSM_ERR_ALIGN, "pointer alignment (x, z, y, and B for rank >= 4: min(16, rank * element) bytes)");
+        if (!aligned(x, va) || !aligned(z, va) || !aligned(y, va) ||
+            (rank >= 4 && (!aligned(B, va) || !aligned(C, va))))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x, z, y, and B, C for rank >= 4: min(16, rank * element) bytes)");
         if ((double)batch * L * d_inner * rank > 4.0e18)
             return fail(SSM_ERR_SHAPE, "problem too large");
     }

@@ -19,9 +19,10 @@
 // exponential per state: the exponential is shared by R outputs.
 //
 // From rank 4 the rescan and the summaries compute B_t x_t on the matrix cores, with
-// B_t's rows staged through LDS (mimo_bx, mimo_steps). The decode step (k_mimo_step)
-// advances one token per (layer, sequence, channel) with the VALU form of the same step
-// function.
+// B_t's rows staged through LDS (mimo_bx, mimo_steps); with bf16 inputs the rescan also
+// takes the outputs' sums over the states, sum_n C_t[n][r] h[n], there, with C_t's rows
+// staged through LDS transposed (mimo_update, CStage). The decode step (k_mimo_step) advances one token per (layer,
+// sequence, channel) with the VALU form of the same step function.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 #include "ssm_stream.h"
@@ -31,6 +32,14 @@ namespace {
 
 typedef uint32_t u32x2 __attribute__((vector_size(8)));
 typedef uint32_t u32x4 __attribute__((vector_size(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a and b rounded to bf16 (to nearest even) and packed, a in the low half: one
+// v_cvt_pk_bf16_f32 (two scalar conversions would each take one, plus a shift and an or).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 
 // The R elements of one channel in one row, as loaded (raw bits).
 template <typename IO, int R>
@@ -92,7 +101,7 @@ struct VecStream {
             } else {
 #pragma unroll
                 for (int k = 0; k < R / 2; ++k)
-                    v.w[k] = (uint32_t)f32_to_bf16(y[2 * k]) | ((uint32_t)f32_to_bf16(y[2 * k + 1]) << 16);
+                    v.w[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
             }
         } else {
 #pragma unroll
@@ -153,7 +162,7 @@ __device__ __forceinline__ void st_vec(IO *p, const float (&y)[R]) {
         } else {
 #pragma unroll
             for (int k = 0; k < R / 2; ++k)
-                v.w[k] = (uint32_t)f32_to_bf16(y[2 * k]) | ((uint32_t)f32_to_bf16(y[2 * k + 1]) << 16);
+                v.w[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
         }
     } else {
 #pragma unroll
@@ -213,68 +222,133 @@ __device__ __forceinline__ f4m mma_bf16(u32x2 a, u32x2 b, f4m c) {
                                                   c, 0, 0, 0);
 }
 
+// v[n0 + i] (i = 0..3) for the group of states n0 = 4 g (mimo_bx_group), or for all N.
+template <typename IO, int N, int R, typename P>
+__device__ __forceinline__ f4m mimo_bx_group(P brow, const VecRaw<IO, R> &xr, int g) {
+    static_assert(R == 4 || R == 8, "matrix path: ranks 4 and 8");
+    // N < 4: rows past the last state only fill result registers that are not used
+    const uint32_t n = min(4u * g + (threadIdx.x & 3u), (uint32_t)N - 1u);
+    const P p = brow + n * (uint32_t)(R * sizeof(IO));
+    f4m d = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+        for (int k = 0; k < R / 4; ++k) {
+            const u32x2 av = ld_at<u32x2>(p + 8 * k);
+            const u32x2 bv = {xr.w[2 * k], xr.w[2 * k + 1]};
+            d = mma_bf16(av, bv, d);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < R / 4; ++k) {
+            const u32x4 t = ld_at<u32x4>(p + 16 * k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(t[j]), xr.at(4 * k + j), d, 0, 0, 0);
+        }
+    }
+    return d;
+}
+
 template <typename IO, int N, int R, typename P>
 __device__ __forceinline__ void mimo_bx(P brow, const VecRaw<IO, R> &xr, float (&v)[N]) {
-    static_assert(R == 4 || R == 8, "matrix path: ranks 4 and 8");
-    const uint32_t q = threadIdx.x & 3u;
-    constexpr int G = (N + 3) / 4;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        // N < 4: rows past the last state only fill result registers that are not used
-        const uint32_t n = min(4u * g + q, (uint32_t)N - 1u);
-        const P p = brow + n * (uint32_t)(R * sizeof(IO));
-        f4m d = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (sizeof(IO) == 2) {
-#pragma unroll
-            for (int k = 0; k < R / 4; ++k) {
-                const u32x2 av = ld_at<u32x2>(p + 8 * k);
-                const u32x2 bv = {xr.w[2 * k], xr.w[2 * k + 1]};
-                d = mma_bf16(av, bv, d);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < R / 4; ++k) {
-                const u32x4 t = ld_at<u32x4>(p + 16 * k);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    d = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(t[j]), xr.at(4 * k + j), d, 0, 0, 0);
-            }
-        }
+    for (int g = 0; g < (N + 3) / 4; ++g) {
+        const f4m d = mimo_bx_group<IO, N, R>(brow, xr, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (4 * g + i < N) v[4 * g + i] = d[i];
     }
 }
 
+// Outputs on the matrix cores: bf16 inputs from rank 4, at least 4 states (fp32 inputs
+// keep the exact VALU sums: the fp32 matrix form, one v_mfma_f32_4x4x1_16b_f32 per state
+// and four ranks, measured no faster than the multiply-adds it replaces).
+template <typename IO, int N, int R>
+constexpr bool kMatOutput = kMatInput<R> && sizeof(IO) == 2 && N >= 4;
+
+// The A operands of the matrix outputs for one step: quad(n0, g) = the bf16 values
+// C_t[n0 + k][4g + l%4], k = 0..3, of lane l, packed two to a word. COpsLds reads them
+// from the wave's C slot (CStage), COpsGlb from the step's C row in global memory (the
+// ragged tail), CNone stands in where the outputs are not on the matrix cores.
+template <int N>
+struct COpsLds {
+    const SSM_LDS uint16_t *p;  // the lane's rank-(l%4) row of the step, [R][N] layout
+    __device__ __forceinline__ u32x2 quad(int n0, int g) const {
+        return *(const SSM_LDS u32x2 *)(p + 4 * g * N + n0);
+    }
+};
+template <int N, int R>
+struct COpsGlb {
+    const uint16_t *p;  // the step's C row, [N][R]
+    __device__ __forceinline__ u32x2 quad(int n0, int g) const {
+        const uint16_t *c = p + n0 * R + 4 * g + (threadIdx.x & 3u);
+        return u32x2{(uint32_t)c[0] | ((uint32_t)c[R] << 16), (uint32_t)c[2 * R] | ((uint32_t)c[3 * R] << 16)};
+    }
+};
+struct CNone {};
+
 // One step of one channel. The prefill rescan takes the matrix path from rank 4 (MAT),
 // the decode step always the VALU path: it is bound by HBM, and the matrix operands'
 // registers would cost it waves (65.3 against 58-60 us per call at rank 4). Up to rank 2
 // the two therefore perform the same operations and L decode steps equal a one-chunk
-// prefill bit for bit; from rank 4 they differ in the rounding of the input sum.
+// prefill bit for bit; from rank 4 they differ in the rounding of the sums.
 // VALU path:  xd[r] = dt x[r];  for n ascending: h[n] = fma(e2(dt A[n] log2 e), h[n],
-//             mimo_input(n));  acc[r] = fma(C[n][r], h[n], acc[r])
-// Matrix path: v = B_t x_t (mimo_bx);  for n ascending: h[n] = fma(e2(dt A[n] log2 e),
-//             h[n], dt v[n]);  acc[r] = fma(C[n][r], h[n], acc[r])
-// (r ascending, acc from 0). Bp / Cp read element e0 + n R + r of the step's B / C
-// through the scalar unit; brow is the step's B row for the matrix operands.
-template <typename IO, int N, int R, bool MAT, typename Row, typename P>
+//             mimo_input(n));  acc[r] = fma(C[n][r], h[n], acc[r])  (r ascending, acc
+//             from 0). Bp / Cp read element e0 + n R + r of the step's B / C through the
+//             scalar unit.
+// Matrix path: v = B_t x_t (mimo_bx_group, four states at a time; brow the step's B
+//             row);  for n ascending: h[n] = fma(e2(dt A[n] log2 e), h[n], dt v[n]).
+//             Outputs with bf16 inputs (kMatOutput): after each group of four states
+//             n0 .. n0+3, acc[4g .. 4g+3] += sum_k C_t[n0+k][4g+i] h[n0+k] by one
+//             v_mfma_f32_4x4x4_16b_bf16 per group g of four ranks: lane m supplies
+//             C_t[n0+k][4g + m%4] (cops, bf16 and exact) as the A operand and lane l its
+//             own h[n0+k] rounded to bf16 as the B operand, so result register i of lane
+//             l is rank 4g + i of lane l's channel (the layout of mimo_bx). The state
+//             itself stays fp32; only its copy in the output sum is rounded, which adds
+//             at most 2^-8 sum_n |C[n][r] h[n]| to y[r], the size of y's own rounding
+//             to bf16 on the way out. Otherwise acc[r] = fma(C[n][r], h[n], acc[r]) as
+//             on the VALU path.
+template <typename IO, int N, int R, bool MAT, typename Row, typename P, typename COps>
 __device__ __forceinline__ void mimo_update(float (&h)[N], const float (&A2)[N], float dv,
                                             const VecRaw<IO, R> &xr, const float (&xv)[R],
-                                            const Row &Bp, const Row &Cp, P brow, int64_t e0,
-                                            float (&acc)[R]) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+                                            const Row &Bp, const Row &Cp, P brow, const COps &cops,
+                                            int64_t e0, float (&acc)[R]) {
     if constexpr (MAT) {
-        float v[N];
-        mimo_bx<IO, N, R>(brow, xr, v);
+        // group by group of four states, so that only four input terms are live
+        constexpr bool kOut = kMatOutput<IO, N, R>;
+        f4m d[R / 4];
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const int64_t e = e0 + n * R;
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], dv * v[n]);
+        for (int g = 0; g < R / 4; ++g) d[g] = f4m{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < (N + 3) / 4; ++q) {
+            const f4m v = mimo_bx_group<IO, N, R>(brow, xr, q);
+#pragma unroll
+            for (int i = 0; i < 4 && 4 * q + i < N; ++i) {
+                const int n = 4 * q + i;
+                h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], dv * v[i]);
+                if constexpr (!kOut) {
+                    const int64_t e = e0 + n * R;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(Cp.ld(e + r), h[n], acc[r]);
+                }
+            }
+            if constexpr (kOut) {
+                const u32x2 hp = {pack_bf16x2(h[4 * q], h[4 * q + 1]), pack_bf16x2(h[4 * q + 2], h[4 * q + 3])};
+#pragma unroll
+                for (int g = 0; g < R / 4; ++g) d[g] = mma_bf16(cops.quad(4 * q, g), hp, d[g]);
+            }
+        }
+        if constexpr (kOut) {
+#pragma unroll
+            for (int g = 0; g < R / 4; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[4 * g + i] = d[g][i];
         }
     } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
         float xd[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) xd[r] = dv * xv[r];
@@ -299,11 +373,13 @@ __device__ __forceinline__ void mimo_out(float Dd, const float (&xv)[R], const f
     }
 }
 
-// One block of KU steps of loaded inputs (raw bits, widened at use).
-template <typename IO, int R, int KU>
+// One block of KU steps of loaded inputs (raw bits, widened at use), and the lane's
+// CW words of the block's C rows when the outputs are on the matrix cores.
+template <typename IO, int R, int KU, int CW>
 struct MimoBlock {
     VecRaw<IO, R> x[KU], z[KU];
     uint32_t dt[KU];
+    uint32_t cw[CW];
 };
 
 struct MimoStreams {
@@ -313,8 +389,8 @@ struct MimoStreams {
     uint32_t rbd;  // bytes per dt row
 };
 
-template <typename IO, int R, bool GATED, int KU>
-__device__ __forceinline__ void load_mimo_block(MimoBlock<IO, R, KU> &s, const VecStream<IO, R> &x,
+template <typename IO, int R, bool GATED, int KU, int CW>
+__device__ __forceinline__ void load_mimo_block(MimoBlock<IO, R, KU, CW> &s, const VecStream<IO, R> &x,
                                                 const RowStream<IO> &dt, const VecStream<IO, R> &z,
                                                 const MimoStreams &o, uint32_t row) {
 #pragma unroll
@@ -365,32 +441,99 @@ struct BStage {
     }
 };
 
-// Vector-memory instructions one block of KU steps issues: x, dt (and z) per step, and
-// the B staging loads on the matrix path.
-template <typename IO, int N, int R, bool GATED, int KU>
+// Staging of C_t rows for the matrix outputs (rescan; bf16, from rank 4). The block's C
+// rows, [KU][N][R] elements and contiguous, are loaded into registers with the block's
+// x, dt and z (kWords words per lane, one vector load). At the start of the block each
+// lane writes its elements to the wave's slot in LDS transposed to [KU][R][N], so that
+// the four operands lane l takes for rank r and states n0 .. n0+3 are one 8-byte read
+// (the lanes of one rank read the same address: a broadcast). One slot suffices: a
+// wave's LDS accesses complete in order, so a block's writes follow every read of the
+// block before.
+template <typename IO, int N, int R, int KU>
+struct CStage {
+    static constexpr int kRowBytes = N * R * (int)sizeof(IO);
+    static constexpr int kBlockBytes = KU * kRowBytes;
+    static constexpr int kWords = (kBlockBytes + 255) / 256;  // per lane
+    static constexpr int kSlotElems = KU * N * R;
+    static_assert(sizeof(IO) == 2, "bf16 operands");
+    static_assert(kWords == 1 || kWords == 2 || kWords == 4, "C block of 4 .. 1024 bytes");
+    __amdgpu_buffer_rsrc_t r;  // this walk's C rows, from its first row on
+    SSM_LDS uint16_t *slot;    // the wave's kSlotElems elements
+    uint32_t voff;             // the lane's first byte in a block (clamped into the block)
+    __device__ __forceinline__ void init(const IO *C0, SSM_LDS uint16_t *s) {
+        r = __builtin_amdgcn_make_buffer_rsrc(const_cast<IO *>(C0), 0, -1, kRsrcWord3);
+        slot = s;
+        voff = min((threadIdx.x & 63u) * 4u * kWords, (uint32_t)(kBlockBytes - 4 * kWords));
+    }
+    __device__ __forceinline__ void load(uint32_t (&w)[kWords], uint32_t row) const {
+        const uint32_t so = row * (uint32_t)kRowBytes;
+        if constexpr (kWords == 1) {
+            w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, so, 0);
+        } else if constexpr (kWords == 2) {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, so, 0);
+            w[0] = t[0]; w[1] = t[1];
+        } else {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, so, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = t[k];
+        }
+    }
+    __device__ __forceinline__ void put(const uint32_t (&w)[kWords]) const {
+        // with fewer than 64 * kWords words in a block the lanes past them only reread
+        // the block's last words: they write nothing
+        if constexpr (kBlockBytes < 256 * kWords)
+            if ((threadIdx.x & 63u) * 4u * kWords >= (uint32_t)kBlockBytes) return;
+        const uint32_t e0 = voff / 2u;  // the lane's first element
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t e = e0 + (uint32_t)(2 * k + j);
+                const uint32_t st = e / (uint32_t)(N * R), n = (e / R) % N, rr = e % R;
+                slot[(st * R + rr) * N + n] = (uint16_t)(j ? w[k] >> 16 : w[k]);
+            }
+        }
+    }
+    // The lane's operands for step j of the block (rank 4g + l%4 at [4 g N + n]).
+    __device__ __forceinline__ COpsLds<N> ops(int j) const {
+        return COpsLds<N>{slot + (j * R + (int)(threadIdx.x & 3u)) * N};
+    }
+};
+
+// Vector-memory instructions one block of KU steps issues: x, dt (and z) per step, the
+// B staging loads on the matrix path and the C load when the outputs are on it too.
+template <typename IO, int N, int R, bool GATED, int KU, bool WITH_C>
 constexpr int block_vm_ops() {
     constexpr int vx = VecRaw<IO, R>::kBytes == 32 ? 2 : 1;
-    return KU * (vx + 1 + (GATED ? vx : 0)) + (kMatInput<R> ? BStage<IO, N, R, KU>::kLoads : 0);
+    return KU * (vx + 1 + (GATED ? vx : 0)) + (kMatInput<R> ? BStage<IO, N, R, KU>::kLoads : 0) +
+           (WITH_C && kMatOutput<IO, N, R> ? 1 : 0);
 }
 
-// Calls body(i, x_i, dt_i, z_i, brow_i) for i = 0 .. steps-1, with the next block of KU
-// rows in flight while the current one is computed (as stream_steps does for scalar
-// rows). brow_i is step i's row of B (an LDS pointer from the staging ring, or, in the
-// ragged tail, a global pointer) on the matrix path, and unused (null) otherwise.
-// B0: the walk's first B row (global; matrix path only); ring: the wave's 2 slots.
-template <typename IO, int N, int R, bool GATED, int KU, typename Body>
+// Calls body(i, x_i, dt_i, z_i, brow_i, cops_i) for i = 0 .. steps-1, with the next
+// block of KU rows in flight while the current one is computed (as stream_steps does for
+// scalar rows). brow_i is step i's row of B (an LDS pointer from the staging ring, or,
+// in the ragged tail, a global pointer) on the matrix path, and unused (null) otherwise;
+// cops_i gives the step's C operands of the matrix outputs (WITH_C with kMatOutput;
+// CNone otherwise). B0, C0: the walk's first B and C rows (global); ring: the wave's 2
+// B slots; cslot: the wave's C slot (WITH_C with kMatOutput only).
+template <typename IO, int N, int R, bool GATED, int KU, bool WITH_C, typename Body>
 __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowStream<IO> &dt,
                                            const VecStream<IO, R> &z, const MimoStreams &o,
-                                           const IO *B0, SSM_LDS char *ring, uint32_t steps,
-                                           uint32_t prio_scale, Body &&body) {
+                                           const IO *B0, SSM_LDS char *ring, const IO *C0,
+                                           SSM_LDS uint16_t *cslot, uint32_t steps, uint32_t prio_scale,
+                                           Body &&body) {
     constexpr bool kMat = kMatInput<R>;
-    constexpr int kOps = block_vm_ops<IO, N, R, GATED, KU>();
+    constexpr bool kC = WITH_C && kMatOutput<IO, N, R>;
+    constexpr int kOps = block_vm_ops<IO, N, R, GATED, KU, WITH_C>();
     typedef BStage<IO, N, R, KU> Stg;
+    typedef CStage<uint16_t, N, R, KU> CStg;
     Stg st;
+    CStg cst;
     if constexpr (kMat) {
         st.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<IO *>(B0), 0, -1, kRsrcWord3);
         st.ring = ring;
     }
+    if constexpr (kC) cst.init((const uint16_t *)C0, cslot);
     // This block's staged rows are complete once only the next block's loads are pending.
     // On the matrix path a next block is always issued (the last block loads its own rows
     // again, into the idle buffer and slot), so that this wait is one straight-line
@@ -408,12 +551,21 @@ __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowS
         if constexpr (kMat) return st.row_at(slot, j);
         else return (const SSM_LDS char *)nullptr;
     };
+    auto cops = [&](int j) {
+        if constexpr (kC) return cst.ops(j);
+        else return CNone{};
+    };
+    constexpr int CW = kC ? CStg::kWords : 1;
+    auto load_block = [&](MimoBlock<IO, R, KU, CW> &buf, uint32_t row) {
+        load_mimo_block<IO, R, GATED, KU>(buf, x, dt, z, o, row);
+        if constexpr (kC) cst.load(buf.cw, row);
+    };
     const uint32_t full = steps / KU;
     uint32_t i = 0;
-    MimoBlock<IO, R, KU> bufA, bufB;
+    MimoBlock<IO, R, KU, CW> bufA, bufB;
     if (full > 0) {
         if constexpr (kMat) st.stage(0, 0);
-        load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, 0);
+        load_block(bufA, 0);
     }
     for (uint32_t k = 0; k < full; k += 2) {
         if (prio_scale) set_priority(steps - i, prio_scale);
@@ -421,13 +573,14 @@ __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowS
         if (kMat || more1) {
             const uint32_t nxt = more1 ? i + KU : i;
             if constexpr (kMat) st.stage(1, nxt);
-            load_mimo_block<IO, R, GATED, KU>(bufB, x, dt, z, o, nxt);
+            load_block(bufB, nxt);
         }
         ready();
+        if constexpr (kC) cst.put(bufA.cw);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufA.x[j], RowStream<IO>::widen(bufA.dt[j]), bufA.z[j], brow(0, j));
+            body(i + j, bufA.x[j], RowStream<IO>::widen(bufA.dt[j]), bufA.z[j], brow(0, j), cops(j));
         }
         i += KU;
         if (!more1) break;
@@ -435,24 +588,26 @@ __device__ __forceinline__ void mimo_steps(const VecStream<IO, R> &x, const RowS
         if (kMat || more2) {
             const uint32_t nxt = more2 ? i + KU : i;
             if constexpr (kMat) st.stage(0, nxt);
-            load_mimo_block<IO, R, GATED, KU>(bufA, x, dt, z, o, nxt);
+            load_block(bufA, nxt);
         }
         ready();
+        if constexpr (kC) cst.put(bufB.cw);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
-            body(i + j, bufB.x[j], RowStream<IO>::widen(bufB.dt[j]), bufB.z[j], brow(1, j));
+            body(i + j, bufB.x[j], RowStream<IO>::widen(bufB.dt[j]), bufB.z[j], brow(1, j), cops(j));
         }
         i += KU;
     }
     if (prio_scale) __builtin_amdgcn_s_setprio(0);
-    for (; i < steps; ++i) {  // ragged tail, one step at a time, B rows read directly
+    for (; i < steps; ++i) {  // ragged tail, one step at a time, B and C rows read directly
         const VecRaw<IO, R> xv = x.ld(o.vx, i * o.rbx);
         const float dv = dt.ld(o.vd, i * o.rbd);
         VecRaw<IO, R> zv{};
         if (GATED) zv = z.ld(o.vx, i * o.rbx);
         const char *g = kMat ? (const char *)B0 + (size_t)i * BStage<IO, N, R, KU>::kRowBytes : nullptr;
-        body(i, xv, dv, zv, g);
+        if constexpr (kC) body(i, xv, dv, zv, g, COpsGlb<N, R>{(const uint16_t *)C0 + (size_t)i * N * R});
+        else body(i, xv, dv, zv, g, CNone{});
     }
 }
 
@@ -489,13 +644,14 @@ __device__ __forceinline__ MimoStreams mimo_offsets(const ScanArgs &a, int64_t d
 }
 
 // Steps of x / z / y rows are R elements per channel: blocks of 4 steps for R <= 2,
-// 2 for wider ranks (keeps the ping-pong buffers within the register budget).
-template <int R> constexpr int kMimoKU = R <= 2 ? 4 : 2;
+// 2 for wider ranks with bf16 inputs and 1 with fp32 ones (keeps the ping-pong buffers
+// within the register budget of the waves the rescan is compiled for).
+template <typename IO, int R> constexpr int kMimoKU = R <= 2 ? 4 : sizeof(IO) == 4 ? 1 : 2;
 
 // ---------------------------------------------------------------- chunk summary
 template <typename IO, int N, int R>
 __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
-    constexpr int KU = kMimoKU<R>;
+    constexpr int KU = kMimoKU<IO, R>;
     __shared__ __attribute__((aligned(16))) char ring_mem[4 * Ring<IO, N, R, KU>::kBytes];
     const LaneId ln = lane_id(a);
     const int c = blockIdx.y;
@@ -520,9 +676,10 @@ __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
     const UniRow<IO, N * R> Bp(a.B, ln.b * a.L * N * R);
     SSM_LDS char *ring = (SSM_LDS char *)ring_mem + (threadIdx.x / 64) * Ring<IO, N, R, KU>::kBytes;
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
-    mimo_steps<IO, N, R, false, KU>(xs, dws, xs, o, (const IO *)a.B + rw * N * R, ring, T - ts,
-                                    kSummaryPrioScale,
-                                    [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &, auto brow) {
+    mimo_steps<IO, N, R, false, KU, false>(xs, dws, xs, o, (const IO *)a.B + rw * N * R, ring, nullptr,
+                                           nullptr, T - ts, kSummaryPrioScale,
+                                           [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &,
+                                               auto brow, auto) {
         const int64_t t = t0 + ts + i;
         S += (double)dv;
         if constexpr (kMatInput<R>) {
@@ -550,16 +707,16 @@ __global__ __launch_bounds__(256) void k_mimo_summary(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------- rescan + epilogue
-// Waves per SIMD the rescan is compiled for: 5 up to rank 4 (the planner then cuts
-// the sequence into enough chunks for 5 waves on every SIMD). Rank 8 is left to the
-// compiler (4 waves with bf16 inputs, 3 with fp32 and a gate, whose registers would
-// otherwise spill).
-template <int R> constexpr int kMimoWavesPerSimd = R <= 4 ? 5 : 1;
+// Waves per SIMD the rescan is compiled for: 5 up to rank 4, 4 at rank 8 (the planner
+// cuts the sequence into enough chunks for that many waves on every SIMD).
+template <int R> constexpr int kMimoWavesPerSimd = R <= 4 ? 5 : 4;
 
 template <typename IO, int N, int R, bool GATED>
 __global__ __launch_bounds__(256, kMimoWavesPerSimd<R>) void k_mimo_scan(ScanArgs a) {
-    constexpr int KU = kMimoKU<R>;
+    constexpr int KU = kMimoKU<IO, R>;
+    constexpr int kCSlot = kMatOutput<IO, N, R> ? CStage<uint16_t, N, R, KU>::kSlotElems : 8;
     __shared__ __attribute__((aligned(16))) char ring_mem[4 * Ring<IO, N, R, KU>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t cslot_mem[4 * kCSlot];
     const LaneId ln = lane_id(a);
     const int c = blockIdx.y;
     const int64_t t0 = (int64_t)c * a.T;
@@ -584,13 +741,16 @@ __global__ __launch_bounds__(256, kMimoWavesPerSimd<R>) void k_mimo_scan(ScanArg
     const UniRow<IO, N * R> Bp(a.B, ln.b * a.L * N * R);
     const UniRow<IO, N * R> Cp(a.C, ln.b * a.L * N * R);
     SSM_LDS char *ring = (SSM_LDS char *)ring_mem + (threadIdx.x / 64) * Ring<IO, N, R, KU>::kBytes;
-    mimo_steps<IO, N, R, GATED, KU>(xs, dts, zs, o, (const IO *)a.B + t_row0 * N * R, ring, steps, steps,
-                                    [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &zr, auto brow) {
+    SSM_LDS uint16_t *cslot = (SSM_LDS uint16_t *)cslot_mem + (threadIdx.x / 64) * kCSlot;
+    mimo_steps<IO, N, R, GATED, KU, true>(xs, dts, zs, o, (const IO *)a.B + t_row0 * N * R, ring,
+                                          (const IO *)a.C + t_row0 * N * R, cslot, steps, steps,
+                                          [&](uint32_t i, const VecRaw<IO, R> &xr, float dv, const VecRaw<IO, R> &zr,
+                                              auto brow, auto cops) {
         const int64_t t = t0 + i;
         float xv[R], acc[R], yv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
-        mimo_update<IO, N, R, kMatInput<R>>(h, A2, dv, xr, xv, Bp, Cp, brow, t * N * R, acc);
+        mimo_update<IO, N, R, kMatInput<R>>(h, A2, dv, xr, xv, Bp, Cp, brow, cops, t * N * R, acc);
         mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
         if (ln.live) ys.st(o.vx, i * o.rbx, yv);
     });
@@ -695,7 +855,7 @@ __global__ __launch_bounds__(256) void k_mimo_step(StepArgs a) {
     float xv[R], acc[R], yv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) xv[r] = xr.at(r);
-    mimo_update<IO, N, R, false>(h, A2, dv, xr, xv, Bp, Cp, (const char *)nullptr, 0, acc);
+    mimo_update<IO, N, R, false>(h, A2, dv, xr, xv, Bp, Cp, (const char *)nullptr, CNone{}, 0, acc);
     mimo_out<IO, R, GATED>(Dd, xv, acc, zr, yv);
 #pragma unroll
     for (int n = 0; n < N; ++n) sh[tid * P + n] = h[n];

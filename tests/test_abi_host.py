@@ -229,8 +229,8 @@ def test_trapezoid_argument_errors(lib):
 def test_mimo_argument_errors(lib):
     p = lambda v: None if v is None else ctypes.c_void_p(v)
 
-    def scan(x=0x100000, z=None, y=0x200000, B=0x1000, N=4, R=4, io=1, L=8, ws=None, wsb=0, Dn=4):
-        return lib.ssm_scan_fwd_mimo(p(x), p(0x1000), p(0x1000), p(B), p(0x1000), p(0x1000), p(z),
+    def scan(x=0x100000, z=None, y=0x200000, B=0x1000, C=0x1000, N=4, R=4, io=1, L=8, ws=None, wsb=0, Dn=4):
+        return lib.ssm_scan_fwd_mimo(p(x), p(0x1000), p(0x1000), p(B), p(C), p(0x1000), p(z),
                                      None, p(y), None, 1, L, Dn, N, R, io, 0, p(ws), wsb, None)
     for bad in (0, 3, 16, -1):
         assert scan(R=bad) == UNSUP
@@ -239,7 +239,11 @@ def test_mimo_argument_errors(lib):
     assert scan(x=0x100004) == ALIGN          # bf16, rank 4: 8-byte vectors
     assert scan(y=0x200002, R=2) == ALIGN     # bf16, rank 2: 4-byte vectors
     assert scan(z=0x300008, R=8, io=0) == ALIGN   # fp32, rank 8: 16-byte vectors
-    assert scan(B=0x1002) == ALIGN            # B, C through the scalar unit: 4 bytes
+    assert scan(B=0x1002, R=2) == ALIGN       # up to rank 2 B, C go through the scalar unit: 4 bytes
+    assert scan(C=0x1002, R=1) == ALIGN
+    assert scan(B=0x1004) == ALIGN            # from rank 4 B, C are vector loads: min(16, R * element)
+    assert scan(C=0x1004) == ALIGN
+    assert scan(C=0x1008, R=8) == ALIGN
     assert scan(x=None) == NULL
     # workspace: two [n_chunks - 1][batch][d_inner][d_state] fp32 arrays. Ranks 2 and 4
     # are planned for 5 waves per SIMD (40 chunks of the 256k sequence over 128

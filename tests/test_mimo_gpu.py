@@ -189,7 +189,9 @@ def test_mimo_decode_equals_one_chunk_prefill(io, R):
     # L decode steps (one layer, n_seq = batch) against a one-chunk prefill of the same
     # tokens. Up to rank 2 both run the same VALU operations: bit for bit. From rank 4
     # the prefill sums B_t x_t on the matrix cores and the decode on the VALU: the same
-    # fp32 results up to the rounding of that sum.
+    # fp32 states up to the rounding of that sum. With bf16 inputs the prefill's output
+    # sums run there too, on the state rounded to bf16 (an error of the order of y's own
+    # rounding to bf16); with fp32 inputs they stay fp32 multiply-adds.
     b, L, Dn, N = 3, 40, 96, 16
     shape, d = _draw((b, L, Dn, N, R, io, True, True, L), seed=5)
     say("MIMO prefill vs decode", io)
@@ -207,7 +209,8 @@ def test_mimo_decode_equals_one_chunk_prefill(io, R):
     if R <= 2:
         assert bitwise_equal(yd, y) and bitwise_equal(h[0], hf)
     else:
-        # y: one rounding step of the output type; h: fp32 rounding over L = 40 steps
+        # y: one rounding step of the output type (bf16: plus the bf16 operand of the
+        # output sum); h: fp32 rounding over L = 40 steps
         assert rel_err(yd, oracle.to_f64(y)) <= (1e-5 if io == "f32" else 2 ** -7)
         assert rel_err(h[0], oracle.to_f64(hf)) <= 1e-5
 
