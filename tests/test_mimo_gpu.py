@@ -32,6 +32,11 @@ CASES = [
     (1, 1, 1, 4, 4, "f32", True, True, 0),            # one step, one channel
     (1, 4501, 33, 16, 4, "f32", True, True, 64),      # 71 chunks
     (2, 777, 96, 16, 2, "bf16", False, True, 5),      # chunks shorter than a register block
+    # bf16 from rank 4: outputs on the matrix cores (at least 4 states), C staged in LDS
+    (1, 300, 130, 16, 4, "bf16", True, True, 45),     # odd chunks: a ragged step each
+    (2, 301, 96, 4, 4, "bf16", True, True, 37),       # C block of 64 bytes: 16 lanes stage it
+    (1, 250, 80, 8, 8, "bf16", False, False, 33),     # N 8, rank 8, ragged steps
+    (1, 100, 64, 2, 4, "bf16", True, False, 0),       # 2 states: B x on the matrix cores only
 ]
 
 
