@@ -346,6 +346,12 @@ ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev
  * decay-horizon bound, which does not depend on rank) and the errors are those of
  * ssm_scan_fwd_ex. The workspace comes from ssm_scan_fwd_mimo_workspace (0 for an
  * invalid shape or rank). y may be x itself but must not overlap it otherwise.
+ * Arithmetic: the state is fp32 throughout. From rank 4 the sum over ranks for B_t x_t
+ * is formed on the matrix cores (exact products, fp32 sums), and with bf16 io (and
+ * d_state >= 4) so are the output sums over states, whose state operand is rounded to
+ * bf16 (to nearest even): that adds at most 2^-8 sum_n |C[n][r] h[n]| to y[r], the
+ * size of y's own rounding to bf16. With fp32 io the output sums are fp32 fused
+ * multiply-adds, as in the decode.
  *
  * ssm_step_mimo: one decode token of the same recurrence for every (layer, sequence,
  * channel), h updated in place.
@@ -353,8 +359,9 @@ ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev
  *   x_t, z_t, y_t : [n_layers, n_seq, d_inner, rank] of io;  dt_t: [n_layers, n_seq, d_inner]
  *   B_t, C_t   : [n_layers, n_seq, d_state, rank] of io (4-byte aligned)
  *   A, D       : as ssm_step
- * Per channel the fp32 operations are, in this order (the same as the prefill's, so
- * L steps equal a one-chunk prefill, chunk_len = L, bit for bit):
+ * Per channel the fp32 operations are, in this order (up to rank 2 the same as the
+ * prefill's, so L steps equal a one-chunk prefill, chunk_len = L, bit for bit; from
+ * rank 4 the prefill forms its sums as described above):
  *   xd[r] = dt x[r];  for n ascending: u = B[n][0] xd[0], then u = fma(B[n][r], xd[r], u)
  *   for r = 1 .. rank-1; h[n] = fma(e2(dt (A[n] log2 e)), h[n], u);
  *   acc[r] = fma(C[n][r], h[n], acc[r]) (acc from 0);  y[r] = fma(D, x[r], acc[r]),
