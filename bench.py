@@ -346,9 +346,11 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
 
 
 def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None, trap=False,
-               mimo=0):
+               mimo=0, one_call=False):
     """conv_k None: ssm_step; else ssm_step_fused with a conv_k-tap filter. trap:
-    ssm_step_trap, given the previous token's x and B. mimo R > 0: ssm_step_mimo."""
+    ssm_step_trap, given the previous token's x and B. mimo R > 0: ssm_step_mimo.
+    one_call: each token is one call over all layers (n_layers = Ln: the [layers, seqs,
+    ...] tensors as they are) instead of one call per layer."""
     dev = "cuda"
     Ln, S, Dn, N = shape.n_layers, shape.n_seq, shape.d_inner, shape.d_state
     par = workloads.make_decode_params(shape, dev)
@@ -369,30 +371,34 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
     h_l = [h[l:l + 1] for l in range(Ln)]
     per_layer = [{k: (None if v is None else v[l:l + 1]) for k, v in t.items()} for t in toks
                  for l in range(Ln)]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps * Ln)]
+    calls = 1 if one_call else Ln  # calls per token
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps * calls)]
+
+    def call(t, pv, hh, A, D, p, yy):
+        if fused:
+            ssm.ssm_step_fused(hh, p["conv_state"], t["x"], t["dt"], A, t["B"], t["C"], D, t["z"],
+                               conv_w=p["conv_w"], conv_b=p["conv_b"], dt_bias=p["dt_bias"], y_t=yy)
+        elif trap:
+            ssm.ssm_step_trap(hh, pv["x"], pv["B"], t["x"], t["dt"], A, t["B"], t["C"], D, t["z"],
+                              y_t=yy)
+        elif mimo:
+            ssm.ssm_step_mimo(hh, t["x"], t["dt"], A, t["B"], t["C"], D, t["z"], y_t=yy)
+        else:
+            ssm.ssm_step(hh, t["x"], t["dt"], A, t["B"], t["C"], D, t["z"], y_t=yy)
 
     def token(k, timed):
-        for l in range(Ln):
-            t = per_layer[k * Ln + l]
+        for l in range(calls):
             if timed:
-                ev[2 * ((k - warmup) * Ln + l)].record()
-            if fused:
-                p = ist_l[l]
-                ssm.ssm_step_fused(h_l[l], p["conv_state"], t["x"], t["dt"], A_l[l], t["B"], t["C"],
-                                   D_l[l], t["z"], conv_w=p["conv_w"], conv_b=p["conv_b"],
-                                   dt_bias=p["dt_bias"], y_t=y[l:l + 1])
-            elif trap:
-                pv = per_layer[(k - 1) * Ln + l] if k > 0 else {"x": None, "B": None}
-                ssm.ssm_step_trap(h_l[l], pv["x"], pv["B"], t["x"], t["dt"], A_l[l], t["B"], t["C"],
-                                  D_l[l], t["z"], y_t=y[l:l + 1])
-            elif mimo:
-                ssm.ssm_step_mimo(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
-                                  y_t=y[l:l + 1])
+                ev[2 * ((k - warmup) * calls + l)].record()
+            if one_call:
+                pv = toks[k - 1] if k > 0 else {"x": None, "B": None}
+                call(toks[k], pv, h, par["A"], par["D"], ist if fused else None, y)
             else:
-                ssm.ssm_step(h_l[l], t["x"], t["dt"], A_l[l], t["B"], t["C"], D_l[l], t["z"],
-                             y_t=y[l:l + 1])
+                pv = per_layer[(k - 1) * Ln + l] if k > 0 else {"x": None, "B": None}
+                call(per_layer[k * Ln + l], pv, h_l[l], A_l[l], D_l[l], ist_l[l] if fused else None,
+                     y[l:l + 1])
             if timed:
-                ev[2 * ((k - warmup) * Ln + l) + 1].record()
+                ev[2 * ((k - warmup) * calls + l) + 1].record()
 
     for k in range(warmup):
         token(k, False)
@@ -422,14 +428,14 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
         gev[1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern = gev[0].elapsed_time(gev[1]) / (steps * Ln)
+        kern = gev[0].elapsed_time(gev[1]) / (steps * calls)
     else:
         t0 = time.perf_counter()
         for k in range(warmup, warmup + steps):
             token(k, True)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps * Ln)) / (steps * Ln)
+        kern = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps * calls)) / (steps * calls)
     io_bytes = 2 if shape.io == "bf16" else 4
     nbytes = decode_bytes(shape, io_bytes)
     lane_ops = decode_lane_ops(shape)
@@ -446,10 +452,10 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3,
         "elements_per_step": Ln * S * Dn, "bytes_per_step": nbytes,
-        "lane_ops_per_elem": lane_ops, "dominant_ms": kern * Ln, "per_call_ms": kern,
+        "lane_ops_per_elem": lane_ops, "dominant_ms": kern * calls, "per_call_ms": kern,
         "kernel": "k_mimo_step" if mimo else "k_step", "source": "mimo_step" if mimo else "step",
-        "phases_ms": {"ssm_step_per_layer": kern},
-        "graph": graph,
+        "phases_ms": {"ssm_step_all_layers" if one_call else "ssm_step_per_layer": kern},
+        "graph": graph, "calls_per_token": calls,
     }
     return info, None
 
@@ -639,6 +645,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="decode: launch the per-layer calls eagerly instead of replaying one "
                          "captured HIP graph per token")
+    ap.add_argument("--one-call", action="store_true",
+                    help="decode: one call per token over all layers (n_layers = 28 in one "
+                         "launch) instead of one call per layer")
     ap.add_argument("--fused", action="store_true",
                     help="through ssm_scan_fwd_fused / ssm_step_fused (conv + silu and softplus "
                          "fused into the load stage)")
@@ -692,7 +701,7 @@ def main():
     if is_decode:
         info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph,
                              conv_k=args.conv_k if args.fused else None, trap=args.trap,
-                             mimo=args.mimo)
+                             mimo=args.mimo, one_call=args.one_call)
     else:
         if args.backward and (shape.complex_state or args.fused):
             print("--backward applies to the real-state prefill workloads", file=sys.stderr)
@@ -714,7 +723,7 @@ def main():
     hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
     traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "") + \
         ("+backward" if args.backward else "") + ("+trap" if args.trap else "") + \
-        (f"+mimo{args.mimo}" if args.mimo else "")
+        (f"+mimo{args.mimo}" if args.mimo else "") + ("+one_call" if is_decode and args.one_call else "")
     traffic = traffic_for(info, traffic_key)
     if hbm_frac >= alu_frac:
         roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
@@ -733,7 +742,7 @@ def main():
     if is_decode:
         cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
-               "calls_per_step": shape.n_layers, "hip_graph_per_token": info["graph"]}
+               "calls_per_step": info["calls_per_token"], "hip_graph_per_token": info["graph"]}
         if args.fused:
             cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
                                   "softplus_dt": True, "entry_point": "ssm_step_fused"}

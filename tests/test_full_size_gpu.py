@@ -47,6 +47,7 @@ def test_full_size_batched_decode_512_steps():
     par = make_decode_params(shape, "cuda")
     h = torch.zeros((Ln, S, Dn, N), device="cuda")
     h_rep = torch.zeros_like(h)
+    h_pl = torch.zeros_like(h)  # advanced by one call per layer, as bench.py times by default
     # 4096 sampled (layer, sequence, channel) triples, followed through every step
     g = torch.Generator().manual_seed(21)
     flat = torch.randperm(Ln * S * Dn, generator=g)[:4096]
@@ -63,10 +64,16 @@ def test_full_size_batched_decode_512_steps():
         y = ssm.ssm_step(h, inp["x"], inp["dt"], par["A"], inp["B"], inp["C"], par["D"], inp["z"])
         y_rep = ssm.ssm_step_replay(h_rep, inp["x"], inp["dt"], par["A"], inp["B"], inp["C"],
                                     par["D"], inp["z"])
+        y_pl = torch.empty_like(y)
+        for l in range(Ln):
+            sl = lambda v: v[l:l + 1]
+            ssm.ssm_step(sl(h_pl), sl(inp["x"]), sl(inp["dt"]), sl(par["A"]), sl(inp["B"]), sl(inp["C"]),
+                         sl(par["D"]), sl(inp["z"]), y_t=sl(y_pl))
         if k in compare_at:
             torch.cuda.synchronize()
             assert bitwise_equal(y, y_rep), f"y differs from replay at step {k}"
             assert bitwise_equal(h, h_rep), f"state differs from replay at step {k}"
+            assert bitwise_equal(y, y_pl) and bitwise_equal(h, h_pl), f"per-layer calls differ at step {k}"
         # the oracle follows the sampled triples as 4096 one-channel "layers"
         xs = inp["x"][lic, sic, dic].cpu().view(1, 1, -1)
         ds = inp["dt"][lic, sic, dic].cpu().view(1, 1, -1)
