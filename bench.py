@@ -524,12 +524,33 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False, m
         oracle.scan_threaded(*args, threads=threads, complex_state=shape.complex_state)
     dt = time.perf_counter() - t0
     elems = shape.batch * shape.L * k
+    # The same oracle on one thread, over one thread's share of the sample (the first
+    # k / threads channels), so that it takes about as long as the run above.
+    k1 = max(1, k // threads)
+    t1 = time.perf_counter()
+    if trap or mimo:
+        work(np.arange(k1))
+    else:
+        import numpy as np
+
+        def one(t, dim):  # the first k1 channels (torch tensors, or numpy after the input stage)
+            if t is None:
+                return None
+            v = t[:, :, :k1] if dim == 2 else t[:k1]
+            return v.contiguous() if hasattr(v, "contiguous") else np.ascontiguousarray(v)
+        oracle.scan_threaded(one(args[0], 2), one(args[1], 2), one(args[2], 0), args[3], args[4],
+                             one(args[5], 0), one(args[6], 2), threads=1, complex_state=shape.complex_state)
+    dt1 = time.perf_counter() - t1
+    elems1 = shape.batch * shape.L * k1
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{k} of {shape.d_inner} channels over all {shape.L} steps x batch "
                       f"{shape.batch} ({elems} elements, {dt:.1f} s wall), fp64 sequential loop "
                       f"per channel{' (exponential-trapezoidal)' if trap else ''}"
                       f"{f' (MIMO, rank {mimo})' if mimo else ''}, channels split "
-                      f"over {threads} threads"}
+                      f"over {threads} threads",
+            "value_1_core": elems1 / dt1,
+            "sample_1_core": f"the first {k1} of those channels on one thread ({elems1} elements, "
+                             f"{dt1:.1f} s wall)"}
 
 
 def cpu_baseline_backward(shape, d, torch, workloads, threads):
@@ -560,7 +581,14 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
     for t in ts: t.join()
     dtm = time.perf_counter() - t0
     elems = shape.batch * shape.L * k
+    t1 = time.perf_counter()
+    work(parts[0])  # one thread's share on one thread, timed alone
+    dt1 = time.perf_counter() - t1
+    elems1 = shape.batch * shape.L * len(parts[0])
     return {"value": elems / dtm, "unit": "elements/s", "cores": len(parts), "kind": "oracle",
+            "value_1_core": elems1 / dt1,
+            "sample_1_core": f"the first {len(parts[0])} of those channels on one thread ({elems1} elements, "
+                             f"{dt1:.1f} s wall)",
             "sample": f"backward: {k} of {shape.d_inner} channels over all {shape.L} steps x batch "
                       f"{shape.batch} ({elems} elements, {dtm:.1f} s wall), fp64 loops per channel "
                       f"(forward keeping every state, then backward), channels split over "
@@ -622,6 +650,12 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
     for t in ts: t.join()
     dtm = time.perf_counter() - t0
     elems = Ln * S * Dn * tokens
+    # one thread's share of the layers on one thread, timed alone
+    n1 = max(1, Ln // len(groups))
+    t1 = time.perf_counter()
+    work(0, n1)
+    dt1 = time.perf_counter() - t1
+    elems1 = n1 * S * Dn * tokens
     what = ("fused decode step (conv + silu, softplus, scan)" if fused else
             "exponential-trapezoidal decode step" if trap else
             f"MIMO decode step (rank {mimo})" if mimo else "decode step")
@@ -629,7 +663,9 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
             "sample": f"{what}: all {Ln} layers x {S} of {shape.n_seq} sequences x {Dn} channels, "
                       f"{tokens} tokens (token 0's inputs each time) with the state carried ({elems} "
                       f"elements, {dtm:.1f} s wall), "
-                      f"fp64, layers split over {len(groups)} threads"}
+                      f"fp64, layers split over {len(groups)} threads",
+            "value_1_core": elems1 / dt1,
+            "sample_1_core": f"the first {n1} of those layers on one thread ({elems1} elements, {dt1:.1f} s wall)"}
 
 
 def main():
