@@ -27,7 +27,7 @@ __all__ = [
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
-    "ssm_scan_fwd_mimo_chunk_len",
+    "ssm_scan_fwd_mimo_chunk_len", "selective_scan",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
-    "ssm_scan_fwd_mimo_chunk_len",
+    "ssm_scan_fwd_mimo_chunk_len", "selective_scan",
 ]
 
 
@@ -542,6 +542,39 @@ def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk
                           _ptr(workspace), ws_bytes, _stream(x))
     _check(st)
     return out
+
+
+class _SelectiveScan(torch.autograd.Function):
+    """ssm_scan_fwd_ex forwards, ssm_scan_bwd backwards (both in the library's kernels)."""
+
+    @staticmethod
+    def forward(ctx, x, dt, A, B, C, D, z, h0, chunk_len):
+        y, h_final = ssm_scan_fwd_ex(x, dt, A, B, C, D, z, h0, chunk_len=chunk_len)
+        ctx.save_for_backward(x, dt, A, B, C, D, z, h0)
+        ctx.chunk_len = chunk_len
+        return y, h_final
+
+    @staticmethod
+    def backward(ctx, dy, dh_final):
+        x, dt, A, B, C, D, z, h0 = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        if dy is None:
+            dy = torch.zeros_like(x)
+        g = ssm_scan_bwd(x, dt, A, B, C, D, z, h0, dy=dy.to(x.dtype).contiguous(),
+                         dh_final=None if dh_final is None else dh_final.float().contiguous(),
+                         chunk_len=ctx.chunk_len, want_dz=z is not None and need[6],
+                         want_dh0=h0 is not None and need[7])
+        cast = lambda t, like: None if t is None else t.to(like.dtype)
+        grads = (g["dx"], g["ddt"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
+                 cast(g["dD"], D), g["dz"], g["dh0"], None)
+        return tuple(gr if (i < len(need) and need[i]) else None for i, gr in enumerate(grads))
+
+
+def selective_scan(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0):
+    """The real-state prefill as a differentiable function: returns (y, h_final), with
+    gradients for x, dt, A, B, C, D, z and h0 from ssm_scan_bwd (dB, dC, dA and dD are
+    computed in float32 and returned in their inputs' dtypes)."""
+    return _SelectiveScan.apply(x, dt, A, B, C, D, z, h0, chunk_len)
 
 
 # ------------------------------------------------------------------ MIMO projections

@@ -197,3 +197,36 @@ def test_backward_full_size_long_context_sampled():
         e = rel_err(v, ref[k])
         assert e <= tol, f"{k}: error {e:.3e}"
     assert rel_err(got["dh0"].index_select(1, idx.cuda()).cpu(), ref["dh0"]) <= tol
+
+
+@pytest.mark.parametrize("io,gated,with_h0", [("f32", True, True), ("bf16", True, False), ("f32", False, False)])
+def test_selective_scan_autograd(io, gated, with_h0):
+    # selective_scan: the prefill as a torch.autograd.Function. Its gradients are
+    # ssm_scan_bwd's for the same dy and dh_final, bit for bit, in the inputs' dtypes;
+    # inputs that need no gradient get none, and the forward is ssm_scan_fwd_ex's.
+    b, L, Dn, N, T = 2, 150, 70, 16, 32
+    shape = ScanShape("autograd", b, L, Dn, N, io, gated=gated, seed=41)
+    d = make_scan_inputs(shape, "cpu")
+    d["h0"] = make_h0(b, Dn, N) if with_h0 else None
+    g = to_dev(d)
+    gen = torch.Generator().manual_seed(42)
+    gy = torch.randn((b, L, Dn), generator=gen).to(g["x"].dtype).cuda()
+    gh = torch.randn((b, Dn, N), generator=gen).cuda()
+    names = ("x", "dt", "A", "B", "C", "D", "z", "h0")
+    leaves = {k: (None if g[k] is None else g[k].clone().requires_grad_(k != "D")) for k in names}
+    say("selective_scan autograd", io, gated, with_h0)
+    y, hf = ssm.selective_scan(*[leaves[k] for k in names], chunk_len=T)
+    ((y.float() * gy.float()).sum() + (hf * gh).sum()).backward()
+    y_ref, hf_ref = ssm.ssm_scan_fwd_ex(*[g[k] for k in names], chunk_len=T)
+    ref = ssm.ssm_scan_bwd(*[g[k] for k in names], dy=gy, dh_final=gh, chunk_len=T)
+    torch.cuda.synchronize()
+    assert bitwise_equal(y.detach(), y_ref) and bitwise_equal(hf.detach(), hf_ref)
+    for k in names:
+        if leaves[k] is None:
+            continue
+        if k == "D":
+            assert leaves[k].grad is None
+            continue
+        grad, want = leaves[k].grad, ref["d" + k]
+        assert grad.dtype == leaves[k].dtype, k
+        assert bitwise_equal(grad, want.to(grad.dtype)), f"d{k} differs from ssm_scan_bwd"
