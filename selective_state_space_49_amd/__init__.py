@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
-    "ssm_scan_fwd_mimo_chunk_len", "selective_scan",
+    "ssm_scan_fwd_mimo_chunk_len",
 ]
 
 
