@@ -228,3 +228,38 @@ def test_decay_horizon_edge_cases(variant):
     yr, hr = oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0)
     assert rel_err(y, yr) <= TOL["f32"], f"y error {rel_err(y, yr)}"
     assert rel_err(hf, hr) <= TOL["f32"], f"h_final error {rel_err(hf, hr)}"
+
+
+def test_prefill_in_captured_graph_matches_eager():
+    # A multi-chunk prefill (summaries, carry, rescan) with its workspace and outputs
+    # allocated beforehand, captured in a graph and replayed several times with eager
+    # prefills and synchronisation between replays: every replay equals the eager call
+    # bit for bit (the library enqueues kernels only: no allocation, no memset nodes).
+    shape = ScanShape("graph", 2, 700, 130, 16, "bf16", gated=True, seed=77)
+    g = to_dev(make_scan_inputs(shape, "cpu"))
+    h0 = make_h0(2, 130, 16).cuda()
+    T = 64  # 11 chunks
+    args = (g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], h0)
+    y_e, h_e = ssm.ssm_scan_fwd_ex(*args, chunk_len=T)
+    torch.cuda.synchronize()
+    ws = torch.empty(ssm.ssm_scan_fwd_workspace_ex(2, 700, 130, 16, T), dtype=torch.uint8, device="cuda")
+    y_g, h_g = torch.empty_like(y_e), torch.empty_like(h_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            ssm.ssm_scan_fwd_ex(*args, chunk_len=T, y=y_g, h_final=h_g, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say("prefill graph replay", rep)
+        y_g.zero_()
+        h_g.zero_()
+        ws.fill_(0xAB)  # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bitwise_equal(y_g, y_e) and bitwise_equal(h_g, h_e), f"replay {rep} differs"
+        ssm.ssm_scan_fwd_ex(*args, chunk_len=T)   # eager work between replays
+        torch.cuda.synchronize()
