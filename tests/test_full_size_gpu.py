@@ -159,3 +159,53 @@ def test_full_size_decode_fused_and_trapezoidal(variant):
     assert rel_err(h[lic, sic, dic].cpu(), h_ref.reshape(M, N)) <= TOL["bf16"]
     if variant == "fused":
         assert bitwise_equal(cs, cs_rep)
+
+
+def _cap_channels(Dn, k, seed):
+    return torch.unique(torch.cat([torch.tensor([0, Dn - 1]), sample_channels(Dn, k, seed=seed)]))
+
+
+def test_prefill_at_the_chunk_cap():
+    # A chunk's rows of a [rows][d_inner] stream are addressed with 32-bit byte offsets,
+    # so the planner keeps them under 2 GiB. fp32 with 8192 channels: a row is 32 KiB and
+    # a chunk at most 65535 steps. Asked for one chunk over 65636 steps, the library
+    # cuts two (65535 + 101), and the first chunk's offsets reach 2^31 - 64 KiB.
+    from workloads import ScanShape
+    b, L, Dn, N = 1, 65636, 8192, 16
+    assert ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, N, L) == 2 * ((Dn * N * 4 + 255) // 256 * 256)
+    shape = ScanShape("cap", b, L, Dn, N, "f32", gated=True, seed=88)
+    say("prefill at the chunk cap: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    say("prefill at the chunk cap: running")
+    y, hf = ssm.ssm_scan_fwd_ex(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], chunk_len=L)
+    torch.cuda.synchronize()
+    idx = _cap_channels(Dn, 14, seed=6)
+    g = lambda t: gather_channels(t, idx)
+    say("prefill at the chunk cap: oracle on", len(idx), "channels")
+    yr, hr = oracle.scan(g(d["x"]), g(d["dt"]), d["A"].cpu()[idx], d["B"].cpu(), d["C"].cpu(),
+                         d["D"].cpu()[idx], g(d["z"]))
+    assert rel_err(g(y), yr) <= TOL["f32"], f"y error {rel_err(g(y), yr)}"
+    assert rel_err(hf.index_select(1, idx.cuda()).cpu(), hr) <= TOL["f32"]
+
+
+def test_mimo_prefill_at_the_chunk_cap():
+    # The same for MIMO rows of d_inner * rank elements: fp32, rank 8, 8192 channels, a
+    # row is 256 KiB and a chunk at most 8191 steps; 8229 steps asked as one chunk run
+    # as 8191 + 38.
+    from workloads import ScanShape, make_mimo_inputs
+    b, L, Dn, N, R = 1, 8229, 8192, 16, 8
+    assert ssm.ssm_scan_fwd_mimo_workspace(b, L, Dn, N, R, L) == 2 * ((Dn * N * 4 + 255) // 256 * 256)
+    shape = ScanShape("mimo_cap", b, L, Dn, N, "f32", gated=True, seed=89)
+    say("MIMO prefill at the chunk cap: inputs")
+    d = make_mimo_inputs(shape, R, "cuda")
+    say("MIMO prefill at the chunk cap: running")
+    y, hf = ssm.ssm_scan_fwd_mimo(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
+                                  chunk_len=L)
+    torch.cuda.synchronize()
+    idx = _cap_channels(Dn, 10, seed=7)
+    g = lambda t: gather_channels(t, idx)
+    say("MIMO prefill at the chunk cap: oracle on", len(idx), "channels")
+    yr, hr = oracle.scan_mimo(g(d["x"]), g(d["dt"]), d["A"].cpu()[idx], d["B"].cpu(), d["C"].cpu(),
+                              d["D"].cpu()[idx], g(d["z"]))
+    assert rel_err(g(y), yr) <= TOL["f32"], f"y error {rel_err(g(y), yr)}"
+    assert rel_err(hf.index_select(1, idx.cuda()).cpu(), hr) <= TOL["f32"]
