@@ -230,3 +230,38 @@ def test_selective_scan_autograd(io, gated, with_h0):
         grad, want = leaves[k].grad, ref["d" + k]
         assert grad.dtype == leaves[k].dtype, k
         assert bitwise_equal(grad, want.to(grad.dtype)), f"d{k} differs from ssm_scan_bwd"
+
+
+def test_backward_at_the_chunk_cap():
+    # The backward's streams, stored states and partials at the chunk cap: fp32 with 8192
+    # channels, one chunk asked over 65636 steps and run as 65535 + 101, so a chunk's row
+    # offsets come within 64 KiB of 2^31 (the stored states, 8.6 GB, and the dB/dC
+    # partials are addressed with 64-bit offsets). dy on a channel sample, as above.
+    b, L, Dn, N = 1, 65636, 8192, 16
+    shape = ScanShape("bwd_cap", b, L, Dn, N, "f32", gated=True, seed=91)
+    say("backward at the chunk cap: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    idx = torch.unique(torch.cat([torch.tensor([0, Dn - 1]), sample_channels(Dn, 10, seed=14)]))
+    g = torch.Generator(device="cuda").manual_seed(92)
+    dy = torch.zeros(d["x"].shape, dtype=d["x"].dtype, device="cuda")
+    dy[:, :, idx.cuda()] = torch.randn((b, L, len(idx)), generator=g, device="cuda")
+    say("backward at the chunk cap: running")
+    got = ssm.ssm_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy, chunk_len=L)
+    torch.cuda.synchronize()
+    rest = torch.ones(Dn, dtype=torch.bool)
+    rest[idx] = False
+    for k in ("dx", "ddt", "dz"):
+        assert not got[k][:, :, rest.cuda()].any(), f"{k} nonzero outside the sample"
+    gc = lambda t: gather_channels(t, idx)
+    sub = {"x": gc(d["x"]), "dt": gc(d["dt"]), "z": gc(d["z"]), "dy": gc(dy), "A": d["A"].cpu()[idx],
+           "B": d["B"].cpu(), "C": d["C"].cpu(), "D": d["D"].cpu()[idx], "h0": None, "dh_final": None}
+    say("backward at the chunk cap: oracle on", len(idx), "channels")
+    ref = _oracle_threaded(sub)
+    tol = TOL["f32"]
+    for k in ("dx", "ddt", "dz"):
+        e = rel_err(gc(got[k]), ref[k])
+        assert e <= tol, f"{k}: error {e:.3e}"
+    for k, v in (("dA", got["dA"].cpu()[idx]), ("dD", got["dD"].cpu()[idx]), ("dB", got["dB"]),
+                 ("dC", got["dC"])):
+        e = rel_err(v, ref[k])
+        assert e <= tol, f"{k}: error {e:.3e}"

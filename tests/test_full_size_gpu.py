@@ -209,3 +209,24 @@ def test_mimo_prefill_at_the_chunk_cap():
                               d["D"].cpu()[idx], g(d["z"]))
     assert rel_err(g(y), yr) <= TOL["f32"], f"y error {rel_err(g(y), yr)}"
     assert rel_err(hf.index_select(1, idx.cuda()).cpu(), hr) <= TOL["f32"]
+
+
+def test_complex_prefill_at_the_chunk_cap():
+    # The complex-state prefill's streams at the same cap (fp32, 8192 channels, one chunk
+    # asked over 65636 steps, run as 65535 + 101).
+    from workloads import ScanShape
+    b, L, Dn, N = 1, 65636, 8192, 16
+    assert ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, L) == 2 * ((Dn * N * 8 + 255) // 256 * 256)
+    shape = ScanShape("complex_cap", b, L, Dn, N, "f32", complex_state=True, gated=False, seed=90)
+    say("complex prefill at the chunk cap: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    say("complex prefill at the chunk cap: running")
+    y, hf = ssm.ssm_scan_fwd_c64(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], chunk_len=L)
+    torch.cuda.synchronize()
+    idx = _cap_channels(Dn, 8, seed=8)
+    g = lambda t: gather_channels(t, idx)
+    say("complex prefill at the chunk cap: oracle on", len(idx), "channels")
+    yr, hr = oracle.scan_complex(g(d["x"]), g(d["dt"]), d["A"].cpu()[idx], d["B"].cpu(), d["C"].cpu(),
+                                 d["D"].cpu()[idx], g(d["z"]))
+    assert rel_err(g(y), yr) <= TOL["f32"], f"y error {rel_err(g(y), yr)}"
+    assert rel_err(hf.index_select(1, idx.cuda()).cpu(), hr) <= TOL["f32"]
