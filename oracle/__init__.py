@@ -65,6 +65,8 @@ def _load():
         lib.oracle_softplus_f64.restype = ctypes.c_int
         lib.oracle_scan_bwd_f64.argtypes = [i64, i64, i64, i64] + [dp] * 18
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
+        lib.oracle_input_stage_bwd_f64.argtypes = [i64, i64, i64, i64] + [dp] * 14
+        lib.oracle_input_stage_bwd_f64.restype = ctypes.c_int
         lib.oracle_scan_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 12
         lib.oracle_scan_trap_f64.restype = ctypes.c_int
         lib.oracle_step_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 11
@@ -234,6 +236,49 @@ def scan_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, conv_w=None, conv_b=No
     u, so = conv_silu(x_in, conv_w, conv_b, conv_state0)
     y, hf = scan(u, softplus(dt_raw, dt_bias), A, B, C, D, z, h0)
     return y, hf, so
+
+
+def input_stage_bwd(x_in, dt_raw, du, ddt, conv_w=None, conv_b=None, conv_state0=None,
+                    dt_bias=None, want_dstate0=True):
+    """Gradients through the input stage (oracle_input_stage_bwd_f64): given du =
+    dLoss/du and ddt = dLoss/ddt for u = silu(conv(x_in)), dt = softplus(dt_raw + bias),
+    returns a dict dx_in, ddt_raw [b, L, Dn]; dconv_w [Dn, K], dconv_b, ddt_bias [Dn]
+    (None without conv_w, conv_b, dt_bias); dconv_state0 [b, K-1, Dn] (None without
+    conv_w or when not wanted). conv_w None: no convolution (u = x_in)."""
+    x_in, dt_raw, du, ddt, w, cb, s0, bias = map(
+        to_f64, (x_in, dt_raw, du, ddt, conv_w, conv_b, conv_state0, dt_bias))
+    b, L, Dn = x_in.shape
+    K = 0 if w is None else w.shape[1]
+    if w is not None: _check(w, (Dn, K), "conv_w")
+    if cb is not None: _check(cb, (Dn,), "conv_b")
+    if s0 is not None: _check(s0, (b, K - 1, Dn), "conv_state0")
+    if bias is not None: _check(bias, (Dn,), "dt_bias")
+    out = {"dx_in": np.empty((b, L, Dn)), "ddt_raw": np.empty((b, L, Dn)),
+           "dconv_w": np.empty((Dn, K)) if K else None,
+           "dconv_b": np.empty(Dn) if (K and cb is not None) else None,
+           "ddt_bias": np.empty(Dn) if bias is not None else None,
+           "dconv_state0": np.empty((b, K - 1, Dn)) if (K and want_dstate0) else None}
+    if _load().oracle_input_stage_bwd_f64(
+            b, L, Dn, K, _p(x_in), _p(dt_raw), _p(w), _p(cb), _p(s0), _p(bias), _p(du), _p(ddt),
+            _p(out["dx_in"]), _p(out["ddt_raw"]), _p(out["dconv_w"]), _p(out["dconv_b"]),
+            _p(out["ddt_bias"]), _p(out["dconv_state0"])) != 0:
+        raise RuntimeError("oracle_input_stage_bwd_f64 failed")
+    return out
+
+
+def scan_fused_bwd(x_in, dt_raw, A, B, C, D, z=None, h0=None, conv_w=None, conv_b=None,
+                   conv_state0=None, dt_bias=None, dy=None, dh_final=None):
+    """Gradients of sum(dy y) + sum(dh_final h_final) for scan_fused: the scan's
+    backward (scan_bwd) on u = silu(conv(x_in)) and dt = softplus(dt_raw + bias), then
+    input_stage_bwd. conv_w None: no convolution (u = x_in). Returns scan_bwd's dict
+    without dx, ddt, plus input_stage_bwd's entries."""
+    u = x_in if conv_w is None else conv_silu(x_in, conv_w, conv_b, conv_state0)[0]
+    dt = softplus(dt_raw, dt_bias)
+    g = scan_bwd(u, dt, A, B, C, D, z, h0, dy=dy, dh_final=dh_final)
+    out = input_stage_bwd(x_in, dt_raw, g.pop("dx"), g.pop("ddt"), conv_w, conv_b, conv_state0,
+                          dt_bias)
+    out.update(g)
+    return out
 
 
 def step_fused(h, conv_state, x_in, dt_raw, A, B, C, D, z=None, conv_w=None, conv_b=None,

@@ -287,6 +287,63 @@ int oracle_softplus_f64(int64_t rows, int64_t Dn, const double *raw, const doubl
     return 0;
 }
 
+/* Gradients through the input stage above, for training: the chain rule of
+ * oracle_conv_silu_f64 and oracle_softplus_f64 written out. With xe the K-1 carried
+ * inputs followed by x (xe_s = conv_input(s), s = -(K-1) .. L-1),
+ *     a_t = cb + sum_k w[k] xe_{t-(K-1)+k},  u_t = silu(a_t),  dt_t = softplus(r_t + bias),
+ * and given du = dLoss/du, ddt = dLoss/ddt:
+ *     da_t = du_t s (1 + a_t (1 - s)),  s = 1 / (1 + e^-a_t)       (silu')
+ *     dxe_{t-(K-1)+k} += w[k] da_t,  dw[k] += da_t xe_{t-(K-1)+k},  dcb += da_t
+ *     dr_t = ddt_t / (1 + e^-(r_t + bias)),  dbias += dr_t        (softplus' = sigmoid)
+ * dx = dxe_0 .. dxe_{L-1}; dstate0 = dxe_{-(K-1)} .. dxe_{-1} (NULL: not wanted).
+ * dw, dcb, dbias are summed over batch and steps. K = 0 means no convolution and no
+ * silu (u = x): dx = du, and w, cb, dw, dcb, state0, dstate0 are unused. cb, bias,
+ * state0 NULL: zero (their gradients then not written when NULL). Every output given
+ * is overwritten. Layouts as oracle_conv_silu_f64; r, ddt, dr [batch][L][Dn]. */
+int oracle_input_stage_bwd_f64(int64_t batch, int64_t L, int64_t Dn, int64_t K,
+                               const double *x, const double *r, const double *w,
+                               const double *cb, const double *state0, const double *bias,
+                               const double *du, const double *ddt, double *dx, double *dr,
+                               double *dw, double *dcb, double *dbias, double *dstate0)
+{
+    if (batch < 0 || L < 0 || Dn < 0 || K < 0) return -1;
+    const int64_t H = K > 0 ? K - 1 : 0;
+    for (int64_t i = 0; i < batch * L * Dn; ++i) dx[i] = 0.0;
+    if (dstate0) for (int64_t i = 0; i < batch * H * Dn; ++i) dstate0[i] = 0.0;
+    if (K > 0) {
+        for (int64_t i = 0; i < Dn * K; ++i) dw[i] = 0.0;
+        if (dcb) for (int64_t d = 0; d < Dn; ++d) dcb[d] = 0.0;
+    }
+    if (dbias) for (int64_t d = 0; d < Dn; ++d) dbias[d] = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t t = 0; t < L; ++t) {
+            for (int64_t d = 0; d < Dn; ++d) {
+                const int64_t e = (b * L + t) * Dn + d;
+                if (K == 0) {
+                    dx[e] = du[e];
+                } else {
+                    double pre = cb ? cb[d] : 0.0;  /* a_t, the convolution before silu */
+                    for (int64_t k = 0; k < K; ++k)
+                        pre = pre + w[d * K + k] * conv_input(x, state0, b, t - H + k, d, L, Dn, K);
+                    const double sg = 1.0 / (1.0 + exp(-pre));
+                    const double da = du[e] * sg * (1.0 + pre * (1.0 - sg));
+                    for (int64_t k = 0; k < K; ++k) {
+                        const int64_t s = t - H + k;
+                        dw[d * K + k] += da * conv_input(x, state0, b, s, d, L, Dn, K);
+                        if (s >= 0) dx[(b * L + s) * Dn + d] += w[d * K + k] * da;
+                        else if (dstate0) dstate0[(b * H + (H + s)) * Dn + d] += w[d * K + k] * da;
+                    }
+                    if (dcb) dcb[d] += da;
+                }
+                const double v = r[e] + (bias ? bias[d] : 0.0);
+                dr[e] = ddt[e] / (1.0 + exp(-v));
+                if (dbias) dbias[d] += dr[e];
+            }
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ backward
  * Gradients of the real-state prefill, for training: given dy = dLoss/dy and
  * optionally dh_final = dLoss/dh_final, the gradients of

@@ -481,6 +481,51 @@ def pin_backward_finite_differences(O, tol=1e-7):
             assert g["dz"] is None
 
 
+def pin_fused_backward_finite_differences(O, tol=1e-7):
+    # The backward through the input stage: every element of the raw input, the raw dt,
+    # the filter, its bias, the carried conv state and the dt bias is perturbed by
+    # +-eps and the difference quotient of the fused scan's loss compared with
+    # scan_fused_bwd's gradient (and the scan's own inputs A, B, C, D, z, h0 once more,
+    # through the input stage). K = 3 with every optional input, K = 1 without bias or
+    # state, and K = 0 (no convolution: u = x_in).
+    def loss(inp, dy, dhf):
+        if inp["conv_w"] is None:
+            y, hf = O.scan(inp["x_in"], O.softplus(inp["dt_raw"], inp["dt_bias"]), inp["A"],
+                           inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+        else:
+            y, hf, _ = O.scan_fused(**inp)
+        return float(np.sum(dy * y) + (np.sum(dhf * hf) if dhf is not None else 0.0))
+
+    for seed, K, full in [(81, 3, True), (82, 1, False), (83, 0, True)]:
+        base = tiny_real(seed, b=2, L=5, Dn=2, N=3, with_h0=full)
+        r = np.random.default_rng(seed + 1)
+        b, L, Dn = base["x"].shape
+        inp = dict(x_in=base.pop("x"), dt_raw=_inv_softplus(base.pop("dt")) - 0.3, **base,
+                   conv_w=r.normal(0, 0.7, (Dn, K)) if K else None,
+                   conv_b=r.normal(0, 0.5, Dn) if (K and full) else None,
+                   conv_state0=r.normal(0, 1, (b, K - 1, Dn)) if (K > 1 and full) else None,
+                   dt_bias=r.normal(0, 0.2, Dn) if full else None)
+        dy = r.normal(0, 1, (b, L, Dn))
+        dhf = r.normal(0, 1, (b, Dn, 3)) if full else None
+        g = O.scan_fused_bwd(**inp, dy=dy, dh_final=dhf)
+        names = {"x_in": "dx_in", "dt_raw": "ddt_raw", "conv_w": "dconv_w", "conv_b": "dconv_b",
+                 "conv_state0": "dconv_state0", "dt_bias": "ddt_bias", "A": "dA", "B": "dB",
+                 "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+        for name, gname in names.items():
+            if inp[name] is None:
+                continue
+            v = inp[name]
+            fd = np.empty(v.shape)
+            for idx in np.ndindex(v.shape):
+                eps = 1e-6 * max(1.0, abs(v[idx]))
+                hi = dict(inp); hi[name] = v.copy(); hi[name][idx] += eps
+                lo = dict(inp); lo[name] = v.copy(); lo[name][idx] -= eps
+                fd[idx] = (loss(hi, dy, dhf) - loss(lo, dy, dhf)) / (2 * eps)
+            scale = max(1.0, float(np.max(np.abs(fd))))
+            err = float(np.max(np.abs(fd - g[gname]))) / scale
+            assert err <= tol, f"fused backward {gname} vs finite differences: {err:.2e} (K={K})"
+
+
 # ----------------------------------------------------------------------------- trapezoid
 
 def brute_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
@@ -719,6 +764,7 @@ ALL_PINS = [
     lambda O: pin_layers_are_independent(O, complex_state=True),
     pin_conv_matches_numpy, pin_conv_impulse, pin_conv_state_carry, pin_softplus,
     pin_fused_identity_filter, pin_fused_step_equals_scan, pin_backward_finite_differences,
+    pin_fused_backward_finite_differences,
     pin_trap_brute_force, pin_trap_a_zero_is_trapezoid_rule, pin_trap_second_order,
     pin_trap_split_resume, pin_trap_step_equals_scan,
     pin_mimo_rank_one_is_siso, pin_mimo_superposition, pin_mimo_brute_force,

@@ -99,6 +99,14 @@ MUTANTS = {
     "mimo_decode_B_layer_dropped": ("const double *Bt = B + (l * n_seq + q) * N * R;", "const double *Bt = B + q * N * R;"),
     "mimo_decode_output_from_old_state": ("hs[n] = dA * hs[n] + u;\n                    for (int64_t r = 0; r < R; ++r) acc[r] = acc[r] + Ct[n * R + r] * hs[n];",
                                           "for (int64_t r = 0; r < R; ++r) acc[r] = acc[r] + Ct[n * R + r] * hs[n];\n                    hs[n] = dA * hs[n] + u;"),
+    "input_bwd_silu_derivative_truncated": ("const double da = du[e] * sg * (1.0 + pre * (1.0 - sg));",
+                                            "const double da = du[e] * sg;"),
+    "input_bwd_filter_flipped": ("if (s >= 0) dx[(b * L + s) * Dn + d] += w[d * K + k] * da;",
+                                 "if (s >= 0) dx[(b * L + s) * Dn + d] += w[d * K + (K - 1 - k)] * da;"),
+    "input_bwd_softplus_derivative_sign": ("dr[e] = ddt[e] / (1.0 + exp(-v));", "dr[e] = ddt[e] / (1.0 + exp(v));"),
+    "input_bwd_state_positions_reversed": ("else if (dstate0) dstate0[(b * H + (H + s)) * Dn + d] += w[d * K + k] * da;",
+                                           "else if (dstate0) dstate0[(b * H + (-1 - s)) * Dn + d] += w[d * K + k] * da;"),
+    "input_bwd_bias_gradient_dropped": ("if (dcb) dcb[d] += da;", "if (dcb) dcb[d] += 0.0 * da;"),
 }
 
 
@@ -126,7 +134,7 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     for fname in ("oracle_scan_f64", "oracle_scan_c128", "oracle_step_f64", "oracle_step_c128",
                   "oracle_state_bytes", "oracle_conv_silu_f64", "oracle_softplus_f64",
                   "oracle_scan_bwd_f64", "oracle_scan_trap_f64", "oracle_step_trap_f64",
-                  "oracle_scan_mimo_f64", "oracle_step_mimo_f64"):
+                  "oracle_scan_mimo_f64", "oracle_step_mimo_f64", "oracle_input_stage_bwd_f64"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
