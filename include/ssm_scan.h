@@ -285,6 +285,43 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
                         ssm_dtype io, int64_t chunk_len, void *workspace,
                         size_t workspace_bytes, void *hip_stream);
 
+/* ssm_scan_bwd_fused: gradients of ssm_scan_fwd_fused's prefill, for training: the
+ * backward above on u = silu(conv(x_in)) and dt = softplus(dt_raw + dt_bias), then the
+ * chain rule back through the input stage ("【大模型】- Jamba 混合 SSM-Transformer",
+ * section 4.1 "Mamba 层": the causal depthwise convolution and silu on x, softplus on
+ * the dt projection's output). With xe the conv_k-1 carried inputs followed by x_in,
+ * a_t = conv_b + sum_k conv_w[k] xe_{t-(K-1)+k} and da_t = du_t silu'(a_t):
+ *   dx_in [batch, L, d_inner] (io):  dx_in_s = sum_k conv_w[k] da_{s+(K-1)-k}
+ *   ddt_raw [batch, L, d_inner] (io): ddt_t / (1 + exp(-(dt_raw_t + dt_bias)))
+ *   dconv_w [d_inner, conv_k], dconv_b, ddt_bias [d_inner] float32: sums over batch and
+ *     steps of da_t xe_{t-(K-1)+k}, da_t and ddt_raw_t (dconv_b, ddt_bias NULL = not
+ *     wanted; dconv_w required when conv_k > 0)
+ *   dconv_state0 [batch, conv_k-1, d_inner] (io, NULL = not wanted): the gradient of
+ *     the carried inputs before step 0 (also when conv_state0 is NULL, i.e. zeros)
+ *   dz, dA, dB, dC, dD, dh0: as ssm_scan_bwd.
+ * conv_k = 0: no convolution and no silu (u = x_in; dx_in = du). Arguments, layouts and
+ * alignment of the forward inputs are those of ssm_scan_fwd_fused (conv_state_out has
+ * no counterpart), the rest those of ssm_scan_bwd; dconv_w, dconv_b, ddt_bias 4 bytes,
+ * dconv_state0 one element. dx_in must not overlap x_in (SSM_ERR_UNSUPPORTED).
+ * u and dt are written in io to the workspace (ssm_scan_bwd_fused_workspace bytes,
+ * 256-byte aligned: the scan backward's, then u, dt, du, ddt of batch * L * d_inner
+ * elements each, then per-chunk partial sums), so with bf16 io the scan backward sees
+ * them rounded to bf16 as ssm_scan_bwd would see bf16 inputs; the input stage's own
+ * arithmetic is fp32. The sums are reduced in a fixed order: results are
+ * deterministic. L == 0: dconv_w, dconv_b, ddt_bias and dconv_state0 are 0. */
+size_t ssm_scan_bwd_fused_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                    int32_t conv_k, ssm_dtype io, int64_t chunk_len);
+ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *h0,
+                              const float *conv_w, const float *conv_b, int32_t conv_k,
+                              const void *conv_state0, const float *dt_bias, const void *dy,
+                              const float *dh_final, void *dx_in, void *ddt_raw, void *dz,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0,
+                              float *dconv_w, float *dconv_b, float *ddt_bias, void *dconv_state0,
+                              int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                              ssm_dtype io, int64_t chunk_len, void *workspace,
+                              size_t workspace_bytes, void *hip_stream);
+
 /* ------------------------------------------------------------------ exponential-trapezoidal
  * ssm_scan_fwd_trap: the prefill of ssm_scan_fwd_ex with the exponential-trapezoidal
  * discretisation that Mamba-3 puts in place of Euler's ("Jamba — SSM-Transformer

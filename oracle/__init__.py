@@ -243,8 +243,8 @@ def input_stage_bwd(x_in, dt_raw, du, ddt, conv_w=None, conv_b=None, conv_state0
     """Gradients through the input stage (oracle_input_stage_bwd_f64): given du =
     dLoss/du and ddt = dLoss/ddt for u = silu(conv(x_in)), dt = softplus(dt_raw + bias),
     returns a dict dx_in, ddt_raw [b, L, Dn]; dconv_w [Dn, K], dconv_b, ddt_bias [Dn]
-    (None without conv_w, conv_b, dt_bias); dconv_state0 [b, K-1, Dn] (None without
-    conv_w or when not wanted). conv_w None: no convolution (u = x_in)."""
+    (None without conv_w, conv_b, dt_bias); dconv_state0 [b, K-1, Dn] (None for K < 2
+    or when not wanted). conv_w None: no convolution (u = x_in)."""
     x_in, dt_raw, du, ddt, w, cb, s0, bias = map(
         to_f64, (x_in, dt_raw, du, ddt, conv_w, conv_b, conv_state0, dt_bias))
     b, L, Dn = x_in.shape
@@ -257,7 +257,7 @@ def input_stage_bwd(x_in, dt_raw, du, ddt, conv_w=None, conv_b=None, conv_state0
            "dconv_w": np.empty((Dn, K)) if K else None,
            "dconv_b": np.empty(Dn) if (K and cb is not None) else None,
            "ddt_bias": np.empty(Dn) if bias is not None else None,
-           "dconv_state0": np.empty((b, K - 1, Dn)) if (K and want_dstate0) else None}
+           "dconv_state0": np.empty((b, K - 1, Dn)) if (K > 1 and want_dstate0) else None}
     if _load().oracle_input_stage_bwd_f64(
             b, L, Dn, K, _p(x_in), _p(dt_raw), _p(w), _p(cb), _p(s0), _p(bias), _p(du), _p(ddt),
             _p(out["dx_in"]), _p(out["ddt_raw"]), _p(out["dconv_w"]), _p(out["dconv_b"]),

@@ -23,7 +23,7 @@ __all__ = [
     "ssm_status_str", "ssm_last_error", "ssm_abi_version", "EXPORTED_SYMBOLS",
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
-    "ssm_scan_bwd", "ssm_scan_bwd_workspace",
+    "ssm_scan_bwd", "ssm_scan_bwd_workspace", "ssm_scan_bwd_fused", "ssm_scan_bwd_fused_workspace",
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
@@ -43,7 +43,7 @@ EXPORTED_SYMBOLS = [
     "ssm_status_str", "ssm_last_error", "ssm_abi_version",
     "ssm_scan_fwd_profiled", "ssm_scan_fwd_c64_profiled",
     "ssm_scan_fwd_fused", "ssm_scan_fwd_fused_profiled", "ssm_step_fused", "ssm_step_fused_replay",
-    "ssm_scan_bwd", "ssm_scan_bwd_workspace",
+    "ssm_scan_bwd", "ssm_scan_bwd_workspace", "ssm_scan_bwd_fused", "ssm_scan_bwd_fused_workspace",
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
@@ -100,6 +100,8 @@ def load_library():
     sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
     sig["ssm_scan_bwd_workspace"] = ([i64, i64, i64, i32, i64], sz)
     sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    sig["ssm_scan_bwd_fused_workspace"] = ([i64, i64, i64, i32, i32, ci, i64], sz)
+    sig["ssm_scan_bwd_fused"] = ([vp] * 10 + [i32] + [vp] * 16 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     trap = [vp] * 12 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_trap"] = (trap, ci)
     sig["ssm_scan_fwd_trap_profiled"] = (trap + [vp, i32], ci)
@@ -540,6 +542,59 @@ def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk
                           _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
                           _ptr(out["dD"]), _ptr(out["dh0"]), b, L, Dn, N, io, chunk_len,
                           _ptr(workspace), ws_bytes, _stream(x))
+    _check(st)
+    return out
+
+
+def ssm_scan_bwd_fused_workspace(batch, L, d_inner, d_state, conv_k, io, chunk_len=0) -> int:
+    return int(load_library().ssm_scan_bwd_fused_workspace(batch, L, d_inner, d_state, conv_k, io,
+                                                           chunk_len))
+
+
+def ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
+                       conv_state0=None, dt_bias=None, dy, dh_final=None, chunk_len=0,
+                       want_dz=True, want_dh0=True, want_dconv_state0=True, workspace=None):
+    """Gradients of ssm_scan_fwd_fused's prefill (see ssm_scan.h). Returns a dict:
+    dx_in, ddt_raw, dz (io dtype; dz None when ungated or not wanted), dA, dB, dC, dD,
+    dh0, dconv_w, dconv_b, ddt_bias (float32; None when the input is absent or not
+    wanted), dconv_state0 (io dtype, for conv_k >= 2)."""
+    lib = load_library()
+    b, L, Dn = x_in.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    K = 0 if conv_w is None else conv_w.shape[-1]
+    _dev(x_in, "x_in"); _dev(dt_raw, "dt_raw", (b, L, Dn)); _dev(z, "z", (b, L, Dn))
+    _dev(dy, "dy", (b, L, Dn))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N)); _dev(h0, "h0", (b, Dn, N), f32)
+    _dev(dh_final, "dh_final", (b, Dn, N), f32)
+    _input_stage(conv_w, conv_b, dt_bias, (), Dn, K)
+    io = _io(x_in, dt_raw, z, B, C, dy)
+    if K > 1:
+        _dev(conv_state0, "conv_state0", (b, K - 1, Dn), x_in.dtype)
+    else:
+        conv_state0 = None
+    dev = x_in.device
+    new = lambda shp, dtp: torch.empty(shp, dtype=dtp, device=dev)
+    out = {"dx_in": new((b, L, Dn), x_in.dtype), "ddt_raw": new((b, L, Dn), x_in.dtype),
+           "dz": new((b, L, Dn), x_in.dtype) if (z is not None and want_dz) else None,
+           "dA": new((Dn, N), f32), "dB": new((b, L, N), f32), "dC": new((b, L, N), f32),
+           "dD": new((Dn,), f32), "dh0": new((b, Dn, N), f32) if want_dh0 else None,
+           "dconv_w": new((Dn, K), f32) if K else None,
+           "dconv_b": new((Dn,), f32) if (K and conv_b is not None) else None,
+           "ddt_bias": new((Dn,), f32) if dt_bias is not None else None,
+           "dconv_state0": new((b, K - 1, Dn), x_in.dtype) if (K > 1 and want_dconv_state0) else None}
+    need = ssm_scan_bwd_fused_workspace(b, L, Dn, N, K, io, chunk_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_bwd_fused(
+        _ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+        _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_state0), _ptr(dt_bias), _ptr(dy), _ptr(dh_final),
+        _ptr(out["dx_in"]), _ptr(out["ddt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
+        _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out["dconv_w"]),
+        _ptr(out["dconv_b"]), _ptr(out["ddt_bias"]), _ptr(out["dconv_state0"]), b, L, Dn, N, io,
+        chunk_len, _ptr(workspace), ws_bytes, _stream(x_in))
     _check(st)
     return out
 

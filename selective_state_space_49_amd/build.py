@@ -22,7 +22,8 @@ LIB = os.path.join(HERE, "libssmscan.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["scan_real.hip", "scan_complex.hip", "step.hip", "scan_bwd.hip", "scan_mimo.hip"]
+HIP_SOURCES = ["scan_real.hip", "scan_complex.hip", "step.hip", "scan_bwd.hip", "scan_mimo.hip",
+               "input_bwd.hip"]
 CPP_SOURCES = ["api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",

@@ -729,6 +729,111 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
                       hip_stream);
 }
 
+// ---------------------------------------------------------------- backward through the input stage
+// The two streaming kernels of the input stage take chunks of their own (independent,
+// about 2048 blocks per launch). Workspace: the scan backward's, then u, dt, du, ddt
+// ([batch][L][d_inner] of io each) and the partial sums ([n][batch][d_inner][conv_k + 2]
+// fp32), each 256-byte aligned.
+struct InBwdPlan {
+    int64_t T;
+    int32_t n_chunks;
+    size_t scan_ws, buf, part, bytes;
+};
+
+ssm_status make_in_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                            int32_t conv_k, ssm_dtype io, int64_t chunk_len, InBwdPlan *p) {
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
+    if (conv_k < 0 || conv_k > 4) return fail(SSM_ERR_UNSUPPORTED, "conv_k %d not in 0..4", conv_k);
+    BwdPlan bp;
+    const ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &bp);
+    if (st != SSM_OK) return st;
+    const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 255) / 256));
+    int64_t n = std::min<int64_t>((2048 + blocks - 1) / blocks, std::max<int64_t>(1, L / 256));
+    n = std::max<int64_t>(n, 1);
+    p->T = L > 0 ? (L + n - 1) / n : 1;
+    p->n_chunks = L > 0 ? (int32_t)((L + p->T - 1) / p->T) : 0;
+    p->scan_ws = ws_round(bp.bytes);
+    p->buf = ws_round((size_t)batch * (size_t)L * (size_t)d_inner * io_bytes(io));
+    p->part = ws_round((size_t)p->n_chunks * (size_t)batch * (size_t)d_inner * (size_t)(conv_k + 2) * sizeof(float));
+    p->bytes = p->scan_ws + 4 * p->buf + p->part;
+    return ok();
+}
+
+size_t ssm_scan_bwd_fused_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                    int32_t conv_k, ssm_dtype io, int64_t chunk_len) {
+    InBwdPlan p;
+    if (make_in_bwd_plan(batch, L, d_inner, d_state, conv_k, io, chunk_len, &p) != SSM_OK) return 0;
+    return p.bytes;
+}
+
+ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *h0,
+                              const float *conv_w, const float *conv_b, int32_t conv_k,
+                              const void *conv_state0, const float *dt_bias, const void *dy,
+                              const float *dh_final, void *dx_in, void *ddt_raw, void *dz,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0,
+                              float *dconv_w, float *dconv_b, float *ddt_bias, void *dconv_state0,
+                              int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                              ssm_dtype io, int64_t chunk_len, void *workspace,
+                              size_t workspace_bytes, void *hip_stream) {
+    InBwdPlan p;
+    ssm_status st = make_in_bwd_plan(batch, L, d_inner, d_state, conv_k, io, chunk_len, &p);
+    if (st != SSM_OK) return st;
+    const size_t eb = io_bytes(io);
+    st = check_input_stage(InputStage{conv_w, conv_b, dt_bias, conv_k, conv_state0, dconv_state0}, eb);
+    if (st != SSM_OK) return st;
+    if (conv_k > 0 && !dconv_w) return fail(SSM_ERR_NULL, "dconv_w is required when conv_k > 0");
+    const bool work = batch > 0 && L > 0;
+    if (work && (!x_in || !dt_raw || !dx_in || !ddt_raw))
+        return fail(SSM_ERR_NULL, "x_in, dt_raw, dx_in and ddt_raw are required");
+    if (!aligned(x_in, eb) || !aligned(dt_raw, eb) || !aligned(dx_in, eb) || !aligned(ddt_raw, eb) ||
+        !aligned(dconv_w, 4) || !aligned(dconv_b, 4) || !aligned(ddt_bias, 4))
+        return fail(SSM_ERR_ALIGN, "pointer alignment (x_in, dt_raw, dx_in, ddt_raw element; dconv_w, dconv_b, ddt_bias 4 B)");
+    const size_t rows = (size_t)batch * (size_t)L * (size_t)d_inner * eb;
+    if (overlaps(dx_in, rows, x_in, rows))
+        return fail(SSM_ERR_UNSUPPORTED, "dx_in must not overlap x_in (a chunk reads the inputs after it)");
+    if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
+        return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed", p.bytes);
+    if (!aligned(workspace, kWsAlign)) return fail(SSM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    char *ws = (char *)workspace;
+    ssm::InBwdArgs a{};
+    a.x_in = x_in; a.dt_raw = dt_raw;
+    a.conv_w = conv_k > 0 ? conv_w : nullptr; a.conv_b = conv_k > 0 ? conv_b : nullptr;
+    a.dt_bias = dt_bias; a.conv_state0 = conv_k > 1 ? conv_state0 : nullptr;
+    a.u = ws ? ws + p.scan_ws : nullptr;
+    a.dt = ws ? ws + p.scan_ws + p.buf : nullptr;
+    a.du = ws ? ws + p.scan_ws + 2 * p.buf : nullptr;
+    a.ddt = ws ? ws + p.scan_ws + 3 * p.buf : nullptr;
+    a.dx_in = dx_in; a.ddt_raw = ddt_raw;
+    a.dconv_state0 = conv_k > 1 ? dconv_state0 : nullptr;
+    a.part = ws ? (float *)(ws + p.scan_ws + 4 * p.buf) : nullptr;
+    a.dconv_w = conv_k > 0 ? dconv_w : nullptr; a.dconv_b = conv_k > 0 ? dconv_b : nullptr;
+    a.ddt_bias = ddt_bias;
+    a.batch = batch; a.L = L; a.Dn = d_inner; a.T = p.T; a.n_chunks = p.n_chunks; a.conv_k = conv_k;
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int iot = io == SSM_BF16 ? 1 : 0;
+    if (work) {
+        st = launch_status(ssm::launch_input_fwd(a, iot, s), "input stage (forward)");
+        if (st != SSM_OK) return st;
+    }
+    st = ssm_scan_bwd(a.u, a.dt, A, B, C, D, z, h0, dy, dh_final, const_cast<void *>(a.du),
+                      const_cast<void *>(a.ddt), dz, dA, dB, dC, dD, dh0, batch, L, d_inner, d_state,
+                      io, chunk_len, ws, p.scan_ws, hip_stream);
+    if (st != SSM_OK) return st;
+    if (work) return launch_status(ssm::launch_input_bwd(a, iot, s), "input stage (backward)");
+    // no steps: the input stage's own gradients are zero
+    const int64_t Kw = conv_k > 0 ? conv_k : 0;
+    const struct { void *p; int64_t n; int eb; } zero[] = {
+        {a.dconv_w, d_inner * Kw, 4}, {a.dconv_b, d_inner, 4}, {a.ddt_bias, d_inner, 4},
+        {a.dconv_state0, batch * (conv_k > 1 ? conv_k - 1 : 0) * d_inner, (int)eb}};
+    for (const auto &zf : zero) {
+        if (!zf.p || zf.n <= 0) continue;
+        st = launch_status(ssm::launch_elem_fill(zf.p, nullptr, zf.n, zf.eb, s), "zero fill");
+        if (st != SSM_OK) return st;
+    }
+    return ok();
+}
+
 const char *ssm_status_str(ssm_status s) {
     switch (s) {
         case SSM_OK: return "ok";

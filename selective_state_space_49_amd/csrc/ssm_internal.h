@@ -121,4 +121,26 @@ constexpr int kSub = 4;  // steps per recomputed sub-chunk of the backward
 hipError_t launch_scan_bwd(const BwdArgs &a, const ScanArgs &fwd, int io, int d_state, bool gated,
                            hipStream_t s);
 
+// ---------------------------------------------------------------- input-stage backward
+// The backward through the fused prefill's input stage (ssm_scan_bwd_fused). Arrays of
+// [batch][L][Dn] are of io unless noted; chunks of T steps (n_chunks of them) are
+// independent.
+struct InBwdArgs {
+    const void *x_in, *dt_raw;              // the fused prefill's inputs
+    const float *conv_w, *conv_b, *dt_bias; // [Dn][conv_k], [Dn], [Dn] (conv_b, dt_bias nullable)
+    const void *conv_state0;                // [batch][conv_k-1][Dn], or null: zeros
+    void *u, *dt;                           // written by launch_input_fwd: silu(conv(x_in)), softplus
+    const void *du, *ddt;                   // the scan's backward on (u, dt): dLoss/du, dLoss/ddt
+    void *dx_in, *ddt_raw;                  // outputs
+    void *dconv_state0;                     // [batch][conv_k-1][Dn], or null: not wanted
+    float *part;                            // workspace: [n_chunks][batch][Dn][conv_k + 2] fp32
+    float *dconv_w, *dconv_b, *ddt_bias;    // outputs, fp32 (null: not wanted)
+    int64_t batch, L, Dn, T;
+    int32_t n_chunks, conv_k;               // conv_k 0..4 (0: u = x_in)
+};
+// u and dt from x_in and dt_raw. io: 0 = f32, 1 = bf16.
+hipError_t launch_input_fwd(const InBwdArgs &a, int io, hipStream_t s);
+// dx_in, ddt_raw, the partials and their sums (dconv_w, dconv_b, ddt_bias), dconv_state0.
+hipError_t launch_input_bwd(const InBwdArgs &a, int io, hipStream_t s);
+
 }  // namespace ssm

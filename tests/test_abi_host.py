@@ -271,3 +271,27 @@ def test_mimo_argument_errors(lib):
     assert step(x=0x1004) == ALIGN
     assert step(y=0x2008, R=8, io=0) == ALIGN
     assert step(B=0x1002) == ALIGN
+
+
+def test_fused_backward_argument_errors(lib):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def call(K=3, w=0x1000, dw=0x2000, dx=0x300000, x=0x100000, ws=None, wsb=0, L=8, io=0, cs0=None, dcs0=None):
+        return lib.ssm_scan_bwd_fused(p(x), p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000), None,
+                                      None, p(w), None, K, p(cs0), None, p(0x1000), None, p(dx),
+                                      p(0x1000), None, p(0x1000), p(0x1000), p(0x1000), p(0x1000), None,
+                                      p(dw), None, None, p(dcs0), 1, L, 4, 4, io, 0, p(ws), wsb, None)
+    assert call(K=5) == UNSUP
+    assert call(K=-1) == UNSUP
+    assert call(w=None) == NULL                 # conv_k > 0 needs the filter
+    assert call(dw=None) == NULL                # and its gradient
+    assert call(dw=0x2002) == ALIGN
+    assert call(io=1, dcs0=0x3001) == ALIGN     # bf16 state gradient must be element-aligned
+    assert call(dx=0x100010) == UNSUP           # dx_in over x_in
+    assert "overlap" in ssm.ssm_last_error()
+    assert call(io=7) == DTYPE
+    need = lib.ssm_scan_bwd_fused_workspace(1, 8, 4, 4, 3, 0, 0)
+    assert need > 0 and call() == WS            # u, dt, du, ddt live in the workspace
+    assert call(ws=0x10080, wsb=need) == ALIGN
+    assert lib.ssm_scan_bwd_fused_workspace(1, 8, 4, 4, 9, 0, 0) == 0
+    assert lib.ssm_scan_bwd_fused_workspace(1, 8, 4, 3, 2, 0, 0) == 0
