@@ -205,20 +205,34 @@ def decode_lane_ops(s) -> float:
 
 
 # ----------------------------------------------------------------- runs
-def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
-    """One step = one ssm_scan_bwd call over the workload (dy ~ N(0, 1) in the I/O dtype)."""
+def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None):
+    """One step = one ssm_scan_bwd call over the workload (dy ~ N(0, 1) in the I/O dtype);
+    with conv_k, one ssm_scan_bwd_fused call (the input stage of a conv_k-tap filter:
+    x and dt of the workload are then the raw x_in and dt_raw)."""
     dev = "cuda"
     log("drawing inputs for", shape.name, "(backward)")
     d = workloads.make_scan_inputs(shape, dev)
     g = torch.Generator(device=dev).manual_seed(shape.seed + 29)
     dy = torch.randn(d["x"].shape, generator=g, device=dev).to(d["x"].dtype)
     b, L, Dn, N = shape.batch, shape.L, shape.d_inner, shape.d_state
-    ws = torch.empty(max(ssm.ssm_scan_bwd_workspace(b, L, Dn, N, chunk_len), 1), dtype=torch.uint8,
-                     device=dev)
+    fused = conv_k is not None
+    if fused:
+        d.update(workloads.make_input_stage(shape, conv_k, dev))
+        io = 1 if shape.io == "bf16" else 0
+        need = ssm.ssm_scan_bwd_fused_workspace(b, L, Dn, N, conv_k, io, chunk_len)
+    else:
+        need = ssm.ssm_scan_bwd_workspace(b, L, Dn, N, chunk_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     log("backward workspace", ws.numel() / 1e9, "GB")
     out = {}
 
     def call():
+        if fused:
+            ssm.ssm_scan_bwd_fused(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                   conv_w=d["conv_w"], conv_b=d["conv_b"], conv_state0=d["conv_state0"],
+                                   dt_bias=d["dt_bias"], dy=dy, chunk_len=chunk_len, workspace=ws,
+                                   want_dh0=False, want_dconv_state0=False)
+            return
         r = ssm.ssm_scan_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy,
                              chunk_len=chunk_len, workspace=ws, out=out, want_dh0=False)
         out.update(r)
@@ -238,12 +252,21 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0):
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1) / steps
     io_bytes = 2 if shape.io == "bf16" else 4
+    nbytes, lane_ops = backward_bytes(shape, io_bytes), backward_lane_ops(shape)
+    if fused:
+        # recompute of u, dt (x_in, dt_raw read; u, dt written) and the chain rule (x_in,
+        # dt_raw, du, ddt read; dx_in, ddt_raw written): 10 more streams; the input stage
+        # forward once more, and its backward: per tap an fma for a_t, dx_in and dw, silu'
+        # (exp, add, rcp, sub, fma, 2 mul) and softplus' (add, mul, exp, add, rcp, mul, add)
+        nbytes += 10 * shape.elements * io_bytes
+        lane_ops += input_stage_lane_ops(conv_k) + 3 * conv_k + 14
     info = {
         "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": {"backward_call": gpu_ms},
-        "elements_per_step": shape.elements, "bytes_per_step": backward_bytes(shape, io_bytes),
-        "lane_ops_per_elem": backward_lane_ops(shape), "chunk_len": chunk_len,
+        "elements_per_step": shape.elements, "bytes_per_step": nbytes,
+        "lane_ops_per_elem": lane_ops, "chunk_len": chunk_len,
         "n_chunks": None, "dominant_ms": gpu_ms, "gpu_ms": gpu_ms,
-        "kernel": "ssm_scan_bwd (all launches)", "source": "bwd",
+        "kernel": "ssm_scan_bwd_fused (all launches)" if fused else "ssm_scan_bwd (all launches)",
+        "source": "bwd",
     }
     return info, d
 
@@ -553,7 +576,7 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False, m
                              f"{dt1:.1f} s wall)"}
 
 
-def cpu_baseline_backward(shape, d, torch, workloads, threads):
+def cpu_baseline_backward(shape, d, torch, workloads, threads, conv_k=None):
     """The oracle's backward on a channel sample over the full sequence, channel groups on
     several threads (dB and dC then cover the sampled channels only; the per-element work
     is the same)."""
@@ -564,7 +587,10 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
     k = sample_width(shape, CPU_SAMPLE_ELEMS // 2)
     idx = workloads.sample_channels(shape.d_inner, k, seed=5)
     g = lambda t: None if t is None else oracle.to_f64(t.index_select(2, idx.to(t.device)))
-    x, dt, z = g(d["x"]), g(d["dt"]), g(d["z"])
+    x, dt, z = g(d["x"]), g(d["dt_raw"] if conv_k is not None else d["dt"]), g(d["z"])
+    sel = lambda t: None if t is None else oracle.to_f64(t.index_select(0, idx.to(t.device)))
+    if conv_k is not None:
+        cw, cb, db, cs = sel(d["conv_w"]), sel(d["conv_b"]), sel(d["dt_bias"]), g(d["conv_state0"])
     A, B, C, D = (oracle.to_f64(d["A"].index_select(0, idx.to(d["A"].device))), oracle.to_f64(d["B"]),
                   oracle.to_f64(d["C"]), oracle.to_f64(d["D"].index_select(0, idx.to(d["D"].device))))
     dy = np.random.default_rng(3).normal(0, 1, x.shape)
@@ -573,7 +599,12 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
 
     def work(p):
         sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, p])
-        oracle.scan_bwd(sub(x), sub(dt), A[p], B, C, D[p], sub(z), dy=sub(dy))
+        if conv_k is not None:
+            oracle.scan_fused_bwd(sub(x), sub(dt), A[p], B, C, D[p], sub(z),
+                                  conv_w=None if cw is None else cw[p], conv_b=None if cb is None else cb[p],
+                                  conv_state0=sub(cs), dt_bias=None if db is None else db[p], dy=sub(dy))
+        else:
+            oracle.scan_bwd(sub(x), sub(dt), A[p], B, C, D[p], sub(z), dy=sub(dy))
 
     t0 = time.perf_counter()
     ts = [threading.Thread(target=work, args=(p,)) for p in parts]
@@ -589,7 +620,8 @@ def cpu_baseline_backward(shape, d, torch, workloads, threads):
             "value_1_core": elems1 / dt1,
             "sample_1_core": f"the first {len(parts[0])} of those channels on one thread ({elems1} elements, "
                              f"{dt1:.1f} s wall)",
-            "sample": f"backward: {k} of {shape.d_inner} channels over all {shape.L} steps x batch "
+            "sample": f"{'backward through the input stage' if conv_k is not None else 'backward'}: "
+                      f"{k} of {shape.d_inner} channels over all {shape.L} steps x batch "
                       f"{shape.batch} ({elems} elements, {dtm:.1f} s wall), fp64 loops per channel "
                       f"(forward keeping every state, then backward), channels split over "
                       f"{len(parts)} threads"}
@@ -739,7 +771,7 @@ def main():
                              conv_k=args.conv_k if args.fused else None, trap=args.trap,
                              mimo=args.mimo, one_call=args.one_call)
     else:
-        if args.backward and (shape.complex_state or args.fused):
+        if args.backward and shape.complex_state:
             print("--backward applies to the real-state prefill workloads", file=sys.stderr)
             sys.exit(2)
         if args.fused and shape.complex_state:
@@ -747,7 +779,8 @@ def main():
             sys.exit(2)
         conv_k = args.conv_k if args.fused else None
         if args.backward:
-            info, d = run_backward(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len)
+            info, d = run_backward(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
+                                   conv_k)
         else:
             info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
                                   conv_k, trap=args.trap, mimo=args.mimo)
@@ -796,7 +829,9 @@ def main():
             cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
                                   "softplus_dt": True, "entry_point": "ssm_scan_fwd_fused"}
         if args.backward:
-            cfg["pass"] = "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)"
+            cfg["pass"] = ("backward through the input stage (ssm_scan_bwd_fused: dx_in, ddt_raw, dconv_w, "
+                           "dconv_b, ddt_bias, dz, dA, dB, dC, dD)" if args.fused else
+                           "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)")
         if args.trap:
             cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
         if args.mimo:
@@ -822,7 +857,8 @@ def main():
     elif not args.no_cpu_baseline and not is_decode:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         if args.backward:
-            out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads)
+            out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads,
+                                                        args.conv_k if args.fused else None)
         else:
             out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
                                                args.conv_k if args.fused else None, trap=args.trap,

@@ -730,8 +730,9 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
 }
 
 // ---------------------------------------------------------------- backward through the input stage
-// The two streaming kernels of the input stage take chunks of their own (independent,
-// about 2048 blocks per launch). Workspace: the scan backward's, then u, dt, du, ddt
+// The two streaming kernels of the input stage take chunks of their own (independent:
+// enough for about 8192 blocks of 256 channels, i.e. 2048 blocks of 256 lanes at four
+// channels per lane, chunks of at least 128 steps). Workspace: the scan backward's, then u, dt, du, ddt
 // ([batch][L][d_inner] of io each) and the partial sums ([n][batch][d_inner][conv_k + 2]
 // fp32), each 256-byte aligned.
 struct InBwdPlan {
@@ -748,7 +749,7 @@ ssm_status make_in_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d
     const ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &bp);
     if (st != SSM_OK) return st;
     const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 255) / 256));
-    int64_t n = std::min<int64_t>((2048 + blocks - 1) / blocks, std::max<int64_t>(1, L / 256));
+    int64_t n = std::min<int64_t>((8192 + blocks - 1) / blocks, std::max<int64_t>(1, L / 128));
     n = std::max<int64_t>(n, 1);
     p->T = L > 0 ? (L + n - 1) / n : 1;
     p->n_chunks = L > 0 ? (int32_t)((L + p->T - 1) / p->T) : 0;
