@@ -27,7 +27,7 @@ __all__ = [
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
-    "ssm_scan_fwd_mimo_chunk_len", "selective_scan",
+    "ssm_scan_fwd_mimo_chunk_len", "selective_scan", "selective_scan_fused",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -630,6 +630,45 @@ def selective_scan(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0):
     gradients for x, dt, A, B, C, D, z and h0 from ssm_scan_bwd (dB, dC, dA and dD are
     computed in float32 and returned in their inputs' dtypes)."""
     return _SelectiveScan.apply(x, dt, A, B, C, D, z, h0, chunk_len)
+
+
+class _SelectiveScanFused(torch.autograd.Function):
+    """ssm_scan_fwd_fused forwards, ssm_scan_bwd_fused backwards."""
+
+    @staticmethod
+    def forward(ctx, x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias, chunk_len):
+        y, h_final, _ = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, conv_w=conv_w, conv_b=conv_b,
+                                           conv_state0=conv_state0, dt_bias=dt_bias, chunk_len=chunk_len,
+                                           want_conv_state=False)
+        ctx.save_for_backward(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias)
+        ctx.chunk_len = chunk_len
+        return y, h_final
+
+    @staticmethod
+    def backward(ctx, dy, dh_final):
+        x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        if dy is None:
+            dy = torch.zeros_like(x_in)
+        g = ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z, h0, conv_w=conv_w, conv_b=conv_b,
+                               conv_state0=conv_state0, dt_bias=dt_bias, dy=dy.to(x_in.dtype).contiguous(),
+                               dh_final=None if dh_final is None else dh_final.float().contiguous(),
+                               chunk_len=ctx.chunk_len, want_dz=z is not None and need[6],
+                               want_dh0=h0 is not None and need[7],
+                               want_dconv_state0=conv_state0 is not None and need[10])
+        cast = lambda t, like: None if (t is None or like is None) else t.to(like.dtype)
+        grads = (g["dx_in"], g["ddt_raw"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
+                 cast(g["dD"], D), g["dz"], g["dh0"], cast(g["dconv_w"], conv_w),
+                 cast(g["dconv_b"], conv_b), g["dconv_state0"], cast(g["ddt_bias"], dt_bias), None)
+        return tuple(gr if need[i] else None for i, gr in enumerate(grads))
+
+
+def selective_scan_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
+                         conv_state0=None, dt_bias=None, chunk_len=0):
+    """The fused prefill (input stage + scan) as a differentiable function: returns
+    (y, h_final), with gradients for every tensor input from ssm_scan_bwd_fused."""
+    return _SelectiveScanFused.apply(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0,
+                                     dt_bias, chunk_len)
 
 
 # ------------------------------------------------------------------ MIMO projections

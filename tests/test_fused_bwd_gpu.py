@@ -98,3 +98,31 @@ def test_fused_backward_deterministic_and_empty():
     torch.cuda.synchronize()
     for k in ("dconv_w", "dconv_b", "ddt_bias", "dconv_state0", "dA", "dD", "dh0"):
         assert not out[k].any(), f"{k} should be 0 for L = 0"
+
+
+def test_selective_scan_fused_autograd():
+    # The fused prefill as a torch.autograd.Function: its forward is ssm_scan_fwd_fused's
+    # and its gradients are ssm_scan_bwd_fused's for the same dy, dh_final, bit for bit.
+    case = (2, 200, 96, 16, "bf16", True, 4, 48, True, True, True)
+    d, s = _draw(case, seed=602)
+    g, t = to_dev(d), to_dev(s)
+    names = ("x", "dt_raw", "A", "B", "C", "D", "z", "h0", "conv_w", "conv_b", "conv_state0", "dt_bias")
+    src = {**g, **t}
+    leaves = {k: src[k].clone().requires_grad_(True) for k in names}
+    say("selective_scan_fused autograd")
+    y, hf = ssm.selective_scan_fused(leaves["x"], leaves["dt_raw"], leaves["A"], leaves["B"], leaves["C"],
+                                     leaves["D"], leaves["z"], leaves["h0"], conv_w=leaves["conv_w"],
+                                     conv_b=leaves["conv_b"], conv_state0=leaves["conv_state0"],
+                                     dt_bias=leaves["dt_bias"], chunk_len=48)
+    ((y.float() * g["dy"].float()).sum() + (hf * g["dh_final"]).sum()).backward()
+    y_ref, hf_ref, _ = ssm.ssm_scan_fwd_fused(g["x"], t["dt_raw"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                              g["h0"], conv_w=t["conv_w"], conv_b=t["conv_b"],
+                                              conv_state0=t["conv_state0"], dt_bias=t["dt_bias"], chunk_len=48)
+    ref = _gpu(d, s, 48)
+    torch.cuda.synchronize()
+    assert bitwise_equal(y.detach(), y_ref) and bitwise_equal(hf.detach(), hf_ref)
+    gname = {"x": "dx_in", "dt_raw": "ddt_raw"}
+    for k in names:
+        grad, want = leaves[k].grad, ref[gname.get(k, "d" + k)]
+        assert grad is not None and grad.dtype == leaves[k].dtype, k
+        assert bitwise_equal(grad, want.to(grad.dtype)), f"{k}: gradient differs from ssm_scan_bwd_fused"
