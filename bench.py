@@ -33,6 +33,9 @@ default 4) and dt the raw dt projection output, and the convolution + silu and
 softplus run inside the scan's load stage (decode: with the carried conv state).
 --trap times the exponential-trapezoidal entry points, --mimo R the MIMO ones (rank-R
 inputs and outputs per channel; elements stay channel-steps, each with R outputs).
+--backward times ssm_scan_bwd on a prefill workload, and with --fused ssm_scan_bwd_fused
+(the gradients through the input stage as well). --one-call times the decode as one call
+over all layers per token instead of one call per layer.
 """
 from __future__ import annotations
 
