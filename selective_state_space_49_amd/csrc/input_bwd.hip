@@ -249,7 +249,11 @@ __global__ __launch_bounds__(256) void k_input_bwd(InBwdArgs a) {
     };
     constexpr int XW = kBlk + (KC > 0 ? KC - 1 : 0);  // inputs a block's windows span
     int64_t t = ln.t1 - 1;
-    // whole blocks of kBlk steps, t - kBlk + 1 .. t, with every load issued first
+    // whole blocks of kBlk steps, t - kBlk + 1 .. t, with every load issued first. A
+    // block's windows span inputs tl-(KC-1) .. t; its top KC-1 (after the first block)
+    // are the previous block's lowest ones, carried over instead of read again.
+    float carry[F][V];
+    bool have = false;
     for (; t - (kBlk - 1) >= ln.t0; t -= kBlk) {
         const int64_t tl = t - (kBlk - 1);
         float duv[kBlk][V], ddv[kBlk][V], rv[kBlk][V], xw[XW][V];
@@ -262,11 +266,27 @@ __global__ __launch_bounds__(256) void k_input_bwd(InBwdArgs a) {
         }
         if constexpr (KC > 0) {
 #pragma unroll
-            for (int i = 0; i < XW; ++i) xe<IO, KC, V>(a, b, d, tl - (KC - 1) + i, xw[i]);
+            for (int i = 0; i < kBlk; ++i) xe<IO, KC, V>(a, b, d, tl - (KC - 1) + i, xw[i]);
+#pragma unroll
+            for (int i = 0; i < KC - 1; ++i) {
+                if (have) {
+#pragma unroll
+                    for (int c = 0; c < V; ++c) xw[kBlk + i][c] = carry[i][c];
+                } else {
+                    xe<IO, KC, V>(a, b, d, tl - (KC - 1) + kBlk + i, xw[kBlk + i]);
+                }
+            }
         }
 #pragma unroll
         for (int j = kBlk - 1; j >= 0; --j)
             step(tl + j, duv[j], ddv[j], rv[j], [&](int k, int c) { return xw[j + k][c]; });
+        if constexpr (KC > 1) {
+#pragma unroll
+            for (int i = 0; i < KC - 1; ++i)
+#pragma unroll
+                for (int c = 0; c < V; ++c) carry[i][c] = xw[i][c];
+            have = true;
+        }
     }
     // the rest (fewer than kBlk steps), one at a time
     for (; t >= ln.t0; --t) {
