@@ -295,3 +295,13 @@ def test_fused_backward_argument_errors(lib):
     assert call(ws=0x10080, wsb=need) == ALIGN
     assert lib.ssm_scan_bwd_fused_workspace(1, 8, 4, 4, 9, 0, 0) == 0
     assert lib.ssm_scan_bwd_fused_workspace(1, 8, 4, 3, 2, 0, 0) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # The benchmark measures one GPU; asked for more it exits with a message (before
+    # touching a GPU or torch).
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr)
