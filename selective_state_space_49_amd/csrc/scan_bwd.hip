@@ -346,7 +346,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     float A2[N], h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        // padding lanes: no decay, so nothing of the clamped channel's A reaches them
+        A2[n] = ln.valid ? a.A[ln.d * N + n] * kLog2e : 0.0f;
         h[n] = hin ? hin[n] : 0.0f;
     }
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     float lam[N], dA[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        lam[n] = mu ? mu[n] : 0.0f;
+        lam[n] = (mu && ln.valid) ? mu[n] : 0.0f;
         dA[n] = 0.0f;
     }
     float dD = 0.0f;
@@ -408,17 +409,19 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         const uint32_t ns = min((uint32_t)kSub, steps - j0);
         // The staged rows and state (complete: the last wait on vmcnt came after their
         // loads were issued; the state is the stored one, or the chunk's incoming state
-        // for the first sub-chunk). Padding lanes read their clamped channel's values
-        // with x and dy set to 0: then dt x = 0 and do = 0, so their dB and dC terms
-        // (lam dt x, do h) are exactly 0 for finite data and need no mask in the
-        // channel sums; their own outputs are not stored.
+        // for the first sub-chunk). Padding lanes stage their clamped channel's rows and
+        // stored states, which another wave writes without any ordering against this
+        // one, so they replace every staged value by 0: x = dt = dy = z = 0 and a zero
+        // start state (and a zero adjoint, below) make every term of theirs exactly 0,
+        // whatever the staged bits hold, and the channel sums need no mask. Their own
+        // outputs are not stored.
         float xv[kSub], dv[kSub], yv[kSub], zv[kSub], start[N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
             xv[j] = ln.valid ? RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]) : 0.0f;
-            dv[j] = RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]);
+            dv[j] = ln.valid ? RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]) : 0.0f;
             yv[j] = ln.valid ? RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]) : 0.0f;
-            zv[j] = GATED ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
+            zv[j] = (GATED && ln.valid) ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
         }
         if constexpr (N % 4 == 0) {
 #pragma unroll
@@ -429,6 +432,10 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         } else {
 #pragma unroll
             for (int n = 0; n < N; ++n) start[n] = __uint_as_float(stg[kStageRows + n * 64 + lane]);
+        }
+        if (!ln.valid) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) start[n] = 0.0f;
         }
         if (k > 0) {
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the LDS reads above are done

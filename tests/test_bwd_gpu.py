@@ -85,6 +85,26 @@ def test_backward_matches_oracle(case):
     _compare(got, _oracle(d), TOL[shape.io])
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_backward_padding_lanes_ignore_stale_workspace(io):
+    # 300 channels in blocks of 256 lanes: waves 1-3 of the second block are all padding
+    # lanes, clamped to channel 299, whose stored states another wave writes. A workspace
+    # full of NaN bits (as a recycled allocation may be) must not reach dB or dC (sums
+    # over the channels of a wave): the padding lanes contribute exact zeros.
+    case = (1, 1000, 300, 16, io, True, 128, True, True)
+    shape, d = _draw(case, seed=530)
+    g = to_dev(d)
+    need = ssm.ssm_scan_bwd_workspace(1, 1000, 300, 16, 128)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # every float NaN
+    say("backward padding lanes, NaN workspace", io)
+    got = ssm.ssm_scan_bwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], g["h0"],
+                           dy=g["dy"], dh_final=g["dh_final"], chunk_len=128, workspace=ws)
+    torch.cuda.synchronize()
+    for k in ("dB", "dC", "dA", "dD", "dx", "ddt"):
+        assert torch.isfinite(got[k].float()).all(), f"{k} is not finite"
+    _compare(got, _oracle(d), TOL[shape.io])
+
+
 def test_backward_empty_sequence():
     shape = ScanShape("bwd0", 2, 0, 40, 16, "f32", seed=510)
     d = make_scan_inputs(shape, "cpu")
