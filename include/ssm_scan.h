@@ -114,6 +114,28 @@ ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const 
                            ssm_dtype io, int64_t chunk_len, void *workspace,
                            size_t workspace_bytes, void *hip_stream);
 
+/* ssm_scan_fwd_noalloc: ssm_scan_fwd_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * It takes no workspace and calls no allocating routine: the chunk summaries live in a
+ * scratch array of SSM_NOALLOC_SCRATCH_BYTES (64 MiB) that the library's code object
+ * holds on every GPU it runs on, from the first use on that GPU until the process ends
+ * (its device address is looked up once per device). Same arguments, kernels, results
+ * and errors as ssm_scan_fwd_ex on the current device (hip_stream must belong to it),
+ * plus SSM_ERR_WORKSPACE, before anything is enqueued, when the plan needs more scratch
+ * than that: ssm_scan_fwd_workspace_ex(batch, L, d_inner, d_state, chunk_len) >
+ * SSM_NOALLOC_SCRATCH_BYTES. The library's own plan (chunk_len = 0) needs at most
+ * 2 * 5120 * 64 * d_state * 4 bytes (42 MB at d_state 16) and always fits. Calls on one
+ * GPU share its scratch, and nothing in it needs to start cleared (each call writes
+ * every summary before reading it); calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race on it and must be ordered by the
+ * caller. */
+#define SSM_NOALLOC_SCRATCH_BYTES (64u << 20)
+ssm_status ssm_scan_fwd_noalloc(const void *x, const void *dt, const float *A, const void *B,
+                                const void *C, const float *D, const void *z, const float *h0,
+                                void *y, float *h_final,
+                                int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                ssm_dtype io, int64_t chunk_len, void *hip_stream);
+
 /* The chunk length each prefill entry point picks for this shape with chunk_len = 0
  * (pure host functions; 0 for an invalid shape). The library cuts the sequence into
  * enough chunks to keep as many waves per SIMD resident as the entry point's rescan

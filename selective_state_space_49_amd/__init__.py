@@ -28,6 +28,7 @@ __all__ = [
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
     "ssm_scan_fwd_mimo_chunk_len", "selective_scan", "selective_scan_fused",
+    "ssm_scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,8 +48,10 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_trap", "ssm_scan_fwd_trap_profiled", "ssm_step_trap", "ssm_step_trap_replay",
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
-    "ssm_scan_fwd_mimo_chunk_len",
+    "ssm_scan_fwd_mimo_chunk_len", "ssm_scan_fwd_noalloc",
 ]
+# SSM_NOALLOC_SCRATCH_BYTES of ssm_scan.h: the scratch ssm_scan_fwd_noalloc has per GPU.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SsmError(RuntimeError):
@@ -86,6 +89,7 @@ def load_library():
         "ssm_scan_fwd": (scan + [vp, sz, vp], ci),
         "ssm_scan_fwd_ex": (scan + [i64, vp, sz, vp], ci),
         "ssm_scan_fwd_c64": (scan + [i64, vp, sz, vp], ci),
+        "ssm_scan_fwd_noalloc": (scan + [i64, vp], ci),
         "ssm_scan_fwd_profiled": (scan + [i64, vp, sz, vp, vp, i32], ci),
         "ssm_scan_fwd_c64_profiled": (scan + [i64, vp, sz, vp, vp, i32], ci),
         "ssm_status_str": ([ci], ctypes.c_char_p),
@@ -254,6 +258,34 @@ def ssm_scan_fwd_ex(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, 
     """Prefill with an explicit chunk length (0 = the library's choice)."""
     return _scan("ssm_scan_fwd_ex", False, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final,
                  workspace, want_h_final)
+
+
+def ssm_scan_fwd_noalloc(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, h_final=None,
+                         want_h_final=True):
+    """Prefill with no workspace: the library's per-GPU scratch array holds the chunk
+    summaries (see ssm_scan.h). The C entry point allocates nothing; y and h_final are
+    allocated here with torch unless given. Calls that overlap in time on one GPU race
+    on the scratch."""
+    lib = load_library()
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    _dev(x, "x"); _dev(dt, "dt", (b, L, Dn)); _dev(z, "z", (b, L, Dn))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N)); _dev(h0, "h0", (b, Dn, N), f32)
+    io = _io(x, dt, z, B, C)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", (b, L, Dn), x.dtype)
+    if h_final is None and want_h_final:
+        h_final = torch.empty((b, Dn, N), dtype=f32, device=x.device)
+    _dev(h_final, "h_final", (b, Dn, N), f32)
+    with torch.cuda.device(x.device):  # the scratch of the tensors' own GPU
+        st = lib.ssm_scan_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(h0), _ptr(y), _ptr(h_final), b, L, Dn, N, io, chunk_len,
+                                      _stream(x))
+    _check(st)
+    return y, h_final
 
 
 def ssm_scan_fwd_c64(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, h_final=None,

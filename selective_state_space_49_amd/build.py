@@ -23,7 +23,7 @@ OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["scan_real.hip", "scan_complex.hip", "step.hip", "scan_bwd.hip", "scan_mimo.hip",
-               "input_bwd.hip"]
+               "input_bwd.hip", "scratch.hip"]
 CPP_SOURCES = ["api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",
@@ -58,7 +58,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """
     objdir = OBJDIR if out == LIB else out + ".objs"
     os.makedirs(objdir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=4) as ex:
+    with ThreadPoolExecutor(max_workers=8) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, objdir, defines), HIP_SOURCES + CPP_SOURCES))
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

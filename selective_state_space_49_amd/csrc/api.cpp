@@ -145,7 +145,7 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
                        int64_t chunk_len, void *workspace, size_t workspace_bytes,
                        void *hip_stream, bool cplx, void *const *events = nullptr,
                        int32_t n_events = 0, const InputStage *in = nullptr,
-                       const Trap *trap = nullptr, int32_t rank = 0) {
+                       const Trap *trap = nullptr, int32_t rank = 0, bool use_scratch = false) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     const bool mimo = rank != 0;
     if (mimo && !valid_rank(rank)) return fail(SSM_ERR_UNSUPPORTED, "rank %d not in {1,2,4,8}", rank);
@@ -213,6 +213,16 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
                                                        batch * conv_rows * d_inner, (int)eb, s),
                                  "conv state fill");
         return ok();
+    }
+    if (use_scratch && plan.ws_bytes > 0) {
+        // the no-allocation entry point: the device's own scratch array is the workspace
+        if (plan.ws_bytes > (size_t)SSM_NOALLOC_SCRATCH_BYTES)
+            return fail(SSM_ERR_WORKSPACE,
+                        "this chunk plan needs %zu bytes of scratch; ssm_scan_fwd_noalloc has %zu "
+                        "(use a longer chunk_len, or ssm_scan_fwd_ex with a workspace)",
+                        plan.ws_bytes, (size_t)SSM_NOALLOC_SCRATCH_BYTES);
+        st = launch_status(ssm::scratch_buffer(&workspace, &workspace_bytes), "scratch lookup");
+        if (st != SSM_OK) return st;
     }
     if (plan.ws_bytes > 0) {
         if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required", plan.ws_bytes);
@@ -502,6 +512,16 @@ ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const 
                            size_t workspace_bytes, void *hip_stream) {
     return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
                        chunk_len, workspace, workspace_bytes, hip_stream, false);
+}
+
+ssm_status ssm_scan_fwd_noalloc(const void *x, const void *dt, const float *A, const void *B,
+                                const void *C, const float *D, const void *z, const float *h0,
+                                void *y, float *h_final, int64_t batch, int64_t L,
+                                int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                int64_t chunk_len, void *hip_stream) {
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, nullptr, 0, hip_stream, false, nullptr, 0, nullptr, nullptr, 0,
+                       true);
 }
 
 ssm_status ssm_scan_fwd_c64(const void *x, const void *dt, const float *A, const void *B,

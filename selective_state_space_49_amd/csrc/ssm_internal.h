@@ -83,6 +83,9 @@ hipError_t launch_carry(const ScanArgs &a, int d_state, hipStream_t s);
 // dst[i] = src ? src[i] : 0 for count elements of elem_bytes (2 or 4) bytes each.
 hipError_t launch_elem_fill(void *dst, const void *src, int64_t count, int elem_bytes,
                             hipStream_t s);
+// The device address and size of the current device's scratch array (scratch.hip),
+// looked up once per device. Allocates nothing.
+hipError_t scratch_buffer(void **ptr, size_t *bytes);
 
 hipError_t launch_step_real(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                             hipStream_t s);

@@ -105,6 +105,33 @@ def test_scan_argument_errors(lib):
     assert "d_state" in ssm.ssm_last_error() or "chunk" in ssm.ssm_last_error()
 
 
+def test_noalloc_argument_errors(lib):
+    # The no-allocation prefill validates like ssm_scan_fwd_ex and rejects, before
+    # anything is enqueued (no GPU is touched), a plan that needs more scratch than its
+    # per-GPU array holds.
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def call(x=0x1000, A=0x1000, y=0x1000, batch=1, L=8, Dn=4, N=4, io=0, chunk=0):
+        return lib.ssm_scan_fwd_noalloc(p(x), p(0x1000), p(A), p(0x1000), p(0x1000), p(0x1000),
+                                        None, None, p(y), None, batch, L, Dn, N, io, chunk, None)
+
+    assert call(N=3) == UNSUP
+    assert call(io=2) == DTYPE
+    assert call(x=None) == NULL
+    assert call(A=0x1004) == ALIGN
+    assert call(batch=-1) == SHAPE
+    assert call(L=0) == OK  # nothing to do (no h_final wanted), nothing enqueued
+    # 256k steps of 8192 channels in 64-step chunks: 4096 chunks, 2 x 4095 x 512 KiB of
+    # summaries, far beyond the 64 MiB of scratch
+    need = ssm.ssm_scan_fwd_workspace_ex(1, 262144, 8192, 16, 64)
+    assert need > ssm.NOALLOC_SCRATCH_BYTES
+    assert call(L=262144, Dn=8192, N=16, io=1, chunk=64) == WS
+    assert "scratch" in ssm.ssm_last_error() and str(ssm.NOALLOC_SCRATCH_BYTES) in ssm.ssm_last_error()
+    # the library's own plan for the workloads fits
+    for (b, L, Dn) in [(2, 4096, 8192), (1, 262144, 8192), (4, 8192, 4096), (3, 5000, 300)]:
+        assert 0 < ssm.ssm_scan_fwd_workspace(b, L, Dn, 16) <= ssm.NOALLOC_SCRATCH_BYTES
+
+
 def test_step_argument_errors(lib):
     p = ctypes.c_void_p
     a = dict(h=0x1000, x=0x1000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None, y=0x1000)
