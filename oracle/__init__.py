@@ -67,9 +67,9 @@ def _load():
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_input_stage_bwd_f64.argtypes = [i64, i64, i64, i64] + [dp] * 14
         lib.oracle_input_stage_bwd_f64.restype = ctypes.c_int
-        lib.oracle_scan_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 12
+        lib.oracle_scan_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 13
         lib.oracle_scan_trap_f64.restype = ctypes.c_int
-        lib.oracle_step_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 11
+        lib.oracle_step_trap_f64.argtypes = [i64, i64, i64, i64] + [dp] * 12
         lib.oracle_step_trap_f64.restype = ctypes.c_int
         lib.oracle_scan_mimo_f64.argtypes = [i64] * 5 + [dp] * 10
         lib.oracle_scan_mimo_f64.restype = ctypes.c_int
@@ -331,11 +331,13 @@ def _check(a, shape, name):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(a.shape)}")
 
 
-def scan_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
+def scan_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None, lam=None):
     """Real-state prefill with the exponential-trapezoidal discretisation. As scan(),
-    plus the input before step 0: x_prev [b, Dn] and B_prev [b, N] (None: zero).
-    Returns (y [b, L, Dn], h_final [b, Dn, N])."""
-    x, dt, A, B, C, D, z, h0, x_prev, B_prev = map(to_f64, (x, dt, A, B, C, D, z, h0, x_prev, B_prev))
+    plus the input before step 0: x_prev [b, Dn] and B_prev [b, N] (None: zero), and
+    the weight of each step's current input lam [b, L, Dn] (None: 1/2, the trapezoid
+    rule; 1 is Euler's step). Returns (y [b, L, Dn], h_final [b, Dn, N])."""
+    x, dt, A, B, C, D, z, h0, x_prev, B_prev, lam = map(
+        to_f64, (x, dt, A, B, C, D, z, h0, x_prev, B_prev, lam))
     b, L, Dn = x.shape
     N = A.shape[1]
     _check(dt, (b, L, Dn), "dt"); _check(B, (b, L, N), "B"); _check(C, (b, L, N), "C")
@@ -344,21 +346,22 @@ def scan_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
     if h0 is not None: _check(h0, (b, Dn, N), "h0")
     if x_prev is not None: _check(x_prev, (b, Dn), "x_prev")
     if B_prev is not None: _check(B_prev, (b, N), "B_prev")
+    if lam is not None: _check(lam, (b, L, Dn), "lam")
     y = np.empty((b, L, Dn)); hf = np.empty((b, Dn, N))
     rc = _load().oracle_scan_trap_f64(b, L, Dn, N, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
-                                      _p(z), _p(h0), _p(x_prev), _p(B_prev), _p(y), _p(hf))
+                                      _p(z), _p(h0), _p(x_prev), _p(B_prev), _p(lam), _p(y), _p(hf))
     if rc != 0:
         raise RuntimeError("oracle_scan_trap_f64 failed")
     return y, hf
 
 
-def step_trap(h, x_prev, B_prev, x, dt, A, B, C, D, z=None):
-    """One exponential-trapezoidal decode token. h: [Ln, S, Dn, N]; x_prev, x, dt, z:
-    [Ln, S, Dn]; B_prev, B, C: [Ln, S, N]; A: [Ln, Dn, N]; D: [Ln, Dn]. x_prev and
-    B_prev are the previous token's x and B (None: no previous input). Returns
-    (y [Ln, S, Dn], h_new) without touching h."""
+def step_trap(h, x_prev, B_prev, x, dt, A, B, C, D, z=None, lam=None):
+    """One exponential-trapezoidal decode token. h: [Ln, S, Dn, N]; x_prev, x, dt, z,
+    lam: [Ln, S, Dn]; B_prev, B, C: [Ln, S, N]; A: [Ln, Dn, N]; D: [Ln, Dn]. x_prev and
+    B_prev are the previous token's x and B (None: no previous input); lam the weight
+    of the current input (None: 1/2). Returns (y [Ln, S, Dn], h_new) without touching h."""
     h = to_f64(h).copy()
-    x_prev, B_prev, x, dt, A, B, C, D, z = map(to_f64, (x_prev, B_prev, x, dt, A, B, C, D, z))
+    x_prev, B_prev, x, dt, A, B, C, D, z, lam = map(to_f64, (x_prev, B_prev, x, dt, A, B, C, D, z, lam))
     Ln, S, Dn = x.shape
     N = h.shape[-1]
     _check(h, (Ln, S, Dn, N), "h"); _check(B, (Ln, S, N), "B"); _check(C, (Ln, S, N), "C")
@@ -366,9 +369,10 @@ def step_trap(h, x_prev, B_prev, x, dt, A, B, C, D, z=None):
     if z is not None: _check(z, (Ln, S, Dn), "z")
     if x_prev is not None: _check(x_prev, (Ln, S, Dn), "x_prev")
     if B_prev is not None: _check(B_prev, (Ln, S, N), "B_prev")
+    if lam is not None: _check(lam, (Ln, S, Dn), "lam")
     y = np.empty((Ln, S, Dn))
     rc = _load().oracle_step_trap_f64(Ln, S, Dn, N, _p(h), _p(x_prev), _p(B_prev), _p(x), _p(dt),
-                                      _p(A), _p(B), _p(C), _p(D), _p(z), _p(y))
+                                      _p(lam), _p(A), _p(B), _p(C), _p(D), _p(z), _p(y))
     if rc != 0:
         raise RuntimeError("oracle_step_trap_f64 failed")
     return y, h

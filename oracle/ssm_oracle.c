@@ -438,28 +438,36 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
  *
  * "Jamba — SSM-Transformer Híbrido", section "Mamba-3: a linha de base de SSM puro
  * em 2026", item 1: Mamba-3 replaces the Euler discretisation (Bbar = dt B, above)
- * by a recurrence in which a convolution-like operation acts on the state input
- * inside the recurrence. The page gives no formula; the reading taken here is the
- * plain rule the name describes. Over a step of length dt the exact update of
- * h' = A h + B(s) x(s) adds the integral of exp(A (dt - s)) B(s) x(s) over [0, dt];
- * Euler takes dt B_t x_t, the trapezoid rule averages the integrand at both ends:
+ * by a more expressive recurrence in which a convolution-like operation acts on the
+ * state input inside the recurrence. The key-terms tables of the zh and hi lessons
+ * ("Phase 10 · 21 Jamba hybrid SSM-Transformer") add that this recurrence subsumes
+ * Mamba-2's Euler discretisation, so Euler must be one of its settings. No page gives
+ * a formula; the reading taken here is the rule the name describes, with a weight.
+ * Over a step of length dt the exact update of h' = A h + B(s) x(s) adds the integral
+ * of exp(A (dt - s)) B(s) x(s) over [0, dt]. A two-point rule over the step's ends,
+ * the current input with weight lambda and the older one (decayed across the step)
+ * with weight 1 - lambda, gives
  *
- *     h_t = dA h_{t-1} + (dt/2) (dA B_{t-1} x_{t-1} + B_t x_t),   dA = exp(dt A),
+ *     h_t = dA h_{t-1} + dt ((1 - lam_t) dA B_{t-1} x_{t-1} + lam_t B_t x_t),
+ *     dA = exp(dt A):
  *
- * a two-tap filter over the state inputs B x, with the older tap decayed. The first
+ * a two-tap filter over the state inputs B x. lam_t = 1 is Euler's step (the scan
+ * above); lam_t = 1/2 is the trapezoid rule, the default (lam = NULL); a data-
+ * dependent lam, like dt, makes the rule more expressive than either. The first
  * step's previous input is B_prev x_prev (NULL: zero, a sequence with no input
  * before it); a caller resuming a sequence passes the last step of the previous
  * part. y_t is as in the Euler scan. Order of operations:
- *     dA = exp(dt * A[d][n]);  w = 0.5 * dt;
- *     h[n] = (dA * h[n]) + w * ((dA * (Bp[n] * xp)) + (B[n] * x));
+ *     dA = exp(dt * A[d][n]);  wc = dt * lam;  wp = dt * (1 - lam);
+ *     h[n] = (dA * h[n]) + ((wp * (dA * (Bp[n] * xp))) + (wc * (B[n] * x)));
  *     acc = acc + C[n] * h[n]  (n ascending);  y = acc + D[d] * x;  then the gate.
- * Layouts as above; x_prev [batch][Dn], B_prev [batch][N].
+ * Layouts as above; lam [batch][L][Dn] like dt (NULL: 1/2 everywhere); x_prev
+ * [batch][Dn], B_prev [batch][N].
  */
 int oracle_scan_trap_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
                          const double *x, const double *dt, const double *A,
                          const double *B, const double *C, const double *Dv,
                          const double *z, const double *h0,
-                         const double *x_prev, const double *B_prev,
+                         const double *x_prev, const double *B_prev, const double *lam,
                          double *y, double *h_final)
 {
     if (batch < 0 || L < 0 || Dn < 0 || N <= 0) return -1;
@@ -477,12 +485,13 @@ int oracle_scan_trap_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
                 const int64_t i = (b * L + t) * Dn + d;
                 const int64_t s = (b * L + t) * N;
                 const double xv = x[i], dv = dt[i];
-                const double w = 0.5 * dv;
+                const double lv = lam ? lam[i] : 0.5;
+                const double wc = dv * lv, wp = dv * (1.0 - lv);
                 double acc = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
                     const double dA = exp(dv * A[d * N + n]);
                     const double prev = Bp ? Bp[n] * xp : 0.0;
-                    h[n] = dA * h[n] + w * (dA * prev + B[s + n] * xv);
+                    h[n] = dA * h[n] + (wp * (dA * prev) + wc * (B[s + n] * xv));
                     acc = acc + C[s + n] * h[n];
                 }
                 double yv = acc + Dv[d] * xv;
@@ -501,12 +510,13 @@ int oracle_scan_trap_f64(int64_t batch, int64_t L, int64_t Dn, int64_t N,
 
 /* One decode token of the exponential-trapezoidal recurrence; h updated in place.
  * x_prev [n_layers][n_seq][Dn] and B_prev [n_layers][n_seq][N] are the previous
- * token's x and B (NULL: no previous input). */
+ * token's x and B (NULL: no previous input); lam [n_layers][n_seq][Dn] is the token's
+ * weight (NULL: 1/2). */
 int oracle_step_trap_f64(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N,
                          double *h, const double *x_prev, const double *B_prev,
-                         const double *x, const double *dt, const double *A,
-                         const double *B, const double *C, const double *Dv,
-                         const double *z, double *y)
+                         const double *x, const double *dt, const double *lam,
+                         const double *A, const double *B, const double *C,
+                         const double *Dv, const double *z, double *y)
 {
     if (n_layers < 0 || n_seq < 0 || Dn < 0 || N <= 0) return -1;
     const int has_prev = x_prev && B_prev;
@@ -518,12 +528,13 @@ int oracle_step_trap_f64(int64_t n_layers, int64_t n_seq, int64_t Dn, int64_t N,
                 double *hs = h + i * N;
                 const double *Ad = A + (l * Dn + d) * N;
                 const double xv = x[i], dv = dt[i];
-                const double w = 0.5 * dv;
+                const double lv = lam ? lam[i] : 0.5;
+                const double wc = dv * lv, wp = dv * (1.0 - lv);
                 double acc = 0.0;
                 for (int64_t n = 0; n < N; ++n) {
                     const double dA = exp(dv * Ad[n]);
                     const double prev = has_prev ? B_prev[s + n] * x_prev[i] : 0.0;
-                    hs[n] = dA * hs[n] + w * (dA * prev + B[s + n] * xv);
+                    hs[n] = dA * hs[n] + (wp * (dA * prev) + wc * (B[s + n] * xv));
                     acc = acc + C[s + n] * hs[n];
                 }
                 double yv = acc + Dv[l * Dn + d] * xv;

@@ -26,13 +26,17 @@ pages or plain mathematics fix:
   backward      central finite differences of sum(dy y) + sum(dh_final h_final)
                 through the forward oracle, for every element of every input, against
                 the backward oracle's gradients.
-  trapezoid     the exponential-trapezoidal discretisation (the plain reading of the
-                Mamba-3 item on the same page): each step's two input taps written
-                out as a sum with exp of summed dt; with A = 0 the state is exactly
-                numpy's trapezoid rule over the samples B x on the time grid; against
-                the closed-form solution of the continuous ODE the error falls about
-                4x per halved step (second order), where Euler's halves; split/resume
-                with the previous input passed on, and L decode steps, bit for bit.
+  trapezoid     the exponential-trapezoidal discretisation (the reading of the
+                Mamba-3 item on the same page, and of the key-terms rows that say it
+                subsumes Euler's): each step's two input taps, weighted lam and 1 - lam,
+                written out as a sum with exp of summed dt, for the default weight 1/2
+                and for random weights; weight 1 is the Euler scan and its decode step;
+                with A = 0 and weight 1/2 the state is exactly numpy's trapezoid rule
+                over the samples B x on the time grid; against the closed-form solution
+                of the continuous ODE the error falls about 4x per halved step at
+                weight 1/2 (second order) and 2x at weight 1, as Euler's does;
+                split/resume with the previous input passed on, and L decode steps,
+                bit for bit, with random weights.
   MIMO          the reading of Mamba-3's matrix-valued projections (B_t, C_t of size
                 N x R, R inputs and outputs per channel): rank 1 is the scan above
                 bit for bit; with no skip, gate or initial state each output is the
@@ -528,13 +532,15 @@ def pin_fused_backward_finite_differences(O, tol=1e-7):
 
 # ----------------------------------------------------------------------------- trapezoid
 
-def brute_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
+def brute_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None, lam=None):
     """The exponential-trapezoidal state written out: with S_t the running sum of dt
-    (S_-1 = 0), p_s = B_s x_s and p_-1 the input before step 0,
-        h_t = exp(A S_t) h0 + sum_{s<=t} (dt_s / 2) (exp(A (S_t - S_s)) p_s
-                                                  + exp(A (S_t - S_{s-1})) p_{s-1})."""
+    (S_-1 = 0), p_s = B_s x_s, p_-1 the input before step 0 and lam_s the weight of
+    step s's current input (1/2 when lam is None),
+        h_t = exp(A S_t) h0 + sum_{s<=t} dt_s (lam_s exp(A (S_t - S_s)) p_s
+                                               + (1 - lam_s) exp(A (S_t - S_{s-1})) p_{s-1})."""
     b, L, Dn = x.shape
     N = A.shape[1]
+    lam = np.full((b, L, Dn), 0.5) if lam is None else lam
     S = np.concatenate([np.zeros((b, 1, Dn)), np.cumsum(dt, axis=1)], axis=1)   # S[:, t+1] = S_t
     y = np.zeros((b, L, Dn)); hf = np.zeros((b, Dn, N))
     for bi in range(b):
@@ -546,9 +552,10 @@ def brute_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
             for t in range(L):
                 h = np.zeros(N) if h0 is None else np.exp(A[d] * S[bi, t + 1, d]) * h0[bi, d]
                 for s_ in range(t + 1):
-                    wgt = dt[bi, s_, d] / 2.0
-                    h = h + wgt * (np.exp(A[d] * (S[bi, t + 1, d] - S[bi, s_ + 1, d])) * p[s_ + 1]
-                                   + np.exp(A[d] * (S[bi, t + 1, d] - S[bi, s_, d])) * p[s_])
+                    lv = lam[bi, s_, d]
+                    h = h + dt[bi, s_, d] * (
+                        lv * np.exp(A[d] * (S[bi, t + 1, d] - S[bi, s_ + 1, d])) * p[s_ + 1]
+                        + (1.0 - lv) * np.exp(A[d] * (S[bi, t + 1, d] - S[bi, s_, d])) * p[s_])
                 yv = float(C[bi, t] @ h) + D[d] * x[bi, t, d]
                 if z is not None:
                     yv *= silu(z[bi, t, d])
@@ -559,15 +566,44 @@ def brute_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None):
 
 
 def pin_trap_brute_force(O, tol=1e-12):
-    for seed, with_prev in [(71, True), (72, False)]:
+    # the default weight (1/2, the trapezoid rule) and random per-step weights in [0, 1]
+    for seed, with_prev, with_lam in [(71, True, False), (72, False, False), (76, True, True),
+                                      (77, False, True)]:
         inp = tiny_real(seed, L=16)
         r = np.random.default_rng(seed + 100)
         b, L, Dn = inp["x"].shape
         xp = r.normal(0, 1, (b, Dn)) if with_prev else None
         Bp = r.normal(0, 1, (b, inp["A"].shape[1])) if with_prev else None
-        y, hf = O.scan_trap(**inp, x_prev=xp, B_prev=Bp)
-        yb, hb = brute_trap(**inp, x_prev=xp, B_prev=Bp)
-        assert _rel(y, yb) <= tol and _rel(hf, hb) <= tol, f"trapezoid vs brute force (prev={with_prev})"
+        lam = r.uniform(0.0, 1.0, (b, L, Dn)) if with_lam else None
+        y, hf = O.scan_trap(**inp, x_prev=xp, B_prev=Bp, lam=lam)
+        yb, hb = brute_trap(**inp, x_prev=xp, B_prev=Bp, lam=lam)
+        assert _rel(y, yb) <= tol and _rel(hf, hb) <= tol, \
+            f"trapezoid vs brute force (prev={with_prev}, lam={with_lam})"
+        if not with_lam:  # an explicit weight of 1/2 is the default
+            y2, h2 = O.scan_trap(**inp, x_prev=xp, B_prev=Bp, lam=np.full((b, L, Dn), 0.5))
+            assert _bitwise(y2, y) and _bitwise(h2, hf), "lam = 1/2 differs from the default"
+
+
+def pin_trap_lambda_one_is_euler(O, tol=1e-13):
+    # Weight 1 on the current input is Euler's step: the plain scan (and its decode
+    # step), whatever the previous input holds.
+    inp = tiny_real(78, L=24)
+    r = np.random.default_rng(178)
+    b, L, Dn = inp["x"].shape
+    N = inp["A"].shape[1]
+    ones = np.ones((b, L, Dn))
+    y, hf = O.scan_trap(**inp, x_prev=r.normal(0, 1, (b, Dn)), B_prev=r.normal(0, 1, (b, N)), lam=ones)
+    ye, he = O.scan(**inp)
+    assert _rel(y, ye) <= tol and _rel(hf, he) <= tol, "lam = 1 is not the Euler scan"
+    Ln, S = 2, 3
+    h = r.normal(0, 1, (Ln, S, Dn, N))
+    x = r.normal(0, 1, (Ln, S, Dn)); dt = np.log1p(np.exp(r.normal(-1, 0.5, (Ln, S, Dn))))
+    B = r.normal(0, 1, (Ln, S, N)); C = r.normal(0, 1, (Ln, S, N)); z = r.normal(0, 1, (Ln, S, Dn))
+    A = -np.exp(r.normal(0, 0.5, (Ln, Dn, N))); D = r.normal(1, 0.1, (Ln, Dn))
+    yt, ht = O.step_trap(h, r.normal(0, 1, (Ln, S, Dn)), r.normal(0, 1, (Ln, S, N)), x, dt, A, B, C, D, z,
+                         lam=np.ones((Ln, S, Dn)))
+    ys, hs = O.step(h, x, dt, A, B, C, D, z)
+    assert _rel(yt, ys) <= tol and _rel(ht, hs) <= tol, "decode with lam = 1 is not the Euler step"
 
 
 def pin_trap_a_zero_is_trapezoid_rule(O, tol=1e-12):
@@ -597,20 +633,26 @@ def pin_trap_second_order(O):
     # Euler scan's (first order) ~2x.
     a, bb, w, T, h0 = 1.3, 0.7, 2.1, 3.0, 0.4
     exact = np.exp(-a * T) * h0 + bb * (a * np.cos(w * T) + w * np.sin(w * T) - a * np.exp(-a * T)) / (a * a + w * w)
-    errs, errs_euler = [], []
+    # With the weight 1 (Euler's step inside the same rule) it is first order again.
+    errs, errs_euler, errs_one = [], [], []
     for M in (40, 80, 160):
         dt = np.full((1, M, 1), T / M)
         s = np.arange(1, M + 1) * (T / M)
         x = np.cos(w * s).reshape(1, M, 1)
         B = np.full((1, M, 1), bb); C = np.ones((1, M, 1))
         A = np.full((1, 1), -a); D = np.zeros(1); H0 = np.full((1, 1, 1), h0)
-        _, hf = O.scan_trap(x, dt, A, B, C, D, None, H0, x_prev=np.ones((1, 1)), B_prev=np.full((1, 1), bb))
+        prev = dict(x_prev=np.ones((1, 1)), B_prev=np.full((1, 1), bb))
+        _, hf = O.scan_trap(x, dt, A, B, C, D, None, H0, **prev)
+        _, h1 = O.scan_trap(x, dt, A, B, C, D, None, H0, **prev, lam=np.ones((1, M, 1)))
         _, he = O.scan(x, dt, A, B, C, D, None, H0)
         errs.append(abs(hf[0, 0, 0] - exact)); errs_euler.append(abs(he[0, 0, 0] - exact))
+        errs_one.append(abs(h1[0, 0, 0] - exact))
     for e1, e2 in zip(errs, errs[1:]):
         assert 3.6 <= e1 / e2 <= 4.4, f"trapezoid convergence ratio {e1 / e2:.3f}"
     for e1, e2 in zip(errs_euler, errs_euler[1:]):
         assert 1.7 <= e1 / e2 <= 2.3, f"Euler convergence ratio {e1 / e2:.3f}"
+    for e1, e2 in zip(errs_one, errs_one[1:]):
+        assert 1.7 <= e1 / e2 <= 2.3, f"lam = 1 convergence ratio {e1 / e2:.3f}"
 
 
 def pin_trap_split_resume(O):
@@ -619,16 +661,18 @@ def pin_trap_split_resume(O):
     b, L, Dn = inp["x"].shape
     N = inp["A"].shape[1]
     xp, Bp = r.normal(0, 1, (b, Dn)), r.normal(0, 1, (b, N))
-    y, hf = O.scan_trap(**inp, x_prev=xp, B_prev=Bp)
+    lam = r.uniform(0.0, 1.0, (b, L, Dn))
+    y, hf = O.scan_trap(**inp, x_prev=xp, B_prev=Bp, lam=lam)
     k = 13
     part = lambda v, sl: None if v is None else v[:, sl]
     y1, h1 = O.scan_trap(part(inp["x"], slice(0, k)), part(inp["dt"], slice(0, k)), inp["A"],
                          part(inp["B"], slice(0, k)), part(inp["C"], slice(0, k)), inp["D"],
-                         part(inp["z"], slice(0, k)), inp["h0"], x_prev=xp, B_prev=Bp)
+                         part(inp["z"], slice(0, k)), inp["h0"], x_prev=xp, B_prev=Bp,
+                         lam=part(lam, slice(0, k)))
     y2, h2 = O.scan_trap(part(inp["x"], slice(k, L)), part(inp["dt"], slice(k, L)), inp["A"],
                          part(inp["B"], slice(k, L)), part(inp["C"], slice(k, L)), inp["D"],
                          part(inp["z"], slice(k, L)), h1, x_prev=inp["x"][:, k - 1],
-                         B_prev=inp["B"][:, k - 1])
+                         B_prev=inp["B"][:, k - 1], lam=part(lam, slice(k, L)))
     assert _bitwise(np.concatenate([y1, y2], axis=1), y) and _bitwise(h2, hf), "trapezoid split/resume"
 
 
@@ -643,15 +687,18 @@ def pin_trap_step_equals_scan(O):
     A = -np.exp(r.normal(0, 0.5, (Ln, Dn, N))); D = r.normal(1, 0.1, (Ln, Dn))
     h = r.normal(0, 1, (Ln, S, Dn, N))
     xp0, Bp0 = r.normal(0, 1, (Ln, S, Dn)), r.normal(0, 1, (Ln, S, N))
+    lam = r.uniform(0.0, 1.0, (Ln, S, L, Dn))
     hs, ys = h, []
     for t in range(L):
         xp = xp0 if t == 0 else x[:, :, t - 1]
         Bp = Bp0 if t == 0 else B[:, :, t - 1]
-        yt, hs = O.step_trap(hs, xp, Bp, x[:, :, t], dt[:, :, t], A, B[:, :, t], C[:, :, t], D, z[:, :, t])
+        yt, hs = O.step_trap(hs, xp, Bp, x[:, :, t], dt[:, :, t], A, B[:, :, t], C[:, :, t], D, z[:, :, t],
+                             lam=lam[:, :, t])
         ys.append(yt)
     ys = np.stack(ys, axis=2)
     for l in range(Ln):
-        yl, hl = O.scan_trap(x[l], dt[l], A[l], B[l], C[l], D[l], z[l], h[l], x_prev=xp0[l], B_prev=Bp0[l])
+        yl, hl = O.scan_trap(x[l], dt[l], A[l], B[l], C[l], D[l], z[l], h[l], x_prev=xp0[l], B_prev=Bp0[l],
+                             lam=lam[l])
         assert _bitwise(ys[l], yl) and _bitwise(hs[l], hl), f"trapezoid decode vs prefill, layer {l}"
 
 
@@ -765,7 +812,8 @@ ALL_PINS = [
     pin_conv_matches_numpy, pin_conv_impulse, pin_conv_state_carry, pin_softplus,
     pin_fused_identity_filter, pin_fused_step_equals_scan, pin_backward_finite_differences,
     pin_fused_backward_finite_differences,
-    pin_trap_brute_force, pin_trap_a_zero_is_trapezoid_rule, pin_trap_second_order,
+    pin_trap_brute_force, pin_trap_lambda_one_is_euler, pin_trap_a_zero_is_trapezoid_rule,
+    pin_trap_second_order,
     pin_trap_split_resume, pin_trap_step_equals_scan,
     pin_mimo_rank_one_is_siso, pin_mimo_superposition, pin_mimo_brute_force,
     pin_mimo_split_resume, pin_mimo_step_equals_scan,

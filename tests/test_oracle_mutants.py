@@ -69,17 +69,31 @@ MUTANTS = {
     "bwd_dD_ungated": ("dD[d] += dout * xv;", "dD[d] += dy[i] * xv;"),
     "bwd_dh_final_ignored": ("lam[n] = dh_final ? dh_final[(b * Dn + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
     "bwd_dB_without_dt": ("dB[s + n] += lt * dv * xv;", "dB[s + n] += lt * xv;"),
-    "trap_prev_not_decayed": ("                    const double prev = Bp ? Bp[n] * xp : 0.0;\n                    h[n] = dA * h[n] + w * (dA * prev + B[s + n] * xv);",
-                              "                    const double prev = Bp ? Bp[n] * xp : 0.0;\n                    h[n] = dA * h[n] + w * (prev + B[s + n] * xv);"),
-    "trap_full_step_weight": ("const double w = 0.5 * dv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);\n                    const double prev = Bp",
-                              "const double w = dv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);\n                    const double prev = Bp"),
+    "trap_prev_not_decayed": ("h[n] = dA * h[n] + (wp * (dA * prev) + wc * (B[s + n] * xv));",
+        "h[n] = dA * h[n] + (wp * prev + wc * (B[s + n] * xv));"),
+    "trap_default_weight_is_euler": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+        "const double lv = lam ? lam[i] : 1.0;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "trap_older_weight_full": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+        "const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "trap_older_weight_without_dt": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+        "const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "trap_weights_swapped": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+        "const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * (1.0 - lv), wp = dv * lv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "trap_lambda_ignored": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+        "const double lv = 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "trap_lambda_of_next_step": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);",
+        "const double lv = lam ? lam[(b * L + (t + 1) % L) * Dn + d] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * A[d * N + n]);"),
+    "trap_decode_lambda_ignored": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * Ad[n]);",
+        "const double lv = 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * Ad[n]);"),
+    "trap_decode_weights_swapped": ("const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * lv, wp = dv * (1.0 - lv);\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * Ad[n]);",
+        "const double lv = lam ? lam[i] : 0.5;\n                const double wc = dv * (1.0 - lv), wp = dv * lv;\n                double acc = 0.0;\n                for (int64_t n = 0; n < N; ++n) {\n                    const double dA = exp(dv * Ad[n]);"),
     "trap_prev_input_not_advanced": ("                xp = xv;\n", ""),
     "trap_prev_B_row_ahead": ("                Bp = B + s;", "                Bp = B + s + N;"),
     "trap_first_prev_ignored": ("double xp = has_prev ? x_prev[b * Dn + d] : 0.0;", "double xp = 0.0;"),
     "trap_decode_prev_is_current_B": ("const double prev = has_prev ? B_prev[s + n] * x_prev[i] : 0.0;",
                                       "const double prev = has_prev ? B[s + n] * x_prev[i] : 0.0;"),
-    "trap_decode_prev_not_decayed": ("hs[n] = dA * hs[n] + w * (dA * prev + B[s + n] * xv);",
-                                     "hs[n] = dA * hs[n] + w * (prev + B[s + n] * xv);"),
+    "trap_decode_prev_not_decayed": ("hs[n] = dA * hs[n] + (wp * (dA * prev) + wc * (B[s + n] * xv));",
+                                     "hs[n] = dA * hs[n] + (wp * prev + wc * (B[s + n] * xv));"),
     "mimo_B_transposed": ("const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[n * R + r]) * xv[r];",
                           "const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[r * N + n]) * xv[r];"),
     "mimo_dt_dropped_from_input": ("const double dA = exp(dv * A[d * N + n]);\n                    double u = 0.0;\n                    for (int64_t r = 0; r < R; ++r) u = u + (dv * Bt[n * R + r]) * xv[r];",
