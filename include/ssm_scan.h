@@ -139,8 +139,9 @@ ssm_status ssm_scan_fwd_noalloc(const void *x, const void *dt, const float *A, c
 /* The chunk length each prefill entry point picks for this shape with chunk_len = 0
  * (pure host functions; 0 for an invalid shape). The library cuts the sequence into
  * enough chunks to keep as many waves per SIMD resident as the entry point's rescan
- * kernel is compiled for: 5 for ssm_scan_fwd / _ex / _trap and ssm_scan_fwd_mimo up to
- * rank 4, 4 for ssm_scan_fwd_fused, ssm_scan_fwd_c64 and rank 8 (and the backward).
+ * kernel is compiled for: 5 for ssm_scan_fwd / _ex / _trap (without lam) and
+ * ssm_scan_fwd_mimo up to rank 4, 4 for ssm_scan_fwd_fused, ssm_scan_fwd_c64,
+ * ssm_scan_fwd_trap with lam and rank 8 (and the backward).
  * A plan with fewer chunks needs no more workspace, so ssm_scan_fwd_workspace_ex(...,
  * 0) also suffices for ssm_scan_fwd_fused. */
 int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
@@ -347,42 +348,51 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
 /* ------------------------------------------------------------------ exponential-trapezoidal
  * ssm_scan_fwd_trap: the prefill of ssm_scan_fwd_ex with the exponential-trapezoidal
  * discretisation that Mamba-3 puts in place of Euler's ("Jamba — SSM-Transformer
- * Híbrido", section "Mamba-3: a linha de base de SSM puro em 2026", item 1: a
- * convolution-like operation on the state input inside the recurrence). The page gives
- * no formula; the reading implemented is the trapezoid rule on the step's input
- * integral:
- *     h_t = exp(dt_t A) h_{t-1} + (dt_t / 2) (exp(dt_t A) B_{t-1} x_{t-1} + B_t x_t),
- * y_t as in ssm_scan_fwd. x_prev [batch, d_inner] and B_prev [batch, d_state] (io
- * dtype) are the input before step 0: NULL and NULL for a sequence with no earlier
- * input; to resume a sequence pass the last step's x and B of the previous part (with
- * its h_final as h0). Given together or not at all (else SSM_ERR_NULL). Other arguments,
- * layouts, the chunking (with the same decay-horizon bound) and the workspace
- * (ssm_scan_fwd_workspace_ex) are those of ssm_scan_fwd_ex. y must not overlap x or
- * x_prev (SSM_ERR_UNSUPPORTED): a chunk's rescan reads the row before it. Alignment:
- * as ssm_scan_fwd_ex; x_prev one element, B_prev 4 bytes.
+ * Híbrido", section "Mamba-3: a linha de base de SSM puro em 2026", item 1: a more
+ * expressive recurrence, a convolution-like operation on the state input inside the
+ * recurrence; the key-terms rows "Exponential-trapezoidal discretization" of the zh and
+ * hi lessons "Phase 10 · 21 Jamba hybrid SSM-Transformer": it subsumes Mamba-2's Euler
+ * discretisation). No page gives a formula; the reading implemented is a two-point rule
+ * on the step's input integral, the current input weighted lam_t and the older one
+ * (decayed across the step) 1 - lam_t:
+ *     h_t = exp(dt_t A) h_{t-1} + dt_t ((1 - lam_t) exp(dt_t A) B_{t-1} x_{t-1} + lam_t B_t x_t),
+ * y_t as in ssm_scan_fwd. lam [batch, L, d_inner] (io dtype, laid out like dt) is the
+ * weight per step and channel: 1 is Euler's step (ssm_scan_fwd's recurrence), 1/2 the
+ * trapezoid rule; NULL = 1/2 everywhere. Any value is accepted; [0, 1] keeps both taps
+ * non-negative. x_prev [batch, d_inner] and B_prev [batch, d_state] (io dtype) are the
+ * input before step 0: NULL and NULL for a sequence with no earlier input; to resume a
+ * sequence pass the last step's x and B of the previous part (with its h_final as h0).
+ * Given together or not at all (else SSM_ERR_NULL). Other arguments, layouts, the
+ * chunking (with the same decay-horizon bound) and the workspace
+ * (ssm_scan_fwd_workspace_ex) are those of ssm_scan_fwd_ex. y must not overlap x, x_prev
+ * or lam (SSM_ERR_UNSUPPORTED): a chunk's rescan reads the row before it. Alignment: as
+ * ssm_scan_fwd_ex; x_prev and lam one element, B_prev 4 bytes.
  *
  * ssm_step_trap: one decode token of the same recurrence. x_prev [n_layers, n_seq,
  * d_inner] and B_prev [n_layers, n_seq, d_state] are the previous token's x_t and B_t
  * (NULL and NULL before the first token); the caller keeps them, the library keeps
- * only h. Otherwise as ssm_step; B_prev is aligned like B_t. ssm_step_trap_replay is
- * its one-thread-per-channel reference with the same fp32 operations in the same
- * order: per state n, with w = 0.5 dt_t and a = exp(dt_t A[n]),
- *     h[n] = fma(a, fma(w x_prev, B_prev[n], h[n]), (w x_t) B_t[n]),
+ * only h. lam_t [n_layers, n_seq, d_inner] is the token's weight (NULL = 1/2).
+ * Otherwise as ssm_step; B_prev is aligned like B_t, lam_t one element.
+ * ssm_step_trap_replay is its one-thread-per-channel reference with the same fp32
+ * operations in the same order: with lam = lam_t (or 1/2), wc = dt_t * lam,
+ * wp = dt_t * (1 - lam), up = wp * x_prev, uc = wc * x_t, and per state n with
+ * a = exp(dt_t A[n]),
+ *     h[n] = fma(a, fma(up, B_prev[n], h[n]), uc * B_t[n]),
  * then the output as in ssm_step; the two agree bit for bit. */
 ssm_status ssm_scan_fwd_trap(const void *x, const void *dt, const float *A, const void *B,
                              const void *C, const float *D, const void *z, const float *h0,
-                             const void *x_prev, const void *B_prev, void *y, float *h_final,
-                             int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                             ssm_dtype io, int64_t chunk_len, void *workspace,
+                             const void *x_prev, const void *B_prev, const void *lam, void *y,
+                             float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                             int32_t d_state, ssm_dtype io, int64_t chunk_len, void *workspace,
                              size_t workspace_bytes, void *hip_stream);
 ssm_status ssm_step_trap(float *h, const void *x_prev, const void *B_prev, const void *x_t,
-                         const void *dt_t, const float *A, const void *B_t, const void *C_t,
-                         const float *D, const void *z_t, void *y_t, int64_t n_layers,
-                         int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
-                         void *hip_stream);
+                         const void *dt_t, const void *lam_t, const float *A, const void *B_t,
+                         const void *C_t, const float *D, const void *z_t, void *y_t,
+                         int64_t n_layers, int64_t n_seq, int64_t d_inner, int32_t d_state,
+                         ssm_dtype io, void *hip_stream);
 ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev,
-                                const void *x_t, const void *dt_t, const float *A,
-                                const void *B_t, const void *C_t, const float *D,
+                                const void *x_t, const void *dt_t, const void *lam_t,
+                                const float *A, const void *B_t, const void *C_t, const float *D,
                                 const void *z_t, void *y_t, int64_t n_layers, int64_t n_seq,
                                 int64_t d_inner, int32_t d_state, ssm_dtype io,
                                 void *hip_stream);
@@ -473,10 +483,11 @@ ssm_status ssm_scan_fwd_fused_profiled(const void *x_in, const void *dt_raw, con
 ssm_status ssm_scan_fwd_trap_profiled(const void *x, const void *dt, const float *A,
                                       const void *B, const void *C, const float *D,
                                       const void *z, const float *h0, const void *x_prev,
-                                      const void *B_prev, void *y, float *h_final, int64_t batch,
-                                      int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
-                                      int64_t chunk_len, void *workspace, size_t workspace_bytes,
-                                      void *hip_stream, void *const *events, int32_t n_events);
+                                      const void *B_prev, const void *lam, void *y,
+                                      float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                                      int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream,
+                                      void *const *events, int32_t n_events);
 ssm_status ssm_scan_fwd_mimo_profiled(const void *x, const void *dt, const float *A,
                                       const void *B, const void *C, const float *D,
                                       const void *z, const float *h0, void *y, float *h_final,
@@ -488,7 +499,7 @@ ssm_status ssm_scan_fwd_mimo_profiled(const void *x, const void *dt, const float
 /* ------------------------------------------------------------------ misc */
 const char *ssm_status_str(ssm_status s);   /* static string, never NULL */
 const char *ssm_last_error(void);           /* this thread's last detail, "" if none */
-int32_t ssm_abi_version(void);              /* 1 */
+int32_t ssm_abi_version(void);              /* 2 */
 
 #ifdef __cplusplus
 }

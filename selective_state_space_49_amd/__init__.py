@@ -106,11 +106,11 @@ def load_library():
     sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     sig["ssm_scan_bwd_fused_workspace"] = ([i64, i64, i64, i32, i32, ci, i64], sz)
     sig["ssm_scan_bwd_fused"] = ([vp] * 10 + [i32] + [vp] * 16 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
-    trap = [vp] * 12 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
+    trap = [vp] * 13 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_trap"] = (trap, ci)
     sig["ssm_scan_fwd_trap_profiled"] = (trap + [vp, i32], ci)
     for name in ("ssm_step_trap", "ssm_step_trap_replay"):
-        sig[name] = ([vp] * 11 + [i64, i64, i64, i32, ci, vp], ci)
+        sig[name] = ([vp] * 12 + [i64, i64, i64, i32, ci, vp], ci)
     sig["ssm_scan_fwd_mimo_workspace"] = ([i64, i64, i64, i32, i32, i64], sz)
     mimo = [vp] * 10 + [i64, i64, i64, i32, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_mimo"] = (mimo, ci)
@@ -351,13 +351,14 @@ def ssm_step_c64_replay(h, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
 
 # ------------------------------------------------------------------ exponential-trapezoidal
 def ssm_scan_fwd_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=None, *,
-                      chunk_len=0, y=None, h_final=None, workspace=None, want_h_final=True,
-                      events=None):
+                      lam=None, chunk_len=0, y=None, h_final=None, workspace=None,
+                      want_h_final=True, events=None):
     """Prefill with the exponential-trapezoidal discretisation (see ssm_scan.h):
-    h_t = a_t h_{t-1} + (dt_t/2)(a_t B_{t-1} x_{t-1} + B_t x_t). x_prev [b, d_inner] and
-    B_prev [b, d_state] (io dtype, both or neither) are the input before step 0.
-    events: None, or 4 raw hipEvent_t handles for the profiled entry point.
-    Returns (y, h_final)."""
+    h_t = a_t h_{t-1} + dt_t((1 - lam_t) a_t B_{t-1} x_{t-1} + lam_t B_t x_t). lam
+    [b, L, d_inner] (io dtype) weighs each step's current input (None: 1/2, the
+    trapezoid rule; 1 is Euler's step). x_prev [b, d_inner] and B_prev [b, d_state]
+    (io dtype, both or neither) are the input before step 0. events: None, or 4 raw
+    hipEvent_t handles for the profiled entry point. Returns (y, h_final)."""
     lib = load_library()
     b, L, Dn = x.shape
     N = A.shape[1]
@@ -365,8 +366,8 @@ def ssm_scan_fwd_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=No
     _dev(x, "x"); _dev(dt, "dt", (b, L, Dn)); _dev(z, "z", (b, L, Dn))
     _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
     _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N)); _dev(h0, "h0", (b, Dn, N), f32)
-    _dev(x_prev, "x_prev", (b, Dn)); _dev(B_prev, "B_prev", (b, N))
-    io = _io(x, dt, z, B, C, x_prev, B_prev)
+    _dev(x_prev, "x_prev", (b, Dn)); _dev(B_prev, "B_prev", (b, N)); _dev(lam, "lam", (b, L, Dn))
+    io = _io(x, dt, z, B, C, x_prev, B_prev, lam)
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y", (b, L, Dn), x.dtype)
@@ -378,8 +379,8 @@ def ssm_scan_fwd_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=No
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev),
-            _ptr(B_prev), _ptr(y), _ptr(h_final), b, L, Dn, N, io, chunk_len, _ptr(workspace),
-            ws_bytes, _stream(x)]
+            _ptr(B_prev), _ptr(lam), _ptr(y), _ptr(h_final), b, L, Dn, N, io, chunk_len,
+            _ptr(workspace), ws_bytes, _stream(x)]
     if events is not None:
         if len(events) != 4:
             raise ValueError("need exactly 4 event handles")
@@ -391,7 +392,7 @@ def ssm_scan_fwd_trap(x, dt, A, B, C, D, z=None, h0=None, x_prev=None, B_prev=No
     return y, h_final
 
 
-def _step_trap(fn_name, h, x_prev, B_prev, x, dt, A, B, C, D, z, y):
+def _step_trap(fn_name, h, x_prev, B_prev, x, dt, A, B, C, D, z, y, lam):
     lib = load_library()
     Ln, S, Dn = x.shape
     N = A.shape[2]
@@ -401,27 +402,32 @@ def _step_trap(fn_name, h, x_prev, B_prev, x, dt, A, B, C, D, z, y):
     _dev(A, "A", (Ln, Dn, N), f32); _dev(D, "D", (Ln, Dn), f32)
     _dev(B, "B_t", (Ln, S, N)); _dev(C, "C_t", (Ln, S, N))
     _dev(x_prev, "x_prev", (Ln, S, Dn)); _dev(B_prev, "B_prev", (Ln, S, N))
-    io = _io(x, dt, z, B, C, x_prev, B_prev)
+    _dev(lam, "lam_t", (Ln, S, Dn))
+    io = _io(x, dt, z, B, C, x_prev, B_prev, lam)
     if y is None:
         y = torch.empty_like(x)
     _dev(y, "y_t", (Ln, S, Dn), x.dtype)
-    st = getattr(lib, fn_name)(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x), _ptr(dt), _ptr(A),
-                               _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), Ln, S, Dn, N, io,
-                               _stream(x))
+    st = getattr(lib, fn_name)(_ptr(h), _ptr(x_prev), _ptr(B_prev), _ptr(x), _ptr(dt), _ptr(lam),
+                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), Ln, S, Dn, N,
+                               io, _stream(x))
     _check(st)
     return y
 
 
-def ssm_step_trap(h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
+def ssm_step_trap(h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, lam_t=None,
+                  y_t=None):
     """One exponential-trapezoidal decode token: h updated in place, returns y_t.
-    x_prev and B_prev are the previous token's x_t and B_t (None and None at the start)."""
-    return _step_trap("ssm_step_trap", h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t, y_t)
+    x_prev and B_prev are the previous token's x_t and B_t (None and None at the start);
+    lam_t [n_layers, n_seq, d_inner] the token's weight (None: 1/2)."""
+    return _step_trap("ssm_step_trap", h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t, y_t,
+                      lam_t)
 
 
-def ssm_step_trap_replay(h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, y_t=None):
+def ssm_step_trap_replay(h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t=None, *, lam_t=None,
+                         y_t=None):
     """Reference-order replay of ssm_step_trap, one thread per channel."""
     return _step_trap("ssm_step_trap_replay", h, x_prev, B_prev, x_t, dt_t, A, B_t, C_t, D, z_t,
-                      y_t)
+                      y_t, lam_t)
 
 
 # ------------------------------------------------------------------ fused input stage

@@ -46,12 +46,13 @@ constexpr int64_t kTargetWaves = 4 * kSimds;
 
 // Waves per SIMD each rescan is compiled for (its __launch_bounds__ minimum, or what
 // its registers allow).
-enum class Family { Plain, Fused, Complex, Mimo, Backward };
+enum class Family { Plain, Fused, Complex, Mimo, Backward, TrapWeighted };
 int32_t waves_per_simd(Family f, int32_t rank = 1) {
     switch (f) {
         case Family::Plain: return 5;     // plain and exponential-trapezoidal rescans
         case Family::Mimo: return rank <= 4 ? 5 : 4;
-        default: return 4;                // input stage, complex state, backward
+        default: return 4;                // input stage, complex state, backward, and the
+                                          // exponential-trapezoidal rescan with a weight stream
     }
 }
 constexpr int64_t kMinChunk = 64;       // shortest chunk the planner picks
@@ -119,9 +120,10 @@ struct InputStage {
 };
 
 // The exponential-trapezoidal entry points: the input before the first step (prefill:
-// [batch][Dn] and [batch][N]; decode: the previous token's x and B). Both or neither.
+// [batch][Dn] and [batch][N]; decode: the previous token's x and B; both or neither),
+// and the weight of each step's current input (laid out like dt; null: 1/2).
 struct Trap {
-    const void *x_prev, *B_prev;
+    const void *x_prev, *B_prev, *lam;
 };
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -150,7 +152,8 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     const bool mimo = rank != 0;
     if (mimo && !valid_rank(rank)) return fail(SSM_ERR_UNSUPPORTED, "rank %d not in {1,2,4,8}", rank);
     Plan plan;
-    const Family fam = cplx ? Family::Complex : in ? Family::Fused : mimo ? Family::Mimo : Family::Plain;
+    const Family fam = cplx ? Family::Complex : in ? Family::Fused : mimo ? Family::Mimo
+                     : (trap && trap->lam) ? Family::TrapWeighted : Family::Plain;
     ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan, mimo ? rank : 1,
                               waves_per_simd(fam, rank));
     if (st != SSM_OK) return st;
@@ -193,13 +196,14 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     if (trap) {
         if ((trap->x_prev == nullptr) != (trap->B_prev == nullptr))
             return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
-        if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, 4))
-            return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev element, B_prev 4 B)");
+        if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, 4) || !aligned(trap->lam, eb))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev, lam element, B_prev 4 B)");
         // The rescan of chunk c reads the last row of chunk c-1 while y is written.
         const size_t stream_bytes = (size_t)(batch * L * d_inner) * eb;
         if (overlaps(y, stream_bytes, x, stream_bytes) ||
-            overlaps(y, stream_bytes, trap->x_prev, (size_t)(batch * d_inner) * eb))
-            return fail(SSM_ERR_UNSUPPORTED, "y must not overlap x or x_prev in the trapezoidal scan");
+            overlaps(y, stream_bytes, trap->x_prev, (size_t)(batch * d_inner) * eb) ||
+            overlaps(y, stream_bytes, trap->lam, stream_bytes))
+            return fail(SSM_ERR_UNSUPPORTED, "y must not overlap x, x_prev or lam in the trapezoidal scan");
     }
     hipStream_t s = (hipStream_t)hip_stream;
     const int64_t state_floats = batch * d_inner * d_state * (cplx ? 2 : 1);
@@ -255,6 +259,7 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     } else if (trap) {
         a.x_prev = trap->x_prev;
         a.B_prev = trap->B_prev;
+        a.lam = trap->lam;
         e = ssm::launch_scan_trap(a, iot, d_state, z != nullptr, s, ev);
     } else if (mimo) {
         e = ssm::launch_scan_mimo(a, iot, d_state, z != nullptr, s, ev);
@@ -296,8 +301,8 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     if (trap) {
         if ((trap->x_prev == nullptr) != (trap->B_prev == nullptr))
             return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
-        if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, bc))
-            return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev element; B_prev as B_t)");
+        if (!aligned(trap->x_prev, eb) || !aligned(trap->B_prev, bc) || !aligned(trap->lam, eb))
+            return fail(SSM_ERR_ALIGN, "pointer alignment (x_prev, lam_t element; B_prev as B_t)");
     }
     if (mimo) {
         const size_t va = std::min<size_t>(16, (size_t)rank * eb);
@@ -324,6 +329,7 @@ ssm_status step_common(float *h, const void *x, const void *dt, const float *A, 
     } else if (trap) {
         a.x_prev = trap->x_prev;
         a.B_prev = trap->B_prev;
+        a.lam = trap->lam;
         e = ssm::launch_step_trap(a, iot, d_state, z != nullptr, replay, s);
     } else if (mimo) {
         a.rank = rank;
@@ -642,11 +648,11 @@ ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, co
 
 ssm_status ssm_scan_fwd_trap(const void *x, const void *dt, const float *A, const void *B,
                              const void *C, const float *D, const void *z, const float *h0,
-                             const void *x_prev, const void *B_prev, void *y, float *h_final,
-                             int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                             ssm_dtype io, int64_t chunk_len, void *workspace,
+                             const void *x_prev, const void *B_prev, const void *lam, void *y,
+                             float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                             int32_t d_state, ssm_dtype io, int64_t chunk_len, void *workspace,
                              size_t workspace_bytes, void *hip_stream) {
-    const Trap tr{x_prev, B_prev};
+    const Trap tr{x_prev, B_prev, lam};
     return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
                        chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0,
                        nullptr, &tr);
@@ -655,34 +661,35 @@ ssm_status ssm_scan_fwd_trap(const void *x, const void *dt, const float *A, cons
 ssm_status ssm_scan_fwd_trap_profiled(const void *x, const void *dt, const float *A,
                                       const void *B, const void *C, const float *D,
                                       const void *z, const float *h0, const void *x_prev,
-                                      const void *B_prev, void *y, float *h_final, int64_t batch,
-                                      int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
-                                      int64_t chunk_len, void *workspace, size_t workspace_bytes,
-                                      void *hip_stream, void *const *events, int32_t n_events) {
+                                      const void *B_prev, const void *lam, void *y,
+                                      float *h_final, int64_t batch, int64_t L, int64_t d_inner,
+                                      int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream,
+                                      void *const *events, int32_t n_events) {
     if (!events) return fail(SSM_ERR_NULL, "events are required");
-    const Trap tr{x_prev, B_prev};
+    const Trap tr{x_prev, B_prev, lam};
     return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
                        chunk_len, workspace, workspace_bytes, hip_stream, false, events, n_events,
                        nullptr, &tr);
 }
 
 ssm_status ssm_step_trap(float *h, const void *x_prev, const void *B_prev, const void *x_t,
-                         const void *dt_t, const float *A, const void *B_t, const void *C_t,
-                         const float *D, const void *z_t, void *y_t, int64_t n_layers,
-                         int64_t n_seq, int64_t d_inner, int32_t d_state, ssm_dtype io,
-                         void *hip_stream) {
-    const Trap tr{x_prev, B_prev};
+                         const void *dt_t, const void *lam_t, const float *A, const void *B_t,
+                         const void *C_t, const float *D, const void *z_t, void *y_t,
+                         int64_t n_layers, int64_t n_seq, int64_t d_inner, int32_t d_state,
+                         ssm_dtype io, void *hip_stream) {
+    const Trap tr{x_prev, B_prev, lam_t};
     return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
                        io, hip_stream, false, false, nullptr, &tr);
 }
 
 ssm_status ssm_step_trap_replay(float *h, const void *x_prev, const void *B_prev,
-                                const void *x_t, const void *dt_t, const float *A,
-                                const void *B_t, const void *C_t, const float *D,
+                                const void *x_t, const void *dt_t, const void *lam_t,
+                                const float *A, const void *B_t, const void *C_t, const float *D,
                                 const void *z_t, void *y_t, int64_t n_layers, int64_t n_seq,
                                 int64_t d_inner, int32_t d_state, ssm_dtype io,
                                 void *hip_stream) {
-    const Trap tr{x_prev, B_prev};
+    const Trap tr{x_prev, B_prev, lam_t};
     return step_common(h, x_t, dt_t, A, B_t, C_t, D, z_t, y_t, n_layers, n_seq, d_inner, d_state,
                        io, hip_stream, false, true, nullptr, &tr);
 }
@@ -871,6 +878,6 @@ const char *ssm_status_str(ssm_status s) {
 
 const char *ssm_last_error(void) { return g_err; }
 
-int32_t ssm_abi_version(void) { return 1; }
+int32_t ssm_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -55,6 +55,7 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
 // The kernels read x and dt as given.
 struct NoInput {
     static constexpr bool kTrap = false;
+    static constexpr bool kW = false;  // no weight stream
     static constexpr int kWavesPerSimd = 5;
     static constexpr bool kRawPrefetch = true;  // see StepIn (ssm_stream.h)
     __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
@@ -69,6 +70,7 @@ struct NoInput {
 template <typename IO, int KC>
 struct MambaInput {
     static constexpr bool kTrap = false;
+    static constexpr bool kW = false;
     static constexpr int kWavesPerSimd = 4;
     static constexpr bool kRawPrefetch = false;
     ConvSilu<(KC > 0 ? KC : 1)> conv;
@@ -117,20 +119,31 @@ struct MambaInput {
 
 // The exponential-trapezoidal discretisation (the Mamba-3 item of "Jamba —
 // SSM-Transformer Híbrido", section "Mamba-3: a linha de base de SSM puro em 2026",
-// which names the rule but gives no formula): the step's input integral is taken by
-// the trapezoid rule over its two ends,
-//     h_t = a_t h_{t-1} + (dt_t / 2) (a_t B_{t-1} x_{t-1} + B_t x_t),
-// evaluated as a_t (h_{t-1} + (dt_t/2) x_{t-1} B_{t-1}) + (dt_t/2) x_t B_t. The
-// recurrence stays linear in h with a known input term, so chunk summaries, the carry
-// and the rescan are unchanged apart from that term; each walk starts with the input
-// before its first row (the row before, or x_prev / B_prev before step 0). x and dt are
-// read as given.
-template <typename IO>
+// which names the rule, and the key-terms rows of the zh and hi lessons, which say it
+// subsumes Euler's; no page gives a formula): the step's input integral is taken by a
+// two-point rule over its ends, the current input weighted lam_t, the older one (decayed
+// across the step) 1 - lam_t,
+//     h_t = a_t h_{t-1} + dt_t ((1 - lam_t) a_t B_{t-1} x_{t-1} + lam_t B_t x_t),
+// evaluated as a_t (h_{t-1} + wp x_{t-1} B_{t-1}) + wc x_t B_t with wc = dt_t lam_t and
+// wp = dt_t (1 - lam_t). lam = 1 is Euler's step, lam = 1/2 (LAM = false: no weight
+// stream) the trapezoid rule. The recurrence stays linear in h with a known input term,
+// so chunk summaries, the carry and the rescan are unchanged apart from that term; each
+// walk starts with the input before its first row (the row before, or x_prev / B_prev
+// before step 0). x and dt are read as given; lam is a fourth stream laid out like dt.
+template <typename IO, bool LAM>
 struct TrapInput {
     static constexpr bool kTrap = true;
-    static constexpr int kWavesPerSimd = 5;
+    static constexpr bool kW = LAM;
+    // The weight stream's prefetch buffers spill registers at five waves per SIMD.
+    static constexpr int kWavesPerSimd = LAM ? 4 : 5;
     static constexpr bool kRawPrefetch = false;
     float xprev;  // x of the step before the current one
+    // The weights of the older and the current input for a step of length dv.
+    __device__ __forceinline__ static void weights(float dv, float lr, float &wp, float &wc) {
+        const float lv = LAM ? lr : 0.5f;
+        wc = dv * lv;
+        wp = dv * (1.0f - lv);
+    }
     __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
     __device__ __forceinline__ void history(const ScanArgs &a, int64_t b, int64_t d, int64_t t) {
         if (t > 0) xprev = Io<IO>::ld((const IO *)a.x + (b * a.L + t - 1) * a.Dn + d);
@@ -254,17 +267,19 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
     // 2. end state from zero over rows [ts, T) of the chunk
     const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
     const int64_t rw = row0 + (int64_t)ts * a.Dn;
-    const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw);
+    const RowStream<IO> xs((const IO *)a.x + rw), dws((const IO *)a.dt + rw),
+        lws(In::kW ? (const IO *)a.lam + rw : (const IO *)a.x + rw);
     double S = 0.0;  // sum of dt, needed only when the window is the whole chunk
     float bp[N];     // trapezoidal rule: B of the step before, carried from step to step
     if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0 + ts, bp);
-    stream_steps<IO, false, 4, In::kRawPrefetch>(xs, dws, dws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float) {
+    stream_steps_w<IO, false, 4, In::kRawPrefetch, In::kW>(xs, dws, dws, lws, voff, rb, T - ts, kSummaryPrioScale, [&](uint32_t i, float xr, float dr, float, float lr) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + ts + i;
         S += (double)dv;
         if constexpr (In::kTrap) {
-            const float w = 0.5f * dv;
-            const float up = w * in.xprev, uc = w * xv;
+            float wp, wc;
+            In::weights(dv, lr, wp, wc);
+            const float up = wp * in.xprev, uc = wc * xv;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float bn = Bp.ld(t * N + n);
@@ -316,7 +331,8 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
-        zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0);
+        zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0),
+        lws(In::kW ? (const IO *)a.lam + row0 : (const IO *)a.x + row0);
     const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
     const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     In in;
@@ -324,13 +340,14 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     in.history(a, ln.b, ln.d, t0);
     float bp[N];  // trapezoidal rule: B of the step before, carried from step to step
     if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0, bp);
-    stream_steps<IO, GATED, 4, In::kRawPrefetch>(xs, dts, zs, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv) {
+    stream_steps_w<IO, GATED, 4, In::kRawPrefetch, In::kW>(xs, dts, zs, lws, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv, float lr) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
         float acc = 0.0f;
         if constexpr (In::kTrap) {
-            const float w = 0.5f * dv;
-            const float up = w * in.xprev, uc = w * xv;
+            float wp, wc;
+            In::weights(dv, lr, wp, wc);
+            const float up = wp * in.xprev, uc = wc * xv;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float bn = Bp.ld(t * N + n);
@@ -434,8 +451,11 @@ hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, 
 
 hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev) {
-    return io == 0 ? launch_io<float, TrapInput<float>>(a, d_state, gated, s, ev)
-                   : launch_io<bf16_bits, TrapInput<bf16_bits>>(a, d_state, gated, s, ev);
+    if (a.lam)
+        return io == 0 ? launch_io<float, TrapInput<float, true>>(a, d_state, gated, s, ev)
+                       : launch_io<bf16_bits, TrapInput<bf16_bits, true>>(a, d_state, gated, s, ev);
+    return io == 0 ? launch_io<float, TrapInput<float, false>>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits, TrapInput<bf16_bits, false>>(a, d_state, gated, s, ev);
 }
 
 hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,

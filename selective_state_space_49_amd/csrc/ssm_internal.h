@@ -32,6 +32,8 @@ struct ScanArgs {
     // Exponential-trapezoidal entry point only: the input before step 0.
     const void *x_prev;       // [batch][Dn] of io, or null (then B_prev is null too)
     const void *B_prev;       // [batch][N] of io, or null
+    const void *lam;          // [batch][L][Dn] of io: weight of each step's current input,
+                              // or null (1/2)
     // MIMO entry point only: inputs and outputs per channel (x, z, y are [batch][L][Dn][rank],
     // B and C [batch][L][N][rank]); 1 elsewhere.
     int32_t rank;
@@ -52,6 +54,7 @@ struct StepArgs {
     // Exponential-trapezoidal entry point only: the previous token's x and B.
     const void *x_prev;   // [n_layers][n_seq][Dn] of io, or null (then B_prev is null too)
     const void *B_prev;   // [n_layers][n_seq][N] of io, or null
+    const void *lam;      // [n_layers][n_seq][Dn] of io: the token's weight, or null (1/2)
     // MIMO entry point only: rank (x, z, y are [n_layers][n_seq][Dn][rank], B and C
     // [n_layers][n_seq][N][rank]); 1 elsewhere.
     int32_t rank;
@@ -63,7 +66,7 @@ struct StepArgs {
 // consecutive records).
 hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev);
-// The same with the exponential-trapezoidal discretisation (x_prev, B_prev of a).
+// The same with the exponential-trapezoidal discretisation (x_prev, B_prev, lam of a).
 hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev);
 // The same with MIMO projections of rank a.rank (1, 2, 4 or 8).
@@ -95,7 +98,7 @@ hipError_t launch_step_fused(const StepArgs &a, int io, int d_state, bool gated,
                              hipStream_t s);
 // MIMO decode of rank a.rank (1, 2, 4 or 8).
 hipError_t launch_step_mimo(const StepArgs &a, int io, int d_state, bool gated, hipStream_t s);
-// Exponential-trapezoidal decode (x_prev, B_prev of a).
+// Exponential-trapezoidal decode (x_prev, B_prev, lam of a).
 hipError_t launch_step_trap(const StepArgs &a, int io, int d_state, bool gated, bool replay,
                             hipStream_t s);
 

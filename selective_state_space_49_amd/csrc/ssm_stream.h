@@ -68,11 +68,13 @@ template <> struct RowStream<float> {
 // keeps each raw value live until its step, though, and the kernels with the most
 // registers in use (the exponential-trapezoidal and input-stage rescans) then spill
 // (6.9 -> 19.7 ms): they widen at load time (RAW = false).
-template <int KU, bool RAW>
+// W: a fourth stream (the exponential-trapezoidal weight) is streamed alongside.
+template <int KU, bool RAW, bool W = false>
 struct StepIn {
     // raw bits (RAW), else the widened values
     typedef typename std::conditional<RAW, uint32_t, float>::type T;
     T x[KU], dt[KU], z[KU];
+    T w[W ? KU : 1];
 };
 
 // Issue priority by remaining work. The SIMD arbiter favours the oldest of the waves
@@ -91,20 +93,23 @@ __device__ __forceinline__ void set_priority(uint32_t remaining, uint32_t scale)
     else __builtin_amdgcn_s_setprio(0);
 }
 
-template <typename IO, bool GATED, int KU, bool RAW>
-__device__ __forceinline__ void load_block(StepIn<KU, RAW> &s, const RowStream<IO> &x,
+template <typename IO, bool GATED, int KU, bool RAW, bool W>
+__device__ __forceinline__ void load_block(StepIn<KU, RAW, W> &s, const RowStream<IO> &x,
                                            const RowStream<IO> &dt, const RowStream<IO> &z,
-                                           uint32_t voff, uint32_t row, uint32_t rb) {
+                                           const RowStream<IO> &w, uint32_t voff, uint32_t row,
+                                           uint32_t rb) {
 #pragma unroll
     for (int k = 0; k < KU; ++k) {
         if constexpr (RAW) {
             s.x[k] = x.ldraw(voff, (row + k) * rb);
             s.dt[k] = dt.ldraw(voff, (row + k) * rb);
             if (GATED) s.z[k] = z.ldraw(voff, (row + k) * rb);
+            if constexpr (W) s.w[k] = w.ldraw(voff, (row + k) * rb);
         } else {
             s.x[k] = x.ld(voff, (row + k) * rb);
             s.dt[k] = dt.ld(voff, (row + k) * rb);
             if (GATED) s.z[k] = z.ld(voff, (row + k) * rb);
+            if constexpr (W) s.w[k] = w.ld(voff, (row + k) * rb);
         }
     }
 }
@@ -115,36 +120,39 @@ __device__ __forceinline__ float use_value(T v) {
     else return v;
 }
 
-// Calls body(i, x_i, dt_i, z_i) for i = 0 .. steps-1 (rows of the streams); voff is
-// the lane's byte offset in a row and rb the bytes per row. prio_scale: see
-// set_priority (0 = leave the priority alone).
-template <typename IO, bool GATED, int KU, bool RAW = true, typename Body>
-__device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowStream<IO> &dt,
-                                             const RowStream<IO> &z, uint32_t voff, uint32_t rb,
-                                             uint32_t steps, uint32_t prio_scale, Body &&body) {
+// Calls body(i, x_i, dt_i, z_i, w_i) for i = 0 .. steps-1 (rows of the streams; w_i is
+// 0 unless W); voff is the lane's byte offset in a row and rb the bytes per row.
+// prio_scale: see set_priority (0 = leave the priority alone).
+template <typename IO, bool GATED, int KU, bool RAW, bool W, typename Body>
+__device__ __forceinline__ void stream_steps_w(const RowStream<IO> &x, const RowStream<IO> &dt,
+                                               const RowStream<IO> &z, const RowStream<IO> &w,
+                                               uint32_t voff, uint32_t rb, uint32_t steps,
+                                               uint32_t prio_scale, Body &&body) {
     const uint32_t full = steps / KU;
     uint32_t i = 0;
-    StepIn<KU, RAW> bufA, bufB;
-    if (full > 0) load_block<IO, GATED, KU, RAW>(bufA, x, dt, z, voff, 0, rb);
+    StepIn<KU, RAW, W> bufA, bufB;
+    if (full > 0) load_block<IO, GATED, KU, RAW, W>(bufA, x, dt, z, w, voff, 0, rb);
     for (uint32_t k = 0; k < full; k += 2) {
         if (prio_scale) set_priority(steps - i, prio_scale);
         // block k is in bufA: fetch block k+1 into bufB, then compute block k
-        if (k + 1 < full) load_block<IO, GATED, KU, RAW>(bufB, x, dt, z, voff, i + KU, rb);
+        if (k + 1 < full) load_block<IO, GATED, KU, RAW, W>(bufB, x, dt, z, w, voff, i + KU, rb);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
             body(i + j, use_value<IO, RAW>(bufA.x[j]), use_value<IO, RAW>(bufA.dt[j]),
-                 GATED ? use_value<IO, RAW>(bufA.z[j]) : 0.0f);
+                 GATED ? use_value<IO, RAW>(bufA.z[j]) : 0.0f,
+                 W ? use_value<IO, RAW>(bufA.w[W ? j : 0]) : 0.0f);
         }
         i += KU;
         if (k + 1 >= full) break;
         // block k+1 is in bufB: fetch block k+2 into bufA, then compute block k+1
-        if (k + 2 < full) load_block<IO, GATED, KU, RAW>(bufA, x, dt, z, voff, i + KU, rb);
+        if (k + 2 < full) load_block<IO, GATED, KU, RAW, W>(bufA, x, dt, z, w, voff, i + KU, rb);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             __builtin_amdgcn_sched_barrier(0);
             body(i + j, use_value<IO, RAW>(bufB.x[j]), use_value<IO, RAW>(bufB.dt[j]),
-                 GATED ? use_value<IO, RAW>(bufB.z[j]) : 0.0f);
+                 GATED ? use_value<IO, RAW>(bufB.z[j]) : 0.0f,
+                 W ? use_value<IO, RAW>(bufB.w[W ? j : 0]) : 0.0f);
         }
         i += KU;
     }
@@ -152,8 +160,19 @@ __device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowSt
     for (; i < steps; ++i) {  // ragged tail, one step at a time
         const float xv = x.ld(voff, i * rb), dv = dt.ld(voff, i * rb);
         const float zv = GATED ? z.ld(voff, i * rb) : 0.0f;
-        body(i, xv, dv, zv);
+        const float wv = W ? w.ld(voff, i * rb) : 0.0f;
+        body(i, xv, dv, zv, wv);
     }
+}
+
+// The same over x, dt (and z) only: body(i, x_i, dt_i, z_i).
+template <typename IO, bool GATED, int KU, bool RAW = true, typename Body>
+__device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowStream<IO> &dt,
+                                             const RowStream<IO> &z, uint32_t voff, uint32_t rb,
+                                             uint32_t steps, uint32_t prio_scale, Body &&body) {
+    stream_steps_w<IO, GATED, KU, RAW, false>(
+        x, dt, z, z, voff, rb, steps, prio_scale,
+        [&](uint32_t i, float xv, float dv, float zv, float) { body(i, xv, dv, zv); });
 }
 
 // ---------------------------------------------------------------- decay horizon

@@ -95,16 +95,24 @@ struct StepMamba {
 
 // The exponential-trapezoidal step (see scan_real.hip): x and dt as given, plus the
 // previous token's x (x_prev, per channel) and B (B_prev, per sequence); null x_prev
-// and B_prev (the entry point accepts both or neither) mean no previous input. The
-// update of state n is
-//     h = a (h + w x_prev B_prev[n]) + w x B[n],   w = dt / 2, a = exp(dt A[n]).
+// and B_prev (the entry point accepts both or neither) mean no previous input; lam is
+// the token's weight per channel (null: 1/2). The update of state n is
+//     h = a (h + up B_prev[n]) + uc B[n],   a = exp(dt A[n]),
+//     up = (dt (1 - lam)) x_prev,   uc = (dt lam) x.
 template <typename IO>
 struct StepTrap {
     static constexpr bool kTrap = true;
-    float xprev;
+    float xprev, lam;
     template <typename Chan>
     __device__ __forceinline__ void apply(const StepArgs &a, const Chan &c, float &, float &) {
         xprev = a.x_prev ? Io<IO>::ld((const IO *)a.x_prev + c.ch) : 0.0f;
+        lam = a.lam ? Io<IO>::ld((const IO *)a.lam + c.ch) : 0.5f;
+    }
+    // The two input weights times their inputs, in the order both decode kernels use.
+    __device__ __forceinline__ void taps(float dv, float xv, float &up, float &uc) const {
+        const float wc = dv * lam, wp = dv * (1.0f - lam);
+        up = wp * xprev;
+        uc = wc * xv;
     }
     __device__ __forceinline__ void store(const StepArgs &) const {}
 };
@@ -237,18 +245,18 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
     const float Dd = a.D[hc.l * a.Dn + hc.d];
     In in;
     in.apply(a, hc, xv, dv);
+    float uph = 0.0f, uch = 0.0f;  // exponential-trapezoidal step: the home channel's taps
+    if constexpr (In::kTrap) in.taps(dv, xv, uph, uch);
 
     float acc = 0.0f;
 #pragma unroll
     for (int r = 0; r < G; ++r) {
         const int src = r * CPR + lane / G;
-        const float xr = G == 1 ? xv : __shfl(xv, src, 64);
         const float dr = G == 1 ? dv : __shfl(dv, src, 64);
         float p = 0.0f;
         if constexpr (In::kTrap) {
-            const float xpr = G == 1 ? in.xprev : __shfl(in.xprev, src, 64);
-            const float w = 0.5f * dr;
-            const float up = w * xpr, uc = w * xr;
+            const float up = G == 1 ? uph : __shfl(uph, src, 64);
+            const float uc = G == 1 ? uch : __shfl(uch, src, 64);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const float a2 = av[r][k] * kLog2e;
@@ -256,6 +264,7 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
                 p = __builtin_fmaf(cv[k], hv[r][k], p);
             }
         } else {
+            const float xr = G == 1 ? xv : __shfl(xv, src, 64);
             const float u = dr * xr;
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -308,8 +317,8 @@ __global__ __launch_bounds__(256) void k_step_replay(StepArgs a) {
     float p[G];
     if constexpr (In::kTrap) {
         const IO *Pp = a.B_prev ? (const IO *)a.B_prev + c.lq * N : nullptr;
-        const float w = 0.5f * dv;
-        const float up = w * in.xprev, uc = w * xv;
+        float up, uc;
+        in.taps(dv, xv, up, uc);
         for (int g = 0; g < G; ++g) {
             p[g] = 0.0f;
             for (int k = 0; k < K; ++k) {

@@ -6,6 +6,7 @@ tol = 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 state). The same
 criterion is applied to the final state.
 """
 import sys
+import threading
 
 import numpy as np
 import torch
@@ -45,3 +46,20 @@ def bitwise_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
 def gather_channels(t, idx, axis=2):
     """Channels idx (a CPU index tensor) of a device tensor, copied to the host."""
     return None if t is None else t.index_select(axis, idx.to(t.device)).cpu()
+
+
+def threaded_channels(fn, n_channels, threads=16):
+    """fn(sl) -> (y [.., .., k], h [.., k, ..]) on the channel slice sl of a sample,
+    run from several threads (the oracle releases the GIL; channels are independent)
+    and joined along the channel axes: y's axis 2 (or its last axis for rank > 1
+    outputs, with channels at axis 2) and h's axis 1."""
+    parts = [p for p in np.array_split(np.arange(n_channels), max(1, threads)) if len(p)]
+    res = [None] * len(parts)
+
+    def work(i, p):
+        res[i] = fn(slice(int(p[0]), int(p[-1]) + 1))
+
+    ts = [threading.Thread(target=work, args=(i, p)) for i, p in enumerate(parts)]
+    for t in ts: t.start()
+    for t in ts: t.join()
+    return (np.concatenate([r[0] for r in res], axis=2), np.concatenate([r[1] for r in res], axis=1))

@@ -43,7 +43,7 @@ __all__ = [
     "ScanShape", "DecodeShape", "WORKLOADS", "SCAN_WORKLOADS", "io_torch_dtype",
     "make_scan_inputs", "make_decode_params", "make_decode_step", "make_h0",
     "sample_channels", "SLAB_ELEMS", "make_input_stage", "make_decode_input_stage",
-    "make_decode_dt_raw", "make_mimo_inputs", "make_mimo_decode_step",
+    "make_decode_dt_raw", "make_mimo_inputs", "make_mimo_decode_step", "make_trap_weight",
 ]
 
 # Elements drawn per randn call for big tensors (fixed: part of the seeded recipe).
@@ -187,6 +187,29 @@ def make_prev_input(batch: int, d_inner: int, d_state: int, io: str = "f32", dev
     dt = torch.float32 if io == "f32" else torch.bfloat16
     return {"x_prev": _normal((batch, d_inner), 0.0, 1.0, g, device, dt),
             "B_prev": _normal((batch, d_state), 0.0, 1.0, g, device, dt)}
+
+
+def make_trap_weight(shape, io: str = "f32", device="cpu", kind: str = "random",
+                     seed: int = 37) -> torch.Tensor:
+    """The weight of each step's current input in the exponential-trapezoidal rule, laid
+    out like dt (shape = (batch, L, d_inner), or (n_layers, n_seq, d_inner) for a decode
+    token), in the I/O dtype: kind "random" ~ U(0, 1) per element (drawn in float32 slab
+    by slab), "half" = 1/2 (the trapezoid rule), "one" = 1 (Euler's step)."""
+    shape = tuple(int(v) for v in shape)
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    if kind == "half":
+        return torch.full(shape, 0.5, dtype=dt, device=device)
+    if kind == "one":
+        return torch.ones(shape, dtype=dt, device=device)
+    if kind != "random":
+        raise ValueError(f"unknown weight kind {kind!r}")
+    g = _gen(seed, device)
+    n = math.prod(shape)
+    out = torch.empty(n, dtype=dt, device=device)
+    for s0 in range(0, n, SLAB_ELEMS):
+        s1 = min(n, s0 + SLAB_ELEMS)
+        out[s0:s1] = torch.rand(s1 - s0, generator=g, device=device, dtype=torch.float32).to(dt)
+    return out.view(shape)
 
 
 def make_h0(batch: int, d_inner: int, d_state: int, complex_state=False, device="cpu",
