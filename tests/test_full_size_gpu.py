@@ -1,9 +1,13 @@
 """The four large workloads at full size, in the launch configuration the benchmark
-times (the library's own chunk plan), checked on sampled channels.
+times (the library's own chunk plan).
 
-Channels are independent, so the oracle run on a subset of channels over the full
-sequence is exact for those channels. Inputs are drawn on the GPU with a seeded
-generator; the sampled channels are copied to the host for the oracle.
+The Jamba-shaped layer and the complex workload are checked on every channel, the 256k
+prefill on 1024 sampled channels that reach every 64-lane wave, the decode on 4096
+sampled (layer, sequence, channel) triples against the oracle and bit for bit against
+its replay kernel over the whole state at every one of its 512 steps. Channels are
+independent, so the oracle run on a subset of channels over the full sequence is exact
+for those channels. Inputs are drawn on the GPU with a seeded generator; the compared
+channels are copied to the host for the oracle.
 """
 import numpy as np
 import pytest
@@ -18,9 +22,13 @@ from workloads import (WORKLOADS, make_decode_params, make_decode_step, make_sca
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,k", [("jamba_layer_prefill", 256), ("long_context_256k", 24),
-                                    ("complex_rotation", 48)])
-def test_full_size_prefill_sampled(name, k):
+# Every channel of the Jamba-shaped layer (batch 2, L 4096, 8192 channels) and of the
+# complex workload (batch 4, L 8192, 4096 channels); 1024 of the 256k prefill's 8192
+# channels (every 64-lane wave reached: a wave's decay horizon is decided for all its
+# lanes together). The oracle runs on 16 host threads over disjoint channel groups.
+@pytest.mark.parametrize("name,k", [("jamba_layer_prefill", None), ("long_context_256k", 1024),
+                                    ("complex_rotation", None)])
+def test_full_size_prefill(name, k):
     shape = WORKLOADS[name]
     say("full-size prefill", name, "generating inputs")
     d = make_scan_inputs(shape, "cuda")
@@ -29,12 +37,17 @@ def test_full_size_prefill_sampled(name, k):
     say("full-size prefill", name, "running")
     y, hf = fn(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"])
     torch.cuda.synchronize()
-    idx = sample_channels(shape.d_inner, k, seed=5)
-    g = lambda t: gather_channels(t, idx)
-    ora = oracle.scan_complex if shape.complex_state else oracle.scan
+    if k is None:
+        idx = torch.arange(shape.d_inner)
+    else:
+        idx = sample_channels(shape.d_inner, k, seed=5)
+        waves = torch.unique(idx // 64)
+        assert len(waves) == shape.d_inner // 64, "the sample misses a wave"
+    g = lambda t: None if t is None else gather_channels(t, idx)
     say("full-size prefill", name, "oracle on", len(idx), "channels")
-    yr, hr = ora(g(d["x"]), g(d["dt"]), d["A"].cpu()[idx], d["B"].cpu(), d["C"].cpu(),
-                 d["D"].cpu()[idx], g(d["z"]))
+    yr, hr = oracle.scan_threaded(g(d["x"]), g(d["dt"]), d["A"].cpu()[idx], d["B"].cpu(), d["C"].cpu(),
+                                  d["D"].cpu()[idx], g(d["z"]), threads=16,
+                                  complex_state=shape.complex_state)
     tol = TOL[shape.io]
     assert rel_err(g(y), yr) <= tol, f"y error {rel_err(g(y), yr)}"
     assert rel_err(hf.index_select(1, idx.cuda()).cpu(), hr) <= tol
@@ -56,7 +69,6 @@ def test_full_size_batched_decode_512_steps():
     A_s = par["A"].cpu()[li, di].view(1, 4096, N)
     h_ref = torch.zeros((1, 1, 4096, N), dtype=torch.float64).numpy()
     lic, sic, dic = li.cuda(), si.cuda(), di.cuda()
-    compare_at = {0, 255, 511}
     for k in range(shape.steps):
         inp = make_decode_step(shape, k, "cuda")
         if k % 64 == 0:
@@ -69,11 +81,10 @@ def test_full_size_batched_decode_512_steps():
             sl = lambda v: v[l:l + 1]
             ssm.ssm_step(sl(h_pl), sl(inp["x"]), sl(inp["dt"]), sl(par["A"]), sl(inp["B"]), sl(inp["C"]),
                          sl(par["D"]), sl(inp["z"]), y_t=sl(y_pl))
-        if k in compare_at:
-            torch.cuda.synchronize()
-            assert bitwise_equal(y, y_rep), f"y differs from replay at step {k}"
-            assert bitwise_equal(h, h_rep), f"state differs from replay at step {k}"
-            assert bitwise_equal(y, y_pl) and bitwise_equal(h, h_pl), f"per-layer calls differ at step {k}"
+        # y_t and the whole state, bit for bit, at every step (compared on the device)
+        assert bitwise_equal(y, y_rep), f"y differs from replay at step {k}"
+        assert bitwise_equal(h, h_rep), f"state differs from replay at step {k}"
+        assert bitwise_equal(y, y_pl) and bitwise_equal(h, h_pl), f"per-layer calls differ at step {k}"
         # the oracle follows the sampled triples as 4096 one-channel "layers"
         xs = inp["x"][lic, sic, dic].cpu().view(1, 1, -1)
         ds = inp["dt"][lic, sic, dic].cpu().view(1, 1, -1)
