@@ -11,21 +11,25 @@ drawn with the seeded recipe of ``workloads`` and are resident in HBM before the
 timed region starts. W untimed warm-up steps are followed by exactly K timed
 steps bracketed by device synchronisation. Prints one JSON line.
 
-The default workload is the long-context prefill (batch 1, L = 262144, 8192
-channels, N = 16, bf16 inputs, fp32 state) at which the throughput target is set.
+By default all five workloads run, one after another, each with its own timing,
+roofline and CPU baseline (the "workloads" key); the headline fields are the
+long-context prefill's (batch 1, L = 262144, 8192 channels, N = 16, bf16 inputs,
+fp32 state), at which the throughput target is set. --workload NAME runs one.
 
 Roofline: the dominant kernel's average duration is measured with HIP events
 recorded by the library itself on the launch stream (ssm_scan_fwd_profiled), and
-its algorithmic work is compared with two ceilings: HBM bytes against 8 TB/s, and
-vector-ALU instructions (one lane-op each, transcendentals included) against
-256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. The reported bound is the one the kernel
-is closer to. HBM traffic measured with
-rocprofv3 counters is read from profiles/traffic.json when it was taken on the
-current kernel source (by hash), else null.
+its algorithmic bytes against 8 TB/s are the headline (bound "hbm": the metric's
+roofline). Beside it, "alu_view" gives the vector-ALU issue ceiling: VALU
+instructions per element, and issue slots per element with a transcendental
+charged two slots, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, and what that
+ceiling allows in elements/s and as a fraction of HBM peak. HBM traffic measured
+with rocprofv3 counters is read from profiles/traffic.json when it was taken on
+the current kernel source (by hash), else null.
 
 The CPU baseline is the fp64 oracle as it stands, run on a bounded sample of the
 same workload (a subset of channels over the full sequence; channels are
-independent) from several host threads.
+independent) from as many threads as this process has host cores (its CPU affinity,
+capped by a cgroup quota if one is set), with nproc and the CPU model recorded.
 
 --fused times the same workload through ssm_scan_fwd_fused / ssm_step_fused instead:
 x is the input of the MambaBlock's causal depthwise convolution (--conv-k taps,
@@ -703,14 +707,173 @@ def cpu_baseline_decode(shape, workloads, threads, conv_k=None, seqs=4, tokens=1
             "sample_1_core": f"the first {n1} of those layers on one thread ({elems1} elements, {dt1:.1f} s wall)"}
 
 
+def trans_per_elem(shape, variant: dict) -> float:
+    """Transcendental instructions (exp, log, rcp, sin, cos) among the VALU instructions
+    per element: the hardware issues each in two slots (SQ_ACTIVE_INST_VALU charges it
+    twice), so issue slots per element = VALU instructions + transcendentals. Real state:
+    one exp per state; complex: exp, sin, cos per state; the gate exp + rcp per output;
+    the input stage softplus (exp, log, rcp) and silu (exp, rcp); the backward: the
+    forward walk, the recomputation and the adjoint update each one exp per state, and
+    the gate's derivative (exp, rcp)."""
+    N = shape.d_state
+    g = 2 if getattr(shape, "gated", True) else 0
+    if variant.get("backward"):
+        t = 3 * N + g
+        if variant.get("conv_k") is not None:
+            t += 3 + (2 if variant["conv_k"] else 0) + 3
+        return t
+    R = variant.get("mimo") or 1
+    t = (3 * N if getattr(shape, "complex_state", False) else N) + g * R
+    if variant.get("conv_k") is not None:
+        t += 3 + (2 if variant["conv_k"] else 0)
+    return t
+
+
+def host_cpus() -> dict:
+    """The host cores this process may use: the CPU affinity set, capped by a cgroup CPU
+    quota where one is set, plus nproc and the CPU model for the record."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = float(q) / float(per)
+    except (OSError, ValueError):
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = aff if quota is None else max(1, min(aff, int(quota + 0.5)))
+    return {"nproc": os.cpu_count(), "affinity": aff, "cgroup_quota_cores": quota,
+            "cpu_model": model, "threads": usable}
+
+
+def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, workloads,
+            chunk_len=0, graph=True, one_call=False):
+    """Run one workload (one configuration of the path) and return its record."""
+    shape = workloads.WORKLOADS[name]
+    is_decode = isinstance(shape, workloads.DecodeShape)
+    conv_k, trap, mimo, backward = (variant.get("conv_k"), variant.get("trap", False),
+                                    variant.get("mimo", 0), variant.get("backward", False))
+    steps = max(1, steps if not is_decode else min(steps, 64))
+    if is_decode:
+        info, d = run_decode(shape, steps, warmup, torch, ssm, workloads, graph=graph, conv_k=conv_k,
+                             trap=trap, mimo=mimo, one_call=one_call)
+    elif backward:
+        info, d = run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k)
+    else:
+        info, d = run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k,
+                              trap=trap, mimo=mimo)
+    elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
+    dom_s = info["dominant_ms"] / 1e3
+    hbm_ach = info["bytes_per_step"] / dom_s / 1e9
+    lane_ops = info["lane_ops_per_elem"]
+    trans = trans_per_elem(shape, variant)
+    slots = lane_ops + trans
+    alu_ach = info["elements_per_step"] * lane_ops / dom_s / 1e12
+    slot_ach = info["elements_per_step"] * slots / dom_s / 1e12
+    traffic_key = name + (f"+input_stage_k{conv_k}" if conv_k is not None else "") + \
+        ("+backward" if backward else "") + ("+trap" if trap else "") + \
+        (f"+mimo{mimo}" if mimo else "") + ("+one_call" if is_decode and one_call else "")
+    # The metric names the HBM roofline: it is the headline bound for every workload;
+    # the vector-ALU issue ceiling, which the bf16 and complex prefills reach first, is
+    # reported beside it.
+    roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm_ach / HBM_PEAK_GBS, 4), "traffic": traffic_for(info, traffic_key),
+            "kernel": info["kernel"],
+            "kernel_ms": round(info["dominant_ms"] if not is_decode else info["per_call_ms"], 4),
+            "bytes_per_launch": info["bytes_per_step"] if not is_decode else
+            info["bytes_per_step"] / info["calls_per_token"],
+            "alu_view": {
+                "valu_instr_per_elem": lane_ops, "transcendental_per_elem": trans,
+                "issue_slots_per_elem": slots,
+                "achieved_T_instr_s": round(alu_ach, 2), "achieved_T_slots_s": round(slot_ach, 2),
+                "peak_T_slots_s": round(VALU_PEAK_TLANE, 2),
+                "frac_instr": round(alu_ach / VALU_PEAK_TLANE, 4),
+                "frac_issue_slots": round(slot_ach / VALU_PEAK_TLANE, 4),
+                "ceiling_elements_s": round(VALU_PEAK_TLANE * 1e12 / slots, 1),
+                "ceiling_hbm_frac": round(VALU_PEAK_TLANE * 1e12 / slots * info["bytes_per_step"]
+                                          / info["elements_per_step"] / 1e9 / HBM_PEAK_GBS, 4)}}
+    if is_decode:
+        cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
+               "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io, "state": "f32",
+               "calls_per_step": info["calls_per_token"], "hip_graph_per_token": info["graph"]}
+        if conv_k is not None:
+            cfg["input_stage"] = {"conv_k": conv_k, "conv_silu": conv_k > 0, "softplus_dt": True,
+                                  "entry_point": "ssm_step_fused"}
+        if trap:
+            cfg["discretisation"] = "exponential-trapezoidal (ssm_step_trap)"
+        if mimo:
+            cfg["mimo_rank"] = mimo
+            cfg["entry_point"] = "ssm_step_mimo"
+    else:
+        cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L, "d_inner": shape.d_inner,
+               "d_state": shape.d_state, "io": shape.io, "state": "c64" if shape.complex_state else "f32",
+               "complex_state": shape.complex_state, "gated": shape.gated,
+               "chunk_len": info["chunk_len"], "n_chunks": info["n_chunks"]}
+        if conv_k is not None:
+            cfg["input_stage"] = {"conv_k": conv_k, "conv_silu": conv_k > 0, "softplus_dt": True,
+                                  "entry_point": "ssm_scan_fwd_fused"}
+        if backward:
+            cfg["pass"] = ("backward through the input stage (ssm_scan_bwd_fused: dx_in, ddt_raw, dconv_w, "
+                           "dconv_b, ddt_bias, dz, dA, dB, dC, dD)" if conv_k is not None else
+                           "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)")
+        if trap:
+            cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
+        if mimo:
+            cfg["mimo_rank"] = mimo
+            cfg["entry_point"] = "ssm_scan_fwd_mimo"
+    whole = info["bytes_per_step"] / (info["ms_per_step"] / 1e3) / 1e9
+    rec = {"value": round(elems_s, 1), "unit": "elements/s", "steps": steps, "warmup": warmup,
+           "ms_per_step": round(info["ms_per_step"], 4), "config": cfg,
+           "achieved_hbm_GBps_whole_step": round(whole, 1),
+           "hbm_frac_whole_step": round(whole / HBM_PEAK_GBS, 4),
+           "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
+           "roofline": roof}
+    if mimo:
+        rec["mimo_outputs_per_s"] = round(elems_s * mimo, 1)  # R outputs per channel-step
+    cpu = None
+    if with_cpu and not (is_decode and shape.complex_state):
+        if is_decode:
+            cpu = cpu_baseline_decode(shape, workloads, threads, conv_k, trap=trap, mimo=mimo)
+        elif backward:
+            cpu = cpu_baseline_backward(shape, d, torch, workloads, threads, conv_k)
+        else:
+            cpu = cpu_baseline(shape, d, torch, workloads, threads, conv_k, trap=trap, mimo=mimo)
+        cpu.update({"nproc": cpus["nproc"], "cpu_model": cpus["cpu_model"],
+                    "affinity_cores": cpus["affinity"], "cgroup_quota_cores": cpus["cgroup_quota_cores"]})
+    rec["cpu_baseline"] = cpu
+    del d
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+# The five workloads of the metric, in the order they run by default; the 256k prefill
+# (the configuration the metric is quoted on) is the headline.
+ALL_WORKLOADS = ["tiny_f32", "jamba_layer_prefill", "long_context_256k", "batched_decode",
+                 "complex_rotation"]
+HEADLINE = "long_context_256k"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long_context_256k")
+    ap.add_argument("--workload", default=None,
+                    help="one workload only (default: all five, the 256k prefill as the headline; "
+                         "with --fused, --trap, --mimo or --backward: the 256k prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (default: every host core this process may use)")
     ap.add_argument("--chunk-len", type=int, default=0,
                     help="prefill chunk length (0 = the library's own plan)")
     ap.add_argument("--no-graph", action="store_true",
@@ -757,117 +920,52 @@ def main():
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
         return
     ssm.load_library()
-    shape = workloads.WORKLOADS[args.workload]
-    is_decode = isinstance(shape, workloads.DecodeShape)
-    steps = max(1, args.steps if not is_decode else min(args.steps, 64))
-    if args.trap and (args.fused or args.backward or shape.complex_state):
-        print("--trap applies to the real-state prefill and decode workloads, without --fused "
-              "or --backward", file=sys.stderr)
-        sys.exit(2)
-    if args.mimo and (args.mimo not in (1, 2, 4, 8) or args.fused or args.backward or args.trap
-                      or shape.complex_state):
-        print("--mimo R (R in 1, 2, 4, 8) applies to the real-state prefill and decode workloads, "
-              "without --fused, --backward or --trap", file=sys.stderr)
-        sys.exit(2)
-    if is_decode:
-        info, d = run_decode(shape, steps, args.warmup, torch, ssm, workloads, graph=not args.no_graph,
-                             conv_k=args.conv_k if args.fused else None, trap=args.trap,
-                             mimo=args.mimo, one_call=args.one_call)
-    else:
-        if args.backward and shape.complex_state:
-            print("--backward applies to the real-state prefill workloads", file=sys.stderr)
+    variant = {"conv_k": args.conv_k if args.fused else None, "trap": args.trap, "mimo": args.mimo,
+               "backward": args.backward}
+    is_variant = args.fused or args.trap or args.mimo or args.backward
+    names = [args.workload] if args.workload else ([HEADLINE] if is_variant else ALL_WORKLOADS)
+    for n in names:
+        shape = workloads.WORKLOADS[n]
+        is_decode = isinstance(shape, workloads.DecodeShape)
+        if args.trap and (args.fused or args.backward or shape.complex_state):
+            print("--trap applies to the real-state prefill and decode workloads, without --fused "
+                  "or --backward", file=sys.stderr)
             sys.exit(2)
-        if args.fused and shape.complex_state:
-            print("--fused applies to the real-state prefill workloads", file=sys.stderr)
+        if args.mimo and (args.mimo not in (1, 2, 4, 8) or args.fused or args.backward or args.trap
+                          or shape.complex_state):
+            print("--mimo R (R in 1, 2, 4, 8) applies to the real-state prefill and decode workloads, "
+                  "without --fused, --backward or --trap", file=sys.stderr)
             sys.exit(2)
-        conv_k = args.conv_k if args.fused else None
-        if args.backward:
-            info, d = run_backward(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
-                                   conv_k)
-        else:
-            info, d = run_prefill(shape, steps, args.warmup, torch, ssm, workloads, args.chunk_len,
-                                  conv_k, trap=args.trap, mimo=args.mimo)
-
-    elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
-    dom_s = info["dominant_ms"] / 1e3
-    hbm_ach = info["bytes_per_step"] / dom_s / 1e9
-    alu_ach = info["elements_per_step"] * info["lane_ops_per_elem"] / dom_s / 1e12
-    hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / VALU_PEAK_TLANE
-    traffic_key = args.workload + (f"+input_stage_k{args.conv_k}" if args.fused else "") + \
-        ("+backward" if args.backward else "") + ("+trap" if args.trap else "") + \
-        (f"+mimo{args.mimo}" if args.mimo else "") + ("+one_call" if is_decode and args.one_call else "")
-    traffic = traffic_for(info, traffic_key)
-    if hbm_frac >= alu_frac:
-        roof = {"bound": "hbm", "achieved": round(hbm_ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(hbm_frac, 4)}
-    else:
-        roof = {"bound": "alu", "achieved": round(alu_ach, 2), "peak": round(VALU_PEAK_TLANE, 2),
-                "unit": "T VALU lane-instr/s", "frac": round(alu_frac, 4)}
-    roof["traffic"] = traffic
-    roof["kernel"] = info["kernel"]
-    roof["kernel_ms"] = round(info["dominant_ms"] if not is_decode else info["per_call_ms"], 4)
-    roof["hbm_view"] = {"achieved_GBps": round(hbm_ach, 1), "peak_GBps": HBM_PEAK_GBS,
-                        "frac": round(hbm_frac, 4)}
-    roof["alu_view"] = {"achieved_Tlane_op_s": round(alu_ach, 2),
-                        "peak_Tlane_op_s": round(VALU_PEAK_TLANE, 2), "frac": round(alu_frac, 4),
-                        "lane_ops_per_elem": info["lane_ops_per_elem"]}
-    if is_decode:
-        cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
-               "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
-               "calls_per_step": info["calls_per_token"], "hip_graph_per_token": info["graph"]}
-        if args.fused:
-            cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
-                                  "softplus_dt": True, "entry_point": "ssm_step_fused"}
-        if args.trap:
-            cfg["discretisation"] = "exponential-trapezoidal (ssm_step_trap)"
-        if args.mimo:
-            cfg["mimo_rank"] = args.mimo
-            cfg["entry_point"] = "ssm_step_mimo"
-    else:
-        cfg = {"workload": shape.name, "batch": shape.batch, "L": shape.L,
-               "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io,
-               "complex_state": shape.complex_state, "gated": shape.gated,
-               "chunk_len": info["chunk_len"], "n_chunks": info["n_chunks"]}
-        if args.fused:
-            cfg["input_stage"] = {"conv_k": args.conv_k, "conv_silu": args.conv_k > 0,
-                                  "softplus_dt": True, "entry_point": "ssm_scan_fwd_fused"}
-        if args.backward:
-            cfg["pass"] = ("backward through the input stage (ssm_scan_bwd_fused: dx_in, ddt_raw, dconv_w, "
-                           "dconv_b, ddt_bias, dz, dA, dB, dC, dD)" if args.fused else
-                           "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)")
-        if args.trap:
-            cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
-        if args.mimo:
-            cfg["mimo_rank"] = args.mimo
-            cfg["entry_point"] = "ssm_scan_fwd_mimo"
+        if not is_decode and (args.backward or args.fused) and shape.complex_state:
+            print("--backward and --fused apply to the real-state workloads", file=sys.stderr)
+            sys.exit(2)
+    cpus = host_cpus()
+    threads = args.cpu_threads or cpus["threads"]
+    recs = {}
+    for n in names:
+        log("workload", n)
+        recs[n] = measure(n, variant, args.steps, args.warmup, not args.no_cpu_baseline, threads, cpus,
+                          torch, ssm, workloads, args.chunk_len, graph=not args.no_graph,
+                          one_call=args.one_call)
+    head_name = HEADLINE if HEADLINE in recs else names[0]
+    head = recs[head_name]
+    io = head["config"]["io"]
     out = {
-        "metric": METRIC, "value": round(elems_s, 1), "unit": "elements/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(info["ms_per_step"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded, resident in HBM before timing)", "config": cfg,
-        "achieved_hbm_GBps_whole_step": round(info["bytes_per_step"] / (info["ms_per_step"] / 1e3) / 1e9, 1),
-        "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
-        "roofline": roof,
+        "metric": METRIC, "value": head["value"], "unit": "elements/s", "n_gpus": 1,
+        "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": io, "arithmetic": "fp32 state and fp32 arithmetic; inputs and outputs in " + io,
+        "data": "synthetic (seeded, resident in HBM before timing)", "config": head["config"],
+        "achieved_hbm_GBps_whole_step": head["achieved_hbm_GBps_whole_step"],
+        "hbm_frac_whole_step": head["hbm_frac_whole_step"],
+        "phases_ms": head["phases_ms"], "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
     }
-    if args.mimo:
-        # each element (channel-step) has R inputs and R outputs
-        out["mimo_outputs_per_s"] = round(elems_s * args.mimo, 1)
-    if not args.no_cpu_baseline and is_decode and not shape.complex_state:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        out["cpu_baseline"] = cpu_baseline_decode(shape, workloads, threads,
-                                                  args.conv_k if args.fused else None, trap=args.trap,
-                                                  mimo=args.mimo)
-    elif not args.no_cpu_baseline and not is_decode:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        if args.backward:
-            out["cpu_baseline"] = cpu_baseline_backward(shape, d, torch, workloads, threads,
-                                                        args.conv_k if args.fused else None)
-        else:
-            out["cpu_baseline"] = cpu_baseline(shape, d, torch, workloads, threads,
-                                               args.conv_k if args.fused else None, trap=args.trap,
-                                               mimo=args.mimo)
-    else:
-        out["cpu_baseline"] = None
+    if "mimo_outputs_per_s" in head:
+        out["mimo_outputs_per_s"] = head["mimo_outputs_per_s"]
+    if len(recs) > 1:
+        out["workloads"] = {n: {k: v for k, v in r.items() if k not in ("steps", "warmup")}
+                            for n, r in recs.items()}
     print(json.dumps(out), flush=True)
 
 
