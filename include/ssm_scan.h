@@ -123,8 +123,9 @@ ssm_status ssm_scan_fwd_ex(const void *x, const void *dt, const float *A, const 
  * and errors as ssm_scan_fwd_ex on the current device (hip_stream must belong to it),
  * plus SSM_ERR_WORKSPACE, before anything is enqueued, when the plan needs more scratch
  * than that: ssm_scan_fwd_workspace_ex(batch, L, d_inner, d_state, chunk_len) >
- * SSM_NOALLOC_SCRATCH_BYTES. The library's own plan (chunk_len = 0) needs at most
- * 2 * 5120 * 64 * d_state * 4 bytes (42 MB at d_state 16) and always fits. Calls on one
+ * SSM_NOALLOC_SCRATCH_BYTES. The library's own plan (chunk_len = 0) needs less than
+ * 2 * (5 waves per SIMD * SIMDs) * 64 * d_state * 4 bytes: 42 MB at d_state 16 on the
+ * 1024 SIMDs of MI355X, which fits. Calls on one
  * GPU share its scratch, and nothing in it needs to start cleared (each call writes
  * every summary before reading it); calls that overlap in time on one GPU (on
  * different streams, or from different threads) race on it and must be ordered by the
@@ -137,7 +138,12 @@ ssm_status ssm_scan_fwd_noalloc(const void *x, const void *dt, const float *A, c
                                 ssm_dtype io, int64_t chunk_len, void *hip_stream);
 
 /* The chunk length each prefill entry point picks for this shape with chunk_len = 0
- * (pure host functions; 0 for an invalid shape). The library cuts the sequence into
+ * (host functions; 0 for an invalid shape). The plan is made for the current device: its
+ * compute-unit count is queried once per device (hipDeviceGetAttribute) and cached for
+ * the process; a positive integer in the environment variable SSMSCAN_CU_COUNT at that
+ * first query replaces it (to plan for another part or partition), and with no device
+ * to query the plan assumes MI355X's 256 compute units (1024 SIMDs), uncached. The
+ * library cuts the sequence into
  * enough chunks to keep as many waves per SIMD resident as the entry point's rescan
  * kernel is compiled for: 5 for ssm_scan_fwd / _ex / _trap (without lam) and
  * ssm_scan_fwd_mimo up to rank 4, 4 for ssm_scan_fwd_fused, ssm_scan_fwd_c64,

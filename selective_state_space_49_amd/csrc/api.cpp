@@ -6,9 +6,11 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ssm_internal.h"
 #include "ssm_scan.h"
@@ -39,10 +41,49 @@ bool valid_rank(int32_t r) { return r == 1 || r == 2 || r == 4 || r == 8; }
 size_t io_bytes(ssm_dtype io) { return io == SSM_BF16 ? 2 : 4; }
 
 // Waves wanted per launch for the chunk rescan: as many as the rescan kernel is
-// compiled to keep resident per SIMD, on 1024 SIMDs (256 CUs). One wave more than a
+// compiled to keep resident per SIMD, on every SIMD of the device. One wave more than a
 // round holds would start a second, mostly idle round, so the count must not exceed it.
-constexpr int64_t kSimds = 1024;
-constexpr int64_t kTargetWaves = 4 * kSimds;
+//
+// Device properties cache: the compute-unit count of each device, queried once (the
+// first plan made while that device is current) and kept for the process. A CDNA
+// compute unit has four SIMDs. SSMSCAN_CU_COUNT (a positive integer in the environment
+// when the device is first queried) replaces the queried count, to plan for another
+// part or partition. With no device to query (no GPU, or the HIP runtime reports an
+// error) the plan assumes MI355X's 256 compute units and caches nothing.
+constexpr int64_t kSimdsPerCu = 4;
+constexpr int32_t kDefaultCus = 256;
+constexpr int kMaxDevices = 64;
+std::mutex g_prop_mu;
+int32_t g_cus[kMaxDevices];  // 0: not queried yet
+
+int32_t env_cus() {
+    const char *e = getenv("SSMSCAN_CU_COUNT");
+    const long v = e ? strtol(e, nullptr, 10) : 0;
+    return v > 0 && v < (1 << 20) ? (int32_t)v : 0;
+}
+
+int64_t device_simds() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();  // leave no error behind for the next launch check
+        const int32_t e = env_cus();
+        return (int64_t)(e ? e : kDefaultCus) * kSimdsPerCu;
+    }
+    std::lock_guard<std::mutex> lock(g_prop_mu);
+    if (!g_cus[dev]) {
+        int32_t cus = env_cus();
+        if (!cus) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+                cus = v;
+            else
+                (void)hipGetLastError();
+        }
+        if (!cus) return (int64_t)kDefaultCus * kSimdsPerCu;  // not cached: try again next time
+        g_cus[dev] = cus;
+    }
+    return (int64_t)g_cus[dev] * kSimdsPerCu;
+}
 
 // Waves per SIMD each rescan is compiled for (its __launch_bounds__ minimum, or what
 // its registers allow).
@@ -59,7 +100,7 @@ constexpr int64_t kMinChunk = 64;       // shortest chunk the planner picks
 constexpr int64_t kMaxChunks = 65535;   // grid y limit
 constexpr size_t kWsAlign = 256;
 
-int64_t auto_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int64_t target_waves = kTargetWaves) {
+int64_t auto_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int64_t target_waves) {
     if (L <= 0) return 1;
     const int64_t waves_per_chunk = std::max<int64_t>(1, batch * ((d_inner + 63) / 64));
     int64_t chunks = (target_waves + waves_per_chunk - 1) / waves_per_chunk;
@@ -91,7 +132,7 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
     // (MIMO rows of x, z and y hold rank elements per channel.)
     const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 31) / (d_inner * rank * 4) - 1);
     int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
-                              : auto_chunk_len(batch, L, d_inner, waves_per_simd * kSimds);
+                              : auto_chunk_len(batch, L, d_inner, waves_per_simd * device_simds());
     T = std::min(T, cap);
     // MIMO: a chunk's rows of B (d_state * rank elements each) also span less than 2 GiB,
     // since the matrix path stages them through buffer loads with 32-bit offsets.
@@ -758,8 +799,8 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
 
 // ---------------------------------------------------------------- backward through the input stage
 // The two streaming kernels of the input stage take chunks of their own (independent:
-// enough for about 8192 blocks of 256 channels, i.e. 2048 blocks of 256 lanes at four
-// channels per lane, chunks of at least 128 steps). Workspace: the scan backward's, then u, dt, du, ddt
+// enough for about 8 blocks of 256 channels per SIMD, 8192 on 256 CUs, i.e. 2 blocks of
+// 256 lanes per SIMD at four channels per lane, chunks of at least 128 steps). Workspace: the scan backward's, then u, dt, du, ddt
 // ([batch][L][d_inner] of io each) and the partial sums ([n][batch][d_inner][conv_k + 2]
 // fp32), each 256-byte aligned.
 struct InBwdPlan {
@@ -776,7 +817,8 @@ ssm_status make_in_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d
     const ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &bp);
     if (st != SSM_OK) return st;
     const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 255) / 256));
-    int64_t n = std::min<int64_t>((8192 + blocks - 1) / blocks, std::max<int64_t>(1, L / 128));
+    const int64_t want = 8 * device_simds();
+    int64_t n = std::min<int64_t>((want + blocks - 1) / blocks, std::max<int64_t>(1, L / 128));
     n = std::max<int64_t>(n, 1);
     p->T = L > 0 ? (L + n - 1) / n : 1;
     p->n_chunks = L > 0 ? (int32_t)((L + p->T - 1) / p->T) : 0;

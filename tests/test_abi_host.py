@@ -57,7 +57,8 @@ def test_plan_and_workspace(lib):
         chunks = -(-L // T)
         assert 64 <= T <= L and chunks * b * (Dn // 64) >= 2048
         assert ssm.ssm_scan_fwd_workspace(b, L, Dn, 16) == ssm.ssm_scan_fwd_workspace_ex(b, L, Dn, 16, 0)
-    # Each entry point's plan gives every one of the 1024 SIMDs as many waves as its
+    # Each entry point's plan gives every one of the 1024 SIMDs (256 CUs: the planner's
+    # default when no GPU can be queried, as here, and MI355X's count) as many waves as its
     # rescan is compiled to keep: 5 (plain, trapezoidal) -> 40 chunks of the 256k
     # sequence over its 128 channel waves; 4 (input stage) -> 32; complex: 4 x 64 waves
     # per chunk, 4 per SIMD -> 16 chunks.
@@ -72,6 +73,41 @@ def test_plan_and_workspace(lib):
     # Invalid sizes give 0 from the query.
     assert ssm.ssm_scan_fwd_workspace(1, 10, 8, 3) == 0
     assert ssm.ssm_scan_fwd_fused_chunk_len(1, 10, 8, 3) == 0
+
+
+_PLAN_PROBE = """
+import sys
+sys.path.insert(0, {root!r})
+import selective_state_space_49_amd as ssm
+ssm.load_library()
+c = lambda L, T: -(-L // T)
+print(c(262144, ssm.ssm_scan_fwd_chunk_len(1, 262144, 8192, 16)),
+      c(262144, ssm.ssm_scan_fwd_fused_chunk_len(1, 262144, 8192, 16)),
+      c(8192, ssm.ssm_scan_fwd_c64_chunk_len(4, 8192, 4096, 16)),
+      c(4096, ssm.ssm_scan_fwd_chunk_len(2, 4096, 8192, 16)))
+"""
+
+
+@pytest.mark.parametrize("cus,want", [(None, "40 32 16 20"), ("256", "40 32 16 20"),
+                                      ("128", "20 16 8 10"), ("32", "5 5 2 3"), ("0", "40 32 16 20")])
+def test_chunk_plan_follows_the_device_cu_count(lib, cus, want):
+    # The planner sizes the plan by the device's compute units (4 SIMDs each), queried
+    # once and cached; SSMSCAN_CU_COUNT replaces the count (here, with no GPU, the
+    # planner's default of 256 CUs otherwise). 5 waves per SIMD for the plain rescan:
+    # 40 chunks of the 256k sequence's 128 channel waves on 256 CUs, 20 on 128, 5 on 32
+    # (the fused plan's 4 chunks on 32 CUs are capped at 65535 steps, 2 GiB of fp32 rows: 5);
+    # the fused (4 waves) and complex (4 waves, 4 x 64 waves per chunk) plans likewise;
+    # a non-positive count is ignored.
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("SSMSCAN_CU_COUNT", None)
+    if cus is not None:
+        env["SSMSCAN_CU_COUNT"] = cus
+    r = subprocess.run([sys.executable, "-c", _PLAN_PROBE.format(root=ROOT)], env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == want.split()
 
 
 def _scan_raw(lib, x=0x1000, dt=0x1000, A=0x1000, B=0x1000, C=0x1000, D=0x1000, z=None, h0=None,

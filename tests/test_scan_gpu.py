@@ -263,3 +263,16 @@ def test_prefill_in_captured_graph_matches_eager():
         assert bitwise_equal(y_g, y_e) and bitwise_equal(h_g, h_e), f"replay {rep} differs"
         ssm.ssm_scan_fwd_ex(*args, chunk_len=T)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_chunk_plan_uses_the_device_cu_count():
+    # The planner queries the current device's compute units once and plans 5 rescan
+    # waves per SIMD (4 SIMDs per CU) for the plain prefill: on MI355X (256 CUs) the 256k
+    # workload's 128 channel waves per chunk make 40 chunks, as before the query existed.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say("chunk plan on", cus, "CUs")
+    T = ssm.ssm_scan_fwd_chunk_len(1, 262144, 8192, 16)
+    n = -(-262144 // T)
+    assert n == -(-5 * 4 * cus // 128), (cus, n)
+    if cus == 256:
+        assert n == 40
