@@ -99,12 +99,18 @@ def prefill_lane_ops(s) -> float:
     dt*theta, fract, sin, cos, 2 mul (decay x rotation), 2 mul (dt x B), 4 fma (complex
     update), 2 fma (real part of C h) = 16. Per element: dt*x, D*x + acc; with bf16 I/O
     the widening of x and dt and the output conversion; gated: the gate (mul, exp, add,
-    rcp, mul, mul) and, with bf16 I/O, the widening of z."""
+    rcp, mul, mul) and, with bf16 I/O, the widening of z. The complex state spreads a
+    channel over P = 4 lanes, each of which does the per-element work, plus the sum over
+    its P lanes (2 DPP adds) and, with bf16 I/O, the widening of its share of the staged
+    B and C rows (one per lane-step)."""
     bf16 = s.io == "bf16"
     per_state = 16 if s.complex_state else 5
     per_elem = 2 + (3 if bf16 else 0)
     if s.gated:
         per_elem += 6 + (1 if bf16 else 0)
+    if s.complex_state:
+        P = min(s.d_state, 4)
+        per_elem = P * (per_elem + (P.bit_length() - 1) + (1 if bf16 else 0))
     return s.d_state * per_state + per_elem
 
 

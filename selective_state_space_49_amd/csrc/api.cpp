@@ -91,10 +91,16 @@ enum class Family { Plain, Fused, Complex, Mimo, Backward, TrapWeighted };
 int32_t waves_per_simd(Family f, int32_t rank = 1) {
     switch (f) {
         case Family::Plain: return 5;     // plain and exponential-trapezoidal rescans
+        case Family::Complex: return 5;
         case Family::Mimo: return rank <= 4 ? 5 : 4;
-        default: return 4;                // input stage, complex state, backward, and the
+        default: return 4;                // input stage, backward, and the
                                           // exponential-trapezoidal rescan with a weight stream
     }
+}
+// Lanes per channel: the complex-state kernels spread a channel's states over 4 lanes
+// (fewer states: one lane each); the others keep a channel in one lane.
+int64_t lanes_per_channel(bool cplx, int32_t d_state) {
+    return cplx ? std::min<int32_t>(d_state, 4) : 1;
 }
 constexpr int64_t kMinChunk = 64;       // shortest chunk the planner picks
 constexpr int64_t kMaxChunks = 65535;   // grid y limit
@@ -132,7 +138,8 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
     // (MIMO rows of x, z and y hold rank elements per channel.)
     const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 31) / (d_inner * rank * 4) - 1);
     int64_t T = chunk_len > 0 ? std::min(chunk_len, std::max<int64_t>(L, 1))
-                              : auto_chunk_len(batch, L, d_inner, waves_per_simd * device_simds());
+                              : auto_chunk_len(batch, L, d_inner * lanes_per_channel(cplx, d_state),
+                                               waves_per_simd * device_simds());
     T = std::min(T, cap);
     // MIMO: a chunk's rows of B (d_state * rank elements each) also span less than 2 GiB,
     // since the matrix path stages them through buffer loads with 32-bit offsets.

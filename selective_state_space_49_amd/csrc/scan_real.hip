@@ -237,6 +237,46 @@ __global__ __launch_bounds__(256) void k_carry(ScanArgs a, int64_t M) {
     }
 }
 
+// With few chunks the wave-wide scan above mostly runs on empty lanes. Then one lane
+// per state column walks the chunks in order, carry = P_c carry + H_c, with the loads of
+// kCarryBatch chunks issued before their multiply-adds; the carries are written over H_c
+// as above. The same result up to rounding (a sequential rather than a tree association).
+constexpr int kCarrySeqMax = 64;  // chunk summaries handled by the sequential walk
+constexpr int kCarryBatch = 8;
+
+__global__ __launch_bounds__(256) void k_carry_seq(ScanArgs a, int64_t M) {
+    const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (col >= M) return;
+    const int nsum = a.n_chunks - 1;
+    float carry = a.h0 ? a.h0[col] : 0.0f;
+    for (int c0 = 0; c0 < nsum; c0 += kCarryBatch) {
+        float p[kCarryBatch], h[kCarryBatch];
+#pragma unroll
+        for (int k = 0; k < kCarryBatch; ++k) {
+            if (c0 + k < nsum) {
+                p[k] = a.sumP[(size_t)(c0 + k) * M + col];
+                h[k] = a.sumH[(size_t)(c0 + k) * M + col];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kCarryBatch; ++k) {
+            if (c0 + k < nsum) {
+                carry = __builtin_fmaf(p[k], carry, h[k]);
+                a.sumH[(size_t)(c0 + k) * M + col] = carry;
+            }
+        }
+    }
+}
+
+// The carry over the chunk summaries of M state columns: sequential for up to
+// kCarrySeqMax summaries, else the tiled wave scan.
+inline void carry_launch(const ScanArgs &a, int64_t M, hipStream_t s) {
+    if (a.n_chunks - 1 <= kCarrySeqMax)
+        hipLaunchKernelGGL(k_carry_seq, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, a, M);
+    else
+        hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+}
+
 // ---------------------------------------------------------------- chunk summary
 // Chunk summary: end state from a zero start and total decay, walking only the
 // window back to the decay horizon (see horizon_start).
@@ -404,7 +444,7 @@ hipError_t launch_t(const ScanArgs &a, bool gated, hipStream_t s, hipEvent_t con
     mark(ev, 1, s);
     if (a.n_chunks > 1) {
         const int64_t M = a.batch * a.Dn * N;
-        hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+        carry_launch(a, M, s);
     }
     mark(ev, 2, s);
     if (gated)
@@ -479,7 +519,7 @@ hipError_t launch_summary_carry_io(const ScanArgs &a, int d_state, hipStream_t s
         default: return hipErrorInvalidValue;
     }
     const int64_t M = a.batch * a.Dn * d_state;
-    hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+    carry_launch(a, M, s);
     return hipGetLastError();
 }
 }  // namespace
@@ -492,7 +532,7 @@ hipError_t launch_summary_carry(const ScanArgs &a, int io, int d_state, hipStrea
 hipError_t launch_carry(const ScanArgs &a, int d_state, hipStream_t s) {
     if (a.n_chunks <= 1) return hipSuccess;
     const int64_t M = a.batch * a.Dn * d_state;
-    hipLaunchKernelGGL(k_carry, dim3((unsigned)((M + 63) / 64)), dim3(256), 0, s, a, M);
+    carry_launch(a, M, s);
     return hipGetLastError();
 }
 

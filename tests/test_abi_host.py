@@ -60,12 +60,12 @@ def test_plan_and_workspace(lib):
     # Each entry point's plan gives every one of the 1024 SIMDs (256 CUs: the planner's
     # default when no GPU can be queried, as here, and MI355X's count) as many waves as its
     # rescan is compiled to keep: 5 (plain, trapezoidal) -> 40 chunks of the 256k
-    # sequence over its 128 channel waves; 4 (input stage) -> 32; complex: 4 x 64 waves
-    # per chunk, 4 per SIMD -> 16 chunks.
+    # sequence over its 128 channel waves; 4 (input stage) -> 32; complex: 4 lanes per
+    # channel, 4 x 256 waves per chunk, 5 per SIMD -> 5 chunks.
     n_chunks = lambda L, T: -(-L // T)
     assert n_chunks(262144, ssm.ssm_scan_fwd_chunk_len(1, 262144, 8192, 16)) == 40
     assert n_chunks(262144, ssm.ssm_scan_fwd_fused_chunk_len(1, 262144, 8192, 16)) == 32
-    assert n_chunks(8192, ssm.ssm_scan_fwd_c64_chunk_len(4, 8192, 4096, 16)) == 16
+    assert n_chunks(8192, ssm.ssm_scan_fwd_c64_chunk_len(4, 8192, 4096, 16)) == 5
     assert n_chunks(4096, ssm.ssm_scan_fwd_chunk_len(2, 4096, 8192, 16)) == 20
     Tf = ssm.ssm_scan_fwd_fused_chunk_len(1, 262144, 8192, 16)
     assert ssm.ssm_scan_fwd_workspace_ex(1, 262144, 8192, 16, 0) >= \
@@ -88,15 +88,16 @@ print(c(262144, ssm.ssm_scan_fwd_chunk_len(1, 262144, 8192, 16)),
 """
 
 
-@pytest.mark.parametrize("cus,want", [(None, "40 32 16 20"), ("256", "40 32 16 20"),
-                                      ("128", "20 16 8 10"), ("32", "5 5 2 3"), ("0", "40 32 16 20")])
+@pytest.mark.parametrize("cus,want", [(None, "40 32 5 20"), ("256", "40 32 5 20"),
+                                      ("128", "20 16 3 10"), ("32", "5 5 1 3"), ("0", "40 32 5 20")])
 def test_chunk_plan_follows_the_device_cu_count(lib, cus, want):
     # The planner sizes the plan by the device's compute units (4 SIMDs each), queried
     # once and cached; SSMSCAN_CU_COUNT replaces the count (here, with no GPU, the
     # planner's default of 256 CUs otherwise). 5 waves per SIMD for the plain rescan:
     # 40 chunks of the 256k sequence's 128 channel waves on 256 CUs, 20 on 128, 5 on 32
     # (the fused plan's 4 chunks on 32 CUs are capped at 65535 steps, 2 GiB of fp32 rows: 5);
-    # the fused (4 waves) and complex (4 waves, 4 x 64 waves per chunk) plans likewise;
+    # the fused (4 waves) and complex (5 waves, 4 lanes per channel: 4 x 256 waves per
+    # chunk) plans likewise;
     # a non-positive count is ignored.
     import subprocess
     import sys

@@ -20,6 +20,8 @@ CASES = [
     (2, 129, 65, 2, "bf16", True, True, 16),
     (1, 77, 3, 1, "f32", False, True, 8),
     (1, 4300, 16, 4, "f32", False, True, 64),   # 68 chunks: two carry tiles
+    (2, 1500, 300, 16, "bf16", True, True, 0),  # library's plan; 64-channel blocks, the last ragged
+    (1, 203, 130, 16, "f32", False, True, 50),  # ragged blocks of 4-step rows
 ]
 
 
