@@ -862,6 +862,28 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
     return rec
 
 
+def copy_ceiling(torch, nbytes=1 << 32, reps=5):
+    """Practical HBM ceiling for context: a device-to-device copy of nbytes (read + write
+    of nbytes each), best of reps, timed with events on the current stream."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (best / 1e3) / 1e9
+    return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": f"device copy of {nbytes >> 30} GiB (read + write), best of {reps}, torch copy_"}
+
+
 # The five workloads of the metric, in the order they run by default; the 256k prefill
 # (the configuration the metric is quoted on) is the headline.
 ALL_WORKLOADS = ["tiny_f32", "jamba_layer_prefill", "long_context_256k", "batched_decode",
@@ -969,6 +991,7 @@ def main():
     }
     if "mimo_outputs_per_s" in head:
         out["mimo_outputs_per_s"] = head["mimo_outputs_per_s"]
+    out["hbm_copy_ceiling"] = copy_ceiling(torch)
     if len(recs) > 1:
         out["workloads"] = {n: {k: v for k, v in r.items() if k not in ("steps", "warmup")}
                             for n, r in recs.items()}
