@@ -35,7 +35,8 @@ capped by a cgroup quota if one is set), with nproc and the CPU model recorded.
 x is the input of the MambaBlock's causal depthwise convolution (--conv-k taps,
 default 4) and dt the raw dt projection output, and the convolution + silu and
 softplus run inside the scan's load stage (decode: with the carried conv state).
---trap times the exponential-trapezoidal entry points, --mimo R the MIMO ones (rank-R
+--trap times the exponential-trapezoidal entry points (--trap-weight random: with the
+per-step weight stream), --mimo R the MIMO ones (rank-R
 inputs and outputs per channel; elements stay channel-steps, each with R outputs).
 --backward times ssm_scan_bwd on a prefill workload, and with --fused ssm_scan_bwd_fused
 (the gradients through the input stage as well). --one-call times the decode as one call
@@ -285,7 +286,7 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
 
 
 def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None, trap=False,
-                mimo=0):
+                mimo=0, lam=False):
     """conv_k None: ssm_scan_fwd; else ssm_scan_fwd_fused with a conv_k-tap filter.
     trap: ssm_scan_fwd_trap (exponential-trapezoidal), with an input before step 0.
     mimo R > 0: ssm_scan_fwd_mimo with rank-R projections."""
@@ -294,6 +295,8 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     d = workloads.make_mimo_inputs(shape, mimo, dev) if mimo else workloads.make_scan_inputs(shape, dev)
     if trap:
         d.update(workloads.make_prev_input(shape.batch, shape.d_inner, shape.d_state, shape.io, dev))
+        d["lam"] = (workloads.make_trap_weight((shape.batch, shape.L, shape.d_inner), shape.io, dev,
+                                               kind="random") if lam else None)
     fused = conv_k is not None
     if fused:
         d.update(workloads.make_input_stage(shape, conv_k, dev))
@@ -302,9 +305,10 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     cplx = shape.complex_state
     y = torch.empty_like(d["x"])
     hf = torch.empty((b, Dn, N) + ((2,) if cplx else ()), dtype=torch.float32, device=dev)
+    # (the weighted trapezoidal rescan, like the fused one, is planned for 4 waves per SIMD)
     T = chunk_len or (ssm.ssm_scan_fwd_c64_chunk_len(b, L, Dn, N) if cplx
                       else ssm.ssm_scan_fwd_mimo_chunk_len(b, L, Dn, N, mimo) if mimo
-                      else ssm.ssm_scan_fwd_fused_chunk_len(b, L, Dn, N) if fused
+                      else ssm.ssm_scan_fwd_fused_chunk_len(b, L, Dn, N) if fused or (trap and lam)
                       else ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N))
     ws_n = (ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, T) if cplx
             else ssm.ssm_scan_fwd_mimo_workspace(b, L, Dn, N, mimo, T) if mimo
@@ -330,8 +334,8 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
                                    events=[e.cuda_event for e in events])
         elif trap:
             ssm.ssm_scan_fwd_trap(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
-                                  d["x_prev"], d["B_prev"], y=y, h_final=hf, workspace=ws,
-                                  chunk_len=T, events=[e.cuda_event for e in events])
+                                  d["x_prev"], d["B_prev"], lam=d["lam"], y=y, h_final=hf,
+                                  workspace=ws, chunk_len=T, events=[e.cuda_event for e in events])
         elif mimo:
             ssm.ssm_scan_fwd_mimo(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], None,
                                   y=y, h_final=hf, workspace=ws, chunk_len=T,
@@ -367,6 +371,9 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     if trap:
         nbytes += shape.batch * (shape.d_inner + shape.d_state) * io_bytes   # x_prev, B_prev
         lane_ops += trap_lane_ops(shape.d_state)
+        if lam:  # the weight stream: read once; widened, 1 - lam and one more product
+            nbytes += elems * io_bytes
+            lane_ops += 3 if shape.io == "bf16" else 2
     if mimo:
         nbytes = mimo_prefill_bytes(shape, io_bytes, mimo)
         lane_ops = mimo_lane_ops(shape, mimo, matrix=mimo >= 4)
@@ -382,7 +389,7 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
 
 
 def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=None, trap=False,
-               mimo=0, one_call=False):
+               mimo=0, one_call=False, lam=False):
     """conv_k None: ssm_step; else ssm_step_fused with a conv_k-tap filter. trap:
     ssm_step_trap, given the previous token's x and B. mimo R > 0: ssm_step_mimo.
     one_call: each token is one call over all layers (n_layers = Ln: the [layers, seqs,
@@ -394,6 +401,10 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
     log("drawing", warmup + steps, "token steps of inputs")
     toks = [workloads.make_mimo_decode_step(shape, mimo, k, dev) if mimo
             else workloads.make_decode_step(shape, k, dev) for k in range(warmup + steps)]
+    if trap:  # each token's weight (random in [0, 1]) or none (1/2)
+        for k, t in enumerate(toks):
+            t["lam"] = (workloads.make_trap_weight((Ln, S, Dn), shape.io, dev, kind="random", seed=100 + k)
+                        if lam else None)
     fused = conv_k is not None
     if fused:
         ist = workloads.make_decode_input_stage(shape, conv_k, dev)
@@ -416,7 +427,7 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
                                conv_w=p["conv_w"], conv_b=p["conv_b"], dt_bias=p["dt_bias"], y_t=yy)
         elif trap:
             ssm.ssm_step_trap(hh, pv["x"], pv["B"], t["x"], t["dt"], A, t["B"], t["C"], D, t["z"],
-                              y_t=yy)
+                              lam_t=t["lam"], y_t=yy)
         elif mimo:
             ssm.ssm_step_mimo(hh, t["x"], t["dt"], A, t["B"], t["C"], D, t["z"], y_t=yy)
         else:
@@ -482,6 +493,9 @@ def run_decode(shape, steps, warmup, torch, ssm, workloads, graph=True, conv_k=N
     if trap:
         nbytes += Ln * S * (Dn + N) * io_bytes   # the previous token's x and B
         lane_ops += trap_lane_ops(N)
+        if lam:
+            nbytes += Ln * S * Dn * io_bytes     # the token's weight
+            lane_ops += 3 if shape.io == "bf16" else 2
     if mimo:
         nbytes = mimo_decode_bytes(shape, io_bytes, mimo)
         lane_ops = mimo_lane_ops(shape, mimo)
@@ -542,6 +556,8 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False, m
         import numpy as np
         xp = oracle.to_f64(d["x_prev"].index_select(1, idx).cpu()) if trap else None
         Bq = oracle.to_f64(d["B_prev"].cpu()) if trap else None
+        lw = (oracle.to_f64(d["lam"].index_select(2, idx).cpu())
+              if trap and d.get("lam") is not None else None)
         f = [oracle.to_f64(a) for a in args]
         parts = [p for p in np.array_split(np.arange(k), threads) if len(p)]
 
@@ -551,7 +567,8 @@ def cpu_baseline(shape, d, torch, workloads, threads, conv_k=None, trap=False, m
                 oracle.scan_mimo(sub(f[0]), sub(f[1]), f[2][p], f[3], f[4], f[5][p], sub(f[6]))
             else:
                 oracle.scan_trap(sub(f[0]), sub(f[1]), f[2][p], f[3], f[4], f[5][p], sub(f[6]),
-                                 x_prev=np.ascontiguousarray(xp[:, p]), B_prev=Bq)
+                                 x_prev=np.ascontiguousarray(xp[:, p]), B_prev=Bq,
+                                 lam=None if lw is None else sub(lw))
         t0 = time.perf_counter()
         ts = [threading.Thread(target=work, args=(p,)) for p in parts]
         for t in ts: t.start()
@@ -768,15 +785,16 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
     is_decode = isinstance(shape, workloads.DecodeShape)
     conv_k, trap, mimo, backward = (variant.get("conv_k"), variant.get("trap", False),
                                     variant.get("mimo", 0), variant.get("backward", False))
+    lam = trap and variant.get("lam", False)
     steps = max(1, steps if not is_decode else min(steps, 64))
     if is_decode:
         info, d = run_decode(shape, steps, warmup, torch, ssm, workloads, graph=graph, conv_k=conv_k,
-                             trap=trap, mimo=mimo, one_call=one_call)
+                             trap=trap, mimo=mimo, one_call=one_call, lam=lam)
     elif backward:
         info, d = run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k)
     else:
         info, d = run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k,
-                              trap=trap, mimo=mimo)
+                              trap=trap, mimo=mimo, lam=lam)
     elems_s = info["elements_per_step"] / (info["ms_per_step"] / 1e3)
     dom_s = info["dominant_ms"] / 1e3
     hbm_ach = info["bytes_per_step"] / dom_s / 1e9
@@ -786,7 +804,7 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
     alu_ach = info["elements_per_step"] * lane_ops / dom_s / 1e12
     slot_ach = info["elements_per_step"] * slots / dom_s / 1e12
     traffic_key = name + (f"+input_stage_k{conv_k}" if conv_k is not None else "") + \
-        ("+backward" if backward else "") + ("+trap" if trap else "") + \
+        ("+backward" if backward else "") + ("+trap" if trap else "") + ("_lam" if lam else "") + \
         (f"+mimo{mimo}" if mimo else "") + ("+one_call" if is_decode and one_call else "")
     # The metric names the HBM roofline: it is the headline bound for every workload;
     # the vector-ALU issue ceiling, which the bf16 and complex prefills reach first, is
@@ -816,6 +834,7 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
                                   "entry_point": "ssm_step_fused"}
         if trap:
             cfg["discretisation"] = "exponential-trapezoidal (ssm_step_trap)"
+            cfg["trap_weight"] = "random per token and channel" if lam else "1/2 (none given)"
         if mimo:
             cfg["mimo_rank"] = mimo
             cfg["entry_point"] = "ssm_step_mimo"
@@ -833,6 +852,7 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
                            "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)")
         if trap:
             cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
+            cfg["trap_weight"] = "random per step and channel" if lam else "1/2 (none given)"
         if mimo:
             cfg["mimo_rank"] = mimo
             cfg["entry_point"] = "ssm_scan_fwd_mimo"
@@ -916,6 +936,9 @@ def main():
     ap.add_argument("--conv-k", type=int, default=4, help="filter taps with --fused (0..4)")
     ap.add_argument("--trap", action="store_true",
                     help="the exponential-trapezoidal entry points (ssm_scan_fwd_trap, ssm_step_trap)")
+    ap.add_argument("--trap-weight", choices=("none", "random"), default="none",
+                    help="with --trap: no weight (1/2, the trapezoid rule) or a random weight in "
+                         "[0, 1] per step and channel (the weight stream)")
     ap.add_argument("--mimo", type=int, default=0, metavar="R",
                     help="the MIMO entry points (ssm_scan_fwd_mimo, ssm_step_mimo) with rank R "
                          "(1, 2, 4 or 8)")
@@ -949,7 +972,7 @@ def main():
         return
     ssm.load_library()
     variant = {"conv_k": args.conv_k if args.fused else None, "trap": args.trap, "mimo": args.mimo,
-               "backward": args.backward}
+               "backward": args.backward, "lam": args.trap_weight == "random"}
     is_variant = args.fused or args.trap or args.mimo or args.backward
     names = [args.workload] if args.workload else ([HEADLINE] if is_variant else ALL_WORKLOADS)
     for n in names:
