@@ -378,6 +378,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     __shared__ uint32_t stage_mem[4 * Stage<N>::dwords];  // blocks have at most 4 waves
     SSM_LDS uint32_t *stg = (SSM_LDS uint32_t *)stage_mem + (threadIdx.x / 64) * Stage<N>::dwords;
     const int lane = threadIdx.x & 63;
+    const bool pad_wave = __builtin_amdgcn_ballot_w64(!ln.valid) != 0;  // uniform
     const uint32_t nsub = (steps + kSub - 1) / kSub;
     __builtin_amdgcn_s_waitcnt(0);  // the walk's stored states are written before they are read back
     if (nsub > 0) {
@@ -414,14 +415,15 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         // one, so they replace every staged value by 0: x = dt = dy = z = 0 and a zero
         // start state (and a zero adjoint, below) make every term of theirs exactly 0,
         // whatever the staged bits hold, and the channel sums need no mask. Their own
-        // outputs are not stored.
+        // outputs are not stored. The reads are unconditional and the replacement is
+        // taken only by a wave that holds padding lanes (a uniform branch).
         float xv[kSub], dv[kSub], yv[kSub], zv[kSub], start[N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
-            xv[j] = ln.valid ? RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]) : 0.0f;
-            dv[j] = ln.valid ? RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]) : 0.0f;
-            yv[j] = ln.valid ? RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]) : 0.0f;
-            zv[j] = (GATED && ln.valid) ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
+            xv[j] = RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]);
+            dv[j] = RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]);
+            yv[j] = RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]);
+            zv[j] = GATED ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
         }
         if constexpr (N % 4 == 0) {
 #pragma unroll
@@ -433,24 +435,36 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
 #pragma unroll
             for (int n = 0; n < N; ++n) start[n] = __uint_as_float(stg[kStageRows + n * 64 + lane]);
         }
-        if (!ln.valid) {
+        if (pad_wave) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) start[n] = 0.0f;
+            for (int j = 0; j < kSub; ++j) {
+                xv[j] = ln.valid ? xv[j] : 0.0f;
+                dv[j] = ln.valid ? dv[j] : 0.0f;
+                yv[j] = ln.valid ? yv[j] : 0.0f;
+                zv[j] = ln.valid ? zv[j] : 0.0f;
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) start[n] = ln.valid ? start[n] : 0.0f;
         }
         if (k > 0) {
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the LDS reads above are done
             stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, (k - 1) * kSub, kSub,
                                     k > 1 ? a.ckpt + (sub0 + k - 1) * M : hin_row, st_voff, lane);
         }
+        // The sub-chunk's rows of B and C, and of the dB/dC partials, from bases set here
+        // once: the per-step offsets are then constants.
+        const int64_t e_sub = (ln.b * a.L + t0 + j0) * N;
+        const UniRow<IO, N> Bk(a.B, e_sub), Ck(a.C, e_sub);
+        float *pk = pbc + (size_t)(ln.b * a.L + t0 + j0) * pbc_step;
         float hs[kSub][N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
-            const int64_t t = t0 + j0 + (j < (int)ns ? j : 0);
+            const int jr = j < (int)ns ? j : 0;
             const float u = dv[j] * xv[j];
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 const float prev = j == 0 ? start[n] : hs[j - 1][n];
-                hs[j][n] = __builtin_fmaf(e2(dv[j] * A2[n]), prev, u * Bp.ld(t * N + n));
+                hs[j][n] = __builtin_fmaf(e2(dv[j] * A2[n]), prev, u * Bk.ld(jr * N + n));
             }
         }
 #pragma unroll
@@ -459,10 +473,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
             // The next sub-chunk's staging loads were issued before any store still in
             // flight here but this step's: wait for them before its stores.
             if (j == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            const int64_t t = t0 + j0 + j;
             float acc = 0.0f;
 #pragma unroll
-            for (int n = 0; n < N; ++n) acc = __builtin_fmaf(Cp.ld(t * N + n), hs[j][n], acc);
+            for (int n = 0; n < N; ++n) acc = __builtin_fmaf(Ck.ld(j * N + n), hs[j][n], acc);
             const float o = __builtin_fmaf(Dd, xv[j], acc);
             float gp;
             const float dout = gate_grad<GATED>(yv[j], zv[j], gp);
@@ -472,8 +485,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
             float vals[V];
 #pragma unroll
             for (int n = 0; n < N; ++n) {
-                const float bn = Bp.ld(t * N + n);
-                const float lt = __builtin_fmaf(dout, Cp.ld(t * N + n), lam[n]);
+                const float bn = Bk.ld(j * N + n);
+                const float lt = __builtin_fmaf(dout, Ck.ld(j * N + n), lam[n]);
                 const float w = __builtin_fmaf(-u, bn, hs[j][n]);  // a_t h_{t-1}
                 const float q = lt * w;
                 vals[n] = lt * u;                // dB_t[n] term
@@ -492,7 +505,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
             const float tot = wave_reduce_transpose<V>(vals);
             constexpr int sh = 6 - Log2<V>::v;
             if ((lane & ((1 << sh) - 1)) == 0)
-                pbc[(size_t)(ln.b * a.L + t) * pbc_step + (lane >> sh)] = tot;
+                pk[(size_t)j * pbc_step + (lane >> sh)] = tot;
         }
     }
     if (ln.valid) {
