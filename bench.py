@@ -824,7 +824,10 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
                 "frac_issue_slots": round(slot_ach / VALU_PEAK_TLANE, 4),
                 "ceiling_elements_s": round(VALU_PEAK_TLANE * 1e12 / slots, 1),
                 "ceiling_hbm_frac": round(VALU_PEAK_TLANE * 1e12 / slots * info["bytes_per_step"]
-                                          / info["elements_per_step"] / 1e9 / HBM_PEAK_GBS, 4)}}
+                                          / info["elements_per_step"] / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "issue slots charge a transcendental two, as SQ_ACTIVE_INST_VALU does; "
+                        "transcendentals partly overlap other VALU issue, so frac_issue_slots can "
+                        "pass 1 and the slot ceiling is a little below what the chip sustains"}}
     if is_decode:
         cfg = {"workload": shape.name, "n_layers": shape.n_layers, "n_seq": shape.n_seq,
                "d_inner": shape.d_inner, "d_state": shape.d_state, "io": shape.io, "state": "f32",
@@ -863,6 +866,11 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
            "hbm_frac_whole_step": round(whole / HBM_PEAK_GBS, 4),
            "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
            "roofline": roof}
+    if "summary" in info["phases_ms"]:
+        # The chunk summaries walk back only until every state's decay reaches 2^-48, so
+        # their time depends on dt and A: slow decay walks whole chunks.
+        rec["summary_depends_on_inputs"] = ("chunk summaries walk back until the decay reaches "
+                                            "2^-48; slower decay (smaller dt*|A|) walks more of each chunk")
     if mimo:
         rec["mimo_outputs_per_s"] = round(elems_s * mimo, 1)  # R outputs per channel-step
     cpu = None
@@ -1012,6 +1020,8 @@ def main():
         "phases_ms": head["phases_ms"], "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
     }
+    if "summary_depends_on_inputs" in head:
+        out["summary_depends_on_inputs"] = head["summary_depends_on_inputs"]
     if "mimo_outputs_per_s" in head:
         out["mimo_outputs_per_s"] = head["mimo_outputs_per_s"]
     out["hbm_copy_ceiling"] = copy_ceiling(torch)
