@@ -305,10 +305,9 @@ def run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k
     cplx = shape.complex_state
     y = torch.empty_like(d["x"])
     hf = torch.empty((b, Dn, N) + ((2,) if cplx else ()), dtype=torch.float32, device=dev)
-    # (the weighted trapezoidal rescan, like the fused one, is planned for 4 waves per SIMD)
     T = chunk_len or (ssm.ssm_scan_fwd_c64_chunk_len(b, L, Dn, N) if cplx
                       else ssm.ssm_scan_fwd_mimo_chunk_len(b, L, Dn, N, mimo) if mimo
-                      else ssm.ssm_scan_fwd_fused_chunk_len(b, L, Dn, N) if fused or (trap and lam)
+                      else ssm.ssm_scan_fwd_fused_chunk_len(b, L, Dn, N) if fused
                       else ssm.ssm_scan_fwd_chunk_len(b, L, Dn, N))
     ws_n = (ssm.ssm_scan_fwd_c64_workspace(b, L, Dn, N, T) if cplx
             else ssm.ssm_scan_fwd_mimo_workspace(b, L, Dn, N, mimo, T) if mimo

@@ -145,9 +145,10 @@ ssm_status ssm_scan_fwd_noalloc(const void *x, const void *dt, const float *A, c
  * to query the plan assumes MI355X's 256 compute units (1024 SIMDs), uncached. The
  * library cuts the sequence into
  * enough chunks to keep as many waves per SIMD resident as the entry point's rescan
- * kernel is compiled for: 5 for ssm_scan_fwd / _ex / _trap (without lam) and
- * ssm_scan_fwd_mimo up to rank 4, 4 for ssm_scan_fwd_fused, ssm_scan_fwd_c64,
- * ssm_scan_fwd_trap with lam and rank 8 (and the backward).
+ * kernel is compiled for: 5 for ssm_scan_fwd / _ex / _trap (with or without lam),
+ * ssm_scan_fwd_c64 (whose channels take 4 lanes each) and ssm_scan_fwd_mimo up to rank
+ * 4; 4 for ssm_scan_fwd_fused and rank 8 (and the backward). ssm_scan_fwd_trap uses the
+ * plan of ssm_scan_fwd_chunk_len.
  * A plan with fewer chunks needs no more workspace, so ssm_scan_fwd_workspace_ex(...,
  * 0) also suffices for ssm_scan_fwd_fused. */
 int64_t ssm_scan_fwd_chunk_len(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);

@@ -91,10 +91,10 @@ enum class Family { Plain, Fused, Complex, Mimo, Backward, TrapWeighted };
 int32_t waves_per_simd(Family f, int32_t rank = 1) {
     switch (f) {
         case Family::Plain: return 5;     // plain and exponential-trapezoidal rescans
+        case Family::TrapWeighted: return 5;  // its rescan prefetches 2 rows at a time
         case Family::Complex: return 5;
         case Family::Mimo: return rank <= 4 ? 5 : 4;
-        default: return 4;                // input stage, backward, and the
-                                          // exponential-trapezoidal rescan with a weight stream
+        default: return 4;                // input stage, backward
     }
 }
 // Lanes per channel: the complex-state kernels spread a channel's states over 4 lanes
@@ -122,8 +122,8 @@ struct Plan {
 };
 
 // waves_per_simd: what the rescan of the entry point is compiled for (5 for the plain,
-// trapezoidal and MIMO rescans up to rank 4; 4 for the input stage, the complex state,
-// MIMO rank 8 and the backward's own plan).
+// trapezoidal, complex and MIMO rescans up to rank 4; 4 for the input stage, MIMO rank 8
+// and the backward's own plan).
 ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, int64_t chunk_len,
                      bool cplx, Plan *p, int32_t rank = 1, int32_t waves_per_simd = 4) {
     if (batch < 0 || L < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "batch/L must be >= 0 and d_inner >= 1");

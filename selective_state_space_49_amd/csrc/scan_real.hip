@@ -57,6 +57,7 @@ struct NoInput {
     static constexpr bool kTrap = false;
     static constexpr bool kW = false;  // no weight stream
     static constexpr int kWavesPerSimd = 5;
+    static constexpr int kKU = 4;               // rows prefetched per block
     static constexpr bool kRawPrefetch = true;  // see StepIn (ssm_stream.h)
     __device__ __forceinline__ void params(const ScanArgs &, int64_t) {}
     __device__ __forceinline__ void history(const ScanArgs &, int64_t, int64_t, int64_t) {}
@@ -71,7 +72,8 @@ template <typename IO, int KC>
 struct MambaInput {
     static constexpr bool kTrap = false;
     static constexpr bool kW = false;
-    static constexpr int kWavesPerSimd = 4;
+    static constexpr int kWavesPerSimd = 4;  // at five (prefetching 2 rows per block to fit)
+    static constexpr int kKU = 4;            // the extra summary windows cost more than it gains
     static constexpr bool kRawPrefetch = false;
     ConvSilu<(KC > 0 ? KC : 1)> conv;
     float dbias;
@@ -135,7 +137,8 @@ struct TrapInput {
     static constexpr bool kTrap = true;
     static constexpr bool kW = LAM;
     // The weight stream's prefetch buffers spill registers at five waves per SIMD.
-    static constexpr int kWavesPerSimd = LAM ? 4 : 5;
+    static constexpr int kWavesPerSimd = 5;
+    static constexpr int kKU = LAM ? 2 : 4;  // the weight stream's blocks of 4 rows would spill
     static constexpr bool kRawPrefetch = false;
     float xprev;  // x of the step before the current one
     // The weights of the older and the current input for a step of length dv.
@@ -348,8 +351,8 @@ __global__ __launch_bounds__(256) void k_chunk_summary(ScanArgs a) {
 // ---------------------------------------------------------------- rescan + epilogue
 // Compiled for at least In::kWavesPerSimd waves per SIMD, and the planner cuts the
 // sequence into enough chunks to give every SIMD that many: 5 for the plain and the
-// trapezoidal rescan (5 against 4: 6.25 -> 5.88 ms on the 256k rescan), 4 with the
-// input stage, whose registers would spill at 5.
+// trapezoidal rescans (5 against 4: 6.25 -> 5.88 ms on the 256k rescan; with the weight
+// stream, blocks of 2 rows instead of 4 keep it from spilling), 4 with the input stage.
 template <typename IO, int N, bool GATED, typename In>
 __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs a) {
     const LaneId ln = lane_id(a);
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     in.history(a, ln.b, ln.d, t0);
     float bp[N];  // trapezoidal rule: B of the step before, carried from step to step
     if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0, bp);
-    stream_steps_w<IO, GATED, 4, In::kRawPrefetch, In::kW>(xs, dts, zs, lws, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv, float lr) {
+    stream_steps_w<IO, GATED, In::kKU, In::kRawPrefetch, In::kW>(xs, dts, zs, lws, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv, float lr) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
         float acc = 0.0f;
