@@ -22,10 +22,10 @@
 //      decay reaches 2^-kHorizon (the mirror of the forward's horizon);
 //   3. the forward's carry kernel over the chunks in reverse order, seeded with
 //      dh_final: the adjoint entering every chunk from the right;
-//   4. k_bwd_chunk: per chunk, a forward walk from the incoming state that stores the
-//      state every kSub steps, then a backward walk by sub-chunks: each sub-chunk's
-//      kSub states are recomputed into registers from its stored start and the
-//      gradients of its steps emitted. dB_t and dC_t, summed over channels, are reduced
+//   4. k_bwd_walk: per chunk, a forward walk from the incoming state that stores the
+//      state every kSub steps; k_bwd_chunk: per chunk, a backward walk by sub-chunks:
+//      each sub-chunk's kSub states are recomputed into registers from its stored start
+//      and the gradients of its steps emitted. dB_t and dC_t, summed over channels, are reduced
 //      across the 64 lanes of the wave (a transposing butterfly of lane permutations:
 //      2N values over 64 lanes in 2N - 1 exchanges plus the final levels) and stored
 //      per wave;
@@ -291,8 +291,9 @@ __device__ __forceinline__ void row_to_lds(const RowStream<IO> &s, SSM_LDS uint3
 }
 
 // Stage sub-chunk rows j0 .. j0 + kSub - 1 (rows past the chunk's ns read row j0) and
-// the lane's state entering the sub-chunk, at byte st_voff of the [batch][Dn][N] state
-// array st (null: a zero state). Both use buffer loads: the compiler then leaves their
+// the lane's state entering the sub-chunk from the stored states' row st (null: a zero
+// state), in the layout of ckpt_at: at byte st_voff, and for N % 4 == 0 its 16-byte
+// pieces st_qstride bytes apart. Both use buffer loads: the compiler then leaves their
 // waits to the kernel (a global-address load to LDS makes it wait for every store in
 // flight before the next LDS read).
 template <typename IO, int N, bool GATED>
@@ -300,7 +301,7 @@ __device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream
                                           const RowStream<IO> &dts, const RowStream<IO> &dys,
                                           const RowStream<IO> &zs, uint32_t voff, uint32_t rb,
                                           uint32_t j0, uint32_t ns, const float *st,
-                                          uint32_t st_voff, int lane) {
+                                          uint32_t st_voff, uint32_t st_qstride, int lane) {
 #pragma unroll
     for (int j = 0; j < kSub; ++j) {
         const uint32_t r = (j0 + (j < (int)ns ? j : 0)) * rb;
@@ -318,7 +319,7 @@ __device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream
 #pragma unroll
             for (int q = 0; q < N / 4; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSM_LDS void *)(stg + kStageRows + q * 256), 16,
-                                                         st_voff + 16 * q, 0, 0, 0);
+                                                         st_voff, q * st_qstride, 0, 0);
         } else {
 #pragma unroll
             for (int n = 0; n < N; ++n)
@@ -326,6 +327,65 @@ __device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream
                                                          st_voff + 4 * n, 0, 0, 0);
         }
     }
+}
+
+// ---------------------------------------------------------------- stored states
+// Row s of ckpt (M = batch Dn N floats) holds the state entering step kSub s. For
+// N % 4 == 0 a row is laid out [batch][N / 4][Dn][4]: the q-th 16-byte piece of every
+// channel of a wave is one contiguous 1 KB run, so each of a lane's four 16-byte stores
+// and loads covers whole cache lines with the wave's other lanes. Otherwise [batch][Dn][N].
+template <int N>
+__device__ __forceinline__ size_t ckpt_at(int64_t b, int64_t d, int q, int64_t Dn) {
+    return N % 4 == 0 ? ((size_t)(b * (N / 4) + q) * Dn + d) * 4 : (size_t)(b * Dn + d) * N;
+}
+
+// ---------------------------------------------------------------- forward walk
+// Per chunk, a forward walk from the state entering it that stores the state entering
+// every sub-chunk (ckpt), the chunk's own incoming state included. A kernel of its own: inside the gradient
+// kernel, at that kernel's two waves per SIMD, the walk took a third of the backward;
+// alone it keeps many more waves resident. Waves get issue priority by remaining work.
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void k_bwd_walk(BwdArgs a) {
+    const Lane ln = lane_of(a);
+    if (!ln.valid) return;  // no cross-lane work here
+    const int c = blockIdx.y;
+    const int64_t t0 = (int64_t)c * a.T;
+    const uint32_t steps = (uint32_t)(min(a.L, t0 + a.T) - t0);
+    const uint32_t rb = (uint32_t)(a.Dn * sizeof(IO));
+    const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
+    const size_t M = (size_t)a.batch * a.Dn * N;
+    const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
+    const float *hin_row = c == 0 ? a.h0 : a.sumH + (size_t)(c - 1) * M;
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[ln.d * N + n] * kLog2e;
+        h[n] = hin_row ? hin_row[col + n] : 0.0f;
+    }
+    const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
+    const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0);
+    const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
+    const size_t sub0 = (size_t)(t0 / kSub);
+    stream_steps<IO, false, 4, false>(xs, dts, dts, voff, rb, steps, steps, [&](uint32_t i, float xv, float dv, float) {
+        if (i % kSub == 0) {  // the chunk's incoming state too
+            float *row = a.ckpt + (sub0 + i / kSub) * M;
+            if constexpr (N % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < N / 4; ++q) {
+                    const f4v v = {h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+                    *(f4v *)(row + ckpt_at<N>(ln.b, ln.d, q, a.Dn)) = v;
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) row[ckpt_at<N>(ln.b, ln.d, 0, a.Dn) + n] = h[n];
+            }
+        }
+        const int64_t t = t0 + i;
+        const float u = dv * xv;
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * Bp.ld(t * N + n));
+    });
 }
 
 // ---------------------------------------------------------------- gradients
@@ -340,51 +400,30 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const uint32_t voff = (uint32_t)ln.d * (uint32_t)sizeof(IO);
     const size_t M = (size_t)a.batch * a.Dn * N;
     const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
-    const float *hin_row = c == 0 ? a.h0 : a.sumH + (size_t)(c - 1) * M;  // state entering the chunk
-    const float *hin = hin_row ? hin_row + col : nullptr;
-    const uint32_t st_voff = (uint32_t)(col * sizeof(float));  // < 2 GiB (checked on the host)
-    float A2[N], h[N];
+    // the lane's stored states (< 2 GiB per row: checked on the host)
+    const uint32_t st_voff = (uint32_t)(ckpt_at<N>(ln.b, ln.d, 0, a.Dn) * sizeof(float));
+    const uint32_t st_qstride = (uint32_t)(a.Dn * 16);
+    float A2[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         // padding lanes: no decay, so nothing of the clamped channel's A reaches them
         A2[n] = ln.valid ? a.A[ln.d * N + n] * kLog2e : 0.0f;
-        h[n] = hin ? hin[n] : 0.0f;
     }
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
         dys((const IO *)a.dy + row0), zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0);
-    const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
-    const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     const size_t sub0 = (size_t)(t0 / kSub);  // global index of the chunk's first sub-chunk
-    // 1. forward walk, storing the state entering every sub-chunk but the first
-    // Issue priority by remaining work (see set_priority): the walk comes first, then
-    // the sub-chunks count down, so the waves sharing a SIMD finish close together.
-    __builtin_amdgcn_s_setprio(3);
-    // Inputs widened at load: with the raw bits held to the step (as the forward rescans
-    // do) this walk measured about 2% slower over the whole backward.
-    stream_steps<IO, false, 4, false>(xs, dts, dts, voff, rb, steps, 0, [&](uint32_t i, float xv, float dv, float) {
-        if (i > 0 && i % kSub == 0 && ln.valid) {
-            float *ck = a.ckpt + (sub0 + i / kSub) * M + col;
-#pragma unroll
-            for (int n = 0; n < N; ++n) ck[n] = h[n];
-        }
-        const int64_t t = t0 + i;
-        const float u = dv * xv;
-#pragma unroll
-        for (int n = 0; n < N; ++n)
-            h[n] = __builtin_fmaf(e2(dv * A2[n]), h[n], u * Bp.ld(t * N + n));
-    });
-    // 2. backward walk by sub-chunks, each staged in LDS during the previous one
+    // The states entering the chunk's sub-chunks were stored by k_bwd_walk. The walk
+    // by sub-chunks goes backwards, each staged in LDS during the previous one.
     __shared__ uint32_t stage_mem[4 * Stage<N>::dwords];  // blocks have at most 4 waves
     SSM_LDS uint32_t *stg = (SSM_LDS uint32_t *)stage_mem + (threadIdx.x / 64) * Stage<N>::dwords;
     const int lane = threadIdx.x & 63;
     const bool pad_wave = __builtin_amdgcn_ballot_w64(!ln.valid) != 0;  // uniform
     const uint32_t nsub = (steps + kSub - 1) / kSub;
-    __builtin_amdgcn_s_waitcnt(0);  // the walk's stored states are written before they are read back
     if (nsub > 0) {
         const uint32_t k = nsub - 1;
         stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, k * kSub, steps - k * kSub,
-                                k > 0 ? a.ckpt + (sub0 + k) * M : hin_row, st_voff, lane);
+                                a.ckpt + (sub0 + k) * M, st_voff, st_qstride, lane);
     }
     __builtin_amdgcn_s_waitcnt(0);
     const int64_t mu_entry = (int64_t)a.n_chunks - 2 - c;  // adjoint entering from the right
@@ -449,7 +488,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         if (k > 0) {
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the LDS reads above are done
             stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, (k - 1) * kSub, kSub,
-                                    k > 1 ? a.ckpt + (sub0 + k - 1) * M : hin_row, st_voff, lane);
+                                    a.ckpt + (sub0 + k - 1) * M, st_voff, st_qstride, lane);
         }
         // The sub-chunk's rows of B and C, and of the dB/dC partials, from bases set here
         // once: the per-step offsets are then constants.
@@ -601,6 +640,7 @@ hipError_t launch_n(const BwdArgs &a, const ScanArgs &fwd, int io, bool gated, h
         e = launch_carry(r, N, s);
         if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL((k_bwd_walk<IO, N>), dim3(gx, a.n_chunks), blk, 0, s, a);
     if (gated) hipLaunchKernelGGL((k_bwd_chunk<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
     else hipLaunchKernelGGL((k_bwd_chunk<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
     const int64_t nad = a.Dn * (N + 1);
