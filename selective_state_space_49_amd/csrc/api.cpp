@@ -396,6 +396,7 @@ struct BwdPlan {
     size_t off[8];  // byte offsets of sumP, sumH, revQ, revG, ckpt, partA, partD, partBC
     size_t bytes;
     int32_t waves, threads, dblocks;
+    int64_t ck_rows;  // stored-state rows per chunk
 };
 
 size_t ws_round(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -420,8 +421,9 @@ ssm_status make_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_st
     p->waves = p->dblocks * (p->threads / 64);
     const size_t M = (size_t)batch * d_inner * d_state * sizeof(float);
     const size_t C = (size_t)p->fwd.n_chunks;
+    p->ck_rows = (std::min<int64_t>(p->fwd.T, L) + 2 * ssm::kSub - 1) / (2 * ssm::kSub);
     const size_t sizes[8] = {(C - 1) * M, (C - 1) * M, (C - 1) * M, (C - 1) * M,
-                             (size_t)((L + ssm::kSub - 1) / ssm::kSub) * M, C * M,
+                             C * (size_t)p->ck_rows * M, C * M,
                              C * (size_t)batch * d_inner * sizeof(float),
                              (size_t)batch * L * p->waves * 2 * d_state * sizeof(float)};
     size_t at = 0;
@@ -489,6 +491,7 @@ ssm_status bwd_common(const void *x, const void *dt, const float *A, const void 
     a.batch = batch; a.L = L; a.Dn = d_inner; a.T = plan.fwd.T;
     a.n_chunks = plan.fwd.n_chunks; a.dblocks = plan.dblocks; a.threads = plan.threads;
     a.waves = plan.waves;
+    a.ck_rows = plan.ck_rows;
     const int iot = io == SSM_BF16 ? 1 : 0;
     return launch_status(ssm::launch_scan_bwd(a, f, iot, d_state, z != nullptr, s), "backward launch");
 }

@@ -274,7 +274,8 @@ __global__ __launch_bounds__(256) void k_bwd_summary(BwdArgs a) {
 // The compiler does not order these loads against LDS reads, so the kernel waits
 // explicitly: vmcnt(0) before the LDS is read, lgkmcnt(0) before it is refilled.
 #define SSM_LDS __attribute__((address_space(3)))
-constexpr int kStageRows = 4 * kSub * 64;
+constexpr int kPair = 2 * kSub;               // rows staged at a time: two pieces
+constexpr int kStageRows = 4 * kPair * 64;
 template <int N> struct Stage { static constexpr int dwords = kStageRows + N * 64; };
 
 typedef float f4v __attribute__((ext_vector_type(4)));
@@ -290,10 +291,10 @@ __device__ __forceinline__ void row_to_lds(const RowStream<IO> &s, SSM_LDS uint3
         __builtin_amdgcn_raw_ptr_buffer_load_lds(s.r, (SSM_LDS void *)dst, 4, voff, soff, 0, 0);
 }
 
-// Stage sub-chunk rows j0 .. j0 + kSub - 1 (rows past the chunk's ns read row j0) and
-// the lane's state entering the sub-chunk from the stored states' row st (null: a zero
-// state), in the layout of ckpt_at: at byte st_voff, and for N % 4 == 0 its 16-byte
-// pieces st_qstride bytes apart. Both use buffer loads: the compiler then leaves their
+// Stage the rows j0 .. j0 + kPair - 1 of a pair of pieces (rows past the chunk's ns
+// read row j0) and the lane's state entering the pair from the stored states' row st
+// (null: a zero state), in the layout of ckpt_at: at byte st_voff, and for N % 4 == 0
+// its 16-byte pieces st_qstride bytes apart. Both use buffer loads: the compiler then leaves their
 // waits to the kernel (a global-address load to LDS makes it wait for every store in
 // flight before the next LDS read).
 template <typename IO, int N, bool GATED>
@@ -303,12 +304,12 @@ __device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream
                                           uint32_t j0, uint32_t ns, const float *st,
                                           uint32_t st_voff, uint32_t st_qstride, int lane) {
 #pragma unroll
-    for (int j = 0; j < kSub; ++j) {
+    for (int j = 0; j < kPair; ++j) {
         const uint32_t r = (j0 + (j < (int)ns ? j : 0)) * rb;
-        row_to_lds<IO>(xs, stg + (0 * kSub + j) * 64, voff, r);
-        row_to_lds<IO>(dts, stg + (1 * kSub + j) * 64, voff, r);
-        row_to_lds<IO>(dys, stg + (2 * kSub + j) * 64, voff, r);
-        if (GATED) row_to_lds<IO>(zs, stg + (3 * kSub + j) * 64, voff, r);
+        row_to_lds<IO>(xs, stg + (0 * kPair + j) * 64, voff, r);
+        row_to_lds<IO>(dts, stg + (1 * kPair + j) * 64, voff, r);
+        row_to_lds<IO>(dys, stg + (2 * kPair + j) * 64, voff, r);
+        if (GATED) row_to_lds<IO>(zs, stg + (3 * kPair + j) * 64, voff, r);
     }
     if (!st) {
 #pragma unroll
@@ -330,7 +331,10 @@ __device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream
 }
 
 // ---------------------------------------------------------------- stored states
-// Row s of ckpt (M = batch Dn N floats) holds the state entering step kSub s. For
+// Row c R + p of ckpt (M = batch Dn N floats, R = ck_rows rows per chunk) holds the state
+// entering step kPair p of chunk c: every second piece's start is stored, and the other
+// piece's start is recomputed from it (half the stored bytes, for one more 4-step walk
+// per two pieces in the gradient kernel). For
 // N % 4 == 0 a row is laid out [batch][N / 4][Dn][4]: the q-th 16-byte piece of every
 // channel of a wave is one contiguous 1 KB run, so each of a lane's four 16-byte stores
 // and loads covers whole cache lines with the wave's other lanes. Otherwise [batch][Dn][N].
@@ -341,7 +345,7 @@ __device__ __forceinline__ size_t ckpt_at(int64_t b, int64_t d, int q, int64_t D
 
 // ---------------------------------------------------------------- forward walk
 // Per chunk, a forward walk from the state entering it that stores the state entering
-// every sub-chunk (ckpt), the chunk's own incoming state included. A kernel of its own: inside the gradient
+// every pair of pieces (ckpt), the chunk's own incoming state included. A kernel of its own: inside the gradient
 // kernel, at that kernel's two waves per SIMD, the walk took a third of the backward;
 // alone it keeps many more waves resident. Waves get issue priority by remaining work.
 template <typename IO, int N>
@@ -365,10 +369,10 @@ __global__ __launch_bounds__(256) void k_bwd_walk(BwdArgs a) {
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0);
     const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
-    const size_t sub0 = (size_t)(t0 / kSub);
+    const size_t row0c = (size_t)c * a.ck_rows;  // the chunk's first row of stored states
     stream_steps<IO, false, 4, false>(xs, dts, dts, voff, rb, steps, steps, [&](uint32_t i, float xv, float dv, float) {
-        if (i % kSub == 0) {  // the chunk's incoming state too
-            float *row = a.ckpt + (sub0 + i / kSub) * M;
+        if (i % kPair == 0) {  // the chunk's incoming state too
+            float *row = a.ckpt + (row0c + i / kPair) * M;
             if constexpr (N % 4 == 0) {
 #pragma unroll
                 for (int q = 0; q < N / 4; ++q) {
@@ -412,18 +416,18 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
         dys((const IO *)a.dy + row0), zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0);
-    const size_t sub0 = (size_t)(t0 / kSub);  // global index of the chunk's first sub-chunk
-    // The states entering the chunk's sub-chunks were stored by k_bwd_walk. The walk
-    // by sub-chunks goes backwards, each staged in LDS during the previous one.
+    const size_t row0c = (size_t)c * a.ck_rows;  // the chunk's first row of stored states
+    // The states entering every second piece were stored by k_bwd_walk. The walk by
+    // pieces goes backwards; each pair of pieces is staged in LDS during the pair after it.
     __shared__ uint32_t stage_mem[4 * Stage<N>::dwords];  // blocks have at most 4 waves
     SSM_LDS uint32_t *stg = (SSM_LDS uint32_t *)stage_mem + (threadIdx.x / 64) * Stage<N>::dwords;
     const int lane = threadIdx.x & 63;
     const bool pad_wave = __builtin_amdgcn_ballot_w64(!ln.valid) != 0;  // uniform
     const uint32_t nsub = (steps + kSub - 1) / kSub;
     if (nsub > 0) {
-        const uint32_t k = nsub - 1;
-        stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, k * kSub, steps - k * kSub,
-                                a.ckpt + (sub0 + k) * M, st_voff, st_qstride, lane);
+        const uint32_t pp = (nsub - 1) / 2;
+        stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, pp * kPair, steps - pp * kPair,
+                                a.ckpt + (row0c + pp) * M, st_voff, st_qstride, lane);
     }
     __builtin_amdgcn_s_waitcnt(0);
     const int64_t mu_entry = (int64_t)a.n_chunks - 2 - c;  // adjoint entering from the right
@@ -447,22 +451,22 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
         set_priority(k + 1, nsub);
         const uint32_t j0 = k * kSub;
         const uint32_t ns = min((uint32_t)kSub, steps - j0);
+        const int half = (int)(k & 1u);  // the piece's place in its staged pair
         // The staged rows and state (complete: the last wait on vmcnt came after their
-        // loads were issued; the state is the stored one, or the chunk's incoming state
-        // for the first sub-chunk). Padding lanes stage their clamped channel's rows and
-        // stored states, which another wave writes without any ordering against this
-        // one, so they replace every staged value by 0: x = dt = dy = z = 0 and a zero
-        // start state (and a zero adjoint, below) make every term of theirs exactly 0,
+        // loads were issued). Padding lanes stage their clamped channel's rows and
+        // states, so they replace every staged value by 0: x = dt = dy = z = 0 and a zero
+        // start state (and a zero adjoint, above) make every term of theirs exactly 0,
         // whatever the staged bits hold, and the channel sums need no mask. Their own
         // outputs are not stored. The reads are unconditional and the replacement is
         // taken only by a wave that holds padding lanes (a uniform branch).
         float xv[kSub], dv[kSub], yv[kSub], zv[kSub], start[N];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
-            xv[j] = RowStream<IO>::widen(stg[(0 * kSub + j) * 64 + lane]);
-            dv[j] = RowStream<IO>::widen(stg[(1 * kSub + j) * 64 + lane]);
-            yv[j] = RowStream<IO>::widen(stg[(2 * kSub + j) * 64 + lane]);
-            zv[j] = GATED ? RowStream<IO>::widen(stg[(3 * kSub + j) * 64 + lane]) : 0.0f;
+            const int row = half * kSub + j;
+            xv[j] = RowStream<IO>::widen(stg[(0 * kPair + row) * 64 + lane]);
+            dv[j] = RowStream<IO>::widen(stg[(1 * kPair + row) * 64 + lane]);
+            yv[j] = RowStream<IO>::widen(stg[(2 * kPair + row) * 64 + lane]);
+            zv[j] = GATED ? RowStream<IO>::widen(stg[(3 * kPair + row) * 64 + lane]) : 0.0f;
         }
         if constexpr (N % 4 == 0) {
 #pragma unroll
@@ -485,10 +489,29 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
 #pragma unroll
             for (int n = 0; n < N; ++n) start[n] = ln.valid ? start[n] : 0.0f;
         }
-        if (k > 0) {
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the LDS reads above are done
-            stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, (k - 1) * kSub, kSub,
-                                    a.ckpt + (sub0 + k - 1) * M, st_voff, st_qstride, lane);
+        if (half) {
+            // The second piece of a pair starts where the first ends: walk the first
+            // piece (whole, since a later one exists) from the pair's stored state.
+            const UniRow<IO, N> Bw(a.B, (ln.b * a.L + t0 + j0 - kSub) * N);
+#pragma unroll
+            for (int j = 0; j < kSub; ++j) {
+                float x0 = RowStream<IO>::widen(stg[(0 * kPair + j) * 64 + lane]);
+                float d0 = RowStream<IO>::widen(stg[(1 * kPair + j) * 64 + lane]);
+                if (pad_wave) {
+                    x0 = ln.valid ? x0 : 0.0f;
+                    d0 = ln.valid ? d0 : 0.0f;
+                }
+                const float u0 = d0 * x0;
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    start[n] = __builtin_fmaf(e2(d0 * A2[n]), start[n], u0 * Bw.ld(j * N + n));
+            }
+        } else if (k > 0) {
+            // the pair's last reads are done: stage the pair before it
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            const uint32_t pp = k / 2 - 1;
+            stage_sub<IO, N, GATED>(stg, xs, dts, dys, zs, voff, rb, pp * kPair, kPair,
+                                    a.ckpt + (row0c + pp) * M, st_voff, st_qstride, lane);
         }
         // The sub-chunk's rows of B and C, and of the dB/dC partials, from bases set here
         // once: the per-step offsets are then constants.
@@ -509,8 +532,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
 #pragma unroll
         for (int j = kSub - 1; j >= 0; --j) {
             if (j >= (int)ns) continue;  // uniform: every lane of the block has the same ns
-            // The next sub-chunk's staging loads were issued before any store still in
-            // flight here but this step's: wait for them before its stores.
+            // The next pair's staging loads were issued before any store still in flight
+            // here but this step's: wait for them before its stores.
             if (j == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
             float acc = 0.0f;
 #pragma unroll

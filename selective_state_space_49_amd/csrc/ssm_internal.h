@@ -115,13 +115,14 @@ struct BwdArgs {
     float *revQ;    // reverse summaries, reversed chunk order: entry j is chunk n_chunks-1-j
     float *revG;    //   (decay over the chunk, adjoint passed left from a zero carry-in); after
                     //   the reverse carry revG[j] = adjoint entering chunk n_chunks-2-j from the right
-    float *ckpt;    // states every kSub steps   [ceil(L / kSub)][batch][Dn][N]
+    float *ckpt;    // states every 2 kSub steps [n_chunks][ck_rows] rows of batch Dn N floats
     float *partA;   // per-chunk dA              [n_chunks][batch][Dn][N]
     float *partD;   // per-chunk dD              [n_chunks][batch][Dn]
     float *partBC;  // per-wave dB, dC           [batch][L][waves][2N]
     int64_t batch, L, Dn;
     int64_t T;
     int32_t n_chunks, dblocks, threads, waves;  // waves = channel waves per batch row
+    int64_t ck_rows;  // stored-state rows per chunk: ceil(min(T, L) / (2 kSub))
 };
 constexpr int kSub = 4;  // steps per recomputed sub-chunk of the backward
 hipError_t launch_scan_bwd(const BwdArgs &a, const ScanArgs &fwd, int io, int d_state, bool gated,
