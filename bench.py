@@ -186,7 +186,7 @@ def decode_bytes(s, io_bytes: int) -> float:
 def backward_bytes(s, io_bytes: int) -> float:
     """Backward, each input read once and each gradient written once: x, dt, z, dy read,
     dx, ddt, dz written; B, C read and dB, dC (fp32) written; A, D, dA, dD. The states
-    stored every 4 steps and read back are traffic of the method, not of the algorithm."""
+    stored every 8 steps and read back are traffic of the method, not of the algorithm."""
     b, L, Dn, N = s.batch, s.L, s.d_inner, s.d_state
     streams = 3 + 2 * (1 if s.gated else 0) + 1 + 1          # x, dt, (z), dy / dx, ddt, (dz)
     return (b * L * Dn * streams * io_bytes + 2 * b * L * N * (io_bytes + 4)

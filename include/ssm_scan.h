@@ -296,9 +296,9 @@ ssm_status ssm_step_fused_replay(float *h, void *conv_state, const void *x_t, co
  * gate, a_t = exp(dt_t A)).
  * The states are recomputed: chunked as in the forward (the same decay-horizon
  * truncation, applied to the state and, mirrored, to the adjoint), with the state
- * stored every 4 steps in the workspace and each 4-step piece recomputed in
+ * stored every 8 steps in the workspace and each 4-step piece recomputed in
  * registers. The workspace (ssm_scan_bwd_workspace bytes, 256-byte aligned) holds
- * those states (16 bytes per element and state at fp32) and per-chunk and per-wave
+ * those states (8 bytes per element at N = 16, fp32) and per-chunk and per-wave
  * partial sums; dA, dB, dC and dD are reduced from them in a fixed order, so results
  * are deterministic. chunk_len: as in ssm_scan_fwd_ex (rounded down to a multiple of
  * 4 when there are several chunks). L == 0: dA = dD = 0, dh0 = dh_final (or 0).

@@ -252,7 +252,7 @@ def test_backward_argument_errors(lib):
     assert _bwd_raw(lib, dB=0x1002) == ALIGN
     assert _bwd_raw(lib, io=1, dx=0x1001) == ALIGN
     assert _bwd_raw(lib, Dn=0) == SHAPE
-    # several chunks need the workspace: states every 4 steps and the partial sums
+    # several chunks need the workspace: states every 8 steps and the partial sums
     need = ssm.ssm_scan_bwd_workspace(1, 200, 4, 4, 64)
     assert need > ssm.ssm_scan_fwd_workspace_ex(1, 200, 4, 4, 64)
     assert _bwd_raw(lib, L=200, chunk=64) == WS
