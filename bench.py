@@ -39,7 +39,8 @@ softplus run inside the scan's load stage (decode: with the carried conv state).
 per-step weight stream), --mimo R the MIMO ones (rank-R
 inputs and outputs per channel; elements stay channel-steps, each with R outputs).
 --backward times ssm_scan_bwd on a prefill workload, and with --fused ssm_scan_bwd_fused
-(the gradients through the input stage as well). --one-call times the decode as one call
+(the gradients through the input stage as well), with --saved ssm_scan_bwd_saved from the
+states ssm_scan_fwd_save stored (that forward timed apart). --one-call times the decode as one call
 over all layers per token instead of one call per layer.
 """
 from __future__ import annotations
@@ -193,10 +194,11 @@ def backward_bytes(s, io_bytes: int) -> float:
             + 2 * Dn * (N + 1) * 4)
 
 
-def backward_lane_ops(s) -> float:
-    """VALU instructions per element of the gradient kernel: a forward walk storing the
-    states (4 per state + dt*x and widening), the recomputation of each 4-step piece (the
-    same), and the backward step (12 per state: exp argument, exp, lam, a h, lam a h,
+def backward_lane_ops(s, saved=False) -> float:
+    """VALU instructions per element of the backward: a forward walk storing the states
+    every 8 steps (4 per state + dt*x and widening; none with the training forward's
+    states), the recomputation of each 4-step piece (the same, and once more for every
+    second piece, whose start is not stored), and the backward step (12 per state: exp argument, exp, lam, a h, lam a h,
     dB and dC terms, B.lam, A.lam a h, dA, lam a, C.h; plus about 20 per element for the
     gate's derivative, dx, ddt, dz and conversions), plus the sums of dB and dC over the
     wave (2N values over 64 lanes: 2N - 1 exchanges of two or three instructions plus the
@@ -204,7 +206,7 @@ def backward_lane_ops(s) -> float:
     N = s.d_state
     walk = 4 * N + 3
     bfly = {1: 6, 2: 8, 4: 15, 8: 33, 16: 70}[N]
-    return 2 * walk + 12 * N + 20 + bfly
+    return (0 if saved else walk) + 1.5 * walk + 12 * N + 20 + bfly
 
 
 def decode_lane_ops(s) -> float:
@@ -219,10 +221,13 @@ def decode_lane_ops(s) -> float:
 
 
 # ----------------------------------------------------------------- runs
-def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None):
+def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_k=None,
+                 saved=False):
     """One step = one ssm_scan_bwd call over the workload (dy ~ N(0, 1) in the I/O dtype);
     with conv_k, one ssm_scan_bwd_fused call (the input stage of a conv_k-tap filter:
-    x and dt of the workload are then the raw x_in and dt_raw)."""
+    x and dt of the workload are then the raw x_in and dt_raw). saved: one
+    ssm_scan_bwd_saved call from the states one ssm_scan_fwd_save call stored (that
+    forward is timed too, apart, and reported beside the backward)."""
     dev = "cuda"
     log("drawing inputs for", shape.name, "(backward)")
     d = workloads.make_scan_inputs(shape, dev)
@@ -234,13 +239,43 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         d.update(workloads.make_input_stage(shape, conv_k, dev))
         io = 1 if shape.io == "bf16" else 0
         need = ssm.ssm_scan_bwd_fused_workspace(b, L, Dn, N, conv_k, io, chunk_len)
+    elif saved:
+        need = ssm.ssm_scan_bwd_saved_workspace(b, L, Dn, N, chunk_len)
     else:
         need = ssm.ssm_scan_bwd_workspace(b, L, Dn, N, chunk_len)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     log("backward workspace", ws.numel() / 1e9, "GB")
     out = {}
+    fwd_ms = None
+    if saved:
+        states = torch.empty(ssm._states_shape(b, L, Dn, N), dtype=torch.float32, device=dev)
+        log("stored states", states.numel() * 4 / 1e9, "GB")
+        fws = torch.empty(max(ssm.ssm_scan_fwd_save_workspace(b, L, Dn, N, chunk_len), 1),
+                          dtype=torch.uint8, device=dev)
+        yb = torch.empty_like(d["x"])
+
+        def fwd():
+            ssm.ssm_scan_fwd_save(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], y=yb,
+                                  states=states, chunk_len=chunk_len, workspace=fws)
+        for _ in range(max(warmup, 1)):
+            fwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fwd()
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_ms = e0.elapsed_time(e1) / steps
+        log("forward with stored states", round(fwd_ms, 4), "ms")
 
     def call():
+        if saved:
+            r = ssm.ssm_scan_bwd_saved(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                       states=states, dy=dy, chunk_len=chunk_len, workspace=ws,
+                                       out=out, want_dh0=False)
+            out.update(r)
+            return
         if fused:
             ssm.ssm_scan_bwd_fused(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                    conv_w=d["conv_w"], conv_b=d["conv_b"], conv_state0=d["conv_state0"],
@@ -266,7 +301,7 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1) / steps
     io_bytes = 2 if shape.io == "bf16" else 4
-    nbytes, lane_ops = backward_bytes(shape, io_bytes), backward_lane_ops(shape)
+    nbytes, lane_ops = backward_bytes(shape, io_bytes), backward_lane_ops(shape, saved)
     if fused:
         # recompute of u, dt (x_in, dt_raw read; u, dt written) and the chain rule (x_in,
         # dt_raw, du, ddt read; dx_in, ddt_raw written): 10 more streams; the input stage
@@ -274,12 +309,16 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         # (exp, add, rcp, sub, fma, 2 mul) and softplus' (add, mul, exp, add, rcp, mul, add)
         nbytes += 10 * shape.elements * io_bytes
         lane_ops += input_stage_lane_ops(conv_k) + 3 * conv_k + 14
+    phases = {"backward_call": gpu_ms}
+    if saved:
+        phases["forward_with_stored_states"] = fwd_ms
     info = {
-        "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": {"backward_call": gpu_ms},
+        "wall_s": wall, "ms_per_step": wall / steps * 1e3, "phases_ms": phases,
         "elements_per_step": shape.elements, "bytes_per_step": nbytes,
         "lane_ops_per_elem": lane_ops, "chunk_len": chunk_len,
         "n_chunks": None, "dominant_ms": gpu_ms, "gpu_ms": gpu_ms,
-        "kernel": "ssm_scan_bwd_fused (all launches)" if fused else "ssm_scan_bwd (all launches)",
+        "kernel": "ssm_scan_bwd_fused (all launches)" if fused else
+                  "ssm_scan_bwd_saved (all launches)" if saved else "ssm_scan_bwd (all launches)",
         "source": "bwd",
     }
     return info, d
@@ -784,13 +823,15 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
     is_decode = isinstance(shape, workloads.DecodeShape)
     conv_k, trap, mimo, backward = (variant.get("conv_k"), variant.get("trap", False),
                                     variant.get("mimo", 0), variant.get("backward", False))
+    saved = backward and variant.get("saved", False)
     lam = trap and variant.get("lam", False)
     steps = max(1, steps if not is_decode else min(steps, 64))
     if is_decode:
         info, d = run_decode(shape, steps, warmup, torch, ssm, workloads, graph=graph, conv_k=conv_k,
                              trap=trap, mimo=mimo, one_call=one_call, lam=lam)
     elif backward:
-        info, d = run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k)
+        info, d = run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k,
+                               saved=saved)
     else:
         info, d = run_prefill(shape, steps, warmup, torch, ssm, workloads, chunk_len, conv_k,
                               trap=trap, mimo=mimo, lam=lam)
@@ -803,7 +844,8 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
     alu_ach = info["elements_per_step"] * lane_ops / dom_s / 1e12
     slot_ach = info["elements_per_step"] * slots / dom_s / 1e12
     traffic_key = name + (f"+input_stage_k{conv_k}" if conv_k is not None else "") + \
-        ("+backward" if backward else "") + ("+trap" if trap else "") + ("_lam" if lam else "") + \
+        ("+backward" if backward else "") + ("_saved" if saved else "") + ("+trap" if trap else "") + \
+        ("_lam" if lam else "") + \
         (f"+mimo{mimo}" if mimo else "") + ("+one_call" if is_decode and one_call else "")
     # The metric names the HBM roofline: it is the headline bound for every workload;
     # the vector-ALU issue ceiling, which the bf16 and complex prefills reach first, is
@@ -851,6 +893,8 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
         if backward:
             cfg["pass"] = ("backward through the input stage (ssm_scan_bwd_fused: dx_in, ddt_raw, dconv_w, "
                            "dconv_b, ddt_bias, dz, dA, dB, dC, dD)" if conv_k is not None else
+                           "backward from the training forward's stored states (ssm_scan_bwd_saved: "
+                           "dx, ddt, dz, dA, dB, dC, dD)" if saved else
                            "backward (ssm_scan_bwd: dx, ddt, dz, dA, dB, dC, dD)")
         if trap:
             cfg["discretisation"] = "exponential-trapezoidal (ssm_scan_fwd_trap)"
@@ -951,6 +995,9 @@ def main():
                          "(1, 2, 4 or 8)")
     ap.add_argument("--backward", action="store_true",
                     help="time ssm_scan_bwd (gradients of the prefill) on the prefill workload")
+    ap.add_argument("--saved", action="store_true",
+                    help="with --backward: ssm_scan_bwd_saved from ssm_scan_fwd_save's stored "
+                         "states (the forward timed apart)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -979,7 +1026,8 @@ def main():
         return
     ssm.load_library()
     variant = {"conv_k": args.conv_k if args.fused else None, "trap": args.trap, "mimo": args.mimo,
-               "backward": args.backward, "lam": args.trap_weight == "random"}
+               "backward": args.backward, "lam": args.trap_weight == "random",
+               "saved": args.saved}
     is_variant = args.fused or args.trap or args.mimo or args.backward
     names = [args.workload] if args.workload else ([HEADLINE] if is_variant else ALL_WORKLOADS)
     for n in names:

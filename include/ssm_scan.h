@@ -315,6 +315,43 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
                         ssm_dtype io, int64_t chunk_len, void *workspace,
                         size_t workspace_bytes, void *hip_stream);
 
+/* Training with stored states: ssm_scan_fwd_save is ssm_scan_fwd_ex that also writes the
+ * state entering every 8th step to `states` (caller-owned device memory of
+ * ssm_scan_fwd_save_states_bytes: ceil(L / 8) rows of batch * d_inner * d_state fp32, row
+ * r the state entering step 8 r, row 0 h0 or zeros; within a row, for d_state a multiple
+ * of 4, [batch][d_state / 4][d_inner][4], else [batch][d_inner][d_state]). y and h_final
+ * equal ssm_scan_fwd_ex's bit for bit for the same chunk length; with several chunks the
+ * chunk length is rounded down to a multiple of 8 (at least 8), and the workspace is
+ * ssm_scan_fwd_save_workspace bytes. ssm_scan_bwd_saved is ssm_scan_bwd given those
+ * states instead of h0: it reads them where ssm_scan_bwd recomputes them by a forward
+ * walk of every chunk (the forward's chunk summaries, the carry over them and that walk
+ * are skipped), and its workspace (ssm_scan_bwd_saved_workspace) holds no states; its
+ * chunk length is rounded the same way. The states must come from ssm_scan_fwd_save on
+ * the same x, dt, A, B and h0 and be unchanged since. The stored states (8 bytes per
+ * element at d_state = 16) cost the forward their writes; the backward saves its walk:
+ * at batch 1, L = 262144, d_inner = 8192 they are 17 GB. SSM_ERR_UNSUPPORTED when a state
+ * row (batch * d_inner * d_state * 4 bytes) is 2 GiB or more; SSM_ERR_NULL without
+ * states (L > 0); states 16-byte aligned, other arguments as in ssm_scan_fwd_ex and
+ * ssm_scan_bwd. Floating point: the backward reads the states the forward computed, so
+ * its gradients agree with ssm_scan_bwd's to rounding, not bit for bit. */
+size_t ssm_scan_fwd_save_states_bytes(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state);
+size_t ssm_scan_fwd_save_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                   int64_t chunk_len);
+ssm_status ssm_scan_fwd_save(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, const float *h0,
+                             void *y, float *h_final, float *states, int64_t batch, int64_t L,
+                             int64_t d_inner, int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+size_t ssm_scan_bwd_saved_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                    int64_t chunk_len);
+ssm_status ssm_scan_bwd_saved(const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *states,
+                              const void *dy, const float *dh_final, void *dx, void *ddt, void *dz,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0, int64_t batch,
+                              int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                              int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                              void *hip_stream);
+
 /* ssm_scan_bwd_fused: gradients of ssm_scan_fwd_fused's prefill, for training: the
  * backward above on u = silu(conv(x_in)) and dt = softplus(dt_raw + dt_bias), then the
  * chain rule back through the input stage ("【大模型】- Jamba 混合 SSM-Transformer",
@@ -506,7 +543,7 @@ ssm_status ssm_scan_fwd_mimo_profiled(const void *x, const void *dt, const float
 /* ------------------------------------------------------------------ misc */
 const char *ssm_status_str(ssm_status s);   /* static string, never NULL */
 const char *ssm_last_error(void);           /* this thread's last detail, "" if none */
-int32_t ssm_abi_version(void);              /* 2 */
+int32_t ssm_abi_version(void);              /* 3 */
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,8 @@ __all__ = [
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
     "ssm_scan_fwd_mimo_chunk_len", "selective_scan", "selective_scan_fused",
     "ssm_scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "ssm_scan_fwd_save", "ssm_scan_fwd_save_workspace", "ssm_scan_fwd_save_states_bytes",
+    "ssm_scan_bwd_saved", "ssm_scan_bwd_saved_workspace", "STATE_EVERY",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,7 +51,11 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_mimo", "ssm_scan_fwd_mimo_profiled", "ssm_scan_fwd_mimo_workspace",
     "ssm_step_mimo", "ssm_scan_fwd_fused_chunk_len", "ssm_scan_fwd_c64_chunk_len",
     "ssm_scan_fwd_mimo_chunk_len", "ssm_scan_fwd_noalloc",
+    "ssm_scan_fwd_save", "ssm_scan_fwd_save_workspace", "ssm_scan_fwd_save_states_bytes",
+    "ssm_scan_bwd_saved", "ssm_scan_bwd_saved_workspace",
 ]
+# Steps between the states ssm_scan_fwd_save stores for ssm_scan_bwd_saved.
+STATE_EVERY = 8
 # SSM_NOALLOC_SCRATCH_BYTES of ssm_scan.h: the scratch ssm_scan_fwd_noalloc has per GPU.
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -104,6 +110,11 @@ def load_library():
     sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
     sig["ssm_scan_bwd_workspace"] = ([i64, i64, i64, i32, i64], sz)
     sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    sig["ssm_scan_bwd_saved"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    sig["ssm_scan_bwd_saved_workspace"] = ([i64, i64, i64, i32, i64], sz)
+    sig["ssm_scan_fwd_save"] = ([vp] * 11 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    sig["ssm_scan_fwd_save_workspace"] = ([i64, i64, i64, i32, i64], sz)
+    sig["ssm_scan_fwd_save_states_bytes"] = ([i64, i64, i64, i32], sz)
     sig["ssm_scan_bwd_fused_workspace"] = ([i64, i64, i64, i32, i32, ci, i64], sz)
     sig["ssm_scan_bwd_fused"] = ([vp] * 10 + [i32] + [vp] * 16 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     trap = [vp] * 13 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
@@ -258,6 +269,54 @@ def ssm_scan_fwd_ex(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, 
     """Prefill with an explicit chunk length (0 = the library's choice)."""
     return _scan("ssm_scan_fwd_ex", False, x, dt, A, B, C, D, z, h0, chunk_len, y, h_final,
                  workspace, want_h_final)
+
+
+def _states_shape(b, L, Dn, N):
+    """The stored states' layout (ssm_scan.h): ceil(L / 8) rows; in a row [b][N/4][Dn][4]
+    for N a multiple of 4, else [b][Dn][N]."""
+    rows = (L + STATE_EVERY - 1) // STATE_EVERY
+    return (rows, b, N // 4, Dn, 4) if N % 4 == 0 else (rows, b, Dn, N)
+
+
+def ssm_scan_fwd_save_states_bytes(batch, L, d_inner, d_state) -> int:
+    return int(load_library().ssm_scan_fwd_save_states_bytes(batch, L, d_inner, d_state))
+
+
+def ssm_scan_fwd_save_workspace(batch, L, d_inner, d_state, chunk_len=0) -> int:
+    return int(load_library().ssm_scan_fwd_save_workspace(batch, L, d_inner, d_state, chunk_len))
+
+
+def ssm_scan_fwd_save(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, h_final=None,
+                      states=None, workspace=None):
+    """The training forward: ssm_scan_fwd_ex's y and h_final, and the state entering every
+    8th step (float32, shaped as _states_shape) for ssm_scan_bwd_saved."""
+    lib = load_library()
+    b, L, Dn = x.shape
+    N = A.shape[1]
+    f32 = torch.float32
+    _dev(x, "x"); _dev(dt, "dt", (b, L, Dn)); _dev(z, "z", (b, L, Dn))
+    _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
+    _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N)); _dev(h0, "h0", (b, Dn, N), f32)
+    io = _io(x, dt, z, B, C)
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", (b, L, Dn), x.dtype)
+    if h_final is None:
+        h_final = torch.empty((b, Dn, N), dtype=f32, device=dev)
+    _dev(h_final, "h_final", (b, Dn, N), f32)
+    if states is None:
+        states = torch.empty(_states_shape(b, L, Dn, N), dtype=f32, device=dev)
+    _dev(states, "states", _states_shape(b, L, Dn, N), f32)
+    need = ssm_scan_fwd_save_workspace(b, L, Dn, N, chunk_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssm_scan_fwd_save(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(h0), _ptr(y), _ptr(h_final), _ptr(states), b, L, Dn, N, io,
+                               chunk_len, _ptr(workspace), ws_bytes, _stream(x))
+    _check(st)
+    return y, h_final, states
 
 
 def ssm_scan_fwd_noalloc(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, y=None, h_final=None,
@@ -547,6 +606,24 @@ def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk
     Returns a dict: dx, ddt, dz (io dtype, dz None when ungated or not wanted), dA, dB, dC,
     dD, dh0 (float32; dh0 None when not wanted). out: an optional dict of preallocated
     outputs with those names."""
+    return _bwd("ssm_scan_bwd", x, dt, A, B, C, D, z, h0, None, dy, dh_final, chunk_len, want_dz,
+                want_dh0, workspace, out)
+
+
+def ssm_scan_bwd_saved_workspace(batch, L, d_inner, d_state, chunk_len=0) -> int:
+    return int(load_library().ssm_scan_bwd_saved_workspace(batch, L, d_inner, d_state, chunk_len))
+
+
+def ssm_scan_bwd_saved(x, dt, A, B, C, D, z=None, *, states, dy, dh_final=None, chunk_len=0,
+                       want_dz=True, want_dh0=True, workspace=None, out=None):
+    """ssm_scan_bwd with the states ssm_scan_fwd_save stored (see ssm_scan.h); the same
+    dict of gradients."""
+    return _bwd("ssm_scan_bwd_saved", x, dt, A, B, C, D, z, None, states, dy, dh_final, chunk_len,
+                want_dz, want_dh0, workspace, out)
+
+
+def _bwd(fn_name, x, dt, A, B, C, D, z, h0, states, dy, dh_final, chunk_len, want_dz, want_dh0,
+         workspace, out):
     lib = load_library()
     b, L, Dn = x.shape
     N = A.shape[1]
@@ -555,6 +632,9 @@ def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk
     _dev(A, "A", (Dn, N), f32); _dev(D, "D", (Dn,), f32)
     _dev(B, "B", (b, L, N)); _dev(C, "C", (b, L, N))
     _dev(h0, "h0", (b, Dn, N), f32); _dev(dh_final, "dh_final", (b, Dn, N), f32)
+    saved = fn_name == "ssm_scan_bwd_saved"
+    if saved:
+        _dev(states, "states", _states_shape(b, L, Dn, N), f32)
     io = _io(x, dt, z, B, C, dy)
     out = dict(out or {})
     dev = x.device
@@ -571,15 +651,15 @@ def ssm_scan_bwd(x, dt, A, B, C, D, z=None, h0=None, *, dy, dh_final=None, chunk
         _dev(out[k], k, shp, dtp)
     out.setdefault("dz", None)
     out.setdefault("dh0", None)
-    need = ssm_scan_bwd_workspace(b, L, Dn, N, chunk_len)
+    need = (ssm_scan_bwd_saved_workspace if saved else ssm_scan_bwd_workspace)(b, L, Dn, N, chunk_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ssm_scan_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                          _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
-                          _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
-                          _ptr(out["dD"]), _ptr(out["dh0"]), b, L, Dn, N, io, chunk_len,
-                          _ptr(workspace), ws_bytes, _stream(x))
+    st = getattr(lib, fn_name)(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(states if saved else h0),
+        _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dz"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), b, L, Dn, N, io,
+        chunk_len, _ptr(workspace), ws_bytes, _stream(x))
     _check(st)
     return out
 
@@ -641,33 +721,43 @@ class _SelectiveScan(torch.autograd.Function):
     """ssm_scan_fwd_ex forwards, ssm_scan_bwd backwards (both in the library's kernels)."""
 
     @staticmethod
-    def forward(ctx, x, dt, A, B, C, D, z, h0, chunk_len):
-        y, h_final = ssm_scan_fwd_ex(x, dt, A, B, C, D, z, h0, chunk_len=chunk_len)
-        ctx.save_for_backward(x, dt, A, B, C, D, z, h0)
+    def forward(ctx, x, dt, A, B, C, D, z, h0, chunk_len, save_states):
+        if save_states:
+            y, h_final, states = ssm_scan_fwd_save(x, dt, A, B, C, D, z, h0, chunk_len=chunk_len)
+        else:
+            y, h_final = ssm_scan_fwd_ex(x, dt, A, B, C, D, z, h0, chunk_len=chunk_len)
+            states = None
+        ctx.save_for_backward(x, dt, A, B, C, D, z, h0, states)
         ctx.chunk_len = chunk_len
         return y, h_final
 
     @staticmethod
     def backward(ctx, dy, dh_final):
-        x, dt, A, B, C, D, z, h0 = ctx.saved_tensors
+        x, dt, A, B, C, D, z, h0, states = ctx.saved_tensors
         need = ctx.needs_input_grad
         if dy is None:
             dy = torch.zeros_like(x)
-        g = ssm_scan_bwd(x, dt, A, B, C, D, z, h0, dy=dy.to(x.dtype).contiguous(),
-                         dh_final=None if dh_final is None else dh_final.float().contiguous(),
-                         chunk_len=ctx.chunk_len, want_dz=z is not None and need[6],
-                         want_dh0=h0 is not None and need[7])
+        kw = dict(dy=dy.to(x.dtype).contiguous(),
+                  dh_final=None if dh_final is None else dh_final.float().contiguous(),
+                  chunk_len=ctx.chunk_len, want_dz=z is not None and need[6],
+                  want_dh0=h0 is not None and need[7])
+        if states is not None:
+            g = ssm_scan_bwd_saved(x, dt, A, B, C, D, z, states=states, **kw)
+        else:
+            g = ssm_scan_bwd(x, dt, A, B, C, D, z, h0, **kw)
         cast = lambda t, like: None if t is None else t.to(like.dtype)
         grads = (g["dx"], g["ddt"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
-                 cast(g["dD"], D), g["dz"], g["dh0"], None)
+                 cast(g["dD"], D), g["dz"], g["dh0"], None, None)
         return tuple(gr if (i < len(need) and need[i]) else None for i, gr in enumerate(grads))
 
 
-def selective_scan(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0):
+def selective_scan(x, dt, A, B, C, D, z=None, h0=None, *, chunk_len=0, save_states=False):
     """The real-state prefill as a differentiable function: returns (y, h_final), with
     gradients for x, dt, A, B, C, D, z and h0 from ssm_scan_bwd (dB, dC, dA and dD are
-    computed in float32 and returned in their inputs' dtypes)."""
-    return _SelectiveScan.apply(x, dt, A, B, C, D, z, h0, chunk_len)
+    computed in float32 and returned in their inputs' dtypes). save_states: the forward
+    stores the state every 8 steps (ssm_scan_fwd_save) and the backward reads them
+    (ssm_scan_bwd_saved) instead of recomputing them."""
+    return _SelectiveScan.apply(x, dt, A, B, C, D, z, h0, chunk_len, save_states)
 
 
 class _SelectiveScanFused(torch.autograd.Function):

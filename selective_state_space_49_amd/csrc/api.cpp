@@ -124,8 +124,11 @@ struct Plan {
 // waves_per_simd: what the rescan of the entry point is compiled for (5 for the plain,
 // trapezoidal, complex and MIMO rescans up to rank 4; 4 for the input stage, MIMO rank 8
 // and the backward's own plan).
+// multiple: with several chunks, chunk lengths are rounded down to a multiple of it (the
+// training forward's chunks start where a stored state belongs).
 ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state, int64_t chunk_len,
-                     bool cplx, Plan *p, int32_t rank = 1, int32_t waves_per_simd = 4) {
+                     bool cplx, Plan *p, int32_t rank = 1, int32_t waves_per_simd = 4,
+                     int64_t multiple = 1) {
     if (batch < 0 || L < 0 || d_inner < 1) return fail(SSM_ERR_SHAPE, "batch/L must be >= 0 and d_inner >= 1");
     if (!valid_state(d_state)) return fail(SSM_ERR_UNSUPPORTED, "d_state %d not in {1,2,4,8,16}", d_state);
     if (chunk_len < 0) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be >= 0");
@@ -144,6 +147,7 @@ ssm_status make_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
     // MIMO: a chunk's rows of B (d_state * rank elements each) also span less than 2 GiB,
     // since the matrix path stages them through buffer loads with 32-bit offsets.
     if (rank > 1) T = std::min(T, std::max<int64_t>(1, ((int64_t)1 << 31) / ((int64_t)d_state * rank * 4) - 1));
+    if (multiple > 1 && T < L) T = std::max(multiple, T / multiple * multiple);
     const int64_t n_chunks = L > 0 ? (L + T - 1) / T : 1;
     if (n_chunks > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n_chunks, (long long)kMaxChunks);
     p->T = T;
@@ -195,7 +199,8 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
                        int64_t chunk_len, void *workspace, size_t workspace_bytes,
                        void *hip_stream, bool cplx, void *const *events = nullptr,
                        int32_t n_events = 0, const InputStage *in = nullptr,
-                       const Trap *trap = nullptr, int32_t rank = 0, bool use_scratch = false) {
+                       const Trap *trap = nullptr, int32_t rank = 0, bool use_scratch = false,
+                       float *states = nullptr) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     const bool mimo = rank != 0;
     if (mimo && !valid_rank(rank)) return fail(SSM_ERR_UNSUPPORTED, "rank %d not in {1,2,4,8}", rank);
@@ -203,11 +208,16 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
     const Family fam = cplx ? Family::Complex : in ? Family::Fused : mimo ? Family::Mimo
                      : (trap && trap->lam) ? Family::TrapWeighted : Family::Plain;
     ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, cplx, &plan, mimo ? rank : 1,
-                              waves_per_simd(fam, rank));
+                              waves_per_simd(fam, rank), states ? ssm::kStateEvery : 1);
     if (st != SSM_OK) return st;
     const bool work = batch > 0 && L > 0;
     if (work && (!x || !dt || !A || !B || !C || !D || !y))
         return fail(SSM_ERR_NULL, "x, dt, A, B, C, D and y are required");
+    if (states) {
+        if (!aligned(states, 16)) return fail(SSM_ERR_ALIGN, "states must be 16-byte aligned");
+        if ((double)batch * d_inner * d_state * 4.0 >= 2147483648.0)
+            return fail(SSM_ERR_UNSUPPORTED, "stored states need batch * d_inner * d_state * 4 below 2 GiB");
+    }
     const size_t eb = io_bytes(io);
     if (!aligned(x, eb) || !aligned(dt, eb) || !aligned(z, eb) || !aligned(y, eb) ||
         !aligned(B, 4) || !aligned(C, 4) || !aligned(A, 16) || !aligned(D, 4) ||
@@ -311,6 +321,9 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         e = ssm::launch_scan_trap(a, iot, d_state, z != nullptr, s, ev);
     } else if (mimo) {
         e = ssm::launch_scan_mimo(a, iot, d_state, z != nullptr, s, ev);
+    } else if (states) {
+        a.states = states;
+        e = ssm::launch_scan_save(a, iot, d_state, z != nullptr, s, ev);
     } else {
         e = cplx ? ssm::launch_scan_complex(a, iot, d_state, z != nullptr, s, ev)
                  : ssm::launch_scan_real(a, iot, d_state, z != nullptr, s, ev);
@@ -401,14 +414,18 @@ struct BwdPlan {
 
 size_t ws_round(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// saved: the states come from the training forward (chunks start at multiples of
+// kStateEvery, and the workspace holds no states of its own).
 ssm_status make_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                         int64_t chunk_len, BwdPlan *p) {
+                         int64_t chunk_len, BwdPlan *p, bool saved = false) {
     ssm_status st = make_plan(batch, L, d_inner, d_state, chunk_len, false, &p->fwd, 1,
                               waves_per_simd(Family::Backward));
     if (st != SSM_OK) return st;
     if (p->fwd.n_chunks > 1) {
-        int64_t T = p->fwd.T / ssm::kSub * ssm::kSub;
-        if (T < ssm::kSub) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be at least %d for the backward", ssm::kSub);
+        // (from stored states, chunk lengths are rounded as ssm_scan_fwd_save rounds them)
+        const int64_t m = saved ? ssm::kStateEvery : ssm::kSub;
+        int64_t T = saved ? std::max<int64_t>(m, p->fwd.T / m * m) : p->fwd.T / m * m;
+        if (T < m) return fail(SSM_ERR_UNSUPPORTED, "chunk_len must be at least %d for the backward", (int)m);
         const int64_t n = (L + T - 1) / T;
         if (n > kMaxChunks) return fail(SSM_ERR_UNSUPPORTED, "chunk_len gives %lld chunks (max %lld)", (long long)n, (long long)kMaxChunks);
         p->fwd.T = T;
@@ -421,9 +438,9 @@ ssm_status make_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_st
     p->waves = p->dblocks * (p->threads / 64);
     const size_t M = (size_t)batch * d_inner * d_state * sizeof(float);
     const size_t C = (size_t)p->fwd.n_chunks;
-    p->ck_rows = (std::min<int64_t>(p->fwd.T, L) + 2 * ssm::kSub - 1) / (2 * ssm::kSub);
+    p->ck_rows = (std::min<int64_t>(p->fwd.T, L) + ssm::kStateEvery - 1) / ssm::kStateEvery;
     const size_t sizes[8] = {(C - 1) * M, (C - 1) * M, (C - 1) * M, (C - 1) * M,
-                             C * (size_t)p->ck_rows * M, C * M,
+                             saved ? 0 : C * (size_t)p->ck_rows * M, C * M,
                              C * (size_t)batch * d_inner * sizeof(float),
                              (size_t)batch * L * p->waves * 2 * d_state * sizeof(float)};
     size_t at = 0;
@@ -440,15 +457,16 @@ ssm_status bwd_common(const void *x, const void *dt, const float *A, const void 
                       const float *dh_final, void *dx, void *ddt, void *dz, float *dA, float *dB,
                       float *dC, float *dD, float *dh0, int64_t batch, int64_t L, int64_t d_inner,
                       int32_t d_state, ssm_dtype io, int64_t chunk_len, void *workspace,
-                      size_t workspace_bytes, void *hip_stream) {
+                      size_t workspace_bytes, void *hip_stream, const float *states = nullptr) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     BwdPlan plan;
-    ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &plan);
+    ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &plan, states != nullptr);
     if (st != SSM_OK) return st;
     if (!A || !D || !dA || !dD) return fail(SSM_ERR_NULL, "A, D, dA and dD are required");
     const bool work = batch > 0 && L > 0;
     if (work && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
         return fail(SSM_ERR_NULL, "x, dt, B, C, dy, dx, ddt, dB and dC are required");
+    if (!aligned(states, 16)) return fail(SSM_ERR_ALIGN, "states must be 16-byte aligned");
     const size_t eb = io_bytes(io);
     if (!aligned(x, eb) || !aligned(dt, eb) || !aligned(z, eb) || !aligned(dy, eb) ||
         !aligned(dx, eb) || !aligned(ddt, eb) || !aligned(dz, eb) || !aligned(B, 4) ||
@@ -484,7 +502,8 @@ ssm_status bwd_common(const void *x, const void *dt, const float *A, const void 
     a.sumH = f.sumH;
     a.revQ = (float *)(ws + plan.off[2]);
     a.revG = (float *)(ws + plan.off[3]);
-    a.ckpt = (float *)(ws + plan.off[4]);
+    a.ckpt = states ? const_cast<float *>(states) : (float *)(ws + plan.off[4]);
+    a.saved = states != nullptr;
     a.partA = (float *)(ws + plan.off[5]);
     a.partD = (float *)(ws + plan.off[6]);
     a.partBC = (float *)(ws + plan.off[7]);
@@ -807,6 +826,52 @@ ssm_status ssm_scan_bwd(const void *x, const void *dt, const float *A, const voi
                       hip_stream);
 }
 
+size_t ssm_scan_fwd_save_states_bytes(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state) {
+    if (batch < 0 || L < 0 || d_inner < 1 || !valid_state(d_state)) return 0;
+    const int64_t rows = (L + ssm::kStateEvery - 1) / ssm::kStateEvery;
+    return (size_t)rows * (size_t)batch * (size_t)d_inner * (size_t)d_state * sizeof(float);
+}
+
+size_t ssm_scan_fwd_save_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                   int64_t chunk_len) {
+    Plan p;
+    if (make_plan(batch, L, d_inner, d_state, chunk_len, false, &p, 1, waves_per_simd(Family::Plain),
+                  ssm::kStateEvery) != SSM_OK)
+        return 0;
+    return p.ws_bytes;
+}
+
+ssm_status ssm_scan_fwd_save(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z, const float *h0,
+                             void *y, float *h_final, float *states, int64_t batch, int64_t L,
+                             int64_t d_inner, int32_t d_state, ssm_dtype io, int64_t chunk_len,
+                             void *workspace, size_t workspace_bytes, void *hip_stream) {
+    if (batch > 0 && L > 0 && !states) return fail(SSM_ERR_NULL, "states is required");
+    return scan_common(x, dt, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0,
+                       nullptr, nullptr, 0, false, batch > 0 && L > 0 ? states : nullptr);
+}
+
+size_t ssm_scan_bwd_saved_workspace(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                    int64_t chunk_len) {
+    BwdPlan p;
+    if (make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &p, true) != SSM_OK) return 0;
+    return p.bytes;
+}
+
+ssm_status ssm_scan_bwd_saved(const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *states,
+                              const void *dy, const float *dh_final, void *dx, void *ddt, void *dz,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0, int64_t batch,
+                              int64_t L, int64_t d_inner, int32_t d_state, ssm_dtype io,
+                              int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                              void *hip_stream) {
+    if (batch > 0 && L > 0 && !states) return fail(SSM_ERR_NULL, "states is required");
+    return bwd_common(x, dt, A, B, C, D, z, nullptr, dy, dh_final, dx, ddt, dz, dA, dB, dC, dD, dh0,
+                      batch, L, d_inner, d_state, io, chunk_len, workspace, workspace_bytes,
+                      hip_stream, batch > 0 && L > 0 ? states : nullptr);
+}
+
 // ---------------------------------------------------------------- backward through the input stage
 // The two streaming kernels of the input stage take chunks of their own (independent:
 // enough for about 8 blocks of 256 channels per SIMD, 8192 on 256 CUs, i.e. 2 blocks of
@@ -930,6 +995,6 @@ const char *ssm_status_str(ssm_status s) {
 
 const char *ssm_last_error(void) { return g_err; }
 
-int32_t ssm_abi_version(void) { return 2; }
+int32_t ssm_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -331,17 +331,13 @@ __device__ __forceinline__ void stage_sub(SSM_LDS uint32_t *stg, const RowStream
 }
 
 // ---------------------------------------------------------------- stored states
-// Row c R + p of ckpt (M = batch Dn N floats, R = ck_rows rows per chunk) holds the state
-// entering step kPair p of chunk c: every second piece's start is stored, and the other
-// piece's start is recomputed from it (half the stored bytes, for one more 4-step walk
-// per two pieces in the gradient kernel). For
-// N % 4 == 0 a row is laid out [batch][N / 4][Dn][4]: the q-th 16-byte piece of every
-// channel of a wave is one contiguous 1 KB run, so each of a lane's four 16-byte stores
-// and loads covers whole cache lines with the wave's other lanes. Otherwise [batch][Dn][N].
-template <int N>
-__device__ __forceinline__ size_t ckpt_at(int64_t b, int64_t d, int q, int64_t Dn) {
-    return N % 4 == 0 ? ((size_t)(b * (N / 4) + q) * Dn + d) * 4 : (size_t)(b * Dn + d) * N;
-}
+// Row c R + p of ckpt (R = ck_rows rows per chunk) holds the state entering step
+// kStateEvery p of chunk c, in the layout of state_at: every second piece's start is
+// stored, and the other piece's start is recomputed from it (half the stored bytes, for
+// one more 4-step walk per two pieces in the gradient kernel). With the training
+// forward's states (saved) chunks start at multiples of kStateEvery and R = T / 8, so
+// that row is the global row t / kStateEvery the forward wrote.
+static_assert(kStateEvery == 2 * kSub, "a stored state starts every pair of pieces");
 
 // ---------------------------------------------------------------- forward walk
 // Per chunk, a forward walk from the state entering it that stores the state entering
@@ -377,11 +373,11 @@ __global__ __launch_bounds__(256) void k_bwd_walk(BwdArgs a) {
 #pragma unroll
                 for (int q = 0; q < N / 4; ++q) {
                     const f4v v = {h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
-                    *(f4v *)(row + ckpt_at<N>(ln.b, ln.d, q, a.Dn)) = v;
+                    *(f4v *)(row + state_at<N>(ln.b, ln.d, q, a.Dn)) = v;
                 }
             } else {
 #pragma unroll
-                for (int n = 0; n < N; ++n) row[ckpt_at<N>(ln.b, ln.d, 0, a.Dn) + n] = h[n];
+                for (int n = 0; n < N; ++n) row[state_at<N>(ln.b, ln.d, 0, a.Dn) + n] = h[n];
             }
         }
         const int64_t t = t0 + i;
@@ -405,7 +401,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdArgs a) {
     const size_t M = (size_t)a.batch * a.Dn * N;
     const size_t col = (size_t)(ln.b * a.Dn + ln.d) * N;
     // the lane's stored states (< 2 GiB per row: checked on the host)
-    const uint32_t st_voff = (uint32_t)(ckpt_at<N>(ln.b, ln.d, 0, a.Dn) * sizeof(float));
+    const uint32_t st_voff = (uint32_t)(state_at<N>(ln.b, ln.d, 0, a.Dn) * sizeof(float));
     const uint32_t st_qstride = (uint32_t)(a.Dn * 16);
     float A2[N];
 #pragma unroll
@@ -649,7 +645,8 @@ __global__ void k_bwd_reduce_BC1(BwdArgs a) {
 
 template <typename IO, int N>
 hipError_t launch_n(const BwdArgs &a, const ScanArgs &fwd, int io, bool gated, hipStream_t s) {
-    hipError_t e = launch_summary_carry(fwd, io, N, s);
+    // the states entering the chunks, for the walk (not needed with the forward's states)
+    hipError_t e = a.saved ? hipSuccess : launch_summary_carry(fwd, io, N, s);
     if (e != hipSuccess) return e;
     const unsigned gx = (unsigned)(a.batch * a.dblocks);
     const dim3 blk(a.threads);
@@ -663,7 +660,7 @@ hipError_t launch_n(const BwdArgs &a, const ScanArgs &fwd, int io, bool gated, h
         e = launch_carry(r, N, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_bwd_walk<IO, N>), dim3(gx, a.n_chunks), blk, 0, s, a);
+    if (!a.saved) hipLaunchKernelGGL((k_bwd_walk<IO, N>), dim3(gx, a.n_chunks), blk, 0, s, a);
     if (gated) hipLaunchKernelGGL((k_bwd_chunk<IO, N, true>), dim3(gx, a.n_chunks), blk, 0, s, a);
     else hipLaunchKernelGGL((k_bwd_chunk<IO, N, false>), dim3(gx, a.n_chunks), blk, 0, s, a);
     const int64_t nad = a.Dn * (N + 1);

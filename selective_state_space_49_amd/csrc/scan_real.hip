@@ -54,6 +54,7 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
 // ---------------------------------------------------------------- input stage
 // The kernels read x and dt as given.
 struct NoInput {
+    static constexpr bool kSave = false;  // store the state every kStateEvery steps
     static constexpr bool kTrap = false;
     static constexpr bool kW = false;  // no weight stream
     static constexpr int kWavesPerSimd = 5;
@@ -66,10 +67,18 @@ struct NoInput {
     __device__ __forceinline__ void store_state(const ScanArgs &, int64_t, int64_t) const {}
 };
 
+// The training forward: the plain scan that also stores the state entering every
+// kStateEvery-th step for the backward (ScanArgs::states).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+struct SaveInput : NoInput {
+    static constexpr bool kSave = true;
+};
+
 // The MambaBlock input stage: u = silu(causal conv of KC taps over x) (KC = 0: x as
 // is) and dt = softplus(dt + dt_bias).
 template <typename IO, int KC>
 struct MambaInput {
+    static constexpr bool kSave = false;
     static constexpr bool kTrap = false;
     static constexpr bool kW = false;
     static constexpr int kWavesPerSimd = 4;  // at five (prefetching 2 rows per block to fit)
@@ -134,9 +143,9 @@ struct MambaInput {
 // before step 0). x and dt are read as given; lam is a fourth stream laid out like dt.
 template <typename IO, bool LAM>
 struct TrapInput {
+    static constexpr bool kSave = false;
     static constexpr bool kTrap = true;
     static constexpr bool kW = LAM;
-    // The weight stream's prefetch buffers spill registers at five waves per SIMD.
     static constexpr int kWavesPerSimd = 5;
     static constexpr int kKU = LAM ? 2 : 4;  // the weight stream's blocks of 4 rows would spill
     static constexpr bool kRawPrefetch = false;
@@ -383,6 +392,9 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     in.history(a, ln.b, ln.d, t0);
     float bp[N];  // trapezoidal rule: B of the step before, carried from step to step
     if constexpr (In::kTrap) in.template prev_row<N>(a, Bp, ln.b, t0, bp);
+    // training forward: the lane's byte offset in a stored-state row, and between pieces
+    const uint32_t sv_off = In::kSave ? (uint32_t)(state_at<N>(ln.b, ln.d, 0, a.Dn) * 4) : 0u;
+    const uint32_t sv_qstride = (uint32_t)(a.Dn * 16);
     stream_steps_w<IO, GATED, In::kKU, In::kRawPrefetch, In::kW>(xs, dts, zs, lws, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv, float lr) {
         const float xv = in.x(xr), dv = in.dt(dr);
         const int64_t t = t0 + i;
@@ -401,6 +413,26 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
             }
             in.xprev = xv;
         } else {
+            if constexpr (In::kSave) {
+                // the state entering step t (chunks start at multiples of kStateEvery),
+                // through a buffer resource based at its row (a row is below 2 GiB)
+                if (i % kStateEvery == 0) {
+                    const auto r = __builtin_amdgcn_make_buffer_rsrc(
+                        a.states + (size_t)(t / kStateEvery) * a.batch * a.Dn * N, 0, -1, kRsrcWord3);
+                    if constexpr (N % 4 == 0) {
+#pragma unroll
+                        for (int q = 0; q < N / 4; ++q) {
+                            const u32x4 v = {__float_as_uint(h[4 * q]), __float_as_uint(h[4 * q + 1]),
+                                             __float_as_uint(h[4 * q + 2]), __float_as_uint(h[4 * q + 3])};
+                            __builtin_amdgcn_raw_buffer_store_b128(v, r, sv_off, q * sv_qstride, 0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int n = 0; n < N; ++n)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h[n]), r, sv_off + 4u * n, 0, 0);
+                    }
+                }
+            }
             const float u = dv * xv;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
@@ -490,6 +522,12 @@ hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, 
                             hipEvent_t const *ev) {
     return io == 0 ? launch_io<float, NoInput>(a, d_state, gated, s, ev)
                    : launch_io<bf16_bits, NoInput>(a, d_state, gated, s, ev);
+}
+
+hipError_t launch_scan_save(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev) {
+    return io == 0 ? launch_io<float, SaveInput>(a, d_state, gated, s, ev)
+                   : launch_io<bf16_bits, SaveInput>(a, d_state, gated, s, ev);
 }
 
 hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,

@@ -37,7 +37,22 @@ struct ScanArgs {
     // MIMO entry point only: inputs and outputs per channel (x, z, y are [batch][L][Dn][rank],
     // B and C [batch][L][N][rank]); 1 elsewhere.
     int32_t rank;
+    // Training forward only: the state entering every kStateEvery-th step, in the
+    // stored-state layout (state_at); null elsewhere. Chunks start at multiples of
+    // kStateEvery.
+    float *states;
 };
+
+// The backward's stored states: row r (batch Dn N floats) holds the state entering step
+// kStateEvery r. For N % 4 == 0 a row is laid out [batch][N / 4][Dn][4], so the q-th
+// 16-byte piece of the 64 channels of a wave is one contiguous 1 KB run and a wave's
+// 16-byte stores and loads cover whole cache lines; otherwise [batch][Dn][N]. state_at
+// gives the float index in a row of piece q (the first of its 4 states) of channel d.
+constexpr int kStateEvery = 8;
+template <int N>
+__host__ __device__ inline size_t state_at(int64_t b, int64_t d, int q, int64_t Dn) {
+    return N % 4 == 0 ? ((size_t)(b * (N / 4) + q) * Dn + d) * 4 : (size_t)(b * Dn + d) * N;
+}
 
 struct StepArgs {
     float *h;
@@ -64,6 +79,8 @@ struct StepArgs {
 // ev: NULL, or 4 events recorded on s before the summary kernel, after it, after the
 // carry kernel and after the rescan kernel (phases that do not run leave two
 // consecutive records).
+hipError_t launch_scan_save(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
+                            hipEvent_t const *ev);
 hipError_t launch_scan_real(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                             hipEvent_t const *ev);
 // The same with the exponential-trapezoidal discretisation (x_prev, B_prev, lam of a).
@@ -115,14 +132,16 @@ struct BwdArgs {
     float *revQ;    // reverse summaries, reversed chunk order: entry j is chunk n_chunks-1-j
     float *revG;    //   (decay over the chunk, adjoint passed left from a zero carry-in); after
                     //   the reverse carry revG[j] = adjoint entering chunk n_chunks-2-j from the right
-    float *ckpt;    // states every 2 kSub steps [n_chunks][ck_rows] rows of batch Dn N floats
+    float *ckpt;    // states every kStateEvery = 2 kSub steps, [n_chunks][ck_rows] rows of
+                    // batch Dn N floats (state_at); with saved, the training forward's
     float *partA;   // per-chunk dA              [n_chunks][batch][Dn][N]
     float *partD;   // per-chunk dD              [n_chunks][batch][Dn]
     float *partBC;  // per-wave dB, dC           [batch][L][waves][2N]
     int64_t batch, L, Dn;
     int64_t T;
     int32_t n_chunks, dblocks, threads, waves;  // waves = channel waves per batch row
-    int64_t ck_rows;  // stored-state rows per chunk: ceil(min(T, L) / (2 kSub))
+    int64_t ck_rows;  // stored-state rows per chunk: ceil(min(T, L) / kStateEvery)
+    bool saved;       // ckpt holds the training forward's states: no walk
 };
 constexpr int kSub = 4;  // steps per recomputed sub-chunk of the backward
 hipError_t launch_scan_bwd(const BwdArgs &a, const ScanArgs &fwd, int io, int d_state, bool gated,

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ssm.ssm_abi_version() == 2
+    assert ssm.ssm_abi_version() == 3
     for s in range(8):
         assert ssm.ssm_status_str(s)
     assert ssm.ssm_status_str(99) == "unknown status"
@@ -263,6 +263,39 @@ def test_backward_argument_errors(lib):
     assert _bwd_raw(lib, batch=4, Dn=1 << 23, N=16, L=8) == UNSUP
     assert "2 GiB" in ssm.ssm_last_error()
     assert ssm.ssm_scan_bwd_workspace(4, 8, 1 << 23, 16, 0) == 0
+
+
+def test_stored_state_training_argument_errors(lib):
+    # ssm_scan_fwd_save and ssm_scan_bwd_saved: checked before any launch (no GPU here).
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def fwd(states=0x2000, N=4, L=64, chunk=0, ws=None, wsb=0, x=0x1000):
+        return lib.ssm_scan_fwd_save(p(x), p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                     None, None, p(0x1000), None, p(states), 1, L, 4, N, 0, chunk,
+                                     p(ws), wsb, None)
+
+    def bwd(states=0x2000, L=64, chunk=0, ws=None, wsb=0):
+        return lib.ssm_scan_bwd_saved(p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                      p(0x1000), None, p(states), p(0x1000), None, p(0x1000),
+                                      p(0x1000), None, p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                      None, 1, L, 4, 4, 0, chunk, p(ws), wsb, None)
+    assert fwd(states=None) == NULL and bwd(states=None) == NULL
+    assert fwd(states=0x2008) == ALIGN and bwd(states=0x2008) == ALIGN
+    assert fwd(N=3) == UNSUP and fwd(x=None) == NULL
+    # the state every 8 steps: ceil(L / 8) rows of batch * d_inner * d_state floats
+    assert ssm.ssm_scan_fwd_save_states_bytes(2, 17, 5, 16) == 3 * 2 * 5 * 16 * 4
+    assert ssm.ssm_scan_fwd_save_states_bytes(2, 0, 5, 16) == 0
+    # chunk lengths are rounded down to a multiple of 8 (at least 8): 20 plans as 16
+    assert ssm.ssm_scan_fwd_save_workspace(1, 200, 4, 4, 20) == ssm.ssm_scan_fwd_workspace_ex(1, 200, 4, 4, 16)
+    assert ssm.ssm_scan_bwd_saved_workspace(1, 200, 4, 4, 20) == ssm.ssm_scan_bwd_saved_workspace(1, 200, 4, 4, 16)
+    # no stored states of its own
+    assert ssm.ssm_scan_bwd_saved_workspace(1, 2000, 64, 16, 64) < ssm.ssm_scan_bwd_workspace(1, 2000, 64, 16, 64)
+    need = ssm.ssm_scan_fwd_save_workspace(1, 200, 4, 4, 16)
+    assert fwd(L=200, chunk=16) == WS and fwd(L=200, chunk=16, ws=0x10000, wsb=need - 1) == WS
+    need = ssm.ssm_scan_bwd_saved_workspace(1, 200, 4, 4, 16)
+    assert bwd(L=200, chunk=16) == WS and bwd(L=200, chunk=16, ws=0x10000, wsb=need - 1) == WS
+    # L = 0 needs no states
+    assert fwd(states=None, L=0) != NULL
 
 
 def test_trapezoid_argument_errors(lib):
