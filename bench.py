@@ -26,6 +26,9 @@ ceiling allows in elements/s and as a fraction of HBM peak. HBM traffic measured
 with rocprofv3 counters is read from profiles/traffic.json when it was taken on
 the current kernel source (by hash), else null.
 
+With no variant flag the run ends with the 256k prefill's backward ("backward": ssm_scan_bwd,
+and ssm_scan_bwd_saved from the training forward's stored states).
+
 The CPU baseline is the fp64 oracle as it stands, run on a bounded sample of the
 same workload (a subset of channels over the full sequence; channels are
 independent) from as many threads as this process has host cores (its CPU affinity,
@@ -1075,6 +1078,18 @@ def main():
     if len(recs) > 1:
         out["workloads"] = {n: {k: v for k, v in r.items() if k not in ("steps", "warmup")}
                             for n, r in recs.items()}
+    if not is_variant and not args.workload:
+        # The default run also times the 256k prefill's backward (row f2): ssm_scan_bwd,
+        # and ssm_scan_bwd_saved from the training forward's stored states (that forward
+        # timed apart), each with its roofline record; the oracle's backward as baseline.
+        back = {}
+        for key, var, cpu in (("ssm_scan_bwd", {"backward": True}, True),
+                              ("ssm_scan_bwd_saved", {"backward": True, "saved": True}, False)):
+            log("workload", HEADLINE, key)
+            r = measure(HEADLINE, var, args.steps, args.warmup, cpu and not args.no_cpu_baseline,
+                        threads, cpus, torch, ssm, workloads, args.chunk_len)
+            back[key] = {k: v for k, v in r.items() if k not in ("steps", "warmup")}
+        out["backward"] = back
     print(json.dumps(out), flush=True)
 
 

@@ -102,6 +102,23 @@ def test_backward_from_stored_states_matches_oracle(case):
     _compare(got, _oracle(d), TOL[shape.io])
 
 
+def test_stored_states_do_not_depend_on_either_chunk_plan():
+    # The rows are global (row r: the state entering step 8 r), so the backward may cut
+    # its chunks differently from the forward that stored them.
+    case = (2, 500, 130, 16, "bf16", True, 0, True, True)
+    shape, d = _draw(case, seed=315)
+    g = to_dev(d)
+    say("stored states across chunk plans")
+    _, _, st = ssm.ssm_scan_fwd_save(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], g["h0"],
+                                     chunk_len=24)
+    ref = _oracle(d)
+    for T in (0, 64, 1000):
+        got = ssm.ssm_scan_bwd_saved(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["z"], states=st,
+                                     dy=g["dy"], dh_final=g["dh_final"], chunk_len=T)
+        torch.cuda.synchronize()
+        _compare(got, ref, TOL[shape.io])
+
+
 def test_backward_from_stored_states_edges():
     # L = 0: no states are needed (dA = dD = 0, dh0 = dh_final); states are required for
     # L > 0; the backward's chunk length is rounded down to a multiple of 8.
