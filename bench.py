@@ -43,7 +43,8 @@ per-step weight stream), --mimo R the MIMO ones (rank-R
 inputs and outputs per channel; elements stay channel-steps, each with R outputs).
 --backward times ssm_scan_bwd on a prefill workload, and with --fused ssm_scan_bwd_fused
 (the gradients through the input stage as well), with --saved ssm_scan_bwd_saved from the
-states ssm_scan_fwd_save stored (that forward timed apart). --one-call times the decode as one call
+states ssm_scan_fwd_save stored (with --fused: ssm_scan_bwd_fused_saved from
+ssm_scan_fwd_fused_save's; that forward timed apart). --one-call times the decode as one call
 over all layers per token instead of one call per layer.
 """
 from __future__ import annotations
@@ -229,8 +230,9 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
     """One step = one ssm_scan_bwd call over the workload (dy ~ N(0, 1) in the I/O dtype);
     with conv_k, one ssm_scan_bwd_fused call (the input stage of a conv_k-tap filter:
     x and dt of the workload are then the raw x_in and dt_raw). saved: one
-    ssm_scan_bwd_saved call from the states one ssm_scan_fwd_save call stored (that
-    forward is timed too, apart, and reported beside the backward)."""
+    ssm_scan_bwd_saved call (with conv_k, ssm_scan_bwd_fused_saved) from the states one
+    ssm_scan_fwd_save (ssm_scan_fwd_fused_save) call stored (that forward is timed too,
+    apart, and reported beside the backward)."""
     dev = "cuda"
     log("drawing inputs for", shape.name, "(backward)")
     d = workloads.make_scan_inputs(shape, dev)
@@ -241,7 +243,8 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
     if fused:
         d.update(workloads.make_input_stage(shape, conv_k, dev))
         io = 1 if shape.io == "bf16" else 0
-        need = ssm.ssm_scan_bwd_fused_workspace(b, L, Dn, N, conv_k, io, chunk_len)
+        need = (ssm.ssm_scan_bwd_fused_saved_workspace if saved else ssm.ssm_scan_bwd_fused_workspace)(
+            b, L, Dn, N, conv_k, io, chunk_len)
     elif saved:
         need = ssm.ssm_scan_bwd_saved_workspace(b, L, Dn, N, chunk_len)
     else:
@@ -258,6 +261,13 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         yb = torch.empty_like(d["x"])
 
         def fwd():
+            if fused:
+                ssm.ssm_scan_fwd_fused_save(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                            conv_w=d["conv_w"], conv_b=d["conv_b"],
+                                            conv_state0=d["conv_state0"], dt_bias=d["dt_bias"], y=yb,
+                                            states=states, chunk_len=chunk_len, workspace=fws,
+                                            want_conv_state=False)
+                return
             ssm.ssm_scan_fwd_save(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], y=yb,
                                   states=states, chunk_len=chunk_len, workspace=fws)
         for _ in range(max(warmup, 1)):
@@ -273,6 +283,13 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         log("forward with stored states", round(fwd_ms, 4), "ms")
 
     def call():
+        if saved and fused:
+            ssm.ssm_scan_bwd_fused_saved(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                         states=states, conv_w=d["conv_w"], conv_b=d["conv_b"],
+                                         conv_state0=d["conv_state0"], dt_bias=d["dt_bias"], dy=dy,
+                                         chunk_len=chunk_len, workspace=ws, want_dh0=False,
+                                         want_dconv_state0=False)
+            return
         if saved:
             r = ssm.ssm_scan_bwd_saved(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                        states=states, dy=dy, chunk_len=chunk_len, workspace=ws,
@@ -320,8 +337,8 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         "elements_per_step": shape.elements, "bytes_per_step": nbytes,
         "lane_ops_per_elem": lane_ops, "chunk_len": chunk_len,
         "n_chunks": None, "dominant_ms": gpu_ms, "gpu_ms": gpu_ms,
-        "kernel": "ssm_scan_bwd_fused (all launches)" if fused else
-                  "ssm_scan_bwd_saved (all launches)" if saved else "ssm_scan_bwd (all launches)",
+        "kernel": ("ssm_scan_bwd_fused" if fused else "ssm_scan_bwd") + ("_saved" if saved else "")
+                  + " (all launches)",
         "source": "bwd",
     }
     return info, d
@@ -894,7 +911,10 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
             cfg["input_stage"] = {"conv_k": conv_k, "conv_silu": conv_k > 0, "softplus_dt": True,
                                   "entry_point": "ssm_scan_fwd_fused"}
         if backward:
-            cfg["pass"] = ("backward through the input stage (ssm_scan_bwd_fused: dx_in, ddt_raw, dconv_w, "
+            cfg["pass"] = ("backward through the input stage from the fused training forward's stored "
+                           "states (ssm_scan_bwd_fused_saved: dx_in, ddt_raw, dconv_w, dconv_b, ddt_bias, "
+                           "dz, dA, dB, dC, dD)" if conv_k is not None and saved else
+                           "backward through the input stage (ssm_scan_bwd_fused: dx_in, ddt_raw, dconv_w, "
                            "dconv_b, ddt_bias, dz, dA, dB, dC, dD)" if conv_k is not None else
                            "backward from the training forward's stored states (ssm_scan_bwd_saved: "
                            "dx, ddt, dz, dA, dB, dC, dD)" if saved else
@@ -1000,7 +1020,8 @@ def main():
                     help="time ssm_scan_bwd (gradients of the prefill) on the prefill workload")
     ap.add_argument("--saved", action="store_true",
                     help="with --backward: ssm_scan_bwd_saved from ssm_scan_fwd_save's stored "
-                         "states (the forward timed apart)")
+                         "states (with --fused: ssm_scan_bwd_fused_saved from "
+                         "ssm_scan_fwd_fused_save's; the forward timed apart)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")

@@ -389,6 +389,37 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
                               ssm_dtype io, int64_t chunk_len, void *workspace,
                               size_t workspace_bytes, void *hip_stream);
 
+/* Training the fused prefill with stored states: ssm_scan_fwd_fused_save is
+ * ssm_scan_fwd_fused that also writes the scan's state entering every 8th step to
+ * `states`, in ssm_scan_fwd_save's layout and size (ssm_scan_fwd_save_states_bytes; its
+ * chunks rounded as ssm_scan_fwd_save rounds them, and ssm_scan_fwd_save_workspace bytes
+ * of workspace suffice); ssm_scan_bwd_fused_saved is ssm_scan_bwd_fused given those
+ * states instead of h0 (the scan's backward reads them as ssm_scan_bwd_saved does), with
+ * ssm_scan_bwd_fused_saved_workspace bytes of workspace. Errors as in the fused and
+ * stored-state entry points above. */
+ssm_status ssm_scan_fwd_fused_save(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                                   const void *C, const float *D, const void *z, const float *h0,
+                                   const float *conv_w, const float *conv_b, int32_t conv_k,
+                                   const void *conv_state0, void *conv_state_out,
+                                   const float *dt_bias, void *y, float *h_final, float *states,
+                                   int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                   ssm_dtype io, int64_t chunk_len, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+size_t ssm_scan_bwd_fused_saved_workspace(int64_t batch, int64_t L, int64_t d_inner,
+                                          int32_t d_state, int32_t conv_k, ssm_dtype io,
+                                          int64_t chunk_len);
+ssm_status ssm_scan_bwd_fused_saved(const void *x_in, const void *dt_raw, const float *A,
+                                    const void *B, const void *C, const float *D, const void *z,
+                                    const float *states, const float *conv_w, const float *conv_b,
+                                    int32_t conv_k, const void *conv_state0, const float *dt_bias,
+                                    const void *dy, const float *dh_final, void *dx_in,
+                                    void *ddt_raw, void *dz, float *dA, float *dB, float *dC,
+                                    float *dD, float *dh0, float *dconv_w, float *dconv_b,
+                                    float *ddt_bias, void *dconv_state0, int64_t batch, int64_t L,
+                                    int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                    int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream);
+
 /* ------------------------------------------------------------------ exponential-trapezoidal
  * ssm_scan_fwd_trap: the prefill of ssm_scan_fwd_ex with the exponential-trapezoidal
  * discretisation that Mamba-3 puts in place of Euler's ("Jamba — SSM-Transformer

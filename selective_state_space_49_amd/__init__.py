@@ -31,6 +31,7 @@ __all__ = [
     "ssm_scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
     "ssm_scan_fwd_save", "ssm_scan_fwd_save_workspace", "ssm_scan_fwd_save_states_bytes",
     "ssm_scan_bwd_saved", "ssm_scan_bwd_saved_workspace", "STATE_EVERY",
+    "ssm_scan_fwd_fused_save", "ssm_scan_bwd_fused_saved", "ssm_scan_bwd_fused_saved_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +54,7 @@ EXPORTED_SYMBOLS = [
     "ssm_scan_fwd_mimo_chunk_len", "ssm_scan_fwd_noalloc",
     "ssm_scan_fwd_save", "ssm_scan_fwd_save_workspace", "ssm_scan_fwd_save_states_bytes",
     "ssm_scan_bwd_saved", "ssm_scan_bwd_saved_workspace",
+    "ssm_scan_fwd_fused_save", "ssm_scan_bwd_fused_saved", "ssm_scan_bwd_fused_saved_workspace",
 ]
 # Steps between the states ssm_scan_fwd_save stores for ssm_scan_bwd_saved.
 STATE_EVERY = 8
@@ -108,6 +110,7 @@ def load_library():
     fused = [vp] * 10 + [i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_fused"] = (fused, ci)
     sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
+    sig["ssm_scan_fwd_fused_save"] = ([vp] * 10 + [i32] + [vp] * 6 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     sig["ssm_scan_bwd_workspace"] = ([i64, i64, i64, i32, i64], sz)
     sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     sig["ssm_scan_bwd_saved"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
@@ -117,6 +120,8 @@ def load_library():
     sig["ssm_scan_fwd_save_states_bytes"] = ([i64, i64, i64, i32], sz)
     sig["ssm_scan_bwd_fused_workspace"] = ([i64, i64, i64, i32, i32, ci, i64], sz)
     sig["ssm_scan_bwd_fused"] = ([vp] * 10 + [i32] + [vp] * 16 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    sig["ssm_scan_bwd_fused_saved"] = sig["ssm_scan_bwd_fused"]
+    sig["ssm_scan_bwd_fused_saved_workspace"] = sig["ssm_scan_bwd_fused_workspace"]
     trap = [vp] * 13 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_trap"] = (trap, ci)
     sig["ssm_scan_fwd_trap_profiled"] = (trap + [vp, i32], ci)
@@ -500,11 +505,12 @@ def _input_stage(conv_w, conv_b, dt_bias, lead, Dn, conv_k):
 def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
                        conv_state0=None, dt_bias=None, chunk_len=0, y=None, h_final=None,
                        conv_state_out=None, workspace=None, want_h_final=True,
-                       want_conv_state=True, events=None):
+                       want_conv_state=True, events=None, states=None):
     """Prefill with the MambaBlock input stage fused into the load: the scan runs on
     u = silu(causal depthwise conv(x_in)) and dt = softplus(dt_raw + dt_bias).
     conv_w [d_inner, K] (None: no convolution); conv_b, dt_bias [d_inner] or None;
-    conv_state0 [b, K-1, d_inner] or None (zeros). Returns (y, h_final, conv_state_out)."""
+    conv_state0 [b, K-1, d_inner] or None (zeros). Returns (y, h_final, conv_state_out).
+    states (see ssm_scan_fwd_fused_save): ssm_scan_fwd_fused_save stores them there."""
     lib = load_library()
     b, L, Dn = x_in.shape
     N = A.shape[1]
@@ -528,14 +534,24 @@ def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None
     if h_final is None and want_h_final:
         h_final = torch.empty((b, Dn, N), dtype=f32, device=x_in.device)
     _dev(h_final, "h_final", (b, Dn, N), f32)
-    need = ssm_scan_fwd_workspace_ex(b, L, Dn, N, chunk_len)
+    save = states is not None
+    if save:
+        _dev(states, "states", _states_shape(b, L, Dn, N), f32)
+    need = (ssm_scan_fwd_save_workspace if save else ssm_scan_fwd_workspace_ex)(b, L, Dn, N, chunk_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x_in.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    args = [_ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+    head = [_ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
             _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_state0), _ptr(conv_state_out),
-            _ptr(dt_bias), _ptr(y), _ptr(h_final), b, L, Dn, N, io, chunk_len, _ptr(workspace),
-            ws_bytes, _stream(x_in)]
+            _ptr(dt_bias), _ptr(y), _ptr(h_final)]
+    tail = [b, L, Dn, N, io, chunk_len, _ptr(workspace), ws_bytes, _stream(x_in)]
+    args = head + tail
+    if save:
+        if events is not None:
+            raise ValueError("the fused training forward is not profiled")
+        st = lib.ssm_scan_fwd_fused_save(*head, _ptr(states), *tail)
+        _check(st)
+        return y, h_final, conv_state_out
     if events is not None:
         if len(events) != 4:
             raise ValueError("need exactly 4 event handles")
@@ -550,6 +566,17 @@ def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None
 def ssm_scan_fwd_fused_profiled(*a, events, **k):
     """ssm_scan_fwd_fused recording 4 HIP events at the kernel boundaries."""
     return ssm_scan_fwd_fused(*a, events=events, **k)
+
+
+def ssm_scan_fwd_fused_save(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, states=None, **k):
+    """The fused training forward: ssm_scan_fwd_fused's results and the scan's state
+    entering every 8th step (float32, shaped as _states_shape) for ssm_scan_bwd_fused_saved.
+    Returns (y, h_final, conv_state_out, states)."""
+    b, L, Dn = x_in.shape
+    if states is None:
+        states = torch.empty(_states_shape(b, L, Dn, A.shape[1]), dtype=torch.float32, device=x_in.device)
+    y, hf, cs = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, states=states, **k)
+    return y, hf, cs, states
 
 
 def _step_fused(fn_name, h, conv_state, x, dt, A, B, C, D, z, conv_w, conv_b, dt_bias, y):
@@ -669,14 +696,28 @@ def ssm_scan_bwd_fused_workspace(batch, L, d_inner, d_state, conv_k, io, chunk_l
                                                            chunk_len))
 
 
+def ssm_scan_bwd_fused_saved_workspace(batch, L, d_inner, d_state, conv_k, io, chunk_len=0) -> int:
+    return int(load_library().ssm_scan_bwd_fused_saved_workspace(batch, L, d_inner, d_state, conv_k,
+                                                                 io, chunk_len))
+
+
+def ssm_scan_bwd_fused_saved(x_in, dt_raw, A, B, C, D, z=None, *, states, **k):
+    """ssm_scan_bwd_fused from the states ssm_scan_fwd_fused_save stored (see ssm_scan.h);
+    the same dict of gradients."""
+    return ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z, None, states=states, **k)
+
+
 def ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
                        conv_state0=None, dt_bias=None, dy, dh_final=None, chunk_len=0,
-                       want_dz=True, want_dh0=True, want_dconv_state0=True, workspace=None):
+                       want_dz=True, want_dh0=True, want_dconv_state0=True, workspace=None,
+                       states=None):
     """Gradients of ssm_scan_fwd_fused's prefill (see ssm_scan.h). Returns a dict:
     dx_in, ddt_raw, dz (io dtype; dz None when ungated or not wanted), dA, dB, dC, dD,
     dh0, dconv_w, dconv_b, ddt_bias (float32; None when the input is absent or not
-    wanted), dconv_state0 (io dtype, for conv_k >= 2)."""
+    wanted), dconv_state0 (io dtype, for conv_k >= 2). states: from stored states
+    (ssm_scan_bwd_fused_saved; h0 is then not given)."""
     lib = load_library()
+    saved = states is not None
     b, L, Dn = x_in.shape
     N = A.shape[1]
     f32 = torch.float32
@@ -702,12 +743,17 @@ def ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None
            "dconv_b": new((Dn,), f32) if (K and conv_b is not None) else None,
            "ddt_bias": new((Dn,), f32) if dt_bias is not None else None,
            "dconv_state0": new((b, K - 1, Dn), x_in.dtype) if (K > 1 and want_dconv_state0) else None}
-    need = ssm_scan_bwd_fused_workspace(b, L, Dn, N, K, io, chunk_len)
+    if saved:
+        if h0 is not None:
+            raise ValueError("h0 is in the stored states")
+        _dev(states, "states", _states_shape(b, L, Dn, N), f32)
+    need = (ssm_scan_bwd_fused_saved_workspace if saved else ssm_scan_bwd_fused_workspace)(
+        b, L, Dn, N, K, io, chunk_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.ssm_scan_bwd_fused(
-        _ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+    st = getattr(lib, "ssm_scan_bwd_fused_saved" if saved else "ssm_scan_bwd_fused")(
+        _ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(states if saved else h0),
         _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_state0), _ptr(dt_bias), _ptr(dy), _ptr(dh_final),
         _ptr(out["dx_in"]), _ptr(out["ddt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
         _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out["dconv_w"]),
@@ -764,39 +810,48 @@ class _SelectiveScanFused(torch.autograd.Function):
     """ssm_scan_fwd_fused forwards, ssm_scan_bwd_fused backwards."""
 
     @staticmethod
-    def forward(ctx, x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias, chunk_len):
-        y, h_final, _ = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, conv_w=conv_w, conv_b=conv_b,
-                                           conv_state0=conv_state0, dt_bias=dt_bias, chunk_len=chunk_len,
-                                           want_conv_state=False)
-        ctx.save_for_backward(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias)
+    def forward(ctx, x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias, chunk_len,
+                save_states):
+        kw = dict(conv_w=conv_w, conv_b=conv_b, conv_state0=conv_state0, dt_bias=dt_bias,
+                  chunk_len=chunk_len, want_conv_state=False)
+        if save_states:
+            y, h_final, _, states = ssm_scan_fwd_fused_save(x_in, dt_raw, A, B, C, D, z, h0, **kw)
+        else:
+            y, h_final, _ = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, **kw)
+            states = None
+        ctx.save_for_backward(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias,
+                              states)
         ctx.chunk_len = chunk_len
         return y, h_final
 
     @staticmethod
     def backward(ctx, dy, dh_final):
-        x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias = ctx.saved_tensors
+        x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias, states = ctx.saved_tensors
         need = ctx.needs_input_grad
         if dy is None:
             dy = torch.zeros_like(x_in)
-        g = ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z, h0, conv_w=conv_w, conv_b=conv_b,
-                               conv_state0=conv_state0, dt_bias=dt_bias, dy=dy.to(x_in.dtype).contiguous(),
+        g = ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z, None if states is not None else h0,
+                               conv_w=conv_w, conv_b=conv_b, conv_state0=conv_state0, dt_bias=dt_bias,
+                               dy=dy.to(x_in.dtype).contiguous(),
                                dh_final=None if dh_final is None else dh_final.float().contiguous(),
                                chunk_len=ctx.chunk_len, want_dz=z is not None and need[6],
                                want_dh0=h0 is not None and need[7],
-                               want_dconv_state0=conv_state0 is not None and need[10])
+                               want_dconv_state0=conv_state0 is not None and need[10], states=states)
         cast = lambda t, like: None if (t is None or like is None) else t.to(like.dtype)
         grads = (g["dx_in"], g["ddt_raw"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
                  cast(g["dD"], D), g["dz"], g["dh0"], cast(g["dconv_w"], conv_w),
-                 cast(g["dconv_b"], conv_b), g["dconv_state0"], cast(g["ddt_bias"], dt_bias), None)
+                 cast(g["dconv_b"], conv_b), g["dconv_state0"], cast(g["ddt_bias"], dt_bias), None, None)
         return tuple(gr if need[i] else None for i, gr in enumerate(grads))
 
 
 def selective_scan_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
-                         conv_state0=None, dt_bias=None, chunk_len=0):
+                         conv_state0=None, dt_bias=None, chunk_len=0, save_states=False):
     """The fused prefill (input stage + scan) as a differentiable function: returns
-    (y, h_final), with gradients for every tensor input from ssm_scan_bwd_fused."""
+    (y, h_final), with gradients for every tensor input from ssm_scan_bwd_fused.
+    save_states: the forward stores the scan's state every 8 steps
+    (ssm_scan_fwd_fused_save) and the backward reads them (ssm_scan_bwd_fused_saved)."""
     return _SelectiveScanFused.apply(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0,
-                                     dt_bias, chunk_len)
+                                     dt_bias, chunk_len, save_states)
 
 
 # ------------------------------------------------------------------ MIMO projections

@@ -313,6 +313,7 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         a.conv_state0 = conv_rows ? in->conv_state0 : nullptr;
         a.conv_state_out = conv_rows ? in->conv_state : nullptr;
         a.dt_bias = in->dt_bias;
+        a.states = states;  // the fused training forward, or null
         e = ssm::launch_scan_fused(a, iot, d_state, z != nullptr, s, ev);
     } else if (trap) {
         a.x_prev = trap->x_prev;
@@ -677,6 +678,21 @@ ssm_status ssm_scan_fwd_fused(const void *x_in, const void *dt_raw, const float 
                        chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0, &in);
 }
 
+ssm_status ssm_scan_fwd_fused_save(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                                   const void *C, const float *D, const void *z, const float *h0,
+                                   const float *conv_w, const float *conv_b, int32_t conv_k,
+                                   const void *conv_state0, void *conv_state_out,
+                                   const float *dt_bias, void *y, float *h_final, float *states,
+                                   int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                                   ssm_dtype io, int64_t chunk_len, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream) {
+    if (batch > 0 && L > 0 && !states) return fail(SSM_ERR_NULL, "states is required");
+    const InputStage in{conv_w, conv_b, dt_bias, conv_k, conv_state0, conv_state_out};
+    return scan_common(x_in, dt_raw, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
+                       chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0, &in,
+                       nullptr, 0, false, batch > 0 && L > 0 ? states : nullptr);
+}
+
 ssm_status ssm_scan_fwd_fused_profiled(const void *x_in, const void *dt_raw, const float *A,
                                        const void *B, const void *C, const float *D,
                                        const void *z, const float *h0, const float *conv_w,
@@ -885,11 +901,12 @@ struct InBwdPlan {
 };
 
 ssm_status make_in_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                            int32_t conv_k, ssm_dtype io, int64_t chunk_len, InBwdPlan *p) {
+                            int32_t conv_k, ssm_dtype io, int64_t chunk_len, InBwdPlan *p,
+                            bool saved = false) {
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_DTYPE, "io dtype %d unknown", (int)io);
     if (conv_k < 0 || conv_k > 4) return fail(SSM_ERR_UNSUPPORTED, "conv_k %d not in 0..4", conv_k);
     BwdPlan bp;
-    const ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &bp);
+    const ssm_status st = make_bwd_plan(batch, L, d_inner, d_state, chunk_len, &bp, saved);
     if (st != SSM_OK) return st;
     const int64_t blocks = std::max<int64_t>(1, batch * ((d_inner + 255) / 256));
     const int64_t want = 8 * device_simds();
@@ -911,18 +928,19 @@ size_t ssm_scan_bwd_fused_workspace(int64_t batch, int64_t L, int64_t d_inner, i
     return p.bytes;
 }
 
-ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float *A, const void *B,
-                              const void *C, const float *D, const void *z, const float *h0,
-                              const float *conv_w, const float *conv_b, int32_t conv_k,
-                              const void *conv_state0, const float *dt_bias, const void *dy,
-                              const float *dh_final, void *dx_in, void *ddt_raw, void *dz,
-                              float *dA, float *dB, float *dC, float *dD, float *dh0,
-                              float *dconv_w, float *dconv_b, float *ddt_bias, void *dconv_state0,
-                              int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                              ssm_dtype io, int64_t chunk_len, void *workspace,
-                              size_t workspace_bytes, void *hip_stream) {
+namespace {
+ssm_status bwd_fused_common(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                            const void *C, const float *D, const void *z, const float *h0,
+                            const float *states, const float *conv_w, const float *conv_b,
+                            int32_t conv_k, const void *conv_state0, const float *dt_bias,
+                            const void *dy, const float *dh_final, void *dx_in, void *ddt_raw,
+                            void *dz, float *dA, float *dB, float *dC, float *dD, float *dh0,
+                            float *dconv_w, float *dconv_b, float *ddt_bias, void *dconv_state0,
+                            int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                            ssm_dtype io, int64_t chunk_len, void *workspace,
+                            size_t workspace_bytes, void *hip_stream, bool saved) {
     InBwdPlan p;
-    ssm_status st = make_in_bwd_plan(batch, L, d_inner, d_state, conv_k, io, chunk_len, &p);
+    ssm_status st = make_in_bwd_plan(batch, L, d_inner, d_state, conv_k, io, chunk_len, &p, saved);
     if (st != SSM_OK) return st;
     const size_t eb = io_bytes(io);
     st = check_input_stage(InputStage{conv_w, conv_b, dt_bias, conv_k, conv_state0, dconv_state0}, eb);
@@ -931,6 +949,8 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
     const bool work = batch > 0 && L > 0;
     if (work && (!x_in || !dt_raw || !dx_in || !ddt_raw))
         return fail(SSM_ERR_NULL, "x_in, dt_raw, dx_in and ddt_raw are required");
+    if (saved && work && !states) return fail(SSM_ERR_NULL, "states is required");
+    if (!aligned(states, 16)) return fail(SSM_ERR_ALIGN, "states must be 16-byte aligned");
     if (!aligned(x_in, eb) || !aligned(dt_raw, eb) || !aligned(dx_in, eb) || !aligned(ddt_raw, eb) ||
         !aligned(dconv_w, 4) || !aligned(dconv_b, 4) || !aligned(ddt_bias, 4))
         return fail(SSM_ERR_ALIGN, "pointer alignment (x_in, dt_raw, dx_in, ddt_raw element; dconv_w, dconv_b, ddt_bias 4 B)");
@@ -961,9 +981,9 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
         st = launch_status(ssm::launch_input_fwd(a, iot, s), "input stage (forward)");
         if (st != SSM_OK) return st;
     }
-    st = ssm_scan_bwd(a.u, a.dt, A, B, C, D, z, h0, dy, dh_final, const_cast<void *>(a.du),
-                      const_cast<void *>(a.ddt), dz, dA, dB, dC, dD, dh0, batch, L, d_inner, d_state,
-                      io, chunk_len, ws, p.scan_ws, hip_stream);
+    st = bwd_common(a.u, a.dt, A, B, C, D, z, saved ? nullptr : h0, dy, dh_final, const_cast<void *>(a.du),
+                    const_cast<void *>(a.ddt), dz, dA, dB, dC, dD, dh0, batch, L, d_inner, d_state,
+                    io, chunk_len, ws, p.scan_ws, hip_stream, saved && work ? states : nullptr);
     if (st != SSM_OK) return st;
     if (work) return launch_status(ssm::launch_input_bwd(a, iot, s), "input stage (backward)");
     // no steps: the input stage's own gradients are zero
@@ -977,6 +997,48 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
         if (st != SSM_OK) return st;
     }
     return ok();
+}
+}  // namespace
+
+ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float *A, const void *B,
+                              const void *C, const float *D, const void *z, const float *h0,
+                              const float *conv_w, const float *conv_b, int32_t conv_k,
+                              const void *conv_state0, const float *dt_bias, const void *dy,
+                              const float *dh_final, void *dx_in, void *ddt_raw, void *dz,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0,
+                              float *dconv_w, float *dconv_b, float *ddt_bias, void *dconv_state0,
+                              int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
+                              ssm_dtype io, int64_t chunk_len, void *workspace,
+                              size_t workspace_bytes, void *hip_stream) {
+    return bwd_fused_common(x_in, dt_raw, A, B, C, D, z, h0, nullptr, conv_w, conv_b, conv_k,
+                            conv_state0, dt_bias, dy, dh_final, dx_in, ddt_raw, dz, dA, dB, dC, dD,
+                            dh0, dconv_w, dconv_b, ddt_bias, dconv_state0, batch, L, d_inner,
+                            d_state, io, chunk_len, workspace, workspace_bytes, hip_stream, false);
+}
+
+size_t ssm_scan_bwd_fused_saved_workspace(int64_t batch, int64_t L, int64_t d_inner,
+                                          int32_t d_state, int32_t conv_k, ssm_dtype io,
+                                          int64_t chunk_len) {
+    InBwdPlan p;
+    if (make_in_bwd_plan(batch, L, d_inner, d_state, conv_k, io, chunk_len, &p, true) != SSM_OK) return 0;
+    return p.bytes;
+}
+
+ssm_status ssm_scan_bwd_fused_saved(const void *x_in, const void *dt_raw, const float *A,
+                                    const void *B, const void *C, const float *D, const void *z,
+                                    const float *states, const float *conv_w, const float *conv_b,
+                                    int32_t conv_k, const void *conv_state0, const float *dt_bias,
+                                    const void *dy, const float *dh_final, void *dx_in,
+                                    void *ddt_raw, void *dz, float *dA, float *dB, float *dC,
+                                    float *dD, float *dh0, float *dconv_w, float *dconv_b,
+                                    float *ddt_bias, void *dconv_state0, int64_t batch, int64_t L,
+                                    int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                    int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream) {
+    return bwd_fused_common(x_in, dt_raw, A, B, C, D, z, nullptr, states, conv_w, conv_b, conv_k,
+                            conv_state0, dt_bias, dy, dh_final, dx_in, ddt_raw, dz, dA, dB, dC, dD,
+                            dh0, dconv_w, dconv_b, ddt_bias, dconv_state0, batch, L, d_inner,
+                            d_state, io, chunk_len, workspace, workspace_bytes, hip_stream, true);
 }
 
 const char *ssm_status_str(ssm_status s) {

@@ -32,6 +32,8 @@
 // it is loaded (ssm_input_stage.h). Every lane then walks its chunk with the last
 // KC-1 convolution inputs in registers, starting from the rows just before the
 // chunk (or the carried convolution state before step 0).
+#include <type_traits>
+
 #include "ssm_device.h"
 #include "ssm_input_stage.h"
 #include "ssm_internal.h"
@@ -126,6 +128,13 @@ struct MambaInput {
             }
         }
     }
+};
+
+// The fused training forward: MambaInput's prefill that also stores the state entering
+// every kStateEvery-th step (ScanArgs::states), as SaveInput does for the plain scan.
+template <typename IO, int KC>
+struct MambaSave : MambaInput<IO, KC> {
+    static constexpr bool kSave = true;
 };
 
 // The exponential-trapezoidal discretisation (the Mamba-3 item of "Jamba —
@@ -505,15 +514,18 @@ hipError_t launch_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
     return hipErrorInvalidValue;
 }
 
-template <typename IO>
+template <typename IO, int KC, bool SAVE>
+using FusedIn = typename std::conditional<SAVE, MambaSave<IO, KC>, MambaInput<IO, KC>>::type;
+
+template <typename IO, bool SAVE>
 hipError_t launch_fused_io(const ScanArgs &a, int d_state, bool gated, hipStream_t s,
                            hipEvent_t const *ev) {
     switch (a.conv_k) {
-        case 0: return launch_io<IO, MambaInput<IO, 0>>(a, d_state, gated, s, ev);
-        case 1: return launch_io<IO, MambaInput<IO, 1>>(a, d_state, gated, s, ev);
-        case 2: return launch_io<IO, MambaInput<IO, 2>>(a, d_state, gated, s, ev);
-        case 3: return launch_io<IO, MambaInput<IO, 3>>(a, d_state, gated, s, ev);
-        case 4: return launch_io<IO, MambaInput<IO, 4>>(a, d_state, gated, s, ev);
+        case 0: return launch_io<IO, FusedIn<IO, 0, SAVE>>(a, d_state, gated, s, ev);
+        case 1: return launch_io<IO, FusedIn<IO, 1, SAVE>>(a, d_state, gated, s, ev);
+        case 2: return launch_io<IO, FusedIn<IO, 2, SAVE>>(a, d_state, gated, s, ev);
+        case 3: return launch_io<IO, FusedIn<IO, 3, SAVE>>(a, d_state, gated, s, ev);
+        case 4: return launch_io<IO, FusedIn<IO, 4, SAVE>>(a, d_state, gated, s, ev);
     }
     return hipErrorInvalidValue;
 }
@@ -543,8 +555,11 @@ hipError_t launch_scan_trap(const ScanArgs &a, int io, int d_state, bool gated, 
 
 hipError_t launch_scan_fused(const ScanArgs &a, int io, int d_state, bool gated, hipStream_t s,
                              hipEvent_t const *ev) {
-    return io == 0 ? launch_fused_io<float>(a, d_state, gated, s, ev)
-                   : launch_fused_io<bf16_bits>(a, d_state, gated, s, ev);
+    if (a.states)
+        return io == 0 ? launch_fused_io<float, true>(a, d_state, gated, s, ev)
+                       : launch_fused_io<bf16_bits, true>(a, d_state, gated, s, ev);
+    return io == 0 ? launch_fused_io<float, false>(a, d_state, gated, s, ev)
+                   : launch_fused_io<bf16_bits, false>(a, d_state, gated, s, ev);
 }
 
 namespace {

@@ -397,6 +397,39 @@ def test_fused_backward_argument_errors(lib):
     assert lib.ssm_scan_bwd_fused_workspace(1, 8, 4, 3, 2, 0, 0) == 0
 
 
+def test_fused_stored_state_argument_errors(lib):
+    # ssm_scan_fwd_fused_save and ssm_scan_bwd_fused_saved: checked before any launch.
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+
+    def fwd(states=0x4000, L=8, N=4, chunk=0, ws=None, wsb=0):
+        return lib.ssm_scan_fwd_fused_save(p(0x100000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                           p(0x1000), None, None, p(0x1000), None, 4, None, None,
+                                           None, p(0x200000), None, p(states), 1, L, 4, N, 0, chunk,
+                                           p(ws), wsb, None)
+
+    def bwd(states=0x4000, L=8, ws=None, wsb=0, chunk=0):
+        return lib.ssm_scan_bwd_fused_saved(p(0x100000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                            p(0x1000), None, p(states), p(0x1000), None, 3, None,
+                                            None, p(0x1000), None, p(0x300000), p(0x1000), None,
+                                            p(0x1000), p(0x1000), p(0x1000), p(0x1000), None,
+                                            p(0x2000), None, None, None, 1, L, 4, 4, 0, chunk, p(ws),
+                                            wsb, None)
+    assert fwd(states=None) == NULL and bwd(states=None) == NULL
+    assert fwd(states=0x4008) == ALIGN and bwd(states=0x4008) == ALIGN
+    assert fwd(N=3) == UNSUP
+    assert fwd(states=None, L=0) != NULL and bwd(states=None, L=0) != NULL
+    need = lib.ssm_scan_bwd_fused_saved_workspace(1, 8, 4, 4, 3, 0, 0)
+    assert need > 0 and bwd() == WS
+    assert bwd(ws=0x10000, wsb=need - 1) == WS
+    # no stored states of its own: less than the plain fused backward's workspace
+    assert (lib.ssm_scan_bwd_fused_saved_workspace(1, 2000, 64, 16, 4, 0, 64)
+            < lib.ssm_scan_bwd_fused_workspace(1, 2000, 64, 16, 4, 0, 64))
+    # chunk lengths are rounded down to a multiple of 8 (at least 8)
+    assert (lib.ssm_scan_bwd_fused_saved_workspace(1, 200, 4, 4, 4, 0, 20)
+            == lib.ssm_scan_bwd_fused_saved_workspace(1, 200, 4, 4, 4, 0, 16))
+    assert lib.ssm_scan_bwd_fused_saved_workspace(1, 8, 4, 4, 9, 0, 0) == 0
+
+
 def test_bench_refuses_more_than_one_gpu():
     # The benchmark measures one GPU; asked for more it exits with a message (before
     # touching a GPU or torch).

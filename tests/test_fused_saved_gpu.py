@@ -1,0 +1,141 @@
+"""Training the fused prefill with stored states on the GPU: ssm_scan_fwd_fused_save
+(the fused forward that also stores the scan's state entering every 8th step) and
+ssm_scan_bwd_fused_saved (the fused backward that reads those states instead of
+recomputing them).
+
+- The forward's y, h_final and conv state equal ssm_scan_fwd_fused's bit for bit for
+  the same chunk length (a multiple of 8), and stored rows equal the oracle's state
+  after 8 r steps of the fused prefill (the oracle's scan_fused over the first 8 r
+  steps) to the forward's tolerance.
+- The backward's gradients match the oracle's scan_fused_bwd to the fused backward's
+  tolerance on the plain fused backward's cases.
+- selective_scan_fused(save_states=True) returns exactly what the direct calls return.
+"""
+import pytest
+import torch
+
+import oracle
+import selective_state_space_49_amd as ssm
+from tests.gpu_util import TOL, bitwise_equal, rel_err, say, to_dev
+from tests.test_fused_bwd_gpu import CASES, GRADS, _draw, _ids, _oracle
+
+pytestmark = pytest.mark.gpu
+EVERY = ssm.STATE_EVERY
+
+
+def _rows(states, b, Dn, N):
+    """Stored states as [rows, b, Dn, N]."""
+    if N % 4 == 0:
+        return states.permute(0, 1, 3, 2, 4).reshape(states.shape[0], b, Dn, N)
+    return states
+
+
+def _fwd(fn, g, t, chunk_len):
+    return fn(g["x"], t["dt_raw"], g["A"], g["B"], g["C"], g["D"], g["z"], g["h0"], conv_w=t["conv_w"],
+              conv_b=t["conv_b"], conv_state0=t["conv_state0"], dt_bias=t["dt_bias"], chunk_len=chunk_len)
+
+
+def _oracle_fwd(x, dt_raw, B, C, z, d, s):
+    """The oracle's fused prefill; without a filter (conv_k = 0) the scan runs on x_in."""
+    if s["conv_w"] is None:
+        return oracle.scan(x, oracle.softplus(dt_raw, s["dt_bias"]), d["A"], B, C, d["D"], z, d["h0"])
+    y, hf, _ = oracle.scan_fused(x, dt_raw, d["A"], B, C, d["D"], z, d["h0"], conv_w=s["conv_w"],
+                                 conv_b=s["conv_b"], conv_state0=s["conv_state0"], dt_bias=s["dt_bias"])
+    return y, hf
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_fused_forward_save_matches_fused_and_stores_the_oracle_states(case):
+    d, s = _draw(case, seed=610)
+    b, L, Dn, N, io = case[:5]
+    T = case[7] // EVERY * EVERY
+    g, t = to_dev(d), to_dev(s)
+    say("fused forward with stored states", _ids(case))
+    y, hf, cs, st = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, T)
+    torch.cuda.synchronize()
+    if T > 0:  # the same chunks as ssm_scan_fwd_fused: the same bits
+        y2, hf2, cs2 = _fwd(ssm.ssm_scan_fwd_fused, g, t, T)
+        torch.cuda.synchronize()
+        assert bitwise_equal(y, y2) and bitwise_equal(hf, hf2)
+        assert (cs is None) == (cs2 is None) and (cs is None or bitwise_equal(cs, cs2))
+    tol = TOL[io]
+    yr, hr = _oracle_fwd(d["x"], s["dt_raw"], d["B"], d["C"], d["z"], d, s)
+    assert rel_err(y, yr) <= tol and rel_err(hf, hr) <= tol
+    rows = _rows(st, b, Dn, N).cpu()
+    n = rows.shape[0]
+    assert n == (L + EVERY - 1) // EVERY
+    cut = lambda v, k: None if v is None else v[:, :k]
+    for r in sorted({0, 1, n // 2, n - 1} & set(range(n))):
+        k = r * EVERY
+        if k == 0:
+            ref = torch.zeros((b, Dn, N), dtype=torch.float64) if d["h0"] is None else d["h0"].double()
+        else:
+            _, ref = _oracle_fwd(d["x"][:, :k], s["dt_raw"][:, :k], d["B"][:, :k], d["C"][:, :k],
+                                 cut(d["z"], k), d, s)
+        e = rel_err(rows[r], ref)
+        assert e <= tol, f"stored state {r} (step {k}): error {e:.3e}"
+
+
+def _saved(d, s, chunk_len):
+    g, t = to_dev(d), to_dev(s)
+    _, _, _, st = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, chunk_len)
+    return ssm.ssm_scan_bwd_fused_saved(g["x"], t["dt_raw"], g["A"], g["B"], g["C"], g["D"], g["z"],
+                                        states=st, conv_w=t["conv_w"], conv_b=t["conv_b"],
+                                        conv_state0=t["conv_state0"], dt_bias=t["dt_bias"], dy=g["dy"],
+                                        dh_final=g["dh_final"], chunk_len=chunk_len)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_fused_backward_from_stored_states_matches_oracle(case):
+    d, s = _draw(case)
+    say("fused backward from stored states", _ids(case))
+    got = _saved(d, s, case[7])
+    torch.cuda.synchronize()
+    ref = _oracle(d, s)
+    tol = TOL[case[4]]
+    for k in GRADS:
+        if ref.get(k) is None:
+            assert got[k] is None, f"{k} should be absent"
+            continue
+        assert got[k] is not None, f"{k} missing"
+        e = rel_err(got[k], ref[k])
+        assert e <= tol, f"{k}: error {e:.3e} > {tol}"
+
+
+def test_fused_training_with_no_steps():
+    case = (2, 0, 16, 4, "f32", True, 4, 0, True, True, True)
+    d, s = _draw(case, seed=611)
+    g, t = to_dev(d), to_dev(s)
+    say("fused training with stored states, L = 0")
+    y, hf, cs, st = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, 0)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and st.numel() == 0
+    assert bitwise_equal(hf, g["h0"]) and bitwise_equal(cs, t["conv_state0"])
+    out = _saved(d, s, 0)
+    torch.cuda.synchronize()
+    for k in ("dA", "dB", "dC", "dD", "dconv_w", "dconv_b", "ddt_bias", "dconv_state0"):
+        assert out[k] is not None and not out[k].any(), f"{k} should be 0 for L = 0"
+
+
+def test_selective_scan_fused_with_stored_states():
+    case = (2, 200, 96, 16, "bf16", True, 4, 48, True, True, True)
+    d, s = _draw(case, seed=612)
+    g, t = to_dev(d), to_dev(s)
+    names = ("x", "dt_raw", "A", "B", "C", "D", "z", "conv_w", "conv_b", "conv_state0", "dt_bias")
+    src = {**g, **t}
+    leaves = {k: src[k].clone().requires_grad_(True) for k in names}
+    say("selective_scan_fused with stored states")
+    y, hf = ssm.selective_scan_fused(leaves["x"], leaves["dt_raw"], leaves["A"], leaves["B"], leaves["C"],
+                                     leaves["D"], leaves["z"], g["h0"], conv_w=leaves["conv_w"],
+                                     conv_b=leaves["conv_b"], conv_state0=leaves["conv_state0"],
+                                     dt_bias=leaves["dt_bias"], chunk_len=48, save_states=True)
+    ((y.float() * g["dy"].float()).sum() + (hf * g["dh_final"]).sum()).backward()
+    y_ref, hf_ref, _, _ = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, 48)
+    ref = _saved(d, s, 48)
+    torch.cuda.synchronize()
+    assert bitwise_equal(y.detach(), y_ref) and bitwise_equal(hf.detach(), hf_ref)
+    gname = {"x": "dx_in", "dt_raw": "ddt_raw"}
+    for k in names:
+        grad, want = leaves[k].grad, ref[gname.get(k, "d" + k)]
+        assert grad is not None and grad.dtype == leaves[k].dtype, k
+        assert bitwise_equal(grad, want.to(grad.dtype)), f"{k}: gradient differs from ssm_scan_bwd_fused_saved"
