@@ -10,14 +10,20 @@ recomputing them).
 - The backward's gradients match the oracle's scan_fused_bwd to the fused backward's
   tolerance on the plain fused backward's cases.
 - selective_scan_fused(save_states=True) returns exactly what the direct calls return.
+- Full size: the 256k prefill with a 4-tap filter, both fused backwards (from the
+  recomputed states and from the stored ones) on a channel sample against the oracle.
 """
+import threading
+
+import numpy as np
 import pytest
 import torch
 
 import oracle
 import selective_state_space_49_amd as ssm
-from tests.gpu_util import TOL, bitwise_equal, rel_err, say, to_dev
+from tests.gpu_util import TOL, bitwise_equal, gather_channels, rel_err, say, to_dev
 from tests.test_fused_bwd_gpu import CASES, GRADS, _draw, _ids, _oracle
+from workloads import WORKLOADS, make_input_stage, make_scan_inputs, sample_channels
 
 pytestmark = pytest.mark.gpu
 EVERY = ssm.STATE_EVERY
@@ -139,3 +145,80 @@ def test_selective_scan_fused_with_stored_states():
         grad, want = leaves[k].grad, ref[gname.get(k, "d" + k)]
         assert grad is not None and grad.dtype == leaves[k].dtype, k
         assert bitwise_equal(grad, want.to(grad.dtype)), f"{k}: gradient differs from ssm_scan_bwd_fused_saved"
+
+
+def _oracle_fused_threaded(d, s, threads=16):
+    """The oracle's scan_fused_bwd on disjoint channel groups from several threads:
+    per-channel gradients are concatenated, dB and dC (sums over channels) added up."""
+    Dn = d["x"].shape[2]
+    parts = [p for p in np.array_split(np.arange(Dn), threads) if len(p)]
+    res = [None] * len(parts)
+    f = {k: (None if v is None else oracle.to_f64(v)) for k, v in {**d, **s}.items()}
+
+    def work(i, idx):
+        sub = lambda a, ax: None if a is None else np.ascontiguousarray(np.take(a, idx, axis=ax))
+        res[i] = oracle.scan_fused_bwd(sub(f["x"], 2), sub(f["dt_raw"], 2), f["A"][idx], f["B"], f["C"],
+                                       f["D"][idx], sub(f["z"], 2), None, conv_w=f["conv_w"][idx],
+                                       conv_b=f["conv_b"][idx], conv_state0=sub(f["conv_state0"], 2),
+                                       dt_bias=f["dt_bias"][idx], dy=sub(f["dy"], 2))
+
+    ts = [threading.Thread(target=work, args=(i, idx)) for i, idx in enumerate(parts)]
+    for t in ts: t.start()
+    for t in ts: t.join()
+    out = {}
+    for k, ax in (("dx_in", 2), ("ddt_raw", 2), ("dz", 2), ("dA", 0), ("dD", 0), ("dconv_w", 0),
+                  ("dconv_b", 0), ("ddt_bias", 0), ("dconv_state0", 2)):
+        out[k] = np.concatenate([r[k] for r in res], axis=ax)
+    out["dB"] = sum(r["dB"] for r in res)
+    out["dC"] = sum(r["dC"] for r in res)
+    return out
+
+
+def test_fused_backwards_full_size_long_context_sampled():
+    # The 256k prefill (batch 1, L 262144, 8192 channels, N 16, bf16) with a 4-tap filter,
+    # in the library's own plans as the benchmark times them. dy is nonzero on a channel
+    # sample only: channels stay independent through the depthwise filter, so every other
+    # channel's gradients are exactly 0 and dB, dC hold the sample's contributions.
+    shape = WORKLOADS["long_context_256k"]
+    say("fused backwards 256k: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    s = make_input_stage(shape, 4, "cuda")
+    idx = sample_channels(shape.d_inner, 256, seed=19)
+    g = torch.Generator(device="cuda").manual_seed(89)
+    dy = torch.zeros(d["x"].shape, dtype=d["x"].dtype, device="cuda")
+    dy[:, :, idx.cuda()] = torch.randn((shape.batch, shape.L, len(idx)), generator=g,
+                                       device="cuda").to(dy.dtype)
+    kw = dict(conv_w=s["conv_w"], conv_b=s["conv_b"], conv_state0=s["conv_state0"], dt_bias=s["dt_bias"])
+    say("fused backwards 256k: ssm_scan_bwd_fused")
+    got = {"recomputed": ssm.ssm_scan_bwd_fused(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                                dy=dy, **kw)}
+    torch.cuda.synchronize()
+    say("fused backwards 256k: training forward and ssm_scan_bwd_fused_saved")
+    _, _, _, st = ssm.ssm_scan_fwd_fused_save(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                              want_conv_state=False, **kw)
+    got["stored"] = ssm.ssm_scan_bwd_fused_saved(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"],
+                                                 d["z"], states=st, dy=dy, **kw)
+    torch.cuda.synchronize()
+    del st
+    rest = torch.ones(shape.d_inner, dtype=torch.bool)
+    rest[idx] = False
+    gc = lambda t: gather_channels(t, idx)
+    sub_d = {"x": gc(d["x"]), "z": gc(d["z"]), "dy": gc(dy), "A": d["A"].cpu()[idx], "B": d["B"].cpu(),
+             "C": d["C"].cpu(), "D": d["D"].cpu()[idx]}
+    sub_s = {"dt_raw": gc(s["dt_raw"]), "conv_w": s["conv_w"].cpu()[idx], "conv_b": s["conv_b"].cpu()[idx],
+             "conv_state0": gc(s["conv_state0"]), "dt_bias": s["dt_bias"].cpu()[idx]}
+    say("fused backwards 256k: oracle on", len(idx), "channels")
+    ref = _oracle_fused_threaded(sub_d, sub_s)
+    tol = TOL["bf16"]
+    for name, out in got.items():
+        for k in ("dx_in", "ddt_raw", "dz", "dconv_state0"):
+            assert not out[k][:, :, rest.cuda()].any(), f"{name}: {k} nonzero outside the sample"
+            e = rel_err(gc(out[k]), ref[k])
+            assert e <= tol, f"{name}: {k}: error {e:.3e}"
+        for k in ("dA", "dD", "dconv_w", "dconv_b", "ddt_bias"):
+            assert not out[k][rest.cuda()].any(), f"{name}: {k} nonzero outside the sample"
+            e = rel_err(out[k].cpu()[idx], ref[k])
+            assert e <= tol, f"{name}: {k}: error {e:.3e}"
+        for k in ("dB", "dC"):
+            e = rel_err(out[k], ref[k])
+            assert e <= tol, f"{name}: {k}: error {e:.3e}"
