@@ -53,6 +53,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -81,10 +82,16 @@ def log(*a):
 
 
 def source_hash(kind: str) -> str:
+    """Hash of the code (comments and whitespace removed) of a kernel kind's sources: the
+    stored traffic of a kernel is reported only while this hash is the one it was
+    counted under."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind] + COMMON_HEADERS:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

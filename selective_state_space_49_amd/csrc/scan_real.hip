@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
                 // the state entering step t (chunks start at multiples of kStateEvery),
                 // through a buffer resource based at its row (a row is below 2 GiB);
                 // streaming stores (glc slc), as the compiler's nontemporal stores are:
-                // 7.74-7.93 -> 7.51-7.59 ms for the 256k forward on one box
+                // 7.74-7.93 -> 7.51-7.59 ms for the 256k forward on one MI355X
                 if (i % kStateEvery == 0) {
                     const auto r = __builtin_amdgcn_make_buffer_rsrc(
                         a.states + (size_t)(t / kStateEvery) * a.batch * a.Dn * N, 0, -1, kRsrcWord3);
