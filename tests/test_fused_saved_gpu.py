@@ -8,7 +8,7 @@ recomputing them).
   after 8 r steps of the fused prefill (the oracle's scan_fused over the first 8 r
   steps) to the forward's tolerance.
 - The backward's gradients match the oracle's scan_fused_bwd to the fused backward's
-  tolerance on the plain fused backward's cases.
+  tolerance on the plain fused backward's cases and two with fewer than 4 states.
 - selective_scan_fused(save_states=True) returns exactly what the direct calls return.
 - Full size: the 256k prefill with a 4-tap filter, both fused backwards (from the
   recomputed states and from the stored ones) on a channel sample against the oracle.
@@ -27,6 +27,11 @@ from workloads import WORKLOADS, make_input_stage, make_scan_inputs, sample_chan
 
 pytestmark = pytest.mark.gpu
 EVERY = ssm.STATE_EVERY
+# the fused backward's cases, and state sizes below 4 (stored as [batch][D][N] rows)
+SAVE_CASES = CASES + [
+    (2, 203, 65, 2, "f32", True, 3, 16, True, True, True),
+    (3, 129, 64, 1, "bf16", True, 4, 16, True, True, True),
+]
 
 
 def _rows(states, b, Dn, N):
@@ -50,7 +55,7 @@ def _oracle_fwd(x, dt_raw, B, C, z, d, s):
     return y, hf
 
 
-@pytest.mark.parametrize("case", CASES, ids=_ids)
+@pytest.mark.parametrize("case", SAVE_CASES, ids=_ids)
 def test_fused_forward_save_matches_fused_and_stores_the_oracle_states(case):
     d, s = _draw(case, seed=610)
     b, L, Dn, N, io = case[:5]
@@ -91,7 +96,7 @@ def _saved(d, s, chunk_len):
                                         dh_final=g["dh_final"], chunk_len=chunk_len)
 
 
-@pytest.mark.parametrize("case", CASES, ids=_ids)
+@pytest.mark.parametrize("case", SAVE_CASES, ids=_ids)
 def test_fused_backward_from_stored_states_matches_oracle(case):
     d, s = _draw(case)
     say("fused backward from stored states", _ids(case))
