@@ -266,14 +266,17 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         fws = torch.empty(max(ssm.ssm_scan_fwd_save_workspace(b, L, Dn, N, chunk_len), 1),
                           dtype=torch.uint8, device=dev)
         yb = torch.empty_like(d["x"])
+        # the fused training forward stores the scan's inputs u and dt as well
+        u_st = torch.empty_like(d["x"]) if fused else None
+        dt_st = torch.empty_like(d["x"]) if fused else None
 
         def fwd():
             if fused:
                 ssm.ssm_scan_fwd_fused_save(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                             conv_w=d["conv_w"], conv_b=d["conv_b"],
                                             conv_state0=d["conv_state0"], dt_bias=d["dt_bias"], y=yb,
-                                            states=states, chunk_len=chunk_len, workspace=fws,
-                                            want_conv_state=False)
+                                            states=states, u_out=u_st, dt_out=dt_st, chunk_len=chunk_len,
+                                            workspace=fws, want_conv_state=False)
                 return
             ssm.ssm_scan_fwd_save(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], y=yb,
                                   states=states, chunk_len=chunk_len, workspace=fws)
@@ -292,7 +295,7 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
     def call():
         if saved and fused:
             ssm.ssm_scan_bwd_fused_saved(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
-                                         states=states, conv_w=d["conv_w"], conv_b=d["conv_b"],
+                                         states=states, u=u_st, dt=dt_st, conv_w=d["conv_w"], conv_b=d["conv_b"],
                                          conv_state0=d["conv_state0"], dt_bias=d["dt_bias"], dy=dy,
                                          chunk_len=chunk_len, workspace=ws, want_dh0=False,
                                          want_dconv_state0=False)
@@ -333,9 +336,10 @@ def run_backward(shape, steps, warmup, torch, ssm, workloads, chunk_len=0, conv_
         # recompute of u, dt (x_in, dt_raw read; u, dt written) and the chain rule (x_in,
         # dt_raw, du, ddt read; dx_in, ddt_raw written): 10 more streams; the input stage
         # forward once more, and its backward: per tap an fma for a_t, dx_in and dw, silu'
-        # (exp, add, rcp, sub, fma, 2 mul) and softplus' (add, mul, exp, add, rcp, mul, add)
-        nbytes += 10 * shape.elements * io_bytes
-        lane_ops += input_stage_lane_ops(conv_k) + 3 * conv_k + 14
+        # (exp, add, rcp, sub, fma, 2 mul) and softplus' (add, mul, exp, add, rcp, mul, add).
+        # From the fused training forward's u and dt (saved): the chain rule only.
+        nbytes += (6 if saved else 10) * shape.elements * io_bytes
+        lane_ops += (0 if saved else input_stage_lane_ops(conv_k)) + 3 * conv_k + 14
     phases = {"backward_call": gpu_ms}
     if saved:
         phases["forward_with_stored_states"] = fwd_ms

@@ -393,24 +393,33 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
  * ssm_scan_fwd_fused that also writes the scan's state entering every 8th step to
  * `states`, in ssm_scan_fwd_save's layout and size (ssm_scan_fwd_save_states_bytes; its
  * chunks rounded as ssm_scan_fwd_save rounds them, and ssm_scan_fwd_save_workspace bytes
- * of workspace suffice); ssm_scan_bwd_fused_saved is ssm_scan_bwd_fused given those
- * states instead of h0 (the scan's backward reads them as ssm_scan_bwd_saved does), with
- * ssm_scan_bwd_fused_saved_workspace bytes of workspace. Errors as in the fused and
- * stored-state entry points above. */
+ * of workspace suffice), and the scan's inputs as the input stage makes them, u =
+ * silu(conv(x_in)) to u_out and dt = softplus(dt_raw + dt_bias) to dt_out ([batch][L]
+ * [d_inner] of io each, rounded to io as ssm_scan_bwd_fused rounds them; neither may
+ * overlap x_in, dt_raw, y or the other: SSM_ERR_UNSUPPORTED). ssm_scan_bwd_fused_saved
+ * is ssm_scan_bwd_fused given those states (instead of h0), u and dt: the scan's backward
+ * reads the states as ssm_scan_bwd_saved does and runs on the given u and dt, so the
+ * input stage is not evaluated again before it; ssm_scan_bwd_fused_saved_workspace bytes
+ * of workspace (no u and dt of its own). The gradients agree with ssm_scan_bwd_fused's
+ * to rounding (the stored states come from the forward's unrounded u and dt, the
+ * recomputed ones from the rounded). Errors as in the fused and stored-state entry points
+ * above; states, u_out and dt_out (u and dt) are required when batch * L > 0. */
 ssm_status ssm_scan_fwd_fused_save(const void *x_in, const void *dt_raw, const float *A, const void *B,
                                    const void *C, const float *D, const void *z, const float *h0,
                                    const float *conv_w, const float *conv_b, int32_t conv_k,
                                    const void *conv_state0, void *conv_state_out,
                                    const float *dt_bias, void *y, float *h_final, float *states,
-                                   int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                                   ssm_dtype io, int64_t chunk_len, void *workspace,
-                                   size_t workspace_bytes, void *hip_stream);
+                                   void *u_out, void *dt_out, int64_t batch, int64_t L,
+                                   int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                   int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream);
 size_t ssm_scan_bwd_fused_saved_workspace(int64_t batch, int64_t L, int64_t d_inner,
                                           int32_t d_state, int32_t conv_k, ssm_dtype io,
                                           int64_t chunk_len);
 ssm_status ssm_scan_bwd_fused_saved(const void *x_in, const void *dt_raw, const float *A,
                                     const void *B, const void *C, const float *D, const void *z,
-                                    const float *states, const float *conv_w, const float *conv_b,
+                                    const float *states, const void *u, const void *dt,
+                                    const float *conv_w, const float *conv_b,
                                     int32_t conv_k, const void *conv_state0, const float *dt_bias,
                                     const void *dy, const float *dh_final, void *dx_in,
                                     void *ddt_raw, void *dz, float *dA, float *dB, float *dC,

@@ -110,7 +110,7 @@ def load_library():
     fused = [vp] * 10 + [i32, vp, vp, vp, vp, vp, i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_fused"] = (fused, ci)
     sig["ssm_scan_fwd_fused_profiled"] = (fused + [vp, i32], ci)
-    sig["ssm_scan_fwd_fused_save"] = ([vp] * 10 + [i32] + [vp] * 6 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
+    sig["ssm_scan_fwd_fused_save"] = ([vp] * 10 + [i32] + [vp] * 8 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     sig["ssm_scan_bwd_workspace"] = ([i64, i64, i64, i32, i64], sz)
     sig["ssm_scan_bwd"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     sig["ssm_scan_bwd_saved"] = ([vp] * 18 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
@@ -120,7 +120,7 @@ def load_library():
     sig["ssm_scan_fwd_save_states_bytes"] = ([i64, i64, i64, i32], sz)
     sig["ssm_scan_bwd_fused_workspace"] = ([i64, i64, i64, i32, i32, ci, i64], sz)
     sig["ssm_scan_bwd_fused"] = ([vp] * 10 + [i32] + [vp] * 16 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
-    sig["ssm_scan_bwd_fused_saved"] = sig["ssm_scan_bwd_fused"]
+    sig["ssm_scan_bwd_fused_saved"] = ([vp] * 12 + [i32] + [vp] * 16 + [i64, i64, i64, i32, ci, i64, vp, sz, vp], ci)
     sig["ssm_scan_bwd_fused_saved_workspace"] = sig["ssm_scan_bwd_fused_workspace"]
     trap = [vp] * 13 + [i64, i64, i64, i32, ci, i64, vp, sz, vp]
     sig["ssm_scan_fwd_trap"] = (trap, ci)
@@ -505,12 +505,13 @@ def _input_stage(conv_w, conv_b, dt_bias, lead, Dn, conv_k):
 def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
                        conv_state0=None, dt_bias=None, chunk_len=0, y=None, h_final=None,
                        conv_state_out=None, workspace=None, want_h_final=True,
-                       want_conv_state=True, events=None, states=None):
+                       want_conv_state=True, events=None, states=None, u_out=None, dt_out=None):
     """Prefill with the MambaBlock input stage fused into the load: the scan runs on
     u = silu(causal depthwise conv(x_in)) and dt = softplus(dt_raw + dt_bias).
     conv_w [d_inner, K] (None: no convolution); conv_b, dt_bias [d_inner] or None;
     conv_state0 [b, K-1, d_inner] or None (zeros). Returns (y, h_final, conv_state_out).
-    states (see ssm_scan_fwd_fused_save): ssm_scan_fwd_fused_save stores them there."""
+    states, u_out, dt_out (see ssm_scan_fwd_fused_save): ssm_scan_fwd_fused_save stores
+    them there."""
     lib = load_library()
     b, L, Dn = x_in.shape
     N = A.shape[1]
@@ -537,6 +538,10 @@ def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None
     save = states is not None
     if save:
         _dev(states, "states", _states_shape(b, L, Dn, N), f32)
+        _dev(u_out, "u_out", (b, L, Dn), x_in.dtype)
+        _dev(dt_out, "dt_out", (b, L, Dn), x_in.dtype)
+        if u_out is None or dt_out is None:
+            raise ValueError("the fused training forward stores u and dt too: give u_out and dt_out")
     need = (ssm_scan_fwd_save_workspace if save else ssm_scan_fwd_workspace_ex)(b, L, Dn, N, chunk_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x_in.device)
@@ -549,7 +554,7 @@ def ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None
     if save:
         if events is not None:
             raise ValueError("the fused training forward is not profiled")
-        st = lib.ssm_scan_fwd_fused_save(*head, _ptr(states), *tail)
+        st = lib.ssm_scan_fwd_fused_save(*head, _ptr(states), _ptr(u_out), _ptr(dt_out), *tail)
         _check(st)
         return y, h_final, conv_state_out
     if events is not None:
@@ -568,15 +573,22 @@ def ssm_scan_fwd_fused_profiled(*a, events, **k):
     return ssm_scan_fwd_fused(*a, events=events, **k)
 
 
-def ssm_scan_fwd_fused_save(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, states=None, **k):
-    """The fused training forward: ssm_scan_fwd_fused's results and the scan's state
-    entering every 8th step (float32, shaped as _states_shape) for ssm_scan_bwd_fused_saved.
-    Returns (y, h_final, conv_state_out, states)."""
+def ssm_scan_fwd_fused_save(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, states=None, u_out=None,
+                            dt_out=None, **k):
+    """The fused training forward: ssm_scan_fwd_fused's results, the scan's state entering
+    every 8th step (float32, shaped as _states_shape) and its inputs u and dt (x_in's
+    dtype and shape) for ssm_scan_bwd_fused_saved.
+    Returns (y, h_final, conv_state_out, states, u, dt)."""
     b, L, Dn = x_in.shape
     if states is None:
         states = torch.empty(_states_shape(b, L, Dn, A.shape[1]), dtype=torch.float32, device=x_in.device)
-    y, hf, cs = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, states=states, **k)
-    return y, hf, cs, states
+    if u_out is None:
+        u_out = torch.empty_like(x_in)
+    if dt_out is None:
+        dt_out = torch.empty_like(x_in)
+    y, hf, cs = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, states=states, u_out=u_out,
+                                   dt_out=dt_out, **k)
+    return y, hf, cs, states, u_out, dt_out
 
 
 def _step_fused(fn_name, h, conv_state, x, dt, A, B, C, D, z, conv_w, conv_b, dt_bias, y):
@@ -701,21 +713,21 @@ def ssm_scan_bwd_fused_saved_workspace(batch, L, d_inner, d_state, conv_k, io, c
                                                                  io, chunk_len))
 
 
-def ssm_scan_bwd_fused_saved(x_in, dt_raw, A, B, C, D, z=None, *, states, **k):
-    """ssm_scan_bwd_fused from the states ssm_scan_fwd_fused_save stored (see ssm_scan.h);
-    the same dict of gradients."""
-    return ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z, None, states=states, **k)
+def ssm_scan_bwd_fused_saved(x_in, dt_raw, A, B, C, D, z=None, *, states, u, dt, **k):
+    """ssm_scan_bwd_fused from the states, u and dt that ssm_scan_fwd_fused_save stored
+    (see ssm_scan.h); the same dict of gradients."""
+    return ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z, None, states=states, u=u, dt=dt, **k)
 
 
 def ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None, conv_b=None,
                        conv_state0=None, dt_bias=None, dy, dh_final=None, chunk_len=0,
                        want_dz=True, want_dh0=True, want_dconv_state0=True, workspace=None,
-                       states=None):
+                       states=None, u=None, dt=None):
     """Gradients of ssm_scan_fwd_fused's prefill (see ssm_scan.h). Returns a dict:
     dx_in, ddt_raw, dz (io dtype; dz None when ungated or not wanted), dA, dB, dC, dD,
     dh0, dconv_w, dconv_b, ddt_bias (float32; None when the input is absent or not
-    wanted), dconv_state0 (io dtype, for conv_k >= 2). states: from stored states
-    (ssm_scan_bwd_fused_saved; h0 is then not given)."""
+    wanted), dconv_state0 (io dtype, for conv_k >= 2). states, u, dt: from what the
+    fused training forward stored (ssm_scan_bwd_fused_saved; h0 is then not given)."""
     lib = load_library()
     saved = states is not None
     b, L, Dn = x_in.shape
@@ -746,15 +758,20 @@ def ssm_scan_bwd_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=None
     if saved:
         if h0 is not None:
             raise ValueError("h0 is in the stored states")
+        if u is None or dt is None:
+            raise ValueError("the backward from stored states takes the forward's u and dt too")
         _dev(states, "states", _states_shape(b, L, Dn, N), f32)
+        _dev(u, "u", (b, L, Dn), x_in.dtype)
+        _dev(dt, "dt", (b, L, Dn), x_in.dtype)
     need = (ssm_scan_bwd_fused_saved_workspace if saved else ssm_scan_bwd_fused_workspace)(
         b, L, Dn, N, K, io, chunk_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lead = [_ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z)]
+    lead += [_ptr(states), _ptr(u), _ptr(dt)] if saved else [_ptr(h0)]
     st = getattr(lib, "ssm_scan_bwd_fused_saved" if saved else "ssm_scan_bwd_fused")(
-        _ptr(x_in), _ptr(dt_raw), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(states if saved else h0),
-        _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_state0), _ptr(dt_bias), _ptr(dy), _ptr(dh_final),
+        *lead, _ptr(conv_w), _ptr(conv_b), K, _ptr(conv_state0), _ptr(dt_bias), _ptr(dy), _ptr(dh_final),
         _ptr(out["dx_in"]), _ptr(out["ddt_raw"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]),
         _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out["dconv_w"]),
         _ptr(out["dconv_b"]), _ptr(out["ddt_bias"]), _ptr(out["dconv_state0"]), b, L, Dn, N, io,
@@ -815,18 +832,18 @@ class _SelectiveScanFused(torch.autograd.Function):
         kw = dict(conv_w=conv_w, conv_b=conv_b, conv_state0=conv_state0, dt_bias=dt_bias,
                   chunk_len=chunk_len, want_conv_state=False)
         if save_states:
-            y, h_final, _, states = ssm_scan_fwd_fused_save(x_in, dt_raw, A, B, C, D, z, h0, **kw)
+            y, h_final, _, states, u, dt = ssm_scan_fwd_fused_save(x_in, dt_raw, A, B, C, D, z, h0, **kw)
         else:
             y, h_final, _ = ssm_scan_fwd_fused(x_in, dt_raw, A, B, C, D, z, h0, **kw)
-            states = None
+            states = u = dt = None
         ctx.save_for_backward(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias,
-                              states)
+                              states, u, dt)
         ctx.chunk_len = chunk_len
         return y, h_final
 
     @staticmethod
     def backward(ctx, dy, dh_final):
-        x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias, states = ctx.saved_tensors
+        x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0, dt_bias, states, u, dt = ctx.saved_tensors
         need = ctx.needs_input_grad
         if dy is None:
             dy = torch.zeros_like(x_in)
@@ -836,7 +853,8 @@ class _SelectiveScanFused(torch.autograd.Function):
                                dh_final=None if dh_final is None else dh_final.float().contiguous(),
                                chunk_len=ctx.chunk_len, want_dz=z is not None and need[6],
                                want_dh0=h0 is not None and need[7],
-                               want_dconv_state0=conv_state0 is not None and need[10], states=states)
+                               want_dconv_state0=conv_state0 is not None and need[10], states=states,
+                               u=u, dt=dt)
         cast = lambda t, like: None if (t is None or like is None) else t.to(like.dtype)
         grads = (g["dx_in"], g["ddt_raw"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
                  cast(g["dD"], D), g["dz"], g["dh0"], cast(g["dconv_w"], conv_w),
@@ -848,8 +866,8 @@ def selective_scan_fused(x_in, dt_raw, A, B, C, D, z=None, h0=None, *, conv_w=No
                          conv_state0=None, dt_bias=None, chunk_len=0, save_states=False):
     """The fused prefill (input stage + scan) as a differentiable function: returns
     (y, h_final), with gradients for every tensor input from ssm_scan_bwd_fused.
-    save_states: the forward stores the scan's state every 8 steps
-    (ssm_scan_fwd_fused_save) and the backward reads them (ssm_scan_bwd_fused_saved)."""
+    save_states: the forward stores the scan's state every 8 steps and its inputs u and dt
+    (ssm_scan_fwd_fused_save), and the backward reads them (ssm_scan_bwd_fused_saved)."""
     return _SelectiveScanFused.apply(x_in, dt_raw, A, B, C, D, z, h0, conv_w, conv_b, conv_state0,
                                      dt_bias, chunk_len, save_states)
 

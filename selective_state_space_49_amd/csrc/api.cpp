@@ -169,6 +169,7 @@ struct InputStage {
     int32_t conv_k;
     const void *conv_state0;  // prefill only
     void *conv_state;         // prefill: conv_state_out; decode: the state, in place
+    void *u_out = nullptr, *dt_out = nullptr;  // the fused training forward: u and dt out
 };
 
 // The exponential-trapezoidal entry points: the input before the first step (prefill:
@@ -313,7 +314,9 @@ ssm_status scan_common(const void *x, const void *dt, const float *A, const void
         a.conv_state0 = conv_rows ? in->conv_state0 : nullptr;
         a.conv_state_out = conv_rows ? in->conv_state : nullptr;
         a.dt_bias = in->dt_bias;
-        a.states = states;  // the fused training forward, or null
+        a.states = states;  // the fused training forward (with u_out, dt_out), or null
+        a.u_out = in->u_out;
+        a.dt_out = in->dt_out;
         e = ssm::launch_scan_fused(a, iot, d_state, z != nullptr, s, ev);
     } else if (trap) {
         a.x_prev = trap->x_prev;
@@ -683,11 +686,27 @@ ssm_status ssm_scan_fwd_fused_save(const void *x_in, const void *dt_raw, const f
                                    const float *conv_w, const float *conv_b, int32_t conv_k,
                                    const void *conv_state0, void *conv_state_out,
                                    const float *dt_bias, void *y, float *h_final, float *states,
-                                   int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
-                                   ssm_dtype io, int64_t chunk_len, void *workspace,
-                                   size_t workspace_bytes, void *hip_stream) {
-    if (batch > 0 && L > 0 && !states) return fail(SSM_ERR_NULL, "states is required");
-    const InputStage in{conv_w, conv_b, dt_bias, conv_k, conv_state0, conv_state_out};
+                                   void *u_out, void *dt_out, int64_t batch, int64_t L,
+                                   int64_t d_inner, int32_t d_state, ssm_dtype io,
+                                   int64_t chunk_len, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream) {
+    if (batch > 0 && L > 0 && (!states || !u_out || !dt_out))
+        return fail(SSM_ERR_NULL, "states, u_out and dt_out are required");
+    const size_t eb = io == SSM_BF16 ? 2 : 4;
+    if (!aligned(u_out, eb) || !aligned(dt_out, eb))
+        return fail(SSM_ERR_ALIGN, "u_out and dt_out must be element-aligned");
+    // The rescan writes a chunk's u and dt while other chunks still read x_in, dt_raw
+    // and write y.
+    const size_t rows = (size_t)(batch > 0 && L > 0 ? batch * L * d_inner : 0) * eb;
+    const void *ins[] = {x_in, dt_raw, y};
+    for (const void *p : ins)
+        if (overlaps(u_out, rows, p, rows) || overlaps(dt_out, rows, p, rows))
+            return fail(SSM_ERR_UNSUPPORTED, "u_out and dt_out must not overlap x_in, dt_raw or y");
+    if (overlaps(u_out, rows, dt_out, rows))
+        return fail(SSM_ERR_UNSUPPORTED, "u_out and dt_out must not overlap");
+    InputStage in{conv_w, conv_b, dt_bias, conv_k, conv_state0, conv_state_out};
+    in.u_out = u_out;
+    in.dt_out = dt_out;
     return scan_common(x_in, dt_raw, A, B, C, D, z, h0, y, h_final, batch, L, d_inner, d_state, io,
                        chunk_len, workspace, workspace_bytes, hip_stream, false, nullptr, 0, &in,
                        nullptr, 0, false, batch > 0 && L > 0 ? states : nullptr);
@@ -892,11 +911,13 @@ ssm_status ssm_scan_bwd_saved(const void *x, const void *dt, const float *A, con
 // The two streaming kernels of the input stage take chunks of their own (independent:
 // enough for about 8 blocks of 256 channels per SIMD, 8192 on 256 CUs, i.e. 2 blocks of
 // 256 lanes per SIMD at four channels per lane, chunks of at least 128 steps). Workspace: the scan backward's, then u, dt, du, ddt
-// ([batch][L][d_inner] of io each) and the partial sums ([n][batch][d_inner][conv_k + 2]
+// ([batch][L][d_inner] of io each; u and dt only when they are made here, not given by
+// the fused training forward) and the partial sums ([n][batch][d_inner][conv_k + 2]
 // fp32), each 256-byte aligned.
 struct InBwdPlan {
     int64_t T;
     int32_t n_chunks;
+    int32_t nbuf;  // io buffers in the workspace: 4 (u, dt, du, ddt) or 2 (du, ddt)
     size_t scan_ws, buf, part, bytes;
 };
 
@@ -917,7 +938,8 @@ ssm_status make_in_bwd_plan(int64_t batch, int64_t L, int64_t d_inner, int32_t d
     p->scan_ws = ws_round(bp.bytes);
     p->buf = ws_round((size_t)batch * (size_t)L * (size_t)d_inner * io_bytes(io));
     p->part = ws_round((size_t)p->n_chunks * (size_t)batch * (size_t)d_inner * (size_t)(conv_k + 2) * sizeof(float));
-    p->bytes = p->scan_ws + 4 * p->buf + p->part;
+    p->nbuf = saved ? 2 : 4;
+    p->bytes = p->scan_ws + (size_t)p->nbuf * p->buf + p->part;
     return ok();
 }
 
@@ -931,7 +953,8 @@ size_t ssm_scan_bwd_fused_workspace(int64_t batch, int64_t L, int64_t d_inner, i
 namespace {
 ssm_status bwd_fused_common(const void *x_in, const void *dt_raw, const float *A, const void *B,
                             const void *C, const float *D, const void *z, const float *h0,
-                            const float *states, const float *conv_w, const float *conv_b,
+                            const float *states, const void *u_saved, const void *dt_saved,
+                            const float *conv_w, const float *conv_b,
                             int32_t conv_k, const void *conv_state0, const float *dt_bias,
                             const void *dy, const float *dh_final, void *dx_in, void *ddt_raw,
                             void *dz, float *dA, float *dB, float *dC, float *dD, float *dh0,
@@ -949,8 +972,11 @@ ssm_status bwd_fused_common(const void *x_in, const void *dt_raw, const float *A
     const bool work = batch > 0 && L > 0;
     if (work && (!x_in || !dt_raw || !dx_in || !ddt_raw))
         return fail(SSM_ERR_NULL, "x_in, dt_raw, dx_in and ddt_raw are required");
-    if (saved && work && !states) return fail(SSM_ERR_NULL, "states is required");
+    if (saved && work && (!states || !u_saved || !dt_saved))
+        return fail(SSM_ERR_NULL, "states, u and dt are required");
     if (!aligned(states, 16)) return fail(SSM_ERR_ALIGN, "states must be 16-byte aligned");
+    if (!aligned(u_saved, eb) || !aligned(dt_saved, eb))
+        return fail(SSM_ERR_ALIGN, "u and dt must be element-aligned");
     if (!aligned(x_in, eb) || !aligned(dt_raw, eb) || !aligned(dx_in, eb) || !aligned(ddt_raw, eb) ||
         !aligned(dconv_w, 4) || !aligned(dconv_b, 4) || !aligned(ddt_bias, 4))
         return fail(SSM_ERR_ALIGN, "pointer alignment (x_in, dt_raw, dx_in, ddt_raw element; dconv_w, dconv_b, ddt_bias 4 B)");
@@ -965,19 +991,21 @@ ssm_status bwd_fused_common(const void *x_in, const void *dt_raw, const float *A
     a.x_in = x_in; a.dt_raw = dt_raw;
     a.conv_w = conv_k > 0 ? conv_w : nullptr; a.conv_b = conv_k > 0 ? conv_b : nullptr;
     a.dt_bias = dt_bias; a.conv_state0 = conv_k > 1 ? conv_state0 : nullptr;
-    a.u = ws ? ws + p.scan_ws : nullptr;
-    a.dt = ws ? ws + p.scan_ws + p.buf : nullptr;
-    a.du = ws ? ws + p.scan_ws + 2 * p.buf : nullptr;
-    a.ddt = ws ? ws + p.scan_ws + 3 * p.buf : nullptr;
+    // u and dt: from the fused training forward, or made here from x_in and dt_raw
+    char *io_bufs = ws ? ws + p.scan_ws : nullptr;
+    a.u = saved ? const_cast<void *>(u_saved) : io_bufs;
+    a.dt = saved ? const_cast<void *>(dt_saved) : (ws ? io_bufs + p.buf : nullptr);
+    a.du = ws ? io_bufs + (size_t)(p.nbuf - 2) * p.buf : nullptr;
+    a.ddt = ws ? io_bufs + (size_t)(p.nbuf - 1) * p.buf : nullptr;
     a.dx_in = dx_in; a.ddt_raw = ddt_raw;
     a.dconv_state0 = conv_k > 1 ? dconv_state0 : nullptr;
-    a.part = ws ? (float *)(ws + p.scan_ws + 4 * p.buf) : nullptr;
+    a.part = ws ? (float *)(io_bufs + (size_t)p.nbuf * p.buf) : nullptr;
     a.dconv_w = conv_k > 0 ? dconv_w : nullptr; a.dconv_b = conv_k > 0 ? dconv_b : nullptr;
     a.ddt_bias = ddt_bias;
     a.batch = batch; a.L = L; a.Dn = d_inner; a.T = p.T; a.n_chunks = p.n_chunks; a.conv_k = conv_k;
     hipStream_t s = (hipStream_t)hip_stream;
     const int iot = io == SSM_BF16 ? 1 : 0;
-    if (work) {
+    if (work && !saved) {
         st = launch_status(ssm::launch_input_fwd(a, iot, s), "input stage (forward)");
         if (st != SSM_OK) return st;
     }
@@ -1010,7 +1038,7 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
                               int64_t batch, int64_t L, int64_t d_inner, int32_t d_state,
                               ssm_dtype io, int64_t chunk_len, void *workspace,
                               size_t workspace_bytes, void *hip_stream) {
-    return bwd_fused_common(x_in, dt_raw, A, B, C, D, z, h0, nullptr, conv_w, conv_b, conv_k,
+    return bwd_fused_common(x_in, dt_raw, A, B, C, D, z, h0, nullptr, nullptr, nullptr, conv_w, conv_b, conv_k,
                             conv_state0, dt_bias, dy, dh_final, dx_in, ddt_raw, dz, dA, dB, dC, dD,
                             dh0, dconv_w, dconv_b, ddt_bias, dconv_state0, batch, L, d_inner,
                             d_state, io, chunk_len, workspace, workspace_bytes, hip_stream, false);
@@ -1026,7 +1054,8 @@ size_t ssm_scan_bwd_fused_saved_workspace(int64_t batch, int64_t L, int64_t d_in
 
 ssm_status ssm_scan_bwd_fused_saved(const void *x_in, const void *dt_raw, const float *A,
                                     const void *B, const void *C, const float *D, const void *z,
-                                    const float *states, const float *conv_w, const float *conv_b,
+                                    const float *states, const void *u, const void *dt,
+                                    const float *conv_w, const float *conv_b,
                                     int32_t conv_k, const void *conv_state0, const float *dt_bias,
                                     const void *dy, const float *dh_final, void *dx_in,
                                     void *ddt_raw, void *dz, float *dA, float *dB, float *dC,
@@ -1035,7 +1064,7 @@ ssm_status ssm_scan_bwd_fused_saved(const void *x_in, const void *dt_raw, const 
                                     int64_t d_inner, int32_t d_state, ssm_dtype io,
                                     int64_t chunk_len, void *workspace, size_t workspace_bytes,
                                     void *hip_stream) {
-    return bwd_fused_common(x_in, dt_raw, A, B, C, D, z, nullptr, states, conv_w, conv_b, conv_k,
+    return bwd_fused_common(x_in, dt_raw, A, B, C, D, z, nullptr, states, u, dt, conv_w, conv_b, conv_k,
                             conv_state0, dt_bias, dy, dh_final, dx_in, ddt_raw, dz, dA, dB, dC, dD,
                             dh0, dconv_w, dconv_b, ddt_bias, dconv_state0, batch, L, d_inner,
                             d_state, io, chunk_len, workspace, workspace_bytes, hip_stream, true);

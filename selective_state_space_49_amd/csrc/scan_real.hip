@@ -57,6 +57,7 @@ __device__ __forceinline__ LaneId lane_id(const ScanArgs &a) {
 // The kernels read x and dt as given.
 struct NoInput {
     static constexpr bool kSave = false;  // store the state every kStateEvery steps
+    static constexpr bool kSaveIn = false;  // store the scan's inputs u and dt
     static constexpr bool kTrap = false;
     static constexpr bool kW = false;  // no weight stream
     static constexpr int kWavesPerSimd = 5;
@@ -81,6 +82,7 @@ struct SaveInput : NoInput {
 template <typename IO, int KC>
 struct MambaInput {
     static constexpr bool kSave = false;
+    static constexpr bool kSaveIn = false;
     static constexpr bool kTrap = false;
     static constexpr bool kW = false;
     static constexpr int kWavesPerSimd = 4;  // at five (prefetching 2 rows per block to fit)
@@ -131,10 +133,13 @@ struct MambaInput {
 };
 
 // The fused training forward: MambaInput's prefill that also stores the state entering
-// every kStateEvery-th step (ScanArgs::states), as SaveInput does for the plain scan.
+// every kStateEvery-th step (ScanArgs::states), as SaveInput does for the plain scan, and
+// the scan's inputs u and dt as it makes them (ScanArgs::u_out, dt_out), so that the
+// backward need not make them again.
 template <typename IO, int KC>
 struct MambaSave : MambaInput<IO, KC> {
     static constexpr bool kSave = true;
+    static constexpr bool kSaveIn = true;
 };
 
 // The exponential-trapezoidal discretisation (the Mamba-3 item of "Jamba —
@@ -153,6 +158,7 @@ struct MambaSave : MambaInput<IO, KC> {
 template <typename IO, bool LAM>
 struct TrapInput {
     static constexpr bool kSave = false;
+    static constexpr bool kSaveIn = false;
     static constexpr bool kTrap = true;
     static constexpr bool kW = LAM;
     static constexpr int kWavesPerSimd = 5;
@@ -393,7 +399,9 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     const int64_t row0 = (ln.b * a.L + t0) * a.Dn;
     const RowStream<IO> xs((const IO *)a.x + row0), dts((const IO *)a.dt + row0),
         zs(GATED ? (const IO *)a.z + row0 : (const IO *)a.x + row0), ys((IO *)a.y + row0),
-        lws(In::kW ? (const IO *)a.lam + row0 : (const IO *)a.x + row0);
+        lws(In::kW ? (const IO *)a.lam + row0 : (const IO *)a.x + row0),
+        uos(In::kSaveIn ? (IO *)a.u_out + row0 : (IO *)a.y + row0),
+        dtos(In::kSaveIn ? (IO *)a.dt_out + row0 : (IO *)a.y + row0);
     const UniRow<IO, N> Bp(a.B, ln.b * a.L * N);
     const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     In in;
@@ -406,6 +414,10 @@ __global__ __launch_bounds__(256, In::kWavesPerSimd) void k_chunk_scan(ScanArgs 
     const uint32_t sv_qstride = (uint32_t)(a.Dn * 16);
     stream_steps_w<IO, GATED, In::kKU, In::kRawPrefetch, In::kW>(xs, dts, zs, lws, voff, rb, steps, steps, [&](uint32_t i, float xr, float dr, float zv, float lr) {
         const float xv = in.x(xr), dv = in.dt(dr);
+        if constexpr (In::kSaveIn) {
+            uos.st(voff, i * rb, xv);
+            dtos.st(voff, i * rb, dv);
+        }
         const int64_t t = t0 + i;
         float acc = 0.0f;
         if constexpr (In::kTrap) {

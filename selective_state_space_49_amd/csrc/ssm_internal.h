@@ -41,6 +41,9 @@ struct ScanArgs {
     // stored-state layout (state_at); null elsewhere. Chunks start at multiples of
     // kStateEvery.
     float *states;
+    // Fused training forward only: the scan's inputs u and dt as the input stage makes
+    // them, rounded to io, [batch][L][Dn]; null elsewhere.
+    void *u_out, *dt_out;
 };
 
 // The backward's stored states: row r (batch Dn N floats) holds the state entering step

@@ -401,21 +401,28 @@ def test_fused_stored_state_argument_errors(lib):
     # ssm_scan_fwd_fused_save and ssm_scan_bwd_fused_saved: checked before any launch.
     p = lambda v: None if v is None else ctypes.c_void_p(v)
 
-    def fwd(states=0x4000, L=8, N=4, chunk=0, ws=None, wsb=0):
+    # x_in is 1*8*4*4 = 128 bytes at 0x100000, y at 0x200000, dt_raw at 0x1000
+    def fwd(states=0x4000, u=0x500000, dt=0x600000, L=8, N=4, chunk=0, ws=None, wsb=0):
         return lib.ssm_scan_fwd_fused_save(p(0x100000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
                                            p(0x1000), None, None, p(0x1000), None, 4, None, None,
-                                           None, p(0x200000), None, p(states), 1, L, 4, N, 0, chunk,
-                                           p(ws), wsb, None)
+                                           None, p(0x200000), None, p(states), p(u), p(dt), 1, L, 4, N,
+                                           0, chunk, p(ws), wsb, None)
 
-    def bwd(states=0x4000, L=8, ws=None, wsb=0, chunk=0):
+    def bwd(states=0x4000, u=0x500000, dt=0x600000, L=8, ws=None, wsb=0, chunk=0):
         return lib.ssm_scan_bwd_fused_saved(p(0x100000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
-                                            p(0x1000), None, p(states), p(0x1000), None, 3, None,
-                                            None, p(0x1000), None, p(0x300000), p(0x1000), None,
+                                            p(0x1000), None, p(states), p(u), p(dt), p(0x1000), None, 3,
+                                            None, None, p(0x1000), None, p(0x300000), p(0x1000), None,
                                             p(0x1000), p(0x1000), p(0x1000), p(0x1000), None,
                                             p(0x2000), None, None, None, 1, L, 4, 4, 0, chunk, p(ws),
                                             wsb, None)
     assert fwd(states=None) == NULL and bwd(states=None) == NULL
+    assert fwd(u=None) == NULL and fwd(dt=None) == NULL       # the scan's inputs are stored too
+    assert bwd(u=None) == NULL and bwd(dt=None) == NULL
     assert fwd(states=0x4008) == ALIGN and bwd(states=0x4008) == ALIGN
+    assert fwd(u=0x500002) == ALIGN and bwd(dt=0x600001) == ALIGN
+    assert fwd(u=0x100040) == UNSUP                           # u over x_in
+    assert "overlap" in ssm.ssm_last_error()
+    assert fwd(dt=0x200010) == UNSUP and fwd(u=0x500000, dt=0x500020) == UNSUP
     assert fwd(N=3) == UNSUP
     assert fwd(states=None, L=0) != NULL and bwd(states=None, L=0) != NULL
     need = lib.ssm_scan_bwd_fused_saved_workspace(1, 8, 4, 4, 3, 0, 0)

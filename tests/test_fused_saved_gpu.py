@@ -1,10 +1,11 @@
 """Training the fused prefill with stored states on the GPU: ssm_scan_fwd_fused_save
-(the fused forward that also stores the scan's state entering every 8th step) and
-ssm_scan_bwd_fused_saved (the fused backward that reads those states instead of
-recomputing them).
+(the fused forward that also stores the scan's state entering every 8th step and its
+inputs u and dt) and ssm_scan_bwd_fused_saved (the fused backward that reads them instead
+of recomputing them).
 
 - The forward's y, h_final and conv state equal ssm_scan_fwd_fused's bit for bit for
-  the same chunk length (a multiple of 8), and stored rows equal the oracle's state
+  the same chunk length (a multiple of 8), the stored u and dt the oracle's input stage
+  (to the forward's tolerance), and stored rows equal the oracle's state
   after 8 r steps of the fused prefill (the oracle's scan_fused over the first 8 r
   steps) to the forward's tolerance.
 - The backward's gradients match the oracle's scan_fused_bwd to the fused backward's
@@ -62,7 +63,7 @@ def test_fused_forward_save_matches_fused_and_stores_the_oracle_states(case):
     T = case[7] // EVERY * EVERY
     g, t = to_dev(d), to_dev(s)
     say("fused forward with stored states", _ids(case))
-    y, hf, cs, st = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, T)
+    y, hf, cs, st, u, dtv = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, T)
     torch.cuda.synchronize()
     if T > 0:  # the same chunks as ssm_scan_fwd_fused: the same bits
         y2, hf2, cs2 = _fwd(ssm.ssm_scan_fwd_fused, g, t, T)
@@ -72,6 +73,10 @@ def test_fused_forward_save_matches_fused_and_stores_the_oracle_states(case):
     tol = TOL[io]
     yr, hr = _oracle_fwd(d["x"], s["dt_raw"], d["B"], d["C"], d["z"], d, s)
     assert rel_err(y, yr) <= tol and rel_err(hf, hr) <= tol
+    # the stored scan inputs: u = silu(conv(x_in)) (x_in without a filter) and dt = softplus
+    ur = d["x"] if s["conv_w"] is None else oracle.conv_silu(d["x"], s["conv_w"], s["conv_b"], s["conv_state0"])[0]
+    assert u.dtype == d["x"].dtype and dtv.dtype == d["x"].dtype
+    assert rel_err(u, ur) <= tol and rel_err(dtv, oracle.softplus(s["dt_raw"], s["dt_bias"])) <= tol
     rows = _rows(st, b, Dn, N).cpu()
     n = rows.shape[0]
     assert n == (L + EVERY - 1) // EVERY
@@ -89,9 +94,9 @@ def test_fused_forward_save_matches_fused_and_stores_the_oracle_states(case):
 
 def _saved(d, s, chunk_len):
     g, t = to_dev(d), to_dev(s)
-    _, _, _, st = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, chunk_len)
+    _, _, _, st, u, dtv = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, chunk_len)
     return ssm.ssm_scan_bwd_fused_saved(g["x"], t["dt_raw"], g["A"], g["B"], g["C"], g["D"], g["z"],
-                                        states=st, conv_w=t["conv_w"], conv_b=t["conv_b"],
+                                        states=st, u=u, dt=dtv, conv_w=t["conv_w"], conv_b=t["conv_b"],
                                         conv_state0=t["conv_state0"], dt_bias=t["dt_bias"], dy=g["dy"],
                                         dh_final=g["dh_final"], chunk_len=chunk_len)
 
@@ -118,9 +123,9 @@ def test_fused_training_with_no_steps():
     d, s = _draw(case, seed=611)
     g, t = to_dev(d), to_dev(s)
     say("fused training with stored states, L = 0")
-    y, hf, cs, st = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, 0)
+    y, hf, cs, st, u, dtv = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, 0)
     torch.cuda.synchronize()
-    assert y.numel() == 0 and st.numel() == 0
+    assert y.numel() == 0 and st.numel() == 0 and u.numel() == 0 and dtv.numel() == 0
     assert bitwise_equal(hf, g["h0"]) and bitwise_equal(cs, t["conv_state0"])
     out = _saved(d, s, 0)
     torch.cuda.synchronize()
@@ -141,7 +146,7 @@ def test_selective_scan_fused_with_stored_states():
                                      conv_b=leaves["conv_b"], conv_state0=leaves["conv_state0"],
                                      dt_bias=leaves["dt_bias"], chunk_len=48, save_states=True)
     ((y.float() * g["dy"].float()).sum() + (hf * g["dh_final"]).sum()).backward()
-    y_ref, hf_ref, _, _ = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, 48)
+    y_ref, hf_ref, _, _, _, _ = _fwd(ssm.ssm_scan_fwd_fused_save, g, t, 48)
     ref = _saved(d, s, 48)
     torch.cuda.synchronize()
     assert bitwise_equal(y.detach(), y_ref) and bitwise_equal(hf.detach(), hf_ref)
@@ -199,12 +204,12 @@ def test_fused_backwards_full_size_long_context_sampled():
                                                 dy=dy, **kw)}
     torch.cuda.synchronize()
     say("fused backwards 256k: training forward and ssm_scan_bwd_fused_saved")
-    _, _, _, st = ssm.ssm_scan_fwd_fused_save(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["z"],
-                                              want_conv_state=False, **kw)
+    _, _, _, st, u, dtv = ssm.ssm_scan_fwd_fused_save(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"],
+                                                      d["z"], want_conv_state=False, **kw)
     got["stored"] = ssm.ssm_scan_bwd_fused_saved(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"],
-                                                 d["z"], states=st, dy=dy, **kw)
+                                                 d["z"], states=st, u=u, dt=dtv, dy=dy, **kw)
     torch.cuda.synchronize()
-    del st
+    del st, u, dtv
     rest = torch.ones(shape.d_inner, dtype=torch.bool)
     rest[idx] = False
     gc = lambda t: gather_channels(t, idx)
