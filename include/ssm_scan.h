@@ -402,8 +402,9 @@ ssm_status ssm_scan_bwd_fused(const void *x_in, const void *dt_raw, const float 
  * input stage is not evaluated again before it; ssm_scan_bwd_fused_saved_workspace bytes
  * of workspace (no u and dt of its own). The gradients agree with ssm_scan_bwd_fused's
  * to rounding (the stored states come from the forward's unrounded u and dt, the
- * recomputed ones from the rounded). Errors as in the fused and stored-state entry points
- * above; states, u_out and dt_out (u and dt) are required when batch * L > 0. */
+ * recomputed ones from the rounded); u and dt must not overlap dx_in, ddt_raw or dz
+ * (SSM_ERR_UNSUPPORTED). Errors as in the fused and stored-state entry points above;
+ * states, u_out and dt_out (u and dt) are required when batch * L > 0. */
 ssm_status ssm_scan_fwd_fused_save(const void *x_in, const void *dt_raw, const float *A, const void *B,
                                    const void *C, const float *D, const void *z, const float *h0,
                                    const float *conv_w, const float *conv_b, int32_t conv_k,

@@ -697,7 +697,7 @@ ssm_status ssm_scan_fwd_fused_save(const void *x_in, const void *dt_raw, const f
         return fail(SSM_ERR_ALIGN, "u_out and dt_out must be element-aligned");
     // The rescan writes a chunk's u and dt while other chunks still read x_in, dt_raw
     // and write y.
-    const size_t rows = (size_t)(batch > 0 && L > 0 ? batch * L * d_inner : 0) * eb;
+    const size_t rows = (size_t)(batch > 0 && L > 0 && d_inner > 0 ? batch * L * d_inner : 0) * eb;
     const void *ins[] = {x_in, dt_raw, y};
     for (const void *p : ins)
         if (overlaps(u_out, rows, p, rows) || overlaps(dt_out, rows, p, rows))
@@ -983,6 +983,14 @@ ssm_status bwd_fused_common(const void *x_in, const void *dt_raw, const float *A
     const size_t rows = (size_t)batch * (size_t)L * (size_t)d_inner * eb;
     if (overlaps(dx_in, rows, x_in, rows))
         return fail(SSM_ERR_UNSUPPORTED, "dx_in must not overlap x_in (a chunk reads the inputs after it)");
+    if (saved) {
+        // the scan's backward reads u and dt while it writes dz and the input stage's
+        // backward writes dx_in and ddt_raw
+        const void *outs[] = {dx_in, ddt_raw, dz};
+        for (const void *o : outs)
+            if (overlaps(u_saved, rows, o, rows) || overlaps(dt_saved, rows, o, rows))
+                return fail(SSM_ERR_UNSUPPORTED, "u and dt must not overlap dx_in, ddt_raw or dz");
+    }
     if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes))
         return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes needed", p.bytes);
     if (!aligned(workspace, kWsAlign)) return fail(SSM_ERR_ALIGN, "workspace must be 256-byte aligned");

@@ -423,6 +423,7 @@ def test_fused_stored_state_argument_errors(lib):
     assert fwd(u=0x100040) == UNSUP                           # u over x_in
     assert "overlap" in ssm.ssm_last_error()
     assert fwd(dt=0x200010) == UNSUP and fwd(u=0x500000, dt=0x500020) == UNSUP
+    assert bwd(u=0x300000) == UNSUP                           # u under dx_in
     assert fwd(N=3) == UNSUP
     assert fwd(states=None, L=0) != NULL and bwd(states=None, L=0) != NULL
     need = lib.ssm_scan_bwd_fused_saved_workspace(1, 8, 4, 4, 3, 0, 0)
