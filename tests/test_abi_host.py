@@ -296,6 +296,18 @@ def test_stored_state_training_argument_errors(lib):
     assert bwd(L=200, chunk=16) == WS and bwd(L=200, chunk=16, ws=0x10000, wsb=need - 1) == WS
     # L = 0 needs no states
     assert fwd(states=None, L=0) != NULL
+    # a stored-state row (batch * d_inner * d_state floats) is addressed with 32-bit
+    # offsets: 2 GiB and more is refused before anything is enqueued
+    big = 1 << 25  # channels: 2^25 * 16 states * 4 bytes = 2 GiB
+    st_fwd = lib.ssm_scan_fwd_save(p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                   None, None, p(0x1000), None, p(0x2000), 1, 64, big, 16, 0, 64,
+                                   p(0x10000), 1 << 40, None)
+    assert st_fwd == UNSUP and "2 GiB" in ssm.ssm_last_error()
+    st_bwd = lib.ssm_scan_bwd_saved(p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000), p(0x1000),
+                                    None, p(0x2000), p(0x1000), None, p(0x1000), p(0x1000), None,
+                                    p(0x1000), p(0x1000), p(0x1000), p(0x1000), None, 1, 64, big, 16, 0,
+                                    64, p(0x10000), 1 << 40, None)
+    assert st_bwd == UNSUP and "2 GiB" in ssm.ssm_last_error()
 
 
 def test_trapezoid_argument_errors(lib):
