@@ -944,10 +944,13 @@ def measure(name, variant, steps, warmup, with_cpu, threads, cpus, torch, ssm, w
            "phases_ms": {k: round(v, 4) for k, v in info["phases_ms"].items()},
            "roofline": roof}
     if "summary" in info["phases_ms"]:
-        # The chunk summaries walk back only until every state's decay reaches 2^-48, so
-        # their time depends on dt and A: slow decay walks whole chunks.
+        # The chunk summaries walk back only until every state's decay reaches 2^-H
+        # (H = 28 + the bit length of the chunk length), so their time depends on dt and
+        # A: slow decay walks whole chunks.
         rec["summary_depends_on_inputs"] = ("chunk summaries walk back until the decay reaches "
-                                            "2^-48; slower decay (smaller dt*|A|) walks more of each chunk")
+                                            "2^-H (H = 28 + the bit length of the chunk length, "
+                                            "41 at 256k); slower decay (smaller dt*|A|) walks more "
+                                            "of each chunk")
     if mimo:
         rec["mimo_outputs_per_s"] = round(elems_s * mimo, 1)  # R outputs per channel-step
     cpu = None

@@ -83,11 +83,12 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * exact re-association of the recurrence; results differ from a sequential fp32
  * loop only by rounding and by one bounded truncation: a chunk's end state is
  * accumulated only over its last steps back to the point where the decay
- * exp(Re A * sum of dt) of every state of 64 neighbouring channels is below 2^-48.
- * What is dropped changes a carried state by at most 2^-48 * (chunk_len *
- * max|dt x B| + |incoming state|), at most 2^-28 of the input scale for chunks
- * below 2^20 steps, below fp32 resolution. NaN or Inf older than that window do not propagate past the chunk
- * boundary. workspace must hold ssm_scan_fwd_workspace(...) bytes
+ * exp(Re A * sum of dt) of every state of 64 neighbouring channels is below 2^-H,
+ * H = 28 + the bit length of chunk_len (41 for chunks of 4096 to 8191 steps). What is
+ * dropped changes a carried state by at most 2^-H * (chunk_len * max|dt x B| +
+ * |incoming state|), which is at most 2^-28 of the input scale for every chunk length,
+ * below fp32 resolution. NaN or Inf older than that window do not propagate past the
+ * chunk boundary. workspace must hold ssm_scan_fwd_workspace(...) bytes
  * (0 is possible, then workspace may be NULL). It is scratch: contents on entry
  * are ignored and on return are unspecified. L == 0 writes h_final = h0 (or
  * zeros) and nothing else. */

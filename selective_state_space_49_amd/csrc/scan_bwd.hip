@@ -19,7 +19,7 @@
 //   1. the forward's chunk summaries and carry: the state entering every chunk;
 //   2. k_bwd_summary: per chunk c >= 1 the adjoint it passes to chunk c-1 from a zero
 //      carry-in, G_c, and its total decay Q_c, over a window that ends where the
-//      decay reaches 2^-kHorizon (the mirror of the forward's horizon);
+//      decay reaches the forward's horizon (horizon_bits), mirrored;
 //   3. the forward's carry kernel over the chunks in reverse order, seeded with
 //      dh_final: the adjoint entering every chunk from the right;
 //   4. k_bwd_walk: per chunk, a forward walk from the incoming state that stores the
@@ -169,14 +169,16 @@ __device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStr
     }
 }
 
-// First row (chunk-relative) from which the decay back to row 0 is below 2^-kHorizon
-// for every state of every lane of the wave, walking dt forward in whole blocks of
-// kB rows: rows at or beyond it reach row 0 with weight below 2^-kHorizon. Returns T when
-// the horizon is not reached within the whole blocks (A >= 0, dt = 0, NaN, short T).
+// First row (chunk-relative) from which the decay back to row 0 is below 2^-H (H =
+// horizon_bits(T), as for the forward's windows) for every state of every lane of the
+// wave, walking dt forward in whole blocks of kB rows: rows at or beyond it reach row 0
+// with weight below 2^-H. Returns T when the horizon is not reached within the whole
+// blocks (A >= 0, dt = 0, NaN, short T).
 template <typename IO>
 __device__ __forceinline__ uint32_t horizon_end(const RowStream<IO> &dt, uint32_t voff,
                                                 uint32_t rb, uint32_t T, float amax) {
     if (!__any(amax < 0.0f) || T < (uint32_t)kB) return T;
+    const float H = horizon_bits(T);
     float S = 0.0f;
     float cur[kB];
     uint32_t nxt[kB];
@@ -193,7 +195,7 @@ __device__ __forceinline__ uint32_t horizon_end(const RowStream<IO> &dt, uint32_
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < kB; ++k) S += cur[k];
-        if (__all(amax * S <= -kHorizon)) return tn;
+        if (__all(amax * S <= -H)) return tn;
         if (!more) return T;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

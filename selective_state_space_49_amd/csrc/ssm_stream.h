@@ -179,12 +179,16 @@ __device__ __forceinline__ void stream_steps(const RowStream<IO> &x, const RowSt
 // The end state of a chunk from a zero start is sum_s W_s[n] dt_s x_s B_s[n] with
 // W_s[n] = exp(A[n] * sum of dt after s). With dt >= 0 and Re A < 0 the weights only
 // shrink going back in time. Once log2(e) * Re A[n] * (sum of dt over the last rows)
-// <= -kHorizon for every state of every lane of a wave, everything older enters the
-// end state with weight below 2^-kHorizon. Dropping it changes a carried state by at
-// most 2^-48 * T * max|dt x B| (at most 2^-28 of the input scale for T < 2^20): below
-// fp32 resolution (2^-24). The chunk's total transfer factor exp(A * sum dt) is then
-// below 2^-48 in modulus and is dropped the same way.
-constexpr float kHorizon = 48.0f;
+// <= -H for every state of every lane of a wave, everything older enters the end state
+// with weight below 2^-H. The chunk's total transfer factor exp(A * sum dt) is then
+// below 2^-H in modulus and is dropped the same way. Dropping both changes a carried
+// state by at most 2^-H * (T * max|dt x B| + |incoming state|). H = 28 + the bit length
+// of the chunk length T makes that at most 2^-28 of the input scale (T + 1 <= 2^bits),
+// 16 times below fp32 resolution (2^-24), for every chunk length: 41 for the 256k
+// prefill's chunks of 6554 steps, 48 for chunks just below 2^20 steps.
+__device__ __forceinline__ float horizon_bits(uint32_t T) {
+    return (float)(28 + 32 - __clz(T));
+}
 // Priority scale of the summary windows (steps): longer windows go first.
 constexpr uint32_t kSummaryPrioScale = 2048;
 constexpr int kB = 32;  // rows per block of the backward walk
@@ -205,6 +209,7 @@ __device__ __forceinline__ uint32_t horizon_start(const RowStream<IO> &dt, uint3
                                                   uint32_t rb, uint32_t T, float amax,
                                                   DtF dtf = DtF()) {
     if (!__any(amax < 0.0f) || T < (uint32_t)kB) return 0;
+    const float H = horizon_bits(T);
     float S = 0.0f;
     float cur[kB];
     uint32_t nxt[kB];
@@ -221,7 +226,7 @@ __device__ __forceinline__ uint32_t horizon_start(const RowStream<IO> &dt, uint3
         __builtin_amdgcn_sched_barrier(0);  // sum the current block while nxt is in flight
 #pragma unroll
         for (int k = 0; k < kB; ++k) S += dtf(cur[k]);
-        if (__all(amax * S <= -kHorizon)) return tn;
+        if (__all(amax * S <= -H)) return tn;
         if (!more) return 0;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
