@@ -35,6 +35,10 @@ template <> struct RowStream<bf16_bits> {
     __device__ __forceinline__ void st(uint32_t voff, uint32_t soff, float v) const {
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, soff, 0);
     }
+    // A streaming store (glc slc): for rows read back only long after.
+    __device__ __forceinline__ void st_stream(uint32_t voff, uint32_t soff, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, soff, 3);
+    }
 };
 
 template <> struct RowStream<float> {
@@ -50,6 +54,9 @@ template <> struct RowStream<float> {
     static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw); }
     __device__ __forceinline__ void st(uint32_t voff, uint32_t soff, float v) const {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    }
+    __device__ __forceinline__ void st_stream(uint32_t voff, uint32_t soff, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 3);
     }
 };
 
