@@ -92,7 +92,8 @@ struct VecStream {
         return v;
     }
 
-    // Stores y[0..R) (rounded to the element type) with one vector store.
+    // Stores y[0..R) (rounded to the element type) with one vector store, streaming
+    // (glc slc): y is written once and read only by the caller's next step.
     __device__ __forceinline__ void st(uint32_t voff, uint32_t soff, const float (&y)[R]) const {
         VecRaw<IO, R> v;
         if constexpr (sizeof(IO) == 2) {
@@ -109,20 +110,20 @@ struct VecStream {
         }
         constexpr int B = VecRaw<IO, R>::kBytes;
         if constexpr (B == 2) {
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v.w[0], r, voff, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v.w[0], r, voff, soff, 3);
         } else if constexpr (B == 4) {
-            __builtin_amdgcn_raw_buffer_store_b32(v.w[0], r, voff, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(v.w[0], r, voff, soff, 3);
         } else if constexpr (B == 8) {
             u32x2 t = {v.w[0], v.w[1]};
-            __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, 3);
         } else if constexpr (B == 16) {
             u32x4 t = {v.w[0], v.w[1], v.w[2], v.w[3]};
-            __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, 3);
         } else {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 u32x4 t = {v.w[4 * h], v.w[4 * h + 1], v.w[4 * h + 2], v.w[4 * h + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(t, r, voff + 16u * h, soff, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(t, r, voff + 16u * h, soff, 3);
             }
         }
     }
