@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256, CSplit<N>::kWaves) void k_chunk_summary_c(Scan
     CStage<IO, N, KU> bst;
     bst.init(B0);
     double S = 0.0;
-    csteps<IO, N, false, false>(xs, dws, dws, voff, rb, bst, bst, bslot, bslot, T - ts, kSummaryPrioScale,
+    csteps<IO, N, false, false>(xs, dws, dws, voff, rb, bst, bst, bslot, bslot, T - ts, min(T, kSummaryPrioScale),
                                 [&](uint32_t i, float xv, float dv, float, const SSM_LDS f2v *bs,
                                     const SSM_LDS f2v *) {
         const float u = dv * xv;
