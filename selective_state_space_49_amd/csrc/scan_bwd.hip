@@ -127,11 +127,11 @@ template <> struct Log2<32> { static constexpr int v = 5; };
 
 // Walks rows steps-1 .. 0 of up to three streams (s2 only if THREE), fetching the
 // block of KU rows below the current one while the current one is computed; calls
-// body(i, v0, v1, v2).
+// body(i, v0, v1, v2). prio_scale: issue priority by remaining rows (set_priority).
 template <typename IO, bool THREE, int KU, typename Body>
 __device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStream<IO> &s1,
                                            const RowStream<IO> &s2, uint32_t voff, uint32_t rb,
-                                           uint32_t steps, Body &&body) {
+                                           uint32_t steps, uint32_t prio_scale, Body &&body) {
     const uint32_t full = steps / KU;
     for (uint32_t i = steps; i > full * KU;) {  // ragged top rows first, one at a time
         --i;
@@ -151,6 +151,7 @@ __device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStr
     load(a0, a1, a2, full - 1);
     for (uint32_t blk = full; blk > 0;) {
         --blk;  // block blk is in a*: fetch blk-1 into b*, compute blk
+        set_priority((blk + 1) * KU, prio_scale);
         if (blk > 0) load(b0, b1, b2, blk - 1);
 #pragma unroll
         for (int k = KU - 1; k >= 0; --k) {
@@ -159,6 +160,7 @@ __device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStr
         }
         if (blk == 0) break;
         --blk;  // block blk is in b*: fetch blk-1 into a*, compute blk
+        set_priority((blk + 1) * KU, prio_scale);
         if (blk > 0) load(a0, a1, a2, blk - 1);
 #pragma unroll
         for (int k = KU - 1; k >= 0; --k) {
@@ -167,6 +169,7 @@ __device__ __forceinline__ void stream_rev(const RowStream<IO> &s0, const RowStr
         }
         if (blk == 0) break;
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // First row (chunk-relative) from which the decay back to row 0 is below 2^-H (H =
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(256) void k_bwd_summary(BwdArgs a) {
     const uint32_t te = horizon_end<IO>(dts, voff, rb, T, amax);
     const UniRow<IO, N> Cp(a.C, ln.b * a.L * N);
     double S = 0.0;
-    stream_rev<IO, GATED, 4>(dts, dys, zs, voff, rb, te, [&](uint32_t i, float dv, float dy, float zv) {
+    // issue priority as the forward summaries take it: windows on a 2048-step scale (longer
+    // ones first), or the chunk's length when shorter
+    stream_rev<IO, GATED, 4>(dts, dys, zs, voff, rb, te, min(T, kSummaryPrioScale), [&](uint32_t i, float dv, float dy, float zv) {
         const int64_t t = t0 + i;
         float gp;
         const float dout = gate_grad<GATED>(dy, zv, gp);
