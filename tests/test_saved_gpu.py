@@ -12,6 +12,7 @@ reads those states instead of recomputing them by a forward walk).
 - Full size: the 256k prefill's backward from stored states on a channel sample, as the
   plain backward's full-size test does it.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -167,6 +168,41 @@ def test_selective_scan_with_stored_states(io, gated, with_h0):
             continue
         grad, want = leaves[k].grad, ref["d" + k]
         assert bitwise_equal(grad, want.to(grad.dtype)), f"d{k} differs from ssm_scan_bwd_saved"
+
+
+def test_forward_save_full_size_every_stored_row_sampled():
+    # The 256k prefill in the library's own plan: every one of the 32768 stored rows, on a
+    # channel sample, against the oracle's state entering that step. The oracle walks the
+    # sequence in 8-step pieces, each resumed from the last one's final state (its
+    # split/resume is exact), so its states are those of one sequential walk. States are
+    # fp32 and the inputs exact bf16 values: the fp32 tolerance applies, row by row.
+    shape = WORKLOADS["long_context_256k"]
+    N, Dn, L = shape.d_state, shape.d_inner, shape.L
+    say("stored states 256k, every row: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    idx = sample_channels(Dn, 32, seed=29)
+    say("stored states 256k, every row: forward")
+    _, _, st = ssm.ssm_scan_fwd_save(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"])
+    torch.cuda.synchronize()
+    rows = _rows(st, shape.batch, Dn, N).index_select(2, idx.cuda()).cpu()
+    del st
+    n = rows.shape[0]
+    assert n == (L + EVERY - 1) // EVERY
+    gc = lambda t: oracle.to_f64(gather_channels(t, idx))
+    x, dt, z = gc(d["x"]), gc(d["dt"]), gc(d["z"])
+    B, C = oracle.to_f64(d["B"].cpu()), oracle.to_f64(d["C"].cpu())
+    A, D = oracle.to_f64(d["A"].cpu()[idx]), oracle.to_f64(d["D"].cpu()[idx])
+    say("stored states 256k, every row: oracle on", len(idx), "channels")
+    ref = np.zeros((n, shape.batch, len(idx), N))
+    h = ref[0].copy()
+    for r in range(1, n):
+        a, b = (r - 1) * EVERY, r * EVERY
+        _, h = oracle.scan(x[:, a:b], dt[:, a:b], A, B[:, a:b], C[:, a:b], D, z[:, a:b], h)
+        ref[r] = h
+    got = oracle.to_f64(rows)
+    err = np.max(np.abs(got - ref), axis=(1, 2, 3)) / np.maximum(np.max(np.abs(ref), axis=(1, 2, 3)), 1e-30)
+    bad = np.nonzero(err > TOL["f32"])[0]
+    assert len(bad) == 0, f"{len(bad)} stored rows off, first {bad[:5]}, worst {err.max():.3e}"
 
 
 def test_backward_from_stored_states_full_size_long_context_sampled():
