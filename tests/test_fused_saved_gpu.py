@@ -11,8 +11,9 @@ of recomputing them).
 - The backward's gradients match the oracle's scan_fused_bwd to the fused backward's
   tolerance on the plain fused backward's cases and two with fewer than 4 states.
 - selective_scan_fused(save_states=True) returns exactly what the direct calls return.
-- Full size: the 256k prefill with a 4-tap filter, both fused backwards (from the
-  recomputed states and from the stored ones) on a channel sample against the oracle.
+- Full size: the 256k prefill with a 4-tap filter, every stored row and the stored u and
+  dt of its training forward on a channel sample against the oracle, and both fused
+  backwards (from the recomputed states and from the stored ones) on a channel sample.
 """
 import threading
 
@@ -182,6 +183,50 @@ def _oracle_fused_threaded(d, s, threads=16):
     out["dB"] = sum(r["dB"] for r in res)
     out["dC"] = sum(r["dC"] for r in res)
     return out
+
+
+def test_fused_forward_save_full_size_every_stored_row_sampled():
+    # The 256k prefill with a 4-tap filter in the library's own plan: every one of the
+    # 32768 stored rows on a channel sample against the oracle's state entering that step,
+    # and the stored u and dt against the oracle's input stage. The oracle makes u and dt
+    # for the whole sequence, then walks the scan in 8-step pieces, each resumed from the
+    # last one's final state (its split/resume is exact). The GPU's scan takes u and dt in
+    # fp32 from its own input stage: the fp32 tolerance applies to the states, row by row;
+    # the stored u and dt are rounded to bf16 and take the bf16 tolerance.
+    shape = WORKLOADS["long_context_256k"]
+    N, Dn, L = shape.d_state, shape.d_inner, shape.L
+    say("fused stored states 256k, every row: inputs")
+    d = make_scan_inputs(shape, "cuda")
+    s = make_input_stage(shape, 4, "cuda")
+    idx = sample_channels(Dn, 32, seed=31)
+    kw = dict(conv_w=s["conv_w"], conv_b=s["conv_b"], conv_state0=s["conv_state0"], dt_bias=s["dt_bias"])
+    say("fused stored states 256k, every row: forward")
+    _, _, _, st, u, dtv = ssm.ssm_scan_fwd_fused_save(d["x"], s["dt_raw"], d["A"], d["B"], d["C"], d["D"],
+                                                      d["z"], want_conv_state=False, **kw)
+    torch.cuda.synchronize()
+    rows = _rows(st, shape.batch, Dn, N).index_select(2, idx.cuda()).cpu()
+    gc = lambda t: gather_channels(t, idx)
+    u_got, dt_got = gc(u), gc(dtv)
+    del st, u, dtv
+    n = rows.shape[0]
+    assert n == (L + EVERY - 1) // EVERY
+    say("fused stored states 256k, every row: oracle on", len(idx), "channels")
+    ur, _ = oracle.conv_silu(gc(d["x"]), s["conv_w"].cpu()[idx], s["conv_b"].cpu()[idx], gc(s["conv_state0"]))
+    dtr = oracle.softplus(gc(s["dt_raw"]), s["dt_bias"].cpu()[idx])
+    assert rel_err(u_got, ur) <= TOL["bf16"] and rel_err(dt_got, dtr) <= TOL["bf16"], "stored u or dt"
+    z = oracle.to_f64(gc(d["z"]))
+    B, C = oracle.to_f64(d["B"].cpu()), oracle.to_f64(d["C"].cpu())
+    A, D = oracle.to_f64(d["A"].cpu()[idx]), oracle.to_f64(d["D"].cpu()[idx])
+    ref = np.zeros((n, shape.batch, len(idx), N))
+    h = ref[0].copy()
+    for r in range(1, n):
+        a, b = (r - 1) * EVERY, r * EVERY
+        _, h = oracle.scan(ur[:, a:b], dtr[:, a:b], A, B[:, a:b], C[:, a:b], D, z[:, a:b], h)
+        ref[r] = h
+    got = oracle.to_f64(rows)
+    err = np.max(np.abs(got - ref), axis=(1, 2, 3)) / np.maximum(np.max(np.abs(ref), axis=(1, 2, 3)), 1e-30)
+    bad = np.nonzero(err > TOL["f32"])[0]
+    assert len(bad) == 0, f"{len(bad)} stored rows off, first {bad[:5]}, worst {err.max():.3e}"
 
 
 def test_fused_backwards_full_size_long_context_sampled():

@@ -9,8 +9,10 @@ reads those states instead of recomputing them by a forward walk).
   on the plain backward's cases (chunks of every length, ragged ends, every state size,
   padding waves, bf16 with N = 1 and odd rows of B and C).
 - selective_scan(save_states=True) returns exactly what the two direct calls return.
-- Full size: the 256k prefill's backward from stored states on a channel sample, as the
-  plain backward's full-size test does it.
+- Full size: every stored row of the 256k training forward on a channel sample against
+  the oracle's sequential states (fp32 tolerance, row by row), and the 256k prefill's
+  backward from stored states on a channel sample, as the plain backward's full-size test
+  does it.
 """
 import numpy as np
 import pytest
